@@ -1,0 +1,168 @@
+"""Seeded synthetic inputs for the gated linear-attention path.
+
+This module holds no arithmetic of the method: it only draws random tensors
+with the shapes and distributions of the workloads and casts them to the
+storage dtype.  Both the HIP path and the CPU oracle take their inputs from
+here; neither imports the other.
+
+Recipe (every workload): a ``torch.Generator`` seeded with the workload's seed
+draws, on the CPU in float32 and in this order, q, k, v, g, h0, dO, dhT (a
+tensor that the workload does not use is not drawn).  Then every tensor except
+the fp32 states (h0, dhT) is cast to the storage dtype with round-to-nearest-
+even.  Document lengths for packed rows come from ``numpy.random.default_rng``
+with the same seed: integers drawn uniformly from the inclusive range until
+they cover T, the last one truncated to fit.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass
+class Case:
+    name: str
+    gate: str                     # "scalar" or "vector"
+    dtype: torch.dtype            # storage dtype of q, k, v, g, o and the gradients
+    q: torch.Tensor               # [B, T, H_qk, d_k]
+    k: torch.Tensor               # [B, T, H_qk, d_k]
+    v: torch.Tensor               # [B, T, H, d_v]
+    g: torch.Tensor               # [B, T, H] or [B, T, H, d_k], natural-log gate
+    dO: torch.Tensor              # [B, T, H, d_v]
+    h0: Optional[torch.Tensor] = None          # [B, H, d_k, d_v] fp32
+    dhT: Optional[torch.Tensor] = None         # [B, H, d_k, d_v] fp32
+    segment_ids: Optional[torch.Tensor] = None  # [B, T] int32
+    chunk: int = 64
+    doc_lengths: Optional[list] = None
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def T(self): return self.q.shape[1]
+    @property
+    def H_qk(self): return self.q.shape[2]
+    @property
+    def d_k(self): return self.q.shape[3]
+    @property
+    def H(self): return self.v.shape[2]
+    @property
+    def d_v(self): return self.v.shape[3]
+
+    def tensors(self):
+        return dict(q=self.q, k=self.k, v=self.v, g=self.g, dO=self.dO, h0=self.h0,
+                    dhT=self.dhT, segment_ids=self.segment_ids)
+
+    def to(self, device):
+        kw = {}
+        for f in ("q", "k", "v", "g", "dO", "h0", "dhT", "segment_ids"):
+            x = getattr(self, f)
+            kw[f] = None if x is None else x.to(device)
+        return dataclasses.replace(self, **kw)
+
+
+def doc_lengths(T: int, lo: int, hi: int, seed: int):
+    """Document lengths drawn from U[lo, hi] (inclusive) until they cover T."""
+    rng = np.random.default_rng(seed)
+    out, tot = [], 0
+    while tot < T:
+        n = int(rng.integers(lo, hi + 1))
+        n = min(n, T - tot)
+        out.append(n)
+        tot += n
+    return out
+
+
+def segment_ids_from_lengths(lengths, T: int) -> torch.Tensor:
+    ids = np.concatenate([np.full(n, i, dtype=np.int32) for i, n in enumerate(lengths)])
+    assert ids.shape[0] == T
+    return torch.from_numpy(ids)
+
+
+def _gate(gen, shape, kind: str):
+    x = torch.randn(shape, generator=gen)
+    if kind == "ssd_mild":       # -0.1 * softplus(N(0,1))
+        return -0.1 * torch.nn.functional.softplus(x)
+    if kind == "ssd_mamba":      # -exp(U(-4,0)) * softplus(N(0,1)); U drawn after N
+        u = torch.rand(shape, generator=gen) * 4.0 - 4.0
+        return -torch.exp(u) * torch.nn.functional.softplus(x)
+    if kind == "gla":            # logsigmoid(N(0,1)) / 16
+        return torch.nn.functional.logsigmoid(x) / 16.0
+    raise ValueError(kind)
+
+
+def make_case(name, *, B, T, H, H_qk, d_k, d_v, gate, dtype, seed, gate_kind,
+              qk_scale=None, with_h0=False, with_dhT=False, lengths=None,
+              chunk=64, gate_mult=1.0) -> Case:
+    gen = torch.Generator().manual_seed(seed)
+    s = (1.0 / math.sqrt(d_k)) if qk_scale is None else qk_scale
+    q = torch.randn((B, T, H_qk, d_k), generator=gen) * s
+    k = torch.randn((B, T, H_qk, d_k), generator=gen) * s
+    v = torch.randn((B, T, H, d_v), generator=gen)
+    gshape = (B, T, H, d_k) if gate == "vector" else (B, T, H)
+    g = _gate(gen, gshape, gate_kind) * gate_mult
+    h0 = torch.randn((B, H, d_k, d_v), generator=gen) * 0.1 if with_h0 else None
+    dO = torch.randn((B, T, H, d_v), generator=gen)
+    dhT = torch.randn((B, H, d_k, d_v), generator=gen) if with_dhT else None
+    seg = None
+    if lengths is not None:
+        assert B == 1 or all(len(x) for x in lengths)
+        seg = segment_ids_from_lengths(lengths, T).reshape(1, T).repeat(B, 1).contiguous()
+    cast = lambda x: x.to(dtype).contiguous()
+    return Case(name=name, gate=gate, dtype=dtype, q=cast(q), k=cast(k), v=cast(v),
+                g=cast(g), dO=cast(dO), h0=h0, dhT=dhT, segment_ids=seg, chunk=chunk,
+                doc_lengths=lengths)
+
+
+# The five workloads (c5 has two layouts of the same 16,384 tokens per step).
+WORKLOADS = {
+    "c1": "SSD scalar gate, fp32, B=1 H=2 T=256 d=64, chunk 64",
+    "c2": "SSD scalar gate, fp32, B=4 T=8192 H=8 (2 q/k groups of 4) d=128, chunk 64",
+    "c3": "GLA vector gate, bf16, B=4 T=4096 H=16 d=128, chunk 64, h0 and dhT",
+    "c4": "SSD scalar gate, bf16, packed documents, B=1 T=65536 H=16 d=128, chunk 64, h0",
+    "c5a": "GLA vector gate, bf16, B=1 T=16384 H=16 d=128, chunk 64, h0 and dhT",
+    "c5b": "GLA vector gate, bf16, B=8 T=2048 H=16 d=128, chunk 64, h0 and dhT",
+}
+
+
+def workload(name: str) -> Case:
+    if name == "c1":
+        return make_case(name, B=1, T=256, H=2, H_qk=2, d_k=64, d_v=64, gate="scalar",
+                         dtype=torch.float32, seed=1, gate_kind="ssd_mild")
+    if name == "c2":
+        return make_case(name, B=4, T=8192, H=8, H_qk=2, d_k=128, d_v=128, gate="scalar",
+                         dtype=torch.float32, seed=2, gate_kind="ssd_mamba")
+    if name == "c3":
+        return make_case(name, B=4, T=4096, H=16, H_qk=16, d_k=128, d_v=128, gate="vector",
+                         dtype=torch.bfloat16, seed=3, gate_kind="gla", with_h0=True,
+                         with_dhT=True)
+    if name == "c4":
+        T = 65536
+        lens = doc_lengths(T, 512, 8192, seed=4)
+        return make_case(name, B=1, T=T, H=16, H_qk=16, d_k=128, d_v=128, gate="scalar",
+                         dtype=torch.bfloat16, seed=4, gate_kind="ssd_mamba", with_h0=True,
+                         lengths=lens)
+    if name == "c5a":
+        return make_case(name, B=1, T=16384, H=16, H_qk=16, d_k=128, d_v=128, gate="vector",
+                         dtype=torch.bfloat16, seed=5, gate_kind="gla", with_h0=True,
+                         with_dhT=True)
+    if name == "c5b":
+        return make_case(name, B=8, T=2048, H=16, H_qk=16, d_k=128, d_v=128, gate="vector",
+                         dtype=torch.bfloat16, seed=5, gate_kind="gla", with_h0=True,
+                         with_dhT=True)
+    raise KeyError(name)
+
+
+def small_case(seed=0, *, B=1, T=100, H=2, H_qk=None, d=64, d_v=None, gate="scalar",
+               dtype=torch.float32, with_h0=True, with_dhT=True, lengths=None,
+               gate_kind=None, gate_mult=1.0) -> Case:
+    """A small case for parity sweeps (same distributions as the workloads)."""
+    H_qk = H if H_qk is None else H_qk
+    d_v = d if d_v is None else d_v
+    gk = gate_kind or ("gla" if gate == "vector" else "ssd_mamba")
+    return make_case("small", B=B, T=T, H=H, H_qk=H_qk, d_k=d, d_v=d_v, gate=gate,
+                     dtype=dtype, seed=seed, gate_kind=gk, with_h0=with_h0,
+                     with_dhT=with_dhT, lengths=lengths, gate_mult=gate_mult)
