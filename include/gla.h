@@ -1,0 +1,129 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) chunk-parallel gated linear attention.
+ *
+ * The operation (per batch row b and head h) is the gated linear-attention
+ * recurrence
+ *
+ *     S_t = diag(alpha_t) S_{t-1} + k_t v_t^T,      o_t = S_t^T q_t,
+ *
+ * with S_{-1} = h0 and hT = S_{T-1}, as written on the FLAT page ("FLAT: Flash
+ * Linear Attention on TPUs", section Linear Attention > Forward Recurrence and
+ * the table of gated forms, whose notation F_t = prod_{s<=t} f_s covers both
+ * gate forms here):
+ *
+ *   - GLA_GATE_SCALAR: one gate per (b, t, h), the Mamba-2 / SSD form;
+ *   - GLA_GATE_VECTOR: one gate per key channel, f_t in R^{d_k}, the GLA form.
+ *
+ * g holds the natural logarithm of the gate, alpha_t = exp(g_t), any finite
+ * value.  There is no internal 1/sqrt(d) scale: callers pre-scale q and k.
+ *
+ * Document resets (JLA page, "JLA: JAX Linear Attention", the segment_ids
+ * paragraph): wherever segment_ids[b,t] differs from segment_ids[b,t-1] the
+ * carried state is dropped before token t is added (alpha_t is then unused),
+ * so a packed row computes exactly what its documents would compute one by
+ * one; h0 seeds only the row's first document and hT is the state after the
+ * row's last token.
+ *
+ * gla_bwd returns the gradients of a scalar loss L given dO = dL/do and
+ * dhT = dL/dhT (FLAT page, Linear Attention > Backward Recurrence: the state
+ * gradient runs backwards in time with the gate scaling it at each step, and
+ * the log-gate gradient is f_t * (grad_{H_t} (.) H_{t-1}) 1_V).  dg is the
+ * gradient with respect to the log gate g; it is 0 at reset tokens.  When
+ * H_qk < H, each q/k head is read by H / H_qk consecutive heads (head h reads
+ * q/k head h / (H / H_qk)) and dq, dk are summed over those heads (FLAT page,
+ * Pallas Kernels > Gated Linear Attention, the paragraph on head sharing).
+ *
+ * Layouts: all tensors are row-major and contiguous.
+ *     q, k, dq, dk           [B, T, H_qk, d_k]   dtype
+ *     v, o, dO, dv           [B, T, H, d_v]      dtype
+ *     g, dg  scalar gate     [B, T, H]           dtype
+ *            vector gate     [B, T, H, d_k]      dtype
+ *     h0, hT, dhT, dh0       [B, H, d_k, d_v]    float32 always
+ *     segment_ids            [B, T]              int32
+ * dtype is GLA_F32 (IEEE float32) or GLA_BF16 (bfloat16); products run on the
+ * matrix cores in that dtype with float32 accumulation, and every state, gate
+ * prefix and gate-gradient sum is carried in float32.  Outputs in bf16 are
+ * rounded to nearest even.
+ *
+ * Pointers: every tensor pointer is a device pointer on the current HIP
+ * device, 16-byte aligned.  Nullable pointers: h0 (zeros), segment_ids (one
+ * document per row), hT (not written), dhT (zeros), dh0 (not written).  All
+ * others are required.  ws is a device workspace of ws_bytes bytes, at least
+ * gla_workspace_size(); it may be NULL when that size is 0.
+ *
+ * Ownership and ordering: the caller allocates and frees every buffer; the
+ * library allocates nothing, frees nothing, never synchronises and keeps no
+ * state between calls.  Work is enqueued on `stream` (a hipStream_t; NULL is
+ * the default stream) and the call returns before it completes.  Inputs are
+ * read only.  Outputs are fully overwritten (never accumulated into) and must
+ * not alias inputs, each other or the workspace.  Two calls that share a
+ * workspace must be ordered on one stream.
+ *
+ * Errors: every argument is checked on the host before anything is launched;
+ * a failed check returns a negative gla_status and enqueues nothing.  Sizes:
+ * B >= 1, T >= 0, H >= 1, 1 <= H_qk <= H with H % H_qk == 0, d_k and d_v in
+ * {64, 128}, chunk == 64.  A launch failure returns GLA_E_LAUNCH.  There is no
+ * fallback path: a shape the kernels do not cover is an error.
+ */
+#ifndef GLA_H
+#define GLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GLA_OK = 0,
+    GLA_E_NULL = -1,        /* a required pointer is NULL */
+    GLA_E_SHAPE = -2,       /* sizes inconsistent or out of range */
+    GLA_E_DTYPE = -3,       /* unknown dtype or gate kind */
+    GLA_E_UNSUPPORTED = -4, /* valid, but no kernel for this d_k / d_v / chunk */
+    GLA_E_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+    GLA_E_WORKSPACE = -6,   /* workspace missing or smaller than required */
+    GLA_E_DEVICE = -7,      /* no HIP device, or the current device is not gfx950 */
+    GLA_E_LAUNCH = -8       /* a kernel launch failed */
+} gla_status;
+
+typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+typedef enum { GLA_GATE_SCALAR = 0, GLA_GATE_VECTOR = 1 } gla_gate;
+
+/* Problem description, passed by pointer (host memory, read during the call). */
+typedef struct {
+    int64_t B, T, H, H_qk, d_k, d_v;
+    int32_t chunk;  /* tokens per chunk; 64 */
+    int32_t gate;   /* gla_gate */
+    int32_t dtype;  /* gla_dtype */
+    int32_t reserved; /* must be 0 */
+} gla_problem;
+
+/* Bytes of device workspace gla_fwd (for_backward == 0) or gla_bwd
+ * (for_backward != 0) needs for this problem.  Writes it to *bytes and returns
+ * GLA_OK, or returns a negative status for an invalid problem. */
+int gla_workspace_size(const gla_problem* p, int for_backward, size_t* bytes);
+
+/* Forward: o (and hT if non-NULL) from q, k, v, g, h0, segment_ids. */
+int gla_fwd(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
+            const float* h0, const int32_t* segment_ids, void* o, float* hT, void* ws,
+            size_t ws_bytes, void* stream);
+
+/* Backward: dq, dk, dv, dg (and dh0 if non-NULL) from the forward's inputs and
+ * the upstream gradients dO and dhT.  Recomputes whatever it needs from the
+ * inputs; it does not read anything gla_fwd produced. */
+int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
+            const float* h0, const int32_t* segment_ids, const void* dO, const float* dhT,
+            void* dq, void* dk, void* dv, void* dg, float* dh0, void* ws, size_t ws_bytes,
+            void* stream);
+
+/* Static description of a status code. */
+const char* gla_status_str(int status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int gla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GLA_H */

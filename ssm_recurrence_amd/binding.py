@@ -1,0 +1,187 @@
+"""ctypes binding of the C ABI in include/gla.h (argument marshalling only).
+
+torch supplies device memory and the current HIP stream; every step of the
+computation runs in the HIP library.  There is no fallback: if the library is
+not built, or the device is not a gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libgla.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "gla.h")
+
+GLA_F32, GLA_BF16 = 0, 1
+GLA_GATE_SCALAR, GLA_GATE_VECTOR = 0, 1
+STATUS = {0: "GLA_OK", -1: "GLA_E_NULL", -2: "GLA_E_SHAPE", -3: "GLA_E_DTYPE",
+          -4: "GLA_E_UNSUPPORTED", -5: "GLA_E_ALIGN", -6: "GLA_E_WORKSPACE",
+          -7: "GLA_E_DEVICE", -8: "GLA_E_LAUNCH"}
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("H_qk", ctypes.c_int64), ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64),
+                ("chunk", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class GlaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = "%s failed: %s (%d)" % (what, STATUS.get(status, "?"), status)
+        try:
+            msg += ": " + load().gla_status_str(status).decode()
+        except Exception:  # pragma: no cover
+            pass
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def load():
+    """Load libgla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("HIP library not built: %s (run ssm_recurrence_amd.build)" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P, vp, sz = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_size_t
+        lib.gla_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz)]
+        lib.gla_workspace_size.restype = ctypes.c_int
+        lib.gla_fwd.argtypes = [P] + [vp] * 9 + [sz, vp]
+        lib.gla_fwd.restype = ctypes.c_int
+        lib.gla_bwd.argtypes = [P] + [vp] * 14 + [sz, vp]
+        lib.gla_bwd.restype = ctypes.c_int
+        lib.gla_status_str.argtypes = [ctypes.c_int]
+        lib.gla_status_str.restype = ctypes.c_char_p
+        lib.gla_version.argtypes = []
+        lib.gla_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/gla.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z_0-9]+)\s*\(", txt)))
+
+
+def make_problem(B, T, H, H_qk, d_k, d_v, gate="scalar", dtype=torch.bfloat16, chunk=64):
+    return Problem(B, T, H, H_qk, d_k, d_v, chunk,
+                   GLA_GATE_VECTOR if gate == "vector" else GLA_GATE_SCALAR,
+                   GLA_BF16 if dtype == torch.bfloat16 else GLA_F32, 0)
+
+
+def workspace_size(prob: Problem, backward: bool) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().gla_workspace_size(ctypes.byref(prob), int(bool(backward)), ctypes.byref(n))
+    if rc:
+        raise GlaError(rc, "gla_workspace_size")
+    return n.value
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def problem_of(q, v, g, gate, chunk=64):
+    B, T, H_qk, d_k = q.shape
+    H, d_v = v.shape[2], v.shape[3]
+    want = (B, T, H, d_k) if gate == "vector" else (B, T, H)
+    if tuple(g.shape) != want:
+        raise ValueError("g has shape %s, expected %s" % (tuple(g.shape), want))
+    return make_problem(B, T, H, H_qk, d_k, d_v, gate, q.dtype, chunk)
+
+
+def _workspace(prob, backward, device, ws):
+    n = workspace_size(prob, backward)
+    if n == 0:
+        return None, 0
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+    return ws, ws.numel()
+
+
+def fwd(q, k, v, g, h0=None, segment_ids=None, *, gate="scalar", chunk=64, want_hT=True,
+        out=None, ws=None):
+    """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g")):
+        _check(t, n, q.dtype)
+    _check(h0, "h0", torch.float32)
+    _check(segment_ids, "segment_ids", torch.int32)
+    prob = problem_of(q, v, g, gate, chunk)
+    B, T, H, d_v, d_k = prob.B, prob.T, prob.H, prob.d_v, prob.d_k
+    o = out if out is not None else torch.empty((B, T, H, d_v), dtype=q.dtype, device=q.device)
+    hT = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device) if want_hT else None
+    ws, nws = _workspace(prob, False, q.device, ws)
+    rc = load().gla_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(h0), _p(segment_ids),
+                        _p(o), _p(hT), _p(ws), nws, _stream())
+    if rc:
+        raise GlaError(rc, "gla_fwd")
+    return o, hT
+
+
+def bwd(q, k, v, g, dO, h0=None, segment_ids=None, dhT=None, *, gate="scalar", chunk=64,
+        want_dh0=True, ws=None):
+    """dq, dk [B,T,H_qk,d_k], dv [B,T,H,d_v], dg (shape of g), dh0 fp32 (or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (dO, "dO")):
+        _check(t, n, q.dtype)
+    _check(h0, "h0", torch.float32)
+    _check(dhT, "dhT", torch.float32)
+    _check(segment_ids, "segment_ids", torch.int32)
+    prob = problem_of(q, v, g, gate, chunk)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    dh0 = (torch.empty((prob.B, prob.H, prob.d_k, prob.d_v), dtype=torch.float32, device=q.device)
+           if want_dh0 else None)
+    ws, nws = _workspace(prob, True, q.device, ws)
+    rc = load().gla_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(h0), _p(segment_ids),
+                        _p(dO), _p(dhT), _p(dq), _p(dk), _p(dv), _p(dg), _p(dh0), _p(ws), nws,
+                        _stream())
+    if rc:
+        raise GlaError(rc, "gla_bwd")
+    return dq, dk, dv, dg, dh0
+
+
+class GLAFunction(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run the HIP library."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, h0, segment_ids, gate):
+        o, hT = fwd(q, k, v, g, h0, segment_ids, gate=gate)
+        ctx.save_for_backward(q, k, v, g, h0, segment_ids)
+        ctx.gate = gate
+        return o, hT
+
+    @staticmethod
+    def backward(ctx, dO, dhT):
+        q, k, v, g, h0, seg = ctx.saved_tensors
+        dO = dO.contiguous() if dO is not None else torch.zeros_like(v)
+        dhT = dhT.contiguous().float() if dhT is not None else None
+        dq, dk, dv, dg, dh0 = bwd(q, k, v, g, dO, h0, seg, dhT, gate=ctx.gate,
+                                  want_dh0=h0 is not None)
+        return dq, dk, dv, dg, dh0, None, None

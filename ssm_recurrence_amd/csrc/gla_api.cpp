@@ -1,0 +1,243 @@
+// gla_api.cpp -- the C ABI declared in include/gla.h: argument checks (all on
+// the host, before anything is enqueued), workspace sizing and dispatch to the
+// gfx950 kernels.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/gla.h"
+#include "gla_common.hpp"
+#include "gla_kernels.hpp"
+
+namespace {
+
+using gla::bf16;
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+// Size and kind checks shared by every entry point.
+int check_problem(const gla_problem* p) {
+    if (!p) return GLA_E_NULL;
+    if (p->dtype != GLA_F32 && p->dtype != GLA_BF16) return GLA_E_DTYPE;
+    if (p->gate != GLA_GATE_SCALAR && p->gate != GLA_GATE_VECTOR) return GLA_E_DTYPE;
+    if (p->reserved != 0) return GLA_E_SHAPE;
+    if (p->B < 1 || p->T < 0 || p->H < 1 || p->H_qk < 1 || p->H_qk > p->H) return GLA_E_SHAPE;
+    if (p->H % p->H_qk != 0) return GLA_E_SHAPE;
+    if (p->d_k < 1 || p->d_v < 1 || p->chunk < 1) return GLA_E_SHAPE;
+    if ((p->d_k != 64 && p->d_k != 128) || (p->d_v != 64 && p->d_v != 128)) return GLA_E_UNSUPPORTED;
+    if (p->chunk != 64) return GLA_E_UNSUPPORTED;
+    // every element count and launch grid must fit
+    int64_t x, bt, bth;
+    if (!mul_ok(p->B, p->T, &bt) || !mul_ok(bt, p->H, &bth) || !mul_ok(bth, 128, &x)) return GLA_E_SHAPE;
+    if (x > ((int64_t)1 << 40)) return GLA_E_SHAPE;
+    const int64_t nc = (p->T + 63) / 64;
+    if (p->B * p->H * (nc > 0 ? nc : 1) > ((int64_t)1 << 31) - 1) return GLA_E_SHAPE;
+    return GLA_OK;
+}
+
+struct WsLayout {
+    size_t S = 0, dS = 0, dq = 0, dk = 0, total = 0;
+};
+
+WsLayout ws_layout(const gla_problem* p, int for_backward) {
+    WsLayout L;
+    if (!for_backward) return L;
+    const int64_t nc = (p->T + 63) / 64;
+    const size_t st = (size_t)p->d_k * (size_t)p->d_v * sizeof(float);
+    const size_t bh = (size_t)(p->B * p->H);
+    size_t off = 0;
+    L.S = off;
+    off += round_up(bh * (size_t)(nc + 1) * st);
+    L.dS = off;
+    off += round_up(bh * (size_t)nc * st);
+    if (p->H_qk != p->H) {
+        const size_t n = (size_t)(p->B * p->T * p->H * p->d_k) * sizeof(float);
+        L.dq = off;
+        off += round_up(n);
+        L.dk = off;
+        off += round_up(n);
+    }
+    L.total = off;
+    return L;
+}
+
+bool aligned(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// The current device must be a gfx950.  The answer is cached per device id.
+int check_device() {
+    static std::mutex mu;
+    static signed char known[64];  // 0 unknown, 1 ok, -1 not gfx950
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GLA_E_DEVICE;
+    if (dev < 64) {
+        std::lock_guard<std::mutex> lock(mu);
+        if (known[dev] == 0) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GLA_E_DEVICE;
+            known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        }
+        return known[dev] == 1 ? GLA_OK : GLA_E_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GLA_E_DEVICE;
+    return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? GLA_OK : GLA_E_DEVICE;
+}
+
+__global__ void k_copy_state(float* dst, const float* src, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+int copy_state(float* dst, const float* src, int64_t n, hipStream_t st) {
+    if (!dst || n == 0) return GLA_OK;
+    hipLaunchKernelGGL(k_copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
+    return hipGetLastError() == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+template <typename T, bool VEC, int DK, int DV>
+hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
+    return gla::launch_pass<T, VEC, DK, DV, gla::MODE_OUT>(a, st);
+}
+
+template <typename T, bool VEC, int DK, int DV>
+hipError_t run_bwd(const gla::PassArgs& pa, const gla::GradArgs& ga, hipStream_t st) {
+    hipError_t e = gla::launch_pass<T, VEC, DK, DV, gla::MODE_STATES>(pa, st);
+    if (e != hipSuccess) return e;
+    e = gla::launch_pass<T, VEC, DK, DV, gla::MODE_DSTATE>(pa, st);
+    if (e != hipSuccess) return e;
+    e = gla::launch_grad<T, VEC, DK, DV>(ga, st);
+    if (e != hipSuccess) return e;
+    if (ga.Hqk != ga.H) {
+        e = gla::launch_group_sum<T, DK>(ga.ws_dq, ga.dq, ga.B, ga.T, ga.H, ga.Hqk, st);
+        if (e != hipSuccess) return e;
+        e = gla::launch_group_sum<T, DK>(ga.ws_dk, ga.dk, ga.B, ga.T, ga.H, ga.Hqk, st);
+    }
+    return e;
+}
+
+// Dispatch over (dtype, gate, d_k, d_v) to a template instance.
+template <template <typename, bool, int, int> class F, typename... Args>
+hipError_t dispatch(const gla_problem* p, Args&&... args) {
+#define GLA_DK_DV(T, VEC)                                                                      \
+    if (p->d_k == 64 && p->d_v == 64) return F<T, VEC, 64, 64>::run(args...);                \
+    if (p->d_k == 64 && p->d_v == 128) return F<T, VEC, 64, 128>::run(args...);              \
+    if (p->d_k == 128 && p->d_v == 64) return F<T, VEC, 128, 64>::run(args...);              \
+    return F<T, VEC, 128, 128>::run(args...);
+    if (p->dtype == GLA_F32) {
+        if (p->gate == GLA_GATE_VECTOR) { GLA_DK_DV(float, true) }
+        GLA_DK_DV(float, false)
+    }
+    if (p->gate == GLA_GATE_VECTOR) { GLA_DK_DV(bf16, true) }
+    GLA_DK_DV(bf16, false)
+#undef GLA_DK_DV
+}
+
+template <typename T, bool VEC, int DK, int DV> struct FwdF {
+    static hipError_t run(const gla::PassArgs& a, hipStream_t st) { return run_fwd<T, VEC, DK, DV>(a, st); }
+};
+template <typename T, bool VEC, int DK, int DV> struct BwdF {
+    static hipError_t run(const gla::PassArgs& pa, const gla::GradArgs& ga, hipStream_t st) {
+        return run_bwd<T, VEC, DK, DV>(pa, ga, st);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+int gla_workspace_size(const gla_problem* p, int for_backward, size_t* bytes) {
+    const int rc = check_problem(p);
+    if (rc) return rc;
+    if (!bytes) return GLA_E_NULL;
+    *bytes = ws_layout(p, for_backward).total;
+    return GLA_OK;
+}
+
+int gla_fwd(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
+            const float* h0, const int32_t* segment_ids, void* o, float* hT, void* ws,
+            size_t ws_bytes, void* stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!q || !k || !v || !g || !o) return GLA_E_NULL;
+    const void* ptrs[] = {q, k, v, g, h0, segment_ids, o, hT, ws};
+    for (const void* x : ptrs)
+        if (x && !aligned(x)) return GLA_E_ALIGN;
+    const WsLayout L = ws_layout(p, 0);
+    if (ws_bytes < L.total || (L.total > 0 && !ws)) return GLA_E_WORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (p->T == 0) return copy_state(hT, h0, p->B * p->H * p->d_k * p->d_v, st);
+
+    gla::PassArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.h0 = h0; a.seg = segment_ids; a.o = o; a.hT = hT;
+    a.B = p->B; a.T = p->T; a.H = p->H; a.Hqk = p->H_qk;
+    return dispatch<FwdF>(p, a, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
+            const float* h0, const int32_t* segment_ids, const void* dO, const float* dhT,
+            void* dq, void* dk, void* dv, void* dg, float* dh0, void* ws, size_t ws_bytes,
+            void* stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg) return GLA_E_NULL;
+    const void* ptrs[] = {q, k, v, g, h0, segment_ids, dO, dhT, dq, dk, dv, dg, dh0, ws};
+    for (const void* x : ptrs)
+        if (x && !aligned(x)) return GLA_E_ALIGN;
+    const WsLayout L = ws_layout(p, 1);
+    if (ws_bytes < L.total || (L.total > 0 && !ws)) return GLA_E_WORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (p->T == 0) return copy_state(dh0, dhT, p->B * p->H * p->d_k * p->d_v, st);
+
+    char* w = (char*)ws;
+    gla::PassArgs pa;
+    memset(&pa, 0, sizeof pa);
+    pa.q = q; pa.k = k; pa.v = v; pa.g = g; pa.dO = dO; pa.h0 = h0; pa.dhT = dhT;
+    pa.seg = segment_ids; pa.dh0 = dh0;
+    pa.ws_S = (float*)(w + L.S);
+    pa.ws_dS = (float*)(w + L.dS);
+    pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.Hqk = p->H_qk;
+    gla::GradArgs ga;
+    memset(&ga, 0, sizeof ga);
+    ga.q = q; ga.k = k; ga.v = v; ga.g = g; ga.dO = dO; ga.seg = segment_ids;
+    ga.ws_S = pa.ws_S; ga.ws_dS = pa.ws_dS;
+    ga.dq = dq; ga.dk = dk; ga.dv = dv; ga.dg = dg;
+    if (p->H_qk != p->H) {
+        ga.ws_dq = (float*)(w + L.dq);
+        ga.ws_dk = (float*)(w + L.dk);
+    }
+    ga.B = p->B; ga.T = p->T; ga.H = p->H; ga.Hqk = p->H_qk;
+    return dispatch<BwdF>(p, pa, ga, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+const char* gla_status_str(int s) {
+    switch (s) {
+        case GLA_OK: return "ok";
+        case GLA_E_NULL: return "a required pointer is NULL";
+        case GLA_E_SHAPE: return "sizes inconsistent or out of range";
+        case GLA_E_DTYPE: return "unknown dtype or gate kind";
+        case GLA_E_UNSUPPORTED: return "no kernel for this d_k / d_v / chunk";
+        case GLA_E_ALIGN: return "a pointer is not 16-byte aligned";
+        case GLA_E_WORKSPACE: return "workspace missing or too small";
+        case GLA_E_DEVICE: return "no HIP device, or the current device is not gfx950";
+        case GLA_E_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int gla_version(void) { return 100; }
+
+}  // extern "C"

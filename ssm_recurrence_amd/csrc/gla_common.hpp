@@ -1,0 +1,178 @@
+// gla_common.hpp -- device helpers shared by the gfx950 kernels: matrix-core
+// fragments, LDS fragment loaders, storage conversions and the chunk prologue
+// (document flags and the chunk-local cumulative log gate).
+//
+// Matrix-core lane layouts (CDNA4, wave64), checked on the hardware:
+//   v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8*(l/16) + e], e < 8;
+//                             B lane l holds B[8*(l/16) + e][l%16];
+//   v_mfma_f32_16x16x4_f32  : A lane l holds A[l%16][l/16]; B lane l holds B[l/16][l%16];
+//   both accumulate into C lane l = C[4*(l/16) + e][l%16], e < 4 ("C layout").
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int C = 64;        // tokens per chunk
+constexpr int NT = 256;      // threads per workgroup (4 waves)
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------------ conversions
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// float -> bf16, round to nearest even (the compiler's conversion does RNE)
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// ------------------------------------------------------------------ matrix-core traits
+template <typename T> struct Mma;
+template <> struct Mma<bf16> {
+    static constexpr int KPL = 8;     // k values per lane per step
+    static constexpr int KSTEP = 32;  // k per instruction
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void set(frag& f, int e, float x) { f[e] = (bf16)x; }
+    static __device__ __forceinline__ frag zero() { frag f; for (int e = 0; e < 8; ++e) f[e] = (bf16)0.0f; return f; }
+};
+template <> struct Mma<float> {
+    static constexpr int KPL = 1;
+    static constexpr int KSTEP = 4;
+    typedef float frag;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void set(frag& f, int, float x) { f = x; }
+    static __device__ __forceinline__ frag zero() { return 0.0f; }
+};
+
+__device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Operand fragment from LDS for one matrix-core step ("natural" k order):
+// lane (i = l%16, j = l/16) receives X(i0 + i, k0 + j*KPL + e), e < KPL, where
+// X(i, k) = base[i*SI + k*SK].  Serves A (i = row m) and B (i = column n).
+template <typename T, int SI, int SK>
+__device__ __forceinline__ typename Mma<T>::frag frag_ld(const T* base, int i0, int k0) {
+    const int l = lane_id();
+    const int i = i0 + (l & 15);
+    const int k = k0 + (l >> 4) * Mma<T>::KPL;
+    typename Mma<T>::frag f;
+    if constexpr (SK == 1 && Mma<T>::KPL == 8) {
+        f = *reinterpret_cast<const bf16x8*>(base + i * SI + k);
+    } else if constexpr (Mma<T>::KPL == 1) {
+        f = base[i * SI + k * SK];
+    } else {
+#pragma unroll
+        for (int e = 0; e < Mma<T>::KPL; ++e) f[e] = base[i * SI + (k + e) * SK];
+    }
+    return f;
+}
+
+// Operand fragment whose k order matches a C-layout accumulator used as the
+// other operand ("ctile" order).  bf16: a 32-wide k step takes rows of two
+// 16-row C tiles, lane group j holding k = 4j+e (e<4) and 16+4j+(e-4) (e>=4).
+// f32: step `sub` (0..3) of a 16-row C tile, lane group j holding k = 4j+sub.
+template <typename T, int SI, int SK>
+__device__ __forceinline__ typename Mma<T>::frag frag_ld_ctile(const T* base, int i0, int k0,
+                                                               int sub) {
+    const int l = lane_id();
+    const int i = i0 + (l & 15);
+    const int j = l >> 4;
+    typename Mma<T>::frag f;
+    if constexpr (Mma<T>::KPL == 1) {
+        f = base[i * SI + (k0 + 4 * j + sub) * SK];
+    } else {
+        (void)sub;
+        if constexpr (SK == 1) {
+            bf16x4 lo = *reinterpret_cast<const bf16x4*>(base + i * SI + k0 + 4 * j);
+            bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + i * SI + k0 + 16 + 4 * j);
+            for (int e = 0; e < 4; ++e) { f[e] = lo[e]; f[4 + e] = hi[e]; }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = base[i * SI + (k0 + 4 * j + e) * SK];
+                f[4 + e] = base[i * SI + (k0 + 16 + 4 * j + e) * SK];
+            }
+        }
+    }
+    return f;
+}
+
+// B (or A) fragment built from fp32 C-layout accumulators: tiles lo (k rows
+// 0..15 of the step) and hi (16..31) for bf16; tile lo, step `sub` for f32.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_from_acc(const f32x4& lo, const f32x4& hi,
+                                                               int sub) {
+    typename Mma<T>::frag f;
+    if constexpr (Mma<T>::KPL == 1) {
+        (void)hi;
+        f = lo[sub];
+    } else {
+        (void)sub;
+        for (int e = 0; e < 4; ++e) { f[e] = (bf16)lo[e]; f[4 + e] = (bf16)hi[e]; }
+    }
+    return f;
+}
+
+// ------------------------------------------------------------------ wave primitives
+__device__ __forceinline__ float wave_incl_scan(float x) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        float y = __shfl_up(x, d, 64);
+        if (l >= d) x += y;
+    }
+    return x;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int y = __shfl_up(x, d, 64);
+        if (l >= d) x += y;
+    }
+    return x;
+}
+
+// ------------------------------------------------------------------ chunk prologue
+// Per chunk: document index of each position (count of resets up to and
+// including it), the first and last reset positions, and validity.
+struct ChunkDocs {
+    int doc[C];     // inclusive prefix count of resets inside the chunk
+    int first_reset;  // C if none
+    int last_reset;   // -1 if none
+    int nvalid;       // positions < T
+};
+
+// Fill `cd` (LDS) for chunk starting at t0 of row b.  Wave 0 does the work;
+// caller synchronises afterwards.
+__device__ __forceinline__ void chunk_docs(ChunkDocs* cd, const int32_t* seg, int64_t b, int64_t T,
+                                           int64_t t0) {
+    if (wave_id() != 0) return;
+    const int r = lane_id();
+    const int64_t t = t0 + r;
+    int reset = 0;
+    if (seg != nullptr && t < T && t > 0) reset = seg[b * T + t] != seg[b * T + t - 1];
+    const int cnt = wave_incl_scan_i(reset);
+    cd->doc[r] = cnt;
+    // first / last reset via ballot
+    const uint64_t m = __ballot(reset);
+    if (r == 0) {
+        cd->first_reset = m ? __builtin_ctzll(m) : C;
+        cd->last_reset = m ? 63 - __builtin_clzll(m) : -1;
+        const int64_t nv = T - t0;
+        cd->nvalid = nv < C ? (int)nv : C;
+    }
+}
+
+}  // namespace gla

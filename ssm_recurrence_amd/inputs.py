@@ -109,7 +109,6 @@ def make_case(name, *, B, T, H, H_qk, d_k, d_v, gate, dtype, seed, gate_kind,
     dhT = torch.randn((B, H, d_k, d_v), generator=gen) if with_dhT else None
     seg = None
     if lengths is not None:
-        assert B == 1 or all(len(x) for x in lengths)
         seg = segment_ids_from_lengths(lengths, T).reshape(1, T).repeat(B, 1).contiguous()
     cast = lambda x: x.to(dtype).contiguous()
     return Case(name=name, gate=gate, dtype=dtype, q=cast(q), k=cast(k), v=cast(v),

@@ -1,0 +1,106 @@
+"""The C-ABI library: it loads, exports every function include/gla.h declares,
+and rejects bad arguments on the host before touching a device (no GPU needed)."""
+import ctypes
+
+import pytest
+import torch
+
+from ssm_recurrence_amd import binding as gb
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gb.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = gb.header_functions()
+    assert set(names) >= {"gla_fwd", "gla_bwd", "gla_workspace_size", "gla_status_str", "gla_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(0, -9, -1):
+        assert lib.gla_status_str(s)
+    assert lib.gla_version() >= 100
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call here fails validation first
+
+
+def call_fwd(lib, prob, ptrs=None, ws_bytes=0):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, h0=None, seg=None, o=FAKE, hT=None, ws=None)
+    p.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_fwd(None if prob is None else ctypes.byref(prob), c(p["q"]), c(p["k"]),
+                       c(p["v"]), c(p["g"]), c(p["h0"]), c(p["seg"]), c(p["o"]), c(p["hT"]),
+                       c(p["ws"]), ws_bytes, None)
+
+
+def call_bwd(lib, prob, ptrs=None, ws_bytes=0):
+    names = ["q", "k", "v", "g", "h0", "seg", "dO", "dhT", "dq", "dk", "dv", "dg", "dh0", "ws"]
+    p = {n: FAKE for n in names}
+    p.update(h0=None, seg=None, dhT=None, dh0=None, ws=None)
+    p.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_bwd(ctypes.byref(prob), *[c(p[n]) for n in names], ws_bytes, None)
+
+
+def prob(**kw):
+    d = dict(B=2, T=100, H=4, H_qk=2, d_k=128, d_v=64, gate="vector", dtype=torch.bfloat16)
+    d.update(kw)
+    return gb.make_problem(**d)
+
+
+def test_null_problem_and_pointers(lib):
+    assert call_fwd(lib, None) == -1
+    assert call_fwd(lib, prob(), {"q": None}) == -1
+    assert call_fwd(lib, prob(), {"o": None}) == -1
+    assert call_bwd(lib, prob(), {"dg": None}) == -1
+    n = ctypes.c_size_t()
+    assert lib.gla_workspace_size(ctypes.byref(prob()), 1, None) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), -2), (dict(T=-1), -2), (dict(H=3, H_qk=2), -2), (dict(H_qk=5, H=4), -2),
+    (dict(d_k=0), -2), (dict(d_k=96), -4), (dict(d_v=32), -4), (dict(chunk=32), -4),
+    (dict(chunk=0), -2),
+])
+def test_shape_errors(lib, kw, code):
+    assert call_fwd(lib, prob(**kw)) == code
+    assert call_bwd(lib, prob(**kw)) == code
+
+
+def test_dtype_and_gate_errors(lib):
+    p = prob()
+    p.dtype = 7
+    assert call_fwd(lib, p) == -3
+    p = prob()
+    p.gate = 2
+    assert call_bwd(lib, p) == -3
+    p = prob()
+    p.reserved = 1
+    assert call_fwd(lib, p) == -2
+
+
+def test_alignment_errors(lib):
+    assert call_fwd(lib, prob(), {"v": FAKE + 4}) == -5
+    assert call_fwd(lib, prob(), {"h0": FAKE + 8}) == -5
+    assert call_bwd(lib, prob(), {"dh0": FAKE + 2}) == -5
+
+
+def test_workspace_errors_and_size(lib):
+    p = prob()
+    n = ctypes.c_size_t()
+    assert lib.gla_workspace_size(ctypes.byref(p), 1, ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert call_bwd(lib, p, {"ws": None}, ws_bytes=n.value) == -6
+    assert call_bwd(lib, p, {"ws": FAKE}, ws_bytes=n.value - 1) == -6
+    assert lib.gla_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_valid_call_without_gpu_reports_device_error(lib):
+    """No silent fallback: with no usable device a valid call returns GLA_E_DEVICE."""
+    assert call_fwd(lib, prob(H_qk=4, d_v=128)) == -7

@@ -1,0 +1,128 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element.
+
+Tolerance (per tensor): max|gpu - oracle| / max|oracle| <= 1e-4 for fp32
+inputs and <= 2e-2 for bf16 inputs (fp32 accumulation), for o, hT and every
+gradient.  The oracle reads exactly the values the GPU reads (bf16 inputs are
+rounded once, when drawn).  Outputs and workspace are poisoned with NaN before
+each call, so any element a kernel fails to write shows up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ssm_recurrence_amd import binding as gb
+from ssm_recurrence_amd.inputs import small_case, workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+@pytest.fixture(autouse=True)
+def nan_poison(monkeypatch):
+    """torch.empty / empty_like return NaN-filled (or 0xFF-filled) memory."""
+    real_empty, real_like = torch.empty, torch.empty_like
+
+    def poison(t):
+        if t.is_floating_point():
+            t.fill_(float("nan"))
+        elif t.dtype == torch.uint8:
+            t.fill_(255)
+        return t
+
+    monkeypatch.setattr(torch, "empty", lambda *a, **k: poison(real_empty(*a, **k)))
+    monkeypatch.setattr(torch, "empty_like", lambda *a, **k: poison(real_like(*a, **k)))
+    yield
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(a)), "non-finite values in GPU output"
+    m = np.max(np.abs(b))
+    d = np.max(np.abs(a - b))
+    return d / m if m > 0 else d
+
+
+def to_np(t):
+    return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_gpu(case, dev="cuda"):
+    c = case.to(dev)
+    o, hT = gb.fwd(c.q, c.k, c.v, c.g, c.h0, c.segment_ids, gate=c.gate)
+    dq, dk, dv, dg, dh0 = gb.bwd(c.q, c.k, c.v, c.g, c.dO, c.h0, c.segment_ids, c.dhT, gate=c.gate)
+    torch.cuda.synchronize()
+    return dict(o=o, hT=hT, dq=dq, dk=dk, dv=dv, dg=dg, dh0=dh0)
+
+
+def run_oracle(case):
+    o, hT = oracle.fwd(case.q, case.k, case.v, case.g, case.h0, case.segment_ids, gate=case.gate)
+    dq, dk, dv, dg, dh0 = oracle.bwd(case.q, case.k, case.v, case.g, case.dO, case.h0,
+                                     case.segment_ids, case.dhT, gate=case.gate)
+    return dict(o=o, hT=hT, dq=dq, dk=dk, dv=dv, dg=dg, dh0=dh0)
+
+
+def check(case, got=None, ref=None):
+    got = got or run_gpu(case)
+    ref = ref or run_oracle(case)
+    tol = TOL[case.dtype]
+    errs = {n: rel(to_np(got[n]), ref[n]) for n in ref}
+    print(case.name, case.gate, case.dtype, tuple(case.q.shape), tuple(case.v.shape),
+          {n: "%.2e" % e for n, e in errs.items()}, flush=True)
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, "parity failed: %s (tol %g)" % (bad, tol)
+    return got, ref
+
+
+SMALL = [
+    # (T, d_k, d_v, gate, dtype, H, H_qk, lengths, h0/dhT)
+    (1, 64, 64, "scalar", torch.float32, 2, 2, None, True),
+    (63, 64, 64, "scalar", torch.float32, 2, 2, None, True),
+    (64, 64, 64, "vector", torch.float32, 2, 2, None, True),
+    (100, 128, 128, "scalar", torch.float32, 2, 1, None, True),
+    (100, 128, 128, "vector", torch.float32, 2, 2, None, True),
+    (130, 64, 128, "vector", torch.float32, 4, 2, None, False),
+    (200, 128, 64, "scalar", torch.float32, 4, 1, [64, 1, 50, 3, 82], True),
+    (1, 128, 128, "vector", torch.bfloat16, 2, 2, None, True),
+    (63, 128, 128, "scalar", torch.bfloat16, 2, 2, None, True),
+    (100, 128, 128, "vector", torch.bfloat16, 4, 4, None, True),
+    (256, 128, 128, "vector", torch.bfloat16, 2, 2, [100, 28, 128], True),
+    (256, 128, 128, "scalar", torch.bfloat16, 4, 2, [64, 64, 1, 1, 1, 60, 65], True),
+    (190, 64, 64, "vector", torch.bfloat16, 2, 1, [5, 7, 1, 100, 77], False),
+    (300, 64, 128, "scalar", torch.bfloat16, 8, 2, None, True),
+]
+
+
+@pytest.mark.parametrize("T,dk,dv,gate,dtype,H,Hqk,lens,hs", SMALL,
+                         ids=["T%d-%d-%d-%s-%s-H%d-%d-%s-%s" % (c[0], c[1], c[2], c[3],
+                              str(c[4])[6:], c[5], c[6], "seg" if c[7] else "noseg",
+                              "h0" if c[8] else "noh0") for c in SMALL])
+def test_small_parity(T, dk, dv, gate, dtype, H, Hqk, lens, hs):
+    case = small_case(seed=T * 7 + dk + H, B=2, T=T, H=H, H_qk=Hqk, d=dk, d_v=dv, gate=gate,
+                      dtype=dtype, with_h0=hs, with_dhT=hs, lengths=lens)
+    check(case)
+
+
+def test_workload_c1():
+    """Scalar-decay fp32, B=1 H=2 T=256 d=64, chunk 64 (the small oracle-sized workload)."""
+    check(workload("c1"))
+
+
+def test_deterministic():
+    case = small_case(seed=3, B=1, T=200, H=4, H_qk=2, d=128, gate="vector", dtype=torch.bfloat16,
+                      lengths=[70, 130])
+    a = run_gpu(case)
+    b = run_gpu(case)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_strong_decay_stays_finite():
+    """Gates 10x stronger than the GLA workload's: no inf or NaN, parity holds."""
+    case = small_case(seed=11, B=1, T=192, H=2, d=128, gate="vector", dtype=torch.bfloat16,
+                      gate_kind="gla", gate_mult=10.0)
+    check(case)
