@@ -1,0 +1,174 @@
+"""Benchmark: chunked gated linear attention forward + backward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one gla_fwd followed by one gla_bwd (the whole hot path) over one
+batch of seeded synthetic inputs already resident in device memory.  The
+default workload is the Mamba-2/SSD shape: scalar decay, fp32, B=4, T=8192,
+8 heads in 2 q/k groups, d_k = d_v = 128, chunk 64.  Prints one JSON line.
+
+The roofline object is for gla_bwd, the dominant call of the step: its
+algorithmic work (FLOPs, or bytes for the bf16 workloads) divided by its mean
+duration, timed with HIP events on the stream the library launches on.  The
+cpu_baseline object times the fp64 CPU oracle on a bounded sample of the same
+workload (one batch row).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"hbm": 8000.0,            # GB/s
+        "mfma_f32": 157.3,        # TFLOP/s, dense fp32 matrix cores
+        "mfma_bf16": 2500.0}      # TFLOP/s, dense bf16 matrix cores
+
+
+def algorithmic(case):
+    """Algorithmic work of one fwd and one bwd (bytes the method must move,
+    FLOPs with the causal half of the chunk products), per the counting used
+    for the rooflines: inputs and outputs at their storage dtype, fp32 states."""
+    B, T, H, Hqk, dk, dv, Cc = case.B, case.T, case.H, case.H_qk, case.d_k, case.d_v, case.chunk
+    es = 2 if case.dtype.__repr__().endswith("bfloat16") else 4
+    gw = dk if case.gate == "vector" else 1
+    qk = B * T * Hqk * dk * es
+    vv = B * T * H * dv * es
+    gg = B * T * H * gw * es
+    st = B * H * dk * dv * 4
+    seg = B * T * 4 if case.segment_ids is not None else 0
+    h0 = st if case.h0 is not None else 0
+    dhT = st if case.dhT is not None else 0
+    fwd_bytes = 2 * qk + vv + gg + h0 + seg + vv + st          # read q k v g (h0, seg); write o, hT
+    bwd_bytes = (2 * qk + vv + gg + vv + h0 + dhT + seg         # read q k v g dO (h0 dhT seg)
+                 + 2 * qk + vv + gg + (st if case.h0 is not None else 0))  # write dq dk dv dg (dh0)
+    th = B * T * H
+    fwd_flops = th * (2 * Cc * dk + 2 * dk * dv + 2 * dk * dv)   # intra (causal half) + readout + update
+    bwd_flops = th * (4 * Cc * dk + 8 * dk * dv)
+    return dict(fwd_bytes=fwd_bytes, bwd_bytes=bwd_bytes, fwd_flops=fwd_flops, bwd_flops=bwd_flops)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ssm_recurrence_amd import binding as gb
+    from ssm_recurrence_amd.inputs import WORKLOADS, workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case_cpu = workload(args.workload)
+    case = case_cpu.to(dev)
+    prob = gb.problem_of(case.q, case.v, case.g, case.gate, case.chunk)
+    B, T, H, dk, dv = case.B, case.T, case.H, case.d_k, case.d_v
+    o = torch.empty((B, T, H, dv), dtype=case.dtype, device=dev)
+    hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    dq, dk_, dv_, dg = (torch.empty_like(case.q), torch.empty_like(case.k),
+                        torch.empty_like(case.v), torch.empty_like(case.g))
+    dh0 = torch.empty_like(case.h0) if case.h0 is not None else None
+    nf, nb = gb.workspace_size(prob, False), gb.workspace_size(prob, True)
+    wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = gb.ctypes.c_void_p(stream.cuda_stream)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        gb.fwd_into(prob, case.q, case.k, case.v, case.g, case.h0, case.segment_ids, o, hT, wsf,
+                    nf, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        gb.bwd_into(prob, case.q, case.k, case.v, case.g, case.h0, case.segment_ids, case.dO,
+                    case.dhT, dq, dk_, dv_, dg, dh0, wsb, nb, sp)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    fwd_us = 1000.0 * sum(fwd_ms) / len(fwd_ms)
+    bwd_us = 1000.0 * sum(bwd_ms) / len(bwd_ms)
+    tokens = B * T
+    value = tokens / (ms_per_step / 1000.0)
+
+    alg = algorithmic(case)
+    bf16 = case.dtype == torch.bfloat16
+    if bf16:
+        bound, peak, unit = "hbm", PEAK["hbm"], "GB/s"
+        achieved = alg["bwd_bytes"] / (bwd_us * 1e-6) / 1e9
+        step_ach = (alg["fwd_bytes"] + alg["bwd_bytes"]) / ((fwd_us + bwd_us) * 1e-6) / 1e9
+    else:
+        bound, peak, unit = "mfma", PEAK["mfma_f32"], "TFLOP/s"
+        achieved = alg["bwd_flops"] / (bwd_us * 1e-6) / 1e12
+        step_ach = (alg["fwd_flops"] + alg["bwd_flops"]) / ((fwd_us + bwd_us) * 1e-6) / 1e12
+    roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": "gla_bwd (all its kernels, one call)",
+            "step_frac": round(step_ach / peak, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        s = case_cpu
+        sl = slice(0, 1)  # one batch row, every head, the full sequence
+        seg = None if s.segment_ids is None else s.segment_ids[sl]
+        h0 = None if s.h0 is None else s.h0[sl]
+        dhT = None if s.dhT is None else s.dhT[sl]
+        c0 = time.perf_counter()
+        oracle.fwd(s.q[sl], s.k[sl], s.v[sl], s.g[sl], h0, seg, gate=s.gate, threads=threads)
+        oracle.bwd(s.q[sl], s.k[sl], s.v[sl], s.g[sl], s.dO[sl], h0, seg, dhT, gate=s.gate,
+                   threads=threads)
+        c1 = time.perf_counter()
+        cpu = {"value": round(T / (c1 - c0), 1), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": "batch row 0 of the workload (%d tokens x %d heads), fwd+bwd, %.1f s"
+                         % (T, H, c1 - c0)}
+
+    out = {
+        "metric": "fwd+bwd µs and tokens/s for chunked GLA/SSD at d=128, % of MFMA/HBM roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "us_fwd": round(fwd_us, 1), "us_bwd": round(bwd_us, 1),
+        "us_fwd_bwd": round(fwd_us + bwd_us, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32", "data": "synthetic (seeded)",
+        "config": {"workload": "%s: %s" % (args.workload, WORKLOADS[args.workload]),
+                   "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
+                   "chunk": case.chunk, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

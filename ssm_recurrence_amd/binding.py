@@ -185,3 +185,20 @@ class GLAFunction(torch.autograd.Function):
         dq, dk, dv, dg, dh0 = bwd(q, k, v, g, dO, h0, seg, dhT, gate=ctx.gate,
                                   want_dh0=h0 is not None)
         return dq, dk, dv, dg, dh0, None, None
+
+
+def fwd_into(prob, q, k, v, g, h0, seg, o, hT, ws, nws, stream=None):
+    """gla_fwd on preallocated buffers (no allocation); raises on a non-zero status."""
+    rc = load().gla_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(h0), _p(seg), _p(o),
+                        _p(hT), _p(ws), nws, stream if stream is not None else _stream())
+    if rc:
+        raise GlaError(rc, "gla_fwd")
+
+
+def bwd_into(prob, q, k, v, g, h0, seg, dO, dhT, dq, dk, dv, dg, dh0, ws, nws, stream=None):
+    """gla_bwd on preallocated buffers (no allocation); raises on a non-zero status."""
+    rc = load().gla_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(h0), _p(seg), _p(dO),
+                        _p(dhT), _p(dq), _p(dk), _p(dv), _p(dg), _p(dh0), _p(ws), nws,
+                        stream if stream is not None else _stream())
+    if rc:
+        raise GlaError(rc, "gla_bwd")

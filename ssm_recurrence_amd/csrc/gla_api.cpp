@@ -103,9 +103,15 @@ int copy_state(float* dst, const float* src, int64_t n, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 
+// Columns of the state per forward workgroup: the widest slice that still
+// gives at least 256 workgroups (one per compute unit), else 16.
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
-    return gla::launch_pass<T, VEC, DK, DV, gla::MODE_OUT>(a, st);
+    const int64_t bh = a.B * a.H;
+    if constexpr (sizeof(T) == 2)  // fp32 tiles with 64 columns exceed the LDS
+        if (DV >= 64 && bh * (DV / 64) >= 256) return gla::launch_fwd<T, VEC, DK, DV, 64>(a, st);
+    if (bh * (DV / 32) >= 256) return gla::launch_fwd<T, VEC, DK, DV, 32>(a, st);
+    return gla::launch_fwd<T, VEC, DK, DV, 16>(a, st);
 }
 
 template <typename T, bool VEC, int DK, int DV>

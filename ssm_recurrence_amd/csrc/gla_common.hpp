@@ -30,6 +30,23 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // float -> bf16, round to nearest even (the compiler's conversion does RNE)
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// Four consecutive elements (8 bytes of bf16, 16 of fp32) as one LDS access.
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> {
+    bf16x4 v;
+    static __device__ __forceinline__ Vec4 load(const bf16* p) { Vec4 r; r.v = *reinterpret_cast<const bf16x4*>(p); return r; }
+    __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<bf16x4*>(p) = v; }
+    __device__ __forceinline__ float get(int e) const { return (float)v[e]; }
+    __device__ __forceinline__ void set(int e, float x) { v[e] = (bf16)x; }
+};
+template <> struct Vec4<float> {
+    f32x4 v;
+    static __device__ __forceinline__ Vec4 load(const float* p) { Vec4 r; r.v = *reinterpret_cast<const f32x4*>(p); return r; }
+    __device__ __forceinline__ void store(float* p) const { *reinterpret_cast<f32x4*>(p) = v; }
+    __device__ __forceinline__ float get(int e) const { return v[e]; }
+    __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
+};
+
 // ------------------------------------------------------------------ matrix-core traits
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
@@ -120,6 +137,42 @@ __device__ __forceinline__ typename Mma<T>::frag frag_from_acc(const f32x4& lo, 
     } else {
         (void)sub;
         for (int e = 0; e < 4; ++e) { f[e] = (bf16)lo[e]; f[4 + e] = (bf16)hi[e]; }
+    }
+    return f;
+}
+
+// Operand fragment "lane i, k packed" from a natural row-major tile X[k][i]
+// (pitch P elements), i.e. a column read, without a transposed copy in LDS.
+// bf16 uses the gfx950 transposing LDS read ds_read_b64_tr_b16: within each
+// group of 16 lanes, lane i receives element e from source lane 4e + i/4,
+// position i%4 (checked on the hardware).  So source lane s of group j points
+// at row k(j, s/4) and columns i0 + 4*(s%4); two reads give 8 k values.
+// Natural k order: k(j, e) = k0 + 8j + e.  ctile order (matching a C-layout
+// accumulator used as the other operand): k0 + 4j + e and k0 + 16 + 4j + e.
+// fp32: one element, k = k0 + j (natural) or k0 + 4j + sub (ctile).
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i16_t lds_read_tr16(const bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
+}
+template <typename T, int P, bool CTILE>
+__device__ __forceinline__ typename Mma<T>::frag frag_col(const T* base, int i0, int k0, int sub = 0) {
+    const int l = lane_id();
+    const int j = l >> 4;
+    typename Mma<T>::frag f;
+    if constexpr (Mma<T>::KPL == 1) {
+        const int k = CTILE ? k0 + 4 * j + sub : k0 + j;
+        f = base[k * P + i0 + (l & 15)];
+    } else {
+        (void)sub;
+        const int s = l & 15;
+        const int col = i0 + 4 * (s & 3);
+        const int r0 = CTILE ? k0 + 4 * j + (s >> 2) : k0 + 8 * j + (s >> 2);
+        const int r1 = CTILE ? r0 + 16 : r0 + 4;
+        // whole-vector casts: extracting the lanes of the returned short vector
+        // one by one is mis-lowered by this compiler (it keeps element 0 only)
+        const bf16x4 a = __builtin_bit_cast(bf16x4, lds_read_tr16(base + r0 * P + col));
+        const bf16x4 b = __builtin_bit_cast(bf16x4, lds_read_tr16(base + r1 * P + col));
+        f = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
     return f;
 }

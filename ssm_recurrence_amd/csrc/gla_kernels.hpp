@@ -32,6 +32,9 @@ struct GradArgs {
 template <typename T, bool VEC, int DK, int DV, int MODE>
 hipError_t launch_pass(const PassArgs& a, hipStream_t st);
 
+template <typename T, bool VEC, int DK, int DV, int NV>
+hipError_t launch_fwd(const PassArgs& a, hipStream_t st);
+
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_grad(const GradArgs& a, hipStream_t st);
 
