@@ -45,26 +45,35 @@ int check_problem(const gla_problem* p) {
 }
 
 struct WsLayout {
-    size_t S = 0, dS = 0, dq = 0, dk = 0, total = 0;
+    size_t S = 0, dq = 0, dk = 0, xs = 0, bnd = 0, total = 0;
 };
 
+// Backward workspace: the state entering every chunk (and the final state) in
+// the input dtype; per-head fp32 dq, dk when heads share q/k; per-slice partial
+// gate-gradient sums for the scalar gate.
 WsLayout ws_layout(const gla_problem* p, int for_backward) {
     WsLayout L;
     if (!for_backward) return L;
     const int64_t nc = (p->T + 63) / 64;
-    const size_t st = (size_t)p->d_k * (size_t)p->d_v * sizeof(float);
+    const size_t es = p->dtype == GLA_BF16 ? 2 : 4;
+    const size_t st = (size_t)p->d_k * (size_t)p->d_v * es;
     const size_t bh = (size_t)(p->B * p->H);
     size_t off = 0;
     L.S = off;
     off += round_up(bh * (size_t)(nc + 1) * st);
-    L.dS = off;
-    off += round_up(bh * (size_t)nc * st);
     if (p->H_qk != p->H) {
         const size_t n = (size_t)(p->B * p->T * p->H * p->d_k) * sizeof(float);
         L.dq = off;
         off += round_up(n);
         L.dk = off;
         off += round_up(n);
+    }
+    if (p->gate == GLA_GATE_SCALAR) {
+        const size_t ns = (size_t)(p->d_k / 64);
+        L.xs = off;
+        off += round_up(bh * ns * (size_t)p->T * sizeof(float));
+        L.bnd = off;
+        off += round_up(bh * ns * (size_t)nc * sizeof(float));
     }
     L.total = off;
     return L;
@@ -115,17 +124,15 @@ hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
 }
 
 template <typename T, bool VEC, int DK, int DV>
-hipError_t run_bwd(const gla::PassArgs& pa, const gla::GradArgs& ga, hipStream_t st) {
-    hipError_t e = gla::launch_pass<T, VEC, DK, DV, gla::MODE_STATES>(pa, st);
+hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t st) {
+    hipError_t e = gla::launch_states<T, VEC, DK, DV>(pa, st);
     if (e != hipSuccess) return e;
-    e = gla::launch_pass<T, VEC, DK, DV, gla::MODE_DSTATE>(pa, st);
+    e = gla::launch_rev<T, VEC, DK, DV>(ra, st);
     if (e != hipSuccess) return e;
-    e = gla::launch_grad<T, VEC, DK, DV>(ga, st);
-    if (e != hipSuccess) return e;
-    if (ga.Hqk != ga.H) {
-        e = gla::launch_group_sum<T, DK>(ga.ws_dq, ga.dq, ga.B, ga.T, ga.H, ga.Hqk, st);
+    if (ra.Hqk != ra.H) {
+        e = gla::launch_group_sum<T, DK>(ra.ws_dq, ra.dq, ra.B, ra.T, ra.H, ra.Hqk, st);
         if (e != hipSuccess) return e;
-        e = gla::launch_group_sum<T, DK>(ga.ws_dk, ga.dk, ga.B, ga.T, ga.H, ga.Hqk, st);
+        e = gla::launch_group_sum<T, DK>(ra.ws_dk, ra.dk, ra.B, ra.T, ra.H, ra.Hqk, st);
     }
     return e;
 }
@@ -151,8 +158,8 @@ template <typename T, bool VEC, int DK, int DV> struct FwdF {
     static hipError_t run(const gla::PassArgs& a, hipStream_t st) { return run_fwd<T, VEC, DK, DV>(a, st); }
 };
 template <typename T, bool VEC, int DK, int DV> struct BwdF {
-    static hipError_t run(const gla::PassArgs& pa, const gla::GradArgs& ga, hipStream_t st) {
-        return run_bwd<T, VEC, DK, DV>(pa, ga, st);
+    static hipError_t run(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t st) {
+        return run_bwd<T, VEC, DK, DV>(pa, ra, st);
     }
 };
 
@@ -211,22 +218,25 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     char* w = (char*)ws;
     gla::PassArgs pa;
     memset(&pa, 0, sizeof pa);
-    pa.q = q; pa.k = k; pa.v = v; pa.g = g; pa.dO = dO; pa.h0 = h0; pa.dhT = dhT;
-    pa.seg = segment_ids; pa.dh0 = dh0;
+    pa.k = k; pa.v = v; pa.g = g; pa.h0 = h0; pa.seg = segment_ids;
     pa.ws_S = (float*)(w + L.S);
-    pa.ws_dS = (float*)(w + L.dS);
     pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.Hqk = p->H_qk;
-    gla::GradArgs ga;
-    memset(&ga, 0, sizeof ga);
-    ga.q = q; ga.k = k; ga.v = v; ga.g = g; ga.dO = dO; ga.seg = segment_ids;
-    ga.ws_S = pa.ws_S; ga.ws_dS = pa.ws_dS;
-    ga.dq = dq; ga.dk = dk; ga.dv = dv; ga.dg = dg;
+    gla::RevArgs ra;
+    memset(&ra, 0, sizeof ra);
+    ra.q = q; ra.k = k; ra.v = v; ra.g = g; ra.dO = dO; ra.seg = segment_ids;
+    ra.ws_S = w + L.S;
+    ra.dhT = dhT; ra.dh0 = dh0;
+    ra.dq = dq; ra.dk = dk; ra.dv = dv; ra.dg = dg;
     if (p->H_qk != p->H) {
-        ga.ws_dq = (float*)(w + L.dq);
-        ga.ws_dk = (float*)(w + L.dk);
+        ra.ws_dq = (float*)(w + L.dq);
+        ra.ws_dk = (float*)(w + L.dk);
     }
-    ga.B = p->B; ga.T = p->T; ga.H = p->H; ga.Hqk = p->H_qk;
-    return dispatch<BwdF>(p, pa, ga, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+    if (p->gate == GLA_GATE_SCALAR) {
+        ra.ws_xs = (float*)(w + L.xs);
+        ra.ws_bnd = (float*)(w + L.bnd);
+    }
+    ra.B = p->B; ra.T = p->T; ra.H = p->H; ra.Hqk = p->H_qk;
+    return dispatch<BwdF>(p, pa, ra, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 
 const char* gla_status_str(int s) {

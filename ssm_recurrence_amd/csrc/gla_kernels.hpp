@@ -6,37 +6,37 @@
 
 namespace gla {
 
-enum { MODE_OUT = 0, MODE_STATES = 1, MODE_DSTATE = 2 };
-
 struct PassArgs {
     const void *q, *k, *v, *g, *dO;
     const float *h0, *dhT;
     const int32_t* seg;
     void* o;
     float *hT, *dh0;
-    float* ws_S;   // [B*H][NC+1][DK][DV]: state entering each chunk, then the final state
-    float* ws_dS;  // [B*H][NC][DK][DV]: gradient of the state at each chunk's end
+    float* ws_S;   // state pass output, [B*H][NC+1][DK][DV] in the input dtype
     int64_t B, T, H, Hqk;
 };
 
-struct GradArgs {
+
+struct RevArgs {
     const void *q, *k, *v, *g, *dO;
     const int32_t* seg;
-    const float* ws_S;
-    const float* ws_dS;
+    const void* ws_S;   // [B*H][NC+1][DK][DV] in the input dtype: state entering each chunk, then hT
+    const float* dhT;
     void *dq, *dk, *dv, *dg;
+    float* dh0;
     float *ws_dq, *ws_dk;  // per-head fp32 [B][T][H][DK] when heads share q/k
+    float *ws_xs, *ws_bnd; // scalar gate: per-slice partial sums [B*H][slices][T], [B*H][slices][NC]
     int64_t B, T, H, Hqk;
 };
 
-template <typename T, bool VEC, int DK, int DV, int MODE>
-hipError_t launch_pass(const PassArgs& a, hipStream_t st);
+template <typename T, bool VEC, int DK, int DV>
+hipError_t launch_states(const PassArgs& a, hipStream_t st);
+
+template <typename T, bool VEC, int DK, int DV>
+hipError_t launch_rev(const RevArgs& a, hipStream_t st);
 
 template <typename T, bool VEC, int DK, int DV, int NV>
 hipError_t launch_fwd(const PassArgs& a, hipStream_t st);
-
-template <typename T, bool VEC, int DK, int DV>
-hipError_t launch_grad(const GradArgs& a, hipStream_t st);
 
 template <typename T, int DK>
 hipError_t launch_group_sum(const float* src, void* dst, int64_t B, int64_t Tn, int64_t H,

@@ -8,6 +8,13 @@ namespace gla {
 
 typedef __attribute__((__vector_size__(16))) int i32x4;
 
+// Row pitch (elements) of [rows][d] tiles in LDS: rows stay 16-byte aligned
+// and consecutive rows shift by 16 bytes across the banks.
+template <typename T> struct Pitch16 {
+    static constexpr int pad = 16 / (int)sizeof(T);
+    static constexpr int of(int d) { return d + pad; }
+};
+
 template <typename T, int D>
 struct TileRegs {
     static constexpr int VE = 16 / (int)sizeof(T);   // elements per 16-byte vector
@@ -90,6 +97,37 @@ __device__ __forceinline__ int64_t xcd_logical_block(int64_t nblocks) {
     const int64_t x = blockIdx.x;
     if (nblocks % 8 != 0) return x;
     return (x % 8) * (nblocks / 8) + x / 8;
+}
+
+// Chunk-local inclusive prefix of the per-channel log gates as one product
+// with a triangular matrix of ones (FLAT page, Pallas Kernels > Gated Linear
+// Attention: a prefix sum is a linear map, so the matrix unit can compute it):
+// beta^T = G^T L^T with L[r][s] = [s <= r]; G is the natural [row][channel]
+// tile (pitch PG), read column-wise.  Wave w computes channel tiles CPW*w .. CPW*w + CPW-1 for all four
+// row tiles; the result is in C layout with lane (r = 16*rt + l%16) holding
+// channels 16*ct + 4*(l/16) + e.
+template <typename T, int CPW, int PG>
+__device__ __forceinline__ void gate_prefix_mfma(const T* sG, f32x4 (&beta)[CPW][4]) {
+    using M = Mma<T>;
+    const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) {
+        const int ct = CPW * w + cc;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 acc = zero4();
+            const int r = 16 * rt + i16;
+            constexpr int KS = M::KSTEP;
+#pragma unroll
+            for (int k0 = 0; k0 < ((16 * (rt + 1) + KS - 1) / KS) * KS; k0 += KS) {
+                typename M::frag lt;
+#pragma unroll
+                for (int e = 0; e < M::KPL; ++e) M::set(lt, e, k0 + j4 * M::KPL + e <= r ? 1.f : 0.f);
+                acc = M::mma(frag_col<T, PG, false>(sG, 16 * ct, k0), lt, acc);
+            }
+            beta[cc][rt] = acc;
+        }
+    }
 }
 
 }  // namespace gla
