@@ -42,15 +42,18 @@ struct RevCfg {
     static constexpr int PV = Pitch16<T>::of(DV);
     static constexpr int PE = 68;                 // fp32 [64][64] tiles
     // QK role
+    // bf16: raw q, k copies (vector gate) and dq, dk, dg output tiles staged for row stores
+    static constexpr bool STAGE_OUT = sizeof(T) == 2;
     static constexpr int QK_BYTES_NOV = (2 + (VEC ? 1 : 0)) * C * PB * (int)sizeof(T) +  // q k g slices
                                         2 * C * PV * (int)sizeof(T) +                   // dO, S0
                                         C * PB * (int)sizeof(T) +                      // dA
-                                        C * PE * 4;                                    // E / x
+                                        C * PE * 4 +                                   // E / x
+                                        (STAGE_OUT ? (VEC ? 5 : 2) : 0) * C * PB * (int)sizeof(T);
     static constexpr bool V_LDS = QK_BYTES_NOV + C * PV * (int)sizeof(T) <= 150 * 1024;
     static constexpr int QK_BYTES = QK_BYTES_NOV + (V_LDS ? C * PV * (int)sizeof(T) : 0);
     // V role
     static constexpr int V_BYTES = (2 + (VEC ? 1 : 0)) * C * PK * (int)sizeof(T) +  // q k g
-                                   2 * C * PB * (int)sizeof(T);                     // dO slice, A
+                                   (STAGE_OUT ? 3 : 2) * C * PB * (int)sizeof(T);   // dO slice, A, dv
     static constexpr int BYTES = QK_BYTES > V_BYTES ? QK_BYTES : V_BYTES;
 };
 
@@ -167,10 +170,16 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
     T* sS = sdO + C * PV;                         // state entering the chunk, [c][n]
     T* sdA = sS + C * PV;                         // [r][s]
     float* sE = reinterpret_cast<float*>(sdA + C * PB);  // exp(beta - m) [r][c]; later x
-    T* sV = reinterpret_cast<T*>(sE + C * PE);    // when it fits
+    T* sOq = reinterpret_cast<T*>(sE + C * PE);   // staged dq, dk (, dg) tiles [r][c]
+    T* sOk = sOq + (Cfg::STAGE_OUT ? C * PB : 0);
+    T* sOg = sOk + (Cfg::STAGE_OUT ? C * PB : 0);
+    T* sQr = sOg + (Cfg::STAGE_OUT && VEC ? C * PB : 0);  // raw q, k (vector gate)
+    T* sKr = sQr + (Cfg::STAGE_OUT && VEC ? C * PB : 0);
+    T* sV = sKr + (Cfg::STAGE_OUT && VEC ? C * PB : 0);   // when it fits
     __shared__ RevChunk ck;
     __shared__ float sEm[64], sEGm[64], sDecay[64];
     __shared__ float sXs[4][C];
+    __shared__ float sBs[4];
 
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t G = a.H / a.Hqk, hq = h / G;
@@ -245,6 +254,10 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
         pq.store_rows(sQ, PB);
         pk.store_rows(sK, PB);
         if constexpr (VEC) pg.store_rows(sG, PB);
+        if constexpr (Cfg::STAGE_OUT && VEC) {
+            pq.store_rows(sQr, PB);
+            pk.store_rows(sKr, PB);
+        }
         if constexpr (V_LDS) pv.store_rows(sV, PV);
         pdo.store_rows(sdO, PV);
         ps.store_rows(sS, PV);
@@ -319,9 +332,27 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
         }
         __syncthreads();
 
-        // ---- dq, dk for this wave's 16 channels, all 64 rows
+        // ---- dq, then dk, for this wave's 16 channels and all 64 rows; each is
+        // folded into x = q*dq - k*dk (fp32, raw inputs) and written out at once,
+        // so the two never occupy registers together
         const float em = VEC ? sEm[cl] : 1.f, egm = VEC ? sEGm[cl] : 1.f;
-        f32x4 dq[4], dk[4];
+        const T* sQraw = (Cfg::STAGE_OUT && VEC) ? sQr : sQ;
+        const T* sKraw = (Cfg::STAGE_OUT && VEC) ? sKr : sK;
+        const bool staged = Cfg::STAGE_OUT && G == 1;
+        auto raw_at = [&](const T* sraw, const T* gbase_qk, int r) -> float {
+            if (VEC && !Cfg::STAGE_OUT)  // fp32 vector gate: raw values from memory
+                return r < nvalid ? to_f32(gbase_qk[(t0 + r) * rs_qk + cl]) : 0.f;
+            return to_f32(sraw[r * PB + cl]);
+        };
+        auto put_grad = [&](T* stile, void* dst, float* wsd, int r, float val) {
+            if (staged) {
+                stile[r * PB + cl] = from_f32<T>(val);
+            } else if (r < nvalid) {
+                if (G == 1) ((T*)dst)[((b * T_ + t0 + r) * a.Hqk + hq) * DK + c] = from_f32<T>(val);
+                else wsd[((b * T_ + t0 + r) * a.H + h) * DK + c] = val;
+            }
+        };
+        float x[4][4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             f32x4 a1 = zero4(), a2 = zero4();
@@ -335,12 +366,11 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rt + 4 * j4 + e;
-                if constexpr (VEC) {
-                    const float E = sE[r * PE + cl];
-                    dq[rt][e] = E * (a1[e] + ck.fq[r] * em * a2[e]);
-                } else {
-                    dq[rt][e] = a1[e] + ck.fq[r] * a2[e];
-                }
+                float dq;
+                if constexpr (VEC) dq = sE[r * PE + cl] * (a1[e] + ck.fq[r] * em * a2[e]);
+                else dq = a1[e] + ck.fq[r] * a2[e];
+                x[rt][e] = raw_at(sQraw, qbase, r) * dq;
+                put_grad(sOq, a.dq, a.ws_dq, r, dq);
             }
         }
 #pragma unroll
@@ -372,48 +402,45 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = 16 * st + 4 * j4 + e;
-                if constexpr (VEC) {
-                    const float Ei = __builtin_amdgcn_rcpf(sE[s * PE + cl]);
-                    dk[st][e] = Ei * (a1[e] + ck.fu[s] * egm * a2[e]);
-                } else {
-                    dk[st][e] = a1[e] + ck.fu[s] * a2[e];
-                }
+                float dk;
+                if constexpr (VEC) dk = __builtin_amdgcn_rcpf(sE[s * PE + cl]) * (a1[e] + ck.fu[s] * egm * a2[e]);
+                else dk = a1[e] + ck.fu[s] * a2[e];
+                x[st][e] -= raw_at(sKraw, kbase, s) * dk;
+                put_grad(sOk, a.dk, a.ws_dk, s, dk);
             }
         }
 
-        // ---- write dq, dk; x = q*dq - k*dk (raw inputs, fp32)
-        const T* qraw = qbase + t0 * rs_qk;
-        const T* kraw = kbase + t0 * rs_qk;
-        float x[4][4];
+        // ---- dS^T <- decay dS^T + dO^T QR  (rows n, this wave's channels), in place
+        {
+            const float dec = VEC ? sDecay[cl] : ck.decay;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+            for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * j4 + e;
-                x[rt][e] = 0.f;
-                if (r < nvalid) {
-                    const float qv = to_f32(qraw[(int64_t)r * rs_qk + cl]);
-                    const float kv = to_f32(kraw[(int64_t)r * rs_qk + cl]);
-                    x[rt][e] = qv * dq[rt][e] - kv * dk[rt][e];
-                    if (G == 1) {
-                        const int64_t o = ((b * T_ + t0 + r) * a.Hqk + hq) * DK + c;
-                        ((T*)a.dq)[o] = from_f32<T>(dq[rt][e]);
-                        ((T*)a.dk)[o] = from_f32<T>(dk[rt][e]);
-                    } else {
-                        const int64_t o = ((b * T_ + t0 + r) * a.H + h) * DK + c;
-                        a.ws_dq[o] = dq[rt][e];
-                        a.ws_dk[o] = dk[rt][e];
-                    }
-                }
+                for (int e = 0; e < 4; ++e) dSt[nt][e] *= dec;
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += KS) {
+                typename M::frag qr = frag_col<T, PB, false>(sQ, 16 * w, k0);
+                frag_scale_k<T>(qr, k0, [&](int r) { return ck.fq[r] * em; });
+#pragma unroll
+                for (int nt = 0; nt < NNT; ++nt)
+                    dSt[nt] = M::mma(frag_col<T, PV, false>(sdO, 16 * nt, k0), qr, dSt[nt]);
             }
+        }
+        // boundary term of the previous chunk: rowsum(S0 * dS) with dS the new gradient
+        const float bnd_chunk = bnd;
+        bnd = rowsum_with([&](int n) { return to_f32(sS[cl * PV + n]); });
 
         // ---- gate gradient
         if constexpr (VEC) {
             T* dgo = (T*)a.dg;
-            const bool plain = first_reset == C && ck.doc[0] == 0;  // no reset in this chunk
-            if (plain) {
-                // suffix sums: in-lane over e, across the 4 lane groups, across row tiles
-                float carry = bnd;
+            auto put_dg = [&](int r, float val) {
+                if constexpr (Cfg::STAGE_OUT) sOg[r * PB + cl] = from_f32<T>(val);
+                else if (r < nvalid) dgo[((b * T_ + t0 + r) * a.H + h) * DK + c] = from_f32<T>(val);
+            };
+            if (first_reset == C) {
+                // no reset in this chunk: suffix sums in-lane over e, across the four
+                // lane groups of a channel, and across row tiles
+                float carry = bnd_chunk;
 #pragma unroll
                 for (int rt = 3; rt >= 0; --rt) {
                     float suf[4];
@@ -428,11 +455,7 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) above += jj > j4 ? tot[jj] : 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * rt + 4 * j4 + e;
-                        if (r < nvalid)
-                            dgo[((b * T_ + t0 + r) * a.H + h) * DK + c] = from_f32<T>(above + suf[e]);
-                    }
+                    for (int e = 0; e < 4; ++e) put_dg(16 * rt + 4 * j4 + e, above + suf[e]);
                     carry += tot[0] + tot[1] + tot[2] + tot[3];
                 }
             } else {
@@ -446,18 +469,18 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 if (j4 == 0) {
-                    float run = bnd;
-                    for (int r = nvalid - 1; r >= 0; --r) {
+                    float run = bnd_chunk;
+                    for (int r = C - 1; r >= 0; --r) {
+                        if (r >= nvalid) { put_dg(r, 0.f); continue; }
                         if (r < nvalid - 1 && ck.doc[r + 1] != ck.doc[r]) run = 0.f;
                         run += sX[r * PE + cl];
                         const bool reset = r > 0 ? ck.doc[r] != ck.doc[r - 1] : ck.doc[0] != 0;
-                        dgo[((b * T_ + t0 + r) * a.H + h) * DK + c] = from_f32<T>(reset ? 0.f : run);
+                        put_dg(r, reset ? 0.f : run);
                     }
                 }
             }
         } else {
             // scalar gate: partial sums over this workgroup's channels; a finisher adds slices
-            float xs[4][4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -465,19 +488,36 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
                     float y = x[rt][e];
 #pragma unroll
                     for (int d = 1; d < 16; d <<= 1) y += __shfl_xor(y, d, 64);
-                    xs[rt][e] = y;
+                    if (i16 == 0) sXs[w][16 * rt + 4 * j4 + e] = y;
                 }
-            float bs = bnd;
+            float bs = bnd_chunk;
 #pragma unroll
             for (int d = 1; d < 16; d <<= 1) bs += __shfl_xor(bs, d, 64);
-            if (i16 == 0)
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sXs[w][16 * rt + 4 * j4 + e] = xs[rt][e];
-            __shared__ float sBs[4];
             if (l == 0) sBs[w] = bs;
-            __syncthreads();
+        }
+        __syncthreads();
+
+        // ---- row stores of the staged tiles; scalar-gate partial sums
+        if (staged) {
+            constexpr int VPR = 64 * (int)sizeof(T) / 16;  // 16-byte vectors per 64-channel row
+            for (int idx = threadIdx.x; idx < C * VPR; idx += NT) {
+                const int r = idx / VPR, cv = (idx % VPR) * (16 / (int)sizeof(T));
+                if (r >= nvalid) continue;
+                const int64_t o = ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cs0 + cv;
+                *reinterpret_cast<i32x4*>((T*)a.dq + o) = *reinterpret_cast<const i32x4*>(sOq + r * PB + cv);
+                *reinterpret_cast<i32x4*>((T*)a.dk + o) = *reinterpret_cast<const i32x4*>(sOk + r * PB + cv);
+            }
+        }
+        if constexpr (VEC && Cfg::STAGE_OUT) {
+            constexpr int VPR = 64 * (int)sizeof(T) / 16;
+            for (int idx = threadIdx.x; idx < C * VPR; idx += NT) {
+                const int r = idx / VPR, cv = (idx % VPR) * (16 / (int)sizeof(T));
+                if (r >= nvalid) continue;
+                const int64_t o = ((b * T_ + t0 + r) * a.H + h) * DK + cs0 + cv;
+                *reinterpret_cast<i32x4*>((T*)a.dg + o) = *reinterpret_cast<const i32x4*>(sOg + r * PB + cv);
+            }
+        }
+        if constexpr (!VEC) {
             if (w == 0) {
                 const int r = l;
                 const float tot = sXs[0][r] + sXs[1][r] + sXs[2][r] + sXs[3][r];
@@ -486,29 +526,6 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
                     a.ws_bnd[(bh * Cfg::NQK + slice) * NC + ci] = sBs[0] + sBs[1] + sBs[2] + sBs[3];
             }
         }
-
-        // ---- dS^T <- decay dS^T + dO^T QR  (rows n, this wave's channels)
-        {
-            const float dec = VEC ? sDecay[cl] : ck.decay;
-            f32x4 U[NNT];
-#pragma unroll
-            for (int nt = 0; nt < NNT; ++nt) U[nt] = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < C; k0 += KS) {
-                typename M::frag qr = frag_col<T, PB, false>(sQ, 16 * w, k0);
-                frag_scale_k<T>(qr, k0, [&](int r) { return ck.fq[r] * em; });
-#pragma unroll
-                for (int nt = 0; nt < NNT; ++nt)
-                    U[nt] = M::mma(frag_col<T, PV, false>(sdO, 16 * nt, k0), qr, U[nt]);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dSt[nt][e] = dec * dSt[nt][e] + U[nt][e];
-        }
-        // boundary term of the previous chunk: rowsum(S0 * dS) with dS the new gradient
-        bnd = rowsum_with([&](int n) { return to_f32(sS[cl * PV + n]); });
-        __syncthreads();
     }
 }
 
@@ -527,6 +544,7 @@ __device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
     T* sG = sK + C * PK;
     T* sdO = sG + (VEC ? C * PK : 0);             // [r][64 columns of the slice]
     T* sA = sdO + C * PB;                          // [r][s]
+    T* sOv = sA + C * PB;                          // staged dv tile [s][column] (bf16)
     __shared__ RevChunk ck;
     __shared__ float sEm[DK], sEGm[DK], sDecay[DK];
 
@@ -676,17 +694,19 @@ __device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = 16 * st + 4 * j4 + e;
-                    if (s < nvalid)
-                        dvo[((b * T_ + t0 + s) * a.H + h) * DV + n] = from_f32<T>(a1[e] + ck.fu[s] * a2[e]);
+                    const float val = a1[e] + ck.fu[s] * a2[e];
+                    if constexpr (Cfg::STAGE_OUT) sOv[s * PB + 16 * w + i16] = from_f32<T>(val);
+                    else if (s < nvalid) dvo[((b * T_ + t0 + s) * a.H + h) * DV + n] = from_f32<T>(val);
                 }
             }
         }
 
-        // ---- dS <- decay dS + QR^T dO  (rows c, this wave's columns)
+        // ---- dS <- decay dS + QR^T dO  (rows c, this wave's columns), in place
         {
-            f32x4 U[NCT];
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) U[ct] = zero4();
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dS[ct][e] *= VEC ? sDecay[16 * ct + 4 * j4 + e] : ck.decay;
 #pragma unroll
             for (int k0 = 0; k0 < C; k0 += KS) {
                 const typename M::frag dob = frag_col<T, PB, false>(sdO, 16 * w, k0);
@@ -695,19 +715,20 @@ __device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
                     typename M::frag qr = frag_col<T, PK, false>(sQ, 16 * ct, k0);
                     const float emc = VEC ? sEm[16 * ct + i16] : 1.f;
                     frag_scale_k<T>(qr, k0, [&](int r) { return ck.fq[r] * emc; });
-                    U[ct] = M::mma(qr, dob, U[ct]);
+                    dS[ct] = M::mma(qr, dob, dS[ct]);
                 }
             }
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int cc = 16 * ct + 4 * j4 + e;
-                    const float dec = VEC ? sDecay[cc] : ck.decay;
-                    dS[ct][e] = dec * dS[ct][e] + U[ct][e];
-                }
         }
         __syncthreads();
+        if constexpr (Cfg::STAGE_OUT) {
+            constexpr int VPR = 64 * (int)sizeof(T) / 16;
+            for (int idx = threadIdx.x; idx < C * VPR; idx += NT) {
+                const int r = idx / VPR, cv = (idx % VPR) * (16 / (int)sizeof(T));
+                if (r >= nvalid) continue;
+                const int64_t o = ((b * T_ + t0 + r) * a.H + h) * DV + n0s + cv;
+                *reinterpret_cast<i32x4*>((T*)a.dv + o) = *reinterpret_cast<const i32x4*>(sOv + r * PB + cv);
+            }
+        }
     }
     if (a.dh0) {
 #pragma unroll

@@ -132,10 +132,12 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
             __syncthreads();
         }
 
-        // S^T[n][c] <- decay_c S^T[n][c] + sum_s v[s][n] KU[s][c]
-        f32x4 U[NNT];
+        // S^T[n][c] <- decay_c S^T[n][c] + sum_s v[s][n] KU[s][c], in place
+        const float dec = VEC ? sDecay[16 * w + i16] : sDecay[0];
 #pragma unroll
-        for (int nt = 0; nt < NNT; ++nt) U[nt] = zero4();
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) St[nt][e] *= dec;
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += M::KSTEP) {
             typename M::frag ku = frag_col<T, PB, false>(sK, 16 * w, k0);
@@ -150,13 +152,8 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
             }
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt)
-                U[nt] = M::mma(frag_col<T, PB, false>(sV, 16 * nt, k0), ku, U[nt]);
+                St[nt] = M::mma(frag_col<T, PB, false>(sV, 16 * nt, k0), ku, St[nt]);
         }
-        const float dec = VEC ? sDecay[16 * w + i16] : sDecay[0];
-#pragma unroll
-        for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) St[nt][e] = dec * St[nt][e] + U[nt][e];
         __syncthreads();
     }
     store_state(NC);
