@@ -24,6 +24,38 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PROFILE = {"c2": "gla_kernels_ssd_fp32_B4_T8192_H8_Hqk2_d128.md",
+           "c3": "gla_kernels_gla_bf16_B4_T4096_H16_d128.md"}
+
+
+def source_hash():
+    """sha256 (first 16 hex) of the HIP sources, as recorded in profile summaries."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "ssm_recurrence_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per gla_bwd call from the committed rocprofv3 counter summary,
+    or None when there is none or the kernels changed since it was taken."""
+    name = PROFILE.get(workload)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_gla_bwd", "source_hash"):
+            k, v = line.split(":", 1)
+            vals[k] = v.strip()
+    if vals.get("source_hash") != source_hash() or "traffic_bytes_per_gla_bwd" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_gla_bwd"])
+
+
 PEAK = {"hbm": 8000.0,            # GB/s
         "mfma_f32": 157.3,        # TFLOP/s, dense fp32 matrix cores
         "mfma_bf16": 2500.0}      # TFLOP/s, dense bf16 matrix cores
@@ -129,8 +161,12 @@ def main():
         bound, peak, unit = "mfma", PEAK["mfma_f32"], "TFLOP/s"
         achieved = alg["bwd_flops"] / (bwd_us * 1e-6) / 1e12
         step_ach = (alg["fwd_flops"] + alg["bwd_flops"]) / ((fwd_us + bwd_us) * 1e-6) / 1e12
+    traffic = measured_traffic(args.workload)
     roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": None,
+            "frac": round(achieved / peak, 4),
+            "traffic": None if traffic is None else round(traffic / 1e6, 1),
+            "traffic_unit": "MB per gla_bwd call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes": round(alg["bwd_bytes"] / 1e6, 1),
             "kernel": "gla_bwd (all its kernels, one call)",
             "step_frac": round(step_ach / peak, 4)}
 
