@@ -47,7 +47,7 @@ struct RevCfg {
     static constexpr int QK_BYTES_NOV = (2 + (VEC ? 1 : 0)) * C * PB * (int)sizeof(T) +  // q k g slices
                                         2 * C * PV * (int)sizeof(T) +                   // dO, S0
                                         C * PB * (int)sizeof(T) +                      // dA
-                                        C * PE * 4 +                                   // E / x
+                                        (VEC ? C * PE * 4 : 0) +                       // E / x (vector gate)
                                         (STAGE_OUT ? (VEC ? 5 : 2) : 0) * C * PB * (int)sizeof(T);
     static constexpr bool V_LDS = QK_BYTES_NOV + C * PV * (int)sizeof(T) <= 150 * 1024;
     static constexpr int QK_BYTES = QK_BYTES_NOV + (V_LDS ? C * PV * (int)sizeof(T) : 0);
@@ -170,7 +170,7 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
     T* sS = sdO + C * PV;                         // state entering the chunk, [c][n]
     T* sdA = sS + C * PV;                         // [r][s]
     float* sE = reinterpret_cast<float*>(sdA + C * PB);  // exp(beta - m) [r][c]; later x
-    T* sOq = reinterpret_cast<T*>(sE + C * PE);   // staged dq, dk (, dg) tiles [r][c]
+    T* sOq = reinterpret_cast<T*>(sE + (VEC ? C * PE : 0));  // staged dq, dk (, dg) tiles [r][c]
     T* sOk = sOq + (Cfg::STAGE_OUT ? C * PB : 0);
     T* sOg = sOk + (Cfg::STAGE_OUT ? C * PB : 0);
     T* sQr = sOg + (Cfg::STAGE_OUT && VEC ? C * PB : 0);  // raw q, k (vector gate)
