@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", type=int, default=0,
+                    help="sequence pieces per (b, h); 0 = the library's own choice")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -108,7 +110,7 @@ def main():
     torch.cuda.set_device(dev)
     case_cpu = workload(args.workload)
     case = case_cpu.to(dev)
-    prob = gb.problem_of(case.q, case.v, case.g, case.gate, case.chunk)
+    prob = gb.problem_of(case.q, case.v, case.g, case.gate, case.chunk, args.split)
     B, T, H, dk, dv = case.B, case.T, case.H, case.d_k, case.d_v
     o = torch.empty((B, T, H, dv), dtype=case.dtype, device=dev)
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
@@ -199,7 +201,7 @@ def main():
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic (seeded)",
         "config": {"workload": "%s: %s" % (args.workload, WORKLOADS[args.workload]),
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
-                   "chunk": case.chunk, "parallelism": "single GPU"},
+                   "chunk": case.chunk, "split": args.split, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

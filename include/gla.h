@@ -62,7 +62,7 @@
  * Errors: every argument is checked on the host before anything is launched;
  * a failed check returns a negative gla_status and enqueues nothing.  Sizes:
  * B >= 1, T >= 0, H >= 1, 1 <= H_qk <= H with H % H_qk == 0, d_k and d_v in
- * {64, 128}, chunk == 64.  A launch failure returns GLA_E_LAUNCH.  There is no
+ * {64, 128}, chunk == 64, split >= 0.  A launch failure returns GLA_E_LAUNCH.  There is no
  * fallback path: a shape the kernels do not cover is an error.
  */
 #ifndef GLA_H
@@ -96,8 +96,24 @@ typedef struct {
     int32_t chunk;  /* tokens per chunk; 64 */
     int32_t gate;   /* gla_gate */
     int32_t dtype;  /* gla_dtype */
-    int32_t reserved; /* must be 0 */
+    int32_t split;  /* sequence pieces per (b, h): 0 = chosen from the sizes; >= 1 forces
+                       that many (fewer if the row has fewer chunks); see below */
 } gla_problem;
+
+/* Sequence split.  The time axis of every (b, h) can be cut into pieces of
+ * whole chunks that run in parallel: a piece maps the state entering it to the
+ * state leaving it by S -> D S + L (D diagonal, the product of the gates over
+ * the piece, 0 once a document starts inside it; L the state the piece builds
+ * from zero), and these maps compose exactly, so a short pass computes (L, D)
+ * per piece, a P-step combine gives each piece its entry state (the state
+ * gradient at its exit, in the backward) and the main kernels then run the
+ * pieces side by side.  The JLA page ("JLA: JAX Linear Attention", the case
+ * of long single sequences among those where it is slower) contrasts such an
+ * exact split with starting each piece early from a zero state, which only
+ * approximates; the chunkwise state passing on the FLAT page (Linear Attention
+ * > Forward Recurrence) is the same identity between chunks.  Results equal
+ * the unsplit ones up to float32 rounding order.  With split == 0 the library splits only when B * H is too
+ * small to occupy the device.  The workspace depends on the split. */
 
 /* Bytes of device workspace gla_fwd (for_backward == 0) or gla_bwd
  * (for_backward != 0) needs for this problem.  Writes it to *bytes and returns

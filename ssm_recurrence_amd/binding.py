@@ -27,7 +27,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("H_qk", ctypes.c_int64), ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64),
                 ("chunk", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("split", ctypes.c_int32)]
 
 
 class GlaError(RuntimeError):
@@ -73,10 +73,11 @@ def header_functions():
     return sorted(set(re.findall(r"\b(gla_[a-z_0-9]+)\s*\(", txt)))
 
 
-def make_problem(B, T, H, H_qk, d_k, d_v, gate="scalar", dtype=torch.bfloat16, chunk=64):
+def make_problem(B, T, H, H_qk, d_k, d_v, gate="scalar", dtype=torch.bfloat16, chunk=64, split=0):
+    """gla_problem; split = sequence pieces per (b, h), 0 = chosen by the library."""
     return Problem(B, T, H, H_qk, d_k, d_v, chunk,
                    GLA_GATE_VECTOR if gate == "vector" else GLA_GATE_SCALAR,
-                   GLA_BF16 if dtype == torch.bfloat16 else GLA_F32, 0)
+                   GLA_BF16 if dtype == torch.bfloat16 else GLA_F32, split)
 
 
 def workspace_size(prob: Problem, backward: bool) -> int:
@@ -106,13 +107,13 @@ def _check(t, name, dtype=None):
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
-def problem_of(q, v, g, gate, chunk=64):
+def problem_of(q, v, g, gate, chunk=64, split=0):
     B, T, H_qk, d_k = q.shape
     H, d_v = v.shape[2], v.shape[3]
     want = (B, T, H, d_k) if gate == "vector" else (B, T, H)
     if tuple(g.shape) != want:
         raise ValueError("g has shape %s, expected %s" % (tuple(g.shape), want))
-    return make_problem(B, T, H, H_qk, d_k, d_v, gate, q.dtype, chunk)
+    return make_problem(B, T, H, H_qk, d_k, d_v, gate, q.dtype, chunk, split)
 
 
 def _workspace(prob, backward, device, ws):
@@ -125,13 +126,13 @@ def _workspace(prob, backward, device, ws):
 
 
 def fwd(q, k, v, g, h0=None, segment_ids=None, *, gate="scalar", chunk=64, want_hT=True,
-        out=None, ws=None):
+        out=None, ws=None, split=0):
     """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g")):
         _check(t, n, q.dtype)
     _check(h0, "h0", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = problem_of(q, v, g, gate, chunk)
+    prob = problem_of(q, v, g, gate, chunk, split)
     B, T, H, d_v, d_k = prob.B, prob.T, prob.H, prob.d_v, prob.d_k
     o = out if out is not None else torch.empty((B, T, H, d_v), dtype=q.dtype, device=q.device)
     hT = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device) if want_hT else None
@@ -144,14 +145,14 @@ def fwd(q, k, v, g, h0=None, segment_ids=None, *, gate="scalar", chunk=64, want_
 
 
 def bwd(q, k, v, g, dO, h0=None, segment_ids=None, dhT=None, *, gate="scalar", chunk=64,
-        want_dh0=True, ws=None):
+        want_dh0=True, ws=None, split=0):
     """dq, dk [B,T,H_qk,d_k], dv [B,T,H,d_v], dg (shape of g), dh0 fp32 (or None)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (dO, "dO")):
         _check(t, n, q.dtype)
     _check(h0, "h0", torch.float32)
     _check(dhT, "dhT", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = problem_of(q, v, g, gate, chunk)
+    prob = problem_of(q, v, g, gate, chunk, split)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

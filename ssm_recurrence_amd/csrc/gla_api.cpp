@@ -29,7 +29,7 @@ int check_problem(const gla_problem* p) {
     if (!p) return GLA_E_NULL;
     if (p->dtype != GLA_F32 && p->dtype != GLA_BF16) return GLA_E_DTYPE;
     if (p->gate != GLA_GATE_SCALAR && p->gate != GLA_GATE_VECTOR) return GLA_E_DTYPE;
-    if (p->reserved != 0) return GLA_E_SHAPE;
+    if (p->split < 0) return GLA_E_SHAPE;
     if (p->B < 1 || p->T < 0 || p->H < 1 || p->H_qk < 1 || p->H_qk > p->H) return GLA_E_SHAPE;
     if (p->H % p->H_qk != 0) return GLA_E_SHAPE;
     if (p->d_k < 1 || p->d_v < 1 || p->chunk < 1) return GLA_E_SHAPE;
@@ -40,25 +40,82 @@ int check_problem(const gla_problem* p) {
     if (!mul_ok(p->B, p->T, &bt) || !mul_ok(bt, p->H, &bth) || !mul_ok(bth, 128, &x)) return GLA_E_SHAPE;
     if (x > ((int64_t)1 << 40)) return GLA_E_SHAPE;
     const int64_t nc = (p->T + 63) / 64;
-    if (p->B * p->H * (nc > 0 ? nc : 1) > ((int64_t)1 << 31) - 1) return GLA_E_SHAPE;
+    // launch grids reach B * H * chunks * 8 workgroups (forward, 16-column slices, split)
+    if (p->B * p->H * (nc > 0 ? nc : 1) > (((int64_t)1 << 31) - 1) / 8) return GLA_E_SHAPE;
     return GLA_OK;
 }
 
-struct WsLayout {
-    size_t S = 0, dq = 0, dk = 0, xs = 0, bnd = 0, total = 0;
+// Sequence pieces per (b, h) and chunks per piece.  One workgroup per compute
+// unit (256) is the target: split only when B * H (times the workgroups per
+// head) falls short of it, and keep at least 8 chunks in a piece so that the
+// summary and combine stay small next to the main pass.
+constexpr int64_t kTargetWG = 256, kMinPieceChunks = 8;
+
+struct Split {
+    int64_t P = 1, PL = 0;
 };
 
-// Backward workspace: the state entering every chunk (and the final state) in
-// the input dtype; per-head fp32 dq, dk when heads share q/k; per-slice partial
-// gate-gradient sums for the scalar gate.
+Split plan_split(const gla_problem* p, int for_backward) {
+    Split s;
+    const int64_t nc = (p->T + 63) / 64;
+    s.PL = nc;
+    if (nc == 0) return s;
+    const int64_t bh = p->B * p->H;
+    int64_t P = 1;
+    if (p->split > 0) {
+        P = p->split;
+    } else {
+        int64_t per_head;  // workgroups per (b, h) without a split
+        if (for_backward) {
+            per_head = p->d_k / 64 + p->d_v / 64;
+        } else {
+            // the forward first narrows its column slices (down to 32 columns)
+            if (bh * (p->d_v / 32) >= kTargetWG) return s;
+            per_head = p->d_v / (p->dtype == GLA_BF16 ? 64 : 32);
+        }
+        P = (kTargetWG + bh * per_head - 1) / (bh * per_head);
+        const int64_t pmax = nc / kMinPieceChunks;
+        if (P > pmax) P = pmax;
+        if (P < 1) P = 1;
+    }
+    if (P > nc) P = nc;
+    s.PL = (nc + P - 1) / P;
+    s.P = (nc + s.PL - 1) / s.PL;  // no empty piece
+    return s;
+}
+
+struct WsLayout {
+    size_t S = 0, dq = 0, dk = 0, xs = 0, bnd = 0, pL = 0, pS = 0, pD = 0, total = 0;
+    Split sp;
+};
+
+// Workspace.  Both passes, when the sequence is split: per-piece summaries L
+// and decay products D, and the piece entry states (the backward reuses the two
+// state buffers for the reverse summaries and the state gradients at the piece
+// ends).  Backward only: the state entering every chunk (and the final state)
+// in the input dtype; per-head fp32 dq, dk when heads share q/k; per-slice
+// partial gate-gradient sums for the scalar gate.
 WsLayout ws_layout(const gla_problem* p, int for_backward) {
     WsLayout L;
-    if (!for_backward) return L;
+    L.sp = plan_split(p, for_backward);
     const int64_t nc = (p->T + 63) / 64;
     const size_t es = p->dtype == GLA_BF16 ? 2 : 4;
     const size_t st = (size_t)p->d_k * (size_t)p->d_v * es;
     const size_t bh = (size_t)(p->B * p->H);
     size_t off = 0;
+    if (L.sp.P > 1) {
+        const size_t np = bh * (size_t)L.sp.P;
+        L.pL = off;
+        off += round_up(np * (size_t)(p->d_k * p->d_v) * sizeof(float));
+        L.pS = off;
+        off += round_up(np * (size_t)(p->d_k * p->d_v) * sizeof(float));
+        L.pD = off;
+        off += round_up(np * (size_t)p->d_k * sizeof(float));
+    }
+    if (!for_backward) {
+        L.total = off;
+        return L;
+    }
     L.S = off;
     off += round_up(bh * (size_t)(nc + 1) * st);
     if (p->H_qk != p->H) {
@@ -112,21 +169,49 @@ int copy_state(float* dst, const float* src, int64_t n, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 
+// Piece entry states for a split forward: summaries, then the combine from h0.
+// pa.L_out, pa.D_out hold the summaries and pa.S_in receives the entry states.
+template <typename T, bool VEC, int DK, int DV>
+hipError_t run_split_fwd_states(const gla::PassArgs& pa, hipStream_t st) {
+    hipError_t e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_SUM_FWD, st);
+    if (e != hipSuccess) return e;
+    return gla::launch_piece_combine(pa.L_out, pa.D_out, pa.h0, (float*)pa.S_in, pa.B * pa.H, pa.P, DK, DV,
+                                     false, st);
+}
+
 // Columns of the state per forward workgroup: the widest slice that still
 // gives at least 256 workgroups (one per compute unit), else 16.
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
-    const int64_t bh = a.B * a.H;
+    if (a.P > 1) {
+        const hipError_t e = run_split_fwd_states<T, VEC, DK, DV>(a, st);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t wg = a.B * a.H * a.P;
     if constexpr (sizeof(T) == 2)  // fp32 tiles with 64 columns exceed the LDS
-        if (DV >= 64 && bh * (DV / 64) >= 256) return gla::launch_fwd<T, VEC, DK, DV, 64>(a, st);
-    if (bh * (DV / 32) >= 256) return gla::launch_fwd<T, VEC, DK, DV, 32>(a, st);
+        if (DV >= 64 && wg * (DV / 64) >= 256) return gla::launch_fwd<T, VEC, DK, DV, 64>(a, st);
+    if (wg * (DV / 32) >= 256) return gla::launch_fwd<T, VEC, DK, DV, 32>(a, st);
     return gla::launch_fwd<T, VEC, DK, DV, 16>(a, st);
 }
 
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t st) {
-    hipError_t e = gla::launch_states<T, VEC, DK, DV>(pa, st);
+    hipError_t e;
+    if (pa.P > 1) {
+        e = run_split_fwd_states<T, VEC, DK, DV>(pa, st);
+        if (e != hipSuccess) return e;
+    }
+    e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, st);
     if (e != hipSuccess) return e;
+    if (pa.P > 1) {
+        // reverse summaries into the L buffer, then the state gradients at the piece
+        // ends into the entry-state buffer (both free once the states are written)
+        e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_SUM_REV, st);
+        if (e != hipSuccess) return e;
+        e = gla::launch_piece_combine(pa.L_out, pa.D_out, pa.dhT, (float*)ra.dS_out, pa.B * pa.H, pa.P, DK, DV,
+                                      true, st);
+        if (e != hipSuccess) return e;
+    }
     e = gla::launch_rev<T, VEC, DK, DV>(ra, st);
     if (e != hipSuccess) return e;
     if (ra.Hqk != ra.H) {
@@ -195,6 +280,13 @@ int gla_fwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     memset(&a, 0, sizeof a);
     a.q = q; a.k = k; a.v = v; a.g = g; a.h0 = h0; a.seg = segment_ids; a.o = o; a.hT = hT;
     a.B = p->B; a.T = p->T; a.H = p->H; a.Hqk = p->H_qk;
+    a.P = L.sp.P; a.PL = L.sp.PL;
+    if (a.P > 1) {
+        char* w = (char*)ws;
+        a.L_out = (float*)(w + L.pL);
+        a.S_in = (const float*)(w + L.pS);
+        a.D_out = (float*)(w + L.pD);
+    }
     return dispatch<FwdF>(p, a, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 
@@ -218,9 +310,15 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     char* w = (char*)ws;
     gla::PassArgs pa;
     memset(&pa, 0, sizeof pa);
-    pa.k = k; pa.v = v; pa.g = g; pa.h0 = h0; pa.seg = segment_ids;
+    pa.q = q; pa.k = k; pa.v = v; pa.g = g; pa.dO = dO; pa.h0 = h0; pa.dhT = dhT; pa.seg = segment_ids;
     pa.ws_S = (float*)(w + L.S);
     pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.Hqk = p->H_qk;
+    pa.P = L.sp.P; pa.PL = L.sp.PL;
+    if (pa.P > 1) {
+        pa.L_out = (float*)(w + L.pL);
+        pa.S_in = (const float*)(w + L.pS);
+        pa.D_out = (float*)(w + L.pD);
+    }
     gla::RevArgs ra;
     memset(&ra, 0, sizeof ra);
     ra.q = q; ra.k = k; ra.v = v; ra.g = g; ra.dO = dO; ra.seg = segment_ids;
@@ -236,6 +334,8 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
         ra.ws_bnd = (float*)(w + L.bnd);
     }
     ra.B = p->B; ra.T = p->T; ra.H = p->H; ra.Hqk = p->H_qk;
+    ra.P = L.sp.P; ra.PL = L.sp.PL;
+    if (ra.P > 1) ra.dS_out = (const float*)(w + L.pS);
     return dispatch<BwdF>(p, pa, ra, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 

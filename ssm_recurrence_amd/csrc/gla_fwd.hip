@@ -60,15 +60,20 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
     __shared__ float sEGm[VEC ? DK : 1];
     __shared__ int sAnyReset;
 
-    const int64_t L = xcd_logical_block(a.B * a.H * NVS);
-    const int64_t bh = L / NVS;
+    // block -> (b, h, piece, slice); the slices of one piece are adjacent (one XCD)
+    const int64_t P = a.P;
+    const int64_t L = xcd_logical_block(a.B * a.H * NVS * P);
     const int ns = (int)(L % NVS);
+    const int64_t piece = (L / NVS) % P;
+    const int64_t bh = L / NVS / P;
     const int n0 = ns * NV;
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t G = a.H / a.Hqk, hq = h / G;
     const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
+    const int64_t cbeg = piece * a.PL;
+    const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
 
     const T* q = (const T*)a.q;
     const T* k = (const T*)a.k;
@@ -89,7 +94,8 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = 16 * ct + 4 * j4 + e, n = n0 + 16 * nt + i16;
-            S[i][e] = a.h0 ? a.h0[(bh * DK + c) * DV + n] : 0.f;
+            if (P > 1) S[i][e] = a.S_in[((bh * P + piece) * DK + c) * DV + n];
+            else S[i][e] = a.h0 ? a.h0[(bh * DK + c) * DV + n] : 0.f;
         }
     }
 
@@ -106,9 +112,9 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
         if constexpr (VEC) pg.load(gbase + t0 * rs_g, rs_g, nvalid);
         if (w == 0) rr.load(gbase + t0 * rs_g, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
     };
-    prefetch(0);
+    prefetch(cbeg * C);
 
-    for (int64_t it = 0; it < NC; ++it) {
+    for (int64_t it = cbeg; it < cend; ++it) {
         const int64_t t0 = it * C;
         const int64_t nv64 = T_ - t0;
         const int nvalid = nv64 < C ? (int)nv64 : C;
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
             }
         }
         __syncthreads();
-        if (it + 1 < NC) prefetch(t0 + C);
+        if (it + 1 < cend) prefetch(t0 + C);
 
         if constexpr (VEC) {
             // ---- gate prefix on the matrix cores; QA, KA in place; per-channel factors
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
         __syncthreads();
     }
 
-    if (a.hT) {
+    if (a.hT && piece == P - 1) {
 #pragma unroll
         for (int i = 0; i < UPW; ++i) {
             const int u = w * UPW + i, ct = u / NNT, nt = u % NNT;
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
 
 template <typename T, bool VEC, int DK, int DV, int NV>
 hipError_t launch_fwd(const PassArgs& a, hipStream_t st) {
-    const int64_t grid = a.B * a.H * (DV / NV);
+    const int64_t grid = a.B * a.H * (DV / NV) * a.P;
     hipLaunchKernelGGL((k_fwd<T, VEC, DK, DV, NV>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     return hipGetLastError();
 }

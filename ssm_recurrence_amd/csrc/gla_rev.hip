@@ -155,7 +155,7 @@ __device__ __forceinline__ void rev_chunk_info(RevChunk* ci, const RowRegs& rr) 
 
 // ============================================================== QK role
 template <typename T, bool VEC, int DK, int DV>
-__device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
+__device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int64_t piece, int slice) {
     using Cfg = RevCfg<T, VEC, DK, DV>;
     using M = Mma<T>;
     constexpr int PB = Cfg::PB, PV = Cfg::PV, PE = Cfg::PE;
@@ -189,6 +189,11 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
     const int c = cs0 + cl;                       // ... within the head
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
+    const int64_t P = a.P;
+    const int64_t cbeg = piece * a.PL;
+    const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
+    // gradient of the state at the end of this piece: dhT for the last piece
+    const float* dSend = P > 1 ? a.dS_out + (bh * P + piece) * DK * DV : (a.dhT ? a.dhT + bh * DK * DV : nullptr);
 
     const T* q = (const T*)a.q;
     const T* k = (const T*)a.k;
@@ -210,7 +215,7 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
     for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            dSt[nt][e] = a.dhT ? a.dhT[(bh * DK + c) * DV + 16 * nt + 4 * j4 + e] : 0.f;
+            dSt[nt][e] = dSend ? dSend[c * DV + 16 * nt + 4 * j4 + e] : 0.f;
 
     // boundary term of the last chunk: rowsum(hT * dhT) for this channel
     auto rowsum_with = [&](auto Sget) {
@@ -225,8 +230,8 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
     };
     float bnd;
     {
-        const T* hT = Sws + ((bh * (NC + 1) + NC) * DK + c) * DV;
-        bnd = rowsum_with([&](int n) { return to_f32(hT[n]); });
+        const T* Send = Sws + ((bh * (NC + 1) + cend) * DK + c) * DV;
+        bnd = rowsum_with([&](int n) { return to_f32(Send[n]); });
     }
 
     TileRegs<T, 64> pq, pk, pg;
@@ -244,9 +249,9 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
         ps.load(Sws + ((bh * (NC + 1) + ci) * DK + cs0) * DV, DV, C);
         if (w == 0) rr.load(gbase + t0 * rs_g, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
     };
-    prefetch(NC - 1);
+    prefetch(cend - 1);
 
-    for (int64_t ci = NC - 1; ci >= 0; --ci) {
+    for (int64_t ci = cend - 1; ci >= cbeg; --ci) {
         const int64_t t0 = ci * C;
         const int64_t nv64 = T_ - t0;
         const int nvalid = nv64 < C ? (int)nv64 : C;
@@ -263,7 +268,7 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
         ps.store_rows(sS, PV);
         if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
         __syncthreads();
-        if (ci > 0) prefetch(ci - 1);
+        if (ci > cbeg) prefetch(ci - 1);
         const int first_reset = ck.first_reset, last_reset = ck.last_reset;
 
         if constexpr (VEC) {
@@ -531,7 +536,7 @@ __device__ void rev_qk(const RevArgs& a, char* lds, int64_t bh, int slice) {
 
 // ============================================================== V role
 template <typename T, bool VEC, int DK, int DV>
-__device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
+__device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int64_t piece, int slice) {
     using Cfg = RevCfg<T, VEC, DK, DV>;
     using M = Mma<T>;
     constexpr int PB = Cfg::PB, PK = Cfg::PK;
@@ -555,6 +560,11 @@ __device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
     const int n = n0s + 16 * w + i16;             // this lane's value column
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
+    const int64_t P = a.P;
+    const int64_t cbeg = piece * a.PL;
+    const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
+    // gradient of the state at the end of this piece: dhT for the last piece
+    const float* dSend = P > 1 ? a.dS_out + (bh * P + piece) * DK * DV : (a.dhT ? a.dhT + bh * DK * DV : nullptr);
 
     const T* q = (const T*)a.q;
     const T* k = (const T*)a.k;
@@ -573,7 +583,7 @@ __device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            dS[ct][e] = a.dhT ? a.dhT[(bh * DK + 16 * ct + 4 * j4 + e) * DV + n] : 0.f;
+            dS[ct][e] = dSend ? dSend[(16 * ct + 4 * j4 + e) * DV + n] : 0.f;
 
     TileRegs<T, DK> pq, pk, pg;
     TileRegs<T, 64> pdo;
@@ -588,9 +598,9 @@ __device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
         pdo.load(dobase + t0 * rs_v, rs_v, nvalid);
         if (w == 0) rr.load(gbase + t0 * rs_g, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
     };
-    prefetch(NC - 1);
+    prefetch(cend - 1);
 
-    for (int64_t ci = NC - 1; ci >= 0; --ci) {
+    for (int64_t ci = cend - 1; ci >= cbeg; --ci) {
         const int64_t t0 = ci * C;
         const int64_t nv64 = T_ - t0;
         const int nvalid = nv64 < C ? (int)nv64 : C;
@@ -601,7 +611,7 @@ __device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
         pdo.store_rows(sdO, PB);
         if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
         __syncthreads();
-        if (ci > 0) prefetch(ci - 1);
+        if (ci > cbeg) prefetch(ci - 1);
         const int last_reset = ck.last_reset;
 
         if constexpr (VEC) {
@@ -730,7 +740,7 @@ __device__ void rev_v(const RevArgs& a, char* lds, int64_t bh, int slice) {
             }
         }
     }
-    if (a.dh0) {
+    if (a.dh0 && piece == 0) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -743,11 +753,13 @@ __global__ __launch_bounds__(NT) void k_rev(const RevArgs a) {
     using Cfg = RevCfg<T, VEC, DK, DV>;
     __shared__ __attribute__((aligned(16))) char lds[Cfg::BYTES];
     constexpr int PER = Cfg::NQK + Cfg::NVR;
-    const int64_t L = xcd_logical_block(a.B * a.H * PER);
-    const int64_t bh = L / PER;
+    // block -> (b, h, piece, role); the roles of one piece are adjacent (one XCD)
+    const int64_t L = xcd_logical_block(a.B * a.H * a.P * PER);
     const int role = (int)(L % PER);
-    if (role < Cfg::NQK) rev_qk<T, VEC, DK, DV>(a, lds, bh, role);
-    else rev_v<T, VEC, DK, DV>(a, lds, bh, role - Cfg::NQK);
+    const int64_t piece = (L / PER) % a.P;
+    const int64_t bh = L / PER / a.P;
+    if (role < Cfg::NQK) rev_qk<T, VEC, DK, DV>(a, lds, bh, piece, role);
+    else rev_v<T, VEC, DK, DV>(a, lds, bh, piece, role - Cfg::NQK);
 }
 
 // Scalar gate: dg[u] = sum_{t >= u, same doc} x[t] + [u in last doc] bnd, with x and bnd
@@ -792,7 +804,7 @@ __global__ __launch_bounds__(64) void k_dg_scalar_f32(const RevArgs a, int nslic
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_rev(const RevArgs& a, hipStream_t st) {
     using Cfg = RevCfg<T, VEC, DK, DV>;
-    const int64_t grid = a.B * a.H * (Cfg::NQK + Cfg::NVR);
+    const int64_t grid = a.B * a.H * a.P * (Cfg::NQK + Cfg::NVR);
     hipLaunchKernelGGL((k_rev<T, VEC, DK, DV>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || VEC) return e;

@@ -14,14 +14,32 @@
 // transposed state S^T (rows n, columns c) for them in accumulators, so its
 // C-layout lanes hold four consecutive n of one channel c: the [c][n] stores
 // are 8 bytes wide.
+//
+// Exact sequence split.  With the time axis cut into P pieces of PL chunks, a
+// piece maps the state entering it to the state leaving it by an affine map
+// S -> D_p S + L_p, D_p the diagonal product of the chunk decays over the
+// piece (0 once a document starts inside it) and L_p the state the piece
+// builds from zero; composing these maps is exact, so the pieces run in
+// parallel and only the P-step combine is sequential (the chunkwise state
+// passing of the FLAT page, Linear Attention > Forward Recurrence, applied once
+// more between pieces; the JLA page, "JLA: JAX Linear Attention", among the
+// cases where it is slower, names its own split of long rows exact in the same
+// sense).  The same kernel computes, by MODE:
+//   ST_STATES   per-chunk states of one piece, starting from the piece's entry state;
+//   ST_SUM_FWD  L_p and D_p of one piece (chunks first to last, from zero);
+//   ST_SUM_REV  the reverse map's constant term for the state gradient: from
+//               zero, chunks last to first, dL <- decay dL + QR^T dO with
+//               QR = q exp(beta) on the chunk's first document (the dS update
+//               of the reverse pass).  Its diagonal part is D_p again.
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
 #include "gla_tile.hpp"
 
 namespace gla {
 
-template <typename T, bool VEC, int DK, int DV>
+template <typename T, bool VEC, int DK, int DV, int MODE>
 __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
+    constexpr bool REV = MODE == ST_SUM_REV;
     constexpr int CB = 64, NB = 64;          // block of the state
     constexpr int NCB = DK / CB, NNB = DV / NB;
     constexpr int PB = Pitch16<T>::of(CB);   // pitch of [row][64] tiles
@@ -33,20 +51,26 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) T sG[VEC ? C * PB : 1];
     __shared__ float sFu[C];
     __shared__ float sDecay[CB];
-    __shared__ int sLastReset;
+    __shared__ int sFirstReset, sLastReset;
 
-    const int64_t L = xcd_logical_block(a.B * a.H * NCB * NNB);
-    const int64_t bh = L / (NCB * NNB);
+    // block -> (b, h, piece, state block)
+    const int64_t P = a.P;
+    const int64_t L = xcd_logical_block(a.B * a.H * P * NCB * NNB);
     const int blk = (int)(L % (NCB * NNB));
+    const int64_t piece = (L / (NCB * NNB)) % P;
+    const int64_t bh = L / (NCB * NNB) / P;
     const int c0 = (blk / NNB) * CB, n0 = (blk % NNB) * NB;
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t G = a.H / a.Hqk, hq = h / G;
     const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
+    const int64_t cbeg = piece * a.PL;
+    const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
 
-    const T* k = (const T*)a.k;
-    const T* v = (const T*)a.v;
+    // the reverse summary runs the same update with (q, dO) in place of (k, v)
+    const T* k = (const T*)(REV ? a.q : a.k);
+    const T* v = (const T*)(REV ? a.dO : a.v);
     const T* g = (const T*)a.g;
     const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
     const int64_t rs_g = VEC ? a.H * DK : a.H;
@@ -58,11 +82,20 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
     // S^T tiles of this wave: (nt, channel tile w); lane c = c0 + 16w + i16, rows n
     f32x4 St[NNT];
     const int cme = c0 + 16 * w + i16;
+    const int64_t prow = ((bh * P + piece) * DK + cme) * DV + n0;  // this lane's row of a piece state
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            St[nt][e] = a.h0 ? a.h0[(bh * DK + cme) * DV + n0 + 16 * nt + 4 * j4 + e] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+            const int n = 16 * nt + 4 * j4 + e;
+            float x = 0.f;
+            if constexpr (MODE == ST_STATES) {
+                if (P > 1) x = a.S_in[prow + n];
+                else if (a.h0) x = a.h0[(bh * DK + cme) * DV + n0 + n];
+            }
+            St[nt][e] = x;
+        }
+    float dprod = 1.f;  // product of this lane's channel decays over the chunks seen
 
     TileRegs<T, CB> pk, pg;
     TileRegs<T, NB> pv;
@@ -85,11 +118,13 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
             x.store(dst + 16 * nt + 4 * j4);
         }
     };
-    prefetch(0);
+    const int64_t nchunks = cend - cbeg;
+    prefetch((REV ? cend - 1 : cbeg) * C);
 
-    for (int64_t ci = 0; ci < NC; ++ci) {
+    for (int64_t ii = 0; ii < nchunks; ++ii) {
+        const int64_t ci = REV ? cend - 1 - ii : cbeg + ii;
         const int64_t t0 = ci * C;
-        store_state(ci);
+        if constexpr (MODE == ST_STATES) store_state(ci);
         pk.store_rows(sK, PB);
         pv.store_rows(sV, PB);
         if constexpr (VEC) pg.store_rows(sG, PB);
@@ -97,22 +132,28 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
             const int r = l;
             const uint64_t msk = __ballot(rr.reset);
             const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
-            if (r == 0) sLastReset = last_reset;
+            const int first_reset = msk ? __builtin_ctzll(msk) : C;
+            if (r == 0) {
+                sLastReset = last_reset;
+                sFirstReset = first_reset;
+            }
             if constexpr (!VEC) {
                 const float beta = wave_incl_scan(rr.g);
                 const float Gam = __shfl(beta, 63, 64);
-                sFu[r] = r >= last_reset ? __expf(Gam - beta) : 0.f;
+                if constexpr (REV) sFu[r] = r < first_reset ? __expf(beta) : 0.f;
+                else sFu[r] = r >= last_reset ? __expf(Gam - beta) : 0.f;
                 if (r == 0) sDecay[0] = msk ? 0.f : __expf(Gam);
             }
         }
         __syncthreads();
-        if (ci + 1 < NC) prefetch(t0 + C);
+        if (ii + 1 < nchunks) prefetch(REV ? t0 - C : t0 + C);
 
         if constexpr (VEC) {
-            // per-channel prefix on the matrix cores; KU = k exp(Gamma - beta), last document only
+            // per-channel prefix on the matrix cores; KU = k exp(Gamma - beta), last document
+            // only (reverse summary: QR = q exp(beta), first document only)
             f32x4 beta[1][4];
             gate_prefix_mfma<T, 1, PB>(sG, beta);
-            const int last_reset = sLastReset;
+            const int last_reset = sLastReset, first_reset = sFirstReset;
             const int cl = 16 * w + 4 * j4;  // this lane's 4 channels (block-local)
             float Gam[4];
 #pragma unroll
@@ -122,8 +163,10 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
                 const int r = 16 * rt + i16;
                 Vec4<T> kv = Vec4<T>::load(sK + r * PB + cl);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    kv.set(e, r >= last_reset ? kv.get(e) * __expf(Gam[e] - beta[0][rt][e]) : 0.f);
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (REV) kv.set(e, r < first_reset ? kv.get(e) * __expf(beta[0][rt][e]) : 0.f);
+                    else kv.set(e, r >= last_reset ? kv.get(e) * __expf(Gam[e] - beta[0][rt][e]) : 0.f);
+                }
                 kv.store(sK + r * PB + cl);
             }
             if (i16 == 0)
@@ -134,6 +177,7 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
 
         // S^T[n][c] <- decay_c S^T[n][c] + sum_s v[s][n] KU[s][c], in place
         const float dec = VEC ? sDecay[16 * w + i16] : sDecay[0];
+        dprod *= dec;
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
@@ -156,18 +200,67 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
         }
         __syncthreads();
     }
-    store_state(NC);
+    if constexpr (MODE == ST_STATES) {
+        if (piece == P - 1) store_state(NC);
+    } else {
+        // piece summary: the constant term in fp32, and (forward) the decay product
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+            *reinterpret_cast<f32x4*>(a.L_out + prow + 16 * nt + 4 * j4) = St[nt];
+        if (MODE == ST_SUM_FWD && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
+    }
 }
 
 template <typename T, bool VEC, int DK, int DV>
-hipError_t launch_states(const PassArgs& a, hipStream_t st) {
-    const int64_t grid = a.B * a.H * (DK / 64) * (DV / 64);
-    hipLaunchKernelGGL((k_states<T, VEC, DK, DV>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+hipError_t launch_states(const PassArgs& a, int mode, hipStream_t st) {
+    const int64_t grid = a.B * a.H * a.P * (DK / 64) * (DV / 64);
+    if (mode == ST_SUM_FWD)
+        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_SUM_FWD>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    else if (mode == ST_SUM_REV)
+        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_SUM_REV>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_STATES>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    return hipGetLastError();
+}
+
+// Piece-state combine: one thread per state element (b, h, c, n), P sequential
+// steps of S <- D_p[c] S + L_p[c][n]; out[p] is the state entering piece p
+// (forward) or the state gradient at its end (rev).
+__global__ __launch_bounds__(256) void k_piece_combine(const float* L, const float* D, const float* init,
+                                                       float* out, int64_t BH, int64_t P, int DK, int DV,
+                                                       int rev) {
+    const int64_t per = (int64_t)DK * DV;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= BH * per) return;
+    const int64_t bh = i / per, cn = i % per;
+    const int c = (int)(cn / DV);
+    float s = init ? init[i] : 0.f;
+    const int64_t base = bh * P * per + cn;
+    if (!rev) {
+        out[base] = s;
+        for (int64_t p = 0; p + 1 < P; ++p) {
+            s = D[(bh * P + p) * DK + c] * s + L[base + p * per];
+            out[base + (p + 1) * per] = s;
+        }
+    } else {
+        out[base + (P - 1) * per] = s;
+        for (int64_t p = P - 1; p > 0; --p) {
+            s = D[(bh * P + p) * DK + c] * s + L[base + p * per];
+            out[base + (p - 1) * per] = s;
+        }
+    }
+}
+
+hipError_t launch_piece_combine(const float* L, const float* D, const float* init, float* out, int64_t BH,
+                                int64_t P, int DK, int DV, bool rev, hipStream_t st) {
+    const int64_t n = BH * DK * DV;
+    hipLaunchKernelGGL(k_piece_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, L, D, init, out,
+                       BH, P, DK, DV, rev ? 1 : 0);
     return hipGetLastError();
 }
 
 #define GLA_INST_ST(T, VEC, DK, DV) \
-    template hipError_t launch_states<T, VEC, DK, DV>(const PassArgs&, hipStream_t);
+    template hipError_t launch_states<T, VEC, DK, DV>(const PassArgs&, int, hipStream_t);
 #define GLA_INST_ST_D(T, VEC)                                     \
     GLA_INST_ST(T, VEC, 64, 64) GLA_INST_ST(T, VEC, 64, 128)      \
     GLA_INST_ST(T, VEC, 128, 64) GLA_INST_ST(T, VEC, 128, 128)

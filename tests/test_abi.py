@@ -80,8 +80,9 @@ def test_dtype_and_gate_errors(lib):
     p.gate = 2
     assert call_bwd(lib, p) == -3
     p = prob()
-    p.reserved = 1
+    p.split = -1
     assert call_fwd(lib, p) == -2
+    assert call_bwd(lib, p) == -2
 
 
 def test_alignment_errors(lib):
@@ -98,6 +99,45 @@ def test_workspace_errors_and_size(lib):
     assert call_bwd(lib, p, {"ws": None}, ws_bytes=n.value) == -6
     assert call_bwd(lib, p, {"ws": FAKE}, ws_bytes=n.value - 1) == -6
     assert lib.gla_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == 0
+
+
+def _ws(lib, p, backward):
+    n = ctypes.c_size_t()
+    assert lib.gla_workspace_size(ctypes.byref(p), int(backward), ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_split_workspace(lib):
+    """The sequence split needs piece summaries and entry states: two fp32
+    [B, H, P, d_k, d_v] buffers plus the decay products, in both passes."""
+    B, H, T, d = 1, 2, 64 * 16, 64
+    base = prob(B=B, T=T, H=H, H_qk=H, d_k=d, d_v=d)
+    base.split = 1
+    assert _ws(lib, base, False) == 0
+    bwd1 = _ws(lib, base, True)
+    for P in (2, 4, 16):
+        p = prob(B=B, T=T, H=H, H_qk=H, d_k=d, d_v=d)
+        p.split = P
+        need = 2 * B * H * P * d * d * 4 + B * H * P * d * 4
+        assert _ws(lib, p, False) >= need
+        assert _ws(lib, p, True) >= bwd1 + need
+    # more pieces than chunks: capped at one chunk per piece
+    p = prob(B=B, T=T, H=H, H_qk=H, d_k=d, d_v=d)
+    p.split = 1000
+    q = prob(B=B, T=T, H=H, H_qk=H, d_k=d, d_v=d)
+    q.split = 16
+    assert _ws(lib, p, True) == _ws(lib, q, True)
+
+
+def test_auto_split_only_when_short_of_workgroups(lib):
+    """split = 0: long rows at small B*H are split, large B*H is not."""
+    small_bh = prob(B=1, T=65536, H=16, H_qk=16, d_k=128, d_v=128)
+    large_bh = prob(B=8, T=2048, H=16, H_qk=16, d_k=128, d_v=128)
+    assert _ws(lib, small_bh, False) > 0
+    assert _ws(lib, large_bh, False) == 0
+    one = prob(B=1, T=65536, H=16, H_qk=16, d_k=128, d_v=128)
+    one.split = 1
+    assert _ws(lib, small_bh, True) > _ws(lib, one, True)
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")

@@ -6,6 +6,8 @@ gradient.  The oracle reads exactly the values the GPU reads (bf16 inputs are
 rounded once, when drawn).  Outputs and workspace are poisoned with NaN before
 each call, so any element a kernel fails to write shows up.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -51,10 +53,11 @@ def to_np(t):
     return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(case, dev="cuda"):
+def run_gpu(case, dev="cuda", split=0):
     c = case.to(dev)
-    o, hT = gb.fwd(c.q, c.k, c.v, c.g, c.h0, c.segment_ids, gate=c.gate)
-    dq, dk, dv, dg, dh0 = gb.bwd(c.q, c.k, c.v, c.g, c.dO, c.h0, c.segment_ids, c.dhT, gate=c.gate)
+    o, hT = gb.fwd(c.q, c.k, c.v, c.g, c.h0, c.segment_ids, gate=c.gate, split=split)
+    dq, dk, dv, dg, dh0 = gb.bwd(c.q, c.k, c.v, c.g, c.dO, c.h0, c.segment_ids, c.dhT, gate=c.gate,
+                                 split=split)
     torch.cuda.synchronize()
     return dict(o=o, hT=hT, dq=dq, dk=dk, dv=dv, dg=dg, dh0=dh0)
 
@@ -110,6 +113,76 @@ def test_small_parity(T, dk, dv, gate, dtype, H, Hqk, lens, hs):
 def test_workload_c1():
     """Scalar-decay fp32, B=1 H=2 T=256 d=64, chunk 64 (the small oracle-sized workload)."""
     check(workload("c1"))
+
+
+# Sequence split forced on small rows: pieces of whole chunks, documents that
+# start inside a piece, on a piece boundary and cross several pieces, ragged tails.
+SPLIT = [
+    # (T, d_k, d_v, gate, dtype, H, H_qk, lengths, h0/dhT, split)
+    (640, 64, 64, "scalar", torch.float32, 2, 2, [200, 300, 140], True, 3),
+    (700, 128, 128, "vector", torch.float32, 2, 2, None, True, 4),
+    (1000, 128, 128, "vector", torch.bfloat16, 2, 2, [300, 700], True, 5),
+    (513, 128, 128, "scalar", torch.bfloat16, 4, 2, None, True, 2),
+    (640, 128, 128, "scalar", torch.bfloat16, 2, 2, [256, 384], False, 100),
+    (448, 64, 128, "vector", torch.bfloat16, 4, 1, [10, 50, 4, 300, 84], True, 7),
+]
+
+
+@pytest.mark.parametrize("T,dk,dv,gate,dtype,H,Hqk,lens,hs,split", SPLIT,
+                         ids=["T%d-%d-%d-%s-%s-H%d-%d-%s-%s-P%d" % (c[0], c[1], c[2], c[3],
+                              str(c[4])[6:], c[5], c[6], "seg" if c[7] else "noseg",
+                              "h0" if c[8] else "noh0", c[9]) for c in SPLIT])
+def test_split_parity(T, dk, dv, gate, dtype, H, Hqk, lens, hs, split):
+    case = small_case(seed=T + split, B=2, T=T, H=H, H_qk=Hqk, d=dk, d_v=dv, gate=gate,
+                      dtype=dtype, with_h0=hs, with_dhT=hs, lengths=lens)
+    check(case, got=run_gpu(case, split=split))
+
+
+def subcase(case, b, qh):
+    """Batch row b and q/k head qh (with the heads that read it) of a case."""
+    G = case.H // case.H_qk
+    hs = slice(qh * G, (qh + 1) * G)
+    pick = lambda x, h: None if x is None else x[b:b + 1, :, h].contiguous()
+    st = lambda x: None if x is None else x[b:b + 1, hs].contiguous()
+    return dataclasses.replace(
+        case, q=pick(case.q, slice(qh, qh + 1)), k=pick(case.k, slice(qh, qh + 1)),
+        v=pick(case.v, hs), g=pick(case.g, hs), dO=pick(case.dO, hs), h0=st(case.h0),
+        dhT=st(case.dhT),
+        segment_ids=None if case.segment_ids is None else case.segment_ids[b:b + 1].contiguous())
+
+
+def sub_outputs(got, case, b, qh):
+    G = case.H // case.H_qk
+    hs = slice(qh * G, (qh + 1) * G)
+    qs = slice(qh, qh + 1)
+    out = {}
+    for n, t in got.items():
+        if t is None:
+            out[n] = None
+        elif n in ("hT", "dh0"):
+            out[n] = t[b:b + 1, hs]
+        elif n in ("dq", "dk"):
+            out[n] = t[b:b + 1, :, qs]
+        else:
+            out[n] = t[b:b + 1, :, hs]
+    return out
+
+
+# Full workload sizes in the launch configuration the benchmark times (the
+# library's own split choice); outputs compared on sampled (batch row, q/k head
+# group) pairs, each checked whole against the oracle run on that slice alone.
+FULL = {"c2": [(0, 0), (3, 1)], "c3": [(0, 0), (3, 15)], "c4": [(0, 0), (0, 9), (0, 15)],
+        "c5a": [(0, 0), (0, 15)], "c5b": [(0, 3), (7, 15)]}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(name):
+    case = workload(name)
+    print("full-size", name, tuple(case.q.shape), tuple(case.v.shape), flush=True)
+    got = run_gpu(case)
+    for b, qh in FULL[name]:
+        sub = subcase(case, b, qh)
+        check(sub, got=sub_outputs(got, case, b, qh))
 
 
 def test_deterministic():
