@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=3,
+                    help="extra untimed-region steps after a 512 MB cache flush (median reported)")
     ap.add_argument("--split", type=int, default=0,
                     help="sequence pieces per (b, h); 0 = the library's own choice")
     args = ap.parse_args()
@@ -150,6 +152,20 @@ def main():
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     fwd_us = 1000.0 * sum(fwd_ms) / len(fwd_ms)
     bwd_us = 1000.0 * sum(bwd_ms) / len(bwd_ms)
+    med = lambda xs: 1000.0 * sorted(xs)[len(xs) // 2]
+
+    # cold caches: 512 MB written between steps evicts L2 and the MALL (untimed)
+    cold_f, cold_b = [], []
+    if args.cold > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for i in range(args.cold):
+            flush.fill_(i & 0xFF)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            step(ev)
+            torch.cuda.synchronize()
+            cold_f.append(ev[0].elapsed_time(ev[1]))
+            cold_b.append(ev[1].elapsed_time(ev[2]))
+        del flush
     tokens = B * T
     value = tokens / (ms_per_step / 1000.0)
 
@@ -197,6 +213,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "us_fwd": round(fwd_us, 1), "us_bwd": round(bwd_us, 1),
         "us_fwd_bwd": round(fwd_us + bwd_us, 1),
+        "us_fwd_median": round(med(fwd_ms), 1), "us_bwd_median": round(med(bwd_ms), 1),
+        "us_fwd_cold": round(med(cold_f), 1) if cold_f else None,
+        "us_bwd_cold": round(med(cold_b), 1) if cold_b else None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic (seeded)",
         "config": {"workload": "%s: %s" % (args.workload, WORKLOADS[args.workload]),

@@ -45,11 +45,13 @@ int check_problem(const gla_problem* p) {
     return GLA_OK;
 }
 
-// Sequence pieces per (b, h) and chunks per piece.  One workgroup per compute
-// unit (256) is the target: split only when B * H (times the workgroups per
-// head) falls short of it, and keep at least 8 chunks in a piece so that the
-// summary and combine stay small next to the main pass.
-constexpr int64_t kTargetWG = 256, kMinPieceChunks = 8;
+// Sequence pieces per (b, h) and chunks per piece.  The sequential passes need
+// enough workgroups to occupy the device: the forward's one per compute unit
+// (256), the backward's paired state and state-gradient passes two per unit
+// (their workgroups are small).  Split only when B * H falls short, and keep
+// at least 8 chunks in a piece so that the summary and combine stay small next
+// to the main passes.
+constexpr int64_t kTargetWG = 256, kTargetWGBwd = 512, kMinPieceChunks = 8;
 
 struct Split {
     int64_t P = 1, PL = 0;
@@ -65,15 +67,17 @@ Split plan_split(const gla_problem* p, int for_backward) {
     if (p->split > 0) {
         P = p->split;
     } else {
-        int64_t per_head;  // workgroups per (b, h) without a split
+        int64_t per_head, target;  // workgroups per (b, h) without a split
         if (for_backward) {
-            per_head = p->d_k / 64 + p->d_v / 64;
+            per_head = 2 * (p->d_k / 64) * (p->d_v / 64);
+            target = kTargetWGBwd;
         } else {
             // the forward first narrows its column slices (down to 32 columns)
             if (bh * (p->d_v / 32) >= kTargetWG) return s;
             per_head = p->d_v / (p->dtype == GLA_BF16 ? 64 : 32);
+            target = kTargetWG;
         }
-        P = (kTargetWG + bh * per_head - 1) / (bh * per_head);
+        P = (target + bh * per_head - 1) / (bh * per_head);
         const int64_t pmax = nc / kMinPieceChunks;
         if (P > pmax) P = pmax;
         if (P < 1) P = 1;
@@ -85,16 +89,17 @@ Split plan_split(const gla_problem* p, int for_backward) {
 }
 
 struct WsLayout {
-    size_t S = 0, dq = 0, dk = 0, xs = 0, bnd = 0, pL = 0, pS = 0, pD = 0, total = 0;
+    size_t S = 0, dS = 0, dq = 0, dk = 0, xs = 0, bnd = 0;
+    size_t pL0 = 0, pL1 = 0, pS = 0, pdS = 0, pD = 0, total = 0;
     Split sp;
 };
 
-// Workspace.  Both passes, when the sequence is split: per-piece summaries L
-// and decay products D, and the piece entry states (the backward reuses the two
-// state buffers for the reverse summaries and the state gradients at the piece
-// ends).  Backward only: the state entering every chunk (and the final state)
-// in the input dtype; per-head fp32 dq, dk when heads share q/k; per-slice
-// partial gate-gradient sums for the scalar gate.
+// Workspace.  When the sequence is split: per-piece summaries (L0 forward, L1
+// reverse, fp32), decay products D, and the piece entry states (backward also
+// the state gradients at the piece ends).  Backward only: the state entering
+// every chunk (and the final state) and the state gradient at every chunk's
+// end, in the input dtype; per-head fp32 dq, dk when heads share q/k;
+// per-slice partial gate-gradient sums for the scalar gate.
 WsLayout ws_layout(const gla_problem* p, int for_backward) {
     WsLayout L;
     L.sp = plan_split(p, for_backward);
@@ -105,10 +110,17 @@ WsLayout ws_layout(const gla_problem* p, int for_backward) {
     size_t off = 0;
     if (L.sp.P > 1) {
         const size_t np = bh * (size_t)L.sp.P;
-        L.pL = off;
-        off += round_up(np * (size_t)(p->d_k * p->d_v) * sizeof(float));
+        const size_t pst = round_up(np * (size_t)(p->d_k * p->d_v) * sizeof(float));
+        L.pL0 = off;
+        off += pst;
         L.pS = off;
-        off += round_up(np * (size_t)(p->d_k * p->d_v) * sizeof(float));
+        off += pst;
+        if (for_backward) {
+            L.pL1 = off;
+            off += pst;
+            L.pdS = off;
+            off += pst;
+        }
         L.pD = off;
         off += round_up(np * (size_t)p->d_k * sizeof(float));
     }
@@ -118,6 +130,8 @@ WsLayout ws_layout(const gla_problem* p, int for_backward) {
     }
     L.S = off;
     off += round_up(bh * (size_t)(nc + 1) * st);
+    L.dS = off;
+    off += round_up(bh * (size_t)nc * st);
     if (p->H_qk != p->H) {
         const size_t n = (size_t)(p->B * p->T * p->H * p->d_k) * sizeof(float);
         L.dq = off;
@@ -169,14 +183,30 @@ int copy_state(float* dst, const float* src, int64_t n, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 
+gla::CombineArgs combine_args(const gla::PassArgs& pa, int DK, int DV, int which) {
+    gla::CombineArgs c;
+    c.L_fwd = pa.L_out[0];
+    c.L_rev = pa.L_out[1];
+    c.D = pa.D_out;
+    c.h0 = pa.h0;
+    c.dhT = pa.dhT;
+    c.S_in = (float*)pa.S_in;
+    c.dS_in = (float*)pa.dS_in;
+    c.BH = pa.B * pa.H;
+    c.P = pa.P;
+    c.DK = DK;
+    c.DV = DV;
+    c.which = which;
+    return c;
+}
+
 // Piece entry states for a split forward: summaries, then the combine from h0.
-// pa.L_out, pa.D_out hold the summaries and pa.S_in receives the entry states.
+// pa.L_out[0], pa.D_out hold the summaries and pa.S_in receives the entry states.
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_split_fwd_states(const gla::PassArgs& pa, hipStream_t st) {
     hipError_t e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_SUM_FWD, st);
     if (e != hipSuccess) return e;
-    return gla::launch_piece_combine(pa.L_out, pa.D_out, pa.h0, (float*)pa.S_in, pa.B * pa.H, pa.P, DK, DV,
-                                     false, st);
+    return gla::launch_piece_combine(combine_args(pa, DK, DV, 1), st);
 }
 
 // Columns of the state per forward workgroup: the widest slice that still
@@ -194,25 +224,21 @@ hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
     return gla::launch_fwd<T, VEC, DK, DV, 16>(a, st);
 }
 
+// Backward: (split: both summaries in one launch, both combines in one launch)
+// the state and state-gradient passes in one launch, the chunk-parallel
+// gradients, and the sums over heads that share q/k.
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t st) {
     hipError_t e;
     if (pa.P > 1) {
-        e = run_split_fwd_states<T, VEC, DK, DV>(pa, st);
+        e = gla::launch_states_pair<T, VEC, DK, DV>(pa, true, st);
+        if (e != hipSuccess) return e;
+        e = gla::launch_piece_combine(combine_args(pa, DK, DV, 3), st);
         if (e != hipSuccess) return e;
     }
-    e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, st);
+    e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, st);
     if (e != hipSuccess) return e;
-    if (pa.P > 1) {
-        // reverse summaries into the L buffer, then the state gradients at the piece
-        // ends into the entry-state buffer (both free once the states are written)
-        e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_SUM_REV, st);
-        if (e != hipSuccess) return e;
-        e = gla::launch_piece_combine(pa.L_out, pa.D_out, pa.dhT, (float*)ra.dS_out, pa.B * pa.H, pa.P, DK, DV,
-                                      true, st);
-        if (e != hipSuccess) return e;
-    }
-    e = gla::launch_rev<T, VEC, DK, DV>(ra, st);
+    e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
     if (e != hipSuccess) return e;
     if (ra.Hqk != ra.H) {
         e = gla::launch_group_sum<T, DK>(ra.ws_dq, ra.dq, ra.B, ra.T, ra.H, ra.Hqk, st);
@@ -283,7 +309,7 @@ int gla_fwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     a.P = L.sp.P; a.PL = L.sp.PL;
     if (a.P > 1) {
         char* w = (char*)ws;
-        a.L_out = (float*)(w + L.pL);
+        a.L_out[0] = (float*)(w + L.pL0);
         a.S_in = (const float*)(w + L.pS);
         a.D_out = (float*)(w + L.pD);
     }
@@ -311,18 +337,23 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     gla::PassArgs pa;
     memset(&pa, 0, sizeof pa);
     pa.q = q; pa.k = k; pa.v = v; pa.g = g; pa.dO = dO; pa.h0 = h0; pa.dhT = dhT; pa.seg = segment_ids;
+    pa.dh0 = dh0;
     pa.ws_S = (float*)(w + L.S);
+    pa.ws_dS = w + L.dS;
     pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.Hqk = p->H_qk;
     pa.P = L.sp.P; pa.PL = L.sp.PL;
     if (pa.P > 1) {
-        pa.L_out = (float*)(w + L.pL);
+        pa.L_out[0] = (float*)(w + L.pL0);
+        pa.L_out[1] = (float*)(w + L.pL1);
         pa.S_in = (const float*)(w + L.pS);
+        pa.dS_in = (const float*)(w + L.pdS);
         pa.D_out = (float*)(w + L.pD);
     }
     gla::RevArgs ra;
     memset(&ra, 0, sizeof ra);
     ra.q = q; ra.k = k; ra.v = v; ra.g = g; ra.dO = dO; ra.seg = segment_ids;
     ra.ws_S = w + L.S;
+    ra.ws_dS = w + L.dS;
     ra.dhT = dhT; ra.dh0 = dh0;
     ra.dq = dq; ra.dk = dk; ra.dv = dv; ra.dg = dg;
     if (p->H_qk != p->H) {
@@ -334,8 +365,6 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
         ra.ws_bnd = (float*)(w + L.bnd);
     }
     ra.B = p->B; ra.T = p->T; ra.H = p->H; ra.Hqk = p->H_qk;
-    ra.P = L.sp.P; ra.PL = L.sp.PL;
-    if (ra.P > 1) ra.dS_out = (const float*)(w + L.pS);
     return dispatch<BwdF>(p, pa, ra, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 

@@ -37,25 +37,34 @@
 
 namespace gla {
 
+template <typename T, bool VEC>
+struct StatesLds {
+    static constexpr int PB = Pitch16<T>::of(64);
+    T sK[C * PB];
+    T sV[C * PB];
+    T sG[VEC ? C * PB : 1];
+    float sFu[C];
+    float sDecay[64];
+    int sFirstReset, sLastReset;
+};
+
+// One workgroup: one 64x64 block of the state (or of its gradient) of one
+// piece of one (b, h), walking the piece's chunks in order (reverse order for
+// the gradient modes).  L is the workgroup's logical index within its launch.
 template <typename T, bool VEC, int DK, int DV, int MODE>
-__global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
-    constexpr bool REV = MODE == ST_SUM_REV;
+__device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC>& sm, int64_t L) {
+    constexpr bool REV = MODE == ST_SUM_REV || MODE == ST_DSTATES;
     constexpr int CB = 64, NB = 64;          // block of the state
     constexpr int NCB = DK / CB, NNB = DV / NB;
-    constexpr int PB = Pitch16<T>::of(CB);   // pitch of [row][64] tiles
+    constexpr int PB = StatesLds<T, VEC>::PB;   // pitch of [row][64] tiles
     constexpr int NNT = NB / 16;
     using M = Mma<T>;
+    T* sK = sm.sK;
+    T* sV = sm.sV;
+    T* sG = sm.sG;
 
-    __shared__ __attribute__((aligned(16))) T sK[C * PB];
-    __shared__ __attribute__((aligned(16))) T sV[C * PB];
-    __shared__ __attribute__((aligned(16))) T sG[VEC ? C * PB : 1];
-    __shared__ float sFu[C];
-    __shared__ float sDecay[CB];
-    __shared__ int sFirstReset, sLastReset;
-
-    // block -> (b, h, piece, state block)
+    // logical block -> (b, h, piece, state block)
     const int64_t P = a.P;
-    const int64_t L = xcd_logical_block(a.B * a.H * P * NCB * NNB);
     const int blk = (int)(L % (NCB * NNB));
     const int64_t piece = (L / (NCB * NNB)) % P;
     const int64_t bh = L / (NCB * NNB) / P;
@@ -68,7 +77,7 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
     const int64_t cbeg = piece * a.PL;
     const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
 
-    // the reverse summary runs the same update with (q, dO) in place of (k, v)
+    // the gradient modes run the same update with (q, dO) in place of (k, v)
     const T* k = (const T*)(REV ? a.q : a.k);
     const T* v = (const T*)(REV ? a.dO : a.v);
     const T* g = (const T*)a.g;
@@ -77,12 +86,12 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
     const T* kbase = k + b * T_ * rs_qk + hq * DK + c0;
     const T* vbase = v + b * T_ * rs_v + h * DV + n0;
     const T* gbase = g + b * T_ * rs_g + (VEC ? h * DK + c0 : h);
-    T* ws = (T*)a.ws_S;  // [B*H][NC+1][DK][DV]
 
     // S^T tiles of this wave: (nt, channel tile w); lane c = c0 + 16w + i16, rows n
     f32x4 St[NNT];
     const int cme = c0 + 16 * w + i16;
     const int64_t prow = ((bh * P + piece) * DK + cme) * DV + n0;  // this lane's row of a piece state
+    const int64_t hrow = (bh * DK + cme) * DV + n0;                 // ... of h0, dhT, dh0
 #pragma unroll
     for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
@@ -91,7 +100,10 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
             float x = 0.f;
             if constexpr (MODE == ST_STATES) {
                 if (P > 1) x = a.S_in[prow + n];
-                else if (a.h0) x = a.h0[(bh * DK + cme) * DV + n0 + n];
+                else if (a.h0) x = a.h0[hrow + n];
+            } else if constexpr (MODE == ST_DSTATES) {
+                if (P > 1) x = a.dS_in[prow + n];
+                else if (a.dhT) x = a.dhT[hrow + n];
             }
             St[nt][e] = x;
         }
@@ -108,8 +120,11 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
         if constexpr (VEC) pg.load(gbase + t0 * rs_g, rs_g, nvalid);
         if (w == 0) rr.load(gbase + t0 * rs_g, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
     };
+    // per-chunk stores in the input dtype: the state entering chunk ci ([NC+1] entries),
+    // or the state gradient at the end of chunk ci ([NC] entries)
     auto store_state = [&](int64_t ci) {
-        T* dst = ws + ((bh * (NC + 1) + ci) * DK + cme) * DV + n0;
+        T* dst = MODE == ST_STATES ? (T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cme) * DV + n0
+                                   : (T*)a.ws_dS + ((bh * NC + ci) * DK + cme) * DV + n0;
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt) {
             Vec4<T> x;
@@ -124,7 +139,7 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
     for (int64_t ii = 0; ii < nchunks; ++ii) {
         const int64_t ci = REV ? cend - 1 - ii : cbeg + ii;
         const int64_t t0 = ci * C;
-        if constexpr (MODE == ST_STATES) store_state(ci);
+        if constexpr (MODE == ST_STATES || MODE == ST_DSTATES) store_state(ci);
         pk.store_rows(sK, PB);
         pv.store_rows(sV, PB);
         if constexpr (VEC) pg.store_rows(sG, PB);
@@ -134,15 +149,15 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
             const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
             const int first_reset = msk ? __builtin_ctzll(msk) : C;
             if (r == 0) {
-                sLastReset = last_reset;
-                sFirstReset = first_reset;
+                sm.sLastReset = last_reset;
+                sm.sFirstReset = first_reset;
             }
             if constexpr (!VEC) {
                 const float beta = wave_incl_scan(rr.g);
                 const float Gam = __shfl(beta, 63, 64);
-                if constexpr (REV) sFu[r] = r < first_reset ? __expf(beta) : 0.f;
-                else sFu[r] = r >= last_reset ? __expf(Gam - beta) : 0.f;
-                if (r == 0) sDecay[0] = msk ? 0.f : __expf(Gam);
+                if constexpr (REV) sm.sFu[r] = r < first_reset ? __expf(beta) : 0.f;
+                else sm.sFu[r] = r >= last_reset ? __expf(Gam - beta) : 0.f;
+                if (r == 0) sm.sDecay[0] = msk ? 0.f : __expf(Gam);
             }
         }
         __syncthreads();
@@ -150,10 +165,10 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
 
         if constexpr (VEC) {
             // per-channel prefix on the matrix cores; KU = k exp(Gamma - beta), last document
-            // only (reverse summary: QR = q exp(beta), first document only)
+            // only (gradient modes: QR = q exp(beta), first document only)
             f32x4 beta[1][4];
             gate_prefix_mfma<T, 1, PB>(sG, beta);
-            const int last_reset = sLastReset, first_reset = sFirstReset;
+            const int last_reset = sm.sLastReset, first_reset = sm.sFirstReset;
             const int cl = 16 * w + 4 * j4;  // this lane's 4 channels (block-local)
             float Gam[4];
 #pragma unroll
@@ -171,12 +186,12 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
             }
             if (i16 == 0)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sDecay[cl + e] = last_reset >= 0 ? 0.f : __expf(Gam[e]);
+                for (int e = 0; e < 4; ++e) sm.sDecay[cl + e] = last_reset >= 0 ? 0.f : __expf(Gam[e]);
             __syncthreads();
         }
 
         // S^T[n][c] <- decay_c S^T[n][c] + sum_s v[s][n] KU[s][c], in place
-        const float dec = VEC ? sDecay[16 * w + i16] : sDecay[0];
+        const float dec = VEC ? sm.sDecay[16 * w + i16] : sm.sDecay[0];
         dprod *= dec;
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
@@ -191,7 +206,7 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
                     const int s = k0 + j4 * M::KPL + e;
                     float x;
                     if constexpr (M::KPL == 1) x = to_f32(ku); else x = to_f32(ku[e]);
-                    M::set(ku, e, x * sFu[s]);
+                    M::set(ku, e, x * sm.sFu[s]);
                 }
             }
 #pragma unroll
@@ -202,13 +217,38 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
     }
     if constexpr (MODE == ST_STATES) {
         if (piece == P - 1) store_state(NC);
+    } else if constexpr (MODE == ST_DSTATES) {
+        // the gradient of h0 is the state gradient entering chunk 0
+        if (piece == 0 && a.dh0) {
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt)
+                *reinterpret_cast<f32x4*>(a.dh0 + hrow + 16 * nt + 4 * j4) = St[nt];
+        }
     } else {
         // piece summary: the constant term in fp32, and (forward) the decay product
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
-            *reinterpret_cast<f32x4*>(a.L_out + prow + 16 * nt + 4 * j4) = St[nt];
+            *reinterpret_cast<f32x4*>(a.L_out[MODE == ST_SUM_REV ? 1 : 0] + prow + 16 * nt + 4 * j4) = St[nt];
         if (MODE == ST_SUM_FWD && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
     }
+}
+
+template <typename T, bool VEC, int DK, int DV, int MODE>
+__global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
+    __shared__ __attribute__((aligned(16))) StatesLds<T, VEC> sm;
+    const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / 64);
+    states_body<T, VEC, DK, DV, MODE>(a, sm, xcd_logical_block(n));
+}
+
+// Two independent passes in one launch (the first half of the grid runs MODE_A,
+// the second MODE_B), so that both directions share the device.
+template <typename T, bool VEC, int DK, int DV, int MODE_A, int MODE_B>
+__global__ __launch_bounds__(NT) void k_states2(const PassArgs a) {
+    __shared__ __attribute__((aligned(16))) StatesLds<T, VEC> sm;
+    const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / 64);
+    const int64_t L = xcd_logical_block(2 * n);
+    if (L < n) states_body<T, VEC, DK, DV, MODE_A>(a, sm, L);
+    else states_body<T, VEC, DK, DV, MODE_B>(a, sm, L - n);
 }
 
 template <typename T, bool VEC, int DK, int DV>
@@ -218,49 +258,71 @@ hipError_t launch_states(const PassArgs& a, int mode, hipStream_t st) {
         hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_SUM_FWD>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     else if (mode == ST_SUM_REV)
         hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_SUM_REV>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    else if (mode == ST_DSTATES)
+        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_DSTATES>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     else
         hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_STATES>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     return hipGetLastError();
 }
 
+template <typename T, bool VEC, int DK, int DV>
+hipError_t launch_states_pair(const PassArgs& a, bool summaries, hipStream_t st) {
+    const int64_t grid = 2 * a.B * a.H * a.P * (DK / 64) * (DV / 64);
+    if (summaries)
+        hipLaunchKernelGGL((k_states2<T, VEC, DK, DV, ST_SUM_FWD, ST_SUM_REV>), dim3((unsigned)grid), dim3(NT), 0,
+                           st, a);
+    else
+        hipLaunchKernelGGL((k_states2<T, VEC, DK, DV, ST_STATES, ST_DSTATES>), dim3((unsigned)grid), dim3(NT), 0,
+                           st, a);
+    return hipGetLastError();
+}
+
 // Piece-state combine: one thread per state element (b, h, c, n), P sequential
-// steps of S <- D_p[c] S + L_p[c][n]; out[p] is the state entering piece p
-// (forward) or the state gradient at its end (rev).
-__global__ __launch_bounds__(256) void k_piece_combine(const float* L, const float* D, const float* init,
-                                                       float* out, int64_t BH, int64_t P, int DK, int DV,
-                                                       int rev) {
-    const int64_t per = (int64_t)DK * DV;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= BH * per) return;
+// steps of S <- D_p[c] S + L_p[c][n].  The forward chain (from h0) gives the
+// state entering each piece; the reverse chain (from dhT, last piece first)
+// gives the state gradient at each piece's end.  `which`: 1 forward, 2
+// reverse, 3 both (the second half of the grid runs the reverse chain).
+__global__ __launch_bounds__(256) void k_piece_combine(CombineArgs c) {
+    const int64_t per = (int64_t)c.DK * c.DV;
+    const int64_t n = c.BH * per;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    bool rev = c.which == 2;
+    if (c.which == 3 && i >= n) {
+        rev = true;
+        i -= n;
+    }
+    if (i >= n) return;
     const int64_t bh = i / per, cn = i % per;
-    const int c = (int)(cn / DV);
-    float s = init ? init[i] : 0.f;
+    const int ch = (int)(cn / c.DV);
+    const int64_t P = c.P;
     const int64_t base = bh * P * per + cn;
+    const float* D = c.D;
     if (!rev) {
-        out[base] = s;
+        float s = c.h0 ? c.h0[i] : 0.f;
+        c.S_in[base] = s;
         for (int64_t p = 0; p + 1 < P; ++p) {
-            s = D[(bh * P + p) * DK + c] * s + L[base + p * per];
-            out[base + (p + 1) * per] = s;
+            s = D[(bh * P + p) * c.DK + ch] * s + c.L_fwd[base + p * per];
+            c.S_in[base + (p + 1) * per] = s;
         }
     } else {
-        out[base + (P - 1) * per] = s;
+        float s = c.dhT ? c.dhT[i] : 0.f;
+        c.dS_in[base + (P - 1) * per] = s;
         for (int64_t p = P - 1; p > 0; --p) {
-            s = D[(bh * P + p) * DK + c] * s + L[base + p * per];
-            out[base + (p - 1) * per] = s;
+            s = D[(bh * P + p) * c.DK + ch] * s + c.L_rev[base + p * per];
+            c.dS_in[base + (p - 1) * per] = s;
         }
     }
 }
 
-hipError_t launch_piece_combine(const float* L, const float* D, const float* init, float* out, int64_t BH,
-                                int64_t P, int DK, int DV, bool rev, hipStream_t st) {
-    const int64_t n = BH * DK * DV;
-    hipLaunchKernelGGL(k_piece_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, L, D, init, out,
-                       BH, P, DK, DV, rev ? 1 : 0);
+hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st) {
+    const int64_t n = c.BH * c.DK * c.DV * (c.which == 3 ? 2 : 1);
+    hipLaunchKernelGGL(k_piece_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, c);
     return hipGetLastError();
 }
 
-#define GLA_INST_ST(T, VEC, DK, DV) \
-    template hipError_t launch_states<T, VEC, DK, DV>(const PassArgs&, int, hipStream_t);
+#define GLA_INST_ST(T, VEC, DK, DV)                                                   \
+    template hipError_t launch_states<T, VEC, DK, DV>(const PassArgs&, int, hipStream_t); \
+    template hipError_t launch_states_pair<T, VEC, DK, DV>(const PassArgs&, bool, hipStream_t);
 #define GLA_INST_ST_D(T, VEC)                                     \
     GLA_INST_ST(T, VEC, 64, 64) GLA_INST_ST(T, VEC, 64, 128)      \
     GLA_INST_ST(T, VEC, 128, 64) GLA_INST_ST(T, VEC, 128, 128)

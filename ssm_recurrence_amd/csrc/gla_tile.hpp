@@ -46,6 +46,20 @@ struct TileRegs {
             }
         }
     }
+    // dst[row][col] with pitch P, as 8-byte stores (rows need only 8-byte alignment)
+    __device__ __forceinline__ void store_rows_b64(T* dst, int P) const {
+#pragma unroll
+        for (int i = 0; i < NVEC; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NV_TOT) {
+                const int row = idx / VPR, cv = (idx % VPR) * VE;
+                typedef __attribute__((__vector_size__(8))) int i32x2;
+                const i32x2 lo = {r[i][0], r[i][1]}, hi = {r[i][2], r[i][3]};
+                *reinterpret_cast<i32x2*>(dst + row * P + cv) = lo;
+                *reinterpret_cast<i32x2*>(dst + row * P + cv + VE / 2) = hi;
+            }
+        }
+    }
     // dst[col][row] with pitch P (transpose)
     __device__ __forceinline__ void store_cols(T* dst, int P) const {
 #pragma unroll

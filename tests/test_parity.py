@@ -185,6 +185,41 @@ def test_full_size_sampled(name):
         check(sub, got=sub_outputs(got, case, b, qh))
 
 
+def test_packed_documents_match_separate_runs():
+    """The packed-document workload (B=1, T=65536, H=16, scalar gate, bf16): for
+    sampled heads, every document of the GPU's packed run matches a separate
+    oracle run of that document alone, from h0 for the first document and from
+    zero for the others; hT is the last document's final state and dh0 the first
+    document's initial-state gradient."""
+    case = workload("c4")
+    lens = case.doc_lengths
+    assert lens is not None and len(lens) > 1
+    got = run_gpu(case)
+    tol = TOL[case.dtype]
+    for qh in (0, 11 % case.H_qk):
+        sub = subcase(case, 0, qh)
+        g_sub = {n: to_np(t) for n, t in sub_outputs(got, case, 0, qh).items()}
+        t0 = 0
+        for i, n in enumerate(lens):
+            ts = slice(t0, t0 + n)
+            cut = lambda x: x[:, ts].contiguous()
+            h0 = sub.h0 if i == 0 else None
+            o, hT = oracle.fwd(cut(sub.q), cut(sub.k), cut(sub.v), cut(sub.g), h0, None,
+                               gate=sub.gate)
+            dq, dk, dv, dg, dh0 = oracle.bwd(cut(sub.q), cut(sub.k), cut(sub.v), cut(sub.g),
+                                             cut(sub.dO), h0, None, None, gate=sub.gate)
+            ref = dict(o=o, dq=dq, dk=dk, dv=dv, dg=dg)
+            errs = {k: rel(g_sub[k][:, ts], v) for k, v in ref.items()}
+            if i == len(lens) - 1:
+                errs["hT"] = rel(g_sub["hT"], hT)
+            if i == 0:
+                errs["dh0"] = rel(g_sub["dh0"], dh0)
+            bad = {k: e for k, e in errs.items() if not e <= tol}
+            assert not bad, "head %d document %d [%d, %d): %s" % (qh, i, t0, t0 + n, bad)
+            t0 += n
+        print("head", qh, len(lens), "documents match", flush=True)
+
+
 def test_deterministic():
     case = small_case(seed=3, B=1, T=200, H=4, H_qk=2, d=128, gate="vector", dtype=torch.bfloat16,
                       lengths=[70, 130])
