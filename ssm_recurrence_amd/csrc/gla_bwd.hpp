@@ -70,13 +70,90 @@ __device__ __forceinline__ void frag_scale_k_ctile(typename Mma<T>::frag& f, int
 
 // Chunk-level document data shared by both roles (wave 0 fills it).
 struct RevChunk {
-    int doc[C];
-    float beta[C];   // scalar gate: chunk-local prefix
-    float fq[C];     // readout rows: [r in first doc] (* exp(beta_r) for the scalar gate)
-    float fu[C];     // update rows:  [s in last doc]  (* exp(Gamma - beta_s) for the scalar gate)
+    alignas(16) int doc[C];
+    alignas(16) float beta[C];   // scalar gate: chunk-local prefix
+    alignas(16) float fq[C];     // readout rows: [r in first doc] (* exp(beta_r) for the scalar gate)
+    alignas(16) float fu[C];     // update rows:  [s in last doc]  (* exp(Gamma - beta_s) for the scalar gate)
     float decay;     // scalar gate: exp(Gamma), 0 if the chunk has a reset
     int first_reset, last_reset;
 };
+
+// Store one 16x16 C-layout tile (rows r = 16rt + 4j + e, column s = 16st + i) of
+// an intra-chunk score matrix, causally and document masked (scalar gate: times
+// exp(beta_r - beta_s)), transposed: dstT[s][r], four consecutive r per lane in
+// one 8-byte store.  `live` false stores zeros (the upper tiles a 32-wide k step reads).
+template <typename T, bool VEC, int P>
+__device__ __forceinline__ void store_masked_T(T* dstT, const RevChunk& ck, int rt, int st, bool live,
+                                               const f32x4& acc) {
+    const int l = lane_id(), j = l >> 4, i = l & 15;
+    const int r0 = 16 * rt + 4 * j, s = 16 * st + i;
+    Vec4<T> out;
+    if (live) {
+        const int4 dr = *reinterpret_cast<const int4*>(&ck.doc[r0]);
+        const int ds = ck.doc[s];
+        const int drr[4] = {dr.x, dr.y, dr.z, dr.w};
+        float bs = 0.f, br[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!VEC) {
+            const float4 b4 = *reinterpret_cast<const float4*>(&ck.beta[r0]);
+            br[0] = b4.x; br[1] = b4.y; br[2] = b4.z; br[3] = b4.w;
+            bs = ck.beta[s];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x = 0.f;
+            if (s <= r0 + e && drr[e] == ds) {
+                x = acc[e];
+                if constexpr (!VEC) x *= __expf(br[e] - bs);
+            }
+            out.set(e, x);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out.set(e, 0.f);
+    }
+    out.store(dstT + s * P + r0);
+}
+
+// Same, for a tile computed transposed (rows s = 16st + 4j + e, column r = 16rt + i):
+// stored in natural orientation dst[r][s], four consecutive s per lane.
+template <typename T, bool VEC, int P>
+__device__ __forceinline__ void store_masked_N(T* dst, const RevChunk& ck, int rt, int st, bool live,
+                                               const f32x4& acc) {
+    const int l = lane_id(), j = l >> 4, i = l & 15;
+    const int r = 16 * rt + i, s0 = 16 * st + 4 * j;
+    Vec4<T> out;
+    if (live) {
+        const int4 dsv = *reinterpret_cast<const int4*>(&ck.doc[s0]);
+        const int dr = ck.doc[r];
+        const int dss[4] = {dsv.x, dsv.y, dsv.z, dsv.w};
+        float br = 0.f, bs[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!VEC) {
+            const float4 b4 = *reinterpret_cast<const float4*>(&ck.beta[s0]);
+            bs[0] = b4.x; bs[1] = b4.y; bs[2] = b4.z; bs[3] = b4.w;
+            br = ck.beta[r];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x = 0.f;
+            if (s0 + e <= r && dss[e] == dr) {
+                x = acc[e];
+                if constexpr (!VEC) x *= __expf(br - bs[e]);
+            }
+            out.set(e, x);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out.set(e, 0.f);
+    }
+    out.store(dst + r * P + s0);
+}
+
+// element e of an operand fragment, as float
+template <typename T>
+__device__ __forceinline__ float frag_get(const typename Mma<T>::frag& f, int e) {
+    if constexpr (Mma<T>::KPL == 1) { (void)e; return f; }
+    else return (float)f[e];
+}
 
 template <typename T, bool VEC>
 __device__ __forceinline__ void rev_chunk_info(RevChunk* ci, const RowRegs& rr) {

@@ -178,6 +178,42 @@ __device__ __forceinline__ typename Mma<T>::frag frag_col(const T* base, int i0,
 }
 
 // ------------------------------------------------------------------ wave primitives
+// Data-parallel moves within rows of 16 lanes (checked on the hardware):
+// row_shl:n (0x100 + n) reads lane i + n of the row, 0 past its end;
+// row_ror:n (0x120 + n) reads lane (i - n) mod 16 of the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// lane i of each row of 16: sum of lanes i .. 15 of its row
+__device__ __forceinline__ float row_suffix16(float y) {
+    y += dpp_f<0x101>(y);
+    y += dpp_f<0x102>(y);
+    y += dpp_f<0x104>(y);
+    y += dpp_f<0x108>(y);
+    return y;
+}
+// every lane: sum of its row of 16
+__device__ __forceinline__ float row_sum16(float y) {
+    y += dpp_f<0x121>(y);
+    y += dpp_f<0x122>(y);
+    y += dpp_f<0x124>(y);
+    y += dpp_f<0x128>(y);
+    return y;
+}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// sum_e a[e] * b[e] over a fragment, fp32 accumulation
+template <typename F>
+__device__ __forceinline__ float frag_dot(const F& a, const F& b, float acc) {
+    if constexpr (sizeof(F) == sizeof(float)) {
+        return acc + a * b;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a[e], a[e + 1]}, bf16x2{b[e], b[e + 1]}, acc, false);
+        return acc;
+    }
+}
 __device__ __forceinline__ float wave_incl_scan(float x) {
     const int l = lane_id();
 #pragma unroll

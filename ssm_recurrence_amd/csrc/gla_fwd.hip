@@ -112,6 +112,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
         if constexpr (VEC) pg.load(gbase + t0 * rs_g, rs_g, nvalid);
         if (w == 0) rr.load(gbase + t0 * rs_g, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
     };
+    [[maybe_unused]] const TriOnes<T> tri;  // gate prefix operands (vector gate)
     prefetch(cbeg * C);
 
     for (int64_t it = cbeg; it < cend; ++it) {
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
         if constexpr (VEC) {
             // ---- gate prefix on the matrix cores; QA, KA in place; per-channel factors
             f32x4 beta[CPW][4];
-            gate_prefix_mfma<T, CPW, PK>(sG, beta);
+            gate_prefix_mfma<T, CPW, PK>(sG, tri, beta);
             const bool any_reset = sAnyReset != 0;
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) {

@@ -50,21 +50,19 @@ struct GradCfg {
     // that it fits in the place of the gate tile
     static constexpr int PD = sizeof(T) == 2 ? 68 : 66;
     static constexpr int PE = 68;              // fp32 [64][64] scratch
-    static constexpr bool STAGE = sizeof(T) == 2;  // bf16 outputs go through LDS to row stores
     static constexpr int max_(int a, int b) { return a > b ? a : b; }
 
-    // QK role: q, k (, g) slices and dA; then dO and v.  After the products the
-    // dO / v region holds the staged outputs and the g / dA region the fp32 dg scratch.
+    // QK role: q, k (, g) slices, dA [r][s], dO and v.  The dg scratch of chunks
+    // with documents inside takes the g / dA region once the products are done.
     static constexpr int TILE64 = C * PB * ES;
     static constexpr int QK_OFF_G = 2 * TILE64;
     static constexpr int QK_OFF_DA = QK_OFF_G + (VEC ? TILE64 : 0);
     static constexpr int QK_OFF_DO = QK_OFF_DA + TILE64;
-    static constexpr int QK_REGION = max_(2 * C * PV * ES, STAGE ? (2 + (VEC ? 1 : 0)) * TILE64 : 0);
-    static constexpr int QK_BYTES = QK_OFF_DO + QK_REGION;
+    static constexpr int QK_BYTES = QK_OFF_DO + 2 * C * PV * ES;
     static_assert(!VEC || 2 * TILE64 >= C * PE * 4, "dg scratch does not fit");
 
-    // V role: q, k (, g) for all channels, the dO slice and A; the dS1 slice takes the
-    // place of g once g is consumed when it fits there.  Staged dv reuses q.
+    // V role: q, k (, g) for all channels, the dO slice and A^T; the dS1 slice takes
+    // the place of g once g is consumed when it fits there.
     static constexpr int TILEK = C * PK * ES;
     static constexpr bool DS_IN_G = VEC && DK * PD <= C * PK;
     static constexpr int V_OFF_G = 2 * TILEK;
@@ -79,43 +77,32 @@ struct GradCfg {
 // Small per-workgroup arrays (both roles).
 struct GradSmall {
     RevChunk ck;
-    float sM[128], sEm[128], sEGm[128];   // vector gate: per-channel m, exp(m), exp(Gamma - m)
-    float sDecay[128];
-    float sXs[4][C];                       // scalar gate: per-wave partial sums
+    float sEGm[128];      // vector gate: exp(Gamma - m) per channel (V role)
+    float sBnd[4][16];    // per-wave boundary terms (QK role, chunks with documents inside)
+    float sXs[4][C];      // scalar gate: per-wave partial sums
     float sBs[4];
 };
 
-// out[rt][e] = base[(16rt + 4j + e) * P + col0 + i] for lane (i, j): the values of
-// a natural [row][col] tile at the C-layout positions of this wave's column tile.
-template <typename T, int P>
-__device__ __forceinline__ void col_vals(const T* base, int col0, float (&out)[4][4]) {
-    if constexpr (sizeof(T) == 2) {
+// Four consecutive values of one row of an output, 16 bytes (fp32) or 8 (bf16).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float (&v)[4]) {
+    Vec4<T> x;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const bf16x8 f = frag_col<T, P, true>(base, col0, 32 * p);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                out[2 * p][e] = (float)f[e];
-                out[2 * p + 1][e] = (float)f[4 + e];
-            }
-        }
-    } else {
-        const int l = lane_id();
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[rt][e] = to_f32(base[(16 * rt + 4 * (l >> 4) + e) * P + col0 + (l & 15)]);
-    }
+    for (int e = 0; e < 4; ++e) x.set(e, v[e]);
+    x.store(p);
 }
 
 // ============================================================== QK role
+// Outputs are computed transposed (rows = key channels, columns = chunk rows):
+// lane (i, j) of the wave holds rows r = 16rt + i and the four channels
+// cw + 4j + e, which is also where the gate prefix leaves exp(beta - m), so the
+// gate factors never leave registers and dq, dk, dg go out as 4-channel stores.
 template <typename T, bool VEC, int DK, int DV>
 __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, int64_t ci, int slice) {
     using Cfg = GradCfg<T, VEC, DK, DV>;
     using M = Mma<T>;
     constexpr int PB = Cfg::PB, PV = Cfg::PV, PE = Cfg::PE;
-    constexpr int NNT = DV / 16;
-    constexpr int KS = M::KSTEP;
+    constexpr int KS = M::KSTEP, NKV = DV / KS;
 
     T* sQ = reinterpret_cast<T*>(lds);
     T* sK = sQ + C * PB;
@@ -123,18 +110,14 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     T* sdA = reinterpret_cast<T*>(lds + Cfg::QK_OFF_DA);  // [r][s]
     T* sdO = reinterpret_cast<T*>(lds + Cfg::QK_OFF_DO);
     T* sV = sdO + C * PV;
-    float* sX = reinterpret_cast<float*>(lds + Cfg::QK_OFF_G);  // dg scratch, after the products
-    T* sOq = sdO;                                                // staged outputs, after the products
-    T* sOk = sOq + C * PB;
-    T* sOg = sOk + C * PB;
+    float* sX = reinterpret_cast<float*>(lds + Cfg::QK_OFF_G);  // dg scratch [r][c], after the products
     RevChunk& ck = sm.ck;
 
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t G = a.H / a.Hqk, hq = h / G;
     const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
     const int cs0 = slice * Cfg::CS;
-    const int cl = 16 * w + i16;  // this lane's channel within the slice
-    const int c = cs0 + cl;       // ... within the head
+    const int cw = cs0 + 16 * w;  // first channel of this wave's tile
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
     const int64_t t0 = ci * C;
@@ -146,10 +129,11 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     const T* vrow = (const T*)a.v + (b * T_ + t0) * rs_v + h * DV;
     const T* dorow = (const T*)a.dO + (b * T_ + t0) * rs_v + h * DV;
     const T* grow = (const T*)a.g + (b * T_ + t0) * rs_g + (VEC ? h * DK + cs0 : h);
-    const T* S0 = (const T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + c) * DV;  // row c of S0
-    const T* dS1 = (const T*)a.ws_dS + ((bh * NC + ci) * DK + c) * DV;     // row c of dS1
+    // rows cw + i of S0 and dS1, the A operands of dO S0^T and v dS1^T (k = n)
+    const T* S0 = (const T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
+    const T* dS1 = (const T*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
 
-    // ---- loads: the chunk's tiles, then this lane's rows of S0 and dS1
+    // ---- loads
     TileRegs<T, 64> pq, pk, pg;
     TileRegs<T, DV> pv, pdo;
     RowRegs rr;
@@ -159,20 +143,18 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     pv.load(vrow, rs_v, nvalid);
     pdo.load(dorow, rs_v, nvalid);
     if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
-    // S0 as B operands of dO S0^T (k = n): lane (i, j) holds S0[c][k0 + j*KPL + e]
-    typename M::frag s0f[DV / KS];
+    typename M::frag s0f[NKV], dsf[NKV];
 #pragma unroll
-    for (int kk = 0; kk < DV / KS; ++kk) {
-        if constexpr (M::KPL == 1) s0f[kk] = S0[kk * KS + j4];
-        else s0f[kk] = *reinterpret_cast<const bf16x8*>(S0 + kk * KS + 8 * j4);
+    for (int kk = 0; kk < NKV; ++kk) {
+        if constexpr (M::KPL == 1) {
+            s0f[kk] = S0[kk * KS + j4];
+            dsf[kk] = dS1[kk * KS + j4];
+        } else {
+            s0f[kk] = *reinterpret_cast<const bf16x8*>(S0 + kk * KS + 8 * j4);
+            dsf[kk] = *reinterpret_cast<const bf16x8*>(dS1 + kk * KS + 8 * j4);
+        }
     }
-    // dS1^T in C layout (lane c, rows n = 16nt + 4*j4 + e), and the matching S0 values
-    Vec4<T> dsr[NNT], s0r[NNT];
-#pragma unroll
-    for (int nt = 0; nt < NNT; ++nt) {
-        dsr[nt] = Vec4<T>::load(dS1 + 16 * nt + 4 * j4);
-        s0r[nt] = Vec4<T>::load(S0 + 16 * nt + 4 * j4);
-    }
+    [[maybe_unused]] const TriOnes<T> tri;
 
     pq.store_rows(sQ, PB);
     pk.store_rows(sK, PB);
@@ -180,56 +162,61 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     pv.store_rows(sV, PV);
     pdo.store_rows(sdO, PV);
     if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
-
-    f32x4 dSt[NNT];
-    float sd = 0.f;  // this lane's part of rowsum(S0 * dS1) for channel c
+    // rowsum(S0 * dS1) of channel cw + i16 over this lane's n
+    float sd = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dSt[nt][e] = dsr[nt].get(e);
-            sd += s0r[nt].get(e) * dSt[nt][e];
-        }
+    for (int kk = 0; kk < NKV; ++kk) sd = frag_dot(s0f[kk], dsf[kk], sd);
     __syncthreads();
-    const int first_reset = ck.first_reset, last_reset = ck.last_reset;
 
+    // raw q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e)
+    Vec4<T> qraw[4], kraw[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        qraw[rt] = Vec4<T>::load(sQ + (16 * rt + i16) * PB + 16 * w + 4 * j4);
+        kraw[rt] = Vec4<T>::load(sK + (16 * rt + i16) * PB + 16 * w + 4 * j4);
+    }
+    float E[4][4];  // exp(beta - m) at those positions (vector gate)
+    float em[4], egm[4], dec[4];
     if constexpr (VEC) {
-        // gate prefix on the matrix cores; q, k scaled in place to QA = q exp(beta - m),
-        // KA = k exp(m - beta) with m the prefix at row 31 (factored exponent)
+        // gate prefix on the matrix cores; this wave's q, k columns scaled in place to
+        // QA = q exp(beta - m), KA = k exp(m - beta), m the prefix at row 31 (factored exponent)
         f32x4 beta[1][4];
-        gate_prefix_mfma<T, 1, PB>(sG, beta);
-        const int c4 = 16 * w + 4 * j4;  // this lane's 4 channels (slice-local)
+        gate_prefix_mfma<T, 1, PB>(sG, tri, beta);
         float m[4], Gam[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             m[e] = __shfl(beta[0][1][e], 16 * j4 + 15, 64);
             Gam[e] = __shfl(beta[0][3][e], 16 * j4 + 15, 64);
         }
+        const bool reset_in_chunk = ck.last_reset >= 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            em[e] = __expf(m[e]);
+            egm[e] = __expf(Gam[e] - m[e]);
+            dec[e] = reset_in_chunk ? 0.f : __expf(Gam[e]);
+        }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const int r = 16 * rt + i16;
-            Vec4<T> qv = Vec4<T>::load(sQ + r * PB + c4);
-            Vec4<T> kv = Vec4<T>::load(sK + r * PB + c4);
+            Vec4<T> qa, ka;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float E = __expf(beta[0][rt][e] - m[e]);
-                qv.set(e, qv.get(e) * E);
-                kv.set(e, kv.get(e) * __builtin_amdgcn_rcpf(E));
+                E[rt][e] = __expf(beta[0][rt][e] - m[e]);
+                qa.set(e, qraw[rt].get(e) * E[rt][e]);
+                ka.set(e, kraw[rt].get(e) * __builtin_amdgcn_rcpf(E[rt][e]));
             }
-            qv.store(sQ + r * PB + c4);
-            kv.store(sK + r * PB + c4);
+            qa.store(sQ + (16 * rt + i16) * PB + 16 * w + 4 * j4);
+            ka.store(sK + (16 * rt + i16) * PB + 16 * w + 4 * j4);
         }
-        if (i16 == 0)
+    } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sm.sM[c4 + e] = m[e];
-                sm.sEm[c4 + e] = __expf(m[e]);
-                sm.sEGm[c4 + e] = __expf(Gam[e] - m[e]);
-                sm.sDecay[c4 + e] = last_reset >= 0 ? 0.f : __expf(Gam[e]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            em[e] = egm[e] = 1.f;
+            dec[e] = ck.decay;
+        }
     }
 
-    // ---- dA = dO v^T on the 10 lower tiles (+ the two upper tiles a 32-wide k step reads)
+    // ---- dA^T = v dO^T on the 10 lower tiles (+ the two upper tiles a 32-wide k
+    // step reads), masked, stored as dA[r][s]
     for (int ti = w; ti < 12; ti += 4) {
         const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
         const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
@@ -237,221 +224,147 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
         if (ti < 10) {
 #pragma unroll
             for (int n0 = 0; n0 < DV; n0 += KS)
-                acc = M::mma(frag_ld<T, PV, 1>(sdO, 16 * rt, n0), frag_ld<T, PV, 1>(sV, 16 * st, n0), acc);
+                acc = M::mma(frag_ld<T, PV, 1>(sV, 16 * st, n0), frag_ld<T, PV, 1>(sdO, 16 * rt, n0), acc);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rt + 4 * j4 + e, s = 16 * st + i16;
-            float x = 0.f;
-            if (ti < 10 && s <= r && ck.doc[s] == ck.doc[r]) {
-                x = acc[e];
-                if constexpr (!VEC) x *= __expf(ck.beta[r] - ck.beta[s]);
-            }
-            sdA[r * PB + s] = from_f32<T>(x);
-        }
+        store_masked_N<T, VEC, PB>(sdA, ck, rt, st, ti < 10, acc);
     }
     __syncthreads();
 
-    // ---- exp(beta - m) at this lane's output positions (rows 16rt + 4*j4 + e,
-    // channel cl): the prefix once more, as L G, in the layout of dq and dk
-    f32x4 Ex[4];
-    if constexpr (VEC) {
-        const float mc = sm.sM[cl];
+    const bool gqa = G > 1;
+    float x[4][4];  // q*dq - k*dk
+    // ---- dq^T = KA^T dA^T + [first doc] exp(m) S0 dO^T, times exp(beta - m)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x4 acc = zero4();
-            const int r = 16 * rt + i16;
+    for (int rt = 0; rt < 4; ++rt) {
+        f32x4 a1 = zero4(), a2 = zero4();
+        const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
 #pragma unroll
-            for (int k0 = 0; k0 < ((16 * (rt + 1) + KS - 1) / KS) * KS; k0 += KS) {
-                typename M::frag lt;
+        for (int k0 = 0; k0 < kend; k0 += KS)
+            a1 = M::mma(frag_col<T, PB, false>(sK, 16 * w, k0), frag_ld<T, PB, 1>(sdA, 16 * rt, k0), a1);
 #pragma unroll
-                for (int e = 0; e < M::KPL; ++e) M::set(lt, e, k0 + j4 * M::KPL + e <= r ? 1.f : 0.f);
-                acc = M::mma(lt, frag_col<T, PB, false>(sG, 16 * w, k0), acc);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ex[rt][e] = __expf(acc[e] - mc);
-        }
-    }
-
-    // ---- dq (before the exp(beta - m) factor: dqp), x = QA*dqp = q*dq
-    const float em = VEC ? sm.sEm[cl] : 1.f, egm = VEC ? sm.sEGm[cl] : 1.f;
-    float x[4][4], dqv[4][4], dkv[4][4];
-    {
-        float qa[4][4];
-        col_vals<T, PB>(sQ, 16 * w, qa);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x4 a1 = zero4(), a2 = zero4();
-            const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
-#pragma unroll
-            for (int k0 = 0; k0 < kend; k0 += KS)
-                a1 = M::mma(frag_ld<T, PB, 1>(sdA, 16 * rt, k0), frag_col<T, PB, false>(sK, 16 * w, k0), a1);
-#pragma unroll
-            for (int kk = 0; kk < DV / KS; ++kk)
-                a2 = M::mma(frag_ld<T, PV, 1>(sdO, 16 * rt, kk * KS), s0f[kk], a2);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * j4 + e;
-                const float dqp = a1[e] + ck.fq[r] * em * a2[e];
-                x[rt][e] = qa[rt][e] * dqp;
-                dqv[rt][e] = VEC ? Ex[rt][e] * dqp : dqp;
-            }
-        }
-    }
-    // ---- dk (dkp before the exp(m - beta) factor), x -= KA*dkp; the boundary sum
-    float bs = 0.f;  // this lane's part of sum_s KU[s][c] (v dS1^T)[s][c]
-    {
-        float ka[4][4];
-        col_vals<T, PB>(sK, 16 * w, ka);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            f32x4 a1 = zero4(), a2 = zero4();
-            const int kbeg = (16 * st / KS) * KS;
-#pragma unroll
-            for (int k0 = kbeg; k0 < C; k0 += KS)
-                a1 = M::mma(frag_col<T, PB, false>(sdA, 16 * st, k0), frag_col<T, PB, false>(sQ, 16 * w, k0), a1);
-            if constexpr (M::KPL == 1) {
-#pragma unroll
-                for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-                    for (int sub = 0; sub < 4; ++sub)
-                        a2 = M::mma(frag_ld_ctile<T, PV, 1>(sV, 16 * st, 16 * nt, sub),
-                                    frag_from_acc<T>(dSt[nt], dSt[nt], sub), a2);
-            } else {
-#pragma unroll
-                for (int p = 0; p < NNT / 2; ++p)
-                    a2 = M::mma(frag_ld_ctile<T, PV, 1>(sV, 16 * st, 32 * p, 0),
-                                frag_from_acc<T>(dSt[2 * p], dSt[2 * p + 1], 0), a2);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = 16 * st + 4 * j4 + e;
-                const float inter = ck.fu[s] * egm * a2[e];
-                const float dkp = a1[e] + inter;
-                x[st][e] -= ka[st][e] * dkp;
-                bs += ka[st][e] * inter;
-                dkv[st][e] = VEC ? dkp * __builtin_amdgcn_rcpf(Ex[st][e]) : dkp;
-            }
-        }
-    }
-    // boundary term rowsum(S1 * dS1) for channel c (sum over the four lane groups)
-    sd += __shfl_xor(sd, 16, 64);
-    sd += __shfl_xor(sd, 32, 64);
-    bs += __shfl_xor(bs, 16, 64);
-    bs += __shfl_xor(bs, 32, 64);
-    const float bnd = (VEC ? sm.sDecay[cl] : ck.decay) * sd + bs;
-    __syncthreads();  // every wave is done with dO, v, g and dA: their LDS is reused below
-
-    // ---- outputs dq, dk: staged for row stores (bf16, unshared q/k) or stored directly
-    const bool staged = Cfg::STAGE && G == 1;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+        for (int kk = 0; kk < NKV; ++kk)
+            a2 = M::mma(s0f[kk], frag_ld<T, PV, 1>(sdO, 16 * rt, kk * KS), a2);
+        const int r = 16 * rt + i16;
+        const float fq = ck.fq[r];
+        float dq[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rt + 4 * j4 + e;
-            if (staged) {
-                sOq[r * PB + cl] = from_f32<T>(dqv[rt][e]);
-                sOk[r * PB + cl] = from_f32<T>(dkv[rt][e]);
-            } else if (r < nvalid) {
-                if (G == 1) {
-                    const int64_t o = ((b * T_ + t0 + r) * a.Hqk + hq) * DK + c;
-                    ((T*)a.dq)[o] = from_f32<T>(dqv[rt][e]);
-                    ((T*)a.dk)[o] = from_f32<T>(dkv[rt][e]);
-                } else {
-                    const int64_t o = ((b * T_ + t0 + r) * a.H + h) * DK + c;
-                    a.ws_dq[o] = dqv[rt][e];
-                    a.ws_dk[o] = dkv[rt][e];
-                }
-            }
+            const float dqp = a1[e] + fq * em[e] * a2[e];
+            dq[e] = VEC ? E[rt][e] * dqp : dqp;
+            x[rt][e] = qraw[rt].get(e) * dq[e];
         }
+        if (r < nvalid) {
+            if (!gqa) store4<T>((T*)a.dq + ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4, dq);
+            else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
+        }
+    }
+    // ---- dk^T = QA^T dA + [last doc] exp(Gamma - m) dS1 v^T, times exp(m - beta);
+    // the boundary sum: sum_s KU[s][c] (v dS1^T)[s][c]
+    float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        f32x4 a1 = zero4(), a2 = zero4();
+        const int kbeg = (16 * st / KS) * KS;
+#pragma unroll
+        for (int k0 = kbeg; k0 < C; k0 += KS)
+            a1 = M::mma(frag_col<T, PB, false>(sQ, 16 * w, k0), frag_col<T, PB, false>(sdA, 16 * st, k0), a1);
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk)
+            a2 = M::mma(dsf[kk], frag_ld<T, PV, 1>(sV, 16 * st, kk * KS), a2);
+        const int s = 16 * st + i16;
+        const float fu = ck.fu[s];
+        float dk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float inter = fu * egm[e] * a2[e];
+            const float rE = VEC ? __builtin_amdgcn_rcpf(E[st][e]) : 1.f;
+            const float kr = kraw[st].get(e);
+            dk[e] = (a1[e] + inter) * rE;
+            x[st][e] -= kr * dk[e];
+            bsum[e] += kr * inter * rE;
+        }
+        if (s < nvalid) {
+            if (!gqa) store4<T>((T*)a.dk + ((b * T_ + t0 + s) * a.Hqk + hq) * DK + cw + 4 * j4, dk);
+            else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
+        }
+    }
+    // boundary term rowsum(S1 * dS1) per channel cw + 4j4 + e
+    sd += __shfl_xor(sd, 16, 64);
+    sd += __shfl_xor(sd, 32, 64);
+    float bnd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bnd[e] = dec[e] * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
 
     // ---- gate gradient
     if constexpr (VEC) {
-        T* dgo = (T*)a.dg;
-        auto put_dg = [&](int r, float val) {
-            if constexpr (Cfg::STAGE) sOg[r * PB + cl] = from_f32<T>(val);
-            else if (r < nvalid) dgo[((b * T_ + t0 + r) * a.H + h) * DK + c] = from_f32<T>(val);
-        };
-        if (first_reset == C) {
-            // no reset in this chunk: suffix sums in-lane over e, across the four
-            // lane groups of a channel, and across row tiles
-            float carry = bnd;
+        T* dgo = (T*)a.dg + ((b * T_ + t0) * a.H + h) * DK + cw + 4 * j4;
+        if (ck.first_reset == C) {
+            // no reset in this chunk: suffix sums over the 16 rows of a tile (lanes),
+            // then across tiles, starting from the boundary term
+            float carry[4] = {bnd[0], bnd[1], bnd[2], bnd[3]};
 #pragma unroll
             for (int rt = 3; rt >= 0; --rt) {
-                float suf[4];
-                suf[3] = x[rt][3];
-                suf[2] = suf[3] + x[rt][2];
-                suf[1] = suf[2] + x[rt][1];
-                suf[0] = suf[1] + x[rt][0];
-                float tot[4];
+                float dg[4];
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) tot[jj] = __shfl(suf[0], 16 * jj + i16, 64);
-                float above = carry;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) above += jj > j4 ? tot[jj] : 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) put_dg(16 * rt + 4 * j4 + e, above + suf[e]);
-                carry += tot[0] + tot[1] + tot[2] + tot[3];
+                for (int e = 0; e < 4; ++e) {
+                    const float y = row_suffix16(x[rt][e]);
+                    dg[e] = y + carry[e];
+                    carry[e] += __shfl(y, 0, 16);
+                }
+                const int r = 16 * rt + i16;
+                if (r < nvalid) store4<T>(dgo + (int64_t)r * a.H * DK, dg);
             }
         } else {
-            // documents inside the chunk: serial segmented suffix sum per channel
+            // documents inside the chunk: serial segmented suffix sum per channel in LDS
+            __syncthreads();  // the scratch takes the place of g and dA
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
+                *reinterpret_cast<f32x4*>(sX + (16 * rt + i16) * PE + 16 * w + 4 * j4) =
+                    f32x4{x[rt][0], x[rt][1], x[rt][2], x[rt][3]};
+            if (i16 == 0)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sX[(16 * rt + 4 * j4 + e) * PE + cl] = x[rt][e];
+                for (int e = 0; e < 4; ++e) sm.sBnd[w][4 * j4 + e] = bnd[e];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (j4 == 0) {
-                float run = bnd;
+                const int cl = 16 * w + i16;
+                float run = sm.sBnd[w][i16];
                 for (int r = C - 1; r >= 0; --r) {
-                    if (r >= nvalid) { put_dg(r, 0.f); continue; }
-                    if (r < nvalid - 1 && ck.doc[r + 1] != ck.doc[r]) run = 0.f;
-                    run += sX[r * PE + cl];
-                    const bool reset = r > 0 ? ck.doc[r] != ck.doc[r - 1] : ck.doc[0] != 0;
-                    put_dg(r, reset ? 0.f : run);
+                    float val = 0.f;
+                    if (r < nvalid) {
+                        if (r < nvalid - 1 && ck.doc[r + 1] != ck.doc[r]) run = 0.f;
+                        run += sX[r * PE + cl];
+                        const bool reset = r > 0 ? ck.doc[r] != ck.doc[r - 1] : ck.doc[0] != 0;
+                        val = reset ? 0.f : run;
+                    }
+                    sX[r * PE + cl] = val;
                 }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int r = 16 * rt + i16;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(sX + r * PE + 16 * w + 4 * j4);
+                const float dg[4] = {v[0], v[1], v[2], v[3]};
+                if (r < nvalid) store4<T>(dgo + (int64_t)r * a.H * DK, dg);
             }
         }
     } else {
         // scalar gate: partial sums over this workgroup's channels; a finisher adds slices
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float y = x[rt][e];
-#pragma unroll
-                for (int d = 1; d < 16; d <<= 1) y += __shfl_xor(y, d, 64);
-                if (i16 == 0) sm.sXs[w][16 * rt + 4 * j4 + e] = y;
-            }
-        float bb = bnd;
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) bb += __shfl_xor(bb, d, 64);
+        for (int rt = 0; rt < 4; ++rt) {
+            float y = x[rt][0] + x[rt][1] + x[rt][2] + x[rt][3];
+            y += __shfl_xor(y, 16, 64);
+            y += __shfl_xor(y, 32, 64);
+            if (j4 == 0) sm.sXs[w][16 * rt + i16] = y;
+        }
+        float bb = bnd[0] + bnd[1] + bnd[2] + bnd[3];
+        bb += __shfl_xor(bb, 16, 64);
+        bb += __shfl_xor(bb, 32, 64);
         if (l == 0) sm.sBs[w] = bb;
-    }
-    __syncthreads();
-
-    // ---- row stores of the staged tiles; scalar-gate partial sums
-    if (staged) {
-        constexpr int VPR = 64 * (int)sizeof(T) / 16;  // 16-byte vectors per 64-channel row
-        for (int idx = threadIdx.x; idx < C * VPR; idx += NT) {
-            const int r = idx / VPR, cv = (idx % VPR) * (16 / (int)sizeof(T));
-            if (r >= nvalid) continue;
-            const int64_t o = ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cs0 + cv;
-            *reinterpret_cast<i32x4*>((T*)a.dq + o) = *reinterpret_cast<const i32x4*>(sOq + r * PB + cv);
-            *reinterpret_cast<i32x4*>((T*)a.dk + o) = *reinterpret_cast<const i32x4*>(sOk + r * PB + cv);
-        }
-    }
-    if constexpr (VEC && Cfg::STAGE) {
-        constexpr int VPR = 64 * (int)sizeof(T) / 16;
-        for (int idx = threadIdx.x; idx < C * VPR; idx += NT) {
-            const int r = idx / VPR, cv = (idx % VPR) * (16 / (int)sizeof(T));
-            if (r >= nvalid) continue;
-            const int64_t o = ((b * T_ + t0 + r) * a.H + h) * DK + cs0 + cv;
-            *reinterpret_cast<i32x4*>((T*)a.dg + o) = *reinterpret_cast<const i32x4*>(sOg + r * PB + cv);
-        }
-    }
-    if constexpr (!VEC) {
+        __syncthreads();
         if (w == 0) {
             const int r = l;
             const float tot = sm.sXs[0][r] + sm.sXs[1][r] + sm.sXs[2][r] + sm.sXs[3][r];
@@ -462,6 +375,8 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
 }
 
 // ============================================================== V role
+// dv computed transposed (rows = value columns n, columns = chunk rows s):
+// lane (i, j) holds row s = 16st + i and the four columns n0s + 16w + 4j + e.
 template <typename T, bool VEC, int DK, int DV>
 __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, int64_t ci, int slice) {
     using Cfg = GradCfg<T, VEC, DK, DV>;
@@ -475,16 +390,14 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
     T* sK = sQ + C * PK;
     T* sG = reinterpret_cast<T*>(lds + Cfg::V_OFF_G);   // vector gate only
     T* sdO = reinterpret_cast<T*>(lds + Cfg::V_OFF_DO); // [r][64 columns of the slice]
-    T* sA = reinterpret_cast<T*>(lds + Cfg::V_OFF_A);   // [r][s]
-    T* sdS = reinterpret_cast<T*>(lds + Cfg::V_OFF_DS); // [c][64 columns], after g is consumed
-    T* sOv = sQ;                                         // staged dv [s][column], after A
+    T* sAT = reinterpret_cast<T*>(lds + Cfg::V_OFF_A);  // A transposed, [s][r]
+    T* sdS = reinterpret_cast<T*>(lds + Cfg::V_OFF_DS); // [c][64 columns] (vector gate: after g is consumed)
     RevChunk& ck = sm.ck;
 
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t G = a.H / a.Hqk, hq = h / G;
     const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
     const int n0s = slice * Cfg::NS;
-    const int n = n0s + 16 * w + i16;  // this lane's value column
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
     const int64_t t0 = ci * C;
@@ -508,12 +421,13 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
 #pragma unroll
     for (int u = 0; u < DK / 64; ++u) pds[u].load(dS1 + (int64_t)u * 64 * DV, DV, 64);
     if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
+    [[maybe_unused]] const TriOnes<T> tri;
 
     pq.store_rows(sQ, PK);
     pk.store_rows(sK, PK);
     if constexpr (VEC) pg.store_rows(sG, PK);
     pdo.store_rows(sdO, PB);
-    if constexpr (!Cfg::DS_IN_G) {
+    if constexpr (!VEC) {
 #pragma unroll
         for (int u = 0; u < DK / 64; ++u) pds[u].store_rows_b64(sdS + u * 64 * PD, PD);
     }
@@ -522,7 +436,7 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
 
     if constexpr (VEC) {
         f32x4 beta[CPW][4];
-        gate_prefix_mfma<T, CPW, PK>(sG, beta);
+        gate_prefix_mfma<T, CPW, PK>(sG, tri, beta);
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc) {
             const int c4 = 16 * (CPW * w + cc) + 4 * j4;
@@ -551,13 +465,14 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
                 for (int e = 0; e < 4; ++e) sm.sEGm[c4 + e] = __expf(Gam[e] - m[e]);
         }
         __syncthreads();
-        if constexpr (Cfg::DS_IN_G) {
+        // dS1 rows scaled by exp(Gamma - m) of their channel, so that KA dS1' = KU dS1
 #pragma unroll
-            for (int u = 0; u < DK / 64; ++u) pds[u].store_rows_b64(sdS + u * 64 * PD, PD);
-        }
+        for (int u = 0; u < DK / 64; ++u) pds[u].scale_rows(&sm.sEGm[64 * u]);
+#pragma unroll
+        for (int u = 0; u < DK / 64; ++u) pds[u].store_rows_b64(sdS + u * 64 * PD, PD);
     }
 
-    // ---- A = QA KA^T on the lower tiles (+ two zero upper tiles) -> sA[r][s]
+    // ---- A = QA KA^T on the lower tiles (+ two zero upper tiles), transposed: sAT[s][r]
     for (int ti = w; ti < 12; ti += 4) {
         const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
         const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
@@ -567,53 +482,28 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
             for (int k0 = 0; k0 < DK; k0 += KS)
                 acc = M::mma(frag_ld<T, PK, 1>(sQ, 16 * rt, k0), frag_ld<T, PK, 1>(sK, 16 * st, k0), acc);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * rt + 4 * j4 + e, s = 16 * st + i16;
-            float x = 0.f;
-            if (ti < 10 && s <= r && ck.doc[s] == ck.doc[r]) {
-                x = acc[e];
-                if constexpr (!VEC) x *= __expf(ck.beta[r] - ck.beta[s]);
-            }
-            sA[r * PB + s] = from_f32<T>(x);
-        }
+        store_masked_T<T, VEC, PB>(sAT, ck, rt, st, ti < 10, acc);
     }
     __syncthreads();
 
-    // ---- dv[s][n] for this wave's 16 columns: A^T dO + [s in last doc] KU dS1,
-    // KU = KA exp(Gamma - m) (vector gate) or k (scalar gate: fu carries the factor)
-    T* dvo = (T*)a.dv;
+    // ---- dv^T = dO^T A + [last doc] dS1'^T KA^T (rows n, columns s)
+    T* dvo = (T*)a.dv + ((b * T_ + t0) * a.H + h) * DV + n0s + 16 * w + 4 * j4;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
         f32x4 a1 = zero4(), a2 = zero4();
         const int kbeg = (16 * st / KS) * KS;
 #pragma unroll
         for (int k0 = kbeg; k0 < C; k0 += KS)
-            a1 = M::mma(frag_col<T, PB, false>(sA, 16 * st, k0), frag_col<T, PB, false>(sdO, 16 * w, k0), a1);
+            a1 = M::mma(frag_col<T, PB, false>(sdO, 16 * w, k0), frag_ld<T, PB, 1>(sAT, 16 * st, k0), a1);
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += KS) {
-            typename M::frag ku = frag_ld<T, PK, 1>(sK, 16 * st, k0);
-            if constexpr (VEC) frag_scale_k<T>(ku, k0, [&](int cc) { return sm.sEGm[cc]; });
-            a2 = M::mma(ku, frag_col<T, PD, false>(sdS, 16 * w, k0), a2);
-        }
-        // dv^T tile: lane n, rows s = 16st + 4*j4 + e
+        for (int k0 = 0; k0 < DK; k0 += KS)
+            a2 = M::mma(frag_col<T, PD, false>(sdS, 16 * w, k0), frag_ld<T, PK, 1>(sK, 16 * st, k0), a2);
+        const int s = 16 * st + i16;
+        const float fu = ck.fu[s];
+        float dv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int s = 16 * st + 4 * j4 + e;
-            const float val = a1[e] + ck.fu[s] * a2[e];
-            if constexpr (Cfg::STAGE) sOv[s * PB + 16 * w + i16] = from_f32<T>(val);
-            else if (s < nvalid) dvo[((b * T_ + t0 + s) * a.H + h) * DV + n] = from_f32<T>(val);
-        }
-    }
-    if constexpr (Cfg::STAGE) {
-        __syncthreads();
-        constexpr int VPR = 64 * (int)sizeof(T) / 16;
-        for (int idx = threadIdx.x; idx < C * VPR; idx += NT) {
-            const int r = idx / VPR, cv = (idx % VPR) * (16 / (int)sizeof(T));
-            if (r >= nvalid) continue;
-            const int64_t o = ((b * T_ + t0 + r) * a.H + h) * DV + n0s + cv;
-            *reinterpret_cast<i32x4*>(dvo + o) = *reinterpret_cast<const i32x4*>(sOv + r * PB + cv);
-        }
+        for (int e = 0; e < 4; ++e) dv[e] = a1[e] + fu * a2[e];
+        if (s < nvalid) store4<T>(dvo + (int64_t)s * a.H * DV, dv);
     }
 }
 

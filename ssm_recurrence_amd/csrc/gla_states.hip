@@ -134,6 +134,7 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC>
         }
     };
     const int64_t nchunks = cend - cbeg;
+    [[maybe_unused]] const TriOnes<T> tri;  // gate prefix operands (vector gate)
     prefetch((REV ? cend - 1 : cbeg) * C);
 
     for (int64_t ii = 0; ii < nchunks; ++ii) {
@@ -167,7 +168,7 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC>
             // per-channel prefix on the matrix cores; KU = k exp(Gamma - beta), last document
             // only (gradient modes: QR = q exp(beta), first document only)
             f32x4 beta[1][4];
-            gate_prefix_mfma<T, 1, PB>(sG, beta);
+            gate_prefix_mfma<T, 1, PB>(sG, tri, beta);
             const int last_reset = sm.sLastReset, first_reset = sm.sFirstReset;
             const int cl = 16 * w + 4 * j4;  // this lane's 4 channels (block-local)
             float Gam[4];

@@ -46,6 +46,19 @@ struct TileRegs {
             }
         }
     }
+    // multiply every element of row `row` by scale[row]
+    __device__ __forceinline__ void scale_rows(const float* scale) {
+#pragma unroll
+        for (int i = 0; i < NVEC; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NV_TOT) {
+                const float f = scale[idx / VPR];
+                T* e = reinterpret_cast<T*>(&r[i]);
+#pragma unroll
+                for (int k = 0; k < VE; ++k) e[k] = (T)((float)e[k] * f);
+            }
+        }
+    }
     // dst[row][col] with pitch P, as 8-byte stores (rows need only 8-byte alignment)
     __device__ __forceinline__ void store_rows_b64(T* dst, int P) const {
 #pragma unroll
@@ -113,6 +126,33 @@ __device__ __forceinline__ int64_t xcd_logical_block(int64_t nblocks) {
     return (x % 8) * (nblocks / 8) + x / 8;
 }
 
+// Operands of the triangular matrix of ones L^T (L[r][u] = [u <= r]) for the
+// chunk-local prefix below, one per (row tile rt, k step): element e of lane
+// (i, j) is [k0 + j*KPL + e <= 16 rt + i].  The same fragment serves as A
+// operand of L and as B operand of L^T.  bf16 keeps the six that a 64-row
+// chunk needs in registers (built once per workgroup); fp32 builds each on use.
+template <typename T> struct TriOnes;
+template <> struct TriOnes<bf16> {
+    bf16x8 f[6];  // (rt, k0) = (0, 0), (1, 0), (2, 0), (2, 32), (3, 0), (3, 32)
+    __device__ __forceinline__ TriOnes() {
+        const int l = lane_id(), i = l & 15, j = l >> 4;
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+            const int rt = q < 2 ? q : 2 + (q - 2) / 2;
+            const int k0 = q < 2 ? 0 : 32 * ((q - 2) % 2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[q][e] = (bf16)(k0 + 8 * j + e <= 16 * rt + i ? 1.0f : 0.0f);
+        }
+    }
+    __device__ __forceinline__ bf16x8 get(int rt, int k0) const { return f[rt < 2 ? rt : 2 + 2 * (rt - 2) + k0 / 32]; }
+};
+template <> struct TriOnes<float> {
+    __device__ __forceinline__ float get(int rt, int k0) const {
+        const int l = lane_id();
+        return k0 + (l >> 4) <= 16 * rt + (l & 15) ? 1.0f : 0.0f;
+    }
+};
+
 // Chunk-local inclusive prefix of the per-channel log gates as one product
 // with a triangular matrix of ones (FLAT page, Pallas Kernels > Gated Linear
 // Attention: a prefix sum is a linear map, so the matrix unit can compute it):
@@ -121,24 +161,19 @@ __device__ __forceinline__ int64_t xcd_logical_block(int64_t nblocks) {
 // row tiles; the result is in C layout with lane (r = 16*rt + l%16) holding
 // channels 16*ct + 4*(l/16) + e.
 template <typename T, int CPW, int PG>
-__device__ __forceinline__ void gate_prefix_mfma(const T* sG, f32x4 (&beta)[CPW][4]) {
+__device__ __forceinline__ void gate_prefix_mfma(const T* sG, const TriOnes<T>& L, f32x4 (&beta)[CPW][4]) {
     using M = Mma<T>;
-    const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
+    const int w = wave_id();
 #pragma unroll
     for (int cc = 0; cc < CPW; ++cc) {
         const int ct = CPW * w + cc;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             f32x4 acc = zero4();
-            const int r = 16 * rt + i16;
             constexpr int KS = M::KSTEP;
 #pragma unroll
-            for (int k0 = 0; k0 < ((16 * (rt + 1) + KS - 1) / KS) * KS; k0 += KS) {
-                typename M::frag lt;
-#pragma unroll
-                for (int e = 0; e < M::KPL; ++e) M::set(lt, e, k0 + j4 * M::KPL + e <= r ? 1.f : 0.f);
-                acc = M::mma(frag_col<T, PG, false>(sG, 16 * ct, k0), lt, acc);
-            }
+            for (int k0 = 0; k0 < ((16 * (rt + 1) + KS - 1) / KS) * KS; k0 += KS)
+                acc = M::mma(frag_col<T, PG, false>(sG, 16 * ct, k0), L.get(rt, k0), acc);
             beta[cc][rt] = acc;
         }
     }
