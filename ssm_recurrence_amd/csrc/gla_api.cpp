@@ -46,12 +46,13 @@ int check_problem(const gla_problem* p) {
 }
 
 // Sequence pieces per (b, h) and chunks per piece.  The sequential passes need
-// enough workgroups to occupy the device: the forward's one per compute unit
-// (256), the backward's paired state and state-gradient passes two per unit
-// (their workgroups are small).  Split only when B * H falls short, and keep
-// at least 8 chunks in a piece so that the summary and combine stay small next
-// to the main passes.
-constexpr int64_t kTargetWG = 256, kTargetWGBwd = 512, kMinPieceChunks = 8;
+// enough workgroups to occupy the device.  Forward: one per compute unit (256)
+// at the widest column slice.  Backward: the paired state and state-gradient
+// passes (small workgroups, up to four per unit) are left unsplit from 512
+// workgroups up, since a split adds a summary walk of the same length; below
+// that they are split towards 1024.  At least 8 chunks stay in a piece so that
+// the combine remains small next to the walks.
+constexpr int64_t kTargetWG = 256, kNoSplitBwd = 512, kTargetWGBwd = 1024, kMinPieceChunks = 8;
 
 struct Split {
     int64_t P = 1, PL = 0;
@@ -70,10 +71,9 @@ Split plan_split(const gla_problem* p, int for_backward) {
         int64_t per_head, target;  // workgroups per (b, h) without a split
         if (for_backward) {
             per_head = 2 * (p->d_k / 64) * (p->d_v / 64);
+            if (bh * per_head >= kNoSplitBwd) return s;
             target = kTargetWGBwd;
         } else {
-            // the forward first narrows its column slices (down to 32 columns)
-            if (bh * (p->d_v / 32) >= kTargetWG) return s;
             per_head = p->d_v / (p->dtype == GLA_BF16 ? 64 : 32);
             target = kTargetWG;
         }

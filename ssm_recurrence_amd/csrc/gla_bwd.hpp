@@ -148,6 +148,15 @@ __device__ __forceinline__ void store_masked_N(T* dst, const RevChunk& ck, int r
     out.store(dst + r * P + s0);
 }
 
+// Four consecutive values of one row of an output, 16 bytes (fp32) or 8 (bf16).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float (&v)[4]) {
+    Vec4<T> x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x.set(e, v[e]);
+    x.store(p);
+}
+
 // element e of an operand fragment, as float
 template <typename T>
 __device__ __forceinline__ float frag_get(const typename Mma<T>::frag& f, int e) {

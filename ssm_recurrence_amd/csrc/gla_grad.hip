@@ -83,15 +83,6 @@ struct GradSmall {
     float sBs[4];
 };
 
-// Four consecutive values of one row of an output, 16 bytes (fp32) or 8 (bf16).
-template <typename T>
-__device__ __forceinline__ void store4(T* p, const float (&v)[4]) {
-    Vec4<T> x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x.set(e, v[e]);
-    x.store(p);
-}
-
 // ============================================================== QK role
 // Outputs are computed transposed (rows = key channels, columns = chunk rows):
 // lane (i, j) of the wave holds rows r = 16rt + i and the four channels
@@ -568,6 +559,8 @@ hipError_t launch_dg_scalar(const RevArgs& a, int nslices, bool bf16_out, hipStr
 
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_grad(const RevArgs& a, hipStream_t st) {
+    // bf16 heads of 128 x 128: one eight-wave workgroup per chunk (every input loaded once)
+    if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128) return launch_grad8<VEC>(a, st);
     using Cfg = GradCfg<T, VEC, DK, DV>;
     const int64_t NC = (a.T + C - 1) / C;
     const int64_t grid = a.B * a.H * NC * (Cfg::NQK + Cfg::NVR);

@@ -1,0 +1,403 @@
+// gla_grad8.hip -- chunk-parallel gradients for bf16 heads with 128 key
+// channels and 128 value columns (gfx950): one workgroup of eight waves per
+// (b, h, chunk).
+//
+// Same per-chunk mathematics as gla_grad.hip (FLAT page, "FLAT: Flash Linear
+// Attention on TPUs", Linear Attention > Backward Recurrence): dq, dk and dg
+// from the intra-chunk scores, the state entering the chunk and the state
+// gradient at its end; dv likewise.  The difference is the work split.  On
+// this device a compute unit pulls requested bytes at about the same rate
+// whether they hit in L2 or not, so duplicate requests cost as much as HBM
+// traffic; the two-role kernel asks for each chunk's q, k, g, v and dO two or
+// three times.  Here one workgroup loads every input of its chunk once (about
+// 144 KB: five 64 x 128 tiles, the state rows and the state-gradient rows) and
+// its eight waves share the products:
+//   phase 1  all tiles to LDS, S0 and dS1 rows of the wave's 16 channels to registers;
+//   phase 2  gate prefix and the q, k scaling for the wave's 16 channels, the
+//            scaled dS1 rows to LDS, dA tiles; then A tiles;
+//   phase 3  dq, dk (and the log-gate gradient) for the wave's 16 key channels,
+//            dv for its 16 value columns.
+// The scalar gate's log-gate gradient sums over all 128 channels, which are
+// all in this workgroup, so it is finished here too.
+#include "gla_bwd.hpp"
+#include "gla_common.hpp"
+#include "gla_kernels.hpp"
+#include "gla_tile.hpp"
+
+namespace gla {
+
+template <bool VEC>
+struct Grad8Cfg {
+    using T = bf16;
+    static constexpr int NW = 8, NTH = 64 * NW;
+    static constexpr int DK = 128, DV = 128;
+    static constexpr int P = Pitch16<T>::of(128);  // [rows][128] tiles
+    static constexpr int PB = Pitch16<T>::of(64);  // [64][64] score tiles
+    static constexpr int PE = 132;                 // fp32 [64][128] dg scratch
+    static constexpr int TILE = C * P * 2;
+    static constexpr int OFF_Q = 0, OFF_K = TILE, OFF_G = 2 * TILE;
+    static constexpr int OFF_V = OFF_G + (VEC ? TILE : 0);
+    static constexpr int OFF_DO = OFF_V + TILE;
+    static constexpr int OFF_DA = OFF_DO + TILE;   // dA [r][s]
+    static constexpr int OFF_AT = OFF_DA + C * PB * 2;  // A^T [s][r]
+    static constexpr int OFF_DS = OFF_AT + C * PB * 2;  // dS1' [c][n]
+    static constexpr int BYTES = OFF_DS + DK * P * 2;
+    static_assert(2 * TILE >= C * PE * 4, "dg scratch does not fit in the v / dO region");
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
+    using T = bf16;
+    using Cfg = Grad8Cfg<VEC>;
+    using M = Mma<T>;
+    constexpr int P = Cfg::P, PB = Cfg::PB, PE = Cfg::PE, DK = 128, DV = 128;
+    constexpr int NTH = Cfg::NTH, KS = M::KSTEP, NKV = DV / KS;
+
+    __shared__ __attribute__((aligned(16))) char lds[Cfg::BYTES];
+    __shared__ RevChunk ck;
+    __shared__ float sXs[8][C];
+    __shared__ float sBs[8];
+    __shared__ float sBnd[8][16];
+    T* sQ = reinterpret_cast<T*>(lds + Cfg::OFF_Q);
+    T* sK = reinterpret_cast<T*>(lds + Cfg::OFF_K);
+    T* sG = reinterpret_cast<T*>(lds + Cfg::OFF_G);  // vector gate only
+    T* sV = reinterpret_cast<T*>(lds + Cfg::OFF_V);
+    T* sdO = reinterpret_cast<T*>(lds + Cfg::OFF_DO);
+    T* sdA = reinterpret_cast<T*>(lds + Cfg::OFF_DA);
+    T* sAT = reinterpret_cast<T*>(lds + Cfg::OFF_AT);
+    T* sdS = reinterpret_cast<T*>(lds + Cfg::OFF_DS);
+    float* sX = reinterpret_cast<float*>(lds + Cfg::OFF_V);  // dg scratch [r][c], after dv
+
+    const int64_t T_ = a.T;
+    const int64_t NC = (T_ + C - 1) / C;
+    const int64_t L = xcd_logical_block(a.B * a.H * NC);
+    const int64_t ci = L % NC, bh = L / NC;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t G = a.H / a.Hqk, hq = h / G;
+    const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
+    const int cw = 16 * w;  // the wave's key channels (dq, dk, dg) and value columns (dv)
+    const int64_t t0 = ci * C;
+    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_g = VEC ? a.H * DK : a.H;
+    const T* qrow = (const T*)a.q + (b * T_ + t0) * rs_qk + hq * DK;
+    const T* krow = (const T*)a.k + (b * T_ + t0) * rs_qk + hq * DK;
+    const T* vrow = (const T*)a.v + (b * T_ + t0) * rs_v + h * DV;
+    const T* dorow = (const T*)a.dO + (b * T_ + t0) * rs_v + h * DV;
+    const T* grow = (const T*)a.g + (b * T_ + t0) * rs_g + (VEC ? h * DK : h);
+    // rows cw + i of S0 and dS1 (the A operands of dO S0^T and v dS1^T, k = n)
+    const T* S0 = (const T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
+    const T* dS1 = (const T*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
+
+    // ---- phase 1: loads
+    TileRegs<T, 128, NTH> pq, pk, pg, pv, pdo;
+    RowRegs rr;
+    pq.load(qrow, rs_qk, nvalid);
+    pk.load(krow, rs_qk, nvalid);
+    if constexpr (VEC) pg.load(grow, rs_g, nvalid);
+    pv.load(vrow, rs_v, nvalid);
+    pdo.load(dorow, rs_v, nvalid);
+    if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
+    bf16x8 s0f[NKV], dsf[NKV];
+#pragma unroll
+    for (int kk = 0; kk < NKV; ++kk) {
+        s0f[kk] = *reinterpret_cast<const bf16x8*>(S0 + kk * KS + 8 * j4);
+        dsf[kk] = *reinterpret_cast<const bf16x8*>(dS1 + kk * KS + 8 * j4);
+    }
+    [[maybe_unused]] const TriOnes<T> tri;
+
+    pq.store_rows(sQ, P);
+    pk.store_rows(sK, P);
+    if constexpr (VEC) pg.store_rows(sG, P);
+    pv.store_rows(sV, P);
+    pdo.store_rows(sdO, P);
+    if constexpr (!VEC) {
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk)
+            *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = dsf[kk];
+    }
+    if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
+    float sd = 0.f;  // rowsum(S0 * dS1) of channel cw + i16 over this lane's n
+#pragma unroll
+    for (int kk = 0; kk < NKV; ++kk) sd = frag_dot(s0f[kk], dsf[kk], sd);
+    __syncthreads();
+
+    // ---- phase 2: gate prefix, scaling, dS1' rows, dA
+    // raw q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e)
+    Vec4<T> qraw[4], kraw[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        qraw[rt] = Vec4<T>::load(sQ + (16 * rt + i16) * P + cw + 4 * j4);
+        kraw[rt] = Vec4<T>::load(sK + (16 * rt + i16) * P + cw + 4 * j4);
+    }
+    float E[4][4];
+    float em[4], egm[4], dec[4];
+    if constexpr (VEC) {
+        f32x4 beta[1][4];
+        gate_prefix_mfma<T, 1, P>(sG, tri, beta);  // channel tile w
+        float m[4], Gam[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            m[e] = __shfl(beta[0][1][e], 16 * j4 + 15, 64);
+            Gam[e] = __shfl(beta[0][3][e], 16 * j4 + 15, 64);
+        }
+        const bool reset_in_chunk = ck.last_reset >= 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            em[e] = __expf(m[e]);
+            egm[e] = __expf(Gam[e] - m[e]);
+            dec[e] = reset_in_chunk ? 0.f : __expf(Gam[e]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            Vec4<T> qa, ka;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                E[rt][e] = __expf(beta[0][rt][e] - m[e]);
+                qa.set(e, qraw[rt].get(e) * E[rt][e]);
+                ka.set(e, kraw[rt].get(e) * __builtin_amdgcn_rcpf(E[rt][e]));
+            }
+            qa.store(sQ + (16 * rt + i16) * P + cw + 4 * j4);
+            ka.store(sK + (16 * rt + i16) * P + cw + 4 * j4);
+        }
+        // dS1 rows of this wave's channels scaled by exp(Gamma - m) of the channel
+        // (KA dS1' = KU dS1 for dv); lane i16 holds channel cw + i16, whose prefix
+        // values sit in lane (i16 / 4, 15), element i16 % 4
+        float mi = 0.f, gi = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float mv = __shfl(beta[0][1][e], 16 * (i16 >> 2) + 15, 64);
+            const float gv = __shfl(beta[0][3][e], 16 * (i16 >> 2) + 15, 64);
+            if ((i16 & 3) == e) {
+                mi = mv;
+                gi = gv;
+            }
+        }
+        const float egm_i = __expf(gi - mi);
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) {
+            bf16x8 d = dsf[kk];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[e] = (bf16)((float)d[e] * egm_i);
+            *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = d;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            em[e] = egm[e] = 1.f;
+            dec[e] = ck.decay;
+        }
+    }
+    // dA^T = v dO^T tiles, masked, stored as dA[r][s] (10 lower + 2 zero upper tiles)
+    for (int ti = w; ti < 12; ti += Cfg::NW) {
+        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
+        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+        f32x4 acc = zero4();
+        if (ti < 10) {
+#pragma unroll
+            for (int n0 = 0; n0 < DV; n0 += KS)
+                acc = M::mma(frag_ld<T, P, 1>(sV, 16 * st, n0), frag_ld<T, P, 1>(sdO, 16 * rt, n0), acc);
+        }
+        store_masked_N<T, VEC, PB>(sdA, ck, rt, st, ti < 10, acc);
+    }
+    __syncthreads();
+    // A = QA KA^T tiles (all channels, now scaled), masked, stored transposed A^T[s][r]
+    for (int ti = w; ti < 12; ti += Cfg::NW) {
+        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
+        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+        f32x4 acc = zero4();
+        if (ti < 10) {
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += KS)
+                acc = M::mma(frag_ld<T, P, 1>(sQ, 16 * rt, k0), frag_ld<T, P, 1>(sK, 16 * st, k0), acc);
+        }
+        store_masked_T<T, VEC, PB>(sAT, ck, rt, st, ti < 10, acc);
+    }
+
+    // ---- phase 3a: dq, dk for key channels cw .. cw + 15 (computed transposed)
+    const bool gqa = G > 1;
+    float x[4][4];  // q*dq - k*dk
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        f32x4 a1 = zero4(), a2 = zero4();
+        const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
+#pragma unroll
+        for (int k0 = 0; k0 < kend; k0 += KS)
+            a1 = M::mma(frag_col<T, P, false>(sK, cw, k0), frag_ld<T, PB, 1>(sdA, 16 * rt, k0), a1);
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) a2 = M::mma(s0f[kk], frag_ld<T, P, 1>(sdO, 16 * rt, kk * KS), a2);
+        const int r = 16 * rt + i16;
+        const float fq = ck.fq[r];
+        float dq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float dqp = a1[e] + fq * em[e] * a2[e];
+            dq[e] = VEC ? E[rt][e] * dqp : dqp;
+            x[rt][e] = qraw[rt].get(e) * dq[e];
+        }
+        if (r < nvalid) {
+            if (!gqa) store4<T>((T*)a.dq + ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4, dq);
+            else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
+        }
+    }
+    float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        f32x4 a1 = zero4(), a2 = zero4();
+        const int kbeg = (16 * st / KS) * KS;
+#pragma unroll
+        for (int k0 = kbeg; k0 < C; k0 += KS)
+            a1 = M::mma(frag_col<T, P, false>(sQ, cw, k0), frag_col<T, PB, false>(sdA, 16 * st, k0), a1);
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) a2 = M::mma(dsf[kk], frag_ld<T, P, 1>(sV, 16 * st, kk * KS), a2);
+        const int s = 16 * st + i16;
+        const float fu = ck.fu[s];
+        float dk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float inter = fu * egm[e] * a2[e];
+            const float rE = VEC ? __builtin_amdgcn_rcpf(E[st][e]) : 1.f;
+            const float kr = kraw[st].get(e);
+            dk[e] = (a1[e] + inter) * rE;
+            x[st][e] -= kr * dk[e];
+            bsum[e] += kr * inter * rE;
+        }
+        if (s < nvalid) {
+            if (!gqa) store4<T>((T*)a.dk + ((b * T_ + t0 + s) * a.Hqk + hq) * DK + cw + 4 * j4, dk);
+            else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
+        }
+    }
+    // boundary term rowsum(S1 * dS1) per channel cw + 4j4 + e
+    sd += __shfl_xor(sd, 16, 64);
+    sd += __shfl_xor(sd, 32, 64);
+    float bnd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bnd[e] = dec[e] * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
+    __syncthreads();  // A^T complete
+
+    // ---- phase 3b: dv^T = dO^T A + [last doc] dS1'^T KA^T for value columns cw .. cw + 15
+    {
+        T* dvo = (T*)a.dv + ((b * T_ + t0) * a.H + h) * DV + cw + 4 * j4;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            f32x4 a1 = zero4(), a2 = zero4();
+            const int kbeg = (16 * st / KS) * KS;
+#pragma unroll
+            for (int k0 = kbeg; k0 < C; k0 += KS)
+                a1 = M::mma(frag_col<T, P, false>(sdO, cw, k0), frag_ld<T, PB, 1>(sAT, 16 * st, k0), a1);
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += KS)
+                a2 = M::mma(frag_col<T, P, false>(sdS, cw, k0), frag_ld<T, P, 1>(sK, 16 * st, k0), a2);
+            const int s = 16 * st + i16;
+            const float fu = ck.fu[s];
+            float dv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv[e] = a1[e] + fu * a2[e];
+            if (s < nvalid) store4<T>(dvo + (int64_t)s * a.H * DV, dv);
+        }
+    }
+
+    // ---- phase 3c: log-gate gradient
+    if constexpr (VEC) {
+        T* dgo = (T*)a.dg + ((b * T_ + t0) * a.H + h) * DK + cw + 4 * j4;
+        if (ck.first_reset == C) {
+            float carry[4] = {bnd[0], bnd[1], bnd[2], bnd[3]};
+#pragma unroll
+            for (int rt = 3; rt >= 0; --rt) {
+                float dg[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = row_suffix16(x[rt][e]);
+                    dg[e] = y + carry[e];
+                    carry[e] += __shfl(y, 0, 16);
+                }
+                const int r = 16 * rt + i16;
+                if (r < nvalid) store4<T>(dgo + (int64_t)r * a.H * DK, dg);
+            }
+        } else {
+            // documents inside the chunk: serial segmented suffix sum per channel, in the
+            // scratch that takes the place of v and dO
+            __syncthreads();
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                *reinterpret_cast<f32x4*>(sX + (16 * rt + i16) * PE + cw + 4 * j4) =
+                    f32x4{x[rt][0], x[rt][1], x[rt][2], x[rt][3]};
+            if (i16 == 0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sBnd[w][4 * j4 + e] = bnd[e];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (j4 == 0) {
+                const int c = cw + i16;
+                float run = sBnd[w][i16];
+                for (int r = C - 1; r >= 0; --r) {
+                    float val = 0.f;
+                    if (r < nvalid) {
+                        if (r < nvalid - 1 && ck.doc[r + 1] != ck.doc[r]) run = 0.f;
+                        run += sX[r * PE + c];
+                        const bool reset = r > 0 ? ck.doc[r] != ck.doc[r - 1] : ck.doc[0] != 0;
+                        val = reset ? 0.f : run;
+                    }
+                    sX[r * PE + c] = val;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int r = 16 * rt + i16;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(sX + r * PE + cw + 4 * j4);
+                const float dg[4] = {v[0], v[1], v[2], v[3]};
+                if (r < nvalid) store4<T>(dgo + (int64_t)r * a.H * DK, dg);
+            }
+        }
+    } else {
+        // scalar gate: sum over all 128 channels of this workgroup, then a segmented
+        // suffix sum over the chunk rows (documents end where the next row resets)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            float y = x[rt][0] + x[rt][1] + x[rt][2] + x[rt][3];
+            y += __shfl_xor(y, 16, 64);
+            y += __shfl_xor(y, 32, 64);
+            if (j4 == 0) sXs[w][16 * rt + i16] = y;
+        }
+        float bb = bnd[0] + bnd[1] + bnd[2] + bnd[3];
+        bb += __shfl_xor(bb, 16, 64);
+        bb += __shfl_xor(bb, 32, 64);
+        if (l == 0) sBs[w] = bb;
+        __syncthreads();
+        if (w == 0) {
+            const int r = l;
+            float xt = 0.f, bt = 0.f;
+#pragma unroll
+            for (int u = 0; u < Cfg::NW; ++u) {
+                xt += sXs[u][r];
+                bt += sBs[u];
+            }
+            const int doc = ck.doc[r];
+            float run = (r < nvalid ? xt : 0.f) + (r == nvalid - 1 ? bt : 0.f);
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float y = __shfl_down(run, d, 64);
+                const int dd = __shfl_down(doc, d, 64);
+                if (r + d < 64 && dd == doc) run += y;
+            }
+            const bool reset = r > 0 ? doc != ck.doc[r - 1] : doc != 0;
+            if (r < nvalid) ((T*)a.dg)[(b * T_ + t0 + r) * a.H + h] = from_f32<T>(reset ? 0.f : run);
+        }
+    }
+}
+
+template <bool VEC>
+hipError_t launch_grad8(const RevArgs& a, hipStream_t st) {
+    const int64_t NC = (a.T + C - 1) / C;
+    hipLaunchKernelGGL((k_grad8<VEC>), dim3((unsigned)(a.B * a.H * NC)), dim3(Grad8Cfg<VEC>::NTH), 0, st, a);
+    return hipGetLastError();
+}
+
+template hipError_t launch_grad8<false>(const RevArgs&, hipStream_t);
+template hipError_t launch_grad8<true>(const RevArgs&, hipStream_t);
+
+}  // namespace gla

@@ -58,6 +58,10 @@ hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st);
 // scalar gate: dg from the per-slice partial sums (one wave per chunk)
 hipError_t launch_dg_scalar(const RevArgs& a, int nslices, bool bf16_out, hipStream_t st);
 
+// bf16, d_k = d_v = 128: one eight-wave workgroup per chunk (scalar dg finished in-kernel)
+template <bool VEC>
+hipError_t launch_grad8(const RevArgs& a, hipStream_t st);
+
 // chunk-parallel gradients from the per-chunk states and state gradients
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_grad(const RevArgs& a, hipStream_t st);

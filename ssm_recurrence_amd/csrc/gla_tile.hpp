@@ -15,19 +15,19 @@ template <typename T> struct Pitch16 {
     static constexpr int of(int d) { return d + pad; }
 };
 
-template <typename T, int D>
+template <typename T, int D, int NTH = NT>
 struct TileRegs {
     static constexpr int VE = 16 / (int)sizeof(T);   // elements per 16-byte vector
     static constexpr int VPR = D / VE;                // vectors per row
     static constexpr int NV_TOT = C * VPR;            // vectors per tile
-    static constexpr int NVEC = (NV_TOT + NT - 1) / NT;
+    static constexpr int NVEC = (NV_TOT + NTH - 1) / NTH;
     i32x4 r[NVEC];
 
     // rows t0.. of a row-major tensor (row stride rs elements); rows >= nvalid read as zero
     __device__ __forceinline__ void load(const T* src, int64_t rs, int nvalid) {
 #pragma unroll
         for (int i = 0; i < NVEC; ++i) {
-            const int idx = threadIdx.x + i * NT;
+            const int idx = threadIdx.x + i * NTH;
             const int row = idx / VPR, cv = (idx % VPR) * VE;
             i32x4 z = {0, 0, 0, 0};
             r[i] = z;
@@ -39,7 +39,7 @@ struct TileRegs {
     __device__ __forceinline__ void store_rows(T* dst, int P) const {
 #pragma unroll
         for (int i = 0; i < NVEC; ++i) {
-            const int idx = threadIdx.x + i * NT;
+            const int idx = threadIdx.x + i * NTH;
             if (idx < NV_TOT) {
                 const int row = idx / VPR, cv = (idx % VPR) * VE;
                 *reinterpret_cast<i32x4*>(dst + row * P + cv) = r[i];
@@ -50,7 +50,7 @@ struct TileRegs {
     __device__ __forceinline__ void scale_rows(const float* scale) {
 #pragma unroll
         for (int i = 0; i < NVEC; ++i) {
-            const int idx = threadIdx.x + i * NT;
+            const int idx = threadIdx.x + i * NTH;
             if (idx < NV_TOT) {
                 const float f = scale[idx / VPR];
                 T* e = reinterpret_cast<T*>(&r[i]);
@@ -63,7 +63,7 @@ struct TileRegs {
     __device__ __forceinline__ void store_rows_b64(T* dst, int P) const {
 #pragma unroll
         for (int i = 0; i < NVEC; ++i) {
-            const int idx = threadIdx.x + i * NT;
+            const int idx = threadIdx.x + i * NTH;
             if (idx < NV_TOT) {
                 const int row = idx / VPR, cv = (idx % VPR) * VE;
                 typedef __attribute__((__vector_size__(8))) int i32x2;
@@ -77,7 +77,7 @@ struct TileRegs {
     __device__ __forceinline__ void store_cols(T* dst, int P) const {
 #pragma unroll
         for (int i = 0; i < NVEC; ++i) {
-            const int idx = threadIdx.x + i * NT;
+            const int idx = threadIdx.x + i * NTH;
             if (idx < NV_TOT) {
                 const int row = idx / VPR, cv = (idx % VPR) * VE;
                 const T* e = reinterpret_cast<const T*>(&r[i]);
