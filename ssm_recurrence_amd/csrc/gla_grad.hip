@@ -561,6 +561,8 @@ template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_grad(const RevArgs& a, hipStream_t st) {
     // bf16 heads of 128 x 128: one eight-wave workgroup per chunk (every input loaded once)
     if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128) return launch_grad8<VEC>(a, st);
+    // fp32, scalar gate, 128 x 128: fp32 products as three bf16 matrix-core products
+    if constexpr (sizeof(T) == 4 && !VEC && DK == 128 && DV == 128) return launch_grad_f32s(a, st);
     using Cfg = GradCfg<T, VEC, DK, DV>;
     const int64_t NC = (a.T + C - 1) / C;
     const int64_t grid = a.B * a.H * NC * (Cfg::NQK + Cfg::NVR);

@@ -1,0 +1,390 @@
+// gla_grad_f32s.hip -- chunk-parallel gradients for fp32 inputs with the scalar
+// gate and 128 x 128 heads (gfx950), on the bf16 matrix cores.
+//
+// Every fp32 operand x is held as two bf16 values, hi = bf16(x) and
+// lo = bf16(x - hi), so that x = hi + lo to about 2^-17 relative, and each
+// fp32 product a b is taken as lo_a hi_b + hi_a lo_b + hi_a hi_b (three bf16
+// matrix-core products into one fp32 accumulator; the dropped lo_a lo_b is
+// below 2^-16 of the product).  Three bf16 products cost about a fifth of one
+// fp32 matrix-core product on this device.  The FLAT page ("FLAT: Flash Linear
+// Attention on TPUs", Pallas Kernels > Backward Kernels, the gate-gradient
+// item) splits an fp32 input into two bf16 halves for the same reason, to keep
+// fp32 accuracy on a bf16 matrix unit.
+//
+// The mathematics and the two kinds of workgroups are those of gla_grad.hip
+// (QK: dq, dk and the log-gate partial sums for 64 key channels; V: dv for 64
+// value columns), with every LDS tile stored as a hi plane followed by a lo
+// plane; inputs, outputs and all accumulation stay fp32.
+#include "gla_bwd.hpp"
+#include "gla_common.hpp"
+#include "gla_kernels.hpp"
+#include "gla_tile.hpp"
+
+namespace gla {
+
+namespace {
+
+struct SFrag {
+    bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ f32x4 mma3(const SFrag& a, const SFrag& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split1(float x, bf16& hi, bf16& lo) {
+    hi = (bf16)x;
+    lo = (bf16)(x - (float)hi);
+}
+
+// operand fragments of a split tile (hi plane at base, lo plane PLANE elements later)
+template <int P, int PLANE>
+__device__ __forceinline__ SFrag sld(const bf16* base, int i0, int k0) {
+    return SFrag{frag_ld<bf16, P, 1>(base, i0, k0), frag_ld<bf16, P, 1>(base + PLANE, i0, k0)};
+}
+template <int P, int PLANE>
+__device__ __forceinline__ SFrag scol(const bf16* base, int i0, int k0) {
+    return SFrag{frag_col<bf16, P, false>(base, i0, k0), frag_col<bf16, P, false>(base + PLANE, i0, k0)};
+}
+
+// eight consecutive fp32 values from global memory as a split fragment
+__device__ __forceinline__ SFrag split_ld8(const float* p, float& dot_with, const float* q) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    SFrag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bf16 h, o;
+        split1(a[e], h, o);
+        f.hi[e] = h;
+        f.lo[e] = o;
+        split1(b[e], h, o);
+        f.hi[4 + e] = h;
+        f.lo[4 + e] = o;
+    }
+    if (q) {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(q);
+        const f32x4 d = *reinterpret_cast<const f32x4*>(q + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dot_with += a[e] * c[e] + b[e] * d[e];
+    }
+    return f;
+}
+
+// fp32 tile rows from registers to a split LDS tile (8-byte stores per plane)
+template <int D>
+__device__ __forceinline__ void store_rows_split(const TileRegs<float, D>& t, bf16* dst, int P, int PLANE) {
+    using TR = TileRegs<float, D>;
+#pragma unroll
+    for (int i = 0; i < TR::NVEC; ++i) {
+        const int idx = threadIdx.x + i * NT;
+        if (idx < TR::NV_TOT) {
+            const int row = idx / TR::VPR, cv = (idx % TR::VPR) * 4;
+            const float* f = reinterpret_cast<const float*>(&t.r[i]);
+            Vec4<bf16> hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bf16 h, o;
+                split1(f[e], h, o);
+                hi.v[e] = h;
+                lo.v[e] = o;
+            }
+            hi.store(dst + row * P + cv);
+            lo.store(dst + PLANE + row * P + cv);
+        }
+    }
+}
+
+// masked score tile (scalar gate: times exp(beta_r - beta_s)) to a split tile;
+// NAT: the tile was computed transposed (rows s, column r) and is stored [r][s];
+// otherwise computed [r][s] (rows r, column s) and stored transposed [s][r]
+template <bool NAT, int P, int PLANE>
+__device__ __forceinline__ void store_masked_split(bf16* dst, const RevChunk& ck, int rt, int st, bool live,
+                                                   const f32x4& acc) {
+    const int l = lane_id(), j = l >> 4, i = l & 15;
+    const int row = NAT ? 16 * rt + i : 16 * st + i;          // stored row (r, or s)
+    const int c0 = NAT ? 16 * st + 4 * j : 16 * rt + 4 * j;   // first of four stored columns
+    Vec4<bf16> hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = NAT ? row : c0 + e, s = NAT ? c0 + e : row;
+        float x = 0.f;
+        if (live && s <= r && ck.doc[s] == ck.doc[r]) x = acc[e] * __expf(ck.beta[r] - ck.beta[s]);
+        bf16 h, o;
+        split1(x, h, o);
+        hi.v[e] = h;
+        lo.v[e] = o;
+    }
+    hi.store(dst + row * P + c0);
+    lo.store(dst + PLANE + row * P + c0);
+}
+
+constexpr int DK = 128, DV = 128, KS = 32;
+constexpr int P64 = 72, PL64 = C * P64;                  // [64][64] split tiles
+constexpr int PW = 136, PLW = C * PW;                    // [64][128] split tiles
+constexpr int PD = 68, PLD = DK * PD;                    // [128][64] split tile (state-gradient slice)
+constexpr int QK_BYTES = 2 * (3 * PL64 + 2 * PLW) * 2;
+constexpr int V_BYTES = 2 * (2 * PLW + 2 * PL64 + PLD) * 2;
+constexpr int BYTES = QK_BYTES > V_BYTES ? QK_BYTES : V_BYTES;
+
+struct SmallS {
+    RevChunk ck;
+    float sXs[4][C];
+    float sBs[4];
+};
+
+// ============================================================== QK role
+__device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t ci, int slice) {
+    bf16* sQ = reinterpret_cast<bf16*>(lds);
+    bf16* sK = sQ + 2 * PL64;
+    bf16* sdA = sK + 2 * PL64;  // [r][s]
+    bf16* sdO = sdA + 2 * PL64;
+    bf16* sV = sdO + 2 * PLW;
+    RevChunk& ck = sm.ck;
+
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t G = a.H / a.Hqk, hq = h / G;
+    const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
+    const int cs0 = slice * 64;
+    const int cw = cs0 + 16 * w;
+    const int64_t T_ = a.T;
+    const int64_t NC = (T_ + C - 1) / C;
+    const int64_t t0 = ci * C;
+    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const float* qrow = (const float*)a.q + (b * T_ + t0) * rs_qk + hq * DK + cs0;
+    const float* krow = (const float*)a.k + (b * T_ + t0) * rs_qk + hq * DK + cs0;
+    const float* vrow = (const float*)a.v + (b * T_ + t0) * rs_v + h * DV;
+    const float* dorow = (const float*)a.dO + (b * T_ + t0) * rs_v + h * DV;
+    const float* grow = (const float*)a.g + (b * T_ + t0) * a.H + h;
+    const float* S0 = (const float*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
+    const float* dS1 = (const float*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
+
+    TileRegs<float, 64> pq, pk;
+    TileRegs<float, DV> pv, pdo;
+    RowRegs rr;
+    pq.load(qrow, rs_qk, nvalid);
+    pk.load(krow, rs_qk, nvalid);
+    pv.load(vrow, rs_v, nvalid);
+    pdo.load(dorow, rs_v, nvalid);
+    if (w == 0) rr.load(grow, a.H, a.seg, b, T_, t0, nvalid, true);
+    // raw q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e)
+    f32x4 qraw[4], kraw[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * rt + i16;
+        qraw[rt] = zero4();
+        kraw[rt] = zero4();
+        if (r < nvalid) {
+            qraw[rt] = *reinterpret_cast<const f32x4*>(qrow + r * rs_qk + 16 * w + 4 * j4);
+            kraw[rt] = *reinterpret_cast<const f32x4*>(krow + r * rs_qk + 16 * w + 4 * j4);
+        }
+    }
+    // S0 and dS1 rows cw + i16 as split A operands (k = n); rowsum(S0 * dS1) in fp32
+    float sd = 0.f;
+    SFrag s0f[DV / KS], dsf[DV / KS];
+#pragma unroll
+    for (int kk = 0; kk < DV / KS; ++kk) {
+        float unused = 0.f;
+        s0f[kk] = split_ld8(S0 + kk * KS + 8 * j4, sd, dS1 + kk * KS + 8 * j4);
+        dsf[kk] = split_ld8(dS1 + kk * KS + 8 * j4, unused, nullptr);
+    }
+
+    store_rows_split<64>(pq, sQ, P64, PL64);
+    store_rows_split<64>(pk, sK, P64, PL64);
+    store_rows_split<DV>(pv, sV, PW, PLW);
+    store_rows_split<DV>(pdo, sdO, PW, PLW);
+    if (w == 0) rev_chunk_info<float, false>(&ck, rr);
+    __syncthreads();
+
+    // dA^T = v dO^T tiles, masked, stored dA[r][s]
+    for (int ti = w; ti < 12; ti += 4) {
+        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
+        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+        f32x4 acc = zero4();
+        if (ti < 10) {
+#pragma unroll
+            for (int n0 = 0; n0 < DV; n0 += KS)
+                acc = mma3(sld<PW, PLW>(sV, 16 * st, n0), sld<PW, PLW>(sdO, 16 * rt, n0), acc);
+        }
+        store_masked_split<true, P64, PL64>(sdA, ck, rt, st, ti < 10, acc);
+    }
+    __syncthreads();
+
+    const bool gqa = G > 1;
+    float x[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        f32x4 a1 = zero4(), a2 = zero4();
+        const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
+#pragma unroll
+        for (int k0 = 0; k0 < kend; k0 += KS)
+            a1 = mma3(scol<P64, PL64>(sK, 16 * w, k0), sld<P64, PL64>(sdA, 16 * rt, k0), a1);
+#pragma unroll
+        for (int kk = 0; kk < DV / KS; ++kk) a2 = mma3(s0f[kk], sld<PW, PLW>(sdO, 16 * rt, kk * KS), a2);
+        const int r = 16 * rt + i16;
+        const float fq = ck.fq[r];
+        float dq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dq[e] = a1[e] + fq * a2[e];
+            x[rt][e] = qraw[rt][e] * dq[e];
+        }
+        if (r < nvalid) {
+            if (!gqa) store4<float>((float*)a.dq + ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4, dq);
+            else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
+        }
+    }
+    float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        f32x4 a1 = zero4(), a2 = zero4();
+        const int kbeg = (16 * st / KS) * KS;
+#pragma unroll
+        for (int k0 = kbeg; k0 < C; k0 += KS)
+            a1 = mma3(scol<P64, PL64>(sQ, 16 * w, k0), scol<P64, PL64>(sdA, 16 * st, k0), a1);
+#pragma unroll
+        for (int kk = 0; kk < DV / KS; ++kk) a2 = mma3(dsf[kk], sld<PW, PLW>(sV, 16 * st, kk * KS), a2);
+        const int s = 16 * st + i16;
+        const float fu = ck.fu[s];
+        float dk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float inter = fu * a2[e];
+            dk[e] = a1[e] + inter;
+            x[st][e] -= kraw[st][e] * dk[e];
+            bsum[e] += kraw[st][e] * inter;
+        }
+        if (s < nvalid) {
+            if (!gqa) store4<float>((float*)a.dk + ((b * T_ + t0 + s) * a.Hqk + hq) * DK + cw + 4 * j4, dk);
+            else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
+        }
+    }
+    sd += __shfl_xor(sd, 16, 64);
+    sd += __shfl_xor(sd, 32, 64);
+    float bb = 0.f;  // sum over this lane group's four channels of rowsum(S1 * dS1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bb += ck.decay * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
+    // partial sums over this workgroup's channels; a finisher adds the two slices
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        float y = x[rt][0] + x[rt][1] + x[rt][2] + x[rt][3];
+        y += __shfl_xor(y, 16, 64);
+        y += __shfl_xor(y, 32, 64);
+        if (j4 == 0) sm.sXs[w][16 * rt + i16] = y;
+    }
+    bb += __shfl_xor(bb, 16, 64);
+    bb += __shfl_xor(bb, 32, 64);
+    if (l == 0) sm.sBs[w] = bb;
+    __syncthreads();
+    if (w == 0) {
+        const int r = l;
+        const float tot = sm.sXs[0][r] + sm.sXs[1][r] + sm.sXs[2][r] + sm.sXs[3][r];
+        if (r < nvalid) a.ws_xs[(bh * 2 + slice) * T_ + t0 + r] = tot;
+        if (r == 0) a.ws_bnd[(bh * 2 + slice) * NC + ci] = sm.sBs[0] + sm.sBs[1] + sm.sBs[2] + sm.sBs[3];
+    }
+}
+
+// ============================================================== V role
+__device__ void sv(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t ci, int slice) {
+    bf16* sQ = reinterpret_cast<bf16*>(lds);
+    bf16* sK = sQ + 2 * PLW;
+    bf16* sdO = sK + 2 * PLW;   // [r][64 columns of the slice]
+    bf16* sAT = sdO + 2 * PL64; // [s][r]
+    bf16* sdS = sAT + 2 * PL64; // [c][64 columns]
+    RevChunk& ck = sm.ck;
+
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t G = a.H / a.Hqk, hq = h / G;
+    const int w = wave_id(), j4 = lane_id() >> 4, i16 = lane_id() & 15;
+    const int n0s = slice * 64;
+    const int64_t T_ = a.T;
+    const int64_t NC = (T_ + C - 1) / C;
+    const int64_t t0 = ci * C;
+    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const float* qrow = (const float*)a.q + (b * T_ + t0) * rs_qk + hq * DK;
+    const float* krow = (const float*)a.k + (b * T_ + t0) * rs_qk + hq * DK;
+    const float* dorow = (const float*)a.dO + (b * T_ + t0) * rs_v + h * DV + n0s;
+    const float* grow = (const float*)a.g + (b * T_ + t0) * a.H + h;
+    const float* dS1 = (const float*)a.ws_dS + (bh * NC + ci) * DK * DV + n0s;
+
+    {
+        TileRegs<float, DK> pq, pk;
+        TileRegs<float, 64> pdo, pds0, pds1;
+        RowRegs rr;
+        pq.load(qrow, rs_qk, nvalid);
+        pk.load(krow, rs_qk, nvalid);
+        pdo.load(dorow, rs_v, nvalid);
+        pds0.load(dS1, DV, 64);
+        pds1.load(dS1 + (int64_t)64 * DV, DV, 64);
+        if (w == 0) rr.load(grow, a.H, a.seg, b, T_, t0, nvalid, true);
+        store_rows_split<DK>(pq, sQ, PW, PLW);
+        store_rows_split<DK>(pk, sK, PW, PLW);
+        store_rows_split<64>(pdo, sdO, P64, PL64);
+        store_rows_split<64>(pds0, sdS, PD, PLD);
+        store_rows_split<64>(pds1, sdS + 64 * PD, PD, PLD);
+        if (w == 0) rev_chunk_info<float, false>(&ck, rr);
+    }
+    __syncthreads();
+
+    // A = q k^T tiles, masked with the scalar decay, stored transposed A^T[s][r]
+    for (int ti = w; ti < 12; ti += 4) {
+        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
+        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+        f32x4 acc = zero4();
+        if (ti < 10) {
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += KS)
+                acc = mma3(sld<PW, PLW>(sQ, 16 * rt, k0), sld<PW, PLW>(sK, 16 * st, k0), acc);
+        }
+        store_masked_split<false, P64, PL64>(sAT, ck, rt, st, ti < 10, acc);
+    }
+    __syncthreads();
+
+    // dv^T = dO^T A + [last doc] exp(Gamma - beta_s) dS1^T k^T (rows n, columns s)
+    float* dvo = (float*)a.dv + ((b * T_ + t0) * a.H + h) * DV + n0s + 16 * w + 4 * j4;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        f32x4 a1 = zero4(), a2 = zero4();
+        const int kbeg = (16 * st / KS) * KS;
+#pragma unroll
+        for (int k0 = kbeg; k0 < C; k0 += KS)
+            a1 = mma3(scol<P64, PL64>(sdO, 16 * w, k0), sld<P64, PL64>(sAT, 16 * st, k0), a1);
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += KS)
+            a2 = mma3(scol<PD, PLD>(sdS, 16 * w, k0), sld<PW, PLW>(sK, 16 * st, k0), a2);
+        const int s = 16 * st + i16;
+        const float fu = ck.fu[s];
+        float dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dv[e] = a1[e] + fu * a2[e];
+        if (s < nvalid) store4<float>(dvo + (int64_t)s * a.H * DV, dv);
+    }
+}
+
+__global__ __launch_bounds__(NT) void k_grad_f32s(const RevArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[BYTES];
+    __shared__ SmallS sm;
+    const int64_t NC = (a.T + C - 1) / C;
+    const int64_t L = xcd_logical_block(a.B * a.H * NC * 4);
+    const int role = (int)(L % 4);
+    const int64_t ci = (L / 4) % NC;
+    const int64_t bh = L / 4 / NC;
+    if (role < 2) sqk(a, lds, sm, bh, ci, role);
+    else sv(a, lds, sm, bh, ci, role - 2);
+}
+
+}  // namespace
+
+hipError_t launch_grad_f32s(const RevArgs& a, hipStream_t st) {
+    const int64_t NC = (a.T + C - 1) / C;
+    hipLaunchKernelGGL(k_grad_f32s, dim3((unsigned)(a.B * a.H * NC * 4)), dim3(NT), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_dg_scalar(a, 2, false, st);
+}
+
+}  // namespace gla

@@ -62,6 +62,9 @@ hipError_t launch_dg_scalar(const RevArgs& a, int nslices, bool bf16_out, hipStr
 template <bool VEC>
 hipError_t launch_grad8(const RevArgs& a, hipStream_t st);
 
+// fp32, scalar gate, d_k = d_v = 128: split-bf16 products (includes the dg finisher)
+hipError_t launch_grad_f32s(const RevArgs& a, hipStream_t st);
+
 // chunk-parallel gradients from the per-chunk states and state gradients
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_grad(const RevArgs& a, hipStream_t st);

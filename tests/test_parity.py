@@ -125,6 +125,8 @@ SPLIT = [
     (513, 128, 128, "scalar", torch.bfloat16, 4, 2, None, True, 2),
     (640, 128, 128, "scalar", torch.bfloat16, 2, 2, [256, 384], False, 100),
     (448, 64, 128, "vector", torch.bfloat16, 4, 1, [10, 50, 4, 300, 84], True, 7),
+    (300, 128, 128, "scalar", torch.float32, 4, 2, [100, 50, 150], True, 2),
+    (200, 128, 128, "scalar", torch.float32, 2, 2, None, False, 1),
 ]
 
 
