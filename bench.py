@@ -25,7 +25,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PROFILE = {"c2": "gla_kernels_ssd_fp32_B4_T8192_H8_Hqk2_d128.md",
-           "c3": "gla_kernels_gla_bf16_B4_T4096_H16_d128.md"}
+           "c3": "gla_kernels_gla_bf16_B4_T4096_H16_d128.md",
+           "c4": "gla_kernels_ssd_bf16_packed_B1_T65536_H16_d128.md",
+           "c5a": "gla_kernels_gla_bf16_B1_T16384_H16_d128.md",
+           "c5b": "gla_kernels_gla_bf16_B8_T2048_H16_d128.md"}
 
 
 def source_hash():
@@ -187,6 +190,10 @@ def main():
             "algorithmic_bytes": round(alg["bwd_bytes"] / 1e6, 1),
             "kernel": "gla_bwd (all its kernels, one call)",
             "step_frac": round(step_ach / peak, 4)}
+    if not bf16:
+        # the fp32 products of the gradient kernel run as split-bf16 on the bf16 matrix
+        # cores; the byte roofline of the same call, for comparison
+        roof["hbm_frac"] = round(alg["bwd_bytes"] / (bwd_us * 1e-6) / 1e9 / PEAK["hbm"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
