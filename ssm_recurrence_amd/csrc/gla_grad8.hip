@@ -70,57 +70,67 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
 
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
-    const int64_t L = xcd_logical_block(a.B * a.H * NC);
-    const int64_t ci = L % NC, bh = L / NC;
-    const int64_t b = bh / a.H, h = bh % a.H;
-    const int64_t G = a.H / a.Hqk, hq = h / G;
+    const int64_t nitems = a.B * a.H * NC;
     const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
     const int cw = 16 * w;  // the wave's key channels (dq, dk, dg) and value columns (dv)
-    const int64_t t0 = ci * C;
-    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
     const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
     const int64_t rs_g = VEC ? a.H * DK : a.H;
-    const T* qrow = (const T*)a.q + (b * T_ + t0) * rs_qk + hq * DK;
-    const T* krow = (const T*)a.k + (b * T_ + t0) * rs_qk + hq * DK;
-    const T* vrow = (const T*)a.v + (b * T_ + t0) * rs_v + h * DV;
-    const T* dorow = (const T*)a.dO + (b * T_ + t0) * rs_v + h * DV;
-    const T* grow = (const T*)a.g + (b * T_ + t0) * rs_g + (VEC ? h * DK : h);
+    const int64_t G = a.H / a.Hqk;
+
+    // Scalar gate: a persistent loop over (b, h, chunk) items, the next item's tiles
+    // loaded into registers while the current one computes.  Vector gate: one item
+    // per workgroup (the prefetch registers would not fit next to its gate factors).
+    constexpr bool PREFETCH = !VEC;
+    TileRegs<T, 128, NTH> pq, pk, pg, pv, pdo;
+    RowRegs rr;
+    auto issue = [&](int64_t item) {
+        const int64_t ci = item % NC, bh = item / NC;
+        const int64_t b = bh / a.H, h = bh % a.H, hq = h / G;
+        const int64_t t0 = ci * C;
+        const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+        pq.load((const T*)a.q + (b * T_ + t0) * rs_qk + hq * DK, rs_qk, nvalid);
+        pk.load((const T*)a.k + (b * T_ + t0) * rs_qk + hq * DK, rs_qk, nvalid);
+        const T* grow = (const T*)a.g + (b * T_ + t0) * rs_g + (VEC ? h * DK : h);
+        if constexpr (VEC) pg.load(grow, rs_g, nvalid);
+        pv.load((const T*)a.v + (b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
+        pdo.load((const T*)a.dO + (b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
+        if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
+    };
+    int64_t item = blockIdx.x;
+    if constexpr (PREFETCH) {
+        if (item < nitems) issue(item);
+    }
+    // (vector gate: the stride ends the loop after one item, visibly to the compiler)
+    const int64_t stride = PREFETCH ? (int64_t)gridDim.x : nitems;
+    for (; item < nitems; item += stride) {
+    if constexpr (!PREFETCH) issue(item);
+    const int64_t ci = item % NC, bh = item / NC;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t hq = h / G;
+    const int64_t t0 = ci * C;
+    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
     // rows cw + i of S0 and dS1 (the A operands of dO S0^T and v dS1^T, k = n)
     const T* S0 = (const T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
     const T* dS1 = (const T*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
 
-    // ---- phase 1: loads
-    TileRegs<T, 128, NTH> pq, pk, pg, pv, pdo;
-    RowRegs rr;
-    pq.load(qrow, rs_qk, nvalid);
-    pk.load(krow, rs_qk, nvalid);
-    if constexpr (VEC) pg.load(grow, rs_g, nvalid);
-    pv.load(vrow, rs_v, nvalid);
-    pdo.load(dorow, rs_v, nvalid);
-    if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
+    // ---- phase 1: this item's tiles to LDS; its S0 and dS1 rows to registers
     bf16x8 s0f[NKV], dsf[NKV];
 #pragma unroll
     for (int kk = 0; kk < NKV; ++kk) {
         s0f[kk] = *reinterpret_cast<const bf16x8*>(S0 + kk * KS + 8 * j4);
         dsf[kk] = *reinterpret_cast<const bf16x8*>(dS1 + kk * KS + 8 * j4);
     }
-    [[maybe_unused]] const TriOnes<T> tri;
-
     pq.store_rows(sQ, P);
     pk.store_rows(sK, P);
     if constexpr (VEC) pg.store_rows(sG, P);
     pv.store_rows(sV, P);
     pdo.store_rows(sdO, P);
-    if constexpr (!VEC) {
-#pragma unroll
-        for (int kk = 0; kk < NKV; ++kk)
-            *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = dsf[kk];
-    }
     if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
-    float sd = 0.f;  // rowsum(S0 * dS1) of channel cw + i16 over this lane's n
-#pragma unroll
-    for (int kk = 0; kk < NKV; ++kk) sd = frag_dot(s0f[kk], dsf[kk], sd);
     __syncthreads();
+    if constexpr (PREFETCH) {
+        if (item + stride < nitems) issue(item + stride);
+    }
+    [[maybe_unused]] const TriOnes<T> tri;
 
     // ---- phase 2: gate prefix, scaling, dS1' rows, dA
     // raw q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e)
@@ -187,6 +197,9 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             em[e] = egm[e] = 1.f;
             dec[e] = ck.decay;
         }
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk)
+            *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = dsf[kk];
     }
     // dA^T = v dO^T tiles, masked, stored as dA[r][s] (10 lower + 2 zero upper tiles)
     for (int ti = w; ti < 12; ti += Cfg::NW) {
@@ -268,6 +281,9 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
         }
     }
     // boundary term rowsum(S1 * dS1) per channel cw + 4j4 + e
+    float sd = 0.f;  // rowsum(S0 * dS1) of channel cw + i16 over this lane's n
+#pragma unroll
+    for (int kk = 0; kk < NKV; ++kk) sd = frag_dot(s0f[kk], dsf[kk], sd);
     sd += __shfl_xor(sd, 16, 64);
     sd += __shfl_xor(sd, 32, 64);
     float bnd[4];
@@ -388,12 +404,20 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             if (r < nvalid) ((T*)a.dg)[(b * T_ + t0 + r) * a.H + h] = from_f32<T>(reset ? 0.f : run);
         }
     }
+    __syncthreads();  // LDS and the chunk data are rewritten by the next item
+    }
 }
+
+// scalar gate: one resident workgroup per compute unit (the LDS holds one), each
+// looping over items; vector gate: one workgroup per item
+constexpr int64_t kGrad8Workers = 256;
 
 template <bool VEC>
 hipError_t launch_grad8(const RevArgs& a, hipStream_t st) {
     const int64_t NC = (a.T + C - 1) / C;
-    hipLaunchKernelGGL((k_grad8<VEC>), dim3((unsigned)(a.B * a.H * NC)), dim3(Grad8Cfg<VEC>::NTH), 0, st, a);
+    const int64_t items = a.B * a.H * NC;
+    const int64_t grid = (VEC || items < kGrad8Workers) ? items : kGrad8Workers;
+    hipLaunchKernelGGL((k_grad8<VEC>), dim3((unsigned)grid), dim3(Grad8Cfg<VEC>::NTH), 0, st, a);
     return hipGetLastError();
 }
 
