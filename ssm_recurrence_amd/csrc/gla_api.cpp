@@ -88,6 +88,13 @@ Split plan_split(const gla_problem* p, int for_backward) {
     return s;
 }
 
+// The fp32 scalar-gate 128 x 128 gradient kernel sums dq, dk over the heads that
+// share q/k itself; every other path writes per-head fp32 dq, dk and sums them after.
+bool per_head_dqdk(const gla_problem* p) {
+    if (p->H_qk == p->H) return false;
+    return !(p->dtype == GLA_F32 && p->gate == GLA_GATE_SCALAR && p->d_k == 128 && p->d_v == 128);
+}
+
 struct WsLayout {
     size_t S = 0, dS = 0, dq = 0, dk = 0, xs = 0, bnd = 0;
     size_t pL0 = 0, pL1 = 0, pS = 0, pdS = 0, pD = 0, total = 0;
@@ -132,7 +139,7 @@ WsLayout ws_layout(const gla_problem* p, int for_backward) {
     off += round_up(bh * (size_t)(nc + 1) * st);
     L.dS = off;
     off += round_up(bh * (size_t)nc * st);
-    if (p->H_qk != p->H) {
+    if (per_head_dqdk(p)) {
         const size_t n = (size_t)(p->B * p->T * p->H * p->d_k) * sizeof(float);
         L.dq = off;
         off += round_up(n);
@@ -240,7 +247,7 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
     if (e != hipSuccess) return e;
     e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
     if (e != hipSuccess) return e;
-    if (ra.Hqk != ra.H) {
+    if (ra.ws_dq) {
         e = gla::launch_group_sum<T, DK>(ra.ws_dq, ra.dq, ra.B, ra.T, ra.H, ra.Hqk, st);
         if (e != hipSuccess) return e;
         e = gla::launch_group_sum<T, DK>(ra.ws_dk, ra.dk, ra.B, ra.T, ra.H, ra.Hqk, st);
@@ -356,7 +363,7 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     ra.ws_dS = w + L.dS;
     ra.dhT = dhT; ra.dh0 = dh0;
     ra.dq = dq; ra.dk = dk; ra.dv = dv; ra.dg = dg;
-    if (p->H_qk != p->H) {
+    if (per_head_dqdk(p)) {
         ra.ws_dq = (float*)(w + L.dq);
         ra.ws_dk = (float*)(w + L.dk);
     }

@@ -14,7 +14,8 @@
 // The mathematics and the two kinds of workgroups are those of gla_grad.hip
 // (QK: dq, dk and the log-gate partial sums for 64 key channels; V: dv for 64
 // value columns), with every LDS tile stored as a hi plane followed by a lo
-// plane; inputs, outputs and all accumulation stay fp32.
+// plane; inputs, outputs and all accumulation stay fp32.  A QK workgroup visits
+// all heads that share its q/k head and writes the summed dq, dk itself.
 #include "gla_bwd.hpp"
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
@@ -136,7 +137,13 @@ struct SmallS {
 };
 
 // ============================================================== QK role
-__device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t ci, int slice) {
+// One workgroup per (b, q/k head, chunk, 64-channel slice): q and k are loaded
+// once and the G heads that read them are visited in turn, each with its own v,
+// dO, gate, state and state gradient; dq and dk are summed over those heads in
+// registers (the head-sharing reduction of the FLAT page, Pallas Kernels >
+// Gated Linear Attention, done in place of per-head buffers), and each head's
+// log-gate partial sums are written for the finisher.
+__device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t b, int64_t hq, int64_t ci, int slice) {
     bf16* sQ = reinterpret_cast<bf16*>(lds);
     bf16* sK = sQ + 2 * PL64;
     bf16* sdA = sK + 2 * PL64;  // [r][s]
@@ -144,8 +151,7 @@ __device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t
     bf16* sV = sdO + 2 * PLW;
     RevChunk& ck = sm.ck;
 
-    const int64_t b = bh / a.H, h = bh % a.H;
-    const int64_t G = a.H / a.Hqk, hq = h / G;
+    const int64_t G = a.H / a.Hqk;
     const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
     const int cs0 = slice * 64;
     const int cw = cs0 + 16 * w;
@@ -156,134 +162,140 @@ __device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t
     const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
     const float* qrow = (const float*)a.q + (b * T_ + t0) * rs_qk + hq * DK + cs0;
     const float* krow = (const float*)a.k + (b * T_ + t0) * rs_qk + hq * DK + cs0;
-    const float* vrow = (const float*)a.v + (b * T_ + t0) * rs_v + h * DV;
-    const float* dorow = (const float*)a.dO + (b * T_ + t0) * rs_v + h * DV;
-    const float* grow = (const float*)a.g + (b * T_ + t0) * a.H + h;
-    const float* S0 = (const float*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
-    const float* dS1 = (const float*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
 
-    TileRegs<float, 64> pq, pk;
-    TileRegs<float, DV> pv, pdo;
-    RowRegs rr;
-    pq.load(qrow, rs_qk, nvalid);
-    pk.load(krow, rs_qk, nvalid);
-    pv.load(vrow, rs_v, nvalid);
-    pdo.load(dorow, rs_v, nvalid);
-    if (w == 0) rr.load(grow, a.H, a.seg, b, T_, t0, nvalid, true);
-    // raw q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e)
-    f32x4 qraw[4], kraw[4];
+    {
+        TileRegs<float, 64> pq, pk;
+        pq.load(qrow, rs_qk, nvalid);
+        pk.load(krow, rs_qk, nvalid);
+        store_rows_split<64>(pq, sQ, P64, PL64);
+        store_rows_split<64>(pk, sK, P64, PL64);
+    }
+    float dqs[4][4], dks[4][4];  // dq, dk summed over the heads of the group
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dqs[rt][e] = dks[rt][e] = 0.f;
+
+    for (int64_t gi = 0; gi < G; ++gi) {
+        const int64_t h = hq * G + gi, bh = b * a.H + h;
+        const float* vrow = (const float*)a.v + (b * T_ + t0) * rs_v + h * DV;
+        const float* dorow = (const float*)a.dO + (b * T_ + t0) * rs_v + h * DV;
+        const float* grow = (const float*)a.g + (b * T_ + t0) * a.H + h;
+        const float* S0 = (const float*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
+        const float* dS1 = (const float*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
+
+        TileRegs<float, DV> pv, pdo;
+        RowRegs rr;
+        pv.load(vrow, rs_v, nvalid);
+        pdo.load(dorow, rs_v, nvalid);
+        if (w == 0) rr.load(grow, a.H, a.seg, b, T_, t0, nvalid, true);
+        // S0 and dS1 rows cw + i16 as split A operands (k = n); rowsum(S0 * dS1) in fp32
+        float sd = 0.f;
+        SFrag s0f[DV / KS], dsf[DV / KS];
+#pragma unroll
+        for (int kk = 0; kk < DV / KS; ++kk) {
+            float unused = 0.f;
+            s0f[kk] = split_ld8(S0 + kk * KS + 8 * j4, sd, dS1 + kk * KS + 8 * j4);
+            dsf[kk] = split_ld8(dS1 + kk * KS + 8 * j4, unused, nullptr);
+        }
+        store_rows_split<DV>(pv, sV, PW, PLW);
+        store_rows_split<DV>(pdo, sdO, PW, PLW);
+        if (w == 0) rev_chunk_info<float, false>(&ck, rr);
+        __syncthreads();
+
+        // dA^T = v dO^T tiles, masked, stored dA[r][s]
+        for (int ti = w; ti < 12; ti += 4) {
+            const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
+            const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+            f32x4 acc = zero4();
+            if (ti < 10) {
+#pragma unroll
+                for (int n0 = 0; n0 < DV; n0 += KS)
+                    acc = mma3(sld<PW, PLW>(sV, 16 * st, n0), sld<PW, PLW>(sdO, 16 * rt, n0), acc);
+            }
+            store_masked_split<true, P64, PL64>(sdA, ck, rt, st, ti < 10, acc);
+        }
+        __syncthreads();
+
+        // q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e),
+        // from the split tiles (hi + lo)
+        float x[4][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 a1 = zero4(), a2 = zero4();
+            const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
+#pragma unroll
+            for (int k0 = 0; k0 < kend; k0 += KS)
+                a1 = mma3(scol<P64, PL64>(sK, 16 * w, k0), sld<P64, PL64>(sdA, 16 * rt, k0), a1);
+#pragma unroll
+            for (int kk = 0; kk < DV / KS; ++kk) a2 = mma3(s0f[kk], sld<PW, PLW>(sdO, 16 * rt, kk * KS), a2);
+            const int r = 16 * rt + i16;
+            const float fq = ck.fq[r];
+            const Vec4<bf16> qh = Vec4<bf16>::load(sQ + r * P64 + 16 * w + 4 * j4);
+            const Vec4<bf16> ql = Vec4<bf16>::load(sQ + PL64 + r * P64 + 16 * w + 4 * j4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float dq = a1[e] + fq * a2[e];
+                x[rt][e] = (qh.get(e) + ql.get(e)) * dq;
+                dqs[rt][e] += dq;
+            }
+        }
+        float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            f32x4 a1 = zero4(), a2 = zero4();
+            const int kbeg = (16 * st / KS) * KS;
+#pragma unroll
+            for (int k0 = kbeg; k0 < C; k0 += KS)
+                a1 = mma3(scol<P64, PL64>(sQ, 16 * w, k0), scol<P64, PL64>(sdA, 16 * st, k0), a1);
+#pragma unroll
+            for (int kk = 0; kk < DV / KS; ++kk) a2 = mma3(dsf[kk], sld<PW, PLW>(sV, 16 * st, kk * KS), a2);
+            const int s = 16 * st + i16;
+            const float fu = ck.fu[s];
+            const Vec4<bf16> kh = Vec4<bf16>::load(sK + s * P64 + 16 * w + 4 * j4);
+            const Vec4<bf16> kl = Vec4<bf16>::load(sK + PL64 + s * P64 + 16 * w + 4 * j4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float inter = fu * a2[e];
+                const float dk = a1[e] + inter;
+                const float kr = kh.get(e) + kl.get(e);
+                x[st][e] -= kr * dk;
+                bsum[e] += kr * inter;
+                dks[st][e] += dk;
+            }
+        }
+        sd += __shfl_xor(sd, 16, 64);
+        sd += __shfl_xor(sd, 32, 64);
+        float bb = 0.f;  // sum over this lane group's four channels of rowsum(S1 * dS1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bb += ck.decay * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
+        // partial sums over this workgroup's channels; a finisher adds the two slices
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            float y = x[rt][0] + x[rt][1] + x[rt][2] + x[rt][3];
+            y += __shfl_xor(y, 16, 64);
+            y += __shfl_xor(y, 32, 64);
+            if (j4 == 0) sm.sXs[w][16 * rt + i16] = y;
+        }
+        bb += __shfl_xor(bb, 16, 64);
+        bb += __shfl_xor(bb, 32, 64);
+        if (l == 0) sm.sBs[w] = bb;
+        __syncthreads();  // also: every wave is done with this head's v, dO and dA
+        if (w == 0) {
+            const int r = l;
+            const float tot = sm.sXs[0][r] + sm.sXs[1][r] + sm.sXs[2][r] + sm.sXs[3][r];
+            if (r < nvalid) a.ws_xs[(bh * 2 + slice) * T_ + t0 + r] = tot;
+            if (r == 0) a.ws_bnd[(bh * 2 + slice) * NC + ci] = sm.sBs[0] + sm.sBs[1] + sm.sBs[2] + sm.sBs[3];
+        }
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + i16;
-        qraw[rt] = zero4();
-        kraw[rt] = zero4();
         if (r < nvalid) {
-            qraw[rt] = *reinterpret_cast<const f32x4*>(qrow + r * rs_qk + 16 * w + 4 * j4);
-            kraw[rt] = *reinterpret_cast<const f32x4*>(krow + r * rs_qk + 16 * w + 4 * j4);
+            const int64_t o = ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4;
+            store4<float>((float*)a.dq + o, dqs[rt]);
+            store4<float>((float*)a.dk + o, dks[rt]);
         }
-    }
-    // S0 and dS1 rows cw + i16 as split A operands (k = n); rowsum(S0 * dS1) in fp32
-    float sd = 0.f;
-    SFrag s0f[DV / KS], dsf[DV / KS];
-#pragma unroll
-    for (int kk = 0; kk < DV / KS; ++kk) {
-        float unused = 0.f;
-        s0f[kk] = split_ld8(S0 + kk * KS + 8 * j4, sd, dS1 + kk * KS + 8 * j4);
-        dsf[kk] = split_ld8(dS1 + kk * KS + 8 * j4, unused, nullptr);
-    }
-
-    store_rows_split<64>(pq, sQ, P64, PL64);
-    store_rows_split<64>(pk, sK, P64, PL64);
-    store_rows_split<DV>(pv, sV, PW, PLW);
-    store_rows_split<DV>(pdo, sdO, PW, PLW);
-    if (w == 0) rev_chunk_info<float, false>(&ck, rr);
-    __syncthreads();
-
-    // dA^T = v dO^T tiles, masked, stored dA[r][s]
-    for (int ti = w; ti < 12; ti += 4) {
-        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
-        f32x4 acc = zero4();
-        if (ti < 10) {
-#pragma unroll
-            for (int n0 = 0; n0 < DV; n0 += KS)
-                acc = mma3(sld<PW, PLW>(sV, 16 * st, n0), sld<PW, PLW>(sdO, 16 * rt, n0), acc);
-        }
-        store_masked_split<true, P64, PL64>(sdA, ck, rt, st, ti < 10, acc);
-    }
-    __syncthreads();
-
-    const bool gqa = G > 1;
-    float x[4][4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        f32x4 a1 = zero4(), a2 = zero4();
-        const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
-#pragma unroll
-        for (int k0 = 0; k0 < kend; k0 += KS)
-            a1 = mma3(scol<P64, PL64>(sK, 16 * w, k0), sld<P64, PL64>(sdA, 16 * rt, k0), a1);
-#pragma unroll
-        for (int kk = 0; kk < DV / KS; ++kk) a2 = mma3(s0f[kk], sld<PW, PLW>(sdO, 16 * rt, kk * KS), a2);
-        const int r = 16 * rt + i16;
-        const float fq = ck.fq[r];
-        float dq[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dq[e] = a1[e] + fq * a2[e];
-            x[rt][e] = qraw[rt][e] * dq[e];
-        }
-        if (r < nvalid) {
-            if (!gqa) store4<float>((float*)a.dq + ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4, dq);
-            else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
-        }
-    }
-    float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        f32x4 a1 = zero4(), a2 = zero4();
-        const int kbeg = (16 * st / KS) * KS;
-#pragma unroll
-        for (int k0 = kbeg; k0 < C; k0 += KS)
-            a1 = mma3(scol<P64, PL64>(sQ, 16 * w, k0), scol<P64, PL64>(sdA, 16 * st, k0), a1);
-#pragma unroll
-        for (int kk = 0; kk < DV / KS; ++kk) a2 = mma3(dsf[kk], sld<PW, PLW>(sV, 16 * st, kk * KS), a2);
-        const int s = 16 * st + i16;
-        const float fu = ck.fu[s];
-        float dk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float inter = fu * a2[e];
-            dk[e] = a1[e] + inter;
-            x[st][e] -= kraw[st][e] * dk[e];
-            bsum[e] += kraw[st][e] * inter;
-        }
-        if (s < nvalid) {
-            if (!gqa) store4<float>((float*)a.dk + ((b * T_ + t0 + s) * a.Hqk + hq) * DK + cw + 4 * j4, dk);
-            else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
-        }
-    }
-    sd += __shfl_xor(sd, 16, 64);
-    sd += __shfl_xor(sd, 32, 64);
-    float bb = 0.f;  // sum over this lane group's four channels of rowsum(S1 * dS1)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bb += ck.decay * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
-    // partial sums over this workgroup's channels; a finisher adds the two slices
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        float y = x[rt][0] + x[rt][1] + x[rt][2] + x[rt][3];
-        y += __shfl_xor(y, 16, 64);
-        y += __shfl_xor(y, 32, 64);
-        if (j4 == 0) sm.sXs[w][16 * rt + i16] = y;
-    }
-    bb += __shfl_xor(bb, 16, 64);
-    bb += __shfl_xor(bb, 32, 64);
-    if (l == 0) sm.sBs[w] = bb;
-    __syncthreads();
-    if (w == 0) {
-        const int r = l;
-        const float tot = sm.sXs[0][r] + sm.sXs[1][r] + sm.sXs[2][r] + sm.sXs[3][r];
-        if (r < nvalid) a.ws_xs[(bh * 2 + slice) * T_ + t0 + r] = tot;
-        if (r == 0) a.ws_bnd[(bh * 2 + slice) * NC + ci] = sm.sBs[0] + sm.sBs[1] + sm.sBs[2] + sm.sBs[3];
     }
 }
 
@@ -365,23 +377,29 @@ __device__ void sv(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t 
     }
 }
 
+// Workgroups per (b, q/k head, chunk): 2 QK (one per 64-channel slice, all G heads)
+// and 2G V (one per head and 64-column slice), adjacent so they share one XCD.
 __global__ __launch_bounds__(NT) void k_grad_f32s(const RevArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[BYTES];
     __shared__ SmallS sm;
     const int64_t NC = (a.T + C - 1) / C;
-    const int64_t L = xcd_logical_block(a.B * a.H * NC * 4);
-    const int role = (int)(L % 4);
-    const int64_t ci = (L / 4) % NC;
-    const int64_t bh = L / 4 / NC;
-    if (role < 2) sqk(a, lds, sm, bh, ci, role);
-    else sv(a, lds, sm, bh, ci, role - 2);
+    const int64_t G = a.H / a.Hqk;
+    const int64_t per = 2 + 2 * G;
+    const int64_t L = xcd_logical_block(a.B * a.Hqk * NC * per);
+    const int64_t r = L % per;
+    const int64_t ci = (L / per) % NC;
+    const int64_t bq = L / per / NC;  // b * Hqk + hq
+    const int64_t b = bq / a.Hqk, hq = bq % a.Hqk;
+    if (r < 2) sqk(a, lds, sm, b, hq, ci, (int)r);
+    else sv(a, lds, sm, b * a.H + hq * G + (r - 2) / 2, ci, (int)((r - 2) % 2));
 }
 
 }  // namespace
 
 hipError_t launch_grad_f32s(const RevArgs& a, hipStream_t st) {
     const int64_t NC = (a.T + C - 1) / C;
-    hipLaunchKernelGGL(k_grad_f32s, dim3((unsigned)(a.B * a.H * NC * 4)), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(k_grad_f32s, dim3((unsigned)(a.B * a.Hqk * NC * (2 + 2 * (a.H / a.Hqk)))), dim3(NT), 0,
+                       st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_dg_scalar(a, 2, false, st);
