@@ -209,9 +209,16 @@ gla::CombineArgs combine_args(const gla::PassArgs& pa, int DK, int DV, int which
 
 // Piece entry states for a split forward: summaries, then the combine from h0.
 // pa.L_out[0], pa.D_out hold the summaries and pa.S_in receives the entry states.
+// State-pass block shape: 64 x d_v blocks request each head's v (or dO) once per
+// pass instead of once per 64-channel block; they are used when they still give
+// `want` workgroups.
+bool wide_blocks(const gla::PassArgs& pa, int DK, int64_t passes, int64_t want) {
+    return pa.B * pa.H * pa.P * (DK / 64) * passes >= want;
+}
+
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_split_fwd_states(const gla::PassArgs& pa, hipStream_t st) {
-    hipError_t e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_SUM_FWD, st);
+    hipError_t e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_SUM_FWD, wide_blocks(pa, DK, 1, 256), st);
     if (e != hipSuccess) return e;
     return gla::launch_piece_combine(combine_args(pa, DK, DV, 1), st);
 }
@@ -237,13 +244,14 @@ hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t st) {
     hipError_t e;
+    const bool wide = wide_blocks(pa, DK, 2, 512);
     if (pa.P > 1) {
-        e = gla::launch_states_pair<T, VEC, DK, DV>(pa, true, st);
+        e = gla::launch_states_pair<T, VEC, DK, DV>(pa, true, wide, st);
         if (e != hipSuccess) return e;
         e = gla::launch_piece_combine(combine_args(pa, DK, DV, 3), st);
         if (e != hipSuccess) return e;
     }
-    e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, st);
+    e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
     if (e != hipSuccess) return e;
     e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
     if (e != hipSuccess) return e;

@@ -46,12 +46,13 @@ struct CombineArgs {
 // modes of the state pass: per-chunk states or state gradients, per-piece summaries
 enum { ST_STATES = 0, ST_SUM_FWD = 1, ST_SUM_REV = 2, ST_DSTATES = 3 };
 
+// wide: blocks of 64 key channels x all value columns (else 64 x 64)
 template <typename T, bool VEC, int DK, int DV>
-hipError_t launch_states(const PassArgs& a, int mode, hipStream_t st);
+hipError_t launch_states(const PassArgs& a, int mode, bool wide, hipStream_t st);
 
 // ST_STATES and ST_DSTATES (summaries = false) or ST_SUM_FWD and ST_SUM_REV in one launch
 template <typename T, bool VEC, int DK, int DV>
-hipError_t launch_states_pair(const PassArgs& a, bool summaries, hipStream_t st);
+hipError_t launch_states_pair(const PassArgs& a, bool summaries, bool wide, hipStream_t st);
 
 hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st);
 

@@ -37,26 +37,30 @@
 
 namespace gla {
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int NB>
 struct StatesLds {
     static constexpr int PB = Pitch16<T>::of(64);
+    static constexpr int PN = Pitch16<T>::of(NB);
     T sK[C * PB];
-    T sV[C * PB];
+    T sV[C * PN];
     T sG[VEC ? C * PB : 1];
     float sFu[C];
     float sDecay[64];
     int sFirstReset, sLastReset;
 };
 
-// One workgroup: one 64x64 block of the state (or of its gradient) of one
+// One workgroup: one 64 x NB block of the state (or of its gradient) of one
 // piece of one (b, h), walking the piece's chunks in order (reverse order for
-// the gradient modes).  L is the workgroup's logical index within its launch.
-template <typename T, bool VEC, int DK, int DV, int MODE>
-__device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC>& sm, int64_t L) {
+// the gradient modes).  NB = 64, or all value columns (each head's v, or dO,
+// then requested once per pass instead of once per 64-channel block).  L is the
+// workgroup's logical index within its launch.
+template <typename T, bool VEC, int DK, int DV, int MODE, int NB>
+__device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC, NB>& sm, int64_t L) {
     constexpr bool REV = MODE == ST_SUM_REV || MODE == ST_DSTATES;
-    constexpr int CB = 64, NB = 64;          // block of the state
+    constexpr int CB = 64;                   // block of the state: CB x NB
     constexpr int NCB = DK / CB, NNB = DV / NB;
-    constexpr int PB = StatesLds<T, VEC>::PB;   // pitch of [row][64] tiles
+    constexpr int PB = StatesLds<T, VEC, NB>::PB;   // pitch of [row][64] tiles
+    constexpr int PN = StatesLds<T, VEC, NB>::PN;   // pitch of [row][NB] tiles
     constexpr int NNT = NB / 16;
     using M = Mma<T>;
     T* sK = sm.sK;
@@ -142,7 +146,7 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC>
         const int64_t t0 = ci * C;
         if constexpr (MODE == ST_STATES || MODE == ST_DSTATES) store_state(ci);
         pk.store_rows(sK, PB);
-        pv.store_rows(sV, PB);
+        pv.store_rows(sV, PN);
         if constexpr (VEC) pg.store_rows(sG, PB);
         if (w == 0) {
             const int r = l;
@@ -212,7 +216,7 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC>
             }
 #pragma unroll
             for (int nt = 0; nt < NNT; ++nt)
-                St[nt] = M::mma(frag_col<T, PB, false>(sV, 16 * nt, k0), ku, St[nt]);
+                St[nt] = M::mma(frag_col<T, PN, false>(sV, 16 * nt, k0), ku, St[nt]);
         }
         __syncthreads();
     }
@@ -234,48 +238,60 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC>
     }
 }
 
-template <typename T, bool VEC, int DK, int DV, int MODE>
+template <typename T, bool VEC, int DK, int DV, int MODE, int NB>
 __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
-    __shared__ __attribute__((aligned(16))) StatesLds<T, VEC> sm;
-    const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / 64);
-    states_body<T, VEC, DK, DV, MODE>(a, sm, xcd_logical_block(n));
+    __shared__ __attribute__((aligned(16))) StatesLds<T, VEC, NB> sm;
+    const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
+    states_body<T, VEC, DK, DV, MODE, NB>(a, sm, xcd_logical_block(n));
 }
 
 // Two independent passes in one launch (the first half of the grid runs MODE_A,
 // the second MODE_B), so that both directions share the device.
-template <typename T, bool VEC, int DK, int DV, int MODE_A, int MODE_B>
+template <typename T, bool VEC, int DK, int DV, int MODE_A, int MODE_B, int NB>
 __global__ __launch_bounds__(NT) void k_states2(const PassArgs a) {
-    __shared__ __attribute__((aligned(16))) StatesLds<T, VEC> sm;
-    const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / 64);
+    __shared__ __attribute__((aligned(16))) StatesLds<T, VEC, NB> sm;
+    const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
     const int64_t L = xcd_logical_block(2 * n);
-    if (L < n) states_body<T, VEC, DK, DV, MODE_A>(a, sm, L);
-    else states_body<T, VEC, DK, DV, MODE_B>(a, sm, L - n);
+    if (L < n) states_body<T, VEC, DK, DV, MODE_A, NB>(a, sm, L);
+    else states_body<T, VEC, DK, DV, MODE_B, NB>(a, sm, L - n);
 }
 
-template <typename T, bool VEC, int DK, int DV>
-hipError_t launch_states(const PassArgs& a, int mode, hipStream_t st) {
-    const int64_t grid = a.B * a.H * a.P * (DK / 64) * (DV / 64);
+template <typename T, bool VEC, int DK, int DV, int NB>
+hipError_t launch_states_nb(const PassArgs& a, int mode, hipStream_t st) {
+    const int64_t grid = a.B * a.H * a.P * (DK / 64) * (DV / NB);
     if (mode == ST_SUM_FWD)
-        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_SUM_FWD>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_SUM_FWD, NB>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     else if (mode == ST_SUM_REV)
-        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_SUM_REV>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_SUM_REV, NB>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     else if (mode == ST_DSTATES)
-        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_DSTATES>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_DSTATES, NB>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     else
-        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_STATES>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((k_states<T, VEC, DK, DV, ST_STATES, NB>), dim3((unsigned)grid), dim3(NT), 0, st, a);
     return hipGetLastError();
 }
 
 template <typename T, bool VEC, int DK, int DV>
-hipError_t launch_states_pair(const PassArgs& a, bool summaries, hipStream_t st) {
-    const int64_t grid = 2 * a.B * a.H * a.P * (DK / 64) * (DV / 64);
+hipError_t launch_states(const PassArgs& a, int mode, bool wide, hipStream_t st) {
+    if (wide && DV > 64) return launch_states_nb<T, VEC, DK, DV, DV>(a, mode, st);
+    return launch_states_nb<T, VEC, DK, DV, 64>(a, mode, st);
+}
+
+template <typename T, bool VEC, int DK, int DV, int NB>
+hipError_t launch_states_pair_nb(const PassArgs& a, bool summaries, hipStream_t st) {
+    const int64_t grid = 2 * a.B * a.H * a.P * (DK / 64) * (DV / NB);
     if (summaries)
-        hipLaunchKernelGGL((k_states2<T, VEC, DK, DV, ST_SUM_FWD, ST_SUM_REV>), dim3((unsigned)grid), dim3(NT), 0,
-                           st, a);
+        hipLaunchKernelGGL((k_states2<T, VEC, DK, DV, ST_SUM_FWD, ST_SUM_REV, NB>), dim3((unsigned)grid), dim3(NT),
+                           0, st, a);
     else
-        hipLaunchKernelGGL((k_states2<T, VEC, DK, DV, ST_STATES, ST_DSTATES>), dim3((unsigned)grid), dim3(NT), 0,
-                           st, a);
+        hipLaunchKernelGGL((k_states2<T, VEC, DK, DV, ST_STATES, ST_DSTATES, NB>), dim3((unsigned)grid), dim3(NT),
+                           0, st, a);
     return hipGetLastError();
+}
+
+template <typename T, bool VEC, int DK, int DV>
+hipError_t launch_states_pair(const PassArgs& a, bool summaries, bool wide, hipStream_t st) {
+    if (wide && DV > 64) return launch_states_pair_nb<T, VEC, DK, DV, DV>(a, summaries, st);
+    return launch_states_pair_nb<T, VEC, DK, DV, 64>(a, summaries, st);
 }
 
 // Piece-state combine: one thread per state element (b, h, c, n), P sequential
@@ -322,8 +338,8 @@ hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st) {
 }
 
 #define GLA_INST_ST(T, VEC, DK, DV)                                                   \
-    template hipError_t launch_states<T, VEC, DK, DV>(const PassArgs&, int, hipStream_t); \
-    template hipError_t launch_states_pair<T, VEC, DK, DV>(const PassArgs&, bool, hipStream_t);
+    template hipError_t launch_states<T, VEC, DK, DV>(const PassArgs&, int, bool, hipStream_t); \
+    template hipError_t launch_states_pair<T, VEC, DK, DV>(const PassArgs&, bool, bool, hipStream_t);
 #define GLA_INST_ST_D(T, VEC)                                     \
     GLA_INST_ST(T, VEC, 64, 64) GLA_INST_ST(T, VEC, 64, 128)      \
     GLA_INST_ST(T, VEC, 128, 64) GLA_INST_ST(T, VEC, 128, 128)

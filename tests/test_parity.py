@@ -127,6 +127,9 @@ SPLIT = [
     (448, 64, 128, "vector", torch.bfloat16, 4, 1, [10, 50, 4, 300, 84], True, 7),
     (300, 128, 128, "scalar", torch.float32, 4, 2, [100, 50, 150], True, 2),
     (200, 128, 128, "scalar", torch.float32, 2, 2, None, False, 1),
+    # enough pieces for the state passes' wide blocks (64 key channels x all columns)
+    (4096, 128, 128, "vector", torch.bfloat16, 4, 4, [1000, 3096], True, 32),
+    (4096, 128, 128, "scalar", torch.float32, 4, 2, [2500, 1596], True, 32),
 ]
 
 
