@@ -1,15 +1,8 @@
 // gla_grad_f32s.hip -- chunk-parallel gradients for fp32 inputs with the scalar
 // gate and 128 x 128 heads (gfx950), on the bf16 matrix cores.
 //
-// Every fp32 operand x is held as two bf16 values, hi = bf16(x) and
-// lo = bf16(x - hi), so that x = hi + lo to about 2^-17 relative, and each
-// fp32 product a b is taken as lo_a hi_b + hi_a lo_b + hi_a hi_b (three bf16
-// matrix-core products into one fp32 accumulator; the dropped lo_a lo_b is
-// below 2^-16 of the product).  Three bf16 products cost about a fifth of one
-// fp32 matrix-core product on this device.  The FLAT page ("FLAT: Flash Linear
-// Attention on TPUs", Pallas Kernels > Backward Kernels, the gate-gradient
-// item) splits an fp32 input into two bf16 halves for the same reason, to keep
-// fp32 accuracy on a bf16 matrix unit.
+// fp32 operands are split into bf16 hi/lo pairs and multiplied with three bf16
+// matrix-core products (gla_split.hpp).
 //
 // The mathematics and the two kinds of workgroups are those of gla_grad.hip
 // (QK: dq, dk and the log-gate partial sums for 64 key channels; V: dv for 64
@@ -19,84 +12,12 @@
 #include "gla_bwd.hpp"
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
+#include "gla_split.hpp"
 #include "gla_tile.hpp"
 
 namespace gla {
 
 namespace {
-
-struct SFrag {
-    bf16x8 hi, lo;
-};
-
-__device__ __forceinline__ f32x4 mma3(const SFrag& a, const SFrag& b, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void split1(float x, bf16& hi, bf16& lo) {
-    hi = (bf16)x;
-    lo = (bf16)(x - (float)hi);
-}
-
-// operand fragments of a split tile (hi plane at base, lo plane PLANE elements later)
-template <int P, int PLANE>
-__device__ __forceinline__ SFrag sld(const bf16* base, int i0, int k0) {
-    return SFrag{frag_ld<bf16, P, 1>(base, i0, k0), frag_ld<bf16, P, 1>(base + PLANE, i0, k0)};
-}
-template <int P, int PLANE>
-__device__ __forceinline__ SFrag scol(const bf16* base, int i0, int k0) {
-    return SFrag{frag_col<bf16, P, false>(base, i0, k0), frag_col<bf16, P, false>(base + PLANE, i0, k0)};
-}
-
-// eight consecutive fp32 values from global memory as a split fragment
-__device__ __forceinline__ SFrag split_ld8(const float* p, float& dot_with, const float* q) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-    SFrag f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        bf16 h, o;
-        split1(a[e], h, o);
-        f.hi[e] = h;
-        f.lo[e] = o;
-        split1(b[e], h, o);
-        f.hi[4 + e] = h;
-        f.lo[4 + e] = o;
-    }
-    if (q) {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(q);
-        const f32x4 d = *reinterpret_cast<const f32x4*>(q + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dot_with += a[e] * c[e] + b[e] * d[e];
-    }
-    return f;
-}
-
-// fp32 tile rows from registers to a split LDS tile (8-byte stores per plane)
-template <int D>
-__device__ __forceinline__ void store_rows_split(const TileRegs<float, D>& t, bf16* dst, int P, int PLANE) {
-    using TR = TileRegs<float, D>;
-#pragma unroll
-    for (int i = 0; i < TR::NVEC; ++i) {
-        const int idx = threadIdx.x + i * NT;
-        if (idx < TR::NV_TOT) {
-            const int row = idx / TR::VPR, cv = (idx % TR::VPR) * 4;
-            const float* f = reinterpret_cast<const float*>(&t.r[i]);
-            Vec4<bf16> hi, lo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bf16 h, o;
-                split1(f[e], h, o);
-                hi.v[e] = h;
-                lo.v[e] = o;
-            }
-            hi.store(dst + row * P + cv);
-            lo.store(dst + PLANE + row * P + cv);
-        }
-    }
-}
 
 // masked score tile (scalar gate: times exp(beta_r - beta_s)) to a split tile;
 // NAT: the tile was computed transposed (rows s, column r) and is stored [r][s];
@@ -107,19 +28,14 @@ __device__ __forceinline__ void store_masked_split(bf16* dst, const RevChunk& ck
     const int l = lane_id(), j = l >> 4, i = l & 15;
     const int row = NAT ? 16 * rt + i : 16 * st + i;          // stored row (r, or s)
     const int c0 = NAT ? 16 * st + 4 * j : 16 * rt + 4 * j;   // first of four stored columns
-    Vec4<bf16> hi, lo;
+    float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = NAT ? row : c0 + e, s = NAT ? c0 + e : row;
-        float x = 0.f;
-        if (live && s <= r && ck.doc[s] == ck.doc[r]) x = acc[e] * __expf(ck.beta[r] - ck.beta[s]);
-        bf16 h, o;
-        split1(x, h, o);
-        hi.v[e] = h;
-        lo.v[e] = o;
+        x[e] = 0.f;
+        if (live && s <= r && ck.doc[s] == ck.doc[r]) x[e] = acc[e] * __expf(ck.beta[r] - ck.beta[s]);
     }
-    hi.store(dst + row * P + c0);
-    lo.store(dst + PLANE + row * P + c0);
+    split4_store(x[0], x[1], x[2], x[3], dst + row * P + c0, dst + PLANE + row * P + c0);
 }
 
 constexpr int DK = 128, DV = 128, KS = 32;
