@@ -39,8 +39,10 @@ __device__ __forceinline__ void store_masked_split(bf16* dst, const RevChunk& ck
 }
 
 constexpr int DK = 128, DV = 128, KS = 32;
-constexpr int P64 = 72, PL64 = C * P64;                  // [64][64] split tiles
-constexpr int PW = 136, PLW = C * PW;                    // [64][128] split tiles
+// row pitches (bf16 elements): 16 mod 64 keeps the 16-byte row reads free of
+// LDS bank conflicts on gfx950 (measured); transposed reads are free at these too
+constexpr int P64 = 80, PL64 = C * P64;                  // [64][64] split tiles
+constexpr int PW = 144, PLW = C * PW;                    // [64][128] split tiles
 constexpr int PD = 68, PLD = DK * PD;                    // [128][64] split tile (state-gradient slice)
 constexpr int QK_BYTES = 2 * (3 * PL64 + 2 * PLW) * 2;
 constexpr int V_BYTES = 2 * (2 * PLW + 2 * PL64 + PLD) * 2;
@@ -123,12 +125,10 @@ __device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t b, int64_t 
         for (int ti = w; ti < 12; ti += 4) {
             const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
             const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
-            f32x4 acc = zero4();
-            if (ti < 10) {
-#pragma unroll
-                for (int n0 = 0; n0 < DV; n0 += KS)
-                    acc = mma3(sld<PW, PLW>(sV, 16 * st, n0), sld<PW, PLW>(sdO, 16 * rt, n0), acc);
-            }
+            const f32x4 acc = mma3_chain<DV / KS>(zero4(), ti < 10 ? DV / KS : 0, [&](int i, SFrag& A, SFrag& B) {
+                A = sld<PW, PLW>(sV, 16 * st, i * KS);
+                B = sld<PW, PLW>(sdO, 16 * rt, i * KS);
+            });
             store_masked_split<true, P64, PL64>(sdA, ck, rt, st, ti < 10, acc);
         }
         __syncthreads();
@@ -138,13 +138,15 @@ __device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t b, int64_t 
         float x[4][4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            f32x4 a1 = zero4(), a2 = zero4();
-            const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
-#pragma unroll
-            for (int k0 = 0; k0 < kend; k0 += KS)
-                a1 = mma3(scol<P64, PL64>(sK, 16 * w, k0), sld<P64, PL64>(sdA, 16 * rt, k0), a1);
-#pragma unroll
-            for (int kk = 0; kk < DV / KS; ++kk) a2 = mma3(s0f[kk], sld<PW, PLW>(sdO, 16 * rt, kk * KS), a2);
+            const int nk = (16 * (rt + 1) + KS - 1) / KS;
+            const f32x4 a1 = mma3_chain<C / KS>(zero4(), nk, [&](int i, SFrag& A, SFrag& B) {
+                A = scol<P64, PL64>(sK, 16 * w, i * KS);
+                B = sld<P64, PL64>(sdA, 16 * rt, i * KS);
+            });
+            const f32x4 a2 = mma3_chain<DV / KS>(zero4(), DV / KS, [&](int i, SFrag& A, SFrag& B) {
+                A = s0f[i];
+                B = sld<PW, PLW>(sdO, 16 * rt, i * KS);
+            });
             const int r = 16 * rt + i16;
             const float fq = ck.fq[r];
             const Vec4<bf16> qh = Vec4<bf16>::load(sQ + r * P64 + 16 * w + 4 * j4);
@@ -159,13 +161,15 @@ __device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t b, int64_t 
         float bsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            f32x4 a1 = zero4(), a2 = zero4();
-            const int kbeg = (16 * st / KS) * KS;
-#pragma unroll
-            for (int k0 = kbeg; k0 < C; k0 += KS)
-                a1 = mma3(scol<P64, PL64>(sQ, 16 * w, k0), scol<P64, PL64>(sdA, 16 * st, k0), a1);
-#pragma unroll
-            for (int kk = 0; kk < DV / KS; ++kk) a2 = mma3(dsf[kk], sld<PW, PLW>(sV, 16 * st, kk * KS), a2);
+            const int kb = 16 * st / KS;
+            const f32x4 a1 = mma3_chain<C / KS>(zero4(), C / KS - kb, [&](int i, SFrag& A, SFrag& B) {
+                A = scol<P64, PL64>(sQ, 16 * w, (kb + i) * KS);
+                B = scol<P64, PL64>(sdA, 16 * st, (kb + i) * KS);
+            });
+            const f32x4 a2 = mma3_chain<DV / KS>(zero4(), DV / KS, [&](int i, SFrag& A, SFrag& B) {
+                A = dsf[i];
+                B = sld<PW, PLW>(sV, 16 * st, i * KS);
+            });
             const int s = 16 * st + i16;
             const float fu = ck.fu[s];
             const Vec4<bf16> kh = Vec4<bf16>::load(sK + s * P64 + 16 * w + 4 * j4);
@@ -262,12 +266,10 @@ __device__ void sv(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t 
     for (int ti = w; ti < 12; ti += 4) {
         const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
         const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
-        f32x4 acc = zero4();
-        if (ti < 10) {
-#pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += KS)
-                acc = mma3(sld<PW, PLW>(sQ, 16 * rt, k0), sld<PW, PLW>(sK, 16 * st, k0), acc);
-        }
+        const f32x4 acc = mma3_chain<DK / KS>(zero4(), ti < 10 ? DK / KS : 0, [&](int i, SFrag& A, SFrag& B) {
+            A = sld<PW, PLW>(sQ, 16 * rt, i * KS);
+            B = sld<PW, PLW>(sK, 16 * st, i * KS);
+        });
         store_masked_split<false, P64, PL64>(sAT, ck, rt, st, ti < 10, acc);
     }
     __syncthreads();
@@ -276,14 +278,15 @@ __device__ void sv(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t 
     float* dvo = (float*)a.dv + ((b * T_ + t0) * a.H + h) * DV + n0s + 16 * w + 4 * j4;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-        f32x4 a1 = zero4(), a2 = zero4();
-        const int kbeg = (16 * st / KS) * KS;
-#pragma unroll
-        for (int k0 = kbeg; k0 < C; k0 += KS)
-            a1 = mma3(scol<P64, PL64>(sdO, 16 * w, k0), sld<P64, PL64>(sAT, 16 * st, k0), a1);
-#pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += KS)
-            a2 = mma3(scol<PD, PLD>(sdS, 16 * w, k0), sld<PW, PLW>(sK, 16 * st, k0), a2);
+        const int kb = 16 * st / KS;
+        const f32x4 a1 = mma3_chain<C / KS>(zero4(), C / KS - kb, [&](int i, SFrag& A, SFrag& B) {
+            A = scol<P64, PL64>(sdO, 16 * w, (kb + i) * KS);
+            B = sld<P64, PL64>(sAT, 16 * st, (kb + i) * KS);
+        });
+        const f32x4 a2 = mma3_chain<DK / KS>(zero4(), DK / KS, [&](int i, SFrag& A, SFrag& B) {
+            A = scol<PD, PLD>(sdS, 16 * w, i * KS);
+            B = sld<PW, PLW>(sK, 16 * st, i * KS);
+        });
         const int s = 16 * st + i16;
         const float fu = ck.fu[s];
         float dv[4];

@@ -113,4 +113,27 @@ __device__ __forceinline__ SFrag scol_ctile(const bf16* base, int i0, int k0) {
 // 16..31 of a 32-wide step, ctile order)
 __device__ __forceinline__ SFrag split_acc(const f32x4& lo, const f32x4& hi) { return split8(lo, hi); }
 
+// acc += sum over steps i < n of A_i B_i (three-product split form); ld(i, A, B)
+// reads step i's operands.  The reads of step i + 1 are issued before step
+// i's products (scheduling barriers keep the compiler from merging the two),
+// so LDS latency hides behind the matrix cores.  NMAX bounds n at compile time.
+template <int NMAX, typename LD>
+__device__ __forceinline__ f32x4 mma3_chain(f32x4 acc, int n, LD&& ld) {
+    SFrag a0, b0;
+    if (n > 0) ld(0, a0, b0);
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        if (i < n) {
+            SFrag a1, b1;
+            if (i + 1 < n) ld(i + 1, a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            acc = mma3(a0, b0, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            a0 = a1;
+            b0 = b1;
+        }
+    }
+    return acc;
+}
+
 }  // namespace gla

@@ -31,8 +31,11 @@
 //               zero, chunks last to first, dL <- decay dL + QR^T dO with
 //               QR = q exp(beta) on the chunk's first document (the dS update
 //               of the reverse pass).  Its diagonal part is D_p again.
+#include <type_traits>
+
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
+#include "gla_split.hpp"
 #include "gla_tile.hpp"
 
 namespace gla {
@@ -238,22 +241,186 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
     }
 }
 
+// fp32 inputs with the scalar gate: the same passes on the bf16 matrix cores,
+// every fp32 operand split into bf16 hi/lo halves (three products, gla_split.hpp).
+// Every wave computes the chunk's gate prefix itself (lane = row) so that the
+// row factors can go into k while it is staged: KU = fu k is stored split, and
+// the update needs no further scaling.  Operand reads run one step ahead of the
+// products.
+template <int NB>
+struct StatesLdsS {
+    static constexpr int PB = 64 + 8;   // [64 rows][64 channels], transposed reads
+    static constexpr int PN = NB + 8;   // [64 rows][NB columns], transposed reads
+    bf16 sKu[2 * C * PB];
+    bf16 sV[2 * C * PN];
+};
+
+template <int DK, int DV, int MODE, int NB>
+__device__ __forceinline__ void states_body_f32s(const PassArgs& a, StatesLdsS<NB>& sm, int64_t L) {
+    constexpr bool REV = MODE == ST_SUM_REV || MODE == ST_DSTATES;
+    constexpr int CB = 64, KS = 32;
+    constexpr int NCB = DK / CB, NNB = DV / NB;
+    constexpr int PB = StatesLdsS<NB>::PB, PLB = C * PB;
+    constexpr int PN = StatesLdsS<NB>::PN, PLN = C * PN;
+    constexpr int NNT = NB / 16;
+
+    const int64_t P = a.P;
+    const int blk = (int)(L % (NCB * NNB));
+    const int64_t piece = (L / (NCB * NNB)) % P;
+    const int64_t bh = L / (NCB * NNB) / P;
+    const int c0 = (blk / NNB) * CB, n0 = (blk % NNB) * NB;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t G = a.H / a.Hqk, hq = h / G;
+    const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
+    const int64_t T_ = a.T;
+    const int64_t NC = (T_ + C - 1) / C;
+    const int64_t cbeg = piece * a.PL;
+    const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
+
+    const float* k = (const float*)(REV ? a.q : a.k);
+    const float* v = (const float*)(REV ? a.dO : a.v);
+    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const float* kbase = k + b * T_ * rs_qk + hq * DK + c0;
+    const float* vbase = v + b * T_ * rs_v + h * DV + n0;
+    const float* gbase = (const float*)a.g + b * T_ * a.H + h;
+
+    f32x4 St[NNT];
+    const int cme = c0 + 16 * w + i16;
+    const int64_t prow = ((bh * P + piece) * DK + cme) * DV + n0;
+    const int64_t hrow = (bh * DK + cme) * DV + n0;
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = 16 * nt + 4 * j4 + e;
+            float x = 0.f;
+            if constexpr (MODE == ST_STATES) {
+                if (P > 1) x = a.S_in[prow + n];
+                else if (a.h0) x = a.h0[hrow + n];
+            } else if constexpr (MODE == ST_DSTATES) {
+                if (P > 1) x = a.dS_in[prow + n];
+                else if (a.dhT) x = a.dhT[hrow + n];
+            }
+            St[nt][e] = x;
+        }
+    float dprod = 1.f;
+
+    TileRegs<float, CB> pk;
+    TileRegs<float, NB> pv;
+    RowRegs rr;
+    auto prefetch = [&](int64_t t0) {
+        const int64_t nv64 = T_ - t0;
+        const int nvalid = nv64 < C ? (int)nv64 : C;
+        pk.load(kbase + t0 * rs_qk, rs_qk, nvalid);
+        pv.load(vbase + t0 * rs_v, rs_v, nvalid);
+        rr.load(gbase + t0 * a.H, a.H, a.seg, b, T_, t0, nvalid, true);
+    };
+    auto store_state = [&](int64_t ci) {
+        float* dst = MODE == ST_STATES ? (float*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cme) * DV + n0
+                                       : (float*)a.ws_dS + ((bh * NC + ci) * DK + cme) * DV + n0;
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt + 4 * j4) = St[nt];
+    };
+    const int64_t nchunks = cend - cbeg;
+    prefetch((REV ? cend - 1 : cbeg) * C);
+
+    for (int64_t ii = 0; ii < nchunks; ++ii) {
+        const int64_t ci = REV ? cend - 1 - ii : cbeg + ii;
+        const int64_t t0 = ci * C;
+        if constexpr (MODE == ST_STATES || MODE == ST_DSTATES) store_state(ci);
+        // chunk structure in every wave (lane = row)
+        const uint64_t msk = __ballot(rr.reset);
+        const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
+        const int first_reset = msk ? __builtin_ctzll(msk) : C;
+        const float beta = wave_incl_scan(rr.g);
+        const float Gam = __shfl(beta, 63, 64);
+        float fu;
+        if constexpr (REV) fu = l < first_reset ? __expf(beta) : 0.f;
+        else fu = l >= last_reset ? __expf(Gam - beta) : 0.f;
+        const float dec = msk ? 0.f : __expf(Gam);
+        // stage KU = fu k and v, split
+        {
+            using TR = TileRegs<float, CB>;
+            static_assert(TR::NV_TOT % NT == 0, "");
+#pragma unroll
+            for (int i = 0; i < TR::NVEC; ++i) {
+                const int idx = threadIdx.x + i * NT;
+                const int row = idx / TR::VPR, cv = (idx % TR::VPR) * 4;
+                const float f = __shfl(fu, row, 64);
+                const f32x4 x = __builtin_bit_cast(f32x4, pk.r[i]);
+                split4_store(x[0] * f, x[1] * f, x[2] * f, x[3] * f, sm.sKu + row * PB + cv,
+                             sm.sKu + PLB + row * PB + cv);
+            }
+        }
+        store_rows_split<NB>(pv, sm.sV, PN, PLN);
+        __syncthreads();
+        if (ii + 1 < nchunks) prefetch(REV ? t0 - C : t0 + C);
+
+        // S^T[n][c] <- decay S^T[n][c] + sum_s v[s][n] KU[s][c], in place
+        dprod *= dec;
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) St[nt][e] *= dec;
+        SFrag kf[C / KS];
+#pragma unroll
+        for (int kk = 0; kk < C / KS; ++kk) kf[kk] = scol<PB, PLB>(sm.sKu, 16 * w, kk * KS);
+        SFrag va = scol<PN, PLN>(sm.sV, 0, 0);
+#pragma unroll
+        for (int idx = 0; idx < NNT * (C / KS); ++idx) {
+            const int kk = idx / NNT, nt = idx % NNT;
+            SFrag vb;
+            if (idx + 1 < NNT * (C / KS))
+                vb = scol<PN, PLN>(sm.sV, 16 * ((idx + 1) % NNT), KS * ((idx + 1) / NNT));
+            __builtin_amdgcn_sched_barrier(0);
+            St[nt] = mma3(va, kf[kk], St[nt]);
+            __builtin_amdgcn_sched_barrier(0);
+            va = vb;
+        }
+        __syncthreads();
+    }
+    if constexpr (MODE == ST_STATES) {
+        if (piece == P - 1) store_state(NC);
+    } else if constexpr (MODE == ST_DSTATES) {
+        if (piece == 0 && a.dh0) {
+#pragma unroll
+            for (int nt = 0; nt < NNT; ++nt)
+                *reinterpret_cast<f32x4*>(a.dh0 + hrow + 16 * nt + 4 * j4) = St[nt];
+        }
+    } else {
+#pragma unroll
+        for (int nt = 0; nt < NNT; ++nt)
+            *reinterpret_cast<f32x4*>(a.L_out[MODE == ST_SUM_REV ? 1 : 0] + prow + 16 * nt + 4 * j4) = St[nt];
+        if (MODE == ST_SUM_FWD && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
+    }
+}
+
+// shared memory of a state pass: the split layout for fp32 with the scalar gate
+template <typename T, bool VEC, int NB>
+using StatesLdsFor = typename std::conditional<(sizeof(T) == 4 && !VEC), StatesLdsS<NB>, StatesLds<T, VEC, NB>>::type;
+
+template <typename T, bool VEC, int DK, int DV, int MODE, int NB>
+__device__ __forceinline__ void states_any(const PassArgs& a, StatesLdsFor<T, VEC, NB>& sm, int64_t L) {
+    if constexpr (sizeof(T) == 4 && !VEC) states_body_f32s<DK, DV, MODE, NB>(a, sm, L);
+    else states_body<T, VEC, DK, DV, MODE, NB>(a, sm, L);
+}
+
 template <typename T, bool VEC, int DK, int DV, int MODE, int NB>
 __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
-    __shared__ __attribute__((aligned(16))) StatesLds<T, VEC, NB> sm;
+    __shared__ __attribute__((aligned(16))) StatesLdsFor<T, VEC, NB> sm;
     const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
-    states_body<T, VEC, DK, DV, MODE, NB>(a, sm, xcd_logical_block(n));
+    states_any<T, VEC, DK, DV, MODE, NB>(a, sm, xcd_logical_block(n));
 }
 
 // Two independent passes in one launch (the first half of the grid runs MODE_A,
 // the second MODE_B), so that both directions share the device.
 template <typename T, bool VEC, int DK, int DV, int MODE_A, int MODE_B, int NB>
 __global__ __launch_bounds__(NT) void k_states2(const PassArgs a) {
-    __shared__ __attribute__((aligned(16))) StatesLds<T, VEC, NB> sm;
+    __shared__ __attribute__((aligned(16))) StatesLdsFor<T, VEC, NB> sm;
     const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
     const int64_t L = xcd_logical_block(2 * n);
-    if (L < n) states_body<T, VEC, DK, DV, MODE_A, NB>(a, sm, L);
-    else states_body<T, VEC, DK, DV, MODE_B, NB>(a, sm, L - n);
+    if (L < n) states_any<T, VEC, DK, DV, MODE_A, NB>(a, sm, L);
+    else states_any<T, VEC, DK, DV, MODE_B, NB>(a, sm, L - n);
 }
 
 template <typename T, bool VEC, int DK, int DV, int NB>
