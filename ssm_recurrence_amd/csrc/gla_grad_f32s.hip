@@ -46,7 +46,6 @@ constexpr int PW = 144, PLW = C * PW;                    // [64][128] split tile
 constexpr int PD = 68, PLD = DK * PD;                    // [128][64] split tile (state-gradient slice)
 constexpr int QK_BYTES = 2 * (3 * PL64 + 2 * PLW) * 2;
 constexpr int V_BYTES = 2 * (2 * PLW + 2 * PL64 + PLD) * 2;
-constexpr int BYTES = QK_BYTES > V_BYTES ? QK_BYTES : V_BYTES;
 
 struct SmallS {
     RevChunk ck;
@@ -55,13 +54,73 @@ struct SmallS {
 };
 
 // ============================================================== QK role
-// One workgroup per (b, q/k head, chunk, 64-channel slice): q and k are loaded
-// once and the G heads that read them are visited in turn, each with its own v,
-// dO, gate, state and state gradient; dq and dk are summed over those heads in
-// registers (the head-sharing reduction of the FLAT page, Pallas Kernels >
-// Gated Linear Attention, done in place of per-head buffers), and each head's
-// log-gate partial sums are written for the finisher.
-__device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t b, int64_t hq, int64_t ci, int slice) {
+// Persistent workgroups over (b, q/k head, chunk, 64-channel slice) items: q and
+// k are loaded once per item and the G heads that read them are visited in
+// turn, each with its own v, dO, gate, state and state gradient; dq and dk are
+// summed over those heads in registers (the head-sharing reduction of the FLAT
+// page, Pallas Kernels > Gated Linear Attention, done in place of per-head
+// buffers), and each head's log-gate partial sums are written for the
+// finisher.  The next head's inputs (or the next item's q, k and first head)
+// are loaded into registers while the current head computes.
+
+// inputs of one head of a QK item
+struct QKHeadRegs {
+    TileRegs<float, DV> pv, pdo;
+    RowRegs rr;
+    f32x4 s0[2 * DV / KS], ds[2 * DV / KS];  // S0 and dS1 row cw + i16, channels of lane group j4
+};
+
+struct QKItem {
+    int64_t b, hq, ci;
+    int slice;
+};
+__device__ __forceinline__ QKItem qk_item(const RevArgs& a, int64_t item) {
+    const int64_t NC = (a.T + C - 1) / C;
+    QKItem it;
+    it.slice = (int)(item % 2);
+    it.ci = (item / 2) % NC;
+    const int64_t bq = item / 2 / NC;
+    it.b = bq / a.Hqk;
+    it.hq = bq % a.Hqk;
+    return it;
+}
+
+__device__ __forceinline__ void qk_load_qk(const RevArgs& a, const QKItem& it, TileRegs<float, 64>& pq,
+                                           TileRegs<float, 64>& pk) {
+    const int64_t T_ = a.T, t0 = it.ci * C;
+    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+    const int64_t rs_qk = a.Hqk * DK;
+    const int64_t off = (it.b * T_ + t0) * rs_qk + it.hq * DK + it.slice * 64;
+    pq.load((const float*)a.q + off, rs_qk, nvalid);
+    pk.load((const float*)a.k + off, rs_qk, nvalid);
+}
+
+__device__ __forceinline__ void qk_load_head(const RevArgs& a, const QKItem& it, int64_t gi, QKHeadRegs& R) {
+    const int64_t T_ = a.T, t0 = it.ci * C;
+    const int64_t NC = (T_ + C - 1) / C;
+    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+    const int64_t G = a.H / a.Hqk;
+    const int64_t h = it.hq * G + gi, bh = it.b * a.H + h;
+    const int64_t rs_v = a.H * DV;
+    const int w = wave_id(), j4 = lane_id() >> 4, i16 = lane_id() & 15;
+    const int cw = it.slice * 64 + 16 * w;
+    R.pv.load((const float*)a.v + (it.b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
+    R.pdo.load((const float*)a.dO + (it.b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
+    if (w == 0) R.rr.load((const float*)a.g + (it.b * T_ + t0) * a.H + h, a.H, a.seg, it.b, T_, t0, nvalid, true);
+    const float* S0 = (const float*)a.ws_S + ((bh * (NC + 1) + it.ci) * DK + cw + i16) * DV + 8 * j4;
+    const float* dS1 = (const float*)a.ws_dS + ((bh * NC + it.ci) * DK + cw + i16) * DV + 8 * j4;
+#pragma unroll
+    for (int kk = 0; kk < DV / KS; ++kk) {
+        R.s0[2 * kk] = *reinterpret_cast<const f32x4*>(S0 + kk * KS);
+        R.s0[2 * kk + 1] = *reinterpret_cast<const f32x4*>(S0 + kk * KS + 4);
+        R.ds[2 * kk] = *reinterpret_cast<const f32x4*>(dS1 + kk * KS);
+        R.ds[2 * kk + 1] = *reinterpret_cast<const f32x4*>(dS1 + kk * KS + 4);
+    }
+}
+
+__global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[QK_BYTES];
+    __shared__ SmallS sm;
     bf16* sQ = reinterpret_cast<bf16*>(lds);
     bf16* sK = sQ + 2 * PL64;
     bf16* sdA = sK + 2 * PL64;  // [r][s]
@@ -71,255 +130,282 @@ __device__ void sqk(const RevArgs& a, char* lds, SmallS& sm, int64_t b, int64_t 
 
     const int64_t G = a.H / a.Hqk;
     const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
-    const int cs0 = slice * 64;
-    const int cw = cs0 + 16 * w;
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
-    const int64_t t0 = ci * C;
-    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
-    const float* qrow = (const float*)a.q + (b * T_ + t0) * rs_qk + hq * DK + cs0;
-    const float* krow = (const float*)a.k + (b * T_ + t0) * rs_qk + hq * DK + cs0;
+    const int64_t nitems = a.B * a.Hqk * NC * 2;
+    const int64_t stride = gridDim.x;
 
-    {
-        TileRegs<float, 64> pq, pk;
-        pq.load(qrow, rs_qk, nvalid);
-        pk.load(krow, rs_qk, nvalid);
+    TileRegs<float, 64> pq, pk;
+    QKHeadRegs hr;
+    int64_t item = xcd_logical_block(gridDim.x);
+    if (item < nitems) {
+        const QKItem it = qk_item(a, item);
+        qk_load_qk(a, it, pq, pk);
+        qk_load_head(a, it, 0, hr);
+    }
+    for (; item < nitems; item += stride) {
+        const QKItem it = qk_item(a, item);
+        const int64_t b = it.b, hq = it.hq, ci = it.ci;
+        const int slice = it.slice;
+        const int cw = slice * 64 + 16 * w;
+        const int64_t t0 = ci * C;
+        const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+
         store_rows_split<64>(pq, sQ, P64, PL64);
         store_rows_split<64>(pk, sK, P64, PL64);
-    }
-    float dqs[4][4], dks[4][4];  // dq, dk summed over the heads of the group
+        float dqs[4][4], dks[4][4];  // dq, dk summed over the heads of the group
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dqs[rt][e] = dks[rt][e] = 0.f;
+            for (int e = 0; e < 4; ++e) dqs[rt][e] = dks[rt][e] = 0.f;
 
-    for (int64_t gi = 0; gi < G; ++gi) {
-        const int64_t h = hq * G + gi, bh = b * a.H + h;
-        const float* vrow = (const float*)a.v + (b * T_ + t0) * rs_v + h * DV;
-        const float* dorow = (const float*)a.dO + (b * T_ + t0) * rs_v + h * DV;
-        const float* grow = (const float*)a.g + (b * T_ + t0) * a.H + h;
-        const float* S0 = (const float*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
-        const float* dS1 = (const float*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
-
-        TileRegs<float, DV> pv, pdo;
-        RowRegs rr;
-        pv.load(vrow, rs_v, nvalid);
-        pdo.load(dorow, rs_v, nvalid);
-        if (w == 0) rr.load(grow, a.H, a.seg, b, T_, t0, nvalid, true);
-        // S0 and dS1 rows cw + i16 as split A operands (k = n); rowsum(S0 * dS1) in fp32
-        float sd = 0.f;
-        SFrag s0f[DV / KS], dsf[DV / KS];
+        for (int64_t gi = 0; gi < G; ++gi) {
+            const int64_t h = hq * G + gi, bh = b * a.H + h;
+            // S0 and dS1 rows cw + i16 as split A operands (k = n); rowsum(S0 * dS1) in fp32
+            float sd = 0.f;
+            SFrag s0f[DV / KS], dsf[DV / KS];
 #pragma unroll
-        for (int kk = 0; kk < DV / KS; ++kk) {
-            float unused = 0.f;
-            s0f[kk] = split_ld8(S0 + kk * KS + 8 * j4, sd, dS1 + kk * KS + 8 * j4);
-            dsf[kk] = split_ld8(dS1 + kk * KS + 8 * j4, unused, nullptr);
+            for (int kk = 0; kk < DV / KS; ++kk) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sd += hr.s0[2 * kk][e] * hr.ds[2 * kk][e] + hr.s0[2 * kk + 1][e] * hr.ds[2 * kk + 1][e];
+                s0f[kk] = split8(hr.s0[2 * kk], hr.s0[2 * kk + 1]);
+                dsf[kk] = split8(hr.ds[2 * kk], hr.ds[2 * kk + 1]);
+            }
+            store_rows_split<DV>(hr.pv, sV, PW, PLW);
+            store_rows_split<DV>(hr.pdo, sdO, PW, PLW);
+            if (w == 0) rev_chunk_info<float, false>(&ck, hr.rr);
+            __syncthreads();
+            // the next head's inputs, or the next item's
+            if (gi + 1 < G) {
+                qk_load_head(a, it, gi + 1, hr);
+            } else if (item + stride < nitems) {
+                const QKItem nx = qk_item(a, item + stride);
+                qk_load_qk(a, nx, pq, pk);
+                qk_load_head(a, nx, 0, hr);
+            }
+
+            // dA^T = v dO^T tiles, masked, stored dA[r][s]
+            for (int ti = w; ti < 12; ti += 4) {
+                const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
+                const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+                const f32x4 acc =
+                    mma3_chain<DV / KS>(zero4(), ti < 10 ? DV / KS : 0, [&](int i, SFrag& A, SFrag& B) {
+                        A = sld<PW, PLW>(sV, 16 * st, i * KS);
+                        B = sld<PW, PLW>(sdO, 16 * rt, i * KS);
+                    });
+                store_masked_split<true, P64, PL64>(sdA, ck, rt, st, ti < 10, acc);
+            }
+            __syncthreads();
+
+            // q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e),
+            // from the split tiles (hi + lo)
+            float x[4][4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int nk = (16 * (rt + 1) + KS - 1) / KS;
+                const f32x4 a1 = mma3_chain<C / KS>(zero4(), nk, [&](int i, SFrag& A, SFrag& B) {
+                    A = scol<P64, PL64>(sK, 16 * w, i * KS);
+                    B = sld<P64, PL64>(sdA, 16 * rt, i * KS);
+                });
+                const f32x4 a2 = mma3_chain<DV / KS>(zero4(), DV / KS, [&](int i, SFrag& A, SFrag& B) {
+                    A = s0f[i];
+                    B = sld<PW, PLW>(sdO, 16 * rt, i * KS);
+                });
+                const int r = 16 * rt + i16;
+                const float fq = ck.fq[r];
+                const Vec4<bf16> qh = Vec4<bf16>::load(sQ + r * P64 + 16 * w + 4 * j4);
+                const Vec4<bf16> ql = Vec4<bf16>::load(sQ + PL64 + r * P64 + 16 * w + 4 * j4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float dq = a1[e] + fq * a2[e];
+                    x[rt][e] = (qh.get(e) + ql.get(e)) * dq;
+                    dqs[rt][e] += dq;
+                }
+            }
+            float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int kb = 16 * st / KS;
+                const f32x4 a1 = mma3_chain<C / KS>(zero4(), C / KS - kb, [&](int i, SFrag& A, SFrag& B) {
+                    A = scol<P64, PL64>(sQ, 16 * w, (kb + i) * KS);
+                    B = scol<P64, PL64>(sdA, 16 * st, (kb + i) * KS);
+                });
+                const f32x4 a2 = mma3_chain<DV / KS>(zero4(), DV / KS, [&](int i, SFrag& A, SFrag& B) {
+                    A = dsf[i];
+                    B = sld<PW, PLW>(sV, 16 * st, i * KS);
+                });
+                const int s = 16 * st + i16;
+                const float fu = ck.fu[s];
+                const Vec4<bf16> kh = Vec4<bf16>::load(sK + s * P64 + 16 * w + 4 * j4);
+                const Vec4<bf16> kl = Vec4<bf16>::load(sK + PL64 + s * P64 + 16 * w + 4 * j4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float inter = fu * a2[e];
+                    const float dk = a1[e] + inter;
+                    const float kr = kh.get(e) + kl.get(e);
+                    x[st][e] -= kr * dk;
+                    bsum[e] += kr * inter;
+                    dks[st][e] += dk;
+                }
+            }
+            sd += __shfl_xor(sd, 16, 64);
+            sd += __shfl_xor(sd, 32, 64);
+            float bb = 0.f;  // sum over this lane group's four channels of rowsum(S1 * dS1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bb += ck.decay * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
+            // partial sums over this workgroup's channels; a finisher adds the two slices
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                float y = x[rt][0] + x[rt][1] + x[rt][2] + x[rt][3];
+                y += __shfl_xor(y, 16, 64);
+                y += __shfl_xor(y, 32, 64);
+                if (j4 == 0) sm.sXs[w][16 * rt + i16] = y;
+            }
+            bb += __shfl_xor(bb, 16, 64);
+            bb += __shfl_xor(bb, 32, 64);
+            if (l == 0) sm.sBs[w] = bb;
+            __syncthreads();  // also: every wave is done with this head's v, dO and dA
+            if (w == 0) {
+                const int r = l;
+                const float tot = sm.sXs[0][r] + sm.sXs[1][r] + sm.sXs[2][r] + sm.sXs[3][r];
+                if (r < nvalid) a.ws_xs[(bh * 2 + slice) * T_ + t0 + r] = tot;
+                if (r == 0) a.ws_bnd[(bh * 2 + slice) * NC + ci] = sm.sBs[0] + sm.sBs[1] + sm.sBs[2] + sm.sBs[3];
+            }
         }
-        store_rows_split<DV>(pv, sV, PW, PLW);
-        store_rows_split<DV>(pdo, sdO, PW, PLW);
-        if (w == 0) rev_chunk_info<float, false>(&ck, rr);
-        __syncthreads();
-
-        // dA^T = v dO^T tiles, masked, stored dA[r][s]
-        for (int ti = w; ti < 12; ti += 4) {
-            const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-            const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
-            const f32x4 acc = mma3_chain<DV / KS>(zero4(), ti < 10 ? DV / KS : 0, [&](int i, SFrag& A, SFrag& B) {
-                A = sld<PW, PLW>(sV, 16 * st, i * KS);
-                B = sld<PW, PLW>(sdO, 16 * rt, i * KS);
-            });
-            store_masked_split<true, P64, PL64>(sdA, ck, rt, st, ti < 10, acc);
-        }
-        __syncthreads();
-
-        // q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e),
-        // from the split tiles (hi + lo)
-        float x[4][4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const int nk = (16 * (rt + 1) + KS - 1) / KS;
-            const f32x4 a1 = mma3_chain<C / KS>(zero4(), nk, [&](int i, SFrag& A, SFrag& B) {
-                A = scol<P64, PL64>(sK, 16 * w, i * KS);
-                B = sld<P64, PL64>(sdA, 16 * rt, i * KS);
-            });
-            const f32x4 a2 = mma3_chain<DV / KS>(zero4(), DV / KS, [&](int i, SFrag& A, SFrag& B) {
-                A = s0f[i];
-                B = sld<PW, PLW>(sdO, 16 * rt, i * KS);
-            });
             const int r = 16 * rt + i16;
-            const float fq = ck.fq[r];
-            const Vec4<bf16> qh = Vec4<bf16>::load(sQ + r * P64 + 16 * w + 4 * j4);
-            const Vec4<bf16> ql = Vec4<bf16>::load(sQ + PL64 + r * P64 + 16 * w + 4 * j4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float dq = a1[e] + fq * a2[e];
-                x[rt][e] = (qh.get(e) + ql.get(e)) * dq;
-                dqs[rt][e] += dq;
+            if (r < nvalid) {
+                const int64_t o = ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4;
+                store4<float>((float*)a.dq + o, dqs[rt]);
+                store4<float>((float*)a.dk + o, dks[rt]);
             }
-        }
-        float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int kb = 16 * st / KS;
-            const f32x4 a1 = mma3_chain<C / KS>(zero4(), C / KS - kb, [&](int i, SFrag& A, SFrag& B) {
-                A = scol<P64, PL64>(sQ, 16 * w, (kb + i) * KS);
-                B = scol<P64, PL64>(sdA, 16 * st, (kb + i) * KS);
-            });
-            const f32x4 a2 = mma3_chain<DV / KS>(zero4(), DV / KS, [&](int i, SFrag& A, SFrag& B) {
-                A = dsf[i];
-                B = sld<PW, PLW>(sV, 16 * st, i * KS);
-            });
-            const int s = 16 * st + i16;
-            const float fu = ck.fu[s];
-            const Vec4<bf16> kh = Vec4<bf16>::load(sK + s * P64 + 16 * w + 4 * j4);
-            const Vec4<bf16> kl = Vec4<bf16>::load(sK + PL64 + s * P64 + 16 * w + 4 * j4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float inter = fu * a2[e];
-                const float dk = a1[e] + inter;
-                const float kr = kh.get(e) + kl.get(e);
-                x[st][e] -= kr * dk;
-                bsum[e] += kr * inter;
-                dks[st][e] += dk;
-            }
-        }
-        sd += __shfl_xor(sd, 16, 64);
-        sd += __shfl_xor(sd, 32, 64);
-        float bb = 0.f;  // sum over this lane group's four channels of rowsum(S1 * dS1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bb += ck.decay * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
-        // partial sums over this workgroup's channels; a finisher adds the two slices
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            float y = x[rt][0] + x[rt][1] + x[rt][2] + x[rt][3];
-            y += __shfl_xor(y, 16, 64);
-            y += __shfl_xor(y, 32, 64);
-            if (j4 == 0) sm.sXs[w][16 * rt + i16] = y;
-        }
-        bb += __shfl_xor(bb, 16, 64);
-        bb += __shfl_xor(bb, 32, 64);
-        if (l == 0) sm.sBs[w] = bb;
-        __syncthreads();  // also: every wave is done with this head's v, dO and dA
-        if (w == 0) {
-            const int r = l;
-            const float tot = sm.sXs[0][r] + sm.sXs[1][r] + sm.sXs[2][r] + sm.sXs[3][r];
-            if (r < nvalid) a.ws_xs[(bh * 2 + slice) * T_ + t0 + r] = tot;
-            if (r == 0) a.ws_bnd[(bh * 2 + slice) * NC + ci] = sm.sBs[0] + sm.sBs[1] + sm.sBs[2] + sm.sBs[3];
-        }
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int r = 16 * rt + i16;
-        if (r < nvalid) {
-            const int64_t o = ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4;
-            store4<float>((float*)a.dq + o, dqs[rt]);
-            store4<float>((float*)a.dk + o, dks[rt]);
         }
     }
 }
 
 // ============================================================== V role
-__device__ void sv(const RevArgs& a, char* lds, SmallS& sm, int64_t bh, int64_t ci, int slice) {
+// Persistent workgroups over (b, head, chunk, 64-column slice) items; the next
+// item's inputs are loaded into registers while the current item computes.
+struct VRegs {
+    TileRegs<float, DK> pq, pk;
+    TileRegs<float, 64> pdo, pds0, pds1;
+    RowRegs rr;
+};
+struct VItem {
+    int64_t b, h, hq, ci;
+    int slice;
+};
+__device__ __forceinline__ VItem v_item(const RevArgs& a, int64_t item) {
+    const int64_t NC = (a.T + C - 1) / C;
+    const int64_t G = a.H / a.Hqk;
+    VItem it;
+    it.slice = (int)(item % 2);
+    const int64_t gi = (item / 2) % G;
+    it.ci = (item / 2 / G) % NC;
+    const int64_t bq = item / 2 / G / NC;
+    it.b = bq / a.Hqk;
+    it.hq = bq % a.Hqk;
+    it.h = it.hq * G + gi;
+    return it;
+}
+__device__ __forceinline__ void v_load(const RevArgs& a, const VItem& it, VRegs& R) {
+    const int64_t T_ = a.T, t0 = it.ci * C;
+    const int64_t NC = (T_ + C - 1) / C;
+    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t bh = it.b * a.H + it.h;
+    const int n0s = it.slice * 64;
+    R.pq.load((const float*)a.q + (it.b * T_ + t0) * rs_qk + it.hq * DK, rs_qk, nvalid);
+    R.pk.load((const float*)a.k + (it.b * T_ + t0) * rs_qk + it.hq * DK, rs_qk, nvalid);
+    R.pdo.load((const float*)a.dO + (it.b * T_ + t0) * rs_v + it.h * DV + n0s, rs_v, nvalid);
+    const float* dS1 = (const float*)a.ws_dS + (bh * NC + it.ci) * DK * DV + n0s;
+    R.pds0.load(dS1, DV, 64);
+    R.pds1.load(dS1 + (int64_t)64 * DV, DV, 64);
+    if (wave_id() == 0)
+        R.rr.load((const float*)a.g + (it.b * T_ + t0) * a.H + it.h, a.H, a.seg, it.b, T_, t0, nvalid, true);
+}
+
+__global__ __launch_bounds__(NT) void k_grad_f32s_v(const RevArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[V_BYTES];
+    __shared__ RevChunk ck;
     bf16* sQ = reinterpret_cast<bf16*>(lds);
     bf16* sK = sQ + 2 * PLW;
     bf16* sdO = sK + 2 * PLW;   // [r][64 columns of the slice]
     bf16* sAT = sdO + 2 * PL64; // [s][r]
     bf16* sdS = sAT + 2 * PL64; // [c][64 columns]
-    RevChunk& ck = sm.ck;
 
-    const int64_t b = bh / a.H, h = bh % a.H;
-    const int64_t G = a.H / a.Hqk, hq = h / G;
     const int w = wave_id(), j4 = lane_id() >> 4, i16 = lane_id() & 15;
-    const int n0s = slice * 64;
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
-    const int64_t t0 = ci * C;
-    const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
-    const float* qrow = (const float*)a.q + (b * T_ + t0) * rs_qk + hq * DK;
-    const float* krow = (const float*)a.k + (b * T_ + t0) * rs_qk + hq * DK;
-    const float* dorow = (const float*)a.dO + (b * T_ + t0) * rs_v + h * DV + n0s;
-    const float* grow = (const float*)a.g + (b * T_ + t0) * a.H + h;
-    const float* dS1 = (const float*)a.ws_dS + (bh * NC + ci) * DK * DV + n0s;
+    const int64_t nitems = a.B * a.H * NC * 2;
+    const int64_t stride = gridDim.x;
 
-    {
-        TileRegs<float, DK> pq, pk;
-        TileRegs<float, 64> pdo, pds0, pds1;
-        RowRegs rr;
-        pq.load(qrow, rs_qk, nvalid);
-        pk.load(krow, rs_qk, nvalid);
-        pdo.load(dorow, rs_v, nvalid);
-        pds0.load(dS1, DV, 64);
-        pds1.load(dS1 + (int64_t)64 * DV, DV, 64);
-        if (w == 0) rr.load(grow, a.H, a.seg, b, T_, t0, nvalid, true);
-        store_rows_split<DK>(pq, sQ, PW, PLW);
-        store_rows_split<DK>(pk, sK, PW, PLW);
-        store_rows_split<64>(pdo, sdO, P64, PL64);
-        store_rows_split<64>(pds0, sdS, PD, PLD);
-        store_rows_split<64>(pds1, sdS + 64 * PD, PD, PLD);
-        if (w == 0) rev_chunk_info<float, false>(&ck, rr);
-    }
-    __syncthreads();
+    VRegs R;
+    int64_t item = xcd_logical_block(gridDim.x);
+    if (item < nitems) v_load(a, v_item(a, item), R);
+    for (; item < nitems; item += stride) {
+        const VItem it = v_item(a, item);
+        const int64_t t0 = it.ci * C;
+        const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+        store_rows_split<DK>(R.pq, sQ, PW, PLW);
+        store_rows_split<DK>(R.pk, sK, PW, PLW);
+        store_rows_split<64>(R.pdo, sdO, P64, PL64);
+        store_rows_split<64>(R.pds0, sdS, PD, PLD);
+        store_rows_split<64>(R.pds1, sdS + 64 * PD, PD, PLD);
+        if (w == 0) rev_chunk_info<float, false>(&ck, R.rr);
+        __syncthreads();
+        if (item + stride < nitems) v_load(a, v_item(a, item + stride), R);
 
-    // A = q k^T tiles, masked with the scalar decay, stored transposed A^T[s][r]
-    for (int ti = w; ti < 12; ti += 4) {
-        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
-        const f32x4 acc = mma3_chain<DK / KS>(zero4(), ti < 10 ? DK / KS : 0, [&](int i, SFrag& A, SFrag& B) {
-            A = sld<PW, PLW>(sQ, 16 * rt, i * KS);
-            B = sld<PW, PLW>(sK, 16 * st, i * KS);
-        });
-        store_masked_split<false, P64, PL64>(sAT, ck, rt, st, ti < 10, acc);
-    }
-    __syncthreads();
+        // A = q k^T tiles, masked with the scalar decay, stored transposed A^T[s][r]
+        for (int ti = w; ti < 12; ti += 4) {
+            const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
+            const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+            const f32x4 acc = mma3_chain<DK / KS>(zero4(), ti < 10 ? DK / KS : 0, [&](int i, SFrag& A, SFrag& B) {
+                A = sld<PW, PLW>(sQ, 16 * rt, i * KS);
+                B = sld<PW, PLW>(sK, 16 * st, i * KS);
+            });
+            store_masked_split<false, P64, PL64>(sAT, ck, rt, st, ti < 10, acc);
+        }
+        __syncthreads();
 
-    // dv^T = dO^T A + [last doc] exp(Gamma - beta_s) dS1^T k^T (rows n, columns s)
-    float* dvo = (float*)a.dv + ((b * T_ + t0) * a.H + h) * DV + n0s + 16 * w + 4 * j4;
+        // dv^T = dO^T A + [last doc] exp(Gamma - beta_s) dS1^T k^T (rows n, columns s)
+        float* dvo = (float*)a.dv + ((it.b * T_ + t0) * a.H + it.h) * DV + it.slice * 64 + 16 * w + 4 * j4;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int kb = 16 * st / KS;
-        const f32x4 a1 = mma3_chain<C / KS>(zero4(), C / KS - kb, [&](int i, SFrag& A, SFrag& B) {
-            A = scol<P64, PL64>(sdO, 16 * w, (kb + i) * KS);
-            B = sld<P64, PL64>(sAT, 16 * st, (kb + i) * KS);
-        });
-        const f32x4 a2 = mma3_chain<DK / KS>(zero4(), DK / KS, [&](int i, SFrag& A, SFrag& B) {
-            A = scol<PD, PLD>(sdS, 16 * w, i * KS);
-            B = sld<PW, PLW>(sK, 16 * st, i * KS);
-        });
-        const int s = 16 * st + i16;
-        const float fu = ck.fu[s];
-        float dv[4];
+        for (int st = 0; st < 4; ++st) {
+            const int kb = 16 * st / KS;
+            const f32x4 a1 = mma3_chain<C / KS>(zero4(), C / KS - kb, [&](int i, SFrag& A, SFrag& B) {
+                A = scol<P64, PL64>(sdO, 16 * w, (kb + i) * KS);
+                B = sld<P64, PL64>(sAT, 16 * st, (kb + i) * KS);
+            });
+            const f32x4 a2 = mma3_chain<DK / KS>(zero4(), DK / KS, [&](int i, SFrag& A, SFrag& B) {
+                A = scol<PD, PLD>(sdS, 16 * w, i * KS);
+                B = sld<PW, PLW>(sK, 16 * st, i * KS);
+            });
+            const int s = 16 * st + i16;
+            const float fu = ck.fu[s];
+            float dv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dv[e] = a1[e] + fu * a2[e];
-        if (s < nvalid) store4<float>(dvo + (int64_t)s * a.H * DV, dv);
+            for (int e = 0; e < 4; ++e) dv[e] = a1[e] + fu * a2[e];
+            if (s < nvalid) store4<float>(dvo + (int64_t)s * a.H * DV, dv);
+        }
+        __syncthreads();  // LDS is restaged for the next item
     }
-}
-
-// Workgroups per (b, q/k head, chunk): 2 QK (one per 64-channel slice, all G heads)
-// and 2G V (one per head and 64-column slice), adjacent so they share one XCD.
-__global__ __launch_bounds__(NT) void k_grad_f32s(const RevArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[BYTES];
-    __shared__ SmallS sm;
-    const int64_t NC = (a.T + C - 1) / C;
-    const int64_t G = a.H / a.Hqk;
-    const int64_t per = 2 + 2 * G;
-    const int64_t L = xcd_logical_block(a.B * a.Hqk * NC * per);
-    const int64_t r = L % per;
-    const int64_t ci = (L / per) % NC;
-    const int64_t bq = L / per / NC;  // b * Hqk + hq
-    const int64_t b = bq / a.Hqk, hq = bq % a.Hqk;
-    if (r < 2) sqk(a, lds, sm, b, hq, ci, (int)r);
-    else sv(a, lds, sm, b * a.H + hq * G + (r - 2) / 2, ci, (int)((r - 2) % 2));
 }
 
 }  // namespace
 
 hipError_t launch_grad_f32s(const RevArgs& a, hipStream_t st) {
     const int64_t NC = (a.T + C - 1) / C;
-    hipLaunchKernelGGL(k_grad_f32s, dim3((unsigned)(a.B * a.Hqk * NC * (2 + 2 * (a.H / a.Hqk)))), dim3(NT), 0,
-                       st, a);
-    const hipError_t e = hipGetLastError();
+    const int64_t nqk = a.B * a.Hqk * NC * 2, nv = a.B * a.H * NC * 2;
+    // persistent: one workgroup per compute unit (the LDS allows no more)
+    const int64_t workers = 256;
+    hipLaunchKernelGGL(k_grad_f32s_qk, dim3((unsigned)(nqk < workers ? nqk : workers)), dim3(NT), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_grad_f32s_v, dim3((unsigned)(nv < workers ? nv : workers)), dim3(NT), 0, st, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_dg_scalar(a, 2, false, st);
 }
