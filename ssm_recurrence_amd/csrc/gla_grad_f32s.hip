@@ -60,28 +60,31 @@ struct SmallS {
 // summed over those heads in registers (the head-sharing reduction of the FLAT
 // page, Pallas Kernels > Gated Linear Attention, done in place of per-head
 // buffers), and each head's log-gate partial sums are written for the
-// finisher.  The next head's inputs (or the next item's q, k and first head)
-// are loaded into registers while the current head computes.
+// finisher.  The next head's v, dO and gates (or the next item's q, k and
+// first head) are loaded into registers while the current head computes; a
+// head's state and state-gradient rows are requested before its tiles are staged.
 
-// inputs of one head of a QK item
+// v, dO and gate inputs of one head of a QK item
 struct QKHeadRegs {
     TileRegs<float, DV> pv, pdo;
     RowRegs rr;
-    f32x4 s0[2 * DV / KS], ds[2 * DV / KS];  // S0 and dS1 row cw + i16, channels of lane group j4
 };
 
 struct QKItem {
     int64_t b, hq, ci;
     int slice;
 };
-__device__ __forceinline__ QKItem qk_item(const RevArgs& a, int64_t item) {
-    const int64_t NC = (a.T + C - 1) / C;
+// (item counts fit in 32 bits: the launch bounds B H chunks well below 2^31)
+__device__ __forceinline__ QKItem qk_item(const RevArgs& a, int64_t item64) {
+    const uint32_t NC = (uint32_t)((a.T + C - 1) / C), Hqk = (uint32_t)a.Hqk;
+    const uint32_t item = (uint32_t)item64;
     QKItem it;
-    it.slice = (int)(item % 2);
-    it.ci = (item / 2) % NC;
-    const int64_t bq = item / 2 / NC;
-    it.b = bq / a.Hqk;
-    it.hq = bq % a.Hqk;
+    it.slice = (int)(item & 1);
+    const uint32_t rest = item >> 1;
+    it.ci = rest % NC;
+    const uint32_t bq = rest / NC;
+    it.b = bq / Hqk;
+    it.hq = bq % Hqk;
     return it;
 }
 
@@ -97,25 +100,14 @@ __device__ __forceinline__ void qk_load_qk(const RevArgs& a, const QKItem& it, T
 
 __device__ __forceinline__ void qk_load_head(const RevArgs& a, const QKItem& it, int64_t gi, QKHeadRegs& R) {
     const int64_t T_ = a.T, t0 = it.ci * C;
-    const int64_t NC = (T_ + C - 1) / C;
     const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
     const int64_t G = a.H / a.Hqk;
-    const int64_t h = it.hq * G + gi, bh = it.b * a.H + h;
+    const int64_t h = it.hq * G + gi;
     const int64_t rs_v = a.H * DV;
-    const int w = wave_id(), j4 = lane_id() >> 4, i16 = lane_id() & 15;
-    const int cw = it.slice * 64 + 16 * w;
+    const int w = wave_id();
     R.pv.load((const float*)a.v + (it.b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
     R.pdo.load((const float*)a.dO + (it.b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
     if (w == 0) R.rr.load((const float*)a.g + (it.b * T_ + t0) * a.H + h, a.H, a.seg, it.b, T_, t0, nvalid, true);
-    const float* S0 = (const float*)a.ws_S + ((bh * (NC + 1) + it.ci) * DK + cw + i16) * DV + 8 * j4;
-    const float* dS1 = (const float*)a.ws_dS + ((bh * NC + it.ci) * DK + cw + i16) * DV + 8 * j4;
-#pragma unroll
-    for (int kk = 0; kk < DV / KS; ++kk) {
-        R.s0[2 * kk] = *reinterpret_cast<const f32x4*>(S0 + kk * KS);
-        R.s0[2 * kk + 1] = *reinterpret_cast<const f32x4*>(S0 + kk * KS + 4);
-        R.ds[2 * kk] = *reinterpret_cast<const f32x4*>(dS1 + kk * KS);
-        R.ds[2 * kk + 1] = *reinterpret_cast<const f32x4*>(dS1 + kk * KS + 4);
-    }
 }
 
 __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
@@ -161,16 +153,19 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
 
         for (int64_t gi = 0; gi < G; ++gi) {
             const int64_t h = hq * G + gi, bh = b * a.H + h;
-            // S0 and dS1 rows cw + i16 as split A operands (k = n); rowsum(S0 * dS1) in fp32
-            float sd = 0.f;
-            SFrag s0f[DV / KS], dsf[DV / KS];
+            // S0 and dS1 rows cw + i16 (channels of lane group j4), issued first: they are
+            // first needed after the score tiles
+            f32x4 s0r[2 * DV / KS], dsr[2 * DV / KS];
+            {
+                const float* S0 = (const float*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV + 8 * j4;
+                const float* dS1 = (const float*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV + 8 * j4;
 #pragma unroll
-            for (int kk = 0; kk < DV / KS; ++kk) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sd += hr.s0[2 * kk][e] * hr.ds[2 * kk][e] + hr.s0[2 * kk + 1][e] * hr.ds[2 * kk + 1][e];
-                s0f[kk] = split8(hr.s0[2 * kk], hr.s0[2 * kk + 1]);
-                dsf[kk] = split8(hr.ds[2 * kk], hr.ds[2 * kk + 1]);
+                for (int kk = 0; kk < DV / KS; ++kk) {
+                    s0r[2 * kk] = *reinterpret_cast<const f32x4*>(S0 + kk * KS);
+                    s0r[2 * kk + 1] = *reinterpret_cast<const f32x4*>(S0 + kk * KS + 4);
+                    dsr[2 * kk] = *reinterpret_cast<const f32x4*>(dS1 + kk * KS);
+                    dsr[2 * kk + 1] = *reinterpret_cast<const f32x4*>(dS1 + kk * KS + 4);
+                }
             }
             store_rows_split<DV>(hr.pv, sV, PW, PLW);
             store_rows_split<DV>(hr.pdo, sdO, PW, PLW);
@@ -197,6 +192,18 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
                 store_masked_split<true, P64, PL64>(sdA, ck, rt, st, ti < 10, acc);
             }
             __syncthreads();
+
+            // S0 and dS1 rows as split A operands (k = n); rowsum(S0 * dS1) in fp32
+            float sd = 0.f;
+            SFrag s0f[DV / KS], dsf[DV / KS];
+#pragma unroll
+            for (int kk = 0; kk < DV / KS; ++kk) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sd += s0r[2 * kk][e] * dsr[2 * kk][e] + s0r[2 * kk + 1][e] * dsr[2 * kk + 1][e];
+                s0f[kk] = split8(s0r[2 * kk], s0r[2 * kk + 1]);
+                dsf[kk] = split8(dsr[2 * kk], dsr[2 * kk + 1]);
+            }
 
             // q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e),
             // from the split tiles (hi + lo)
@@ -297,16 +304,18 @@ struct VItem {
     int64_t b, h, hq, ci;
     int slice;
 };
-__device__ __forceinline__ VItem v_item(const RevArgs& a, int64_t item) {
-    const int64_t NC = (a.T + C - 1) / C;
-    const int64_t G = a.H / a.Hqk;
+__device__ __forceinline__ VItem v_item(const RevArgs& a, int64_t item64) {
+    const uint32_t NC = (uint32_t)((a.T + C - 1) / C), Hqk = (uint32_t)a.Hqk;
+    const uint32_t G = (uint32_t)(a.H / a.Hqk);
+    const uint32_t item = (uint32_t)item64;
     VItem it;
-    it.slice = (int)(item % 2);
-    const int64_t gi = (item / 2) % G;
-    it.ci = (item / 2 / G) % NC;
-    const int64_t bq = item / 2 / G / NC;
-    it.b = bq / a.Hqk;
-    it.hq = bq % a.Hqk;
+    it.slice = (int)(item & 1);
+    const uint32_t r1 = item >> 1;
+    const uint32_t gi = r1 % G, r2 = r1 / G;
+    it.ci = r2 % NC;
+    const uint32_t bq = r2 / NC;
+    it.b = bq / Hqk;
+    it.hq = bq % Hqk;
     it.h = it.hq * G + gi;
     return it;
 }
