@@ -75,7 +75,7 @@ Split plan_split(const gla_problem* p, int for_backward) {
             target = kTargetWGBwd;
         } else {
             per_head = p->d_v / (p->dtype == GLA_BF16 ? 64 : 32);
-            if (p->dtype == GLA_F32 && p->gate == GLA_GATE_SCALAR && p->d_k == 128 && p->d_v == 128)
+            if (p->d_k == 128 && p->d_v == 128 && (p->dtype == GLA_BF16 || p->gate == GLA_GATE_SCALAR))
                 per_head = 1;  // one workgroup holds the whole state
             target = kTargetWG;
         }
@@ -236,6 +236,8 @@ hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
     const int64_t wg = a.B * a.H * a.P;
     if constexpr (sizeof(T) == 4 && !VEC && DK == 128 && DV == 128)
         return gla::launch_fwd_f32h(a, st);
+    if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128)
+        return gla::launch_fwd_h<VEC>(a, st);
     if constexpr (sizeof(T) == 2)  // fp32 tiles with 64 columns exceed the LDS
         if (DV >= 64 && wg * (DV / 64) >= 256) return gla::launch_fwd<T, VEC, DK, DV, 64>(a, st);
     if (wg * (DV / 32) >= 256) return gla::launch_fwd<T, VEC, DK, DV, 32>(a, st);

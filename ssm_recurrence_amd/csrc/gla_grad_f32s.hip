@@ -207,7 +207,7 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
 
             // q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e),
             // from the split tiles (hi + lo)
-            float x[4][4];
+            float xr[4];  // per row: sum over this lane's channels of q dq - k dk
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int nk = (16 * (rt + 1) + KS - 1) / KS;
@@ -223,10 +223,11 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
                 const float fq = ck.fq[r];
                 const Vec4<bf16> qh = Vec4<bf16>::load(sQ + r * P64 + 16 * w + 4 * j4);
                 const Vec4<bf16> ql = Vec4<bf16>::load(sQ + PL64 + r * P64 + 16 * w + 4 * j4);
+                xr[rt] = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float dq = a1[e] + fq * a2[e];
-                    x[rt][e] = (qh.get(e) + ql.get(e)) * dq;
+                    xr[rt] += (qh.get(e) + ql.get(e)) * dq;
                     dqs[rt][e] += dq;
                 }
             }
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
                     const float inter = fu * a2[e];
                     const float dk = a1[e] + inter;
                     const float kr = kh.get(e) + kl.get(e);
-                    x[st][e] -= kr * dk;
+                    xr[st] -= kr * dk;
                     bsum[e] += kr * inter;
                     dks[st][e] += dk;
                 }
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
             // partial sums over this workgroup's channels; a finisher adds the two slices
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                float y = x[rt][0] + x[rt][1] + x[rt][2] + x[rt][3];
+                float y = xr[rt];
                 y += __shfl_xor(y, 16, 64);
                 y += __shfl_xor(y, 32, 64);
                 if (j4 == 0) sm.sXs[w][16 * rt + i16] = y;

@@ -75,6 +75,9 @@ hipError_t launch_fwd(const PassArgs& a, hipStream_t st);
 // fp32 inputs, scalar gate, d_k = d_v = 128: the forward on the bf16 matrix cores
 // (split operands), one 8-wave workgroup per (b, h, piece) holding the whole state
 hipError_t launch_fwd_f32h(const PassArgs& a, hipStream_t st);
+// bf16 inputs, either gate, d_k = d_v = 128: one 8-wave workgroup per (b, h, piece)
+template <bool VEC>
+hipError_t launch_fwd_h(const PassArgs& a, hipStream_t st);
 
 template <typename T, int DK>
 hipError_t launch_group_sum(const float* src, void* dst, int64_t B, int64_t Tn, int64_t H,

@@ -132,7 +132,7 @@ def test_split_workspace(lib):
 def test_auto_split_only_when_short_of_workgroups(lib):
     """split = 0: long rows at small B*H are split, large B*H is not."""
     small_bh = prob(B=1, T=65536, H=16, H_qk=16, d_k=128, d_v=128)
-    large_bh = prob(B=8, T=2048, H=16, H_qk=16, d_k=128, d_v=128)
+    large_bh = prob(B=16, T=2048, H=16, H_qk=16, d_k=128, d_v=128)  # one workgroup per head fills the device
     assert _ws(lib, small_bh, False) > 0
     assert _ws(lib, large_bh, False) == 0
     one = prob(B=1, T=65536, H=16, H_qk=16, d_k=128, d_v=128)
