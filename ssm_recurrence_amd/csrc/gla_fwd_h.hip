@@ -38,6 +38,7 @@ constexpr int PQ = DK + 12;   // q (QA)
 constexpr int PKH = DK + 20;  // k (KA)
 constexpr int PH = DK + 8;    // v, last-document v, gate tile
 constexpr int PA = C + 16;    // scores [r][s]
+constexpr int PO = DV + 8;    // output rows, written to HBM a whole row at a time
 
 template <bool VEC>
 struct FwdHLds {
@@ -46,6 +47,7 @@ struct FwdHLds {
     bf16 sV[C * PH];
     bf16 sVu[C * PH];
     bf16 sA[C * PA];
+    bf16 sO[C * PO];
     bf16 sG[VEC ? C * PH : 8];
     bf16 sKU[VEC ? C * PH : 8];    // vector gate: k exp(Gamma - beta), the update's operand
     alignas(16) int sDoc[C];
@@ -78,7 +80,20 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
     const bf16* kbase = (const bf16*)a.k + b * T_ * rs_qk + hq * DK;
     const bf16* vbase = (const bf16*)a.v + b * T_ * rs_v + h * DV;
     const bf16* gbase = (const bf16*)a.g + b * T_ * rs_g + (VEC ? h * DK : h);
-    bf16* obase = (bf16*)a.o + b * T_ * rs_v + h * DV + 16 * w + 4 * j4;
+    bf16* obase = (bf16*)a.o + b * T_ * rs_v + h * DV;
+    // a chunk's output is assembled in LDS and written out at the next chunk's start
+    // with 16-byte stores of whole rows (each wave holds 16 columns of every row)
+    auto write_out = [&](int64_t t0, int nvalid) {
+        using TR = TileRegs<bf16, DV, NTH>;
+#pragma unroll
+        for (int i = 0; i < TR::NVEC; ++i) {
+            const int idx = threadIdx.x + i * NTH;
+            const int row = idx / TR::VPR, cv = (idx % TR::VPR) * TR::VE;
+            if (row < nvalid)
+                *reinterpret_cast<i32x4*>(obase + (t0 + row) * rs_v + cv) =
+                    *reinterpret_cast<const i32x4*>(sm.sO + row * PO + cv);
+        }
+    };
 
     // state tiles ct = 0..7 of column tile w: lane holds S[16ct + 4j4 + e][16w + i16]
     f32x4 S[DK / 16];
@@ -133,7 +148,8 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
             if (l == 0) sm.sAnyReset = msk != 0;
         }
 
-        // ---- staging
+        // ---- staging; the previous chunk's output
+        if (it > cbeg) write_out(t0 - C, C);
         pq.store_rows_b64(sm.sQ, PQ);  // rows of q and k are 8-byte aligned only
         pk.store_rows_b64(sm.sK, PKH);
         pv.store_rows(sm.sV, PH);
@@ -325,15 +341,17 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
                 for (int p = 0; p <= rt / 2; ++p) O = M::mma(vt[p], frag_ld<bf16, PA, 1>(sm.sA, 16 * rt, p * KS), O);
                 const int r = 16 * rt + i16;
                 const float fr = __shfl(fq, r, 64);
-                if (r < nvalid) {
-                    Vec4<bf16> out;
+                Vec4<bf16> out;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out.set(e, O[e] + fr * R[rt][e]);
-                    out.store(obase + (t0 + r) * rs_v);
-                }
+                for (int e = 0; e < 4; ++e) out.set(e, O[e] + fr * R[rt][e]);
+                out.store(sm.sO + r * PO + 16 * w + 4 * j4);
             }
         }
         __syncthreads();
+    }
+    if (cend > cbeg) {
+        const int64_t tl = (cend - 1) * C;
+        write_out(tl, T_ - tl < C ? (int)(T_ - tl) : C);
     }
 
     if (a.hT && piece == P - 1) {
