@@ -241,28 +241,30 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
     }
 }
 
-// fp32 inputs with the scalar gate: the same passes on the bf16 matrix cores,
-// every fp32 operand split into bf16 hi/lo halves (three products, gla_split.hpp).
-// Every wave computes the chunk's gate prefix itself (lane = row) so that the
-// row factors can go into k while it is staged: KU = fu k is stored split, and
-// the update needs no further scaling.  Operand reads run one step ahead of the
-// products.
-template <int NB>
+// Scalar gate: every wave computes the chunk's gate prefix itself (lane = row),
+// so the row factors go into k while it is staged (KU = fu k), and the update
+// needs no further scaling; operand reads run one step ahead of the products.
+// fp32 inputs run on the bf16 matrix cores with every operand split into bf16
+// hi/lo halves (three products, gla_split.hpp); bf16 inputs use one product.
+template <typename T, int NB>
 struct StatesLdsS {
+    static constexpr int PLANES = sizeof(T) == 4 ? 2 : 1;
     static constexpr int PB = 64 + 8;   // [64 rows][64 channels], transposed reads
     static constexpr int PN = NB + 8;   // [64 rows][NB columns], transposed reads
-    bf16 sKu[2 * C * PB];
-    bf16 sV[2 * C * PN];
+    bf16 sKu[PLANES * C * PB];
+    bf16 sV[PLANES * C * PN];
 };
 
-template <int DK, int DV, int MODE, int NB>
-__device__ __forceinline__ void states_body_f32s(const PassArgs& a, StatesLdsS<NB>& sm, int64_t L) {
+template <typename T, int DK, int DV, int MODE, int NB>
+__device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, NB>& sm, int64_t L) {
     constexpr bool REV = MODE == ST_SUM_REV || MODE == ST_DSTATES;
+    constexpr bool SPLIT = sizeof(T) == 4;
     constexpr int CB = 64, KS = 32;
     constexpr int NCB = DK / CB, NNB = DV / NB;
-    constexpr int PB = StatesLdsS<NB>::PB, PLB = C * PB;
-    constexpr int PN = StatesLdsS<NB>::PN, PLN = C * PN;
+    constexpr int PB = StatesLdsS<T, NB>::PB, PLB = C * PB;
+    constexpr int PN = StatesLdsS<T, NB>::PN, PLN = C * PN;
     constexpr int NNT = NB / 16;
+    using Fr = typename std::conditional<SPLIT, SFrag, bf16x8>::type;
 
     const int64_t P = a.P;
     const int blk = (int)(L % (NCB * NNB));
@@ -277,12 +279,12 @@ __device__ __forceinline__ void states_body_f32s(const PassArgs& a, StatesLdsS<N
     const int64_t cbeg = piece * a.PL;
     const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
 
-    const float* k = (const float*)(REV ? a.q : a.k);
-    const float* v = (const float*)(REV ? a.dO : a.v);
+    const T* k = (const T*)(REV ? a.q : a.k);
+    const T* v = (const T*)(REV ? a.dO : a.v);
     const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
-    const float* kbase = k + b * T_ * rs_qk + hq * DK + c0;
-    const float* vbase = v + b * T_ * rs_v + h * DV + n0;
-    const float* gbase = (const float*)a.g + b * T_ * a.H + h;
+    const T* kbase = k + b * T_ * rs_qk + hq * DK + c0;
+    const T* vbase = v + b * T_ * rs_v + h * DV + n0;
+    const T* gbase = (const T*)a.g + b * T_ * a.H + h;
 
     f32x4 St[NNT];
     const int cme = c0 + 16 * w + i16;
@@ -305,8 +307,8 @@ __device__ __forceinline__ void states_body_f32s(const PassArgs& a, StatesLdsS<N
         }
     float dprod = 1.f;
 
-    TileRegs<float, CB> pk;
-    TileRegs<float, NB> pv;
+    TileRegs<T, CB> pk;
+    TileRegs<T, NB> pv;
     RowRegs rr;
     auto prefetch = [&](int64_t t0) {
         const int64_t nv64 = T_ - t0;
@@ -316,10 +318,20 @@ __device__ __forceinline__ void states_body_f32s(const PassArgs& a, StatesLdsS<N
         rr.load(gbase + t0 * a.H, a.H, a.seg, b, T_, t0, nvalid, true);
     };
     auto store_state = [&](int64_t ci) {
-        float* dst = MODE == ST_STATES ? (float*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cme) * DV + n0
-                                       : (float*)a.ws_dS + ((bh * NC + ci) * DK + cme) * DV + n0;
+        T* dst = MODE == ST_STATES ? (T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cme) * DV + n0
+                                   : (T*)a.ws_dS + ((bh * NC + ci) * DK + cme) * DV + n0;
 #pragma unroll
-        for (int nt = 0; nt < NNT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt + 4 * j4) = St[nt];
+        for (int nt = 0; nt < NNT; ++nt) {
+            Vec4<T> x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x.set(e, St[nt][e]);
+            x.store(dst + 16 * nt + 4 * j4);
+        }
+    };
+    auto col = [&](const bf16* base, int i0, int k0, auto pitch) -> Fr {
+        constexpr int PP = decltype(pitch)::value;
+        if constexpr (SPLIT) return scol<PP, C * PP>(base, i0, k0);
+        else return frag_col<bf16, PP, false>(base, i0, k0);
     };
     const int64_t nchunks = cend - cbeg;
     prefetch((REV ? cend - 1 : cbeg) * C);
@@ -338,21 +350,29 @@ __device__ __forceinline__ void states_body_f32s(const PassArgs& a, StatesLdsS<N
         if constexpr (REV) fu = l < first_reset ? __expf(beta) : 0.f;
         else fu = l >= last_reset ? __expf(Gam - beta) : 0.f;
         const float dec = msk ? 0.f : __expf(Gam);
-        // stage KU = fu k and v, split
+        // stage KU = fu k and v (fp32: split)
         {
-            using TR = TileRegs<float, CB>;
+            using TR = TileRegs<T, CB>;
             static_assert(TR::NV_TOT % NT == 0, "");
 #pragma unroll
             for (int i = 0; i < TR::NVEC; ++i) {
                 const int idx = threadIdx.x + i * NT;
-                const int row = idx / TR::VPR, cv = (idx % TR::VPR) * 4;
+                const int row = idx / TR::VPR, cv = (idx % TR::VPR) * TR::VE;
                 const float f = __shfl(fu, row, 64);
-                const f32x4 x = __builtin_bit_cast(f32x4, pk.r[i]);
-                split4_store(x[0] * f, x[1] * f, x[2] * f, x[3] * f, sm.sKu + row * PB + cv,
-                             sm.sKu + PLB + row * PB + cv);
+                if constexpr (SPLIT) {
+                    const f32x4 x = __builtin_bit_cast(f32x4, pk.r[i]);
+                    split4_store(x[0] * f, x[1] * f, x[2] * f, x[3] * f, sm.sKu + row * PB + cv,
+                                 sm.sKu + PLB + row * PB + cv);
+                } else {
+                    bf16x8 x = __builtin_bit_cast(bf16x8, pk.r[i]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * f);
+                    *reinterpret_cast<bf16x8*>(sm.sKu + row * PB + cv) = x;
+                }
             }
         }
-        store_rows_split<NB>(pv, sm.sV, PN, PLN);
+        if constexpr (SPLIT) store_rows_split<NB>(pv, sm.sV, PN, PLN);
+        else pv.store_rows(sm.sV, PN);
         __syncthreads();
         if (ii + 1 < nchunks) prefetch(REV ? t0 - C : t0 + C);
 
@@ -362,18 +382,19 @@ __device__ __forceinline__ void states_body_f32s(const PassArgs& a, StatesLdsS<N
         for (int nt = 0; nt < NNT; ++nt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) St[nt][e] *= dec;
-        SFrag kf[C / KS];
+        Fr kf[C / KS];
 #pragma unroll
-        for (int kk = 0; kk < C / KS; ++kk) kf[kk] = scol<PB, PLB>(sm.sKu, 16 * w, kk * KS);
-        SFrag va = scol<PN, PLN>(sm.sV, 0, 0);
+        for (int kk = 0; kk < C / KS; ++kk) kf[kk] = col(sm.sKu, 16 * w, kk * KS, std::integral_constant<int, PB>());
+        Fr va = col(sm.sV, 0, 0, std::integral_constant<int, PN>());
 #pragma unroll
         for (int idx = 0; idx < NNT * (C / KS); ++idx) {
             const int kk = idx / NNT, nt = idx % NNT;
-            SFrag vb;
+            Fr vb;
             if (idx + 1 < NNT * (C / KS))
-                vb = scol<PN, PLN>(sm.sV, 16 * ((idx + 1) % NNT), KS * ((idx + 1) / NNT));
+                vb = col(sm.sV, 16 * ((idx + 1) % NNT), KS * ((idx + 1) / NNT), std::integral_constant<int, PN>());
             __builtin_amdgcn_sched_barrier(0);
-            St[nt] = mma3(va, kf[kk], St[nt]);
+            if constexpr (SPLIT) St[nt] = mma3(va, kf[kk], St[nt]);
+            else St[nt] = Mma<bf16>::mma(va, kf[kk], St[nt]);
             __builtin_amdgcn_sched_barrier(0);
             va = vb;
         }
@@ -395,13 +416,13 @@ __device__ __forceinline__ void states_body_f32s(const PassArgs& a, StatesLdsS<N
     }
 }
 
-// shared memory of a state pass: the split layout for fp32 with the scalar gate
+// shared memory of a state pass: the scalar-gate layout, or the general one
 template <typename T, bool VEC, int NB>
-using StatesLdsFor = typename std::conditional<(sizeof(T) == 4 && !VEC), StatesLdsS<NB>, StatesLds<T, VEC, NB>>::type;
+using StatesLdsFor = typename std::conditional<!VEC, StatesLdsS<T, NB>, StatesLds<T, VEC, NB>>::type;
 
 template <typename T, bool VEC, int DK, int DV, int MODE, int NB>
 __device__ __forceinline__ void states_any(const PassArgs& a, StatesLdsFor<T, VEC, NB>& sm, int64_t L) {
-    if constexpr (sizeof(T) == 4 && !VEC) states_body_f32s<DK, DV, MODE, NB>(a, sm, L);
+    if constexpr (!VEC) states_body_s<T, DK, DV, MODE, NB>(a, sm, L);
     else states_body<T, VEC, DK, DV, MODE, NB>(a, sm, L);
 }
 
