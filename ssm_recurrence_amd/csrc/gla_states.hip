@@ -246,23 +246,27 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
 // needs no further scaling; operand reads run one step ahead of the products.
 // fp32 inputs run on the bf16 matrix cores with every operand split into bf16
 // hi/lo halves (three products, gla_split.hpp); bf16 inputs use one product.
-template <typename T, int NB>
+template <typename T, int NB, int CB = 64>
 struct StatesLdsS {
     static constexpr int PLANES = sizeof(T) == 4 ? 2 : 1;
-    static constexpr int PB = 64 + 8;   // [64 rows][64 channels], transposed reads
+    static constexpr int PB = CB + 8;   // [64 rows][CB channels], transposed reads
     static constexpr int PN = NB + 8;   // [64 rows][NB columns], transposed reads
     bf16 sKu[PLANES * C * PB];
     bf16 sV[PLANES * C * PN];
 };
 
-template <typename T, int DK, int DV, int MODE, int NB>
-__device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, NB>& sm, int64_t L) {
+// One workgroup: a CB x NB block of the state, CB / 16 waves (wave w owns
+// channel tile w of the block).  CB = 64: 256 threads; CB = 128 with NB = 128:
+// the whole state of a head in one 512-thread workgroup, so each chunk's k and
+// v are requested once per pass.
+template <typename T, int DK, int DV, int MODE, int NB, int CB = 64>
+__device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, NB, CB>& sm, int64_t L) {
     constexpr bool REV = MODE == ST_SUM_REV || MODE == ST_DSTATES;
     constexpr bool SPLIT = sizeof(T) == 4;
-    constexpr int CB = 64, KS = 32;
+    constexpr int KS = 32, NTH = 64 * (CB / 16);
     constexpr int NCB = DK / CB, NNB = DV / NB;
-    constexpr int PB = StatesLdsS<T, NB>::PB, PLB = C * PB;
-    constexpr int PN = StatesLdsS<T, NB>::PN, PLN = C * PN;
+    constexpr int PB = StatesLdsS<T, NB, CB>::PB, PLB = C * PB;
+    constexpr int PN = StatesLdsS<T, NB, CB>::PN, PLN = C * PN;
     constexpr int NNT = NB / 16;
     using Fr = typename std::conditional<SPLIT, SFrag, bf16x8>::type;
 
@@ -307,8 +311,8 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
         }
     float dprod = 1.f;
 
-    TileRegs<T, CB> pk;
-    TileRegs<T, NB> pv;
+    TileRegs<T, CB, NTH> pk;
+    TileRegs<T, NB, NTH> pv;
     RowRegs rr;
     auto prefetch = [&](int64_t t0) {
         const int64_t nv64 = T_ - t0;
@@ -352,11 +356,11 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
         const float dec = msk ? 0.f : __expf(Gam);
         // stage KU = fu k and v (fp32: split)
         {
-            using TR = TileRegs<T, CB>;
-            static_assert(TR::NV_TOT % NT == 0, "");
+            using TR = TileRegs<T, CB, NTH>;
+            static_assert(TR::NV_TOT % NTH == 0, "");
 #pragma unroll
             for (int i = 0; i < TR::NVEC; ++i) {
-                const int idx = threadIdx.x + i * NT;
+                const int idx = threadIdx.x + i * NTH;
                 const int row = idx / TR::VPR, cv = (idx % TR::VPR) * TR::VE;
                 const float f = __shfl(fu, row, 64);
                 if constexpr (SPLIT) {
@@ -371,7 +375,7 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
                 }
             }
         }
-        if constexpr (SPLIT) store_rows_split<NB>(pv, sm.sV, PN, PLN);
+        if constexpr (SPLIT) store_rows_split<NB, NTH>(pv, sm.sV, PN, PLN);
         else pv.store_rows(sm.sV, PN);
         __syncthreads();
         if (ii + 1 < nchunks) prefetch(REV ? t0 - C : t0 + C);
@@ -444,6 +448,27 @@ __global__ __launch_bounds__(NT) void k_states2(const PassArgs a) {
     else states_any<T, VEC, DK, DV, MODE_B, NB>(a, sm, L - n);
 }
 
+// Scalar gate, 128 x 128 heads: the whole state of a head per 512-thread workgroup.
+template <typename T, int DK, int DV, int MODE>
+__global__ __launch_bounds__(512) void k_states_w(const PassArgs a) {
+    __shared__ __attribute__((aligned(16))) StatesLdsS<T, DV, DK> sm;
+    states_body_s<T, DK, DV, MODE, DV, DK>(a, sm, xcd_logical_block(a.B * a.H * a.P));
+}
+template <typename T, int DK, int DV, int MODE_A, int MODE_B>
+__global__ __launch_bounds__(512) void k_states2_w(const PassArgs a) {
+    __shared__ __attribute__((aligned(16))) StatesLdsS<T, DV, DK> sm;
+    const int64_t n = a.B * a.H * a.P;
+    const int64_t L = xcd_logical_block(2 * n);
+    if (L < n) states_body_s<T, DK, DV, MODE_A, DV, DK>(a, sm, L);
+    else states_body_s<T, DK, DV, MODE_B, DV, DK>(a, sm, L - n);
+}
+
+// whole-state workgroups when there are enough of them (one per compute unit);
+// measured: a gain for fp32 (c2: 176 vs 192 us for the state pair), a loss for
+// bf16 (c4: 578 vs 509 us), whose passes stream more bytes per unit of work
+template <typename T, bool VEC, int DK, int DV>
+constexpr bool whole_state_ok() { return sizeof(T) == 4 && !VEC && DK == 128 && DV == 128; }
+
 template <typename T, bool VEC, int DK, int DV, int NB>
 hipError_t launch_states_nb(const PassArgs& a, int mode, hipStream_t st) {
     const int64_t grid = a.B * a.H * a.P * (DK / 64) * (DV / NB);
@@ -460,6 +485,20 @@ hipError_t launch_states_nb(const PassArgs& a, int mode, hipStream_t st) {
 
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_states(const PassArgs& a, int mode, bool wide, hipStream_t st) {
+    if constexpr (whole_state_ok<T, VEC, DK, DV>()) {
+        const int64_t grid = a.B * a.H * a.P;
+        if (wide && grid >= 256) {
+            if (mode == ST_SUM_FWD)
+                hipLaunchKernelGGL((k_states_w<T, DK, DV, ST_SUM_FWD>), dim3((unsigned)grid), dim3(512), 0, st, a);
+            else if (mode == ST_SUM_REV)
+                hipLaunchKernelGGL((k_states_w<T, DK, DV, ST_SUM_REV>), dim3((unsigned)grid), dim3(512), 0, st, a);
+            else if (mode == ST_DSTATES)
+                hipLaunchKernelGGL((k_states_w<T, DK, DV, ST_DSTATES>), dim3((unsigned)grid), dim3(512), 0, st, a);
+            else
+                hipLaunchKernelGGL((k_states_w<T, DK, DV, ST_STATES>), dim3((unsigned)grid), dim3(512), 0, st, a);
+            return hipGetLastError();
+        }
+    }
     if (wide && DV > 64) return launch_states_nb<T, VEC, DK, DV, DV>(a, mode, st);
     return launch_states_nb<T, VEC, DK, DV, 64>(a, mode, st);
 }
@@ -478,6 +517,18 @@ hipError_t launch_states_pair_nb(const PassArgs& a, bool summaries, hipStream_t 
 
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_states_pair(const PassArgs& a, bool summaries, bool wide, hipStream_t st) {
+    if constexpr (whole_state_ok<T, VEC, DK, DV>()) {
+        const int64_t grid = 2 * a.B * a.H * a.P;
+        if (wide && grid >= 256) {
+            if (summaries)
+                hipLaunchKernelGGL((k_states2_w<T, DK, DV, ST_SUM_FWD, ST_SUM_REV>), dim3((unsigned)grid), dim3(512),
+                                   0, st, a);
+            else
+                hipLaunchKernelGGL((k_states2_w<T, DK, DV, ST_STATES, ST_DSTATES>), dim3((unsigned)grid), dim3(512),
+                                   0, st, a);
+            return hipGetLastError();
+        }
+    }
     if (wide && DV > 64) return launch_states_pair_nb<T, VEC, DK, DV, DV>(a, summaries, st);
     return launch_states_pair_nb<T, VEC, DK, DV, 64>(a, summaries, st);
 }
