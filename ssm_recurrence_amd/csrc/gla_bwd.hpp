@@ -167,8 +167,8 @@ __device__ __forceinline__ float frag_get(const typename Mma<T>::frag& f, int e)
 template <typename T, bool VEC>
 __device__ __forceinline__ void rev_chunk_info(RevChunk* ci, const RowRegs& rr) {
     const int r = lane_id();
-    const int doc = wave_incl_scan_i(rr.reset);
-    const uint64_t msk = __ballot(rr.reset);
+    const int doc = wave_incl_scan_i(rr.reset());
+    const uint64_t msk = __ballot(rr.reset());
     const int first_reset = msk ? __builtin_ctzll(msk) : C;
     const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
     ci->doc[r] = doc;
@@ -177,7 +177,7 @@ __device__ __forceinline__ void rev_chunk_info(RevChunk* ci, const RowRegs& rr) 
         ci->last_reset = last_reset;
     }
     if constexpr (!VEC) {
-        const float beta = wave_incl_scan(rr.g);
+        const float beta = wave_incl_scan(rr.g());
         const float Gam = __shfl(beta, 63, 64);
         ci->beta[r] = beta;
         ci->fq[r] = r < first_reset ? __expf(beta) : 0.f;

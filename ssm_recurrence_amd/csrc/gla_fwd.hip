@@ -127,14 +127,14 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
         if constexpr (VEC) pg.store_rows(sG, PK);
         if (w == 0) {
             const int r = l;
-            const int doc = wave_incl_scan_i(rr.reset);
-            const uint64_t msk = __ballot(rr.reset);
+            const int doc = wave_incl_scan_i(rr.reset());
+            const uint64_t msk = __ballot(rr.reset());
             const int first_reset = msk ? __builtin_ctzll(msk) : C;
             const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
             sDoc[r] = doc;
             if (r == 0) sAnyReset = msk != 0;
             if constexpr (!VEC) {
-                const float beta = wave_incl_scan(rr.g);
+                const float beta = wave_incl_scan(rr.g());
                 const float Gam = __shfl(beta, 63, 64);
                 sBeta[r] = beta;
                 sFq[r] = r < first_reset ? __expf(beta) : 0.f;

@@ -105,11 +105,11 @@ __global__ __launch_bounds__(512) void k_fwd_f32h(const PassArgs a) {
         const int nvalid = nv64 < C ? (int)nv64 : C;
 
         // ---- chunk structure, in every wave (lane = row)
-        const int doc = wave_incl_scan_i(rr.reset);
-        const uint64_t msk = __ballot(rr.reset);
+        const int doc = wave_incl_scan_i(rr.reset());
+        const uint64_t msk = __ballot(rr.reset());
         const int first_reset = msk ? __builtin_ctzll(msk) : C;
         const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
-        const float beta = wave_incl_scan(rr.g);
+        const float beta = wave_incl_scan(rr.g());
         const float Gam = __shfl(beta, 63, 64);
         const float fu = l >= last_reset ? __expf(Gam - beta) : 0.f;
         const float fq = l < first_reset ? __expf(beta) : 0.f;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(512) void k_fwd_f32h(const PassArgs a) {
                 const int idx = threadIdx.x + i * NTH;
                 const int row = idx / TR::VPR, cv = (idx % TR::VPR) * 4;
                 const float f = __shfl(fu, row, 64);
-                const f32x4 x = __builtin_bit_cast(f32x4, pv.r[i]);
+                const f32x4 x = __builtin_bit_cast(f32x4, pv.get(i));
                 split4_store(x[0], x[1], x[2], x[3], sV + row * PH + cv, sV + PLH + row * PH + cv);
                 split4_store(x[0] * f, x[1] * f, x[2] * f, x[3] * f, sVu + row * PH + cv,
                              sVu + PLH + row * PH + cv);

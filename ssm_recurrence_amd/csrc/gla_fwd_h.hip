@@ -127,13 +127,13 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
         const int nvalid = nv64 < C ? (int)nv64 : C;
 
         // ---- chunk structure, in every wave (lane = row)
-        const int doc = wave_incl_scan_i(rr.reset);
-        const uint64_t msk = __ballot(rr.reset);
+        const int doc = wave_incl_scan_i(rr.reset());
+        const uint64_t msk = __ballot(rr.reset());
         const int first_reset = msk ? __builtin_ctzll(msk) : C;
         const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
         float fu, fq, decay = 0.f;
         if constexpr (!VEC) {
-            const float beta = wave_incl_scan(rr.g);
+            const float beta = wave_incl_scan(rr.g());
             const float Gam = __shfl(beta, 63, 64);
             fu = l >= last_reset ? __expf(Gam - beta) : 0.f;
             fq = l < first_reset ? __expf(beta) : 0.f;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
                 const int idx = threadIdx.x + i * NTH;
                 const int row = idx / TR::VPR, cv = (idx % TR::VPR) * TR::VE;
                 const float f = __shfl(fu, row, 64);
-                bf16x8 x = __builtin_bit_cast(bf16x8, pv.r[i]);
+                bf16x8 x = __builtin_bit_cast(bf16x8, pv.get(i));
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * f);
                 *reinterpret_cast<bf16x8*>(sm.sVu + row * PH + cv) = x;

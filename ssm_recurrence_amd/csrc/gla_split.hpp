@@ -91,7 +91,7 @@ __device__ __forceinline__ void store_rows_split(const TileRegs<float, D, NTH>& 
         const int idx = threadIdx.x + i * NTH;
         if (idx < TR::NV_TOT) {
             const int row = idx / TR::VPR, cv = (idx % TR::VPR) * 4;
-            const f32x4 f = __builtin_bit_cast(f32x4, t.r[i]);
+            const f32x4 f = __builtin_bit_cast(f32x4, t.get(i));
             split4_store(f[0], f[1], f[2], f[3], dst + row * P + cv, dst + PLANE + row * P + cv);
         }
     }

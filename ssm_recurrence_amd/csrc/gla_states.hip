@@ -153,7 +153,7 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
         if constexpr (VEC) pg.store_rows(sG, PB);
         if (w == 0) {
             const int r = l;
-            const uint64_t msk = __ballot(rr.reset);
+            const uint64_t msk = __ballot(rr.reset());
             const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
             const int first_reset = msk ? __builtin_ctzll(msk) : C;
             if (r == 0) {
@@ -161,7 +161,7 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
                 sm.sFirstReset = first_reset;
             }
             if constexpr (!VEC) {
-                const float beta = wave_incl_scan(rr.g);
+                const float beta = wave_incl_scan(rr.g());
                 const float Gam = __shfl(beta, 63, 64);
                 if constexpr (REV) sm.sFu[r] = r < first_reset ? __expf(beta) : 0.f;
                 else sm.sFu[r] = r >= last_reset ? __expf(Gam - beta) : 0.f;
@@ -345,10 +345,10 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
         const int64_t t0 = ci * C;
         if constexpr (MODE == ST_STATES || MODE == ST_DSTATES) store_state(ci);
         // chunk structure in every wave (lane = row)
-        const uint64_t msk = __ballot(rr.reset);
+        const uint64_t msk = __ballot(rr.reset());
         const int last_reset = msk ? 63 - __builtin_clzll(msk) : -1;
         const int first_reset = msk ? __builtin_ctzll(msk) : C;
-        const float beta = wave_incl_scan(rr.g);
+        const float beta = wave_incl_scan(rr.g());
         const float Gam = __shfl(beta, 63, 64);
         float fu;
         if constexpr (REV) fu = l < first_reset ? __expf(beta) : 0.f;
@@ -364,11 +364,11 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
                 const int row = idx / TR::VPR, cv = (idx % TR::VPR) * TR::VE;
                 const float f = __shfl(fu, row, 64);
                 if constexpr (SPLIT) {
-                    const f32x4 x = __builtin_bit_cast(f32x4, pk.r[i]);
+                    const f32x4 x = __builtin_bit_cast(f32x4, pk.get(i));
                     split4_store(x[0] * f, x[1] * f, x[2] * f, x[3] * f, sm.sKu + row * PB + cv,
                                  sm.sKu + PLB + row * PB + cv);
                 } else {
-                    bf16x8 x = __builtin_bit_cast(bf16x8, pk.r[i]);
+                    bf16x8 x = __builtin_bit_cast(bf16x8, pk.get(i));
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * f);
                     *reinterpret_cast<bf16x8*>(sm.sKu + row * PB + cv) = x;

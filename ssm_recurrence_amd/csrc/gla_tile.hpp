@@ -22,18 +22,27 @@ struct TileRegs {
     static constexpr int NV_TOT = C * VPR;            // vectors per tile
     static constexpr int NVEC = (NV_TOT + NTH - 1) / NTH;
     i32x4 r[NVEC];
+    uint32_t okm;  // bit i: vector i lies in a row before nvalid (else it reads as zero)
 
-    // rows t0.. of a row-major tensor (row stride rs elements); rows >= nvalid read as zero
+    // rows t0.. of a row-major tensor (row stride rs elements); rows >= nvalid read as
+    // zero.  Every lane loads (a row past the end reads row 0 instead) and the
+    // zeroing is applied where the registers are used (get): a select on loaded
+    // registers here would make the compiler wait for every load in flight.
     __device__ __forceinline__ void load(const T* src, int64_t rs, int nvalid) {
+        okm = 0;
 #pragma unroll
         for (int i = 0; i < NVEC; ++i) {
             const int idx = threadIdx.x + i * NTH;
             const int row = idx / VPR, cv = (idx % VPR) * VE;
-            i32x4 z = {0, 0, 0, 0};
-            r[i] = z;
-            if (idx < NV_TOT && row < nvalid)
-                r[i] = *reinterpret_cast<const i32x4*>(src + (int64_t)row * rs + cv);
+            const bool ok = idx < NV_TOT && row < nvalid;
+            r[i] = *reinterpret_cast<const i32x4*>(src + (ok ? (int64_t)row * rs + cv : (int64_t)0));
+            okm |= (uint32_t)ok << i;
         }
+    }
+    // vector i as loaded, or zero past the end
+    __device__ __forceinline__ i32x4 get(int i) const {
+        const i32x4 z = {0, 0, 0, 0};
+        return ((okm >> i) & 1u) ? r[i] : z;
     }
     // dst[row][col] with pitch P
     __device__ __forceinline__ void store_rows(T* dst, int P) const {
@@ -42,7 +51,7 @@ struct TileRegs {
             const int idx = threadIdx.x + i * NTH;
             if (idx < NV_TOT) {
                 const int row = idx / VPR, cv = (idx % VPR) * VE;
-                *reinterpret_cast<i32x4*>(dst + row * P + cv) = r[i];
+                *reinterpret_cast<i32x4*>(dst + row * P + cv) = get(i);
             }
         }
     }
@@ -53,6 +62,8 @@ struct TileRegs {
             const int idx = threadIdx.x + i * NTH;
             if (idx < NV_TOT) {
                 const float f = scale[idx / VPR];
+                r[i] = get(i);
+                okm |= 1u << i;
                 T* e = reinterpret_cast<T*>(&r[i]);
 #pragma unroll
                 for (int k = 0; k < VE; ++k) e[k] = (T)((float)e[k] * f);
@@ -67,7 +78,8 @@ struct TileRegs {
             if (idx < NV_TOT) {
                 const int row = idx / VPR, cv = (idx % VPR) * VE;
                 typedef __attribute__((__vector_size__(8))) int i32x2;
-                const i32x2 lo = {r[i][0], r[i][1]}, hi = {r[i][2], r[i][3]};
+                const i32x4 x = get(i);
+                const i32x2 lo = {x[0], x[1]}, hi = {x[2], x[3]};
                 *reinterpret_cast<i32x2*>(dst + row * P + cv) = lo;
                 *reinterpret_cast<i32x2*>(dst + row * P + cv + VE / 2) = hi;
             }
@@ -80,7 +92,8 @@ struct TileRegs {
             const int idx = threadIdx.x + i * NTH;
             if (idx < NV_TOT) {
                 const int row = idx / VPR, cv = (idx % VPR) * VE;
-                const T* e = reinterpret_cast<const T*>(&r[i]);
+                const i32x4 x = get(i);
+                const T* e = reinterpret_cast<const T*>(&x);
 #pragma unroll
                 for (int k = 0; k < VE; ++k) dst[(cv + k) * P + row] = e[k];
             }
@@ -88,20 +101,46 @@ struct TileRegs {
     }
 };
 
-// Per-lane values for one chunk that wave 0 needs: the scalar gate of row
-// `lane` and the reset flag of row `lane`.
+// Per-lane values for one chunk: the scalar gate of row `lane` and the segment
+// ids of rows lane - 1 and lane.  They are kept as loaded (raw gate bits,
+// unconverted ids) and turned into values only when the chunk is processed
+// (g(), reset()): any arithmetic on a loaded value makes the compiler wait for
+// every load still in flight, which would make the loads issued ahead with
+// this chunk's tiles synchronous.
 struct RowRegs {
-    float g;
-    int reset;
+    uint32_t graw;   // gate bits: bf16 in the low half, or fp32
+    int gkind;       // 0: no gate (vector gate, or row past the end), 2: bf16, 4: fp32
+    int seg_prev, seg_cur;
+    int segok;       // 1 when seg_prev, seg_cur are the ids of rows lane - 1 and lane
     template <typename T>
     __device__ __forceinline__ void load(const T* gcol, int64_t rs_g, const int32_t* seg, int64_t b,
                                          int64_t T_, int64_t t0, int nvalid, bool scalar_gate) {
         const int r = lane_id();
         const int64_t t = t0 + r;
-        g = (scalar_gate && r < nvalid) ? to_f32(gcol[(int64_t)r * rs_g]) : 0.f;
-        reset = 0;
-        if (seg != nullptr && r < nvalid && t > 0) reset = seg[b * T_ + t] != seg[b * T_ + t - 1];
+        const bool ok = r < nvalid;
+        graw = 0;
+        gkind = 0;
+        if (scalar_gate) {
+            const T x = gcol[(int64_t)(ok ? r : 0) * rs_g];  // an existing row even past the end
+            if constexpr (sizeof(T) == 2) graw = (uint32_t)__builtin_bit_cast(uint16_t, x);
+            else graw = __builtin_bit_cast(uint32_t, x);
+            gkind = ok ? (int)sizeof(T) : 0;
+        }
+        seg_prev = seg_cur = 0;
+        segok = 0;
+        if (seg != nullptr && T_ > 1) {
+            const int64_t tc = ok && t > 0 ? t : 1;  // an existing pair of rows
+            seg_prev = seg[b * T_ + tc - 1];
+            seg_cur = seg[b * T_ + tc];
+            segok = ok && t > 0;
+        }
     }
+    // the scalar log gate of row `lane` (0 past the end)
+    __device__ __forceinline__ float g() const {
+        return gkind == 0 ? 0.f : (gkind == 2 ? __uint_as_float(graw << 16) : __uint_as_float(graw));
+    }
+    // 1 if row `lane` starts a new document (its id differs from the previous row's)
+    __device__ __forceinline__ int reset() const { return segok && seg_cur != seg_prev; }
 };
 
 // Document structure of a chunk from the per-row reset flags (wave 0 only).
