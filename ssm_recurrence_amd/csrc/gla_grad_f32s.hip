@@ -60,9 +60,10 @@ struct SmallS {
 // summed over those heads in registers (the head-sharing reduction of the FLAT
 // page, Pallas Kernels > Gated Linear Attention, done in place of per-head
 // buffers), and each head's log-gate partial sums are written for the
-// finisher.  The next head's v, dO and gates (or the next item's q, k and
-// first head) are loaded into registers while the current head computes; a
-// head's state and state-gradient rows are requested before its tiles are staged.
+// finisher.  The next head's v, dO and gates (or the next item's first head)
+// are loaded into registers while the current head computes; a head's state
+// and state-gradient rows are requested before its tiles are staged; q and k
+// are loaded at the item's start (once per G heads).
 
 // v, dO and gate inputs of one head of a QK item
 struct QKHeadRegs {
@@ -127,14 +128,9 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
     const int64_t nitems = a.B * a.Hqk * NC * 2;
     const int64_t stride = gridDim.x;
 
-    TileRegs<float, 64> pq, pk;
     QKHeadRegs hr;
     int64_t item = xcd_logical_block(gridDim.x);
-    if (item < nitems) {
-        const QKItem it = qk_item(a, item);
-        qk_load_qk(a, it, pq, pk);
-        qk_load_head(a, it, 0, hr);
-    }
+    if (item < nitems) qk_load_head(a, qk_item(a, item), 0, hr);
     for (; item < nitems; item += stride) {
         const QKItem it = qk_item(a, item);
         const int64_t b = it.b, hq = it.hq, ci = it.ci;
@@ -143,8 +139,12 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
         const int64_t t0 = ci * C;
         const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
 
-        store_rows_split<64>(pq, sQ, P64, PL64);
-        store_rows_split<64>(pk, sK, P64, PL64);
+        {
+            TileRegs<float, 64> pq, pk;
+            qk_load_qk(a, it, pq, pk);
+            store_rows_split<64>(pq, sQ, P64, PL64);
+            store_rows_split<64>(pk, sK, P64, PL64);
+        }
         float dqs[4][4], dks[4][4];  // dq, dk summed over the heads of the group
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -175,9 +175,7 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
             if (gi + 1 < G) {
                 qk_load_head(a, it, gi + 1, hr);
             } else if (item + stride < nitems) {
-                const QKItem nx = qk_item(a, item + stride);
-                qk_load_qk(a, nx, pq, pk);
-                qk_load_head(a, nx, 0, hr);
+                qk_load_head(a, qk_item(a, item + stride), 0, hr);
             }
 
             // dA^T = v dO^T tiles, masked, stored dA[r][s]
