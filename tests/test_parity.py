@@ -97,6 +97,10 @@ SMALL = [
     (256, 128, 128, "scalar", torch.bfloat16, 4, 2, [64, 64, 1, 1, 1, 60, 65], True),
     (190, 64, 64, "vector", torch.bfloat16, 2, 1, [5, 7, 1, 100, 77], False),
     (300, 64, 128, "scalar", torch.bfloat16, 8, 2, None, True),
+    # one- and two-token rows with segment ids (a reset on the second token)
+    (1, 128, 128, "scalar", torch.bfloat16, 2, 2, [1], True),
+    (2, 128, 128, "scalar", torch.float32, 2, 2, [1, 1], True),
+    (2, 128, 128, "vector", torch.bfloat16, 2, 2, [1, 1], True),
 ]
 
 
