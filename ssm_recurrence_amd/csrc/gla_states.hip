@@ -83,6 +83,11 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
     const int64_t NC = (T_ + C - 1) / C;
     const int64_t cbeg = piece * a.PL;
     const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
+    // Summaries no combine reads: the forward summary of the last piece and the
+    // reverse summary of the first (the last piece's decay product, which the
+    // reverse combine needs, comes from its reverse summary instead).
+    if constexpr (MODE == ST_SUM_FWD) if (piece == P - 1) return;
+    if constexpr (MODE == ST_SUM_REV) if (piece == 0) return;
 
     // the gradient modes run the same update with (q, dO) in place of (k, v)
     const T* k = (const T*)(REV ? a.q : a.k);
@@ -237,7 +242,7 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
             *reinterpret_cast<f32x4*>(a.L_out[MODE == ST_SUM_REV ? 1 : 0] + prow + 16 * nt + 4 * j4) = St[nt];
-        if (MODE == ST_SUM_FWD && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
+        if ((MODE == ST_SUM_FWD || piece == P - 1) && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
     }
 }
 
@@ -282,6 +287,11 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
     const int64_t NC = (T_ + C - 1) / C;
     const int64_t cbeg = piece * a.PL;
     const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
+    // Summaries no combine reads: the forward summary of the last piece and the
+    // reverse summary of the first (the last piece's decay product, which the
+    // reverse combine needs, comes from its reverse summary instead).
+    if constexpr (MODE == ST_SUM_FWD) if (piece == P - 1) return;
+    if constexpr (MODE == ST_SUM_REV) if (piece == 0) return;
 
     const T* k = (const T*)(REV ? a.q : a.k);
     const T* v = (const T*)(REV ? a.dO : a.v);
@@ -416,7 +426,7 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
             *reinterpret_cast<f32x4*>(a.L_out[MODE == ST_SUM_REV ? 1 : 0] + prow + 16 * nt + 4 * j4) = St[nt];
-        if (MODE == ST_SUM_FWD && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
+        if ((MODE == ST_SUM_FWD || piece == P - 1) && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
     }
 }
 
