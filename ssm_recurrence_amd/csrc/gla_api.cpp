@@ -58,6 +58,12 @@ struct Split {
     int64_t P = 1, PL = 0;
 };
 
+// bf16, scalar gate, 128 x 128: the backward walks each piece in reverse with the
+// state gradient resident (no per-chunk state-gradient pass)
+bool walk_bwd(const gla_problem* p) {
+    return p->dtype == GLA_BF16 && p->gate == GLA_GATE_SCALAR && p->d_k == 128 && p->d_v == 128;
+}
+
 Split plan_split(const gla_problem* p, int for_backward) {
     Split s;
     const int64_t nc = (p->T + 63) / 64;
@@ -69,7 +75,11 @@ Split plan_split(const gla_problem* p, int for_backward) {
         P = p->split;
     } else {
         int64_t per_head, target;  // workgroups per (b, h) without a split
-        if (for_backward) {
+        if (for_backward && walk_bwd(p)) {
+            per_head = 1;  // one walking workgroup per piece
+            if (bh >= kTargetWG) return s;
+            target = kTargetWG;
+        } else if (for_backward) {
             per_head = 2 * (p->d_k / 64) * (p->d_v / 64);
             if (bh * per_head >= kNoSplitBwd) return s;
             target = kTargetWGBwd;
@@ -139,8 +149,10 @@ WsLayout ws_layout(const gla_problem* p, int for_backward) {
     }
     L.S = off;
     off += round_up(bh * (size_t)(nc + 1) * st);
-    L.dS = off;
-    off += round_up(bh * (size_t)nc * st);
+    if (!walk_bwd(p)) {
+        L.dS = off;
+        off += round_up(bh * (size_t)nc * st);
+    }
     if (per_head_dqdk(p)) {
         const size_t n = (size_t)(p->B * p->T * p->H * p->d_k) * sizeof(float);
         L.dq = off;
@@ -257,9 +269,15 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
         e = gla::launch_piece_combine(combine_args(pa, DK, DV, 3), st);
         if (e != hipSuccess) return e;
     }
-    e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
-    if (e != hipSuccess) return e;
-    e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
+    if constexpr (sizeof(T) == 2 && !VEC && DK == 128 && DV == 128) {
+        e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, wide_blocks(pa, DK, 1, 256), st);
+        if (e != hipSuccess) return e;
+        e = gla::launch_grad8_walk(ra, st);
+    } else {
+        e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
+        if (e != hipSuccess) return e;
+        e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
+    }
     if (e != hipSuccess) return e;
     if (ra.ws_dq) {
         e = gla::launch_group_sum<T, DK>(ra.ws_dq, ra.dq, ra.B, ra.T, ra.H, ra.Hqk, st);
@@ -360,7 +378,7 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     pa.q = q; pa.k = k; pa.v = v; pa.g = g; pa.dO = dO; pa.h0 = h0; pa.dhT = dhT; pa.seg = segment_ids;
     pa.dh0 = dh0;
     pa.ws_S = (float*)(w + L.S);
-    pa.ws_dS = w + L.dS;
+    pa.ws_dS = walk_bwd(p) ? nullptr : w + L.dS;
     pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.Hqk = p->H_qk;
     pa.P = L.sp.P; pa.PL = L.sp.PL;
     if (pa.P > 1) {
@@ -374,7 +392,7 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     memset(&ra, 0, sizeof ra);
     ra.q = q; ra.k = k; ra.v = v; ra.g = g; ra.dO = dO; ra.seg = segment_ids;
     ra.ws_S = w + L.S;
-    ra.ws_dS = w + L.dS;
+    ra.ws_dS = pa.ws_dS;
     ra.dhT = dhT; ra.dh0 = dh0;
     ra.dq = dq; ra.dk = dk; ra.dv = dv; ra.dg = dg;
     if (per_head_dqdk(p)) {
@@ -386,6 +404,7 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
         ra.ws_bnd = (float*)(w + L.bnd);
     }
     ra.B = p->B; ra.T = p->T; ra.H = p->H; ra.Hqk = p->H_qk;
+    ra.P = pa.P; ra.PL = pa.PL; ra.dS_in = pa.dS_in;
     return dispatch<BwdF>(p, pa, ra, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 

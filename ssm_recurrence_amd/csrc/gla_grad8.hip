@@ -26,7 +26,9 @@
 
 namespace gla {
 
-template <bool VEC>
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+
+template <bool VEC, bool WALK>
 struct Grad8Cfg {
     using T = bf16;
     static constexpr int NW = 8, NTH = 64 * NW;
@@ -34,23 +36,31 @@ struct Grad8Cfg {
     static constexpr int P = Pitch16<T>::of(128);  // [rows][128] tiles
     static constexpr int PB = Pitch16<T>::of(64);  // [64][64] score tiles
     static constexpr int PE = 132;                 // fp32 [64][128] dg scratch
+    static constexpr int PF = 132;                 // fp32 [128][128] state gradient (walk)
     static constexpr int TILE = C * P * 2;
     static constexpr int OFF_Q = 0, OFF_K = TILE, OFF_G = 2 * TILE;
     static constexpr int OFF_V = OFF_G + (VEC ? TILE : 0);
     static constexpr int OFF_DO = OFF_V + TILE;
     static constexpr int OFF_DA = OFF_DO + TILE;   // dA [r][s]
     static constexpr int OFF_AT = OFF_DA + C * PB * 2;  // A^T [s][r]
-    static constexpr int OFF_DS = OFF_AT + C * PB * 2;  // dS1' [c][n]
-    static constexpr int BYTES = OFF_DS + DK * P * 2;
+    static constexpr int OFF_DS = OFF_AT + C * PB * 2;  // dS1' [c][n] (walk: fp32)
+    static constexpr int BYTES = OFF_DS + (WALK ? DK * PF * 4 : DK * P * 2);
     static_assert(2 * TILE >= C * PE * 4, "dg scratch does not fit in the v / dO region");
 };
 
-template <bool VEC>
+// WALK (scalar gate only): a workgroup walks the chunks of one (b, h, piece) from
+// last to first with the state gradient in LDS (fp32), applying the reverse update
+// dS <- decay dS + sum over the chunk's first-document rows of exp(beta_r) q_r dO_r^T
+// after each chunk (FLAT page, Linear Attention > Backward Recurrence: the state
+// gradient runs backwards in time, scaled by the gate at each step), so the state
+// gradient is never written per chunk.
+template <bool VEC, bool WALK>
 __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
+    static_assert(!(VEC && WALK), "the walk is built for the scalar gate");
     using T = bf16;
-    using Cfg = Grad8Cfg<VEC>;
+    using Cfg = Grad8Cfg<VEC, WALK>;
     using M = Mma<T>;
-    constexpr int P = Cfg::P, PB = Cfg::PB, PE = Cfg::PE, DK = 128, DV = 128;
+    constexpr int P = Cfg::P, PB = Cfg::PB, PE = Cfg::PE, PF = Cfg::PF, DK = 128, DV = 128;
     constexpr int NTH = Cfg::NTH, KS = M::KSTEP, NKV = DV / KS;
 
     __shared__ __attribute__((aligned(16))) char lds[Cfg::BYTES];
@@ -66,6 +76,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     T* sdA = reinterpret_cast<T*>(lds + Cfg::OFF_DA);
     T* sAT = reinterpret_cast<T*>(lds + Cfg::OFF_AT);
     T* sdS = reinterpret_cast<T*>(lds + Cfg::OFF_DS);
+    float* sM = reinterpret_cast<float*>(lds + Cfg::OFF_DS);  // walk: state gradient [c][n]
     float* sX = reinterpret_cast<float*>(lds + Cfg::OFF_V);  // dg scratch [r][c], after dv
 
     const int64_t T_ = a.T;
@@ -96,29 +107,69 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
         pdo.load((const T*)a.dO + (b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
         if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
     };
-    int64_t item = blockIdx.x;
-    if constexpr (PREFETCH) {
-        if (item < nitems) issue(item);
-    }
+    // Work order.  Units are items (b, h, chunk), or for the walk pieces (b, h, piece),
+    // strided over the grid; a walk visits its unit's chunks from last to first.
+    // item = bh * NC + chunk in both cases.
+    const int64_t nunits = WALK ? a.B * a.H * a.P : nitems;
+    auto unit_first = [&](int64_t u) -> int64_t {  // the unit's first item
+        if constexpr (WALK) {
+            const int64_t piece = u % a.P, bh = u / a.P;
+            const int64_t ce = (piece + 1) * a.PL < NC ? (piece + 1) * a.PL : NC;
+            return bh * NC + ce - 1;
+        } else {
+            return u;
+        }
+    };
     // (vector gate: the stride ends the loop after one item, visibly to the compiler)
     const int64_t stride = PREFETCH ? (int64_t)gridDim.x : nitems;
-    for (; item < nitems; item += stride) {
+    int64_t unit = blockIdx.x;
+    int64_t item = unit < nunits ? unit_first(unit) : 0;
+    if constexpr (PREFETCH) {
+        if (unit < nunits) issue(item);
+    }
+    for (; unit < nunits;) {
     if constexpr (!PREFETCH) issue(item);
     const int64_t ci = item % NC, bh = item / NC;
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t hq = h / G;
     const int64_t t0 = ci * C;
     const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
+    // the item after this one
+    const int64_t piece = WALK ? unit % a.P : 0;
+    const bool unit_start = WALK ? (ci == ((piece + 1) * a.PL < NC ? (piece + 1) * a.PL : NC) - 1) : true;
+    const bool unit_end = WALK ? ci == piece * a.PL : true;
+    const int64_t next_unit = unit_end ? unit + stride : unit;
+    const int64_t next_item = unit_end ? (next_unit < nunits ? unit_first(next_unit) : 0) : item - 1;
     // rows cw + i of S0 and dS1 (the A operands of dO S0^T and v dS1^T, k = n)
     const T* S0 = (const T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
-    const T* dS1 = (const T*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
 
     // ---- phase 1: this item's tiles to LDS; its S0 and dS1 rows to registers
     bf16x8 s0f[NKV], dsf[NKV];
 #pragma unroll
-    for (int kk = 0; kk < NKV; ++kk) {
-        s0f[kk] = *reinterpret_cast<const bf16x8*>(S0 + kk * KS + 8 * j4);
-        dsf[kk] = *reinterpret_cast<const bf16x8*>(dS1 + kk * KS + 8 * j4);
+    for (int kk = 0; kk < NKV; ++kk) s0f[kk] = *reinterpret_cast<const bf16x8*>(S0 + kk * KS + 8 * j4);
+    if constexpr (WALK) {
+        // the wave's own rows of the state gradient: set at a walk's start (the
+        // gradient at the piece's end), else left by the update after the chunk above
+        float* mrow = sM + (cw + i16) * PF;
+        if (unit_start) {
+            const float* src = a.P > 1 ? a.dS_in + ((bh * a.P + piece) * DK + cw + i16) * DV
+                                       : (a.dhT ? a.dhT + (bh * DK + cw + i16) * DV : nullptr);
+#pragma unroll
+            for (int nt = 0; nt < DV / 16; ++nt)
+                *reinterpret_cast<f32x4*>(mrow + 16 * nt + 4 * j4) =
+                    src ? *reinterpret_cast<const f32x4*>(src + 16 * nt + 4 * j4) : zero4();
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(mrow + kk * KS + 8 * j4);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(mrow + kk * KS + 8 * j4 + 4);
+            const f32x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+            dsf[kk] = __builtin_convertvector(x, bf16x8);
+        }
+    } else {
+        const T* dS1 = (const T*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) dsf[kk] = *reinterpret_cast<const bf16x8*>(dS1 + kk * KS + 8 * j4);
     }
     pq.store_rows(sQ, P);
     pk.store_rows(sK, P);
@@ -128,7 +179,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
     __syncthreads();
     if constexpr (PREFETCH) {
-        if (item + stride < nitems) issue(item + stride);
+        if (next_unit < nunits) issue(next_item);
     }
     [[maybe_unused]] const TriOnes<T> tri;
 
@@ -197,9 +248,11 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             em[e] = egm[e] = 1.f;
             dec[e] = ck.decay;
         }
+        if constexpr (!WALK) {
 #pragma unroll
-        for (int kk = 0; kk < NKV; ++kk)
-            *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = dsf[kk];
+            for (int kk = 0; kk < NKV; ++kk)
+                *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = dsf[kk];
+        }
     }
     // dA^T = v dO^T tiles, masked, stored as dA[r][s] (10 lower + 2 zero upper tiles)
     for (int ti = w; ti < 12; ti += Cfg::NW) {
@@ -294,6 +347,19 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     // ---- phase 3b: dv^T = dO^T A + [last doc] dS1'^T KA^T for value columns cw .. cw + 15
     {
         T* dvo = (T*)a.dv + ((b * T_ + t0) * a.H + h) * DV + cw + 4 * j4;
+        // dS1'^T rows (value columns cw + i16), k = key channel
+        bf16x8 dsc[DK / KS];
+#pragma unroll
+        for (int kk = 0; kk < DK / KS; ++kk) {
+            if constexpr (WALK) {
+                f32x8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = sM[(kk * KS + 8 * j4 + e) * PF + cw + i16];
+                dsc[kk] = __builtin_convertvector(x, bf16x8);
+            } else {
+                dsc[kk] = frag_col<T, P, false>(sdS, cw, kk * KS);
+            }
+        }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             f32x4 a1 = zero4(), a2 = zero4();
@@ -302,8 +368,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             for (int k0 = kbeg; k0 < C; k0 += KS)
                 a1 = M::mma(frag_col<T, P, false>(sdO, cw, k0), frag_ld<T, PB, 1>(sAT, 16 * st, k0), a1);
 #pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += KS)
-                a2 = M::mma(frag_col<T, P, false>(sdS, cw, k0), frag_ld<T, P, 1>(sK, 16 * st, k0), a2);
+            for (int kk = 0; kk < DK / KS; ++kk)
+                a2 = M::mma(dsc[kk], frag_ld<T, P, 1>(sK, 16 * st, kk * KS), a2);
             const int s = 16 * st + i16;
             const float fu = ck.fu[s];
             float dv[4];
@@ -404,7 +470,41 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             if (r < nvalid) ((T*)a.dg)[(b * T_ + t0 + r) * a.H + h] = from_f32<T>(reset ? 0.f : run);
         }
     }
+    if constexpr (WALK) {
+        // ---- phase 4: the state gradient at the previous chunk's end, rows cw + i16
+        // (every wave has read the columns dv needs: the barrier of phase 3c), as
+        // C-layout tiles [n][c]: lane n = 16nt + 4j4 + e, c = cw + i16
+        bf16x8 qf[C / KS];
+#pragma unroll
+        for (int kk = 0; kk < C / KS; ++kk) {
+            qf[kk] = frag_col<T, P, false>(sQ, cw, kk * KS);
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(&ck.fq[kk * KS + 8 * j4]);
+            const f32x4 f1 = *reinterpret_cast<const f32x4*>(&ck.fq[kk * KS + 8 * j4 + 4]);
+            const f32x8 f = __builtin_shufflevector(f0, f1, 0, 1, 2, 3, 4, 5, 6, 7);
+            f32x8 x = __builtin_convertvector(qf[kk], f32x8);
+            qf[kk] = __builtin_convertvector(x * f, bf16x8);
+        }
+        const float dec = ck.decay;
+        float* mrow = sM + (cw + i16) * PF;
+        f32x4 acc[DV / 16];
+#pragma unroll
+        for (int nt = 0; nt < DV / 16; ++nt) acc[nt] = *reinterpret_cast<const f32x4*>(mrow + 16 * nt + 4 * j4) * dec;
+#pragma unroll
+        for (int nt = 0; nt < DV / 16; ++nt)
+#pragma unroll
+            for (int kk = 0; kk < C / KS; ++kk)
+                acc[nt] = M::mma(frag_col<T, P, false>(sdO, 16 * nt, kk * KS), qf[kk], acc[nt]);
+#pragma unroll
+        for (int nt = 0; nt < DV / 16; ++nt) *reinterpret_cast<f32x4*>(mrow + 16 * nt + 4 * j4) = acc[nt];
+        if (unit_end && piece == 0 && a.dh0) {
+#pragma unroll
+            for (int nt = 0; nt < DV / 16; ++nt)
+                *reinterpret_cast<f32x4*>(a.dh0 + (bh * DK + cw + i16) * DV + 16 * nt + 4 * j4) = acc[nt];
+        }
+    }
     __syncthreads();  // LDS and the chunk data are rewritten by the next item
+    unit = next_unit;
+    item = next_item;
     }
 }
 
@@ -417,7 +517,14 @@ hipError_t launch_grad8(const RevArgs& a, hipStream_t st) {
     const int64_t NC = (a.T + C - 1) / C;
     const int64_t items = a.B * a.H * NC;
     const int64_t grid = (VEC || items < kGrad8Workers) ? items : kGrad8Workers;
-    hipLaunchKernelGGL((k_grad8<VEC>), dim3((unsigned)grid), dim3(Grad8Cfg<VEC>::NTH), 0, st, a);
+    hipLaunchKernelGGL((k_grad8<VEC, false>), dim3((unsigned)grid), dim3(Grad8Cfg<VEC, false>::NTH), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad8_walk(const RevArgs& a, hipStream_t st) {
+    const int64_t units = a.B * a.H * a.P;
+    const int64_t grid = units < kGrad8Workers ? units : kGrad8Workers;
+    hipLaunchKernelGGL((k_grad8<false, true>), dim3((unsigned)grid), dim3(Grad8Cfg<false, true>::NTH), 0, st, a);
     return hipGetLastError();
 }
 

@@ -34,6 +34,9 @@ struct RevArgs {
     float *ws_dq, *ws_dk;  // per-head fp32 [B][T][H][DK] when heads share q/k
     float *ws_xs, *ws_bnd; // scalar gate: per-slice partial sums [B*H][slices][T], [B*H][slices][NC]
     int64_t B, T, H, Hqk;
+    // the split of the reverse walk (launch_grad8_walk): P pieces of PL chunks
+    int64_t P, PL;
+    const float* dS_in;    // [B*H][P][DK][DV]: state gradient at each piece's end (P > 1)
 };
 
 struct CombineArgs {
@@ -62,6 +65,10 @@ hipError_t launch_dg_scalar(const RevArgs& a, int nslices, bool bf16_out, hipStr
 // bf16, d_k = d_v = 128: one eight-wave workgroup per chunk (scalar dg finished in-kernel)
 template <bool VEC>
 hipError_t launch_grad8(const RevArgs& a, hipStream_t st);
+// bf16, scalar gate, d_k = d_v = 128: one workgroup per (b, h, piece) walking its
+// chunks last to first with the state gradient resident (needs only the per-chunk
+// states, not the per-chunk state gradients)
+hipError_t launch_grad8_walk(const RevArgs& a, hipStream_t st);
 
 // fp32, scalar gate, d_k = d_v = 128: split-bf16 products (includes the dg finisher)
 hipError_t launch_grad_f32s(const RevArgs& a, hipStream_t st);
