@@ -214,6 +214,15 @@ __device__ __forceinline__ float frag_dot(const F& a, const F& b, float acc) {
         return acc;
     }
 }
+// Tiles of a 64 x 64 causal score matrix in 16 x 16 blocks: ti = 0 .. 9 are the
+// blocks with rt >= st (row-major), 10 and 11 the two zero blocks above the
+// diagonal that a 32-wide k step also reads.  Packed as 2-bit fields, so that the
+// compiler knows rt and st lie in [0, 3] and keeps the index arithmetic in 32
+// bits (a 64-bit multiply-add here reads an undefined high half, and a load in
+// flight to that register would then be waited for).
+__device__ __forceinline__ int score_tile_rt(int ti) { return (0x8ffa94 >> (2 * ti)) & 3; }
+__device__ __forceinline__ int score_tile_st(int ti) { return (0xde4910 >> (2 * ti)) & 3; }
+
 __device__ __forceinline__ float wave_incl_scan(float x) {
     const int l = lane_id();
 #pragma unroll

@@ -142,8 +142,8 @@ __global__ __launch_bounds__(512) void k_fwd_f32h(const PassArgs a) {
         // ---- masked score tiles, computed transposed (rows s, column r), stored sA[r][s];
         // tiles 10 and 11 are the zero tiles (0,1) and (2,3) that a 32-wide step reads
         for (int ti = w; ti < 12; ti += 8) {
-            const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-            const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+            const int rt = score_tile_rt(ti);
+            const int st = score_tile_st(ti);
             f32x4 acc = zero4();
             if (ti < 10) {
 #pragma unroll

@@ -209,8 +209,8 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     // ---- dA^T = v dO^T on the 10 lower tiles (+ the two upper tiles a 32-wide k
     // step reads), masked, stored as dA[r][s]
     for (int ti = w; ti < 12; ti += 4) {
-        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+        const int rt = score_tile_rt(ti);
+        const int st = score_tile_st(ti);
         f32x4 acc = zero4();
         if (ti < 10) {
 #pragma unroll
@@ -465,8 +465,8 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
 
     // ---- A = QA KA^T on the lower tiles (+ two zero upper tiles), transposed: sAT[s][r]
     for (int ti = w; ti < 12; ti += 4) {
-        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+        const int rt = score_tile_rt(ti);
+        const int st = score_tile_st(ti);
         f32x4 acc = zero4();
         if (ti < 10) {
 #pragma unroll

@@ -33,8 +33,10 @@ struct Grad8Cfg {
     using T = bf16;
     static constexpr int NW = 8, NTH = 64 * NW;
     static constexpr int DK = 128, DV = 128;
-    static constexpr int P = Pitch16<T>::of(128);  // [rows][128] tiles
-    static constexpr int PB = Pitch16<T>::of(64);  // [64][64] score tiles
+    // 16-byte row reads of bf16 tiles are free of bank conflicts at pitches of
+    // 16 (mod 64) elements (measured on gfx950; 8 (mod 64) gives two-way conflicts)
+    static constexpr int P = 128 + 16;             // [rows][128] tiles
+    static constexpr int PB = 64 + 16;             // [64][64] score tiles
     static constexpr int PE = 132;                 // fp32 [64][128] dg scratch
     static constexpr int PF = 132;                 // fp32 [128][128] state gradient (walk)
     static constexpr int TILE = C * P * 2;
@@ -65,9 +67,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
 
     __shared__ __attribute__((aligned(16))) char lds[Cfg::BYTES];
     __shared__ RevChunk ck;
-    __shared__ float sXs[8][C];
     __shared__ float sBs[8];
-    __shared__ float sBnd[8][16];
+    __shared__ float sBnd[VEC ? 8 : 1][16];
     T* sQ = reinterpret_cast<T*>(lds + Cfg::OFF_Q);
     T* sK = reinterpret_cast<T*>(lds + Cfg::OFF_K);
     T* sG = reinterpret_cast<T*>(lds + Cfg::OFF_G);  // vector gate only
@@ -78,6 +79,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     T* sdS = reinterpret_cast<T*>(lds + Cfg::OFF_DS);
     float* sM = reinterpret_cast<float*>(lds + Cfg::OFF_DS);  // walk: state gradient [c][n]
     float* sX = reinterpret_cast<float*>(lds + Cfg::OFF_V);  // dg scratch [r][c], after dv
+    // scalar gate: per-wave row sums [8][C] for dg, in the dA tile (read only before dv)
+    float (*sXs)[C] = reinterpret_cast<float (*)[C]>(lds + Cfg::OFF_DA);
 
     const int64_t T_ = a.T;
     const int64_t NC = (T_ + C - 1) / C;
@@ -94,10 +97,11 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     constexpr bool PREFETCH = !VEC;
     TileRegs<T, 128, NTH> pq, pk, pg, pv, pdo;
     RowRegs rr;
-    auto issue = [&](int64_t item) {
-        const int64_t ci = item % NC, bh = item / NC;
-        const int64_t b = bh / a.H, h = bh % a.H, hq = h / G;
-        const int64_t t0 = ci * C;
+    // item indices in 32 bits (the launch checks B * H * NC < 2^31)
+    const uint32_t NC32 = (uint32_t)NC, H32 = (uint32_t)a.H, G32 = (uint32_t)G;
+    auto issue = [&](uint32_t bh, uint32_t ci) {
+        const uint32_t b = bh / H32, h = bh - b * H32, hq = h / G32;
+        const int64_t t0 = (int64_t)ci * C;
         const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
         pq.load((const T*)a.q + (b * T_ + t0) * rs_qk + hq * DK, rs_qk, nvalid);
         pk.load((const T*)a.k + (b * T_ + t0) * rs_qk + hq * DK, rs_qk, nvalid);
@@ -109,39 +113,41 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     };
     // Work order.  Units are items (b, h, chunk), or for the walk pieces (b, h, piece),
     // strided over the grid; a walk visits its unit's chunks from last to first.
-    // item = bh * NC + chunk in both cases.
-    const int64_t nunits = WALK ? a.B * a.H * a.P : nitems;
-    auto unit_first = [&](int64_t u) -> int64_t {  // the unit's first item
+    // A position is (unit, bh, ci, cb): cb is the unit's first chunk (its last in the walk).
+    const uint32_t nunits = (uint32_t)(WALK ? a.B * a.H * a.P : nitems);
+    const uint32_t P32 = (uint32_t)a.P, PL32 = (uint32_t)a.PL;
+    struct Pos { uint32_t unit, bh, ci, cb; };
+    auto unit_pos = [&](uint32_t u) -> Pos {
         if constexpr (WALK) {
-            const int64_t piece = u % a.P, bh = u / a.P;
-            const int64_t ce = (piece + 1) * a.PL < NC ? (piece + 1) * a.PL : NC;
-            return bh * NC + ce - 1;
+            const uint32_t bh = u / P32, cb = (u - bh * P32) * PL32;
+            const uint32_t ce = cb + PL32 < NC32 ? cb + PL32 : NC32;
+            return Pos{u, bh, ce - 1, cb};
         } else {
-            return u;
+            const uint32_t bh = u / NC32, ci = u - bh * NC32;
+            return Pos{u, bh, ci, ci};
         }
     };
-    // (vector gate: the stride ends the loop after one item, visibly to the compiler)
-    const int64_t stride = PREFETCH ? (int64_t)gridDim.x : nitems;
-    int64_t unit = blockIdx.x;
-    int64_t item = unit < nunits ? unit_first(unit) : 0;
+    const uint32_t stride = PREFETCH ? gridDim.x : nunits;
+    Pos cur = unit_pos(blockIdx.x < nunits ? blockIdx.x : 0);
+    cur.unit = blockIdx.x;
+    bool unit_start = true;
     if constexpr (PREFETCH) {
-        if (unit < nunits) issue(item);
+        if (cur.unit < nunits) issue(cur.bh, cur.ci);
     }
-    for (; unit < nunits;) {
-    if constexpr (!PREFETCH) issue(item);
-    const int64_t ci = item % NC, bh = item / NC;
-    const int64_t b = bh / a.H, h = bh % a.H;
-    const int64_t hq = h / G;
-    const int64_t t0 = ci * C;
+    for (; cur.unit < nunits;) {
+    if constexpr (!PREFETCH) issue(cur.bh, cur.ci);
+    const uint32_t ci = cur.ci, bh = cur.bh;
+    const uint32_t b = bh / H32, h = bh - b * H32, hq = h / G32;
+    const int64_t t0 = (int64_t)ci * C;
     const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
     // the item after this one
-    const int64_t piece = WALK ? unit % a.P : 0;
-    const bool unit_start = WALK ? (ci == ((piece + 1) * a.PL < NC ? (piece + 1) * a.PL : NC) - 1) : true;
-    const bool unit_end = WALK ? ci == piece * a.PL : true;
-    const int64_t next_unit = unit_end ? unit + stride : unit;
-    const int64_t next_item = unit_end ? (next_unit < nunits ? unit_first(next_unit) : 0) : item - 1;
+    const bool unit_end = ci == cur.cb;
+    Pos nxt;
+    if (!unit_end) nxt = Pos{cur.unit, bh, ci - 1, cur.cb};
+    else if (cur.unit + stride < nunits) nxt = unit_pos(cur.unit + stride);
+    else nxt = Pos{nunits, 0, 0, 0};
     // rows cw + i of S0 and dS1 (the A operands of dO S0^T and v dS1^T, k = n)
-    const T* S0 = (const T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
+    const T* S0 = (const T*)a.ws_S + (((int64_t)bh * (NC + 1) + ci) * DK + cw + i16) * DV;
 
     // ---- phase 1: this item's tiles to LDS; its S0 and dS1 rows to registers
     bf16x8 s0f[NKV], dsf[NKV];
@@ -152,8 +158,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
         // gradient at the piece's end), else left by the update after the chunk above
         float* mrow = sM + (cw + i16) * PF;
         if (unit_start) {
-            const float* src = a.P > 1 ? a.dS_in + ((bh * a.P + piece) * DK + cw + i16) * DV
-                                       : (a.dhT ? a.dhT + (bh * DK + cw + i16) * DV : nullptr);
+            const float* src = a.P > 1 ? a.dS_in + ((int64_t)cur.unit * DK + cw + i16) * DV
+                                       : (a.dhT ? a.dhT + ((int64_t)bh * DK + cw + i16) * DV : nullptr);
 #pragma unroll
             for (int nt = 0; nt < DV / 16; ++nt)
                 *reinterpret_cast<f32x4*>(mrow + 16 * nt + 4 * j4) =
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             dsf[kk] = __builtin_convertvector(x, bf16x8);
         }
     } else {
-        const T* dS1 = (const T*)a.ws_dS + ((bh * NC + ci) * DK + cw + i16) * DV;
+        const T* dS1 = (const T*)a.ws_dS + (((int64_t)bh * NC + ci) * DK + cw + i16) * DV;
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk) dsf[kk] = *reinterpret_cast<const bf16x8*>(dS1 + kk * KS + 8 * j4);
     }
@@ -178,8 +184,12 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     pdo.store_rows(sdO, P);
     if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
     __syncthreads();
+    // The next item's tiles (after the last item: this one's again, unused).  The
+    // requests are unconditional so that a wait for this item's S0 rows, requested
+    // before them, is counted exactly and does not wait for them as well.
     if constexpr (PREFETCH) {
-        if (next_unit < nunits) issue(next_item);
+        const bool more = nxt.unit < nunits;
+        issue(more ? nxt.bh : bh, more ? nxt.ci : ci);
     }
     [[maybe_unused]] const TriOnes<T> tri;
 
@@ -256,8 +266,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     }
     // dA^T = v dO^T tiles, masked, stored as dA[r][s] (10 lower + 2 zero upper tiles)
     for (int ti = w; ti < 12; ti += Cfg::NW) {
-        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+        const int rt = score_tile_rt(ti);
+        const int st = score_tile_st(ti);
         f32x4 acc = zero4();
         if (ti < 10) {
 #pragma unroll
@@ -269,8 +279,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     __syncthreads();
     // A = QA KA^T tiles (all channels, now scaled), masked, stored transposed A^T[s][r]
     for (int ti = w; ti < 12; ti += Cfg::NW) {
-        const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-        const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+        const int rt = score_tile_rt(ti);
+        const int st = score_tile_st(ti);
         f32x4 acc = zero4();
         if (ti < 10) {
 #pragma unroll
@@ -496,15 +506,16 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
                 acc[nt] = M::mma(frag_col<T, P, false>(sdO, 16 * nt, kk * KS), qf[kk], acc[nt]);
 #pragma unroll
         for (int nt = 0; nt < DV / 16; ++nt) *reinterpret_cast<f32x4*>(mrow + 16 * nt + 4 * j4) = acc[nt];
-        if (unit_end && piece == 0 && a.dh0) {
+        if (unit_end && ci == 0 && a.dh0) {
 #pragma unroll
             for (int nt = 0; nt < DV / 16; ++nt)
-                *reinterpret_cast<f32x4*>(a.dh0 + (bh * DK + cw + i16) * DV + 16 * nt + 4 * j4) = acc[nt];
+                *reinterpret_cast<f32x4*>(a.dh0 + ((int64_t)bh * DK + cw + i16) * DV + 16 * nt + 4 * j4) = acc[nt];
         }
     }
     __syncthreads();  // LDS and the chunk data are rewritten by the next item
-    unit = next_unit;
-    item = next_item;
+    if constexpr (!PREFETCH) break;  // vector gate: one item per workgroup
+    unit_start = unit_end;
+    cur = nxt;
     }
 }
 
@@ -516,12 +527,14 @@ template <bool VEC>
 hipError_t launch_grad8(const RevArgs& a, hipStream_t st) {
     const int64_t NC = (a.T + C - 1) / C;
     const int64_t items = a.B * a.H * NC;
+    if (items >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     const int64_t grid = (VEC || items < kGrad8Workers) ? items : kGrad8Workers;
     hipLaunchKernelGGL((k_grad8<VEC, false>), dim3((unsigned)grid), dim3(Grad8Cfg<VEC, false>::NTH), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_grad8_walk(const RevArgs& a, hipStream_t st) {
+    if (a.B * a.H * ((a.T + C - 1) / C) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     const int64_t units = a.B * a.H * a.P;
     const int64_t grid = units < kGrad8Workers ? units : kGrad8Workers;
     hipLaunchKernelGGL((k_grad8<false, true>), dim3((unsigned)grid), dim3(Grad8Cfg<false, true>::NTH), 0, st, a);

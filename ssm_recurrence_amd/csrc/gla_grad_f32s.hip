@@ -180,8 +180,8 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
 
             // dA^T = v dO^T tiles, masked, stored dA[r][s]
             for (int ti = w; ti < 12; ti += 4) {
-                const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-                const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+                const int rt = score_tile_rt(ti);
+                const int st = score_tile_st(ti);
                 const f32x4 acc =
                     mma3_chain<DV / KS>(zero4(), ti < 10 ? DV / KS : 0, [&](int i, SFrag& A, SFrag& B) {
                         A = sld<PW, PLW>(sV, 16 * st, i * KS);
@@ -368,8 +368,8 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_v(const RevArgs a) {
 
         // A = q k^T tiles, masked with the scalar decay, stored transposed A^T[s][r]
         for (int ti = w; ti < 12; ti += 4) {
-            const int rt = ti < 10 ? (ti < 1 ? 0 : ti < 3 ? 1 : ti < 6 ? 2 : 3) : (ti == 10 ? 0 : 2);
-            const int st = ti < 10 ? ti - rt * (rt + 1) / 2 : (ti == 10 ? 1 : 3);
+            const int rt = score_tile_rt(ti);
+            const int st = score_tile_st(ti);
             const f32x4 acc = mma3_chain<DK / KS>(zero4(), ti < 10 ? DK / KS : 0, [&](int i, SFrag& A, SFrag& B) {
                 A = sld<PW, PLW>(sQ, 16 * rt, i * KS);
                 B = sld<PW, PLW>(sK, 16 * st, i * KS);
