@@ -134,6 +134,9 @@ SPLIT = [
     # enough pieces for the state passes' wide blocks (64 key channels x all columns)
     (4096, 128, 128, "vector", torch.bfloat16, 4, 4, [1000, 3096], True, 32),
     (4096, 128, 128, "scalar", torch.float32, 4, 2, [2500, 1596], True, 32),
+    # bf16 scalar gate, more walking pieces (288) than workgroups (256): some
+    # workgroups walk two pieces in turn; heads share q/k
+    (1100, 128, 128, "scalar", torch.bfloat16, 16, 8, [500, 600], True, 12),
 ]
 
 
