@@ -440,8 +440,19 @@ __device__ __forceinline__ void states_any(const PassArgs& a, StatesLdsFor<T, VE
     else states_body<T, VEC, DK, DV, MODE, NB>(a, sm, L);
 }
 
+// Waves per SIMD the register allocation is held to (more resident workgroups,
+// more loads in flight): the largest count that compiles without spills.  Left
+// alone, the compiler parks accumulators in AGPRs, which count against the same
+// per-SIMD file, and the bf16 passes then run at two or three waves per SIMD.
+template <typename T, bool VEC, int NB>
+constexpr int states_waves() {
+    if constexpr (sizeof(T) == 2) return (!VEC || NB == 64) ? 4 : 2;
+    else return (!VEC && NB == 64) ? 3 : 1;
+}
+
 template <typename T, bool VEC, int DK, int DV, int MODE, int NB>
-__global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(states_waves<T, VEC, NB>())))
+void k_states(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) StatesLdsFor<T, VEC, NB> sm;
     const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
     states_any<T, VEC, DK, DV, MODE, NB>(a, sm, xcd_logical_block(n));
@@ -450,7 +461,8 @@ __global__ __launch_bounds__(NT) void k_states(const PassArgs a) {
 // Two independent passes in one launch (the first half of the grid runs MODE_A,
 // the second MODE_B), so that both directions share the device.
 template <typename T, bool VEC, int DK, int DV, int MODE_A, int MODE_B, int NB>
-__global__ __launch_bounds__(NT) void k_states2(const PassArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(states_waves<T, VEC, NB>())))
+void k_states2(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) StatesLdsFor<T, VEC, NB> sm;
     const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
     const int64_t L = xcd_logical_block(2 * n);
