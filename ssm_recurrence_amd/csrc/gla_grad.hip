@@ -559,8 +559,12 @@ hipError_t launch_dg_scalar(const RevArgs& a, int nslices, bool bf16_out, hipStr
 
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_grad(const RevArgs& a, hipStream_t st) {
-    // bf16 heads of 128 x 128: one eight-wave workgroup per chunk (every input loaded once)
-    if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128) return launch_grad8<VEC>(a, st);
+    // bf16 heads of 128 x 128: one eight-wave workgroup per chunk (every input loaded
+    // once); the scalar gate's are walked instead (launch_grad8_walk), never sent here
+    if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128) {
+        if constexpr (VEC) return launch_grad8(a, st);
+        else return hipErrorInvalidValue;
+    }
     // fp32, scalar gate, 128 x 128: fp32 products as three bf16 matrix-core products
     if constexpr (sizeof(T) == 4 && !VEC && DK == 128 && DV == 128) return launch_grad_f32s(a, st);
     using Cfg = GradCfg<T, VEC, DK, DV>;

@@ -1,6 +1,7 @@
-// gla_grad8.hip -- chunk-parallel gradients for bf16 heads with 128 key
-// channels and 128 value columns (gfx950): one workgroup of eight waves per
-// (b, h, chunk).
+// gla_grad8.hip -- gradients for bf16 heads with 128 key channels and 128 value
+// columns (gfx950), one workgroup of eight waves per chunk at a time: the vector
+// gate one workgroup per (b, h, chunk); the scalar gate a reverse walk, one
+// workgroup per (b, h, piece) carrying the state gradient from chunk to chunk.
 //
 // Same per-chunk mathematics as gla_grad.hip (FLAT page, "FLAT: Flash Linear
 // Attention on TPUs", Linear Attention > Backward Recurrence): dq, dk and dg
@@ -16,9 +17,11 @@
 //   phase 2  gate prefix and the q, k scaling for the wave's 16 channels, the
 //            scaled dS1 rows to LDS, dA tiles; then A tiles;
 //   phase 3  dq, dk (and the log-gate gradient) for the wave's 16 key channels,
-//            dv for its 16 value columns.
+//            dv for its 16 value columns;
+//   phase 4  (walk) the state gradient at the previous chunk's end.
 // The scalar gate's log-gate gradient sums over all 128 channels, which are
-// all in this workgroup, so it is finished here too.
+// all in this workgroup, so it is finished here too.  In the walk the state
+// gradient's rows come from LDS instead of HBM and no state gradient is stored.
 #include "gla_bwd.hpp"
 #include "gla_common.hpp"
 #include "gla_kernels.hpp"
@@ -58,7 +61,7 @@ struct Grad8Cfg {
 // gradient is never written per chunk.
 template <bool VEC, bool WALK>
 __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
-    static_assert(!(VEC && WALK), "the walk is built for the scalar gate");
+    static_assert(VEC != WALK, "the walk serves the scalar gate, one item per workgroup the vector gate");
     using T = bf16;
     using Cfg = Grad8Cfg<VEC, WALK>;
     using M = Mma<T>;
@@ -91,10 +94,10 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     const int64_t rs_g = VEC ? a.H * DK : a.H;
     const int64_t G = a.H / a.Hqk;
 
-    // Scalar gate: a persistent loop over (b, h, chunk) items, the next item's tiles
-    // loaded into registers while the current one computes.  Vector gate: one item
-    // per workgroup (the prefetch registers would not fit next to its gate factors).
-    constexpr bool PREFETCH = !VEC;
+    // The walk: a persistent loop, the next chunk's tiles loaded into registers while
+    // the current one computes.  Vector gate: one item per workgroup (the prefetch
+    // registers would not fit next to its gate factors).
+    constexpr bool PREFETCH = WALK;
     TileRegs<T, 128, NTH> pq, pk, pg, pv, pdo;
     RowRegs rr;
     // item indices in 32 bits (the launch checks B * H * NC < 2^31)
@@ -257,11 +260,6 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
         for (int e = 0; e < 4; ++e) {
             em[e] = egm[e] = 1.f;
             dec[e] = ck.decay;
-        }
-        if constexpr (!WALK) {
-#pragma unroll
-            for (int kk = 0; kk < NKV; ++kk)
-                *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = dsf[kk];
         }
     }
     // dA^T = v dO^T tiles, masked, stored as dA[r][s] (10 lower + 2 zero upper tiles)
@@ -519,17 +517,15 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     }
 }
 
-// scalar gate: one resident workgroup per compute unit (the LDS holds one), each
-// looping over items; vector gate: one workgroup per item
+// the walk: one resident workgroup per compute unit (the LDS holds one), each
+// walking pieces in turn; vector gate: one workgroup per item
 constexpr int64_t kGrad8Workers = 256;
 
-template <bool VEC>
 hipError_t launch_grad8(const RevArgs& a, hipStream_t st) {
     const int64_t NC = (a.T + C - 1) / C;
     const int64_t items = a.B * a.H * NC;
     if (items >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    const int64_t grid = (VEC || items < kGrad8Workers) ? items : kGrad8Workers;
-    hipLaunchKernelGGL((k_grad8<VEC, false>), dim3((unsigned)grid), dim3(Grad8Cfg<VEC, false>::NTH), 0, st, a);
+    hipLaunchKernelGGL((k_grad8<true, false>), dim3((unsigned)items), dim3(Grad8Cfg<true, false>::NTH), 0, st, a);
     return hipGetLastError();
 }
 
@@ -541,7 +537,5 @@ hipError_t launch_grad8_walk(const RevArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template hipError_t launch_grad8<false>(const RevArgs&, hipStream_t);
-template hipError_t launch_grad8<true>(const RevArgs&, hipStream_t);
 
 }  // namespace gla

@@ -62,8 +62,7 @@ hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st);
 // scalar gate: dg from the per-slice partial sums (one wave per chunk)
 hipError_t launch_dg_scalar(const RevArgs& a, int nslices, bool bf16_out, hipStream_t st);
 
-// bf16, d_k = d_v = 128: one eight-wave workgroup per chunk (scalar dg finished in-kernel)
-template <bool VEC>
+// bf16, vector gate, d_k = d_v = 128: one eight-wave workgroup per chunk
 hipError_t launch_grad8(const RevArgs& a, hipStream_t st);
 // bf16, scalar gate, d_k = d_v = 128: one workgroup per (b, h, piece) walking its
 // chunks last to first with the state gradient resident (needs only the per-chunk
