@@ -80,7 +80,7 @@ typedef enum {
     GLA_E_NULL = -1,        /* a required pointer is NULL */
     GLA_E_SHAPE = -2,       /* sizes inconsistent or out of range */
     GLA_E_DTYPE = -3,       /* unknown dtype or gate kind */
-    GLA_E_UNSUPPORTED = -4, /* valid, but no kernel for this d_k / d_v / chunk */
+    GLA_E_UNSUPPORTED = -4, /* valid, but no kernel for this d_k / d_v / chunk (convolution: K, C) */
     GLA_E_ALIGN = -5,       /* a pointer is not 16-byte aligned */
     GLA_E_WORKSPACE = -6,   /* workspace missing or smaller than required */
     GLA_E_DEVICE = -7,      /* no HIP device, or the current device is not gfx950 */
@@ -132,6 +132,51 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
             const float* h0, const int32_t* segment_ids, const void* dO, const float* dhT,
             void* dq, void* dk, void* dv, void* dg, float* dh0, void* ws, size_t ws_bytes,
             void* stream);
+
+/* ---- Short depthwise causal convolution (the step before the recurrence)
+ *
+ * FLAT page ("FLAT: Flash Linear Attention on TPUs"), section Depthwise Causal
+ * Short Convolution: per batch row b, time step t and channel c, with K taps
+ * w[k][c] and a bias[c],
+ *
+ *     z_t = bias + sum_{k=0}^{K-1} w_k * x_{t-(K-1-k)}     (x before t = 0 is 0),
+ *     y_t = SiLU(z_t) = z_t * sigmoid(z_t),
+ *
+ * so tap K-1 multiplies the current input.  The backward takes dy = dL/dy and
+ * returns dx = sum_k w_k * dz_{t+(K-1-k)} (dz past the end is 0), dw[k][c] =
+ * sum over all b, t of x_{t-(K-1-k)} * dz_t and db[c] = sum of dz_t, where
+ * dz = dy * SiLU'(z), SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z).  The
+ * convolution has no document resets (the page's has none).
+ *
+ * Layouts (row-major, contiguous): x, y, dy, dx [B, T, C] in the problem's
+ * dtype; w, dw [K, C], bias, db [C] float32.  Sums run in float32; bf16
+ * outputs are rounded to nearest even.  Sizes: B >= 1, T >= 0, K == 4, C a
+ * multiple of 8.  Pointers are device pointers on the current HIP device,
+ * 16-byte aligned; bias and db may be NULL (no bias; bias gradient not
+ * written), and x, y, dy, dx may be NULL when T == 0; all others are required.  ws is a device workspace of at least
+ * gla_conv_workspace_size() bytes (the backward's per-block partial sums of dw
+ * and db, reduced in a fixed order, so results are the same on every run).
+ * Ownership, ordering and errors are as for gla_fwd / gla_bwd above: the caller
+ * owns every buffer, work is enqueued on `stream`, every argument is checked
+ * before anything is launched, outputs are overwritten and must not alias the
+ * inputs. */
+typedef struct {
+    int64_t B, T, C;  /* batch rows, time steps, channels */
+    int32_t K;        /* taps; 4 */
+    int32_t dtype;    /* gla_dtype of x, y, dy, dx */
+} gla_conv_problem;
+
+/* Bytes of device workspace gla_conv_bwd needs (gla_conv_fwd needs none). */
+int gla_conv_workspace_size(const gla_conv_problem* p, size_t* bytes);
+
+/* Forward: y = SiLU(causal depthwise convolution of x with w, plus bias). */
+int gla_conv_fwd(const gla_conv_problem* p, const void* x, const float* w, const float* bias,
+                 void* y, void* stream);
+
+/* Backward: dx, dw (and db if non-NULL) from x, w, bias and dy; recomputes z. */
+int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const float* bias,
+                 const void* dy, void* dx, float* dw, float* db, void* ws, size_t ws_bytes,
+                 void* stream);
 
 /* Static description of a status code. */
 const char* gla_status_str(int status);

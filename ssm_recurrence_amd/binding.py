@@ -30,6 +30,11 @@ class Problem(ctypes.Structure):
                 ("split", ctypes.c_int32)]
 
 
+class ConvProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("C", ctypes.c_int64),
+                ("K", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
 class GlaError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
@@ -58,6 +63,13 @@ def load():
         lib.gla_fwd.restype = ctypes.c_int
         lib.gla_bwd.argtypes = [P] + [vp] * 14 + [sz, vp]
         lib.gla_bwd.restype = ctypes.c_int
+        CP = ctypes.POINTER(ConvProblem)
+        lib.gla_conv_workspace_size.argtypes = [CP, ctypes.POINTER(sz)]
+        lib.gla_conv_workspace_size.restype = ctypes.c_int
+        lib.gla_conv_fwd.argtypes = [CP] + [vp] * 5
+        lib.gla_conv_fwd.restype = ctypes.c_int
+        lib.gla_conv_bwd.argtypes = [CP] + [vp] * 8 + [sz, vp]
+        lib.gla_conv_bwd.restype = ctypes.c_int
         lib.gla_status_str.argtypes = [ctypes.c_int]
         lib.gla_status_str.restype = ctypes.c_char_p
         lib.gla_version.argtypes = []
@@ -203,3 +215,50 @@ def bwd_into(prob, q, k, v, g, h0, seg, dO, dhT, dq, dk, dv, dg, dh0, ws, nws, s
                         stream if stream is not None else _stream())
     if rc:
         raise GlaError(rc, "gla_bwd")
+
+
+# ---- short depthwise causal convolution (gla_conv_* in include/gla.h)
+def conv_problem(x, K=4):
+    B, T, C = x.shape
+    return ConvProblem(B, T, C, K, GLA_BF16 if x.dtype == torch.bfloat16 else GLA_F32)
+
+
+def conv_workspace_size(prob: ConvProblem) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().gla_conv_workspace_size(ctypes.byref(prob), ctypes.byref(n))
+    if rc:
+        raise GlaError(rc, "gla_conv_workspace_size")
+    return n.value
+
+
+def conv_fwd(x, w, bias=None, out=None):
+    """y [B,T,C] (dtype of x) = SiLU(causal depthwise conv of x with w [K,C] fp32, + bias [C] fp32)."""
+    _check(x, "x")
+    _check(w, "w", torch.float32)
+    _check(bias, "bias", torch.float32)
+    prob = conv_problem(x, w.shape[0])
+    y = torch.empty_like(x) if out is None else out
+    rc = load().gla_conv_fwd(ctypes.byref(prob), _p(x), _p(w), _p(bias), _p(y), _stream())
+    if rc:
+        raise GlaError(rc, "gla_conv_fwd")
+    return y
+
+
+def conv_bwd(x, w, bias, dy, ws=None, want_db=True):
+    """(dx [B,T,C], dw [K,C] fp32, db [C] fp32 or None) given dy = dL/dy."""
+    for t, n in ((x, "x"), (dy, "dy")):
+        _check(t, n, x.dtype)
+    _check(w, "w", torch.float32)
+    _check(bias, "bias", torch.float32)
+    prob = conv_problem(x, w.shape[0])
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    db = torch.empty(x.shape[2], dtype=torch.float32, device=x.device) if want_db else None
+    n = conv_workspace_size(prob)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+    rc = load().gla_conv_bwd(ctypes.byref(prob), _p(x), _p(w), _p(bias), _p(dy), _p(dx), _p(dw),
+                             _p(db), _p(ws), ws.numel(), _stream())
+    if rc:
+        raise GlaError(rc, "gla_conv_bwd")
+    return dx, dw, db

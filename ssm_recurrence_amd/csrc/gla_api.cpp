@@ -408,13 +408,84 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     return dispatch<BwdF>(p, pa, ra, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 
+// ---- short depthwise causal convolution
+static int check_conv(const gla_conv_problem* p) {
+    if (!p) return GLA_E_NULL;
+    if (p->dtype != GLA_F32 && p->dtype != GLA_BF16) return GLA_E_DTYPE;
+    if (p->B < 1 || p->T < 0 || p->C < 1) return GLA_E_SHAPE;
+    if (p->K != 4) return GLA_E_UNSUPPORTED;
+    if (p->C % 8 != 0) return GLA_E_UNSUPPORTED;
+    int64_t bt, x;
+    if (!mul_ok(p->B, p->T, &bt) || !mul_ok(bt, p->C, &x) || x > ((int64_t)1 << 40)) return GLA_E_SHAPE;
+    // grid: C / 512 x T / 256 x B workgroups
+    if (p->B > 65535 || (p->T + 255) / 256 > 65535 || (p->C + 511) / 512 > 65535) return GLA_E_SHAPE;
+    return GLA_OK;
+}
+
+static gla::ConvArgs conv_args(const gla_conv_problem* p) {
+    gla::ConvArgs a;
+    memset(&a, 0, sizeof a);
+    a.B = p->B; a.T = p->T; a.C = p->C;
+    return a;
+}
+
+int gla_conv_workspace_size(const gla_conv_problem* p, size_t* bytes) {
+    const int rc = check_conv(p);
+    if (rc) return rc;
+    if (!bytes) return GLA_E_NULL;
+    *bytes = (size_t)gla::conv_partials(p->B, p->T) * (size_t)(p->K + 1) * (size_t)p->C * sizeof(float);
+    return GLA_OK;
+}
+
+int gla_conv_fwd(const gla_conv_problem* p, const void* x, const float* w, const float* bias, void* y,
+                 void* stream) {
+    int rc = check_conv(p);
+    if (rc) return rc;
+    // (an empty row has no activations: their pointers may then be NULL)
+    if (!w || (p->T > 0 && (!x || !y))) return GLA_E_NULL;
+    const void* ptrs[] = {x, w, bias, y};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return GLA_E_ALIGN;
+    rc = check_device();
+    if (rc) return rc;
+    if (p->T == 0) return GLA_OK;
+    gla::ConvArgs a = conv_args(p);
+    a.x = x; a.w = w; a.bias = bias; a.y = y;
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_conv_fwd<gla::bf16>(a, st)
+                                              : gla::launch_conv_fwd<float>(a, st);
+    return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const float* bias,
+                 const void* dy, void* dx, float* dw, float* db, void* ws, size_t ws_bytes,
+                 void* stream) {
+    int rc = check_conv(p);
+    if (rc) return rc;
+    if (!w || !dw || (p->T > 0 && (!x || !dy || !dx))) return GLA_E_NULL;
+    const void* ptrs[] = {x, w, bias, dy, dx, dw, db, ws};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return GLA_E_ALIGN;
+    size_t need = 0;
+    gla_conv_workspace_size(p, &need);
+    if (ws_bytes < need || (need > 0 && !ws)) return GLA_E_WORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    gla::ConvArgs a = conv_args(p);
+    a.x = x; a.w = w; a.bias = bias; a.dy = dy; a.dx = dx; a.dw = dw; a.db = db; a.ws = (float*)ws;
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_conv_bwd<gla::bf16>(a, st)
+                                              : gla::launch_conv_bwd<float>(a, st);
+    return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
 const char* gla_status_str(int s) {
     switch (s) {
         case GLA_OK: return "ok";
         case GLA_E_NULL: return "a required pointer is NULL";
         case GLA_E_SHAPE: return "sizes inconsistent or out of range";
         case GLA_E_DTYPE: return "unknown dtype or gate kind";
-        case GLA_E_UNSUPPORTED: return "no kernel for this d_k / d_v / chunk";
+        case GLA_E_UNSUPPORTED: return "no kernel for this d_k / d_v / chunk (convolution: K / channel count)";
         case GLA_E_ALIGN: return "a pointer is not 16-byte aligned";
         case GLA_E_WORKSPACE: return "workspace missing or too small";
         case GLA_E_DEVICE: return "no HIP device, or the current device is not gfx950";

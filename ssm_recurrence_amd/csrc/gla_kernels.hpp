@@ -85,6 +85,24 @@ hipError_t launch_fwd_f32h(const PassArgs& a, hipStream_t st);
 template <bool VEC>
 hipError_t launch_fwd_h(const PassArgs& a, hipStream_t st);
 
+// short depthwise causal convolution (K = 4 taps, bias, SiLU), gla_conv.hip
+struct ConvArgs {
+    const void* x;                 // [B][T][C], input dtype
+    const float *w, *bias;         // [K][C], [C] (bias may be null)
+    void* y;                       // forward output [B][T][C]
+    const void* dy;                // backward: upstream gradient [B][T][C]
+    void* dx;                      // backward: [B][T][C]
+    float *dw, *db;                // backward: [K][C], [C] (db may be null)
+    float* ws;                     // backward: per-workgroup partials [conv_partials][K+1][C]
+    int64_t B, T, C;
+};
+int64_t conv_partials(int64_t B, int64_t T);
+template <typename T>
+hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st);
+// the convolution backward and the fixed-order reduction of dW, db (T = 0 included)
+template <typename T>
+hipError_t launch_conv_bwd(const ConvArgs& a, hipStream_t st);
+
 template <typename T, int DK>
 hipError_t launch_group_sum(const float* src, void* dst, int64_t B, int64_t Tn, int64_t H,
                             int64_t Hqk, hipStream_t st);

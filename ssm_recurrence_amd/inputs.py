@@ -165,3 +165,39 @@ def small_case(seed=0, *, B=1, T=100, H=2, H_qk=None, d=64, d_v=None, gate="scal
     return make_case("small", B=B, T=T, H=H, H_qk=H_qk, d_k=d, d_v=d_v, gate=gate,
                      dtype=dtype, seed=seed, gate_kind=gk, with_h0=with_h0,
                      with_dhT=with_dhT, lengths=lengths, gate_mult=gate_mult)
+
+
+# ---- the short depthwise causal convolution
+@dataclasses.dataclass
+class ConvCase:
+    name: str
+    dtype: torch.dtype
+    x: torch.Tensor      # [B, T, C], storage dtype
+    w: torch.Tensor      # [K, C] fp32
+    bias: Optional[torch.Tensor]  # [C] fp32
+    dy: torch.Tensor     # [B, T, C], storage dtype
+
+    def to(self, device):
+        return dataclasses.replace(self, x=self.x.to(device), w=self.w.to(device),
+                                   bias=None if self.bias is None else self.bias.to(device),
+                                   dy=self.dy.to(device))
+
+
+def conv_case(name="conv", *, B, T, C, K=4, dtype=torch.bfloat16, seed=0, bias=True):
+    """Seeded inputs for the convolution: a torch.Generator draws, on the CPU in
+    float32 and in this order, x ~ N(0, 1), w ~ U(-1/sqrt(K), 1/sqrt(K)), bias ~ the
+    same uniform, dy ~ N(0, 1) (the bound is PyTorch's default for a depthwise
+    convolution, fan-in K); x and dy are then cast to the storage dtype."""
+    gen = torch.Generator().manual_seed(seed)
+    bound = 1.0 / math.sqrt(K)
+    x = torch.randn(B, T, C, generator=gen)
+    w = (torch.rand(K, C, generator=gen) * 2 - 1) * bound
+    bb = (torch.rand(C, generator=gen) * 2 - 1) * bound if bias else None
+    dy = torch.randn(B, T, C, generator=gen)
+    return ConvCase(name, dtype, x.to(dtype), w, bb, dy.to(dtype))
+
+
+def conv_workload():
+    """The page's convolution benchmark shape: B=8, S=4096, 2048 channels, K=4,
+    bias and SiLU, bf16 activations."""
+    return conv_case("conv", B=8, T=4096, C=2048, K=4, dtype=torch.bfloat16, seed=11)

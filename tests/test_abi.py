@@ -144,3 +144,51 @@ def test_auto_split_only_when_short_of_workgroups(lib):
 def test_valid_call_without_gpu_reports_device_error(lib):
     """No silent fallback: with no usable device a valid call returns GLA_E_DEVICE."""
     assert call_fwd(lib, prob(H_qk=4, d_v=128)) == -7
+
+
+# ---- the short depthwise causal convolution (gla_conv_*): host-side validation
+def conv_prob(**kw):
+    d = dict(B=2, T=100, C=64, K=4, dtype=1)
+    d.update(kw)
+    return gb.ConvProblem(d["B"], d["T"], d["C"], d["K"], d["dtype"])
+
+
+def call_conv_fwd(lib, p, ptrs=None):
+    q = dict(x=FAKE, w=FAKE, bias=None, y=FAKE)
+    q.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_conv_fwd(None if p is None else ctypes.byref(p), c(q["x"]), c(q["w"]),
+                            c(q["bias"]), c(q["y"]), None)
+
+
+def call_conv_bwd(lib, p, ptrs=None, ws_bytes=0):
+    names = ["x", "w", "bias", "dy", "dx", "dw", "db", "ws"]
+    q = {n: FAKE for n in names}
+    q.update(bias=None, db=None, ws=None)
+    q.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_conv_bwd(ctypes.byref(p), *[c(q[n]) for n in names], ws_bytes, None)
+
+
+def test_conv_argument_errors(lib):
+    assert call_conv_fwd(lib, None) == -1
+    assert call_conv_fwd(lib, conv_prob(), {"x": None}) == -1
+    assert call_conv_bwd(lib, conv_prob(), {"dw": None}) == -1
+    assert call_conv_fwd(lib, conv_prob(B=0)) == -2
+    assert call_conv_fwd(lib, conv_prob(T=-1)) == -2
+    assert call_conv_fwd(lib, conv_prob(K=3)) == -4
+    assert call_conv_fwd(lib, conv_prob(C=12)) == -4
+    assert call_conv_fwd(lib, conv_prob(dtype=5)) == -3
+    assert call_conv_fwd(lib, conv_prob(), {"y": FAKE + 4}) == -5
+    assert call_conv_bwd(lib, conv_prob(), {"db": FAKE + 8}) == -5
+
+
+def test_conv_workspace(lib):
+    p = conv_prob(B=3, T=1000, C=64)
+    n = ctypes.c_size_t()
+    assert lib.gla_conv_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    # one partial [K + 1][C] fp32 per (batch row, 256 time steps)
+    assert n.value == 3 * 4 * 5 * 64 * 4
+    assert call_conv_bwd(lib, p, {"ws": None}, ws_bytes=n.value) == -6
+    assert call_conv_bwd(lib, p, {"ws": FAKE}, ws_bytes=n.value - 1) == -6
+    assert lib.gla_conv_workspace_size(ctypes.byref(p), None) == -1
