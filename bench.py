@@ -1,6 +1,7 @@
 """Benchmark: chunked gated linear attention forward + backward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+python bench.py --workload conv   (the short depthwise causal convolution)
 
 A step is one gla_fwd followed by one gla_bwd (the whole hot path) over one
 batch of seeded synthetic inputs already resident in device memory.  The
@@ -28,7 +29,8 @@ PROFILE = {"c2": "gla_kernels_ssd_fp32_B4_T8192_H8_Hqk2_d128.md",
            "c3": "gla_kernels_gla_bf16_B4_T4096_H16_d128.md",
            "c4": "gla_kernels_ssd_bf16_packed_B1_T65536_H16_d128.md",
            "c5a": "gla_kernels_gla_bf16_B1_T16384_H16_d128.md",
-           "c5b": "gla_kernels_gla_bf16_B8_T2048_H16_d128.md"}
+           "c5b": "gla_kernels_gla_bf16_B8_T2048_H16_d128.md",
+           "conv": "conv_kernels_bf16_B8_T4096_C2048_K4.md"}
 
 
 def source_hash():
@@ -42,21 +44,22 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per gla_bwd call from the committed rocprofv3 counter summary,
-    or None when there is none or the kernels changed since it was taken."""
+def measured_traffic(workload, key="traffic_bytes_per_gla_bwd"):
+    """HBM bytes per backward call (gla_bwd, or gla_conv_bwd: `key`) from the
+    committed rocprofv3 counter summary, or None when there is none or the
+    kernels changed since it was taken."""
     name = PROFILE.get(workload)
     path = os.path.join(ROOT, "profiles", name) if name else None
     if not path or not os.path.exists(path):
         return None
     vals = {}
     for line in open(path):
-        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_gla_bwd", "source_hash"):
+        if ":" in line and line.split(":")[0] in (key, "source_hash"):
             k, v = line.split(":", 1)
             vals[k] = v.strip()
-    if vals.get("source_hash") != source_hash() or "traffic_bytes_per_gla_bwd" not in vals:
+    if vals.get("source_hash") != source_hash() or key not in vals:
         return None
-    return float(vals["traffic_bytes_per_gla_bwd"])
+    return float(vals[key])
 
 
 PEAK = {"hbm": 8000.0,            # GB/s
@@ -111,6 +114,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "conv":
+        conv_main(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     case_cpu = workload(args.workload)
@@ -228,6 +234,99 @@ def main():
         "config": {"workload": "%s: %s" % (args.workload, WORKLOADS[args.workload]),
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
                    "chunk": case.chunk, "split": args.split, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def conv_main(args):
+    """The short depthwise causal convolution (K = 4, bias, SiLU) at the page's
+    benchmark shape: one gla_conv_fwd and one gla_conv_bwd per step."""
+    import torch
+    from ssm_recurrence_amd import binding as gb
+    from ssm_recurrence_amd.inputs import conv_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case_cpu = conv_workload()
+    c = case_cpu.to(dev)
+    B, T, C = c.x.shape
+    K = c.w.shape[0]
+    prob = gb.conv_problem(c.x, K)
+    y, dx = torch.empty_like(c.x), torch.empty_like(c.x)
+    dw, db = torch.empty_like(c.w), torch.empty(C, dtype=torch.float32, device=dev)
+    n = gb.conv_workspace_size(prob)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = gb.ctypes.c_void_p(stream.cuda_stream)
+    lib = gb.load()
+    P = gb.ctypes.byref(prob)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = lib.gla_conv_fwd(P, gb._p(c.x), gb._p(c.w), gb._p(c.bias), gb._p(y), sp)
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= lib.gla_conv_bwd(P, gb._p(c.x), gb._p(c.w), gb._p(c.bias), gb._p(c.dy), gb._p(dx),
+                               gb._p(dw), gb._p(db), gb._p(ws), ws.numel(), sp)
+        if ev is not None:
+            ev[2].record(stream)
+        if rc:
+            raise RuntimeError("gla_conv_* failed: %d" % rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    fwd_us = 1000.0 * sum(fwd_ms) / len(fwd_ms)
+    bwd_us = 1000.0 * sum(bwd_ms) / len(bwd_ms)
+    # algorithmic bytes: forward reads x, writes y; backward reads x, dy, writes dx
+    # (taps, bias and their gradients are C * (2K + 2) * 4 bytes, included)
+    es = c.x.element_size()
+    par = C * (2 * K + 2) * 4
+    fwd_bytes = 2 * B * T * C * es + par
+    bwd_bytes = 3 * B * T * C * es + par
+    achieved = bwd_bytes / (bwd_us * 1e-6) / 1e9
+    traffic = measured_traffic("conv", "traffic_bytes_per_gla_conv_bwd")
+    roof = {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK["hbm"], "unit": "GB/s",
+            "frac": round(achieved / PEAK["hbm"], 4),
+            "traffic": None if traffic is None else round(traffic / 1e6, 1),
+            "traffic_unit": "MB per gla_conv_bwd call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes": round(bwd_bytes / 1e6, 1),
+            "kernel": "gla_conv_bwd (its two kernels, one call)",
+            "step_frac": round((fwd_bytes + bwd_bytes) / ((fwd_us + bwd_us) * 1e-6) / 1e9 / PEAK["hbm"], 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.conv as oc
+        s = case_cpu
+        c0 = time.perf_counter()
+        oc.conv_fwd(s.x, s.w, s.bias)
+        oc.conv_bwd(s.x, s.w, s.bias, s.dy)
+        c1 = time.perf_counter()
+        cpu = {"value": round(B * T / (c1 - c0), 1), "unit": "tokens/s", "cores": 1,
+               "kind": "oracle",
+               "sample": "the whole workload (%d rows x %d steps x %d channels), fwd+bwd in numpy "
+                         "fp64 on one thread, %.1f s" % (B, T, C, c1 - c0)}
+    out = {
+        "metric": "fwd+bwd µs and tokens/s for the short depthwise causal convolution (K=4, bias, SiLU), % of HBM roofline",
+        "value": round(B * T / (ms_per_step / 1000.0), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "us_fwd": round(fwd_us, 1), "us_bwd": round(bwd_us, 1), "us_fwd_bwd": round(fwd_us + bwd_us, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "conv: depthwise causal conv K=4 + bias + SiLU, bf16, B=8 T=4096 C=2048",
+                   "global_batch": B, "seq_len": T, "channels": C, "taps": K,
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
