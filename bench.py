@@ -2,6 +2,8 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
 python bench.py --workload conv   (the short depthwise causal convolution)
+python bench.py --workload c3 --fused   (q, k, v read in place from one projection
+                                          tensor, one fused gradient written)
 
 A step is one gla_fwd followed by one gla_bwd (the whole hot path) over one
 batch of seeded synthetic inputs already resident in device memory.  The
@@ -30,6 +32,7 @@ PROFILE = {"c2": "gla_kernels_ssd_fp32_B4_T8192_H8_Hqk2_d128.md",
            "c4": "gla_kernels_ssd_bf16_packed_B1_T65536_H16_d128.md",
            "c5a": "gla_kernels_gla_bf16_B1_T16384_H16_d128.md",
            "c5b": "gla_kernels_gla_bf16_B8_T2048_H16_d128.md",
+           "c3f": "gla_kernels_gla_bf16_fused_B4_T4096_H16_d128.md",
            "conv": "conv_kernels_bf16_B8_T4096_C2048_K4.md"}
 
 
@@ -99,6 +102,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=3,
                     help="extra untimed-region steps after a 512 MB cache flush (median reported)")
+    ap.add_argument("--fused", action="store_true",
+                    help="q, k, v as views of one [B, T, 2*H_qk*d_k + H*d_v] projection tensor, "
+                         "dq, dk, dv written into one fused gradient of that shape")
     ap.add_argument("--split", type=int, default=0,
                     help="sequence pieces per (b, h); 0 = the library's own choice")
     args = ap.parse_args()
@@ -127,6 +133,18 @@ def main():
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     dq, dk_, dv_, dg = (torch.empty_like(case.q), torch.empty_like(case.k),
                         torch.empty_like(case.v), torch.empty_like(case.g))
+    if args.fused:
+        # the projection output X = q | k | v and one gradient buffer of its shape
+        W = 2 * case.H_qk * dk + H * dv
+        X = torch.empty((B, T, W), dtype=case.dtype, device=dev)
+        dX = torch.empty_like(X)
+        views = gb.fused_views(X, case.H_qk, dk, H, dv)
+        for view, src in zip(views, (case.q, case.k, case.v)):
+            view.copy_(src)
+        packed = dict(q=case.q, k=case.k, v=case.v, dq=dq, dk=dk_, dv=dv_)
+        case.q, case.k, case.v = views
+        dq, dk_, dv_ = gb.fused_views(dX, case.H_qk, dk, H, dv)
+        prob.ld_qk = prob.ld_v = prob.ld_dqk = prob.ld_dv = W
     dh0 = torch.empty_like(case.h0) if case.h0 is not None else None
     nf, nb = gb.workspace_size(prob, False), gb.workspace_size(prob, True)
     wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev)
@@ -178,6 +196,24 @@ def main():
     tokens = B * T
     value = tokens / (ms_per_step / 1000.0)
 
+    # what the packed layout would add around each step: q, k, v split out of the
+    # projection, and dq | dk | dv concatenated into its gradient (timed apart)
+    copies_us = None
+    if args.fused:
+        def copies():
+            packed["q"].copy_(case.q)
+            packed["k"].copy_(case.k)
+            packed["v"].copy_(case.v)
+            torch.cat([packed[n].flatten(2) for n in ("dq", "dk", "dv")], dim=2, out=dX)
+        copies()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            copies()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        copies_us = 1000.0 * ev[0].elapsed_time(ev[1]) / args.steps
+
     alg = algorithmic(case)
     bf16 = case.dtype == torch.bfloat16
     if bf16:
@@ -188,7 +224,7 @@ def main():
         bound, peak, unit = "mfma", PEAK["mfma_f32"], "TFLOP/s"
         achieved = alg["bwd_flops"] / (bwd_us * 1e-6) / 1e12
         step_ach = (alg["fwd_flops"] + alg["bwd_flops"]) / ((fwd_us + bwd_us) * 1e-6) / 1e12
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload + ("f" if args.fused else ""))
     roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": None if traffic is None else round(traffic / 1e6, 1),
@@ -233,10 +269,14 @@ def main():
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic (seeded)",
         "config": {"workload": "%s: %s" % (args.workload, WORKLOADS[args.workload]),
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
-                   "chunk": case.chunk, "split": args.split, "parallelism": "single GPU"},
+                   "chunk": case.chunk, "split": args.split, "parallelism": "single GPU",
+                   "layout": ("q, k, v read from one [B, T, %d] projection tensor; one fused "
+                              "gradient" % W) if args.fused else "packed q, k, v"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if args.fused:
+        out["us_layout_copies_avoided"] = round(copies_us, 1)
     print(json.dumps(out))
 
 

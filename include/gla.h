@@ -33,7 +33,9 @@
  * q/k head h / (H / H_qk)) and dq, dk are summed over those heads (FLAT page,
  * Pallas Kernels > Gated Linear Attention, the paragraph on head sharing).
  *
- * Layouts: all tensors are row-major and contiguous.
+ * Layouts: all tensors are row-major; q, k, v, dq, dk, dv may have token rows
+ * further apart than packed (see the row strides below), every other tensor is
+ * contiguous.
  *     q, k, dq, dk           [B, T, H_qk, d_k]   dtype
  *     v, o, dO, dv           [B, T, H, d_v]      dtype
  *     g, dg  scalar gate     [B, T, H]           dtype
@@ -56,7 +58,9 @@
  * state between calls.  Work is enqueued on `stream` (a hipStream_t; NULL is
  * the default stream) and the call returns before it completes.  Inputs are
  * read only.  Outputs are fully overwritten (never accumulated into) and must
- * not alias inputs, each other or the workspace.  Two calls that share a
+ * not overlap inputs, each other or the workspace (dq, dk and dv may interleave
+ * in one buffer, as in the fused layout below; elements outside them are not
+ * touched).  Two calls that share a
  * workspace must be ordered on one stream.
  *
  * Errors: every argument is checked on the host before anything is launched;
@@ -98,7 +102,25 @@ typedef struct {
     int32_t dtype;  /* gla_dtype */
     int32_t split;  /* sequence pieces per (b, h): 0 = chosen from the sizes; >= 1 forces
                        that many (fewer if the row has fewer chunks); see below */
+    /* Row strides: elements from token (b, t) to token (b, t + 1) (and from the
+     * last token of row b to the first of row b + 1) of q and k (ld_qk), v
+     * (ld_v), dq and dk (ld_dqk) and dv (ld_dv); 0 = packed (H_qk * d_k, or
+     * H * d_v).  Head h of token (b, t) of q starts at q + (b * T + t) * ld_qk
+     * + h * d_k.  A non-zero stride is at least the packed one and a multiple of
+     * 16 bytes.  o, dO, g and dg are always packed. */
+    int64_t ld_qk, ld_v, ld_dqk, ld_dv;
 } gla_problem;
+
+/* Fused projection.  The FLAT page ("FLAT: Flash Linear Attention on TPUs",
+ * sections Gated Linear Attention (the data-movement paragraph) and Full Linear
+ * Attention Layer) has the kernels read q, k and v straight out of the one
+ * projection output and write one fused gradient, so that no layout copies,
+ * splits or concatenations run around them.  With the projection output X of
+ * shape [B, T, W], W = 2 * H_qk * d_k + H * d_v, holding q | k | v along its
+ * last axis, pass q = X, k = X + H_qk * d_k, v = X + 2 * H_qk * d_k and
+ * ld_qk = ld_v = W; with a gradient buffer dX of the same shape, pass dq = dX,
+ * dk = dX + H_qk * d_k, dv = dX + 2 * H_qk * d_k and ld_dqk = ld_dv = W, and
+ * gla_bwd fills dX completely. */
 
 /* Sequence split.  The time axis of every (b, h) can be cut into pieces of
  * whole chunks that run in parallel: a piece maps the state entering it to the

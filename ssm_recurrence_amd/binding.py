@@ -27,7 +27,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("H_qk", ctypes.c_int64), ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64),
                 ("chunk", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("split", ctypes.c_int32)]
+                ("split", ctypes.c_int32), ("ld_qk", ctypes.c_int64), ("ld_v", ctypes.c_int64),
+                ("ld_dqk", ctypes.c_int64), ("ld_dv", ctypes.c_int64)]
 
 
 class ConvProblem(ctypes.Structure):
@@ -85,11 +86,14 @@ def header_functions():
     return sorted(set(re.findall(r"\b(gla_[a-z_0-9]+)\s*\(", txt)))
 
 
-def make_problem(B, T, H, H_qk, d_k, d_v, gate="scalar", dtype=torch.bfloat16, chunk=64, split=0):
-    """gla_problem; split = sequence pieces per (b, h), 0 = chosen by the library."""
+def make_problem(B, T, H, H_qk, d_k, d_v, gate="scalar", dtype=torch.bfloat16, chunk=64, split=0,
+                 ld_qk=0, ld_v=0, ld_dqk=0, ld_dv=0):
+    """gla_problem; split = sequence pieces per (b, h), 0 = chosen by the library;
+    ld_* = row strides of q/k, v, dq/dk, dv in elements (0 = packed)."""
     return Problem(B, T, H, H_qk, d_k, d_v, chunk,
                    GLA_GATE_VECTOR if gate == "vector" else GLA_GATE_SCALAR,
-                   GLA_BF16 if dtype == torch.bfloat16 else GLA_F32, split)
+                   GLA_BF16 if dtype == torch.bfloat16 else GLA_F32, split,
+                   ld_qk, ld_v, ld_dqk, ld_dv)
 
 
 def workspace_size(prob: Problem, backward: bool) -> int:
@@ -108,24 +112,43 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _check(t, name, dtype=None):
+def _check(t, name, dtype=None, strided=False):
     if t is None:
         return
     if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
-    if not t.is_contiguous():
+    if not strided and not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
-def problem_of(q, v, g, gate, chunk=64, split=0):
+def row_stride(t, name):
+    """Elements between consecutive tokens of a [B, T, heads, d] tensor whose heads
+    of one token are packed (0 when the whole tensor is packed); raises for any
+    other layout."""
+    if t.is_contiguous():
+        return 0
+    B, T, nh, d = t.shape
+    s0, s1, s2, s3 = t.stride()
+    ld = s1 if T > 1 else s0
+    ok = (s3 == 1 or d == 1) and (s2 == d or nh == 1) and (T == 1 or s1 == ld) and (B == 1 or s0 == T * ld)
+    if not ok or ld < nh * d:
+        raise ValueError("%s: token rows must hold packed heads, rows ld elements apart "
+                         "(strides %s)" % (name, t.stride()))
+    return ld
+
+
+def problem_of(q, v, g, gate, chunk=64, split=0, k=None):
     B, T, H_qk, d_k = q.shape
     H, d_v = v.shape[2], v.shape[3]
     want = (B, T, H, d_k) if gate == "vector" else (B, T, H)
     if tuple(g.shape) != want:
         raise ValueError("g has shape %s, expected %s" % (tuple(g.shape), want))
-    return make_problem(B, T, H, H_qk, d_k, d_v, gate, q.dtype, chunk, split)
+    ld_qk, ld_v = row_stride(q, "q"), row_stride(v, "v")
+    if k is not None and row_stride(k, "k") != ld_qk:
+        raise ValueError("q and k must have the same row stride")
+    return make_problem(B, T, H, H_qk, d_k, d_v, gate, q.dtype, chunk, split, ld_qk, ld_v)
 
 
 def _workspace(prob, backward, device, ws):
@@ -140,11 +163,12 @@ def _workspace(prob, backward, device, ws):
 def fwd(q, k, v, g, h0=None, segment_ids=None, *, gate="scalar", chunk=64, want_hT=True,
         out=None, ws=None, split=0):
     """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g")):
-        _check(t, n, q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, strided=True)
+    _check(g, "g", q.dtype)
     _check(h0, "h0", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = problem_of(q, v, g, gate, chunk, split)
+    prob = problem_of(q, v, g, gate, chunk, split, k)
     B, T, H, d_v, d_k = prob.B, prob.T, prob.H, prob.d_v, prob.d_k
     o = out if out is not None else torch.empty((B, T, H, d_v), dtype=q.dtype, device=q.device)
     hT = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device) if want_hT else None
@@ -156,18 +180,67 @@ def fwd(q, k, v, g, h0=None, segment_ids=None, *, gate="scalar", chunk=64, want_
     return o, hT
 
 
+def fused_views(X, H_qk, d_k, H, d_v):
+    """q [B,T,H_qk,d_k], k, v [B,T,H,d_v] as views of a fused projection X of shape
+    [B, T, 2*H_qk*d_k + H*d_v] holding q | k | v along its last axis."""
+    B, T, W = X.shape
+    wq = H_qk * d_k
+    if W != 2 * wq + H * d_v:
+        raise ValueError("fused width %d, expected %d" % (W, 2 * wq + H * d_v))
+    return (X[..., :wq].unflatten(-1, (H_qk, d_k)), X[..., wq:2 * wq].unflatten(-1, (H_qk, d_k)),
+            X[..., 2 * wq:].unflatten(-1, (H, d_v)))
+
+
+def _fused_base(q, k, v):
+    """(B, T, W) when q, k, v are the three views fused_views makes of one tensor."""
+    B, T, H_qk, d_k = q.shape
+    H, d_v = v.shape[2], v.shape[3]
+    wq, W, es = H_qk * d_k, 2 * H_qk * d_k + H * d_v, q.element_size()
+    if T == 0 or q.untyped_storage().data_ptr() != v.untyped_storage().data_ptr():
+        return None
+    try:
+        lds = (row_stride(q, "q"), row_stride(k, "k"), row_stride(v, "v"))
+    except ValueError:
+        return None
+    if lds != (W, W, W) or k.data_ptr() != q.data_ptr() + wq * es or v.data_ptr() != q.data_ptr() + 2 * wq * es:
+        return None
+    return B, T, W
+
+
 def bwd(q, k, v, g, dO, h0=None, segment_ids=None, dhT=None, *, gate="scalar", chunk=64,
-        want_dh0=True, ws=None, split=0):
-    """dq, dk [B,T,H_qk,d_k], dv [B,T,H,d_v], dg (shape of g), dh0 fp32 (or None)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (dO, "dO")):
+        want_dh0=True, ws=None, split=0, grads=None):
+    """dq, dk [B,T,H_qk,d_k], dv [B,T,H,d_v], dg (shape of g), dh0 fp32 (or None).
+
+    grads = (dq, dk, dv) writes the gradients into those tensors (token rows may
+    be strided, as q, k, v may be).  Otherwise, when q, k, v are the views
+    fused_views makes of one projection tensor, dq, dk, dv are returned as the
+    same views of one fused gradient tensor (fused_grad() of the result gives
+    it); else they are packed."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, strided=True)
+    for t, n in ((g, "g"), (dO, "dO")):
         _check(t, n, q.dtype)
     _check(h0, "h0", torch.float32)
     _check(dhT, "dhT", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = problem_of(q, v, g, gate, chunk, split)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    prob = problem_of(q, v, g, gate, chunk, split, k)
+    if grads is not None:
+        dq, dk, dv = grads
+        for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+            _check(t, n, q.dtype, strided=True)
+            if t.shape != ref.shape:
+                raise ValueError("%s has shape %s, expected %s" % (n, tuple(t.shape), tuple(ref.shape)))
+        prob.ld_dqk, prob.ld_dv = row_stride(dq, "dq"), row_stride(dv, "dv")
+        if row_stride(dk, "dk") != prob.ld_dqk:
+            raise ValueError("dq and dk must have the same row stride")
+    elif _fused_base(q, k, v) is not None:
+        dX = torch.empty(_fused_base(q, k, v), dtype=q.dtype, device=q.device)
+        dq, dk, dv = fused_views(dX, prob.H_qk, prob.d_k, prob.H, prob.d_v)
+        prob.ld_dqk = prob.ld_dv = dX.shape[2]
+    else:
+        dq = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        dk = torch.empty(k.shape, dtype=q.dtype, device=q.device)
+        dv = torch.empty(v.shape, dtype=q.dtype, device=q.device)
     dg = torch.empty_like(g)
     dh0 = (torch.empty((prob.B, prob.H, prob.d_k, prob.d_v), dtype=torch.float32, device=q.device)
            if want_dh0 else None)
@@ -178,6 +251,14 @@ def bwd(q, k, v, g, dO, h0=None, segment_ids=None, dhT=None, *, gate="scalar", c
     if rc:
         raise GlaError(rc, "gla_bwd")
     return dq, dk, dv, dg, dh0
+
+
+def fused_grad(dq):
+    """The fused gradient tensor [B, T, W] whose first view is dq (as bwd returns it
+    for fused inputs)."""
+    B, T = dq.shape[:2]
+    ld = row_stride(dq, "dq")
+    return dq.as_strided((B, T, ld), (T * ld, ld, 1), dq.storage_offset())
 
 
 class GLAFunction(torch.autograd.Function):
@@ -193,11 +274,41 @@ class GLAFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dO, dhT):
         q, k, v, g, h0, seg = ctx.saved_tensors
-        dO = dO.contiguous() if dO is not None else torch.zeros_like(v)
+        dO = dO.contiguous() if dO is not None else torch.zeros(v.shape, dtype=v.dtype, device=v.device)
         dhT = dhT.contiguous().float() if dhT is not None else None
         dq, dk, dv, dg, dh0 = bwd(q, k, v, g, dO, h0, seg, dhT, gate=ctx.gate,
                                   want_dh0=h0 is not None)
         return dq, dk, dv, dg, dh0, None, None
+
+
+class GLAFusedFunction(torch.autograd.Function):
+    """Autograd wrapper over a fused projection X [B, T, 2*H_qk*d_k + H*d_v]
+    (q | k | v): the kernels read q, k, v in place and the backward writes one
+    fused gradient dX; no split, copy or concatenation runs around them."""
+
+    @staticmethod
+    def forward(ctx, X, g, h0, segment_ids, H_qk, d_k, gate):
+        H = g.shape[2]
+        d_v = (X.shape[2] - 2 * H_qk * d_k) // H
+        q, k, v = fused_views(X, H_qk, d_k, H, d_v)
+        o, hT = fwd(q, k, v, g, h0, segment_ids, gate=gate)
+        ctx.save_for_backward(X, g, h0, segment_ids)
+        ctx.shape = (H_qk, d_k, H, d_v)
+        ctx.gate = gate
+        return o, hT
+
+    @staticmethod
+    def backward(ctx, dO, dhT):
+        X, g, h0, seg = ctx.saved_tensors
+        H_qk, d_k, H, d_v = ctx.shape
+        q, k, v = fused_views(X, H_qk, d_k, H, d_v)
+        dO = dO.contiguous() if dO is not None else torch.zeros(v.shape, dtype=v.dtype, device=v.device)
+        dhT = dhT.contiguous().float() if dhT is not None else None
+        dX = torch.empty_like(X)
+        dq, dk, dv = fused_views(dX, H_qk, d_k, H, d_v)
+        _, _, _, dg, dh0 = bwd(q, k, v, g, dO, h0, seg, dhT, gate=ctx.gate,
+                               want_dh0=h0 is not None, grads=(dq, dk, dv))
+        return dX, dg, dh0, None, None, None, None
 
 
 def fwd_into(prob, q, k, v, g, h0, seg, o, hT, ws, nws, stream=None):

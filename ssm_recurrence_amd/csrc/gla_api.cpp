@@ -42,8 +42,20 @@ int check_problem(const gla_problem* p) {
     const int64_t nc = (p->T + 63) / 64;
     // launch grids reach B * H * chunks * 8 workgroups (forward, 16-column slices, split)
     if (p->B * p->H * (nc > 0 ? nc : 1) > (((int64_t)1 << 31) - 1) / 8) return GLA_E_SHAPE;
+    // row strides: 0 (packed), or at least the packed width, whole 16-byte units,
+    // and every element offset within range
+    const int64_t per16 = p->dtype == GLA_BF16 ? 8 : 4;
+    const int64_t lds[4][2] = {{p->ld_qk, p->H_qk * p->d_k}, {p->ld_v, p->H * p->d_v},
+                               {p->ld_dqk, p->H_qk * p->d_k}, {p->ld_dv, p->H * p->d_v}};
+    for (const auto& l : lds) {
+        if (l[0] == 0) continue;
+        if (l[0] < l[1] || l[0] % per16 != 0) return GLA_E_SHAPE;
+        if (!mul_ok(bt, l[0], &x) || x > ((int64_t)1 << 40)) return GLA_E_SHAPE;
+    }
     return GLA_OK;
 }
+
+int64_t ld_or_packed(int64_t ld, int64_t packed) { return ld ? ld : packed; }
 
 // Sequence pieces per (b, h) and chunks per piece.  The sequential passes need
 // enough workgroups to occupy the device.  Forward: one per compute unit (256)
@@ -280,9 +292,9 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
     }
     if (e != hipSuccess) return e;
     if (ra.ws_dq) {
-        e = gla::launch_group_sum<T, DK>(ra.ws_dq, ra.dq, ra.B, ra.T, ra.H, ra.Hqk, st);
+        e = gla::launch_group_sum<T, DK>(ra.ws_dq, ra.dq, ra.ld_dqk, ra.B, ra.T, ra.H, ra.Hqk, st);
         if (e != hipSuccess) return e;
-        e = gla::launch_group_sum<T, DK>(ra.ws_dk, ra.dk, ra.B, ra.T, ra.H, ra.Hqk, st);
+        e = gla::launch_group_sum<T, DK>(ra.ws_dk, ra.dk, ra.ld_dqk, ra.B, ra.T, ra.H, ra.Hqk, st);
     }
     return e;
 }
@@ -345,6 +357,8 @@ int gla_fwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     memset(&a, 0, sizeof a);
     a.q = q; a.k = k; a.v = v; a.g = g; a.h0 = h0; a.seg = segment_ids; a.o = o; a.hT = hT;
     a.B = p->B; a.T = p->T; a.H = p->H; a.Hqk = p->H_qk;
+    a.ld_qk = ld_or_packed(p->ld_qk, p->H_qk * p->d_k);
+    a.ld_v = ld_or_packed(p->ld_v, p->H * p->d_v);
     a.P = L.sp.P; a.PL = L.sp.PL;
     if (a.P > 1) {
         char* w = (char*)ws;
@@ -380,6 +394,8 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     pa.ws_S = (float*)(w + L.S);
     pa.ws_dS = walk_bwd(p) ? nullptr : w + L.dS;
     pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.Hqk = p->H_qk;
+    pa.ld_qk = ld_or_packed(p->ld_qk, p->H_qk * p->d_k);
+    pa.ld_v = ld_or_packed(p->ld_v, p->H * p->d_v);
     pa.P = L.sp.P; pa.PL = L.sp.PL;
     if (pa.P > 1) {
         pa.L_out[0] = (float*)(w + L.pL0);
@@ -404,6 +420,10 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
         ra.ws_bnd = (float*)(w + L.bnd);
     }
     ra.B = p->B; ra.T = p->T; ra.H = p->H; ra.Hqk = p->H_qk;
+    ra.ld_qk = pa.ld_qk;
+    ra.ld_v = pa.ld_v;
+    ra.ld_dqk = ld_or_packed(p->ld_dqk, p->H_qk * p->d_k);
+    ra.ld_dv = ld_or_packed(p->ld_dv, p->H * p->d_v);
     ra.P = pa.P; ra.PL = pa.PL; ra.dS_in = pa.dS_in;
     return dispatch<BwdF>(p, pa, ra, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
@@ -494,6 +514,6 @@ const char* gla_status_str(int s) {
     }
 }
 
-int gla_version(void) { return 100; }
+int gla_version(void) { return 200; }
 
 }  // extern "C"

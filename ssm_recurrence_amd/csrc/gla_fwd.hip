@@ -79,7 +79,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
     const T* k = (const T*)a.k;
     const T* v = (const T*)a.v;
     const T* g = (const T*)a.g;
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_v = a.ld_v;
     const int64_t rs_g = VEC ? a.H * DK : a.H;
     const T* qbase = q + b * T_ * rs_qk + hq * DK;
     const T* kbase = k + b * T_ * rs_qk + hq * DK;

@@ -68,12 +68,12 @@ __global__ __launch_bounds__(512) void k_fwd_f32h(const PassArgs a) {
     const int64_t cbeg = piece * a.PL;
     const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
 
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_v = a.ld_v, rs_o = a.H * DV;
     const float* qbase = (const float*)a.q + b * T_ * rs_qk + hq * DK;
     const float* kbase = (const float*)a.k + b * T_ * rs_qk + hq * DK;
     const float* vbase = (const float*)a.v + b * T_ * rs_v + h * DV;
     const float* gbase = (const float*)a.g + b * T_ * a.H + h;
-    float* obase = (float*)a.o + b * T_ * rs_v + h * DV + 16 * w + 4 * j4;
+    float* obase = (float*)a.o + b * T_ * rs_o + h * DV + 16 * w + 4 * j4;
 
     // state tiles ct = 0..7 of column tile w: lane holds S[16ct + 4j4 + e][16w + i16]
     f32x4 S[DK / 16];
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(512) void k_fwd_f32h(const PassArgs a) {
                     f32x4 out;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = O[e] + fr * R[rt][e];
-                    *reinterpret_cast<f32x4*>(obase + (t0 + r) * rs_v) = out;
+                    *reinterpret_cast<f32x4*>(obase + (t0 + r) * rs_o) = out;
                 }
             }
         }

@@ -74,13 +74,13 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
     const int64_t cbeg = piece * a.PL;
     const int64_t cend = (cbeg + a.PL < NC) ? cbeg + a.PL : NC;
 
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_v = a.ld_v, rs_o = a.H * DV;
     const int64_t rs_g = VEC ? a.H * DK : a.H;
     const bf16* qbase = (const bf16*)a.q + b * T_ * rs_qk + hq * DK;
     const bf16* kbase = (const bf16*)a.k + b * T_ * rs_qk + hq * DK;
     const bf16* vbase = (const bf16*)a.v + b * T_ * rs_v + h * DV;
     const bf16* gbase = (const bf16*)a.g + b * T_ * rs_g + (VEC ? h * DK : h);
-    bf16* obase = (bf16*)a.o + b * T_ * rs_v + h * DV;
+    bf16* obase = (bf16*)a.o + b * T_ * rs_o + h * DV;
     // a chunk's output is assembled in LDS and written out at the next chunk's start
     // with 16-byte stores of whole rows (each wave holds 16 columns of every row)
     auto write_out = [&](int64_t t0, int nvalid) {
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
             const int idx = threadIdx.x + i * NTH;
             const int row = idx / TR::VPR, cv = (idx % TR::VPR) * TR::VE;
             if (row < nvalid)
-                *reinterpret_cast<i32x4*>(obase + (t0 + row) * rs_v + cv) =
+                *reinterpret_cast<i32x4*>(obase + (t0 + row) * rs_o + cv) =
                     *reinterpret_cast<const i32x4*>(sm.sO + row * PO + cv);
         }
     };

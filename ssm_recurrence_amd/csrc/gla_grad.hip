@@ -113,12 +113,12 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     const int64_t NC = (T_ + C - 1) / C;
     const int64_t t0 = ci * C;
     const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_v = a.ld_v, rs_do = a.H * DV;
     const int64_t rs_g = VEC ? a.H * DK : a.H;
     const T* qrow = (const T*)a.q + (b * T_ + t0) * rs_qk + hq * DK + cs0;
     const T* krow = (const T*)a.k + (b * T_ + t0) * rs_qk + hq * DK + cs0;
     const T* vrow = (const T*)a.v + (b * T_ + t0) * rs_v + h * DV;
-    const T* dorow = (const T*)a.dO + (b * T_ + t0) * rs_v + h * DV;
+    const T* dorow = (const T*)a.dO + (b * T_ + t0) * rs_do + h * DV;
     const T* grow = (const T*)a.g + (b * T_ + t0) * rs_g + (VEC ? h * DK + cs0 : h);
     // rows cw + i of S0 and dS1, the A operands of dO S0^T and v dS1^T (k = n)
     const T* S0 = (const T*)a.ws_S + ((bh * (NC + 1) + ci) * DK + cw + i16) * DV;
@@ -132,7 +132,7 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     pk.load(krow, rs_qk, nvalid);
     if constexpr (VEC) pg.load(grow, rs_g, nvalid);
     pv.load(vrow, rs_v, nvalid);
-    pdo.load(dorow, rs_v, nvalid);
+    pdo.load(dorow, rs_do, nvalid);
     if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
     typename M::frag s0f[NKV], dsf[NKV];
 #pragma unroll
@@ -244,7 +244,7 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
             x[rt][e] = qraw[rt].get(e) * dq[e];
         }
         if (r < nvalid) {
-            if (!gqa) store4<T>((T*)a.dq + ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4, dq);
+            if (!gqa) store4<T>((T*)a.dq + (b * T_ + t0 + r) * a.ld_dqk + hq * DK + cw + 4 * j4, dq);
             else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
         }
     }
@@ -274,7 +274,7 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
             bsum[e] += kr * inter * rE;
         }
         if (s < nvalid) {
-            if (!gqa) store4<T>((T*)a.dk + ((b * T_ + t0 + s) * a.Hqk + hq) * DK + cw + 4 * j4, dk);
+            if (!gqa) store4<T>((T*)a.dk + (b * T_ + t0 + s) * a.ld_dqk + hq * DK + cw + 4 * j4, dk);
             else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
         }
     }
@@ -393,11 +393,11 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
     const int64_t NC = (T_ + C - 1) / C;
     const int64_t t0 = ci * C;
     const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_do = a.H * DV;
     const int64_t rs_g = VEC ? a.H * DK : a.H;
     const T* qrow = (const T*)a.q + (b * T_ + t0) * rs_qk + hq * DK;
     const T* krow = (const T*)a.k + (b * T_ + t0) * rs_qk + hq * DK;
-    const T* dorow = (const T*)a.dO + (b * T_ + t0) * rs_v + h * DV + n0s;
+    const T* dorow = (const T*)a.dO + (b * T_ + t0) * rs_do + h * DV + n0s;
     const T* grow = (const T*)a.g + (b * T_ + t0) * rs_g + (VEC ? h * DK : h);
     const T* dS1 = (const T*)a.ws_dS + (bh * NC + ci) * DK * DV + n0s;  // [c][n0s ..]
 
@@ -408,7 +408,7 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
     pq.load(qrow, rs_qk, nvalid);
     pk.load(krow, rs_qk, nvalid);
     if constexpr (VEC) pg.load(grow, rs_g, nvalid);
-    pdo.load(dorow, rs_v, nvalid);
+    pdo.load(dorow, rs_do, nvalid);
 #pragma unroll
     for (int u = 0; u < DK / 64; ++u) pds[u].load(dS1 + (int64_t)u * 64 * DV, DV, 64);
     if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
@@ -478,7 +478,7 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
     __syncthreads();
 
     // ---- dv^T = dO^T A + [last doc] dS1'^T KA^T (rows n, columns s)
-    T* dvo = (T*)a.dv + ((b * T_ + t0) * a.H + h) * DV + n0s + 16 * w + 4 * j4;
+    T* dvo = (T*)a.dv + (b * T_ + t0) * a.ld_dv + h * DV + n0s + 16 * w + 4 * j4;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
         f32x4 a1 = zero4(), a2 = zero4();
@@ -494,7 +494,7 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
         float dv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) dv[e] = a1[e] + fu * a2[e];
-        if (s < nvalid) store4<T>(dvo + (int64_t)s * a.H * DV, dv);
+        if (s < nvalid) store4<T>(dvo + (int64_t)s * a.ld_dv, dv);
     }
 }
 

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     const int64_t nitems = a.B * a.H * NC;
     const int w = wave_id(), l = lane_id(), j4 = l >> 4, i16 = l & 15;
     const int cw = 16 * w;  // the wave's key channels (dq, dk, dg) and value columns (dv)
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_v = a.ld_v, rs_do = a.H * DV;
     const int64_t rs_g = VEC ? a.H * DK : a.H;
     const int64_t G = a.H / a.Hqk;
 
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
         const T* grow = (const T*)a.g + (b * T_ + t0) * rs_g + (VEC ? h * DK : h);
         if constexpr (VEC) pg.load(grow, rs_g, nvalid);
         pv.load((const T*)a.v + (b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
-        pdo.load((const T*)a.dO + (b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
+        pdo.load((const T*)a.dO + (b * T_ + t0) * rs_do + h * DV, rs_do, nvalid);
         if (w == 0) rr.load(grow, rs_g, a.seg, b, T_, t0, nvalid, !VEC);
     };
     // Work order.  Units are items (b, h, chunk), or for the walk pieces (b, h, piece),
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             x[rt][e] = qraw[rt].get(e) * dq[e];
         }
         if (r < nvalid) {
-            if (!gqa) store4<T>((T*)a.dq + ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4, dq);
+            if (!gqa) store4<T>((T*)a.dq + (b * T_ + t0 + r) * a.ld_dqk + hq * DK + cw + 4 * j4, dq);
             else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
         }
     }
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             bsum[e] += kr * inter * rE;
         }
         if (s < nvalid) {
-            if (!gqa) store4<T>((T*)a.dk + ((b * T_ + t0 + s) * a.Hqk + hq) * DK + cw + 4 * j4, dk);
+            if (!gqa) store4<T>((T*)a.dk + (b * T_ + t0 + s) * a.ld_dqk + hq * DK + cw + 4 * j4, dk);
             else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
         }
     }
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
 
     // ---- phase 3b: dv^T = dO^T A + [last doc] dS1'^T KA^T for value columns cw .. cw + 15
     {
-        T* dvo = (T*)a.dv + ((b * T_ + t0) * a.H + h) * DV + cw + 4 * j4;
+        T* dvo = (T*)a.dv + (b * T_ + t0) * a.ld_dv + h * DV + cw + 4 * j4;
         // dS1'^T rows (value columns cw + i16), k = key channel
         bf16x8 dsc[DK / KS];
 #pragma unroll
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             float dv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) dv[e] = a1[e] + fu * a2[e];
-            if (s < nvalid) store4<T>(dvo + (int64_t)s * a.H * DV, dv);
+            if (s < nvalid) store4<T>(dvo + (int64_t)s * a.ld_dv, dv);
         }
     }
 

@@ -93,7 +93,7 @@ __device__ __forceinline__ void qk_load_qk(const RevArgs& a, const QKItem& it, T
                                            TileRegs<float, 64>& pk) {
     const int64_t T_ = a.T, t0 = it.ci * C;
     const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
-    const int64_t rs_qk = a.Hqk * DK;
+    const int64_t rs_qk = a.ld_qk;
     const int64_t off = (it.b * T_ + t0) * rs_qk + it.hq * DK + it.slice * 64;
     pq.load((const float*)a.q + off, rs_qk, nvalid);
     pk.load((const float*)a.k + off, rs_qk, nvalid);
@@ -104,10 +104,10 @@ __device__ __forceinline__ void qk_load_head(const RevArgs& a, const QKItem& it,
     const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
     const int64_t G = a.H / a.Hqk;
     const int64_t h = it.hq * G + gi;
-    const int64_t rs_v = a.H * DV;
+    const int64_t rs_v = a.ld_v, rs_do = a.H * DV;
     const int w = wave_id();
     R.pv.load((const float*)a.v + (it.b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
-    R.pdo.load((const float*)a.dO + (it.b * T_ + t0) * rs_v + h * DV, rs_v, nvalid);
+    R.pdo.load((const float*)a.dO + (it.b * T_ + t0) * rs_do + h * DV, rs_do, nvalid);
     if (w == 0) R.rr.load((const float*)a.g + (it.b * T_ + t0) * a.H + h, a.H, a.seg, it.b, T_, t0, nvalid, true);
 }
 
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_qk(const RevArgs a) {
         for (int rt = 0; rt < 4; ++rt) {
             const int r = 16 * rt + i16;
             if (r < nvalid) {
-                const int64_t o = ((b * T_ + t0 + r) * a.Hqk + hq) * DK + cw + 4 * j4;
+                const int64_t o = (b * T_ + t0 + r) * a.ld_dqk + hq * DK + cw + 4 * j4;
                 store4<float>((float*)a.dq + o, dqs[rt]);
                 store4<float>((float*)a.dk + o, dks[rt]);
             }
@@ -322,12 +322,12 @@ __device__ __forceinline__ void v_load(const RevArgs& a, const VItem& it, VRegs&
     const int64_t T_ = a.T, t0 = it.ci * C;
     const int64_t NC = (T_ + C - 1) / C;
     const int nvalid = (T_ - t0) < C ? (int)(T_ - t0) : C;
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_do = a.H * DV;
     const int64_t bh = it.b * a.H + it.h;
     const int n0s = it.slice * 64;
     R.pq.load((const float*)a.q + (it.b * T_ + t0) * rs_qk + it.hq * DK, rs_qk, nvalid);
     R.pk.load((const float*)a.k + (it.b * T_ + t0) * rs_qk + it.hq * DK, rs_qk, nvalid);
-    R.pdo.load((const float*)a.dO + (it.b * T_ + t0) * rs_v + it.h * DV + n0s, rs_v, nvalid);
+    R.pdo.load((const float*)a.dO + (it.b * T_ + t0) * rs_do + it.h * DV + n0s, rs_do, nvalid);
     const float* dS1 = (const float*)a.ws_dS + (bh * NC + it.ci) * DK * DV + n0s;
     R.pds0.load(dS1, DV, 64);
     R.pds1.load(dS1 + (int64_t)64 * DV, DV, 64);
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_v(const RevArgs a) {
         __syncthreads();
 
         // dv^T = dO^T A + [last doc] exp(Gamma - beta_s) dS1^T k^T (rows n, columns s)
-        float* dvo = (float*)a.dv + ((it.b * T_ + t0) * a.H + it.h) * DV + it.slice * 64 + 16 * w + 4 * j4;
+        float* dvo = (float*)a.dv + (it.b * T_ + t0) * a.ld_dv + it.h * DV + it.slice * 64 + 16 * w + 4 * j4;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int kb = 16 * st / KS;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(NT) void k_grad_f32s_v(const RevArgs a) {
             float dv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) dv[e] = a1[e] + fu * a2[e];
-            if (s < nvalid) store4<float>(dvo + (int64_t)s * a.H * DV, dv);
+            if (s < nvalid) store4<float>(dvo + (int64_t)s * a.ld_dv, dv);
         }
         __syncthreads();  // LDS is restaged for the next item
     }

@@ -15,6 +15,8 @@ struct PassArgs {
     float* ws_S;   // state pass output, [B*H][NC+1][DK][DV] in the input dtype
     void* ws_dS;   // state-gradient pass output, [B*H][NC][DK][DV] in the input dtype
     int64_t B, T, H, Hqk;
+    // elements between consecutive tokens of q and k, and of v (o, dO are packed)
+    int64_t ld_qk, ld_v;
     // exact sequence split: P pieces of PL chunks each (P = 1: no split)
     int64_t P, PL;
     const float* S_in;    // [B*H][P][DK][DV]: state entering each piece (P > 1)
@@ -34,6 +36,9 @@ struct RevArgs {
     float *ws_dq, *ws_dk;  // per-head fp32 [B][T][H][DK] when heads share q/k
     float *ws_xs, *ws_bnd; // scalar gate: per-slice partial sums [B*H][slices][T], [B*H][slices][NC]
     int64_t B, T, H, Hqk;
+    // elements between consecutive tokens: q and k, v (inputs); dq and dk, dv
+    // (outputs); dO and the per-head fp32 dq, dk are packed
+    int64_t ld_qk, ld_v, ld_dqk, ld_dv;
     // the split of the reverse walk (launch_grad8_walk): P pieces of PL chunks
     int64_t P, PL;
     const float* dS_in;    // [B*H][P][DK][DV]: state gradient at each piece's end (P > 1)
@@ -104,7 +109,7 @@ template <typename T>
 hipError_t launch_conv_bwd(const ConvArgs& a, hipStream_t st);
 
 template <typename T, int DK>
-hipError_t launch_group_sum(const float* src, void* dst, int64_t B, int64_t Tn, int64_t H,
-                            int64_t Hqk, hipStream_t st);
+hipError_t launch_group_sum(const float* src, void* dst, int64_t ld_dst, int64_t B, int64_t Tn,
+                            int64_t H, int64_t Hqk, hipStream_t st);
 
 }  // namespace gla

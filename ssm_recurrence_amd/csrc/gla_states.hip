@@ -93,7 +93,7 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
     const T* k = (const T*)(REV ? a.q : a.k);
     const T* v = (const T*)(REV ? a.dO : a.v);
     const T* g = (const T*)a.g;
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_v = REV ? a.H * DV : a.ld_v;
     const int64_t rs_g = VEC ? a.H * DK : a.H;
     const T* kbase = k + b * T_ * rs_qk + hq * DK + c0;
     const T* vbase = v + b * T_ * rs_v + h * DV + n0;
@@ -295,7 +295,7 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
 
     const T* k = (const T*)(REV ? a.q : a.k);
     const T* v = (const T*)(REV ? a.dO : a.v);
-    const int64_t rs_qk = a.Hqk * DK, rs_v = a.H * DV;
+    const int64_t rs_qk = a.ld_qk, rs_v = REV ? a.H * DV : a.ld_v;
     const T* kbase = k + b * T_ * rs_qk + hq * DK + c0;
     const T* vbase = v + b * T_ * rs_v + h * DV + n0;
     const T* gbase = (const T*)a.g + b * T_ * a.H + h;

@@ -140,6 +140,51 @@ def test_auto_split_only_when_short_of_workgroups(lib):
     assert _ws(lib, small_bh, True) > _ws(lib, one, True)
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(ld_qk=255), -2),                          # below the packed width (2 x 128)
+    (dict(ld_qk=260), -2),                          # not whole 16-byte units in bf16
+    (dict(ld_v=100), -2), (dict(ld_dqk=-8), -2), (dict(ld_dv=1 << 40), -2),
+    (dict(ld_qk=264, ld_v=264, ld_dqk=264, ld_dv=264), -7),   # valid (no device here)
+    (dict(ld_qk=260, dtype=torch.float32), -7),     # 16-byte units of fp32
+    (dict(ld_qk=258, dtype=torch.float32), -2),
+])
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_row_stride_checks(lib, kw, code):
+    """Row strides of q/k, v, dq/dk, dv: 0 (packed) or at least the packed width in
+    whole 16-byte units; valid ones get past the stride checks (to the device
+    check, or the backward's missing workspace)."""
+    assert call_fwd(lib, prob(**kw)) == code
+    assert call_bwd(lib, prob(**kw)) == (-6 if code == -7 else code)
+
+
+def test_row_strides_leave_workspace_unchanged(lib):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.gla_workspace_size(ctypes.byref(prob()), 1, ctypes.byref(a)) == 0
+    assert lib.gla_workspace_size(ctypes.byref(prob(ld_qk=1024, ld_v=1024, ld_dqk=512, ld_dv=4096)), 1,
+                                  ctypes.byref(b)) == 0
+    assert a.value == b.value
+
+
+def test_binding_row_stride_and_fused_views():
+    """Host logic of the binding: row strides read from tensor strides, the fused
+    projection's views, and the fused gradient recovered from dq (CPU tensors)."""
+    B, T, H_qk, d_k, H, d_v = 2, 5, 2, 64, 4, 32
+    W = 2 * H_qk * d_k + H * d_v
+    X = torch.arange(B * T * W, dtype=torch.float32).reshape(B, T, W)
+    q, k, v = gb.fused_views(X, H_qk, d_k, H, d_v)
+    assert q.shape == (B, T, H_qk, d_k) and v.shape == (B, T, H, d_v)
+    assert [gb.row_stride(t, "t") for t in (q, k, v)] == [W, W, W]
+    assert gb.row_stride(X[..., :W].reshape(B, T, 8, W // 8), "x") == 0
+    assert torch.equal(q[1, 3, 1], X[1, 3, d_k:2 * d_k]) and torch.equal(v[0, 4, 3], X[0, 4, -d_v:])
+    assert gb._fused_base(q, k, v) == (B, T, W)
+    assert gb._fused_base(q.contiguous(), k, v) is None
+    assert gb.fused_grad(q).data_ptr() == X.data_ptr() and gb.fused_grad(q).shape == X.shape
+    with pytest.raises(ValueError):
+        gb.row_stride(torch.zeros(B, H, T, d_k).transpose(1, 2), "q")   # heads not packed in a row
+    with pytest.raises(ValueError):
+        gb.fused_views(X[..., 1:], H_qk, d_k, H, d_v)
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
 def test_valid_call_without_gpu_reports_device_error(lib):
     """No silent fallback: with no usable device a valid call returns GLA_E_DEVICE."""
