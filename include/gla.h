@@ -84,7 +84,7 @@ typedef enum {
     GLA_E_NULL = -1,        /* a required pointer is NULL */
     GLA_E_SHAPE = -2,       /* sizes inconsistent or out of range */
     GLA_E_DTYPE = -3,       /* unknown dtype or gate kind */
-    GLA_E_UNSUPPORTED = -4, /* valid, but no kernel for this d_k / d_v / chunk (convolution: K, C) */
+    GLA_E_UNSUPPORTED = -4, /* valid, but no kernel for this d_k / d_v / chunk (convolution: K, C; norm: d) */
     GLA_E_ALIGN = -5,       /* a pointer is not 16-byte aligned */
     GLA_E_WORKSPACE = -6,   /* workspace missing or smaller than required */
     GLA_E_DEVICE = -7,      /* no HIP device, or the current device is not gfx950 */
@@ -199,6 +199,49 @@ int gla_conv_fwd(const gla_conv_problem* p, const void* x, const float* w, const
 int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const float* bias,
                  const void* dy, void* dx, float* dw, float* db, void* ws, size_t ws_bytes,
                  void* stream);
+
+/* ---- Output norm and gate (the step after the recurrence)
+ *
+ * FLAT page ("FLAT: Flash Linear Attention on TPUs"), section Full Linear
+ * Attention Layer: the layer output is the per-head RMSNorm of the recurrence
+ * output o multiplied by a swish output gate.  Per row (b, t, h) of d channels,
+ * with the gate's pre-activation z and one scale vector gamma[d] for every head:
+ *
+ *     r = 1 / sqrt(mean_j o_j^2 + eps),   n = o * r,
+ *     y = gamma * n * swish(z),           swish(z) = z * sigmoid(z).
+ *
+ * The backward takes dy = dL/dy and returns
+ *     dz     = dy * gamma * n * swish'(z),    swish'(z) = s (1 + z (1 - s)), s = sigmoid(z),
+ *     do     = r * (dn - n * mean_j(dn_j n_j)),  dn = dy * gamma * swish(z),
+ *     dgamma = sum over all rows of dy * n * swish(z).
+ *
+ * Layouts (row-major, contiguous): o, z, y, dy, do, dz [B, T, H, d] in the
+ * problem's dtype; gamma, dgamma [d] float32.  Sums run in float32; bf16 outputs
+ * are rounded to nearest even.  Sizes: B >= 1, T >= 0, H >= 1, d in {64, 128},
+ * eps finite and >= 0 (a row of zeros with eps = 0 gives NaN, as the formula
+ * does).  Pointers are device pointers on the current HIP device, 16-byte
+ * aligned; the activation pointers may be NULL when T == 0, the others are
+ * required.  ws is a device workspace of at least gla_norm_gate_workspace_size()
+ * bytes (per-block partial sums of dgamma, reduced in a fixed order: results are
+ * the same on every run).  Ownership, ordering and errors are as for gla_fwd /
+ * gla_bwd above. */
+typedef struct {
+    int64_t B, T, H, d;  /* batch rows, time steps, heads, channels per head */
+    float eps;           /* added to the mean square */
+    int32_t dtype;       /* gla_dtype of o, z, y, dy, do, dz */
+} gla_norm_gate_problem;
+
+/* Bytes of device workspace gla_norm_gate_bwd needs (the forward needs none). */
+int gla_norm_gate_workspace_size(const gla_norm_gate_problem* p, size_t* bytes);
+
+/* Forward: y = gamma * RMSNorm(o) * swish(z), per head. */
+int gla_norm_gate_fwd(const gla_norm_gate_problem* p, const void* o, const void* z,
+                      const float* gamma, void* y, void* stream);
+
+/* Backward: d_o, dz and dgamma from o, z, gamma and dy; recomputes the norm. */
+int gla_norm_gate_bwd(const gla_norm_gate_problem* p, const void* o, const void* z,
+                      const float* gamma, const void* dy, void* d_o, void* dz, float* dgamma,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* gla_status_str(int status);

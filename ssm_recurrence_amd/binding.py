@@ -36,6 +36,11 @@ class ConvProblem(ctypes.Structure):
                 ("K", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class NormGateProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
 class GlaError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
@@ -71,6 +76,13 @@ def load():
         lib.gla_conv_fwd.restype = ctypes.c_int
         lib.gla_conv_bwd.argtypes = [CP] + [vp] * 8 + [sz, vp]
         lib.gla_conv_bwd.restype = ctypes.c_int
+        NP = ctypes.POINTER(NormGateProblem)
+        lib.gla_norm_gate_workspace_size.argtypes = [NP, ctypes.POINTER(sz)]
+        lib.gla_norm_gate_workspace_size.restype = ctypes.c_int
+        lib.gla_norm_gate_fwd.argtypes = [NP] + [vp] * 5
+        lib.gla_norm_gate_fwd.restype = ctypes.c_int
+        lib.gla_norm_gate_bwd.argtypes = [NP] + [vp] * 8 + [sz, vp]
+        lib.gla_norm_gate_bwd.restype = ctypes.c_int
         lib.gla_status_str.argtypes = [ctypes.c_int]
         lib.gla_status_str.restype = ctypes.c_char_p
         lib.gla_version.argtypes = []
@@ -373,3 +385,68 @@ def conv_bwd(x, w, bias, dy, ws=None, want_db=True):
     if rc:
         raise GlaError(rc, "gla_conv_bwd")
     return dx, dw, db
+
+
+# ---- output norm and gate (gla_norm_gate_* in include/gla.h)
+def norm_gate_problem(o, eps=1e-5):
+    B, T, H, d = o.shape
+    return NormGateProblem(B, T, H, d, eps, GLA_BF16 if o.dtype == torch.bfloat16 else GLA_F32)
+
+
+def norm_gate_workspace_size(prob: NormGateProblem) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().gla_norm_gate_workspace_size(ctypes.byref(prob), ctypes.byref(n))
+    if rc:
+        raise GlaError(rc, "gla_norm_gate_workspace_size")
+    return n.value
+
+
+def norm_gate_fwd(o, z, gamma, eps=1e-5, out=None):
+    """y [B,T,H,d] (dtype of o) = gamma * RMSNorm(o) per head * swish(z)."""
+    _check(o, "o")
+    _check(z, "z", o.dtype)
+    _check(gamma, "gamma", torch.float32)
+    if z.shape != o.shape or gamma.shape != (o.shape[3],):
+        raise ValueError("z must be shaped like o and gamma [d]")
+    prob = norm_gate_problem(o, eps)
+    y = torch.empty_like(o) if out is None else out
+    rc = load().gla_norm_gate_fwd(ctypes.byref(prob), _p(o), _p(z), _p(gamma), _p(y), _stream())
+    if rc:
+        raise GlaError(rc, "gla_norm_gate_fwd")
+    return y
+
+
+def norm_gate_bwd(o, z, gamma, dy, eps=1e-5, ws=None):
+    """(do, dz [B,T,H,d], dgamma [d] fp32) given dy = dL/dy."""
+    for t, n in ((o, "o"), (z, "z"), (dy, "dy")):
+        _check(t, n, o.dtype)
+    _check(gamma, "gamma", torch.float32)
+    if z.shape != o.shape or dy.shape != o.shape or gamma.shape != (o.shape[3],):
+        raise ValueError("z and dy must be shaped like o and gamma [d]")
+    prob = norm_gate_problem(o, eps)
+    d_o, dz = torch.empty_like(o), torch.empty_like(o)
+    dgamma = torch.empty_like(gamma)
+    n = norm_gate_workspace_size(prob)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=o.device)
+    rc = load().gla_norm_gate_bwd(ctypes.byref(prob), _p(o), _p(z), _p(gamma), _p(dy), _p(d_o), _p(dz),
+                                  _p(dgamma), _p(ws), ws.numel(), _stream())
+    if rc:
+        raise GlaError(rc, "gla_norm_gate_bwd")
+    return d_o, dz, dgamma
+
+
+class NormGateFunction(torch.autograd.Function):
+    """Autograd wrapper: y = gamma * RMSNorm(o) * swish(z), both passes in the HIP library."""
+
+    @staticmethod
+    def forward(ctx, o, z, gamma, eps):
+        ctx.save_for_backward(o, z, gamma)
+        ctx.eps = eps
+        return norm_gate_fwd(o, z, gamma, eps)
+
+    @staticmethod
+    def backward(ctx, dy):
+        o, z, gamma = ctx.saved_tensors
+        d_o, dz, dgamma = norm_gate_bwd(o, z, gamma, dy.contiguous(), ctx.eps)
+        return d_o, dz, dgamma, None

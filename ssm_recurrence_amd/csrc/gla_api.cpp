@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/gla.h"
 #include "gla_common.hpp"
@@ -325,6 +326,31 @@ template <typename T, bool VEC, int DK, int DV> struct BwdF {
     }
 };
 
+// output norm and gate: checks and the dispatch over (dtype, d)
+int check_norm(const gla_norm_gate_problem* p) {
+    if (!p) return GLA_E_NULL;
+    if (p->dtype != GLA_F32 && p->dtype != GLA_BF16) return GLA_E_DTYPE;
+    if (p->B < 1 || p->T < 0 || p->H < 1 || p->d < 1) return GLA_E_SHAPE;
+    if (!(p->eps >= 0.f) || !(p->eps < 3.0e38f)) return GLA_E_SHAPE;  // (rejects NaN and inf)
+    if (p->d != 64 && p->d != 128) return GLA_E_UNSUPPORTED;
+    int64_t bt, rows, x;
+    if (!mul_ok(p->B, p->T, &bt) || !mul_ok(bt, p->H, &rows) || !mul_ok(rows, p->d, &x) ||
+        x > ((int64_t)1 << 40))
+        return GLA_E_SHAPE;
+    return GLA_OK;
+}
+
+int64_t norm_rows(const gla_norm_gate_problem* p) { return p->B * p->T * p->H; }
+
+template <typename F>
+hipError_t norm_dispatch(const gla_norm_gate_problem* p, F&& f) {
+    if (p->dtype == GLA_BF16)
+        return p->d == 64 ? f(gla::bf16(), std::integral_constant<int, 64>())
+                          : f(gla::bf16(), std::integral_constant<int, 128>());
+    return p->d == 64 ? f(float(), std::integral_constant<int, 64>())
+                      : f(float(), std::integral_constant<int, 128>());
+}
+
 }  // namespace
 
 extern "C" {
@@ -496,6 +522,65 @@ int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const
     hipStream_t st = (hipStream_t)stream;
     const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_conv_bwd<gla::bf16>(a, st)
                                               : gla::launch_conv_bwd<float>(a, st);
+    return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+// ---- output norm and gate
+int gla_norm_gate_workspace_size(const gla_norm_gate_problem* p, size_t* bytes) {
+    const int rc = check_norm(p);
+    if (rc) return rc;
+    if (!bytes) return GLA_E_NULL;
+    int64_t np = 0;
+    norm_dispatch(p, [&](auto t, auto d) {
+        np = gla::norm_gate_partials<decltype(t), decltype(d)::value>(norm_rows(p));
+        return hipSuccess;
+    });
+    *bytes = (size_t)np * (size_t)p->d * sizeof(float);
+    return GLA_OK;
+}
+
+int gla_norm_gate_fwd(const gla_norm_gate_problem* p, const void* o, const void* z, const float* gamma,
+                      void* y, void* stream) {
+    int rc = check_norm(p);
+    if (rc) return rc;
+    if (!gamma || (p->T > 0 && (!o || !z || !y))) return GLA_E_NULL;
+    const void* ptrs[] = {o, z, gamma, y};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return GLA_E_ALIGN;
+    rc = check_device();
+    if (rc) return rc;
+    gla::NormArgs a;
+    memset(&a, 0, sizeof a);
+    a.o = o; a.z = z; a.gamma = gamma; a.y = y; a.rows = norm_rows(p); a.eps = p->eps;
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e = norm_dispatch(p, [&](auto t, auto d) {
+        return gla::launch_norm_gate_fwd<decltype(t), decltype(d)::value>(a, st);
+    });
+    return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+int gla_norm_gate_bwd(const gla_norm_gate_problem* p, const void* o, const void* z, const float* gamma,
+                      const void* dy, void* d_o, void* dz, float* dgamma, void* ws, size_t ws_bytes,
+                      void* stream) {
+    int rc = check_norm(p);
+    if (rc) return rc;
+    if (!gamma || !dgamma || (p->T > 0 && (!o || !z || !dy || !d_o || !dz))) return GLA_E_NULL;
+    const void* ptrs[] = {o, z, gamma, dy, d_o, dz, dgamma, ws};
+    for (const void* q : ptrs)
+        if (q && !aligned(q)) return GLA_E_ALIGN;
+    size_t need = 0;
+    gla_norm_gate_workspace_size(p, &need);
+    if (ws_bytes < need || (need > 0 && !ws)) return GLA_E_WORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    gla::NormArgs a;
+    memset(&a, 0, sizeof a);
+    a.o = o; a.z = z; a.gamma = gamma; a.dy = dy; a.d_o = d_o; a.dz = dz; a.dgamma = dgamma;
+    a.ws = (float*)ws; a.rows = norm_rows(p); a.eps = p->eps;
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e = norm_dispatch(p, [&](auto t, auto d) {
+        return gla::launch_norm_gate_bwd<decltype(t), decltype(d)::value>(a, st);
+    });
     return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 

@@ -108,6 +108,22 @@ hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st);
 template <typename T>
 hipError_t launch_conv_bwd(const ConvArgs& a, hipStream_t st);
 
+// output norm and gate (per-head RMSNorm times a swish gate), gla_norm.hip
+struct NormArgs {
+    const void *o, *z, *dy;  // [rows][D], input dtype (dy: backward)
+    const float* gamma;      // [D]
+    void* y;                 // forward output [rows][D]
+    void *d_o, *dz;          // backward outputs [rows][D]
+    float* dgamma;           // backward output [D]
+    float* ws;               // backward: per-workgroup dgamma partials [norm_gate_partials][D]
+    int64_t rows;
+    float eps;
+};
+template <typename T, int D> int64_t norm_gate_partials(int64_t rows);
+template <typename T, int D> hipError_t launch_norm_gate_fwd(const NormArgs& a, hipStream_t st);
+// the backward and the fixed-order reduction of dgamma (rows = 0 included)
+template <typename T, int D> hipError_t launch_norm_gate_bwd(const NormArgs& a, hipStream_t st);
+
 template <typename T, int DK>
 hipError_t launch_group_sum(const float* src, void* dst, int64_t ld_dst, int64_t B, int64_t Tn,
                             int64_t H, int64_t Hqk, hipStream_t st);

@@ -201,3 +201,34 @@ def conv_workload():
     """The page's convolution benchmark shape: B=8, S=4096, 2048 channels, K=4,
     bias and SiLU, bf16 activations."""
     return conv_case("conv", B=8, T=4096, C=2048, K=4, dtype=torch.bfloat16, seed=11)
+
+
+# ---- the output norm and gate
+@dataclasses.dataclass
+class NormGateCase:
+    name: str
+    dtype: torch.dtype
+    o: torch.Tensor               # [B, T, H, d] recurrence output
+    z: torch.Tensor               # [B, T, H, d] gate pre-activation
+    gamma: torch.Tensor           # [d] fp32
+    dy: torch.Tensor              # [B, T, H, d]
+    eps: float = 1e-5
+
+    def to(self, device):
+        return dataclasses.replace(self, o=self.o.to(device), z=self.z.to(device),
+                                   gamma=self.gamma.to(device), dy=self.dy.to(device))
+
+
+def norm_gate_case(name="norm_gate", *, B, T, H, d=128, dtype=torch.bfloat16, seed=0, eps=1e-5):
+    """o, z, dy ~ N(0, 1), gamma ~ U(0.5, 1.5); bf16 values are rounded once, when drawn."""
+    gen = torch.Generator().manual_seed(seed)
+    o = torch.randn((B, T, H, d), generator=gen).to(dtype)
+    z = torch.randn((B, T, H, d), generator=gen).to(dtype)
+    gamma = torch.rand(d, generator=gen) + 0.5
+    dy = torch.randn((B, T, H, d), generator=gen).to(dtype)
+    return NormGateCase(name, dtype, o, z, gamma, dy, eps)
+
+
+def norm_gate_workload():
+    """The layer shape of the FLAT page's benchmarks: B=8, T=4096, H=16, d=128, bf16."""
+    return norm_gate_case("norm_gate", B=8, T=4096, H=16, d=128, dtype=torch.bfloat16, seed=13)

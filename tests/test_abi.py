@@ -237,3 +237,55 @@ def test_conv_workspace(lib):
     assert call_conv_bwd(lib, p, {"ws": None}, ws_bytes=n.value) == -6
     assert call_conv_bwd(lib, p, {"ws": FAKE}, ws_bytes=n.value - 1) == -6
     assert lib.gla_conv_workspace_size(ctypes.byref(p), None) == -1
+
+
+# ---- the output norm and gate (gla_norm_gate_*): host-side validation
+def norm_prob(**kw):
+    d = dict(B=2, T=100, H=4, d=128, eps=1e-5, dtype=1)
+    d.update(kw)
+    return gb.NormGateProblem(d["B"], d["T"], d["H"], d["d"], d["eps"], d["dtype"])
+
+
+def call_norm_fwd(lib, p, ptrs=None):
+    q = dict(o=FAKE, z=FAKE, gamma=FAKE, y=FAKE)
+    q.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_norm_gate_fwd(None if p is None else ctypes.byref(p), c(q["o"]), c(q["z"]),
+                                 c(q["gamma"]), c(q["y"]), None)
+
+
+def call_norm_bwd(lib, p, ptrs=None, ws_bytes=0):
+    names = ["o", "z", "gamma", "dy", "d_o", "dz", "dgamma", "ws"]
+    q = {n: FAKE for n in names}
+    q.update(ws=None)
+    q.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_norm_gate_bwd(ctypes.byref(p), *[c(q[n]) for n in names], ws_bytes, None)
+
+
+def test_norm_gate_argument_errors(lib):
+    assert call_norm_fwd(lib, None) == -1
+    assert call_norm_fwd(lib, norm_prob(), {"z": None}) == -1
+    assert call_norm_bwd(lib, norm_prob(), {"dgamma": None}) == -1
+    assert call_norm_fwd(lib, norm_prob(B=0)) == -2
+    assert call_norm_fwd(lib, norm_prob(T=-1)) == -2
+    assert call_norm_fwd(lib, norm_prob(eps=-1.0)) == -2
+    assert call_norm_fwd(lib, norm_prob(eps=float("nan"))) == -2
+    assert call_norm_fwd(lib, norm_prob(eps=float("inf"))) == -2
+    assert call_norm_fwd(lib, norm_prob(d=96)) == -4
+    assert call_norm_fwd(lib, norm_prob(dtype=3)) == -3
+    assert call_norm_fwd(lib, norm_prob(), {"o": FAKE + 8}) == -5
+    assert call_norm_bwd(lib, norm_prob(), {"dz": FAKE + 4}) == -5
+
+
+def test_norm_gate_workspace(lib):
+    n = ctypes.c_size_t()
+    assert lib.gla_norm_gate_workspace_size(ctypes.byref(norm_prob()), ctypes.byref(n)) == 0
+    assert n.value > 0 and n.value % (128 * 4) == 0
+    assert call_norm_bwd(lib, norm_prob(), ws_bytes=n.value) == -6
+    assert call_norm_bwd(lib, norm_prob(), {"ws": FAKE}, ws_bytes=n.value - 1) == -6
+    assert lib.gla_norm_gate_workspace_size(ctypes.byref(norm_prob(T=0)), ctypes.byref(n)) == 0
+    assert n.value == 0
+    # at most 768 partials of d floats, however many rows
+    assert lib.gla_norm_gate_workspace_size(ctypes.byref(norm_prob(B=64, T=65536, H=64)), ctypes.byref(n)) == 0
+    assert n.value == 768 * 128 * 4
