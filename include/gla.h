@@ -200,6 +200,53 @@ int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const
                  const void* dy, void* dx, float* dw, float* db, void* ws, size_t ws_bytes,
                  void* stream);
 
+/* ---- Gated delta rule (Gated DeltaNet)
+ *
+ * The pages name the delta-rule layers (FLAT page, "FLAT: Flash Linear
+ * Attention on TPUs", Conclusion, future work 1: DeltaNet, Gated DeltaNet and
+ * Kimi Delta Attention, whose state update is not a plain sum of outer
+ * products; probjax page, "GPU kernels", section Gated DeltaNet: a token-by-
+ * token reference and a chunked WY/UT form whose backward keeps only
+ * chunk-boundary states) without writing the update out.  The update computed
+ * here is the published Gated DeltaNet one, in this library's orientation:
+ *
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
+ *
+ * per batch row b and head h, with alpha_t = exp(g_t) (g: natural-log gate, one
+ * per (b, t, h)) and beta_t the write strength (one per (b, t, h), any finite
+ * value; usually in (0, 1)).  S_{-1} = h0, hT = S_{T-1}; segment_ids resets as
+ * for gla_fwd.  There is no internal normalisation of q or k.  gla_delta_bwd
+ * returns dq, dk, dv, dg (dL/dg, 0 at reset tokens), dbeta and dh0.
+ *
+ * Layouts (row-major, contiguous): q, k, dq, dk [B, T, H, d_k]; v, o, dO, dv
+ * [B, T, H, d_v]; g, dg, beta, dbeta [B, T, H]; h0, hT, dhT, dh0 [B, H, d_k, d_v]
+ * float32; segment_ids [B, T] int32.  dtype as for gla_fwd (all products and
+ * sums in float32).  Sizes: B >= 1, T >= 0, H >= 1, d_k and d_v in {64, 128}.
+ * Nullable: h0, segment_ids, hT, dhT, dh0 (as for gla_fwd / gla_bwd), and the
+ * activation pointers when T == 0.  ws: at least gla_delta_workspace_size()
+ * bytes (per-chunk fp32 intermediates: the chunk's inverse T, U, W, masked
+ * scores, states and state gradients).  Ownership, ordering and errors are as
+ * for gla_fwd / gla_bwd. */
+typedef struct {
+    int64_t B, T, H, d_k, d_v;
+    int32_t dtype;    /* gla_dtype */
+    int32_t reserved; /* 0 */
+} gla_delta_problem;
+
+/* Bytes of device workspace gla_delta_fwd / gla_delta_bwd need. */
+int gla_delta_workspace_size(const gla_delta_problem* p, int for_backward, size_t* bytes);
+
+/* Forward: o (and hT if non-NULL). */
+int gla_delta_fwd(const gla_delta_problem* p, const void* q, const void* k, const void* v,
+                  const void* g, const void* beta, const float* h0, const int32_t* segment_ids,
+                  void* o, float* hT, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward: dq, dk, dv, dg, dbeta (and dh0 if non-NULL); recomputes the forward. */
+int gla_delta_bwd(const gla_delta_problem* p, const void* q, const void* k, const void* v,
+                  const void* g, const void* beta, const float* h0, const int32_t* segment_ids,
+                  const void* dO, const float* dhT, void* dq, void* dk, void* dv, void* dg,
+                  void* dbeta, float* dh0, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Output norm and gate (the step after the recurrence)
  *
  * FLAT page ("FLAT: Flash Linear Attention on TPUs"), section Full Linear

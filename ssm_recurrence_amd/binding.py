@@ -41,6 +41,12 @@ class NormGateProblem(ctypes.Structure):
                 ("d", ctypes.c_int64), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
 
 
+class DeltaProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 class GlaError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
@@ -83,6 +89,13 @@ def load():
         lib.gla_norm_gate_fwd.restype = ctypes.c_int
         lib.gla_norm_gate_bwd.argtypes = [NP] + [vp] * 8 + [sz, vp]
         lib.gla_norm_gate_bwd.restype = ctypes.c_int
+        DP = ctypes.POINTER(DeltaProblem)
+        lib.gla_delta_workspace_size.argtypes = [DP, ctypes.c_int, ctypes.POINTER(sz)]
+        lib.gla_delta_workspace_size.restype = ctypes.c_int
+        lib.gla_delta_fwd.argtypes = [DP] + [vp] * 10 + [sz, vp]
+        lib.gla_delta_fwd.restype = ctypes.c_int
+        lib.gla_delta_bwd.argtypes = [DP] + [vp] * 16 + [sz, vp]
+        lib.gla_delta_bwd.restype = ctypes.c_int
         lib.gla_status_str.argtypes = [ctypes.c_int]
         lib.gla_status_str.restype = ctypes.c_char_p
         lib.gla_version.argtypes = []
@@ -450,3 +463,86 @@ class NormGateFunction(torch.autograd.Function):
         o, z, gamma = ctx.saved_tensors
         d_o, dz, dgamma = norm_gate_bwd(o, z, gamma, dy.contiguous(), ctx.eps)
         return d_o, dz, dgamma, None
+
+
+# ---- gated delta rule (gla_delta_* in include/gla.h)
+def delta_problem(q, v):
+    B, T, H, d_k = q.shape
+    return DeltaProblem(B, T, H, d_k, v.shape[3], GLA_BF16 if q.dtype == torch.bfloat16 else GLA_F32, 0)
+
+
+def delta_workspace_size(prob: DeltaProblem) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().gla_delta_workspace_size(ctypes.byref(prob), 1, ctypes.byref(n))
+    if rc:
+        raise GlaError(rc, "gla_delta_workspace_size")
+    return n.value
+
+
+def _delta_checks(q, k, v, g, beta):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta")):
+        _check(t, n, q.dtype)
+    B, T, H, _ = q.shape
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or g.shape != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("delta rule: q, k [B,T,H,d_k], v [B,T,H,d_v], g, beta [B,T,H]")
+
+
+def delta_fwd(q, k, v, g, beta, h0=None, segment_ids=None, *, want_hT=True, ws=None):
+    """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted)."""
+    _delta_checks(q, k, v, g, beta)
+    _check(h0, "h0", torch.float32)
+    _check(segment_ids, "segment_ids", torch.int32)
+    prob = delta_problem(q, v)
+    B, T, H, d_k = q.shape
+    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    hT = torch.empty((B, H, d_k, v.shape[3]), dtype=torch.float32, device=q.device) if want_hT else None
+    n = delta_workspace_size(prob)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    rc = load().gla_delta_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0),
+                              _p(segment_ids), _p(o), _p(hT), _p(ws), ws.numel(), _stream())
+    if rc:
+        raise GlaError(rc, "gla_delta_fwd")
+    return o, hT
+
+
+def delta_bwd(q, k, v, g, beta, dO, h0=None, segment_ids=None, dhT=None, *, want_dh0=True, ws=None):
+    """dq, dk, dv, dg, dbeta (input dtype) and dh0 fp32 (or None)."""
+    _delta_checks(q, k, v, g, beta)
+    _check(dO, "dO", q.dtype)
+    _check(h0, "h0", torch.float32)
+    _check(dhT, "dhT", torch.float32)
+    _check(segment_ids, "segment_ids", torch.int32)
+    prob = delta_problem(q, v)
+    B, T, H, d_k = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+    dh0 = (torch.empty((B, H, d_k, v.shape[3]), dtype=torch.float32, device=q.device)
+           if want_dh0 else None)
+    n = delta_workspace_size(prob)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    rc = load().gla_delta_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0),
+                              _p(segment_ids), _p(dO), _p(dhT), _p(dq), _p(dk), _p(dv), _p(dg),
+                              _p(dbeta), _p(dh0), _p(ws), ws.numel(), _stream())
+    if rc:
+        raise GlaError(rc, "gla_delta_bwd")
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+class DeltaFunction(torch.autograd.Function):
+    """Autograd wrapper of the gated delta rule: both passes run the HIP library."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, h0, segment_ids):
+        o, hT = delta_fwd(q, k, v, g, beta, h0, segment_ids)
+        ctx.save_for_backward(q, k, v, g, beta, h0, segment_ids)
+        return o, hT
+
+    @staticmethod
+    def backward(ctx, dO, dhT):
+        q, k, v, g, beta, h0, seg = ctx.saved_tensors
+        dO = dO.contiguous() if dO is not None else torch.zeros(v.shape, dtype=v.dtype, device=v.device)
+        dhT = dhT.contiguous().float() if dhT is not None else None
+        dq, dk, dv, dg, dbeta, dh0 = delta_bwd(q, k, v, g, beta, dO, h0, seg, dhT, want_dh0=h0 is not None)
+        return dq, dk, dv, dg, dbeta, dh0, None

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libgla.so")
-SOURCES = ["gla_fwd.hip", "gla_fwd_f32s.hip", "gla_fwd_h.hip", "gla_states.hip", "gla_grad.hip", "gla_grad8.hip", "gla_grad_f32s.hip", "gla_group.hip", "gla_conv.hip", "gla_norm.hip", "gla_api.cpp"]
+SOURCES = ["gla_fwd.hip", "gla_fwd_f32s.hip", "gla_fwd_h.hip", "gla_states.hip", "gla_grad.hip", "gla_grad8.hip", "gla_grad_f32s.hip", "gla_group.hip", "gla_conv.hip", "gla_norm.hip", "gla_delta.hip", "gla_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -351,6 +351,34 @@ hipError_t norm_dispatch(const gla_norm_gate_problem* p, F&& f) {
                       : f(float(), std::integral_constant<int, 128>());
 }
 
+// gated delta rule: checks and the workspace
+int check_delta(const gla_delta_problem* p) {
+    if (!p) return GLA_E_NULL;
+    if (p->dtype != GLA_F32 && p->dtype != GLA_BF16) return GLA_E_DTYPE;
+    if (p->B < 1 || p->T < 0 || p->H < 1 || p->d_k < 1 || p->d_v < 1) return GLA_E_SHAPE;
+    if ((p->d_k != 64 && p->d_k != 128) || (p->d_v != 64 && p->d_v != 128)) return GLA_E_UNSUPPORTED;
+    int64_t bt, bth, x;
+    if (!mul_ok(p->B, p->T, &bt) || !mul_ok(bt, p->H, &bth) || !mul_ok(bth, 128, &x) || x > ((int64_t)1 << 40))
+        return GLA_E_SHAPE;
+    const int64_t nc = (p->T + 63) / 64;
+    if (p->B * p->H * (nc > 0 ? nc : 1) > ((int64_t)1 << 31) - 1) return GLA_E_SHAPE;
+    return GLA_OK;
+}
+
+size_t delta_ws_bytes(const gla_delta_problem* p) {
+    const int64_t nc = (p->T + 63) / 64;
+    return (size_t)(p->B * p->H * nc) * (size_t)gla::delta_ws_floats_per_chunk(p->d_k, p->d_v) * sizeof(float);
+}
+
+gla::DeltaArgs delta_args(const gla_delta_problem* p, void* ws) {
+    gla::DeltaArgs a;
+    memset(&a, 0, sizeof a);
+    a.B = p->B; a.T = p->T; a.H = p->H; a.dk = p->d_k; a.dv = p->d_v;
+    a.ws = (float*)ws;
+    a.ws_chunk = gla::delta_ws_floats_per_chunk(p->d_k, p->d_v);
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -522,6 +550,63 @@ int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const
     hipStream_t st = (hipStream_t)stream;
     const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_conv_bwd<gla::bf16>(a, st)
                                               : gla::launch_conv_bwd<float>(a, st);
+    return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+// ---- gated delta rule
+int gla_delta_workspace_size(const gla_delta_problem* p, int for_backward, size_t* bytes) {
+    (void)for_backward;  // (the two passes share one layout)
+    const int rc = check_delta(p);
+    if (rc) return rc;
+    if (!bytes) return GLA_E_NULL;
+    *bytes = delta_ws_bytes(p);
+    return GLA_OK;
+}
+
+int gla_delta_fwd(const gla_delta_problem* p, const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* h0, const int32_t* segment_ids, void* o, float* hT,
+                  void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_delta(p);
+    if (rc) return rc;
+    if (p->T > 0 && (!q || !k || !v || !g || !beta || !o)) return GLA_E_NULL;
+    const void* ptrs[] = {q, k, v, g, beta, h0, segment_ids, o, hT, ws};
+    for (const void* x : ptrs)
+        if (x && !aligned(x)) return GLA_E_ALIGN;
+    const size_t need = delta_ws_bytes(p);
+    if (ws_bytes < need || (need > 0 && !ws)) return GLA_E_WORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (p->T == 0) return copy_state(hT, h0, p->B * p->H * p->d_k * p->d_v, st);
+    gla::DeltaArgs a = delta_args(p, ws);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.seg = segment_ids; a.o = o; a.hT = hT;
+    const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_delta_fwd<gla::bf16>(a, st)
+                                              : gla::launch_delta_fwd<float>(a, st);
+    return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+int gla_delta_bwd(const gla_delta_problem* p, const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* h0, const int32_t* segment_ids, const void* dO,
+                  const float* dhT, void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dh0,
+                  void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_delta(p);
+    if (rc) return rc;
+    if (p->T > 0 && (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta))
+        return GLA_E_NULL;
+    const void* ptrs[] = {q, k, v, g, beta, h0, segment_ids, dO, dhT, dq, dk, dv, dg, dbeta, dh0, ws};
+    for (const void* x : ptrs)
+        if (x && !aligned(x)) return GLA_E_ALIGN;
+    const size_t need = delta_ws_bytes(p);
+    if (ws_bytes < need || (need > 0 && !ws)) return GLA_E_WORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (p->T == 0) return copy_state(dh0, dhT, p->B * p->H * p->d_k * p->d_v, st);
+    gla::DeltaArgs a = delta_args(p, ws);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.seg = segment_ids; a.dO = dO;
+    a.dhT = dhT; a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_delta_bwd<gla::bf16>(a, st)
+                                              : gla::launch_delta_bwd<float>(a, st);
     return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
 }
 

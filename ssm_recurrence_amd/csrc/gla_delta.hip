@@ -1,0 +1,557 @@
+// gla_delta.hip -- the gated delta rule (Gated DeltaNet), chunked WY/UT form,
+// forward and backward (gfx950).
+//
+// Recurrence (the published Gated DeltaNet update, in this library's state
+// orientation, S d_k x d_v and o = S^T q):
+//     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
+// alpha_t = exp(g_t), with the document resets of the gated linear attention.
+// The pages name it (FLAT page, "FLAT: Flash Linear Attention on TPUs",
+// Conclusion, future work 1; probjax page, "GPU kernels", section Gated
+// DeltaNet: a chunked WY/UT form whose backward keeps only chunk-boundary
+// states) without writing it out.
+//
+// Chunked form, per chunk of C = 64 rows with entry state S0, Gamma_t the
+// chunk-local cumulative log gate (restarting at each document start, the
+// reset row's own gate unused), gamma_t = exp(Gamma_t) for rows the entry
+// state reaches (else 0), E_ts = exp(Gamma_t - Gamma_s) within a document:
+//     A  = strictly lower part of diag(beta) (K K^T (.) E)
+//     T  = (I + A)^-1                      (unit lower triangular)
+//     U  = T (beta (.) V),   W = T (beta gamma (.) K)
+//     Wv = U - W S0                        (the rows' effective writes)
+//     O  = (gamma (.) Q) S0 + ((Q K^T) (.) M) Wv      (M: E with the diagonal)
+//     S1 = c S0 + Kt^T Wv,   c = exp(Gamma_last) when the chunk has no reset
+//          (else 0), Kt_s = exp(Gamma_last - Gamma_s) k_s on the last document.
+// It follows from unrolling the recurrence over the chunk: the write of row t
+// is beta_t (v_t - S_{t-1}^T k_t), and S_{t-1} is the decayed S0 plus the
+// decayed earlier writes.
+//
+// Kernels (every product in fp32 on the vector ALUs, operands from LDS or L2):
+//   k_delta_prep   per (b, h, chunk): the row prologue, T, U, W, the masked
+//                  scores P = (Q K^T) (.) M, gamma (.) Q, Kt, c.
+//   k_delta_state  per (b, h, 16 value columns): the chunks in order; o and hT,
+//                  or (backward) S0 and Wv of every chunk.
+//   k_delta_dstate per (b, h, 16 value columns): the chunks in reverse; the
+//                  state gradient at every chunk's end and dWv, then dh0:
+//                  dWv = P^T dO + Kt dS1,  dS0 = c dS1 + (gamma (.) Q)^T dO - W^T dWv.
+//   k_delta_grad   per (b, h, chunk): dq, dk, dv, dg, dbeta by reverse mode
+//                  through the chunk's steps (dA = -T^T dT T^T for the inverse).
+#include "gla_common.hpp"
+#include "gla_kernels.hpp"
+
+namespace gla {
+
+namespace {
+
+constexpr int DC = 64;     // rows per chunk
+constexpr int DTH = 256;   // threads per workgroup
+constexpr int NSL = 16;    // value columns per workgroup of the sequential passes
+constexpr int LP = 65;     // LDS pitch of 64 x 64 matrices
+
+// C(i, j) = alpha * sj[j] * sum_k A(i, k) B(k, j) + beta * C(i, j) for i < M,
+// j < N, with A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj] and C(i, j) =
+// C[i*ci + j*cj] (any mix of LDS and global memory).  Each thread computes
+// R x R blocks; no barrier inside: the caller synchronises.
+template <int R, typename TA, typename TB>
+__device__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, int64_t ak, const TB* B,
+                   int64_t bk, int64_t bj, float beta, float* C, int64_t ci, int64_t cj,
+                   const float* sj = nullptr) {
+    const int nbi = (M + R - 1) / R, nbj = (N + R - 1) / R;
+    for (int blk = threadIdx.x; blk < nbi * nbj; blk += DTH) {
+        const int i0 = (blk / nbj) * R, j0 = (blk % nbj) * R;
+        float acc[R][R];
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+#pragma unroll
+            for (int w = 0; w < R; ++w) acc[u][w] = 0.f;
+        for (int k = 0; k < K; ++k) {
+            float a[R], b[R];
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                a[u] = i0 + u < M ? to_f32(A[(i0 + u) * ai + k * ak]) : 0.f;
+                b[u] = j0 + u < N ? to_f32(B[k * bk + (j0 + u) * bj]) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < R; ++u)
+#pragma unroll
+                for (int w = 0; w < R; ++w) acc[u][w] += a[u] * b[w];
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+#pragma unroll
+            for (int w = 0; w < R; ++w) {
+                const int i = i0 + u, j = j0 + w;
+                if (i < M && j < N) {
+                    float* c = C + i * ci + j * cj;
+                    const float v = alpha * acc[u][w] * (sj ? sj[j] : 1.f);
+                    *c = beta != 0.f ? v + beta * *c : v;
+                }
+            }
+    }
+}
+
+// out[t] += sign * sum_d X[t*lx + d] Y[t*ly + d] for t < n: one wave per row
+template <typename TX, typename TY>
+__device__ void rowdot(int n, int D, const TX* X, int64_t lx, const TY* Y, int64_t ly, float* out,
+                       float sign) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    for (int t = wv; t < n; t += DTH / 64) {
+        float s = 0.f;
+        for (int d = lane; d < D; d += 64) s += to_f32(X[t * lx + d]) * to_f32(Y[t * ly + d]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+        if (lane == 0) out[t] += sign * s;
+    }
+}
+
+// Per-chunk row data in LDS
+struct Rows {
+    float G[DC];     // Gamma_t (document-local cumulative log gate)
+    float gam[DC];   // gamma_t: exp(Gamma_t) where the entry state reaches row t, else 0
+    float kts[DC];   // exp(Gamma_last - Gamma_s) on the last document, else 0
+    float beta[DC];  // beta_t (0 past the end)
+    float bg[DC];    // beta_t gamma_t
+    int doc[DC];     // document index within the chunk (resets at or before t)
+    int reset[DC];
+    float carry;     // c: exp(Gamma_last) when the chunk has no reset, else 0
+    int n;           // valid rows
+};
+
+// Row prologue (wave 0).  g, beta: [B][T][H]; seg: [B][T] or null.
+template <typename T>
+__device__ void prologue(Rows& R, const DeltaArgs& a, int64_t b, int64_t h, int64_t t0) {
+    if (threadIdx.x >= 64) return;
+    const int t = threadIdx.x;
+    const int64_t T_ = a.T;
+    const int n = (int)(T_ - t0 < DC ? T_ - t0 : DC);
+    const bool valid = t < n;
+    const int64_t row = b * T_ + t0 + t;
+    const bool rs = valid && t0 + t > 0 && a.seg && a.seg[row] != a.seg[row - 1];
+    const float gl = valid && !rs ? to_f32(((const T*)a.g)[row * a.H + h]) : 0.f;
+    const float bt = valid ? to_f32(((const T*)a.beta)[row * a.H + h]) : 0.f;
+    const uint64_t mask = __ballot(rs);
+    const uint64_t upto = t == 63 ? ~0ull : ((2ull << t) - 1);
+    const int doc = __popcll(mask & upto);
+    // inclusive prefix of the gates, then restarted at the document's first row
+    float p = gl;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float o = __shfl_up(p, m, 64);
+        if (t >= m) p += o;
+    }
+    const uint64_t before = mask & upto;
+    const int start = before ? 63 - __clzll(before) : 0;
+    const float pstart = __shfl(p, start, 64);
+    const float G = doc > 0 ? p - pstart : p;  // (the reset row's own gate is 0)
+    const int last = n - 1;
+    const float Glast = __shfl(G, last > 0 ? last : 0, 64);
+    const int doclast = __shfl(doc, last > 0 ? last : 0, 64);
+    R.G[t] = G;
+    R.doc[t] = valid ? doc : -1;
+    R.reset[t] = rs;
+    R.beta[t] = bt;
+    R.gam[t] = valid && doc == 0 ? __expf(G) : 0.f;
+    R.bg[t] = bt * R.gam[t];
+    R.kts[t] = valid && doc == doclast ? __expf(Glast - G) : 0.f;
+    if (t == 0) {
+        R.carry = doclast == 0 ? __expf(Glast) : 0.f;
+        R.n = n;
+    }
+}
+
+__device__ __forceinline__ float decay(const Rows& R, int t, int s) {  // E / M entry, s <= t
+    return R.doc[t] >= 0 && R.doc[t] == R.doc[s] ? __expf(R.G[t] - R.G[s]) : 0.f;
+}
+
+// GE = (K K^T) (.) E strictly below the diagonal (LDS, pitch LP), and
+// T = (I + diag(beta) GE)^-1 by forward substitution (lane j builds column j).
+template <typename T>
+__device__ void wy_inverse(const Rows& R, const T* K, int64_t rs, int D, float* sGE, float* sT) {
+    const int n = R.n;
+    for (int i = threadIdx.x; i < DC * LP; i += DTH) sGE[i] = 0.f;
+    __syncthreads();
+    mm<4>(n, n, D, 1.f, K, rs, 1, K, 1, rs, 0.f, sGE, LP, 1);
+    __syncthreads();
+    for (int i = threadIdx.x; i < DC * DC; i += DTH) {
+        const int t = i / DC, s = i % DC;
+        sGE[t * LP + s] = s < t ? sGE[t * LP + s] * decay(R, t, s) : 0.f;
+    }
+    __syncthreads();
+    if (threadIdx.x < DC) {
+        const int j = threadIdx.x;
+        for (int i = 0; i < DC; ++i) {
+            float acc = i == j ? 1.f : 0.f;
+            const float bi = R.beta[i];
+            for (int m = 0; m < i; ++m) acc -= bi * sGE[i * LP + m] * sT[m * LP + j];
+            sT[i * LP + j] = acc;
+        }
+    }
+    __syncthreads();
+}
+
+// per-chunk workspace blocks (fp32)
+struct ChunkWs {
+    float *T, *U, *W, *P, *Qg, *Kt, *carry, *S0, *Wv, *dS1, *dWv, *gQ, *gK, *gKt, *gW, *gV, *gKb;
+};
+
+__device__ ChunkWs chunk_ws(const DeltaArgs& a, int64_t chunk) {
+    const int64_t D = a.dk, Dv = a.dv;
+    float* p = a.ws + chunk * a.ws_chunk;
+    ChunkWs w;
+    w.T = p; p += DC * DC;
+    w.U = p; p += DC * Dv;
+    w.W = p; p += DC * D;
+    w.P = p; p += DC * DC;
+    w.Qg = p; p += DC * D;
+    w.Kt = p; p += DC * D;
+    w.carry = p; p += 4;
+    w.S0 = p; p += D * Dv;
+    w.Wv = p; p += DC * Dv;
+    w.dS1 = p; p += D * Dv;
+    w.dWv = p; p += DC * Dv;
+    w.gQ = p; p += DC * D;
+    w.gK = p; p += DC * D;
+    w.gKt = p; p += DC * D;
+    w.gW = p; p += DC * D;
+    w.gV = p; p += DC * Dv;
+    w.gKb = p; p += DC * D;
+    return w;
+}
+
+// ---------------------------------------------------------------- prepare
+template <typename T>
+__global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
+    __shared__ Rows R;
+    __shared__ float sGE[DC * LP], sT[DC * LP];
+    const int64_t NC = (a.T + DC - 1) / DC;
+    const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
+    const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
+    const int D = (int)a.dk, Dv = (int)a.dv;
+    const int64_t rk = a.H * D, rv = a.H * Dv;
+    const T* Q = (const T*)a.q + (b * a.T + t0) * rk + h * D;
+    const T* K = (const T*)a.k + (b * a.T + t0) * rk + h * D;
+    const T* V = (const T*)a.v + (b * a.T + t0) * rv + h * Dv;
+    prologue<T>(R, a, b, h, t0);
+    __syncthreads();
+    const int n = R.n;
+    wy_inverse<T>(R, K, rk, D, sGE, sT);
+    ChunkWs w = chunk_ws(a, chunk);
+    // T (whole 64 x 64), c
+    for (int i = threadIdx.x; i < DC * DC; i += DTH) w.T[i] = sT[(i / DC) * LP + i % DC];
+    if (threadIdx.x == 0) w.carry[0] = R.carry;
+    __syncthreads();
+    // P = (Q K^T) (.) M in sGE (reused), then copied whole
+    for (int i = threadIdx.x; i < DC * LP; i += DTH) sGE[i] = 0.f;
+    __syncthreads();
+    mm<4>(n, n, D, 1.f, Q, rk, 1, K, 1, rk, 0.f, sGE, LP, 1);
+    __syncthreads();
+    for (int i = threadIdx.x; i < DC * DC; i += DTH) {
+        const int t = i / DC, s = i % DC;
+        w.P[i] = s <= t ? sGE[t * LP + s] * decay(R, t, s) : 0.f;
+    }
+    // gamma (.) Q and Kt, whole 64 rows
+    for (int i = threadIdx.x; i < DC * D; i += DTH) {
+        const int t = i / D, d = i % D;
+        const bool ok = t < n;
+        w.Qg[i] = ok ? R.gam[t] * to_f32(Q[t * rk + d]) : 0.f;
+        w.Kt[i] = ok ? R.kts[t] * to_f32(K[t * rk + d]) : 0.f;
+    }
+    __syncthreads();
+    // U = T (beta V), W = T (beta gamma K), with beta and beta gamma folded into the
+    // columns of T; rows past n are 0 (T is the identity there and beta is 0)
+    for (int i = threadIdx.x; i < DC * DC; i += DTH) {
+        const int t = i / DC, s = i % DC;
+        sGE[t * LP + s] = sT[t * LP + s] * R.bg[s];
+        sT[t * LP + s] *= R.beta[s];
+    }
+    __syncthreads();
+    mm<4>(DC, Dv, n, 1.f, sT, LP, 1, V, rv, 1, 0.f, w.U, Dv, 1);
+    mm<4>(DC, D, n, 1.f, sGE, LP, 1, K, rk, 1, 0.f, w.W, D, 1);
+}
+
+// ---------------------------------------------------------------- state pass
+template <typename T, bool BWD>
+__global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
+    __shared__ float sS[128 * NSL], sWv[DC * NSL], sO[DC * NSL];
+    const int D = (int)a.dk, Dv = (int)a.dv;
+    const int nsl = Dv / NSL;
+    const int64_t bh = blockIdx.x / nsl, j0 = (blockIdx.x % nsl) * NSL;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t NC = (a.T + DC - 1) / DC;
+    for (int i = threadIdx.x; i < D * NSL; i += DTH) {
+        const int r = i / NSL, j = i % NSL;
+        sS[i] = a.h0 ? a.h0[(bh * D + r) * Dv + j0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int64_t c = 0; c < NC; ++c) {
+        const ChunkWs w = chunk_ws(a, bh * NC + c);
+        const int64_t t0 = c * DC;
+        const int n = (int)(a.T - t0 < DC ? a.T - t0 : DC);
+        const float carry = w.carry[0];
+        if (BWD)
+            for (int i = threadIdx.x; i < D * NSL; i += DTH) w.S0[(i / NSL) * Dv + j0 + i % NSL] = sS[i];
+        // Wv = U - W S0
+        for (int i = threadIdx.x; i < DC * NSL; i += DTH) sWv[i] = w.U[(i / NSL) * Dv + j0 + i % NSL];
+        __syncthreads();
+        mm<2>(DC, NSL, D, -1.f, w.W, D, 1, sS, NSL, 1, 1.f, sWv, NSL, 1);
+        __syncthreads();
+        if (BWD) {
+            for (int i = threadIdx.x; i < DC * NSL; i += DTH) w.Wv[(i / NSL) * Dv + j0 + i % NSL] = sWv[i];
+        } else {
+            // O = (gamma Q) S0 + P Wv
+            mm<2>(DC, NSL, D, 1.f, w.Qg, D, 1, sS, NSL, 1, 0.f, sO, NSL, 1);
+            mm<2>(DC, NSL, DC, 1.f, w.P, DC, 1, sWv, NSL, 1, 1.f, sO, NSL, 1);
+            __syncthreads();
+            T* o = (T*)a.o + (b * a.T + t0) * a.H * Dv + h * Dv + j0;
+            for (int i = threadIdx.x; i < n * NSL; i += DTH)
+                o[(i / NSL) * a.H * Dv + i % NSL] = from_f32<T>(sO[i]);
+        }
+        // S1 = c S0 + Kt^T Wv
+        mm<2>(D, NSL, DC, 1.f, w.Kt, 1, D, sWv, NSL, 1, carry, sS, NSL, 1);
+        __syncthreads();
+    }
+    if (!BWD && a.hT)
+        for (int i = threadIdx.x; i < D * NSL; i += DTH) a.hT[(bh * D + i / NSL) * Dv + j0 + i % NSL] = sS[i];
+}
+
+// ---------------------------------------------------------------- reverse state-gradient pass
+template <typename T>
+__global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
+    __shared__ float sdS[128 * NSL], sdWv[DC * NSL];
+    const int D = (int)a.dk, Dv = (int)a.dv;
+    const int nsl = Dv / NSL;
+    const int64_t bh = blockIdx.x / nsl, j0 = (blockIdx.x % nsl) * NSL;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const int64_t NC = (a.T + DC - 1) / DC;
+    const int64_t rv = a.H * Dv;
+    for (int i = threadIdx.x; i < D * NSL; i += DTH) {
+        const int r = i / NSL, j = i % NSL;
+        sdS[i] = a.dhT ? a.dhT[(bh * D + r) * Dv + j0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int64_t c = NC - 1; c >= 0; --c) {
+        const ChunkWs w = chunk_ws(a, bh * NC + c);
+        const int64_t t0 = c * DC;
+        const int n = (int)(a.T - t0 < DC ? a.T - t0 : DC);
+        const float carry = w.carry[0];
+        const T* dO = (const T*)a.dO + (b * a.T + t0) * rv + h * Dv + j0;
+        for (int i = threadIdx.x; i < D * NSL; i += DTH) w.dS1[(i / NSL) * Dv + j0 + i % NSL] = sdS[i];
+        // dWv = P^T dO + Kt dS1
+        mm<2>(DC, NSL, n, 1.f, w.P, 1, DC, dO, rv, 1, 0.f, sdWv, NSL, 1);
+        mm<2>(DC, NSL, D, 1.f, w.Kt, D, 1, sdS, NSL, 1, 1.f, sdWv, NSL, 1);
+        __syncthreads();
+        for (int i = threadIdx.x; i < DC * NSL; i += DTH) w.dWv[(i / NSL) * Dv + j0 + i % NSL] = sdWv[i];
+        // dS0 = c dS1 + (gamma Q)^T dO - W^T dWv
+        mm<2>(D, NSL, n, 1.f, w.Qg, 1, D, dO, rv, 1, carry, sdS, NSL, 1);
+        mm<2>(D, NSL, DC, -1.f, w.W, 1, D, sdWv, NSL, 1, 1.f, sdS, NSL, 1);
+        __syncthreads();
+    }
+    if (a.dh0)
+        for (int i = threadIdx.x; i < D * NSL; i += DTH) a.dh0[(bh * D + i / NSL) * Dv + j0 + i % NSL] = sdS[i];
+}
+
+// ---------------------------------------------------------------- gradients
+template <typename T>
+__global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
+    __shared__ Rows R;
+    __shared__ float sGE[DC * LP], sT[DC * LP], sX[DC * LP], sY[DC * LP];
+    __shared__ float sdG[DC], sdB[DC], sr1[DC], sr2[DC], sdGC;
+    const int64_t NC = (a.T + DC - 1) / DC;
+    const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
+    const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
+    const int D = (int)a.dk, Dv = (int)a.dv;
+    const int64_t rk = a.H * D, rv = a.H * Dv;
+    const T* Q = (const T*)a.q + (b * a.T + t0) * rk + h * D;
+    const T* K = (const T*)a.k + (b * a.T + t0) * rk + h * D;
+    const T* V = (const T*)a.v + (b * a.T + t0) * rv + h * Dv;
+    const T* dO = (const T*)a.dO + (b * a.T + t0) * rv + h * Dv;
+    prologue<T>(R, a, b, h, t0);
+    for (int i = threadIdx.x; i < DC * LP; i += DTH) sX[i] = 0.f;
+    if (threadIdx.x < DC) {
+        sdG[threadIdx.x] = 0.f;
+        sdB[threadIdx.x] = 0.f;
+    }
+    if (threadIdx.x == 0) sdGC = 0.f;
+    __syncthreads();
+    const int n = R.n;
+    wy_inverse<T>(R, K, rk, D, sGE, sT);
+    const ChunkWs w = chunk_ws(a, chunk);
+
+    // (1) output: dQg = dO S0^T; dP = dO Wv^T
+    mm<4>(n, D, Dv, 1.f, dO, rv, 1, w.S0, 1, Dv, 0.f, w.gQ, D, 1);
+    mm<4>(n, n, Dv, 1.f, dO, rv, 1, w.Wv, 1, Dv, 0.f, sX, LP, 1);
+    // (2) state: dKt = Wv dS1^T
+    mm<4>(n, D, Dv, 1.f, w.Wv, Dv, 1, w.dS1, 1, Dv, 0.f, w.gKt, D, 1);
+    // (3) dW = -dWv S0^T
+    mm<4>(DC, D, Dv, -1.f, w.dWv, Dv, 1, w.S0, 1, Dv, 0.f, w.gW, D, 1);
+    __syncthreads();
+    // dGamma from gamma Q: rowdot(dQg, Qg); from Kt: -rowdot(dKt, Kt) per row, + sum into dGamma_last
+    rowdot(n, D, w.gQ, D, w.Qg, D, sdG, 1.f);
+    if (threadIdx.x < DC) sr1[threadIdx.x] = 0.f;
+    __syncthreads();
+    rowdot(n, D, w.gKt, D, w.Kt, D, sr1, 1.f);
+    // carry term: c <dS1, S0>
+    {
+        float s = 0.f;
+        for (int i = threadIdx.x; i < D * Dv; i += DTH) s += w.dS1[i] * w.S0[i];
+        for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+        if ((threadIdx.x & 63) == 0) sr2[threadIdx.x >> 6] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float tot = 0.f;
+        for (int t = 0; t < n; ++t) tot += sr1[t];
+        sdGC = tot + R.carry * (sr2[0] + sr2[1] + sr2[2] + sr2[3]);
+    }
+    if (threadIdx.x < DC) sdG[threadIdx.x] -= sr1[threadIdx.x];
+    // dP (.) P -> dGamma (rows +, columns -); dP (.) M in sX
+    __syncthreads();
+    if (threadIdx.x < DC) {
+        const int t = threadIdx.x;
+        float rsum = 0.f, csum = 0.f;
+        for (int s = 0; s < DC; ++s) {
+            rsum += sX[t * LP + s] * w.P[t * DC + s];
+            csum += sX[s * LP + t] * w.P[s * DC + t];
+        }
+        sr1[t] = rsum;
+        sr2[t] = csum;
+    }
+    __syncthreads();
+    if (threadIdx.x < DC) sdG[threadIdx.x] += sr1[threadIdx.x] - sr2[threadIdx.x];
+    for (int i = threadIdx.x; i < DC * DC; i += DTH) {
+        const int t = i / DC, s = i % DC;
+        sX[t * LP + s] = s <= t && t < n ? sX[t * LP + s] * decay(R, t, s) : 0.f;
+    }
+    // dQ = gamma dQg (in place), then += (dP (.) M) K; dK = (dP (.) M)^T Q + Kt-scale dKt
+    __syncthreads();
+    for (int i = threadIdx.x; i < DC * D; i += DTH) w.gQ[i] *= R.gam[i / D];
+    for (int i = threadIdx.x; i < DC * D; i += DTH) w.gK[i] = R.kts[i / D] * w.gKt[i];
+    __syncthreads();
+    mm<4>(n, D, n, 1.f, sX, LP, 1, K, rk, 1, 1.f, w.gQ, D, 1);
+    mm<4>(n, D, n, 1.f, sX, 1, LP, Q, rk, 1, 1.f, w.gK, D, 1);
+    __syncthreads();
+    // (4) dT = dWv (beta V)^T + dW (beta gamma K)^T in sY
+    mm<4>(DC, n, Dv, 1.f, w.dWv, Dv, 1, V, 1, rv, 0.f, sY, LP, 1, R.beta);
+    __syncthreads();
+    mm<4>(DC, n, D, 1.f, w.gW, D, 1, K, 1, rk, 1.f, sY, LP, 1, R.bg);
+    __syncthreads();
+    for (int i = threadIdx.x; i < DC * LP; i += DTH)
+        if (i % LP >= n && i % LP < DC) sY[i] = 0.f;
+    // dVb = T^T dWv, dKb = T^T dW (before sT is consumed)
+    mm<4>(n, Dv, DC, 1.f, sT, 1, LP, w.dWv, Dv, 1, 0.f, w.gV, Dv, 1);
+    mm<4>(n, D, DC, 1.f, sT, 1, LP, w.gW, D, 1, 0.f, w.gKb, D, 1);
+    __syncthreads();
+    // (5) dA = -T^T dT T^T: sX = dT T^T, then sY = -T^T sX
+    mm<4>(DC, DC, DC, 1.f, sY, LP, 1, sT, 1, LP, 0.f, sX, LP, 1);
+    __syncthreads();
+    mm<4>(DC, DC, DC, -1.f, sT, 1, LP, sX, LP, 1, 0.f, sY, LP, 1);
+    __syncthreads();
+    // A = diag(beta) GE (strictly lower, same document): dbeta += sum_s dA GE; dGamma via
+    // dA (.) A (rows +, columns -); dG = dA beta E in sX (strictly lower)
+    if (threadIdx.x < DC) {
+        const int t = threadIdx.x;
+        float bsum = 0.f, rsum = 0.f, csum = 0.f;
+        for (int s = 0; s < DC; ++s) {
+            const float ge_ts = sGE[t * LP + s], ge_st = sGE[s * LP + t];
+            const float da_ts = s < t ? sY[t * LP + s] : 0.f, da_st = t < s ? sY[s * LP + t] : 0.f;
+            bsum += da_ts * ge_ts;
+            rsum += da_ts * ge_ts;
+            csum += da_st * R.beta[s] * ge_st;
+        }
+        sdB[t] += bsum;
+        sr1[t] = R.beta[t] * rsum;
+        sr2[t] = csum;
+    }
+    __syncthreads();
+    if (threadIdx.x < DC) sdG[threadIdx.x] += sr1[threadIdx.x] - sr2[threadIdx.x];
+    for (int i = threadIdx.x; i < DC * DC; i += DTH) {
+        const int t = i / DC, s = i % DC;
+        sX[t * LP + s] = s < t && t < n ? sY[t * LP + s] * R.beta[t] * decay(R, t, s) : 0.f;
+    }
+    __syncthreads();
+    // dK += (dG + dG^T) K
+    mm<4>(n, D, n, 1.f, sX, LP, 1, K, rk, 1, 1.f, w.gK, D, 1);
+    __syncthreads();
+    mm<4>(n, D, n, 1.f, sX, 1, LP, K, rk, 1, 1.f, w.gK, D, 1);
+    __syncthreads();
+    // (6) dV = beta dVb; dbeta += V . dVb + gamma K . dKb; dK += beta gamma dKb;
+    //     dGamma += beta gamma K . dKb
+    if (threadIdx.x < DC) sr1[threadIdx.x] = 0.f;
+    if (threadIdx.x >= DC && threadIdx.x < 2 * DC) sr2[threadIdx.x - DC] = 0.f;
+    __syncthreads();
+    rowdot(n, Dv, V, rv, w.gV, Dv, sr1, 1.f);
+    rowdot(n, D, K, rk, w.gKb, D, sr2, 1.f);
+    __syncthreads();
+    if (threadIdx.x < DC) {
+        const int t = threadIdx.x;
+        sdB[t] += sr1[t] + R.gam[t] * sr2[t];
+        sdG[t] += R.bg[t] * sr2[t];
+    }
+    for (int i = threadIdx.x; i < DC * D; i += DTH) w.gK[i] += R.bg[i / D] * w.gKb[i];
+    __syncthreads();
+    // (7) the gate: dGamma_last goes to the last row; dg_u = sum of dGamma over t >= u
+    //     in u's document; 0 at reset rows
+    if (threadIdx.x == 0 && n > 0) sdG[n - 1] += sdGC;
+    __syncthreads();
+    const int64_t row0 = b * a.T + t0;
+    if (threadIdx.x < DC) {
+        const int u = threadIdx.x;
+        if (u < n) {
+            float s = 0.f;
+            for (int t = u; t < n; ++t)
+                if (R.doc[t] == R.doc[u]) s += sdG[t];
+            ((T*)a.dg)[(row0 + u) * a.H + h] = from_f32<T>(R.reset[u] ? 0.f : s);
+            ((T*)a.dbeta)[(row0 + u) * a.H + h] = from_f32<T>(sdB[u]);
+        }
+    }
+    // outputs
+    T* dq = (T*)a.dq + row0 * rk + h * D;
+    T* dk = (T*)a.dk_out + row0 * rk + h * D;
+    T* dv = (T*)a.dv_out + row0 * rv + h * Dv;
+    for (int i = threadIdx.x; i < n * D; i += DTH) {
+        const int t = i / D, d = i % D;
+        dq[t * rk + d] = from_f32<T>(w.gQ[i]);
+        dk[t * rk + d] = from_f32<T>(w.gK[i]);
+    }
+    for (int i = threadIdx.x; i < n * Dv; i += DTH) {
+        const int t = i / Dv, d = i % Dv;
+        dv[t * rv + d] = from_f32<T>(R.beta[t] * w.gV[i]);
+    }
+}
+
+}  // namespace
+
+int64_t delta_ws_floats_per_chunk(int64_t dk, int64_t dv) {
+    return 2 * DC * DC + 4 + 2 * dk * dv + DC * (4 * dv + 8 * dk);
+}
+
+template <typename T>
+hipError_t launch_delta_fwd(const DeltaArgs& a, hipStream_t st) {
+    const int64_t NC = (a.T + DC - 1) / DC;
+    hipLaunchKernelGGL(k_delta_prep<T>, dim3((unsigned)(a.B * a.H * NC)), dim3(DTH), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_delta_state<T, false>), dim3((unsigned)(a.B * a.H * (a.dv / NSL))), dim3(DTH), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st) {
+    const int64_t NC = (a.T + DC - 1) / DC;
+    const dim3 chunks((unsigned)(a.B * a.H * NC)), slices((unsigned)(a.B * a.H * (a.dv / NSL)));
+    hipLaunchKernelGGL(k_delta_prep<T>, chunks, dim3(DTH), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_delta_state<T, true>), slices, dim3(DTH), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_delta_dstate<T>, slices, dim3(DTH), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_delta_grad<T>, chunks, dim3(DTH), 0, st, a);
+    return hipGetLastError();
+}
+
+template hipError_t launch_delta_fwd<float>(const DeltaArgs&, hipStream_t);
+template hipError_t launch_delta_fwd<bf16>(const DeltaArgs&, hipStream_t);
+template hipError_t launch_delta_bwd<float>(const DeltaArgs&, hipStream_t);
+template hipError_t launch_delta_bwd<bf16>(const DeltaArgs&, hipStream_t);
+
+}  // namespace gla

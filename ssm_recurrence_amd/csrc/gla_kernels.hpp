@@ -124,6 +124,23 @@ template <typename T, int D> hipError_t launch_norm_gate_fwd(const NormArgs& a, 
 // the backward and the fixed-order reduction of dgamma (rows = 0 included)
 template <typename T, int D> hipError_t launch_norm_gate_bwd(const NormArgs& a, hipStream_t st);
 
+// the gated delta rule (chunked WY/UT form), gla_delta.hip
+struct DeltaArgs {
+    const void *q, *k, *v, *g, *beta, *dO;  // [B][T][H][d] (g, beta: [B][T][H]), input dtype
+    const float *h0, *dhT;                  // [B][H][dk][dv] or null
+    const int32_t* seg;                     // [B][T] or null
+    void* o;                                // forward output
+    float* hT;                              // forward output or null
+    void *dq, *dk_out, *dv_out, *dg, *dbeta;  // backward outputs
+    float* dh0;                             // backward output or null
+    float* ws;                              // delta_ws_floats_per_chunk floats per (b, h, chunk)
+    int64_t ws_chunk;
+    int64_t B, T, H, dk, dv;
+};
+int64_t delta_ws_floats_per_chunk(int64_t dk, int64_t dv);
+template <typename T> hipError_t launch_delta_fwd(const DeltaArgs& a, hipStream_t st);
+template <typename T> hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st);
+
 template <typename T, int DK>
 hipError_t launch_group_sum(const float* src, void* dst, int64_t ld_dst, int64_t B, int64_t Tn,
                             int64_t H, int64_t Hqk, hipStream_t st);

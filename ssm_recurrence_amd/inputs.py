@@ -232,3 +232,55 @@ def norm_gate_case(name="norm_gate", *, B, T, H, d=128, dtype=torch.bfloat16, se
 def norm_gate_workload():
     """The layer shape of the FLAT page's benchmarks: B=8, T=4096, H=16, d=128, bf16."""
     return norm_gate_case("norm_gate", B=8, T=4096, H=16, d=128, dtype=torch.bfloat16, seed=13)
+
+
+# ---- the gated delta rule
+@dataclasses.dataclass
+class DeltaCase:
+    name: str
+    dtype: torch.dtype
+    q: torch.Tensor               # [B, T, H, d_k], unit norm per row
+    k: torch.Tensor               # [B, T, H, d_k], unit norm per row
+    v: torch.Tensor               # [B, T, H, d_v]
+    g: torch.Tensor               # [B, T, H] natural-log gate
+    beta: torch.Tensor            # [B, T, H] write strength in (0, 1)
+    dO: torch.Tensor              # [B, T, H, d_v]
+    h0: Optional[torch.Tensor] = None
+    dhT: Optional[torch.Tensor] = None
+    segment_ids: Optional[torch.Tensor] = None
+
+    def to(self, device):
+        mv = lambda x: None if x is None else x.to(device)
+        return dataclasses.replace(self, q=mv(self.q), k=mv(self.k), v=mv(self.v), g=mv(self.g),
+                                   beta=mv(self.beta), dO=mv(self.dO), h0=mv(self.h0), dhT=mv(self.dhT),
+                                   segment_ids=mv(self.segment_ids))
+
+
+def delta_case(name="delta", *, B, T, H, d_k=128, d_v=None, dtype=torch.bfloat16, seed=0,
+               lengths=None, with_h0=True, with_dhT=True):
+    """q, k: N(0, 1) rows scaled to unit L2 norm (the delta rule's keys are normalised
+    in its layers); v, dO ~ N(0, 1); g = log sigmoid of N(3, 1) (gates near 0.95);
+    beta = sigmoid of N(0, 1); h0 ~ 0.1 N(0, 1), dhT ~ N(0, 1).  bf16 values are
+    rounded once, when drawn."""
+    d_v = d_k if d_v is None else d_v
+    gen = torch.Generator().manual_seed(seed)
+    unit = lambda x: x / x.norm(dim=-1, keepdim=True)
+    q = unit(torch.randn((B, T, H, d_k), generator=gen))
+    k = unit(torch.randn((B, T, H, d_k), generator=gen))
+    v = torch.randn((B, T, H, d_v), generator=gen)
+    g = torch.nn.functional.logsigmoid(torch.randn((B, T, H), generator=gen) + 3.0)
+    beta = torch.sigmoid(torch.randn((B, T, H), generator=gen))
+    dO = torch.randn((B, T, H, d_v), generator=gen)
+    h0 = torch.randn((B, H, d_k, d_v), generator=gen) * 0.1 if with_h0 else None
+    dhT = torch.randn((B, H, d_k, d_v), generator=gen) if with_dhT else None
+    seg = None
+    if lengths is not None:
+        seg = segment_ids_from_lengths(lengths, T).reshape(1, T).repeat(B, 1).contiguous()
+    cast = lambda x: x.to(dtype).contiguous()
+    return DeltaCase(name, dtype, cast(q), cast(k), cast(v), cast(g), cast(beta), cast(dO), h0, dhT, seg)
+
+
+def delta_workload():
+    """The pages' Gated DeltaNet benchmark layout: bf16, batch 4, 8 heads, chunk 64,
+    d_k = d_v = 128, here at T = 4096."""
+    return delta_case("delta", B=4, T=4096, H=8, d_k=128, dtype=torch.bfloat16, seed=17)

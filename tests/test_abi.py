@@ -289,3 +289,52 @@ def test_norm_gate_workspace(lib):
     # at most 768 partials of d floats, however many rows
     assert lib.gla_norm_gate_workspace_size(ctypes.byref(norm_prob(B=64, T=65536, H=64)), ctypes.byref(n)) == 0
     assert n.value == 768 * 128 * 4
+
+
+# ---- the gated delta rule (gla_delta_*): host-side validation
+def delta_prob(**kw):
+    d = dict(B=2, T=100, H=4, d_k=128, d_v=64, dtype=1)
+    d.update(kw)
+    return gb.DeltaProblem(d["B"], d["T"], d["H"], d["d_k"], d["d_v"], d["dtype"], 0)
+
+
+def call_delta_fwd(lib, p, ptrs=None, ws_bytes=0):
+    names = ["q", "k", "v", "g", "beta", "h0", "seg", "o", "hT", "ws"]
+    q = {n: FAKE for n in names}
+    q.update(h0=None, seg=None, hT=None, ws=None)
+    q.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_delta_fwd(None if p is None else ctypes.byref(p), *[c(q[n]) for n in names], ws_bytes, None)
+
+
+def call_delta_bwd(lib, p, ptrs=None, ws_bytes=0):
+    names = ["q", "k", "v", "g", "beta", "h0", "seg", "dO", "dhT", "dq", "dk", "dv", "dg", "dbeta", "dh0", "ws"]
+    q = {n: FAKE for n in names}
+    q.update(h0=None, seg=None, dhT=None, dh0=None, ws=None)
+    q.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_delta_bwd(ctypes.byref(p), *[c(q[n]) for n in names], ws_bytes, None)
+
+
+def test_delta_argument_errors(lib):
+    assert call_delta_fwd(lib, None) == -1
+    assert call_delta_fwd(lib, delta_prob(), {"beta": None}) == -1
+    assert call_delta_bwd(lib, delta_prob(), {"dbeta": None}) == -1
+    assert call_delta_fwd(lib, delta_prob(B=0)) == -2
+    assert call_delta_bwd(lib, delta_prob(T=-1)) == -2
+    assert call_delta_fwd(lib, delta_prob(d_k=96)) == -4
+    assert call_delta_bwd(lib, delta_prob(d_v=32)) == -4
+    assert call_delta_fwd(lib, delta_prob(dtype=5)) == -3
+    assert call_delta_fwd(lib, delta_prob(), {"g": FAKE + 4}) == -5
+    assert call_delta_bwd(lib, delta_prob(), {"dh0": FAKE + 8}) == -5
+
+
+def test_delta_workspace(lib):
+    n = ctypes.c_size_t()
+    assert lib.gla_delta_workspace_size(ctypes.byref(delta_prob()), 1, ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert call_delta_fwd(lib, delta_prob(), ws_bytes=n.value) == -6
+    assert call_delta_bwd(lib, delta_prob(), {"ws": FAKE}, ws_bytes=n.value - 1) == -6
+    m = ctypes.c_size_t()
+    assert lib.gla_delta_workspace_size(ctypes.byref(delta_prob(T=200)), 1, ctypes.byref(m)) == 0
+    assert m.value == 2 * n.value  # 4 chunks against 2
