@@ -3,6 +3,7 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
 python bench.py --workload conv   (the short depthwise causal convolution)
 python bench.py --workload norm_gate   (the output per-head RMSNorm x swish gate)
+python bench.py --workload delta   (the gated delta rule, chunked WY/UT form)
 python bench.py --workload c3 --fused   (q, k, v read in place from one projection
                                           tensor, one fused gradient written)
 
@@ -35,7 +36,8 @@ PROFILE = {"c2": "gla_kernels_ssd_fp32_B4_T8192_H8_Hqk2_d128.md",
            "c5b": "gla_kernels_gla_bf16_B8_T2048_H16_d128.md",
            "c3f": "gla_kernels_gla_bf16_fused_B4_T4096_H16_d128.md",
            "conv": "conv_kernels_bf16_B8_T4096_C2048_K4.md",
-           "norm_gate": "norm_gate_kernels_bf16_B8_T4096_H16_d128.md"}
+           "norm_gate": "norm_gate_kernels_bf16_B8_T4096_H16_d128.md",
+           "delta": "delta_kernels_bf16_B4_T4096_H8_d128.md"}
 
 
 def source_hash():
@@ -69,7 +71,8 @@ def measured_traffic(workload, key="traffic_bytes_per_gla_bwd"):
 
 PEAK = {"hbm": 8000.0,            # GB/s
         "mfma_f32": 157.3,        # TFLOP/s, dense fp32 matrix cores
-        "mfma_bf16": 2500.0}      # TFLOP/s, dense bf16 matrix cores
+        "mfma_bf16": 2500.0,      # TFLOP/s, dense bf16 matrix cores
+        "valu_f32": 157.3}        # TFLOP/s, fp32 vector ALUs
 
 
 def algorithmic(case):
@@ -127,6 +130,9 @@ def main():
         return
     if args.workload == "norm_gate":
         norm_gate_main(args)
+        return
+    if args.workload == "delta":
+        delta_main(args)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -475,6 +481,123 @@ def norm_gate_main(args):
         "config": {"workload": "norm_gate: per-head RMSNorm x swish gate, bf16, B=8 T=4096 H=16 d=128, "
                                "eps=%g" % c.eps,
                    "global_batch": B, "seq_len": T, "heads": H, "d": d, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def delta_flops(T, C, dk, dv):
+    """FLOPs of the chunked WY/UT gated delta rule per (b, h): dense products of
+    each chunk as the method forms them (the backward recomputes the chunk-local
+    forward terms and the states entering the chunks, as a backward that keeps only
+    chunk-boundary states must)."""
+    nc = (T + C - 1) // C
+    c2k, c2v, cdd, c3 = 2 * C * C * dk, 2 * C * C * dv, 2 * C * dk * dv, 2 * C ** 3
+    prep = 2 * c2k + c2v + c2k + c3 / 3           # K K^T, U, W, Q K^T, the inverse
+    state = 3 * cdd + c2v                          # W S0, (gamma Q) S0, Kt^T Wv; P Wv
+    fwd = prep + state
+    dstate = c2v + 3 * cdd                         # P^T dO; Kt dS1, (gamma Q)^T dO, W^T dWv
+    grad = (c2k + c3 / 3 + 3 * cdd                 # K K^T, inverse; dO S0^T, Wv dS1^T, dWv S0^T
+            + c2v + 2 * c2k                        # dO Wv^T; (dP M) K, (dP M)^T Q
+            + c2v + c2k + c2v + c2k                # dT (two), T^T dWv, T^T dW
+            + 2 * c3 + 2 * c2k)                    # dA = -T^T dT T^T; (dG + dG^T) K
+    bwd = prep + cdd + dstate + grad               # (the state pass without readout: W S0)
+    return nc * fwd, nc * bwd
+
+
+def delta_main(args):
+    """The gated delta rule at the pages' Gated DeltaNet benchmark layout (bf16,
+    batch 4, 8 heads, chunk 64, d = 128) at T = 4096: one gla_delta_fwd and one
+    gla_delta_bwd per step."""
+    import torch
+    from ssm_recurrence_amd import binding as gb
+    from ssm_recurrence_amd.inputs import delta_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case_cpu = delta_workload()
+    c = case_cpu.to(dev)
+    B, T, H, dk = c.q.shape
+    dv = c.v.shape[3]
+    prob = gb.delta_problem(c.q, c.v)
+    o = torch.empty_like(c.v)
+    hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    dq, dk_, dv_, dg, db = (torch.empty_like(c.q), torch.empty_like(c.k), torch.empty_like(c.v),
+                            torch.empty_like(c.g), torch.empty_like(c.beta))
+    dh0 = torch.empty_like(c.h0)
+    n = gb.delta_workspace_size(prob)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = gb.ctypes.c_void_p(stream.cuda_stream)
+    lib = gb.load()
+    P = gb.ctypes.byref(prob)
+    p = gb._p
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = lib.gla_delta_fwd(P, p(c.q), p(c.k), p(c.v), p(c.g), p(c.beta), p(c.h0), p(c.segment_ids),
+                               p(o), p(hT), p(ws), ws.numel(), sp)
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= lib.gla_delta_bwd(P, p(c.q), p(c.k), p(c.v), p(c.g), p(c.beta), p(c.h0), p(c.segment_ids),
+                                p(c.dO), p(c.dhT), p(dq), p(dk_), p(dv_), p(dg), p(db), p(dh0), p(ws),
+                                ws.numel(), sp)
+        if ev is not None:
+            ev[2].record(stream)
+        if rc:
+            raise RuntimeError("gla_delta_* failed: %d" % rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    fwd_us = 1000.0 * sum(fwd_ms) / len(fwd_ms)
+    bwd_us = 1000.0 * sum(bwd_ms) / len(bwd_ms)
+    ff, fb = delta_flops(T, 64, dk, dv)
+    ff, fb = ff * B * H, fb * B * H
+    achieved = fb / (bwd_us * 1e-6) / 1e12
+    roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK["valu_f32"], "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK["valu_f32"], 4), "traffic": None,
+            "algorithmic_flops": round(fb / 1e9, 2),
+            "kernel": "gla_delta_bwd (its four kernels, one call): fp32 products on the vector ALUs",
+            "step_frac": round((ff + fb) / ((fwd_us + bwd_us) * 1e-6) / 1e12 / PEAK["valu_f32"], 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.delta as od
+        s = case_cpu
+        sl = lambda x: None if x is None else x[0:1, :, 0:1].contiguous()  # (b, h) = (0, 0)
+        hs = lambda x: None if x is None else x[0:1, 0:1].contiguous()
+        c0 = time.perf_counter()
+        reps = 0
+        while reps == 0 or time.perf_counter() - c0 < 10.0:
+            od.delta_fwd(sl(s.q), sl(s.k), sl(s.v), sl(s.g), sl(s.beta), hs(s.h0), None)
+            od.delta_bwd(sl(s.q), sl(s.k), sl(s.v), sl(s.g), sl(s.beta), sl(s.dO), hs(s.h0), None, hs(s.dhT))
+            reps += 1
+        c1 = time.perf_counter()
+        cpu = {"value": round(reps * T / H / (c1 - c0), 1), "unit": "tokens/s", "cores": 1,
+               "kind": "oracle",
+               "sample": "one (batch row, head) of the workload (%d steps), fwd+bwd in numpy fp64 on one "
+                         "thread, %d times in %.1f s; tokens/s counts a token as all %d heads" % (T, reps, c1 - c0, H)}
+    out = {
+        "metric": "fwd+bwd µs and tokens/s for the gated delta rule (chunked WY/UT form), % of fp32 vector ALU peak",
+        "value": round(B * T / (ms_per_step / 1000.0), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "us_fwd": round(fwd_us, 1), "us_bwd": round(bwd_us, 1), "us_fwd_bwd": round(fwd_us + bwd_us, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "delta: gated delta rule, bf16, B=4 T=4096 H=8 d_k=d_v=128, chunk 64, h0 and dhT",
+                   "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv, "chunk": 64,
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

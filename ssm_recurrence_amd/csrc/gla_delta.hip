@@ -47,14 +47,16 @@ constexpr int DTH = 256;   // threads per workgroup
 constexpr int NSL = 16;    // value columns per workgroup of the sequential passes
 constexpr int LP = 65;     // LDS pitch of 64 x 64 matrices
 
-// C(i, j) = alpha * sj[j] * sum_k A(i, k) B(k, j) + beta * C(i, j) for i < M,
-// j < N, with A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj] and C(i, j) =
-// C[i*ci + j*cj] (any mix of LDS and global memory).  Each thread computes
-// R x R blocks; no barrier inside: the caller synchronises.
+// C(i, j) = alpha * si[i] * sj[j] * sum_k A(i, k) B(k, j) + beta * C(i, j) for
+// i < M, j < N, with A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj] and
+// C(i, j) = C[i*ci + j*cj] (any mix of LDS and global memory; si, sj optional).
+// Each thread computes R x R blocks, consecutive threads taking consecutive
+// column blocks, so B reads coalesce when bj = 1.  No barrier inside: the
+// caller synchronises.
 template <int R, typename TA, typename TB>
 __device__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, int64_t ak, const TB* B,
                    int64_t bk, int64_t bj, float beta, float* C, int64_t ci, int64_t cj,
-                   const float* sj = nullptr) {
+                   const float* sj = nullptr, const float* si = nullptr) {
     const int nbi = (M + R - 1) / R, nbj = (N + R - 1) / R;
     for (int blk = threadIdx.x; blk < nbi * nbj; blk += DTH) {
         const int i0 = (blk / nbj) * R, j0 = (blk % nbj) * R;
@@ -63,7 +65,27 @@ __device__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, in
         for (int u = 0; u < R; ++u)
 #pragma unroll
             for (int w = 0; w < R; ++w) acc[u][w] = 0.f;
-        for (int k = 0; k < K; ++k) {
+        // KU k steps of loads are issued before their products, so that one wait
+        // covers KU steps' latency (operands often come from L2)
+        constexpr int KU = R >= 4 ? 4 : 8;
+        int k = 0;
+        for (; k + KU <= K; k += KU) {
+            float a[KU][R], b[KU][R];
+#pragma unroll
+            for (int kk = 0; kk < KU; ++kk)
+#pragma unroll
+                for (int u = 0; u < R; ++u) {
+                    a[kk][u] = i0 + u < M ? to_f32(A[(i0 + u) * ai + (k + kk) * ak]) : 0.f;
+                    b[kk][u] = j0 + u < N ? to_f32(B[(k + kk) * bk + (j0 + u) * bj]) : 0.f;
+                }
+#pragma unroll
+            for (int kk = 0; kk < KU; ++kk)
+#pragma unroll
+                for (int u = 0; u < R; ++u)
+#pragma unroll
+                    for (int w = 0; w < R; ++w) acc[u][w] += a[kk][u] * b[kk][w];
+        }
+        for (; k < K; ++k) {
             float a[R], b[R];
 #pragma unroll
             for (int u = 0; u < R; ++u) {
@@ -82,10 +104,135 @@ __device__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, in
                 const int i = i0 + u, j = j0 + w;
                 if (i < M && j < N) {
                     float* c = C + i * ci + j * cj;
-                    const float v = alpha * acc[u][w] * (sj ? sj[j] : 1.f);
+                    const float v = alpha * acc[u][w] * (sj ? sj[j] : 1.f) * (si ? si[i] : 1.f);
                     *c = beta != 0.f ? v + beta * *c : v;
                 }
             }
+    }
+}
+
+// The same product for operands in global memory (L2): k is taken in tiles of
+// KT; each tile of A (M x KT) and B (KT x N) is loaded by the whole workgroup
+// with the unit-stride index running across lanes, written to LDS, and the
+// next tile's loads are issued before the current tile is used.  Every thread
+// accumulates up to NBT blocks of 4 x 4 (M N <= 4096 NBT), M, N <= 128.  `lds`
+// holds MMT_LDS floats.  Contains barriers: every thread of the workgroup calls it.
+constexpr int KT = 32, MMT_LDS = 128 * (KT + 1) + KT * (128 + 1), LDE = 16;
+template <int NBT = 2, typename TA, typename TB>
+__device__ void mmt(int M, int N, int K, float alpha, const TA* A, int64_t ai64, int64_t ak64, const TB* B,
+                    int64_t bk64, int64_t bj64, float beta, float* C, int64_t ci, int64_t cj, float* lds,
+                    const float* sj = nullptr, const float* si = nullptr) {
+    // (offsets within one chunk's operands fit in 32 bits)
+    const int ai = (int)ai64, ak = (int)ak64, bk = (int)bk64, bj = (int)bj64;
+    float* sa = lds;                    // [128][KT + 1]: sa[i][kk]
+    float* sb = lds + 128 * (KT + 1);   // [KT][N + 1]:   sb[kk][j]
+    const int NP = N + 1;
+    const int tid = threadIdx.x;
+    const bool a_i_fast = ai == 1 && ak != 1;  // unit stride along i: lanes run along i
+    const bool b_k_fast = bk == 1 && bj != 1;
+    // element e of a 128 x KT tile: (row, k) with the unit-stride index fastest
+    auto a_ik = [&](int e, int& i, int& kk) {
+        if (a_i_fast) { i = e & 127; kk = e >> 7; } else { i = e / KT; kk = e % KT; }  // (e < 128 KT)
+    };
+    auto b_jk = [&](int e, int& j, int& kb) {
+        if (b_k_fast) { j = e / KT; kb = e % KT; } else { j = e & 127; kb = e >> 7; }
+    };
+    float ra[LDE], rb[LDE];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int r = 0; r < LDE; ++r) {
+            const int e = tid + r * DTH;
+            int i, kk, j, kb;
+            a_ik(e, i, kk);
+            b_jk(e, j, kb);
+            ra[r] = (i < M && k0 + kk < K) ? to_f32(A[i * ai + (k0 + kk) * ak]) : 0.f;
+            rb[r] = (j < N && k0 + kb < K) ? to_f32(B[(k0 + kb) * bk + j * bj]) : 0.f;
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int r = 0; r < LDE; ++r) {
+            const int e = tid + r * DTH;
+            int i, kk, j, kb;
+            a_ik(e, i, kk);
+            b_jk(e, j, kb);
+            if (i < M) sa[i * (KT + 1) + kk] = ra[r];
+            if (j < N) sb[kb * NP + j] = rb[r];
+        }
+    };
+    const int nbj = (N + 3) / 4, nblk = ((M + 3) / 4) * nbj;
+    float acc[NBT][4][4];
+#pragma unroll
+    for (int q = 0; q < NBT; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) acc[q][u][w] = 0.f;
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += KT) {
+        __syncthreads();  // the previous tile is no longer read
+        stash();
+        __syncthreads();
+        if (k0 + KT < K) fetch(k0 + KT);
+#pragma unroll
+        for (int q = 0; q < NBT; ++q) {
+            const int blk = tid + q * DTH;
+            if (blk < nblk) {
+                const int i0 = (blk / nbj) * 4, j0 = (blk % nbj) * 4;
+#pragma unroll 1
+                for (int kk = 0; kk < KT; ++kk) {
+                    float a[4], b[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        a[u] = sa[(i0 + u < 128 ? i0 + u : 127) * (KT + 1) + kk];
+                        b[u] = sb[kk * NP + (j0 + u < N ? j0 + u : N - 1)];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) acc[q][u][w] += a[u] * b[w];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NBT; ++q) {
+        const int blk = tid + q * DTH;
+        if (blk < nblk) {
+            const int i0 = (blk / nbj) * 4, j0 = (blk % nbj) * 4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int i = i0 + u, j = j0 + w;
+                    if (i < M && j < N) {
+                        float* c = C + i * ci + j * cj;
+                        const float v = alpha * acc[q][u][w] * (sj ? sj[j] : 1.f) * (si ? si[i] : 1.f);
+                        *c = beta != 0.f ? v + beta * *c : v;
+                    }
+                }
+        }
+    }
+    __syncthreads();  // (lds free for the next call)
+}
+
+// st(i, ld(i)) for i < n over the workgroup, EB elements per thread at a time
+// with all EB loads issued before the stores (a store through one pointer
+// would otherwise keep the next load, through another, from being issued early).
+template <int EB = 8, typename L, typename S>
+__device__ __forceinline__ void ew(int n, L ld, S st) {
+    for (int base = threadIdx.x; base < n; base += EB * DTH) {
+        float v[EB];
+#pragma unroll
+        for (int u = 0; u < EB; ++u) {
+            const int i = base + u * DTH;
+            v[u] = i < n ? ld(i) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < EB; ++u) {
+            const int i = base + u * DTH;
+            if (i < n) st(i, v[u]);
+        }
     }
 }
 
@@ -162,14 +309,28 @@ __device__ __forceinline__ float decay(const Rows& R, int t, int s) {  // E / M 
     return R.doc[t] >= 0 && R.doc[t] == R.doc[s] ? __expf(R.G[t] - R.G[s]) : 0.f;
 }
 
+// K tile in LDS: rows at an odd number of dwords apart, so that reading a
+// column (one element per row) across lanes is free of bank conflicts
+template <typename T> constexpr int kpad() { return sizeof(T) == 2 ? 2 : 1; }
+template <typename T> __device__ __forceinline__ int kpitch(int D) { return D + kpad<T>(); }
+
+// the chunk's K rows into LDS (rows past n zero)
+template <typename T>
+__device__ void load_k(const Rows& R, const T* K, int64_t rs, int D, T* sK) {
+    const int KP = kpitch<T>(D), n = R.n;
+    ew(DC * D, [&](int i) { const int t = i / D; return t < n ? to_f32(K[t * rs + i % D]) : 0.f; },
+       [&](int i, float v) { sK[(i / D) * KP + i % D] = from_f32<T>(v); });
+}
+
 // GE = (K K^T) (.) E strictly below the diagonal (LDS, pitch LP), and
 // T = (I + diag(beta) GE)^-1 by forward substitution (lane j builds column j).
+// sK: the chunk's K rows (load_k), complete before the call.
 template <typename T>
-__device__ void wy_inverse(const Rows& R, const T* K, int64_t rs, int D, float* sGE, float* sT) {
-    const int n = R.n;
+__device__ void wy_inverse(const Rows& R, const T* sK, int D, float* sGE, float* sT) {
+    const int n = R.n, KP = kpitch<T>(D);
     for (int i = threadIdx.x; i < DC * LP; i += DTH) sGE[i] = 0.f;
     __syncthreads();
-    mm<4>(n, n, D, 1.f, K, rs, 1, K, 1, rs, 0.f, sGE, LP, 1);
+    mm<4>(n, n, D, 1.f, sK, KP, 1, sK, 1, KP, 0.f, sGE, LP, 1);
     __syncthreads();
     for (int i = threadIdx.x; i < DC * DC; i += DTH) {
         const int t = i / DC, s = i % DC;
@@ -177,13 +338,19 @@ __device__ void wy_inverse(const Rows& R, const T* K, int64_t rs, int D, float* 
     }
     __syncthreads();
     if (threadIdx.x < DC) {
+        // lane j keeps column j of T in registers; row i of GE is read as a
+        // broadcast (every lane reads the same address)
         const int j = threadIdx.x;
+        float tc[DC];
+#pragma unroll
         for (int i = 0; i < DC; ++i) {
-            float acc = i == j ? 1.f : 0.f;
-            const float bi = R.beta[i];
-            for (int m = 0; m < i; ++m) acc -= bi * sGE[i * LP + m] * sT[m * LP + j];
-            sT[i * LP + j] = acc;
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc += sGE[i * LP + m] * tc[m];
+            tc[i] = (i == j ? 1.f : 0.f) - R.beta[i] * acc;
         }
+#pragma unroll
+        for (int i = 0; i < DC; ++i) sT[i * LP + j] = tc[i];
     }
     __syncthreads();
 }
@@ -222,10 +389,12 @@ template <typename T>
 __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     __shared__ Rows R;
     __shared__ float sGE[DC * LP], sT[DC * LP];
+    __shared__ T sK[DC * (128 + kpad<T>())];
+    __shared__ float smm[MMT_LDS];
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
     const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
-    const int D = (int)a.dk, Dv = (int)a.dv;
+    const int D = (int)a.dk, Dv = (int)a.dv, KP = kpitch<T>(D);
     const int64_t rk = a.H * D, rv = a.H * Dv;
     const T* Q = (const T*)a.q + (b * a.T + t0) * rk + h * D;
     const T* K = (const T*)a.k + (b * a.T + t0) * rk + h * D;
@@ -233,7 +402,9 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     prologue<T>(R, a, b, h, t0);
     __syncthreads();
     const int n = R.n;
-    wy_inverse<T>(R, K, rk, D, sGE, sT);
+    load_k<T>(R, K, rk, D, sK);
+    __syncthreads();
+    wy_inverse<T>(R, sK, D, sGE, sT);
     ChunkWs w = chunk_ws(a, chunk);
     // T (whole 64 x 64), c
     for (int i = threadIdx.x; i < DC * DC; i += DTH) w.T[i] = sT[(i / DC) * LP + i % DC];
@@ -242,19 +413,17 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     // P = (Q K^T) (.) M in sGE (reused), then copied whole
     for (int i = threadIdx.x; i < DC * LP; i += DTH) sGE[i] = 0.f;
     __syncthreads();
-    mm<4>(n, n, D, 1.f, Q, rk, 1, K, 1, rk, 0.f, sGE, LP, 1);
+    mmt(n, n, D, 1.f, Q, rk, 1, sK, 1, KP, 0.f, sGE, LP, 1, smm);
     __syncthreads();
     for (int i = threadIdx.x; i < DC * DC; i += DTH) {
         const int t = i / DC, s = i % DC;
         w.P[i] = s <= t ? sGE[t * LP + s] * decay(R, t, s) : 0.f;
     }
     // gamma (.) Q and Kt, whole 64 rows
-    for (int i = threadIdx.x; i < DC * D; i += DTH) {
-        const int t = i / D, d = i % D;
-        const bool ok = t < n;
-        w.Qg[i] = ok ? R.gam[t] * to_f32(Q[t * rk + d]) : 0.f;
-        w.Kt[i] = ok ? R.kts[t] * to_f32(K[t * rk + d]) : 0.f;
-    }
+    ew(DC * D, [&](int i) { const int t = i / D; return t < n ? R.gam[t] * to_f32(Q[t * rk + i % D]) : 0.f; },
+       [&](int i, float v) { w.Qg[i] = v; });
+    ew(DC * D, [&](int i) { const int t = i / D; return t < n ? R.kts[t] * to_f32(sK[t * KP + i % D]) : 0.f; },
+       [&](int i, float v) { w.Kt[i] = v; });
     __syncthreads();
     // U = T (beta V), W = T (beta gamma K), with beta and beta gamma folded into the
     // columns of T; rows past n are 0 (T is the identity there and beta is 0)
@@ -264,8 +433,8 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
         sT[t * LP + s] *= R.beta[s];
     }
     __syncthreads();
-    mm<4>(DC, Dv, n, 1.f, sT, LP, 1, V, rv, 1, 0.f, w.U, Dv, 1);
-    mm<4>(DC, D, n, 1.f, sGE, LP, 1, K, rk, 1, 0.f, w.W, D, 1);
+    mmt(DC, Dv, n, 1.f, sT, LP, 1, V, rv, 1, 0.f, w.U, Dv, 1, smm);
+    mm<4>(DC, D, n, 1.f, sGE, LP, 1, sK, KP, 1, 0.f, w.W, D, 1);
 }
 
 // ---------------------------------------------------------------- state pass
@@ -288,14 +457,16 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
         const int n = (int)(a.T - t0 < DC ? a.T - t0 : DC);
         const float carry = w.carry[0];
         if (BWD)
-            for (int i = threadIdx.x; i < D * NSL; i += DTH) w.S0[(i / NSL) * Dv + j0 + i % NSL] = sS[i];
+            for (int i = threadIdx.x; i < D * NSL; i += DTH)  // S0 transposed: [value column][key row]
+                w.S0[(j0 + i / D) * D + i % D] = sS[(i % D) * NSL + i / D];
         // Wv = U - W S0
-        for (int i = threadIdx.x; i < DC * NSL; i += DTH) sWv[i] = w.U[(i / NSL) * Dv + j0 + i % NSL];
+        ew(DC * NSL, [&](int i) { return w.U[(i / NSL) * Dv + j0 + i % NSL]; }, [&](int i, float v) { sWv[i] = v; });
         __syncthreads();
         mm<2>(DC, NSL, D, -1.f, w.W, D, 1, sS, NSL, 1, 1.f, sWv, NSL, 1);
         __syncthreads();
         if (BWD) {
-            for (int i = threadIdx.x; i < DC * NSL; i += DTH) w.Wv[(i / NSL) * Dv + j0 + i % NSL] = sWv[i];
+            for (int i = threadIdx.x; i < DC * NSL; i += DTH)  // Wv transposed: [value column][row]
+                w.Wv[(j0 + i / DC) * DC + i % DC] = sWv[(i % DC) * NSL + i / DC];
         } else {
             // O = (gamma Q) S0 + P Wv
             mm<2>(DC, NSL, D, 1.f, w.Qg, D, 1, sS, NSL, 1, 0.f, sO, NSL, 1);
@@ -334,12 +505,14 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
         const int n = (int)(a.T - t0 < DC ? a.T - t0 : DC);
         const float carry = w.carry[0];
         const T* dO = (const T*)a.dO + (b * a.T + t0) * rv + h * Dv + j0;
-        for (int i = threadIdx.x; i < D * NSL; i += DTH) w.dS1[(i / NSL) * Dv + j0 + i % NSL] = sdS[i];
+        for (int i = threadIdx.x; i < D * NSL; i += DTH)  // dS1 transposed: [value column][key row]
+            w.dS1[(j0 + i / D) * D + i % D] = sdS[(i % D) * NSL + i / D];
         // dWv = P^T dO + Kt dS1
         mm<2>(DC, NSL, n, 1.f, w.P, 1, DC, dO, rv, 1, 0.f, sdWv, NSL, 1);
         mm<2>(DC, NSL, D, 1.f, w.Kt, D, 1, sdS, NSL, 1, 1.f, sdWv, NSL, 1);
         __syncthreads();
-        for (int i = threadIdx.x; i < DC * NSL; i += DTH) w.dWv[(i / NSL) * Dv + j0 + i % NSL] = sdWv[i];
+        for (int i = threadIdx.x; i < DC * NSL; i += DTH)  // dWv transposed: [value column][row]
+            w.dWv[(j0 + i / DC) * DC + i % DC] = sdWv[(i % DC) * NSL + i / DC];
         // dS0 = c dS1 + (gamma Q)^T dO - W^T dWv
         mm<2>(D, NSL, n, 1.f, w.Qg, 1, D, dO, rv, 1, carry, sdS, NSL, 1);
         mm<2>(D, NSL, DC, -1.f, w.W, 1, D, sdWv, NSL, 1, 1.f, sdS, NSL, 1);
@@ -353,8 +526,12 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
 template <typename T>
 __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __shared__ Rows R;
-    __shared__ float sGE[DC * LP], sT[DC * LP], sX[DC * LP], sY[DC * LP];
+    __shared__ float sGE[DC * LP], sT[DC * LP], sXY[2 * DC * LP];
+    float* sX = sXY;
+    float* sY = sXY + DC * LP;
+    T* sK = reinterpret_cast<T*>(sXY);  // (K rows for the inverse only; 64 x 129 fp32 fits)
     __shared__ float sdG[DC], sdB[DC], sr1[DC], sr2[DC], sdGC;
+    __shared__ float smm[MMT_LDS];
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
     const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
@@ -365,7 +542,6 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     const T* V = (const T*)a.v + (b * a.T + t0) * rv + h * Dv;
     const T* dO = (const T*)a.dO + (b * a.T + t0) * rv + h * Dv;
     prologue<T>(R, a, b, h, t0);
-    for (int i = threadIdx.x; i < DC * LP; i += DTH) sX[i] = 0.f;
     if (threadIdx.x < DC) {
         sdG[threadIdx.x] = 0.f;
         sdB[threadIdx.x] = 0.f;
@@ -373,16 +549,22 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     if (threadIdx.x == 0) sdGC = 0.f;
     __syncthreads();
     const int n = R.n;
-    wy_inverse<T>(R, K, rk, D, sGE, sT);
+    load_k<T>(R, K, rk, D, sK);
+    __syncthreads();
+    wy_inverse<T>(R, sK, D, sGE, sT);
+    for (int i = threadIdx.x; i < DC * LP; i += DTH) sX[i] = 0.f;  // (sK is dead)
+    __syncthreads();
     const ChunkWs w = chunk_ws(a, chunk);
+    // S0, Wv, dS1 and dWv are stored transposed ([value column][row]), so that
+    // every product below reads its B operand along rows.
 
     // (1) output: dQg = dO S0^T; dP = dO Wv^T
-    mm<4>(n, D, Dv, 1.f, dO, rv, 1, w.S0, 1, Dv, 0.f, w.gQ, D, 1);
-    mm<4>(n, n, Dv, 1.f, dO, rv, 1, w.Wv, 1, Dv, 0.f, sX, LP, 1);
+    mmt(n, D, Dv, 1.f, dO, rv, 1, w.S0, D, 1, 0.f, w.gQ, D, 1, smm);
+    mmt(n, n, Dv, 1.f, dO, rv, 1, w.Wv, DC, 1, 0.f, sX, LP, 1, smm);
     // (2) state: dKt = Wv dS1^T
-    mm<4>(n, D, Dv, 1.f, w.Wv, Dv, 1, w.dS1, 1, Dv, 0.f, w.gKt, D, 1);
-    // (3) dW = -dWv S0^T
-    mm<4>(DC, D, Dv, -1.f, w.dWv, Dv, 1, w.S0, 1, Dv, 0.f, w.gW, D, 1);
+    mmt(n, D, Dv, 1.f, w.Wv, 1, DC, w.dS1, D, 1, 0.f, w.gKt, D, 1, smm);
+    // (3) dW = -dWv S0^T, stored transposed ([key channel][row])
+    mmt(DC, D, Dv, -1.f, w.dWv, 1, DC, w.S0, D, 1, 0.f, w.gW, 1, DC, smm);
     __syncthreads();
     // dGamma from gamma Q: rowdot(dQg, Qg); from Kt: -rowdot(dKt, Kt) per row, + sum into dGamma_last
     rowdot(n, D, w.gQ, D, w.Qg, D, sdG, 1.f);
@@ -392,7 +574,17 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     // carry term: c <dS1, S0>
     {
         float s = 0.f;
-        for (int i = threadIdx.x; i < D * Dv; i += DTH) s += w.dS1[i] * w.S0[i];
+        for (int base = threadIdx.x; base < D * Dv; base += 8 * DTH) {
+            float x[8], y[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = base + u * DTH;
+                x[u] = i < D * Dv ? w.dS1[i] : 0.f;
+                y[u] = i < D * Dv ? w.S0[i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += x[u] * y[u];
+        }
         for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
         if ((threadIdx.x & 63) == 0) sr2[threadIdx.x >> 6] = s;
     }
@@ -403,14 +595,18 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
         sdGC = tot + R.carry * (sr2[0] + sr2[1] + sr2[2] + sr2[3]);
     }
     if (threadIdx.x < DC) sdG[threadIdx.x] -= sr1[threadIdx.x];
-    // dP (.) P -> dGamma (rows +, columns -); dP (.) M in sX
+    // dP (.) P -> dGamma (rows +, columns -); dP (.) M in sX.  The products
+    // dP (.) P go through sY (free here) so that P is read along rows.
+    __syncthreads();
+    ew(DC * DC, [&](int i) { return sX[(i / DC) * LP + i % DC] * w.P[i]; },
+       [&](int i, float v) { sY[(i / DC) * LP + i % DC] = v; });
     __syncthreads();
     if (threadIdx.x < DC) {
         const int t = threadIdx.x;
         float rsum = 0.f, csum = 0.f;
         for (int s = 0; s < DC; ++s) {
-            rsum += sX[t * LP + s] * w.P[t * DC + s];
-            csum += sX[s * LP + t] * w.P[s * DC + t];
+            rsum += sY[t * LP + s];
+            csum += sY[s * LP + t];
         }
         sr1[t] = rsum;
         sr2[t] = csum;
@@ -423,22 +619,23 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     }
     // dQ = gamma dQg (in place), then += (dP (.) M) K; dK = (dP (.) M)^T Q + Kt-scale dKt
     __syncthreads();
-    for (int i = threadIdx.x; i < DC * D; i += DTH) w.gQ[i] *= R.gam[i / D];
-    for (int i = threadIdx.x; i < DC * D; i += DTH) w.gK[i] = R.kts[i / D] * w.gKt[i];
+    ew(DC * D, [&](int i) { return w.gQ[i] * R.gam[i / D]; }, [&](int i, float v) { w.gQ[i] = v; });
+    ew(DC * D, [&](int i) { return R.kts[i / D] * w.gKt[i]; }, [&](int i, float v) { w.gK[i] = v; });
     __syncthreads();
-    mm<4>(n, D, n, 1.f, sX, LP, 1, K, rk, 1, 1.f, w.gQ, D, 1);
-    mm<4>(n, D, n, 1.f, sX, 1, LP, Q, rk, 1, 1.f, w.gK, D, 1);
+    mmt(n, D, n, 1.f, sX, LP, 1, K, rk, 1, 1.f, w.gQ, D, 1, smm);
+    mmt(n, D, n, 1.f, sX, 1, LP, Q, rk, 1, 1.f, w.gK, D, 1, smm);
     __syncthreads();
-    // (4) dT = dWv (beta V)^T + dW (beta gamma K)^T in sY
-    mm<4>(DC, n, Dv, 1.f, w.dWv, Dv, 1, V, 1, rv, 0.f, sY, LP, 1, R.beta);
-    __syncthreads();
-    mm<4>(DC, n, D, 1.f, w.gW, D, 1, K, 1, rk, 1.f, sY, LP, 1, R.bg);
+    // (4) dT = dWv (beta V)^T + dW (beta gamma K)^T in sY ([i][j]), formed as
+    //     dT^T = diag(beta) V dWv^T + diag(beta gamma) K dW^T
+    mmt(n, DC, Dv, 1.f, V, rv, 1, w.dWv, DC, 1, 0.f, sY, 1, LP, smm, nullptr, R.beta);
+    mmt(n, DC, D, 1.f, K, rk, 1, w.gW, DC, 1, 1.f, sY, 1, LP, smm, nullptr, R.bg);
     __syncthreads();
     for (int i = threadIdx.x; i < DC * LP; i += DTH)
         if (i % LP >= n && i % LP < DC) sY[i] = 0.f;
-    // dVb = T^T dWv, dKb = T^T dW (before sT is consumed)
-    mm<4>(n, Dv, DC, 1.f, sT, 1, LP, w.dWv, Dv, 1, 0.f, w.gV, Dv, 1);
-    mm<4>(n, D, DC, 1.f, sT, 1, LP, w.gW, D, 1, 0.f, w.gKb, D, 1);
+    // dVb = T^T dWv, dKb = T^T dW (before sT is consumed), formed transposed:
+    //     dVb^T = dWv^T T, dKb^T = dW^T T
+    mmt(Dv, n, DC, 1.f, w.dWv, DC, 1, sT, LP, 1, 0.f, w.gV, 1, Dv, smm);
+    mmt(D, n, DC, 1.f, w.gW, DC, 1, sT, LP, 1, 0.f, w.gKb, 1, D, smm);
     __syncthreads();
     // (5) dA = -T^T dT T^T: sX = dT T^T, then sY = -T^T sX
     mm<4>(DC, DC, DC, 1.f, sY, LP, 1, sT, 1, LP, 0.f, sX, LP, 1);
@@ -469,9 +666,8 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     }
     __syncthreads();
     // dK += (dG + dG^T) K
-    mm<4>(n, D, n, 1.f, sX, LP, 1, K, rk, 1, 1.f, w.gK, D, 1);
-    __syncthreads();
-    mm<4>(n, D, n, 1.f, sX, 1, LP, K, rk, 1, 1.f, w.gK, D, 1);
+    mmt(n, D, n, 1.f, sX, LP, 1, K, rk, 1, 1.f, w.gK, D, 1, smm);
+    mmt(n, D, n, 1.f, sX, 1, LP, K, rk, 1, 1.f, w.gK, D, 1, smm);
     __syncthreads();
     // (6) dV = beta dVb; dbeta += V . dVb + gamma K . dKb; dK += beta gamma dKb;
     //     dGamma += beta gamma K . dKb
@@ -486,7 +682,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
         sdB[t] += sr1[t] + R.gam[t] * sr2[t];
         sdG[t] += R.bg[t] * sr2[t];
     }
-    for (int i = threadIdx.x; i < DC * D; i += DTH) w.gK[i] += R.bg[i / D] * w.gKb[i];
+    ew(DC * D, [&](int i) { return w.gK[i] + R.bg[i / D] * w.gKb[i]; }, [&](int i, float v) { w.gK[i] = v; });
     __syncthreads();
     // (7) the gate: dGamma_last goes to the last row; dg_u = sum of dGamma over t >= u
     //     in u's document; 0 at reset rows
@@ -507,15 +703,10 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     T* dq = (T*)a.dq + row0 * rk + h * D;
     T* dk = (T*)a.dk_out + row0 * rk + h * D;
     T* dv = (T*)a.dv_out + row0 * rv + h * Dv;
-    for (int i = threadIdx.x; i < n * D; i += DTH) {
-        const int t = i / D, d = i % D;
-        dq[t * rk + d] = from_f32<T>(w.gQ[i]);
-        dk[t * rk + d] = from_f32<T>(w.gK[i]);
-    }
-    for (int i = threadIdx.x; i < n * Dv; i += DTH) {
-        const int t = i / Dv, d = i % Dv;
-        dv[t * rv + d] = from_f32<T>(R.beta[t] * w.gV[i]);
-    }
+    ew(n * D, [&](int i) { return w.gQ[i]; }, [&](int i, float v) { dq[(i / D) * rk + i % D] = from_f32<T>(v); });
+    ew(n * D, [&](int i) { return w.gK[i]; }, [&](int i, float v) { dk[(i / D) * rk + i % D] = from_f32<T>(v); });
+    ew(n * Dv, [&](int i) { return R.beta[i / Dv] * w.gV[i]; },
+       [&](int i, float v) { dv[(i / Dv) * rv + i % Dv] = from_f32<T>(v); });
 }
 
 }  // namespace
