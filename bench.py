@@ -566,8 +566,11 @@ def delta_main(args):
     ff, fb = delta_flops(T, 64, dk, dv)
     ff, fb = ff * B * H, fb * B * H
     achieved = fb / (bwd_us * 1e-6) / 1e12
+    traffic = measured_traffic("delta", "traffic_bytes_per_gla_delta_bwd")
     roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK["valu_f32"], "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK["valu_f32"], 4), "traffic": None,
+            "frac": round(achieved / PEAK["valu_f32"], 4),
+            "traffic": None if traffic is None else round(traffic / 1e6, 1),
+            "traffic_unit": "MB per gla_delta_bwd call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flops": round(fb / 1e9, 2),
             "kernel": "gla_delta_bwd (its four kernels, one call): fp32 products on the vector ALUs",
             "step_frac": round((ff + fb) / ((fwd_us + bwd_us) * 1e-6) / 1e12 / PEAK["valu_f32"], 4)}
