@@ -43,7 +43,7 @@ namespace gla {
 namespace {
 
 constexpr int DC = 64;     // rows per chunk
-constexpr int DTH = 256;   // threads per workgroup
+constexpr int DTH = 512;   // threads per workgroup (8 waves)
 constexpr int NSL = 16;    // value columns per workgroup of the sequential passes
 constexpr int LP = 65;     // LDS pitch of 64 x 64 matrices
 
@@ -117,8 +117,8 @@ __device__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, in
 // next tile's loads are issued before the current tile is used.  Every thread
 // accumulates up to NBT blocks of 4 x 4 (M N <= 4096 NBT), M, N <= 128.  `lds`
 // holds MMT_LDS floats.  Contains barriers: every thread of the workgroup calls it.
-constexpr int KT = 32, MMT_LDS = 128 * (KT + 1) + KT * (128 + 1), LDE = 16;
-template <int NBT = 2, typename TA, typename TB>
+constexpr int KT = 32, MMT_LDS = 128 * (KT + 1) + KT * (128 + 1), LDE = 128 * KT / DTH;
+template <int NBT = 1, typename TA, typename TB>
 __device__ void mmt(int M, int N, int K, float alpha, const TA* A, int64_t ai64, int64_t ak64, const TB* B,
                     int64_t bk64, int64_t bj64, float beta, float* C, int64_t ci, int64_t cj, float* lds,
                     const float* sj = nullptr, const float* si = nullptr) {
@@ -592,7 +592,9 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     if (threadIdx.x == 0) {
         float tot = 0.f;
         for (int t = 0; t < n; ++t) tot += sr1[t];
-        sdGC = tot + R.carry * (sr2[0] + sr2[1] + sr2[2] + sr2[3]);
+        float cs = 0.f;
+        for (int wv = 0; wv < DTH / 64; ++wv) cs += sr2[wv];
+        sdGC = tot + R.carry * cs;
     }
     if (threadIdx.x < DC) sdG[threadIdx.x] -= sr1[threadIdx.x];
     // dP (.) P -> dGamma (rows +, columns -); dP (.) M in sX.  The products
