@@ -54,9 +54,9 @@ constexpr int LP = 65;     // LDS pitch of 64 x 64 matrices
 // column blocks, so B reads coalesce when bj = 1.  No barrier inside: the
 // caller synchronises.
 template <int R, typename TA, typename TB>
-__device__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, int64_t ak, const TB* B,
-                   int64_t bk, int64_t bj, float beta, float* C, int64_t ci, int64_t cj,
-                   const float* sj = nullptr, const float* si = nullptr) {
+__device__ __forceinline__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, int64_t ak,
+                                   const TB* B, int64_t bk, int64_t bj, float beta, float* C, int64_t ci,
+                                   int64_t cj, const float* sj = nullptr, const float* si = nullptr) {
     const int nbi = (M + R - 1) / R, nbj = (N + R - 1) / R;
     for (int blk = threadIdx.x; blk < nbi * nbj; blk += DTH) {
         const int i0 = (blk / nbj) * R, j0 = (blk % nbj) * R;
@@ -119,7 +119,7 @@ __device__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, in
 // holds MMT_LDS floats.  Contains barriers: every thread of the workgroup calls it.
 constexpr int KT = 32, MMT_LDS = 128 * (KT + 1) + KT * (128 + 1), LDE = 128 * KT / DTH;
 template <int NBT = 1, typename TA, typename TB>
-__device__ void mmt(int M, int N, int K, float alpha, const TA* A, int64_t ai64, int64_t ak64, const TB* B,
+__device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* A, int64_t ai64, int64_t ak64, const TB* B,
                     int64_t bk64, int64_t bj64, float beta, float* C, int64_t ci, int64_t cj, float* lds,
                     const float* sj = nullptr, const float* si = nullptr) {
     // (offsets within one chunk's operands fit in 32 bits)
@@ -238,7 +238,7 @@ __device__ __forceinline__ void ew(int n, L ld, S st) {
 
 // out[t] += sign * sum_d X[t*lx + d] Y[t*ly + d] for t < n: one wave per row
 template <typename TX, typename TY>
-__device__ void rowdot(int n, int D, const TX* X, int64_t lx, const TY* Y, int64_t ly, float* out,
+__device__ __forceinline__ void rowdot(int n, int D, const TX* X, int64_t lx, const TY* Y, int64_t ly, float* out,
                        float sign) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     for (int t = wv; t < n; t += DTH / 64) {
@@ -265,7 +265,7 @@ struct Rows {
 
 // Row prologue (wave 0).  g, beta: [B][T][H]; seg: [B][T] or null.
 template <typename T>
-__device__ void prologue(Rows& R, const DeltaArgs& a, int64_t b, int64_t h, int64_t t0) {
+__device__ __forceinline__ void prologue(Rows& R, const DeltaArgs& a, int64_t b, int64_t h, int64_t t0) {
     if (threadIdx.x >= 64) return;
     const int t = threadIdx.x;
     const int64_t T_ = a.T;
@@ -316,7 +316,7 @@ template <typename T> __device__ __forceinline__ int kpitch(int D) { return D + 
 
 // the chunk's K rows into LDS (rows past n zero)
 template <typename T>
-__device__ void load_k(const Rows& R, const T* K, int64_t rs, int D, T* sK) {
+__device__ __forceinline__ void load_k(const Rows& R, const T* K, int64_t rs, int D, T* sK) {
     const int KP = kpitch<T>(D), n = R.n;
     ew(DC * D, [&](int i) { const int t = i / D; return t < n ? to_f32(K[t * rs + i % D]) : 0.f; },
        [&](int i, float v) { sK[(i / D) * KP + i % D] = from_f32<T>(v); });
@@ -326,7 +326,7 @@ __device__ void load_k(const Rows& R, const T* K, int64_t rs, int D, T* sK) {
 // T = (I + diag(beta) GE)^-1 by forward substitution (lane j builds column j).
 // sK: the chunk's K rows (load_k), complete before the call.
 template <typename T>
-__device__ void wy_inverse(const Rows& R, const T* sK, int D, float* sGE, float* sT) {
+__device__ __forceinline__ void wy_inverse(const Rows& R, const T* sK, int D, float* sGE, float* sT) {
     const int n = R.n, KP = kpitch<T>(D);
     for (int i = threadIdx.x; i < DC * LP; i += DTH) sGE[i] = 0.f;
     __syncthreads();
@@ -360,7 +360,7 @@ struct ChunkWs {
     float *T, *U, *W, *P, *Qg, *Kt, *carry, *S0, *Wv, *dS1, *dWv, *gQ, *gK, *gKt, *gW, *gV, *gKb;
 };
 
-__device__ ChunkWs chunk_ws(const DeltaArgs& a, int64_t chunk) {
+__device__ __forceinline__ ChunkWs chunk_ws(const DeltaArgs& a, int64_t chunk) {
     const int64_t D = a.dk, Dv = a.dv;
     float* p = a.ws + chunk * a.ws_chunk;
     ChunkWs w;
