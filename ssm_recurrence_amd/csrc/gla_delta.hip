@@ -309,9 +309,10 @@ __device__ __forceinline__ float decay(const Rows& R, int t, int s) {  // E / M 
     return R.doc[t] >= 0 && R.doc[t] == R.doc[s] ? __expf(R.G[t] - R.G[s]) : 0.f;
 }
 
-// K tile in LDS: rows at an odd number of dwords apart, so that reading a
-// column (one element per row) across lanes is free of bank conflicts
-template <typename T> constexpr int kpad() { return sizeof(T) == 2 ? 2 : 1; }
+// K tile in LDS.  bf16: rows 16 bytes apart plus 16 (whole 16-byte fragments
+// for the matrix cores, rows spread over the banks); fp32: an odd number of
+// dwords apart (a column read across lanes is free of bank conflicts).
+template <typename T> constexpr int kpad() { return sizeof(T) == 2 ? 8 : 1; }
 template <typename T> __device__ __forceinline__ int kpitch(int D) { return D + kpad<T>(); }
 
 // the chunk's K rows into LDS (rows past n zero)
@@ -322,15 +323,32 @@ __device__ __forceinline__ void load_k(const Rows& R, const T* K, int64_t rs, in
        [&](int i, float v) { sK[(i / D) * KP + i % D] = from_f32<T>(v); });
 }
 
+// G = K K^T (64 x 64, all rows; rows past n are zero in sK) on the matrix cores:
+// 16 tiles of 16 x 16, K fragments read straight from the LDS tile.
+template <typename T, int D>
+__device__ __forceinline__ void gram_mfma(const T* sK, float* sG) {
+    constexpr int KP = D + kpad<T>();
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    for (int t = w; t < 16; t += DTH / 64) {
+        const int i0 = (t >> 2) * 16, j0 = (t & 3) * 16;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += Mma<T>::KSTEP)
+            acc = Mma<T>::mma(frag_ld<T, KP, 1>(sK, i0, k0), frag_ld<T, KP, 1>(sK, j0, k0), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sG[(i0 + 4 * (l >> 4) + e) * LP + j0 + (l & 15)] = acc[e];
+    }
+}
+
 // GE = (K K^T) (.) E strictly below the diagonal (LDS, pitch LP), and
 // T = (I + diag(beta) GE)^-1 by forward substitution (lane j builds column j).
 // sK: the chunk's K rows (load_k), complete before the call.
 template <typename T>
 __device__ __forceinline__ void wy_inverse(const Rows& R, const T* sK, int D, float* sGE, float* sT) {
-    const int n = R.n, KP = kpitch<T>(D);
-    for (int i = threadIdx.x; i < DC * LP; i += DTH) sGE[i] = 0.f;
-    __syncthreads();
-    mm<4>(n, n, D, 1.f, sK, KP, 1, sK, 1, KP, 0.f, sGE, LP, 1);
+    if (D == 128)
+        gram_mfma<T, 128>(sK, sGE);
+    else
+        gram_mfma<T, 64>(sK, sGE);
     __syncthreads();
     for (int i = threadIdx.x; i < DC * DC; i += DTH) {
         const int t = i / DC, s = i % DC;
@@ -389,7 +407,7 @@ template <typename T>
 __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     __shared__ Rows R;
     __shared__ float sGE[DC * LP], sT[DC * LP];
-    __shared__ T sK[DC * (128 + kpad<T>())];
+    __shared__ __attribute__((aligned(16))) T sK[DC * (128 + kpad<T>())];
     __shared__ float smm[MMT_LDS];
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
@@ -526,7 +544,8 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
 template <typename T>
 __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __shared__ Rows R;
-    __shared__ float sGE[DC * LP], sT[DC * LP], sXY[2 * DC * LP];
+    __shared__ float sGE[DC * LP], sT[DC * LP];
+    __shared__ __attribute__((aligned(16))) float sXY[2 * DC * LP];
     float* sX = sXY;
     float* sY = sXY + DC * LP;
     T* sK = reinterpret_cast<T*>(sXY);  // (K rows for the inverse only; 64 x 129 fp32 fits)
