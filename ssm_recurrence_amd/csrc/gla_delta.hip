@@ -69,6 +69,7 @@ __device__ __forceinline__ void mm(int M, int N, int K, float alpha, const TA* A
         // covers KU steps' latency (operands often come from L2)
         constexpr int KU = R >= 4 ? 4 : 8;
         int k = 0;
+#pragma unroll 1
         for (; k + KU <= K; k += KU) {
             float a[KU][R], b[KU][R];
 #pragma unroll
@@ -85,6 +86,7 @@ __device__ __forceinline__ void mm(int M, int N, int K, float alpha, const TA* A
 #pragma unroll
                     for (int w = 0; w < R; ++w) acc[u][w] += a[kk][u] * b[kk][w];
         }
+#pragma unroll 1
         for (; k < K; ++k) {
             float a[R], b[R];
 #pragma unroll
@@ -455,11 +457,49 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     mm<4>(DC, D, n, 1.f, sGE, LP, 1, sK, KP, 1, 0.f, w.W, D, 1);
 }
 
-// ---------------------------------------------------------------- state pass
-template <typename T, bool BWD>
+// ---------------------------------------------------------------- sequential passes
+// The operands a chunk needs are staged through registers: the next chunk's
+// values are loaded while the current chunk computes, then written to LDS in one
+// pass.  LDS layout (floats): W [64][D], Kt [64][D], then (QP) gamma Q [64][D] and
+// P [64][64], then a [64][16] column slice (U, or dO).  Every segment is a
+// multiple of the workgroup size, so each register holds one segment's element.
+template <int D, bool QP> struct SeqLayout {
+    static constexpr int W = 0, KT_ = DC * D, QG = 2 * DC * D;
+    static constexpr int P = QP ? 3 * DC * D : 2 * DC * D;
+    static constexpr int SL = QP ? P + DC * DC : P;
+    static constexpr int TOTAL = SL + DC * NSL;
+    static constexpr int NPF = TOTAL / DTH;
+    static_assert(TOTAL % DTH == 0 && (DC * D) % DTH == 0 && (DC * NSL) % DTH == 0, "segments");
+};
+
+// slice(row, col) gives the [64][16] slice's element (row < 64)
+template <int D, bool QP, typename SliceF>
+__device__ __forceinline__ void seq_fetch(float* pf, const ChunkWs& w, SliceF slice) {
+    using L = SeqLayout<D, QP>;
+#pragma unroll
+    for (int u = 0; u < L::NPF; ++u) {
+        const int e = u * DTH + (int)threadIdx.x;
+        if (u * DTH < L::KT_) pf[u] = w.W[e];
+        else if (u * DTH < L::QG) pf[u] = w.Kt[e - L::KT_];
+        else if (QP && u * DTH < L::P) pf[u] = w.Qg[e - L::QG];
+        else if (QP && u * DTH < L::SL) pf[u] = w.P[e - L::P];
+        else pf[u] = slice((e - L::SL) / NSL, (e - L::SL) % NSL);
+    }
+}
+
+template <int D, bool QP>
+__device__ __forceinline__ void seq_stash(const float* pf, float* sBuf) {
+#pragma unroll
+    for (int u = 0; u < SeqLayout<D, QP>::NPF; ++u) sBuf[u * DTH + threadIdx.x] = pf[u];
+}
+
+// state pass (chunks in order): o and hT, or (BWD) S0 and Wv of every chunk
+template <typename T, bool BWD, int D>
 __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
-    __shared__ float sS[128 * NSL], sWv[DC * NSL], sO[DC * NSL];
-    const int D = (int)a.dk, Dv = (int)a.dv;
+    using L = SeqLayout<D, !BWD>;
+    __shared__ float sBuf[L::TOTAL];
+    __shared__ float sS[D * NSL], sWv[DC * NSL], sO[DC * NSL];
+    const int Dv = (int)a.dv;
     const int nsl = Dv / NSL;
     const int64_t bh = blockIdx.x / nsl, j0 = (blockIdx.x % nsl) * NSL;
     const int64_t b = bh / a.H, h = bh % a.H;
@@ -468,45 +508,59 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
         const int r = i / NSL, j = i % NSL;
         sS[i] = a.h0 ? a.h0[(bh * D + r) * Dv + j0 + j] : 0.f;
     }
-    __syncthreads();
+    float pf[L::NPF];
+    float carry_next;
+    auto fetch = [&](int64_t c) {
+        const ChunkWs w = chunk_ws(a, bh * NC + c);
+        seq_fetch<D, !BWD>(pf, w, [&](int r, int j) { return w.U[r * Dv + j0 + j]; });
+        carry_next = w.carry[0];
+    };
+    fetch(0);
     for (int64_t c = 0; c < NC; ++c) {
         const ChunkWs w = chunk_ws(a, bh * NC + c);
         const int64_t t0 = c * DC;
         const int n = (int)(a.T - t0 < DC ? a.T - t0 : DC);
-        const float carry = w.carry[0];
+        const float carry = carry_next;
+        __syncthreads();  // (the previous chunk no longer reads sBuf; sS is complete)
+        seq_stash<D, !BWD>(pf, sBuf);
         if (BWD)
             for (int i = threadIdx.x; i < D * NSL; i += DTH)  // S0 transposed: [value column][key row]
                 w.S0[(j0 + i / D) * D + i % D] = sS[(i % D) * NSL + i / D];
-        // Wv = U - W S0
-        ew(DC * NSL, [&](int i) { return w.U[(i / NSL) * Dv + j0 + i % NSL]; }, [&](int i, float v) { sWv[i] = v; });
         __syncthreads();
-        mm<2>(DC, NSL, D, -1.f, w.W, D, 1, sS, NSL, 1, 1.f, sWv, NSL, 1);
+        if (c + 1 < NC) fetch(c + 1);
+        // Wv = U - W S0
+        for (int i = threadIdx.x; i < DC * NSL; i += DTH) sWv[i] = sBuf[L::SL + i];
+        __syncthreads();
+        mm<2>(DC, NSL, D, -1.f, sBuf + L::W, D, 1, sS, NSL, 1, 1.f, sWv, NSL, 1);
         __syncthreads();
         if (BWD) {
             for (int i = threadIdx.x; i < DC * NSL; i += DTH)  // Wv transposed: [value column][row]
                 w.Wv[(j0 + i / DC) * DC + i % DC] = sWv[(i % DC) * NSL + i / DC];
         } else {
             // O = (gamma Q) S0 + P Wv
-            mm<2>(DC, NSL, D, 1.f, w.Qg, D, 1, sS, NSL, 1, 0.f, sO, NSL, 1);
-            mm<2>(DC, NSL, DC, 1.f, w.P, DC, 1, sWv, NSL, 1, 1.f, sO, NSL, 1);
+            mm<2>(DC, NSL, D, 1.f, sBuf + L::QG, D, 1, sS, NSL, 1, 0.f, sO, NSL, 1);
+            mm<2>(DC, NSL, DC, 1.f, sBuf + L::P, DC, 1, sWv, NSL, 1, 1.f, sO, NSL, 1);
             __syncthreads();
             T* o = (T*)a.o + (b * a.T + t0) * a.H * Dv + h * Dv + j0;
             for (int i = threadIdx.x; i < n * NSL; i += DTH)
                 o[(i / NSL) * a.H * Dv + i % NSL] = from_f32<T>(sO[i]);
         }
         // S1 = c S0 + Kt^T Wv
-        mm<2>(D, NSL, DC, 1.f, w.Kt, 1, D, sWv, NSL, 1, carry, sS, NSL, 1);
-        __syncthreads();
+        mm<2>(D, NSL, DC, 1.f, sBuf + L::KT_, 1, D, sWv, NSL, 1, carry, sS, NSL, 1);
     }
+    __syncthreads();
     if (!BWD && a.hT)
         for (int i = threadIdx.x; i < D * NSL; i += DTH) a.hT[(bh * D + i / NSL) * Dv + j0 + i % NSL] = sS[i];
 }
 
-// ---------------------------------------------------------------- reverse state-gradient pass
-template <typename T>
+// reverse state-gradient pass (chunks last to first): dS1 and dWv of every
+// chunk, then dh0
+template <typename T, int D>
 __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
-    __shared__ float sdS[128 * NSL], sdWv[DC * NSL];
-    const int D = (int)a.dk, Dv = (int)a.dv;
+    using L = SeqLayout<D, true>;
+    __shared__ float sBuf[L::TOTAL];
+    __shared__ float sdS[D * NSL], sdWv[DC * NSL];
+    const int Dv = (int)a.dv;
     const int nsl = Dv / NSL;
     const int64_t bh = blockIdx.x / nsl, j0 = (blockIdx.x % nsl) * NSL;
     const int64_t b = bh / a.H, h = bh % a.H;
@@ -516,26 +570,37 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
         const int r = i / NSL, j = i % NSL;
         sdS[i] = a.dhT ? a.dhT[(bh * D + r) * Dv + j0 + j] : 0.f;
     }
-    __syncthreads();
-    for (int64_t c = NC - 1; c >= 0; --c) {
+    float pf[L::NPF];
+    float carry_next;
+    auto fetch = [&](int64_t c) {
         const ChunkWs w = chunk_ws(a, bh * NC + c);
         const int64_t t0 = c * DC;
         const int n = (int)(a.T - t0 < DC ? a.T - t0 : DC);
-        const float carry = w.carry[0];
         const T* dO = (const T*)a.dO + (b * a.T + t0) * rv + h * Dv + j0;
+        seq_fetch<D, true>(pf, w, [&](int r, int j) { return r < n ? to_f32(dO[r * rv + j]) : 0.f; });
+        carry_next = w.carry[0];
+    };
+    fetch(NC - 1);
+    for (int64_t c = NC - 1; c >= 0; --c) {
+        const ChunkWs w = chunk_ws(a, bh * NC + c);
+        const float carry = carry_next;
+        __syncthreads();
+        seq_stash<D, true>(pf, sBuf);
         for (int i = threadIdx.x; i < D * NSL; i += DTH)  // dS1 transposed: [value column][key row]
             w.dS1[(j0 + i / D) * D + i % D] = sdS[(i % D) * NSL + i / D];
-        // dWv = P^T dO + Kt dS1
-        mm<2>(DC, NSL, n, 1.f, w.P, 1, DC, dO, rv, 1, 0.f, sdWv, NSL, 1);
-        mm<2>(DC, NSL, D, 1.f, w.Kt, D, 1, sdS, NSL, 1, 1.f, sdWv, NSL, 1);
+        __syncthreads();
+        if (c > 0) fetch(c - 1);
+        // dWv = P^T dO + Kt dS1 (the dO slice is zero past the end)
+        mm<2>(DC, NSL, DC, 1.f, sBuf + L::P, 1, DC, sBuf + L::SL, NSL, 1, 0.f, sdWv, NSL, 1);
+        mm<2>(DC, NSL, D, 1.f, sBuf + L::KT_, D, 1, sdS, NSL, 1, 1.f, sdWv, NSL, 1);
         __syncthreads();
         for (int i = threadIdx.x; i < DC * NSL; i += DTH)  // dWv transposed: [value column][row]
             w.dWv[(j0 + i / DC) * DC + i % DC] = sdWv[(i % DC) * NSL + i / DC];
         // dS0 = c dS1 + (gamma Q)^T dO - W^T dWv
-        mm<2>(D, NSL, n, 1.f, w.Qg, 1, D, dO, rv, 1, carry, sdS, NSL, 1);
-        mm<2>(D, NSL, DC, -1.f, w.W, 1, D, sdWv, NSL, 1, 1.f, sdS, NSL, 1);
-        __syncthreads();
+        mm<2>(D, NSL, DC, 1.f, sBuf + L::QG, 1, D, sBuf + L::SL, NSL, 1, carry, sdS, NSL, 1);
+        mm<2>(D, NSL, DC, -1.f, sBuf + L::W, 1, D, sdWv, NSL, 1, 1.f, sdS, NSL, 1);
     }
+    __syncthreads();
     if (a.dh0)
         for (int i = threadIdx.x; i < D * NSL; i += DTH) a.dh0[(bh * D + i / NSL) * Dv + j0 + i % NSL] = sdS[i];
 }
@@ -742,7 +807,11 @@ hipError_t launch_delta_fwd(const DeltaArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_delta_prep<T>, dim3((unsigned)(a.B * a.H * NC)), dim3(DTH), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_delta_state<T, false>), dim3((unsigned)(a.B * a.H * (a.dv / NSL))), dim3(DTH), 0, st, a);
+    const dim3 slices((unsigned)(a.B * a.H * (a.dv / NSL)));
+    if (a.dk == 128)
+        hipLaunchKernelGGL((k_delta_state<T, false, 128>), slices, dim3(DTH), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_delta_state<T, false, 64>), slices, dim3(DTH), 0, st, a);
     return hipGetLastError();
 }
 
@@ -753,9 +822,15 @@ hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_delta_prep<T>, chunks, dim3(DTH), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_delta_state<T, true>), slices, dim3(DTH), 0, st, a);
+    if (a.dk == 128)
+        hipLaunchKernelGGL((k_delta_state<T, true, 128>), slices, dim3(DTH), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_delta_state<T, true, 64>), slices, dim3(DTH), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_delta_dstate<T>, slices, dim3(DTH), 0, st, a);
+    if (a.dk == 128)
+        hipLaunchKernelGGL((k_delta_dstate<T, 128>), slices, dim3(DTH), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_delta_dstate<T, 64>), slices, dim3(DTH), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_delta_grad<T>, chunks, dim3(DTH), 0, st, a);
     return hipGetLastError();
