@@ -25,7 +25,8 @@
 // is beta_t (v_t - S_{t-1}^T k_t), and S_{t-1} is the decayed S0 plus the
 // decayed earlier writes.
 //
-// Kernels (every product in fp32 on the vector ALUs, operands from LDS or L2):
+// Kernels (products in fp32 on the vector ALUs, operands from LDS or L2, except
+// the Gram matrix K K^T of the inverse, which runs on the matrix cores):
 //   k_delta_prep   per (b, h, chunk): the row prologue, T, U, W, the masked
 //                  scores P = (Q K^T) (.) M, gamma (.) Q, Kt, c.
 //   k_delta_state  per (b, h, 16 value columns): the chunks in order; o and hT,
@@ -202,15 +203,23 @@ __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* 
         const int blk = tid + q * DTH;
         if (blk < nblk) {
             const int i0 = (blk / nbj) * 4, j0 = (blk % nbj) * 4;
+            // (an accumulating call reads all 16 old values before its first store)
+            float old[4][4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int i = i0 + u, j = j0 + w;
+                    old[u][w] = beta != 0.f && i < M && j < N ? C[i * ci + j * cj] : 0.f;
+                }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const int i = i0 + u, j = j0 + w;
                     if (i < M && j < N) {
-                        float* c = C + i * ci + j * cj;
                         const float v = alpha * acc[q][u][w] * (sj ? sj[j] : 1.f) * (si ? si[i] : 1.f);
-                        *c = beta != 0.f ? v + beta * *c : v;
+                        C[i * ci + j * cj] = beta != 0.f ? v + beta * old[u][w] : v;
                     }
                 }
         }
