@@ -117,9 +117,9 @@ __device__ __forceinline__ void mm(int M, int N, int K, float alpha, const TA* A
 // The same product for operands in global memory (L2): k is taken in tiles of
 // KT; each tile of A (M x KT) and B (KT x N) is loaded by the whole workgroup
 // with the unit-stride index running across lanes, written to LDS, and the
-// next tile's loads are issued before the current tile is used.  Every thread
-// accumulates up to NBT blocks of 4 x 4 (M N <= 4096 NBT), M, N <= 128.  `lds`
-// holds MMT_LDS floats.  Contains barriers: every thread of the workgroup calls it.
+// next tile's loads are issued before the current tile is used; the products run
+// on the fp32 matrix cores.  M, N <= 128.  `lds` holds MMT_LDS floats.  Contains
+// barriers: every thread of the workgroup calls it.
 constexpr int KT = 32, MMT_LDS = 128 * (KT + 1) + KT * (128 + 1), LDE = 128 * KT / DTH;
 template <int NBT = 1, typename TA, typename TB>
 __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* A, int64_t ai64, int64_t ak64, const TB* B,
@@ -128,8 +128,8 @@ __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* 
     // (offsets within one chunk's operands fit in 32 bits)
     const int ai = (int)ai64, ak = (int)ak64, bk = (int)bk64, bj = (int)bj64;
     float* sa = lds;                    // [128][KT + 1]: sa[i][kk]
-    float* sb = lds + 128 * (KT + 1);   // [KT][N + 1]:   sb[kk][j]
-    const int NP = N + 1;
+    float* sb = lds + 128 * (KT + 1);   // [KT][128 + 1]: sb[kk][j]
+    constexpr int NP = 128 + 1;
     const int tid = threadIdx.x;
     const bool a_i_fast = ai == 1 && ak != 1;  // unit stride along i: lanes run along i
     const bool b_k_fast = bk == 1 && bj != 1;
@@ -163,14 +163,15 @@ __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* 
             if (j < N) sb[kb * NP + j] = rb[r];
         }
     };
-    const int nbj = (N + 3) / 4, nblk = ((M + 3) / 4) * nbj;
-    float acc[NBT][4][4];
+    // 16 x 16 output tiles on the fp32 matrix cores (full fp32 products and
+    // sums); wave w takes tiles w, w + 8, ...  Rows past M and columns past N of
+    // the LDS tiles hold stale values; they only reach outputs that are dropped.
+    const int wv = tid >> 6, l = tid & 63;
+    const int nti = (M + 15) / 16, ntj = (N + 15) / 16, ntiles = nti * ntj;
+    constexpr int TPW = 128 * 128 / 256 / (DTH / 64);  // tiles per wave at most
+    f32x4 acc[TPW];
 #pragma unroll
-    for (int q = 0; q < NBT; ++q)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) acc[q][u][w] = 0.f;
+    for (int q = 0; q < TPW; ++q) acc[q] = zero4();
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += KT) {
         __syncthreads();  // the previous tile is no longer read
@@ -178,50 +179,35 @@ __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* 
         __syncthreads();
         if (k0 + KT < K) fetch(k0 + KT);
 #pragma unroll
-        for (int q = 0; q < NBT; ++q) {
-            const int blk = tid + q * DTH;
-            if (blk < nblk) {
-                const int i0 = (blk / nbj) * 4, j0 = (blk % nbj) * 4;
-#pragma unroll 1
-                for (int kk = 0; kk < KT; ++kk) {
-                    float a[4], b[4];
+        for (int q = 0; q < TPW; ++q) {
+            const int t = wv + q * (DTH / 64);
+            if (t < ntiles) {
+                const int i0 = (t / ntj) * 16, j0 = (t % ntj) * 16;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        a[u] = sa[(i0 + u < 128 ? i0 + u : 127) * (KT + 1) + kk];
-                        b[u] = sb[kk * NP + (j0 + u < N ? j0 + u : N - 1)];
-                    }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) acc[q][u][w] += a[u] * b[w];
-                }
+                for (int kk = 0; kk < KT; kk += 4)
+                    acc[q] = Mma<float>::mma(frag_ld<float, KT + 1, 1>(sa, i0, kk),
+                                             frag_ld<float, 1, 128 + 1>(sb, j0, kk), acc[q]);
             }
         }
     }
+    // C layout: lane l holds rows 4 (l / 16) + e, column l % 16 of its tile
 #pragma unroll
-    for (int q = 0; q < NBT; ++q) {
-        const int blk = tid + q * DTH;
-        if (blk < nblk) {
-            const int i0 = (blk / nbj) * 4, j0 = (blk % nbj) * 4;
-            // (an accumulating call reads all 16 old values before its first store)
-            float old[4][4];
+    for (int q = 0; q < TPW; ++q) {
+        const int t = wv + q * (DTH / 64);
+        if (t < ntiles) {
+            const int i0 = (t / ntj) * 16 + 4 * (l >> 4), j = (t % ntj) * 16 + (l & 15);
+            float old[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int e = 0; e < 4; ++e)
+                old[e] = beta != 0.f && i0 + e < M && j < N ? C[(i0 + e) * ci + j * cj] : 0.f;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int i = i0 + u, j = j0 + w;
-                    old[u][w] = beta != 0.f && i < M && j < N ? C[i * ci + j * cj] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + e;
+                if (i < M && j < N) {
+                    const float v = alpha * acc[q][e] * (sj ? sj[j] : 1.f) * (si ? si[i] : 1.f);
+                    C[i * ci + j * cj] = beta != 0.f ? v + beta * old[e] : v;
                 }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int i = i0 + u, j = j0 + w;
-                    if (i < M && j < N) {
-                        const float v = alpha * acc[q][u][w] * (sj ? sj[j] : 1.f) * (si ? si[i] : 1.f);
-                        C[i * ci + j * cj] = beta != 0.f ? v + beta * old[u][w] : v;
-                    }
-                }
+            }
         }
     }
     __syncthreads();  // (lds free for the next call)
