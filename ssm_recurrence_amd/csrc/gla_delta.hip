@@ -454,17 +454,24 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
 
 // ---------------------------------------------------------------- sequential passes
 // The operands a chunk needs are staged through registers: the next chunk's
-// values are loaded while the current chunk computes, then written to LDS in one
-// pass.  LDS layout (floats): W [64][D], Kt [64][D], then (QP) gamma Q [64][D] and
-// P [64][64], then a [64][16] column slice (U, or dO).  Every segment is a
-// multiple of the workgroup size, so each register holds one segment's element.
+// values are loaded while the current chunk computes, then written to LDS.
+// Registers hold the segments back to back (W [64][D], Kt [64][D], then (QP)
+// gamma Q [64][D] and P [64][64], then a [64][16] column slice: U, or dO); every
+// segment is a multiple of the workgroup size, so each register holds one
+// segment's element.  In LDS the [64][D] and [64][64] segments get one padding
+// column, so that the matrix-core fragments (16 rows at once) spread over the banks.
 template <int D, bool QP> struct SeqLayout {
-    static constexpr int W = 0, KT_ = DC * D, QG = 2 * DC * D;
-    static constexpr int P = QP ? 3 * DC * D : 2 * DC * D;
-    static constexpr int SL = QP ? P + DC * DC : P;
-    static constexpr int TOTAL = SL + DC * NSL;
-    static constexpr int NPF = TOTAL / DTH;
-    static_assert(TOTAL % DTH == 0 && (DC * D) % DTH == 0 && (DC * NSL) % DTH == 0, "segments");
+    static constexpr int PD = D + 1, PP = DC + 1;
+    static constexpr int NW = DC * D, NPP = DC * DC, NS = DC * NSL;
+    // register (unpadded) offsets
+    static constexpr int UKT = NW, UQG = 2 * NW, UP = QP ? 3 * NW : 2 * NW, USL = QP ? UP + NPP : UP;
+    static constexpr int NPF = (USL + NS) / DTH;
+    // LDS (padded) offsets
+    static constexpr int W = 0, KT_ = DC * PD, QG = 2 * DC * PD;
+    static constexpr int P = QP ? 3 * DC * PD : 2 * DC * PD;
+    static constexpr int SL = QP ? P + DC * PP : P;
+    static constexpr int TOTAL = SL + NS;
+    static_assert(NW % DTH == 0 && NPP % DTH == 0 && NS % DTH == 0, "segments");
 };
 
 // slice(row, col) gives the [64][16] slice's element (row < 64)
@@ -474,18 +481,55 @@ __device__ __forceinline__ void seq_fetch(float* pf, const ChunkWs& w, SliceF sl
 #pragma unroll
     for (int u = 0; u < L::NPF; ++u) {
         const int e = u * DTH + (int)threadIdx.x;
-        if (u * DTH < L::KT_) pf[u] = w.W[e];
-        else if (u * DTH < L::QG) pf[u] = w.Kt[e - L::KT_];
-        else if (QP && u * DTH < L::P) pf[u] = w.Qg[e - L::QG];
-        else if (QP && u * DTH < L::SL) pf[u] = w.P[e - L::P];
-        else pf[u] = slice((e - L::SL) / NSL, (e - L::SL) % NSL);
+        if (u * DTH < L::UKT) pf[u] = w.W[e];
+        else if (u * DTH < L::UQG) pf[u] = w.Kt[e - L::UKT];
+        else if (QP && u * DTH < L::UP) pf[u] = w.Qg[e - L::UQG];
+        else if (QP && u * DTH < L::USL) pf[u] = w.P[e - L::UP];
+        else pf[u] = slice((e - L::USL) / NSL, (e - L::USL) % NSL);
     }
 }
 
 template <int D, bool QP>
 __device__ __forceinline__ void seq_stash(const float* pf, float* sBuf) {
+    using L = SeqLayout<D, QP>;
 #pragma unroll
-    for (int u = 0; u < SeqLayout<D, QP>::NPF; ++u) sBuf[u * DTH + threadIdx.x] = pf[u];
+    for (int u = 0; u < L::NPF; ++u) {
+        const int e = u * DTH + (int)threadIdx.x;
+        int a;
+        if (u * DTH < L::UKT) a = L::W + (e / D) * L::PD + e % D;
+        else if (u * DTH < L::UQG) a = L::KT_ + ((e - L::UKT) / D) * L::PD + (e - L::UKT) % D;
+        else if (QP && u * DTH < L::UP) a = L::QG + ((e - L::UQG) / D) * L::PD + (e - L::UQG) % D;
+        else if (QP && u * DTH < L::USL) a = L::P + ((e - L::UP) / DC) * L::PP + (e - L::UP) % DC;
+        else a = L::SL + (e - L::USL);
+        sBuf[a] = pf[u];
+    }
+}
+
+// C (M x N) = alpha A B + beta C with every operand in LDS, on the fp32 matrix
+// cores: A(i, k) = A[i*SIA + k*SKA], B(k, j) = B[k*SKB + j*SIB], C(i, j) =
+// C[i*CI + j]; M, N multiples of 16, K of 4.  Wave w computes tiles w, w + 8, ...
+// Each output element is read (beta) and written by one lane only.
+template <int M, int N, int K, int SIA, int SKA, int SIB, int SKB, int CI>
+__device__ __forceinline__ void mm_lds(float alpha, const float* A, const float* B, float beta, float* C) {
+    constexpr int NTJ = N / 16, NTILES = (M / 16) * NTJ;
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int t0 = 0; t0 < NTILES; t0 += DTH / 64) {
+        const int t = t0 + wv;
+        if (t < NTILES) {
+            const int i0 = (t / NTJ) * 16, j0 = (t % NTJ) * 16;
+            f32x4 acc = zero4();
+#pragma unroll 8
+            for (int k0 = 0; k0 < K; k0 += 4)
+                acc = Mma<float>::mma(frag_ld<float, SIA, SKA>(A, i0, k0), frag_ld<float, SIB, SKB>(B, j0, k0), acc);
+            const int r0 = i0 + 4 * (l >> 4), j = j0 + (l & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float* c = C + (r0 + e) * CI + j;
+                *c = beta != 0.f ? alpha * acc[e] + beta * *c : alpha * acc[e];
+            }
+        }
+    }
 }
 
 // state pass (chunks in order): o and hT, or (BWD) S0 and Wv of every chunk
@@ -526,22 +570,22 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
         // Wv = U - W S0
         for (int i = threadIdx.x; i < DC * NSL; i += DTH) sWv[i] = sBuf[L::SL + i];
         __syncthreads();
-        mm<2>(DC, NSL, D, -1.f, sBuf + L::W, D, 1, sS, NSL, 1, 1.f, sWv, NSL, 1);
+        mm_lds<DC, NSL, D, L::PD, 1, 1, NSL, NSL>(-1.f, sBuf + L::W, sS, 1.f, sWv);
         __syncthreads();
         if (BWD) {
             for (int i = threadIdx.x; i < DC * NSL; i += DTH)  // Wv transposed: [value column][row]
                 w.Wv[(j0 + i / DC) * DC + i % DC] = sWv[(i % DC) * NSL + i / DC];
         } else {
             // O = (gamma Q) S0 + P Wv
-            mm<2>(DC, NSL, D, 1.f, sBuf + L::QG, D, 1, sS, NSL, 1, 0.f, sO, NSL, 1);
-            mm<2>(DC, NSL, DC, 1.f, sBuf + L::P, DC, 1, sWv, NSL, 1, 1.f, sO, NSL, 1);
+            mm_lds<DC, NSL, D, L::PD, 1, 1, NSL, NSL>(1.f, sBuf + L::QG, sS, 0.f, sO);
+            mm_lds<DC, NSL, DC, L::PP, 1, 1, NSL, NSL>(1.f, sBuf + L::P, sWv, 1.f, sO);
             __syncthreads();
             T* o = (T*)a.o + (b * a.T + t0) * a.H * Dv + h * Dv + j0;
             for (int i = threadIdx.x; i < n * NSL; i += DTH)
                 o[(i / NSL) * a.H * Dv + i % NSL] = from_f32<T>(sO[i]);
         }
         // S1 = c S0 + Kt^T Wv
-        mm<2>(D, NSL, DC, 1.f, sBuf + L::KT_, 1, D, sWv, NSL, 1, carry, sS, NSL, 1);
+        mm_lds<D, NSL, DC, 1, L::PD, 1, NSL, NSL>(1.f, sBuf + L::KT_, sWv, carry, sS);
     }
     __syncthreads();
     if (!BWD && a.hT)
@@ -586,14 +630,14 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
         __syncthreads();
         if (c > 0) fetch(c - 1);
         // dWv = P^T dO + Kt dS1 (the dO slice is zero past the end)
-        mm<2>(DC, NSL, DC, 1.f, sBuf + L::P, 1, DC, sBuf + L::SL, NSL, 1, 0.f, sdWv, NSL, 1);
-        mm<2>(DC, NSL, D, 1.f, sBuf + L::KT_, D, 1, sdS, NSL, 1, 1.f, sdWv, NSL, 1);
+        mm_lds<DC, NSL, DC, 1, L::PP, 1, NSL, NSL>(1.f, sBuf + L::P, sBuf + L::SL, 0.f, sdWv);
+        mm_lds<DC, NSL, D, L::PD, 1, 1, NSL, NSL>(1.f, sBuf + L::KT_, sdS, 1.f, sdWv);
         __syncthreads();
         for (int i = threadIdx.x; i < DC * NSL; i += DTH)  // dWv transposed: [value column][row]
             w.dWv[(j0 + i / DC) * DC + i % DC] = sdWv[(i % DC) * NSL + i / DC];
         // dS0 = c dS1 + (gamma Q)^T dO - W^T dWv
-        mm<2>(D, NSL, DC, 1.f, sBuf + L::QG, 1, D, sBuf + L::SL, NSL, 1, carry, sdS, NSL, 1);
-        mm<2>(D, NSL, DC, -1.f, sBuf + L::W, 1, D, sdWv, NSL, 1, 1.f, sdS, NSL, 1);
+        mm_lds<D, NSL, DC, 1, L::PD, 1, NSL, NSL>(1.f, sBuf + L::QG, sBuf + L::SL, carry, sdS);
+        mm_lds<D, NSL, DC, 1, L::PD, 1, NSL, NSL>(-1.f, sBuf + L::W, sdWv, 1.f, sdS);
     }
     __syncthreads();
     if (a.dh0)
