@@ -25,8 +25,8 @@
 // is beta_t (v_t - S_{t-1}^T k_t), and S_{t-1} is the decayed S0 plus the
 // decayed earlier writes.
 //
-// Kernels (products in fp32 on the vector ALUs, operands from LDS or L2, except
-// the Gram matrix K K^T of the inverse, which runs on the matrix cores):
+// Kernels (products on the fp32 matrix cores, operands staged through LDS; the
+// Gram matrix K K^T of bf16 inputs on the bf16 matrix cores, exact products):
 //   k_delta_prep   per (b, h, chunk): the row prologue, T, U, W, the masked
 //                  scores P = (Q K^T) (.) M, gamma (.) Q, Kt, c.
 //   k_delta_state  per (b, h, 16 value columns): the chunks in order; o and hT,
