@@ -233,17 +233,32 @@ __device__ __forceinline__ void ew(int n, L ld, S st) {
     }
 }
 
-// out[t] += sign * sum_d X[t*lx + d] Y[t*ly + d] for t < n: one wave per row
+// out[t] += sign * sum_d X[t*lx + d] Y[t*ly + d] for t < n (D <= 128): wave w
+// takes rows w, w + 8, ...; all of a wave's loads are issued before its sums.
 template <typename TX, typename TY>
 __device__ __forceinline__ void rowdot(int n, int D, const TX* X, int64_t lx, const TY* Y, int64_t ly, float* out,
-                       float sign) {
+                                       float sign) {
+    constexpr int NWV = DTH / 64, RPW = DC / NWV;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    for (int t = wv; t < n; t += DTH / 64) {
-        float s = 0.f;
-        for (int d = lane; d < D; d += 64) s += to_f32(X[t * lx + d]) * to_f32(Y[t * ly + d]);
+    float x[RPW][2], y[RPW][2];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int t = wv + r * NWV;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int d = lane + 64 * h;
+            const bool ok = t < n && d < D;
+            x[r][h] = ok ? to_f32(X[t * lx + d]) : 0.f;
+            y[r][h] = ok ? to_f32(Y[t * ly + d]) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        float s = x[r][0] * y[r][0] + x[r][1] * y[r][1];
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-        if (lane == 0) out[t] += sign * s;
+        const int t = wv + r * NWV;
+        if (lane == 0 && t < n) out[t] += sign * s;
     }
 }
 
@@ -341,7 +356,7 @@ __device__ __forceinline__ void gram_mfma(const T* sK, float* sG) {
 // T = (I + diag(beta) GE)^-1 by forward substitution (lane j builds column j).
 // sK: the chunk's K rows (load_k), complete before the call.
 template <typename T>
-__device__ __forceinline__ void wy_inverse(const Rows& R, const T* sK, int D, float* sGE, float* sT) {
+__device__ __forceinline__ void gram_masked(const Rows& R, const T* sK, int D, float* sGE) {
     if (D == 128)
         gram_mfma<T, 128>(sK, sGE);
     else
@@ -352,6 +367,11 @@ __device__ __forceinline__ void wy_inverse(const Rows& R, const T* sK, int D, fl
         sGE[t * LP + s] = s < t ? sGE[t * LP + s] * decay(R, t, s) : 0.f;
     }
     __syncthreads();
+}
+
+template <typename T>
+__device__ __forceinline__ void wy_inverse(const Rows& R, const T* sK, int D, float* sGE, float* sT) {
+    gram_masked<T>(R, sK, D, sGE);
     if (threadIdx.x < DC) {
         // lane j keeps column j of T in registers; row i of GE is read as a
         // broadcast (every lane reads the same address)
@@ -673,11 +693,13 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __syncthreads();
     const int n = R.n;
     load_k<T>(R, K, rk, D, sK);
+    const ChunkWs w = chunk_ws(a, chunk);
+    // T as the prepare kernel stored it (this call's own prepare launch)
+    ew(DC * DC, [&](int i) { return w.T[i]; }, [&](int i, float v) { sT[(i / DC) * LP + i % DC] = v; });
     __syncthreads();
-    wy_inverse<T>(R, sK, D, sGE, sT);
+    gram_masked<T>(R, sK, D, sGE);
     for (int i = threadIdx.x; i < DC * LP; i += DTH) sX[i] = 0.f;  // (sK is dead)
     __syncthreads();
-    const ChunkWs w = chunk_ws(a, chunk);
     // S0, Wv, dS1 and dWv are stored transposed ([value column][row]), so that
     // every product below reads its B operand along rows.
 
@@ -763,9 +785,9 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     mmt(D, n, DC, 1.f, w.gW, DC, 1, sT, LP, 1, 0.f, w.gKb, 1, D, smm);
     __syncthreads();
     // (5) dA = -T^T dT T^T: sX = dT T^T, then sY = -T^T sX
-    mm<4>(DC, DC, DC, 1.f, sY, LP, 1, sT, 1, LP, 0.f, sX, LP, 1);
+    mm_lds<DC, DC, DC, LP, 1, LP, 1, LP>(1.f, sY, sT, 0.f, sX);
     __syncthreads();
-    mm<4>(DC, DC, DC, -1.f, sT, 1, LP, sX, LP, 1, 0.f, sY, LP, 1);
+    mm_lds<DC, DC, DC, 1, LP, 1, LP, LP>(-1.f, sT, sX, 0.f, sY);
     __syncthreads();
     // A = diag(beta) GE (strictly lower, same document): dbeta += sum_s dA GE; dGamma via
     // dA (.) A (rows +, columns -); dG = dA beta E in sX (strictly lower)
