@@ -419,12 +419,44 @@ __device__ __forceinline__ ChunkWs chunk_ws(const DeltaArgs& a, int64_t chunk) {
     return w;
 }
 
+// fp32 matrix-core operand fragment (lane i = l % 16, k = l / 16) from an LDS
+// tile of any element type: X(i0 + i, k0 + k), X(i, k) = base[i*SI + k*SK]
+template <int SI, int SK, typename TX>
+__device__ __forceinline__ float frag_f32(const TX* base, int i0, int k0) {
+    const int l = threadIdx.x & 63;
+    return to_f32(base[(i0 + (l & 15)) * SI + (k0 + (l >> 4)) * SK]);
+}
+
+template <int M, int N, int K, int SIA, int SKA, int SIB, int SKB, int CI, typename TA, typename TB>
+__device__ __forceinline__ void mm_lds(float alpha, const TA* A, const TB* B, float beta, float* C) {
+    constexpr int NTJ = N / 16, NTILES = (M / 16) * NTJ;
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int t0 = 0; t0 < NTILES; t0 += DTH / 64) {
+        const int t = t0 + wv;
+        if (t < NTILES) {
+            const int i0 = (t / NTJ) * 16, j0 = (t % NTJ) * 16;
+            f32x4 acc = zero4();
+#pragma unroll 8
+            for (int k0 = 0; k0 < K; k0 += 4)
+                acc = Mma<float>::mma(frag_f32<SIA, SKA>(A, i0, k0), frag_f32<SIB, SKB>(B, j0, k0), acc);
+            const int r0 = i0 + 4 * (l >> 4), j = j0 + (l & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float* c = C + (r0 + e) * CI + j;
+                *c = beta != 0.f ? alpha * acc[e] + beta * *c : alpha * acc[e];
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- prepare
 template <typename T>
 __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     __shared__ Rows R;
     __shared__ float sGE[DC * LP], sT[DC * LP];
     __shared__ __attribute__((aligned(16))) T sK[DC * (128 + kpad<T>())];
+    __shared__ __attribute__((aligned(16))) T sQ[DC * (128 + kpad<T>())];
     __shared__ float smm[MMT_LDS];
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
@@ -438,6 +470,7 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     __syncthreads();
     const int n = R.n;
     load_k<T>(R, K, rk, D, sK);
+    load_k<T>(R, Q, rk, D, sQ);  // (the same row loader)
     __syncthreads();
     wy_inverse<T>(R, sK, D, sGE, sT);
     ChunkWs w = chunk_ws(a, chunk);
@@ -445,17 +478,19 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     for (int i = threadIdx.x; i < DC * DC; i += DTH) w.T[i] = sT[(i / DC) * LP + i % DC];
     if (threadIdx.x == 0) w.carry[0] = R.carry;
     __syncthreads();
-    // P = (Q K^T) (.) M in sGE (reused), then copied whole
-    for (int i = threadIdx.x; i < DC * LP; i += DTH) sGE[i] = 0.f;
-    __syncthreads();
-    mmt(n, n, D, 1.f, Q, rk, 1, sK, 1, KP, 0.f, sGE, LP, 1, smm);
+    // P = (Q K^T) (.) M in sGE (reused), then copied whole; rows past n are zero
+    // in both tiles
+    if (D == 128)
+        mm_lds<DC, DC, 128, 128 + kpad<T>(), 1, 128 + kpad<T>(), 1, LP>(1.f, sQ, sK, 0.f, sGE);
+    else
+        mm_lds<DC, DC, 64, 64 + kpad<T>(), 1, 64 + kpad<T>(), 1, LP>(1.f, sQ, sK, 0.f, sGE);
     __syncthreads();
     for (int i = threadIdx.x; i < DC * DC; i += DTH) {
         const int t = i / DC, s = i % DC;
         w.P[i] = s <= t ? sGE[t * LP + s] * decay(R, t, s) : 0.f;
     }
     // gamma (.) Q and Kt, whole 64 rows
-    ew(DC * D, [&](int i) { const int t = i / D; return t < n ? R.gam[t] * to_f32(Q[t * rk + i % D]) : 0.f; },
+    ew(DC * D, [&](int i) { const int t = i / D; return t < n ? R.gam[t] * to_f32(sQ[t * KP + i % D]) : 0.f; },
        [&](int i, float v) { w.Qg[i] = v; });
     ew(DC * D, [&](int i) { const int t = i / D; return t < n ? R.kts[t] * to_f32(sK[t * KP + i % D]) : 0.f; },
        [&](int i, float v) { w.Kt[i] = v; });
@@ -469,7 +504,10 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     }
     __syncthreads();
     mmt(DC, Dv, n, 1.f, sT, LP, 1, V, rv, 1, 0.f, w.U, Dv, 1, smm);
-    mm<4>(DC, D, n, 1.f, sGE, LP, 1, sK, KP, 1, 0.f, w.W, D, 1);
+    if (D == 128)
+        mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sGE, sK, 0.f, w.W);
+    else
+        mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sGE, sK, 0.f, w.W);
 }
 
 // ---------------------------------------------------------------- sequential passes
@@ -525,33 +563,11 @@ __device__ __forceinline__ void seq_stash(const float* pf, float* sBuf) {
     }
 }
 
-// C (M x N) = alpha A B + beta C with every operand in LDS, on the fp32 matrix
-// cores: A(i, k) = A[i*SIA + k*SKA], B(k, j) = B[k*SKB + j*SIB], C(i, j) =
-// C[i*CI + j]; M, N multiples of 16, K of 4.  Wave w computes tiles w, w + 8, ...
-// Each output element is read (beta) and written by one lane only.
-template <int M, int N, int K, int SIA, int SKA, int SIB, int SKB, int CI>
-__device__ __forceinline__ void mm_lds(float alpha, const float* A, const float* B, float beta, float* C) {
-    constexpr int NTJ = N / 16, NTILES = (M / 16) * NTJ;
-    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-    for (int t0 = 0; t0 < NTILES; t0 += DTH / 64) {
-        const int t = t0 + wv;
-        if (t < NTILES) {
-            const int i0 = (t / NTJ) * 16, j0 = (t % NTJ) * 16;
-            f32x4 acc = zero4();
-#pragma unroll 8
-            for (int k0 = 0; k0 < K; k0 += 4)
-                acc = Mma<float>::mma(frag_ld<float, SIA, SKA>(A, i0, k0), frag_ld<float, SIB, SKB>(B, j0, k0), acc);
-            const int r0 = i0 + 4 * (l >> 4), j = j0 + (l & 15);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float* c = C + (r0 + e) * CI + j;
-                *c = beta != 0.f ? alpha * acc[e] + beta * *c : alpha * acc[e];
-            }
-        }
-    }
-}
-
+// C (M x N) = alpha A B + beta C with A and B in LDS (fp32 or bf16, converted
+// exactly), on the fp32 matrix cores: A(i, k) = A[i*SIA + k*SKA], B(k, j) =
+// B[k*SKB + j*SIB], C(i, j) = C[i*CI + j] (LDS or global); M, N multiples of 16,
+// K of 4.  Wave w computes tiles w, w + 8, ...  Each output element is read
+// (beta) and written by one lane only.
 // state pass (chunks in order): o and hT, or (BWD) S0 and Wv of every chunk
 template <typename T, bool BWD, int D>
 __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
