@@ -457,7 +457,7 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     __shared__ float sGE[DC * LP], sT[DC * LP];
     __shared__ __attribute__((aligned(16))) T sK[DC * (128 + kpad<T>())];
     __shared__ __attribute__((aligned(16))) T sQ[DC * (128 + kpad<T>())];
-    __shared__ float smm[MMT_LDS];
+    T* sV = sQ;  // (V takes Q's place once gamma Q is written)
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
     const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
@@ -495,6 +495,7 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     ew(DC * D, [&](int i) { const int t = i / D; return t < n ? R.kts[t] * to_f32(sK[t * KP + i % D]) : 0.f; },
        [&](int i, float v) { w.Kt[i] = v; });
     __syncthreads();
+    load_k<T>(R, V, rv, Dv, sV);
     // U = T (beta V), W = T (beta gamma K), with beta and beta gamma folded into the
     // columns of T; rows past n are 0 (T is the identity there and beta is 0)
     for (int i = threadIdx.x; i < DC * DC; i += DTH) {
@@ -503,7 +504,10 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
         sT[t * LP + s] *= R.beta[s];
     }
     __syncthreads();
-    mmt(DC, Dv, n, 1.f, sT, LP, 1, V, rv, 1, 0.f, w.U, Dv, 1, smm);
+    if (Dv == 128)
+        mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sT, sV, 0.f, w.U);
+    else
+        mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sT, sV, 0.f, w.U);
     if (D == 128)
         mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sGE, sK, 0.f, w.W);
     else
