@@ -690,9 +690,9 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __shared__ Rows R;
     __shared__ float sGE[DC * LP], sT[DC * LP];
     __shared__ __attribute__((aligned(16))) float sXY[2 * DC * LP];
+    __shared__ __attribute__((aligned(16))) T sK[DC * (128 + kpad<T>())];  // the chunk's K rows
     float* sX = sXY;
     float* sY = sXY + DC * LP;
-    T* sK = reinterpret_cast<T*>(sXY);  // (K rows for the inverse only; 64 x 129 fp32 fits)
     __shared__ float sdG[DC], sdB[DC], sr1[DC], sr2[DC], sdGC;
     __shared__ float smm[MMT_LDS];
     const int64_t NC = (a.T + DC - 1) / DC;
@@ -718,7 +718,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     ew(DC * DC, [&](int i) { return w.T[i]; }, [&](int i, float v) { sT[(i / DC) * LP + i % DC] = v; });
     __syncthreads();
     gram_masked<T>(R, sK, D, sGE);
-    for (int i = threadIdx.x; i < DC * LP; i += DTH) sX[i] = 0.f;  // (sK is dead)
+    for (int i = threadIdx.x; i < DC * LP; i += DTH) sX[i] = 0.f;
     __syncthreads();
     // S0, Wv, dS1 and dWv are stored transposed ([value column][row]), so that
     // every product below reads its B operand along rows.
@@ -789,7 +789,10 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     ew(DC * D, [&](int i) { return w.gQ[i] * R.gam[i / D]; }, [&](int i, float v) { w.gQ[i] = v; });
     ew(DC * D, [&](int i) { return R.kts[i / D] * w.gKt[i]; }, [&](int i, float v) { w.gK[i] = v; });
     __syncthreads();
-    mmt(n, D, n, 1.f, sX, LP, 1, K, rk, 1, 1.f, w.gQ, D, 1, smm);
+    if (D == 128)
+        mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gQ);
+    else
+        mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, w.gQ);
     mmt(n, D, n, 1.f, sX, 1, LP, Q, rk, 1, 1.f, w.gK, D, 1, smm);
     __syncthreads();
     // (4) dT = dWv (beta V)^T + dW (beta gamma K)^T in sY ([i][j]), formed as
@@ -832,9 +835,15 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
         sX[t * LP + s] = s < t && t < n ? sY[t * LP + s] * R.beta[t] * decay(R, t, s) : 0.f;
     }
     __syncthreads();
-    // dK += (dG + dG^T) K
-    mmt(n, D, n, 1.f, sX, LP, 1, K, rk, 1, 1.f, w.gK, D, 1, smm);
-    mmt(n, D, n, 1.f, sX, 1, LP, K, rk, 1, 1.f, w.gK, D, 1, smm);
+    // dK += (dG + dG^T) K (one lane reads and writes each element in both calls)
+    if (D == 128) {
+        mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gK);
+        mm_lds<DC, 128, DC, 1, LP, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gK);
+    } else {
+        mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, w.gK);
+        mm_lds<DC, 64, DC, 1, LP, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, w.gK);
+    }
+    __syncthreads();
     __syncthreads();
     // (6) dV = beta dVb; dbeta += V . dVb + gamma K . dKb; dK += beta gamma dKb;
     //     dGamma += beta gamma K . dKb
