@@ -50,78 +50,15 @@ constexpr int LP = 65;     // LDS pitch of 64 x 64 matrices
 
 // C(i, j) = alpha * si[i] * sj[j] * sum_k A(i, k) B(k, j) + beta * C(i, j) for
 // i < M, j < N, with A(i, k) = A[i*ai + k*ak], B(k, j) = B[k*bk + j*bj] and
-// C(i, j) = C[i*ci + j*cj] (any mix of LDS and global memory; si, sj optional).
-// Each thread computes R x R blocks, consecutive threads taking consecutive
-// column blocks, so B reads coalesce when bj = 1.  No barrier inside: the
-// caller synchronises.
-template <int R, typename TA, typename TB>
-__device__ __forceinline__ void mm(int M, int N, int K, float alpha, const TA* A, int64_t ai, int64_t ak,
-                                   const TB* B, int64_t bk, int64_t bj, float beta, float* C, int64_t ci,
-                                   int64_t cj, const float* sj = nullptr, const float* si = nullptr) {
-    const int nbi = (M + R - 1) / R, nbj = (N + R - 1) / R;
-    for (int blk = threadIdx.x; blk < nbi * nbj; blk += DTH) {
-        const int i0 = (blk / nbj) * R, j0 = (blk % nbj) * R;
-        float acc[R][R];
-#pragma unroll
-        for (int u = 0; u < R; ++u)
-#pragma unroll
-            for (int w = 0; w < R; ++w) acc[u][w] = 0.f;
-        // KU k steps of loads are issued before their products, so that one wait
-        // covers KU steps' latency (operands often come from L2)
-        constexpr int KU = R >= 4 ? 4 : 8;
-        int k = 0;
-#pragma unroll 1
-        for (; k + KU <= K; k += KU) {
-            float a[KU][R], b[KU][R];
-#pragma unroll
-            for (int kk = 0; kk < KU; ++kk)
-#pragma unroll
-                for (int u = 0; u < R; ++u) {
-                    a[kk][u] = i0 + u < M ? to_f32(A[(i0 + u) * ai + (k + kk) * ak]) : 0.f;
-                    b[kk][u] = j0 + u < N ? to_f32(B[(k + kk) * bk + (j0 + u) * bj]) : 0.f;
-                }
-#pragma unroll
-            for (int kk = 0; kk < KU; ++kk)
-#pragma unroll
-                for (int u = 0; u < R; ++u)
-#pragma unroll
-                    for (int w = 0; w < R; ++w) acc[u][w] += a[kk][u] * b[kk][w];
-        }
-#pragma unroll 1
-        for (; k < K; ++k) {
-            float a[R], b[R];
-#pragma unroll
-            for (int u = 0; u < R; ++u) {
-                a[u] = i0 + u < M ? to_f32(A[(i0 + u) * ai + k * ak]) : 0.f;
-                b[u] = j0 + u < N ? to_f32(B[k * bk + (j0 + u) * bj]) : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < R; ++u)
-#pragma unroll
-                for (int w = 0; w < R; ++w) acc[u][w] += a[u] * b[w];
-        }
-#pragma unroll
-        for (int u = 0; u < R; ++u)
-#pragma unroll
-            for (int w = 0; w < R; ++w) {
-                const int i = i0 + u, j = j0 + w;
-                if (i < M && j < N) {
-                    float* c = C + i * ci + j * cj;
-                    const float v = alpha * acc[u][w] * (sj ? sj[j] : 1.f) * (si ? si[i] : 1.f);
-                    *c = beta != 0.f ? v + beta * *c : v;
-                }
-            }
-    }
-}
-
-// The same product for operands in global memory (L2): k is taken in tiles of
-// KT; each tile of A (M x KT) and B (KT x N) is loaded by the whole workgroup
+// C(i, j) = C[i*ci + j*cj], for operands in global memory (L2) or LDS (si, sj
+// optional): k is taken in tiles of KT; each tile of A (M x KT) and B (KT x N)
+// is loaded by the whole workgroup
 // with the unit-stride index running across lanes, written to LDS, and the
 // next tile's loads are issued before the current tile is used; the products run
 // on the fp32 matrix cores.  M, N <= 128.  `lds` holds MMT_LDS floats.  Contains
 // barriers: every thread of the workgroup calls it.
 constexpr int KT = 32, MMT_LDS = 128 * (KT + 1) + KT * (128 + 1), LDE = 128 * KT / DTH;
-template <int NBT = 1, typename TA, typename TB>
+template <typename TA, typename TB>
 __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* A, int64_t ai64, int64_t ak64, const TB* B,
                     int64_t bk64, int64_t bj64, float beta, float* C, int64_t ci, int64_t cj, float* lds,
                     const float* sj = nullptr, const float* si = nullptr) {
