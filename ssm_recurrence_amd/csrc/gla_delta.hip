@@ -57,16 +57,18 @@ constexpr int LP = 65;     // LDS pitch of 64 x 64 matrices
 // next tile's loads are issued before the current tile is used; the products run
 // on the fp32 matrix cores.  M, N <= 128.  `lds` holds MMT_LDS floats.  Contains
 // barriers: every thread of the workgroup calls it.
-constexpr int KT = 32, MMT_LDS = 128 * (KT + 1) + KT * (128 + 1), LDE = 128 * KT / DTH;
+// LDS serves a wave's 32-bit reads in two halves of 32 lanes over 32 banks.  The
+// A tile's pitch is 2 mod 32 (a fragment's half reads 16 rows x 2 columns), the
+// B tile's 16 mod 32 (16 columns x 2 rows): each half-wave read hits 32 banks.
+constexpr int KT = 32, PA = KT + 2, PB = 128 + 16, MMT_LDS = 128 * PA + KT * PB, LDE = 128 * KT / DTH;
 template <typename TA, typename TB>
 __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* A, int64_t ai64, int64_t ak64, const TB* B,
                     int64_t bk64, int64_t bj64, float beta, float* C, int64_t ci, int64_t cj, float* lds,
                     const float* sj = nullptr, const float* si = nullptr) {
     // (offsets within one chunk's operands fit in 32 bits)
     const int ai = (int)ai64, ak = (int)ak64, bk = (int)bk64, bj = (int)bj64;
-    float* sa = lds;                    // [128][KT + 1]: sa[i][kk]
-    float* sb = lds + 128 * (KT + 1);   // [KT][128 + 1]: sb[kk][j]
-    constexpr int NP = 128 + 1;
+    float* sa = lds;              // [128][PA]: sa[i][kk]
+    float* sb = lds + 128 * PA;   // [KT][PB]: sb[kk][j]
     const int tid = threadIdx.x;
     const bool a_i_fast = ai == 1 && ak != 1;  // unit stride along i: lanes run along i
     const bool b_k_fast = bk == 1 && bj != 1;
@@ -96,8 +98,8 @@ __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* 
             int i, kk, j, kb;
             a_ik(e, i, kk);
             b_jk(e, j, kb);
-            if (i < M) sa[i * (KT + 1) + kk] = ra[r];
-            if (j < N) sb[kb * NP + j] = rb[r];
+            if (i < M) sa[i * PA + kk] = ra[r];
+            if (j < N) sb[kb * PB + j] = rb[r];
         }
     };
     // 16 x 16 output tiles on the fp32 matrix cores (full fp32 products and
@@ -122,8 +124,8 @@ __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* 
                 const int i0 = (t / ntj) * 16, j0 = (t % ntj) * 16;
 #pragma unroll
                 for (int kk = 0; kk < KT; kk += 4)
-                    acc[q] = Mma<float>::mma(frag_ld<float, KT + 1, 1>(sa, i0, kk),
-                                             frag_ld<float, 1, 128 + 1>(sb, j0, kk), acc[q]);
+                    acc[q] = Mma<float>::mma(frag_ld<float, PA, 1>(sa, i0, kk),
+                                             frag_ld<float, 1, PB>(sb, j0, kk), acc[q]);
             }
         }
     }
@@ -457,26 +459,45 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
 // Registers hold the segments back to back (W [64][D], Kt [64][D], then (QP)
 // gamma Q [64][D] and P [64][64], then a [64][16] column slice: U, or dO); every
 // segment is a multiple of the workgroup size, so each register holds one
-// segment's element.  In LDS the [64][D] and [64][64] segments get one padding
-// column, so that the matrix-core fragments (16 rows at once) spread over the banks.
-template <int D, bool QP> struct SeqLayout {
-    static constexpr int PD = D + 1, PP = DC + 1;
+// segment's element.  In LDS each segment's row pitch is padded for the way the
+// products read it (32-bit reads are served in two halves of 32 lanes over 32
+// banks): a segment read as 16 rows x 4 columns per fragment (A(i, k) = X[i][k])
+// gets pitch = 2 mod 32 dwords, one read as 16 columns x 4 rows (A(i, k) =
+// X[k][i]) gets 16 mod 32, so that each half of a fragment read hits 32 distinct
+// banks.  REV is the reverse pass, which reads W, gamma Q and P by columns and Kt
+// by rows; the forward state pass reads them the other way.
+template <int D, bool QP, bool REV> struct SeqLayout {
+    static constexpr int RP = D + 2, CP = D + 16;
+    static constexpr int PW = REV ? CP : RP, PK = REV ? RP : CP, PQ = REV ? CP : RP;
+    static constexpr int PP = REV ? DC + 16 : DC + 2;
     static constexpr int NW = DC * D, NPP = DC * DC, NS = DC * NSL;
     // register (unpadded) offsets
     static constexpr int UKT = NW, UQG = 2 * NW, UP = QP ? 3 * NW : 2 * NW, USL = QP ? UP + NPP : UP;
     static constexpr int NPF = (USL + NS) / DTH;
     // LDS (padded) offsets
-    static constexpr int W = 0, KT_ = DC * PD, QG = 2 * DC * PD;
-    static constexpr int P = QP ? 3 * DC * PD : 2 * DC * PD;
+    static constexpr int W = 0, KT_ = DC * PW, QG = KT_ + DC * PK;
+    static constexpr int P = QP ? QG + DC * PQ : QG;
     static constexpr int SL = QP ? P + DC * PP : P;
     static constexpr int TOTAL = SL + NS;
     static_assert(NW % DTH == 0 && NPP % DTH == 0 && NS % DTH == 0, "segments");
 };
 
+// g[(j0 + j) * R + r] = s[r * NSL + j] for an [R][NSL] LDS slice: each wave
+// instruction reads 16 rows x 4 columns (half as many bank repeats as 64
+// consecutive rows) and writes 64-byte runs
+template <int R>
+__device__ __forceinline__ void store_transposed(const float* s, float* g, int64_t j0) {
+    for (int i = threadIdx.x; i < R * NSL; i += DTH) {
+        const int l = i & 63, q = i >> 6;
+        const int j = (q & 3) * 4 + (l >> 4), r = (q >> 2) * 16 + (l & 15);
+        g[(j0 + j) * R + r] = s[r * NSL + j];
+    }
+}
+
 // slice(row, col) gives the [64][16] slice's element (row < 64)
 template <int D, bool QP, typename SliceF>
 __device__ __forceinline__ void seq_fetch(float* pf, const ChunkWs& w, SliceF slice) {
-    using L = SeqLayout<D, QP>;
+    using L = SeqLayout<D, QP, false>;  // (register offsets only)
 #pragma unroll
     for (int u = 0; u < L::NPF; ++u) {
         const int e = u * DTH + (int)threadIdx.x;
@@ -488,16 +509,16 @@ __device__ __forceinline__ void seq_fetch(float* pf, const ChunkWs& w, SliceF sl
     }
 }
 
-template <int D, bool QP>
+template <int D, bool QP, bool REV>
 __device__ __forceinline__ void seq_stash(const float* pf, float* sBuf) {
-    using L = SeqLayout<D, QP>;
+    using L = SeqLayout<D, QP, REV>;
 #pragma unroll
     for (int u = 0; u < L::NPF; ++u) {
         const int e = u * DTH + (int)threadIdx.x;
         int a;
-        if (u * DTH < L::UKT) a = L::W + (e / D) * L::PD + e % D;
-        else if (u * DTH < L::UQG) a = L::KT_ + ((e - L::UKT) / D) * L::PD + (e - L::UKT) % D;
-        else if (QP && u * DTH < L::UP) a = L::QG + ((e - L::UQG) / D) * L::PD + (e - L::UQG) % D;
+        if (u * DTH < L::UKT) a = L::W + (e / D) * L::PW + e % D;
+        else if (u * DTH < L::UQG) a = L::KT_ + ((e - L::UKT) / D) * L::PK + (e - L::UKT) % D;
+        else if (QP && u * DTH < L::UP) a = L::QG + ((e - L::UQG) / D) * L::PQ + (e - L::UQG) % D;
         else if (QP && u * DTH < L::USL) a = L::P + ((e - L::UP) / DC) * L::PP + (e - L::UP) % DC;
         else a = L::SL + (e - L::USL);
         sBuf[a] = pf[u];
@@ -512,7 +533,7 @@ __device__ __forceinline__ void seq_stash(const float* pf, float* sBuf) {
 // state pass (chunks in order): o and hT, or (BWD) S0 and Wv of every chunk
 template <typename T, bool BWD, int D>
 __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
-    using L = SeqLayout<D, !BWD>;
+    using L = SeqLayout<D, !BWD, false>;
     __shared__ float sBuf[L::TOTAL];
     __shared__ float sS[D * NSL], sWv[DC * NSL], sO[DC * NSL];
     const int Dv = (int)a.dv;
@@ -538,23 +559,21 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
         const int n = (int)(a.T - t0 < DC ? a.T - t0 : DC);
         const float carry = carry_next;
         __syncthreads();  // (the previous chunk no longer reads sBuf; sS is complete)
-        seq_stash<D, !BWD>(pf, sBuf);
+        seq_stash<D, !BWD, false>(pf, sBuf);
         if (BWD)
-            for (int i = threadIdx.x; i < D * NSL; i += DTH)  // S0 transposed: [value column][key row]
-                w.S0[(j0 + i / D) * D + i % D] = sS[(i % D) * NSL + i / D];
+            store_transposed<D>(sS, w.S0, j0);  // S0 transposed: [value column][key row]
         __syncthreads();
         if (c + 1 < NC) fetch(c + 1);
         // Wv = U - W S0
         for (int i = threadIdx.x; i < DC * NSL; i += DTH) sWv[i] = sBuf[L::SL + i];
         __syncthreads();
-        mm_lds<DC, NSL, D, L::PD, 1, 1, NSL, NSL>(-1.f, sBuf + L::W, sS, 1.f, sWv);
+        mm_lds<DC, NSL, D, L::PW, 1, 1, NSL, NSL>(-1.f, sBuf + L::W, sS, 1.f, sWv);
         __syncthreads();
         if (BWD) {
-            for (int i = threadIdx.x; i < DC * NSL; i += DTH)  // Wv transposed: [value column][row]
-                w.Wv[(j0 + i / DC) * DC + i % DC] = sWv[(i % DC) * NSL + i / DC];
+            store_transposed<DC>(sWv, w.Wv, j0);  // Wv transposed: [value column][row]
         } else {
             // O = (gamma Q) S0 + P Wv
-            mm_lds<DC, NSL, D, L::PD, 1, 1, NSL, NSL>(1.f, sBuf + L::QG, sS, 0.f, sO);
+            mm_lds<DC, NSL, D, L::PQ, 1, 1, NSL, NSL>(1.f, sBuf + L::QG, sS, 0.f, sO);
             mm_lds<DC, NSL, DC, L::PP, 1, 1, NSL, NSL>(1.f, sBuf + L::P, sWv, 1.f, sO);
             __syncthreads();
             T* o = (T*)a.o + (b * a.T + t0) * a.H * Dv + h * Dv + j0;
@@ -562,7 +581,7 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
                 o[(i / NSL) * a.H * Dv + i % NSL] = from_f32<T>(sO[i]);
         }
         // S1 = c S0 + Kt^T Wv
-        mm_lds<D, NSL, DC, 1, L::PD, 1, NSL, NSL>(1.f, sBuf + L::KT_, sWv, carry, sS);
+        mm_lds<D, NSL, DC, 1, L::PK, 1, NSL, NSL>(1.f, sBuf + L::KT_, sWv, carry, sS);
     }
     __syncthreads();
     if (!BWD && a.hT)
@@ -573,7 +592,7 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
 // chunk, then dh0
 template <typename T, int D>
 __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
-    using L = SeqLayout<D, true>;
+    using L = SeqLayout<D, true, true>;
     __shared__ float sBuf[L::TOTAL];
     __shared__ float sdS[D * NSL], sdWv[DC * NSL];
     const int Dv = (int)a.dv;
@@ -601,20 +620,18 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
         const ChunkWs w = chunk_ws(a, bh * NC + c);
         const float carry = carry_next;
         __syncthreads();
-        seq_stash<D, true>(pf, sBuf);
-        for (int i = threadIdx.x; i < D * NSL; i += DTH)  // dS1 transposed: [value column][key row]
-            w.dS1[(j0 + i / D) * D + i % D] = sdS[(i % D) * NSL + i / D];
+        seq_stash<D, true, true>(pf, sBuf);
+        store_transposed<D>(sdS, w.dS1, j0);  // dS1 transposed: [value column][key row]
         __syncthreads();
         if (c > 0) fetch(c - 1);
         // dWv = P^T dO + Kt dS1 (the dO slice is zero past the end)
         mm_lds<DC, NSL, DC, 1, L::PP, 1, NSL, NSL>(1.f, sBuf + L::P, sBuf + L::SL, 0.f, sdWv);
-        mm_lds<DC, NSL, D, L::PD, 1, 1, NSL, NSL>(1.f, sBuf + L::KT_, sdS, 1.f, sdWv);
+        mm_lds<DC, NSL, D, L::PK, 1, 1, NSL, NSL>(1.f, sBuf + L::KT_, sdS, 1.f, sdWv);
         __syncthreads();
-        for (int i = threadIdx.x; i < DC * NSL; i += DTH)  // dWv transposed: [value column][row]
-            w.dWv[(j0 + i / DC) * DC + i % DC] = sdWv[(i % DC) * NSL + i / DC];
+        store_transposed<DC>(sdWv, w.dWv, j0);  // dWv transposed: [value column][row]
         // dS0 = c dS1 + (gamma Q)^T dO - W^T dWv
-        mm_lds<D, NSL, DC, 1, L::PD, 1, NSL, NSL>(1.f, sBuf + L::QG, sBuf + L::SL, carry, sdS);
-        mm_lds<D, NSL, DC, 1, L::PD, 1, NSL, NSL>(-1.f, sBuf + L::W, sdWv, 1.f, sdS);
+        mm_lds<D, NSL, DC, 1, L::PQ, 1, NSL, NSL>(1.f, sBuf + L::QG, sBuf + L::SL, carry, sdS);
+        mm_lds<D, NSL, DC, 1, L::PW, 1, NSL, NSL>(-1.f, sBuf + L::W, sdWv, 1.f, sdS);
     }
     __syncthreads();
     if (a.dh0)
