@@ -75,6 +75,15 @@ __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; retur
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Block id -> logical id so that consecutive logical ids (the slices of one
+// head) land on the same XCD: the hardware deals consecutive block ids round
+// robin over the 8 XCDs.
+__device__ __forceinline__ int64_t xcd_logical_block(int64_t nblocks) {
+    const int64_t x = blockIdx.x;
+    if (nblocks % 8 != 0) return x;
+    return (x % 8) * (nblocks / 8) + x / 8;
+}
+
 // Operand fragment from LDS for one matrix-core step ("natural" k order):
 // lane (i = l%16, j = l/16) receives X(i0 + i, k0 + j*KPL + e), e < KPL, where
 // X(i, k) = base[i*SI + k*SK].  Serves A (i = row m) and B (i = column n).

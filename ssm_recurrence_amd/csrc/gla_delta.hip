@@ -538,7 +538,8 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
     __shared__ float sS[D * NSL], sWv[DC * NSL], sO[DC * NSL];
     const int Dv = (int)a.dv;
     const int nsl = Dv / NSL;
-    const int64_t bh = blockIdx.x / nsl, j0 = (blockIdx.x % nsl) * NSL;
+    const int64_t lb = xcd_logical_block(gridDim.x);  // the slices of one head share an XCD's L2
+    const int64_t bh = lb / nsl, j0 = (lb % nsl) * NSL;
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t NC = (a.T + DC - 1) / DC;
     for (int i = threadIdx.x; i < D * NSL; i += DTH) {
@@ -597,7 +598,8 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
     __shared__ float sdS[D * NSL], sdWv[DC * NSL];
     const int Dv = (int)a.dv;
     const int nsl = Dv / NSL;
-    const int64_t bh = blockIdx.x / nsl, j0 = (blockIdx.x % nsl) * NSL;
+    const int64_t lb = xcd_logical_block(gridDim.x);  // the slices of one head share an XCD's L2
+    const int64_t bh = lb / nsl, j0 = (lb % nsl) * NSL;
     const int64_t b = bh / a.H, h = bh % a.H;
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t rv = a.H * Dv;

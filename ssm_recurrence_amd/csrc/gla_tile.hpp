@@ -156,15 +156,6 @@ __device__ __forceinline__ void docs_from_flags(ChunkDocs* cd, int reset, int nv
     }
 }
 
-// Block id -> logical id so that consecutive logical ids (the slices of one
-// head) land on the same XCD: the hardware deals consecutive block ids round
-// robin over the 8 XCDs.
-__device__ __forceinline__ int64_t xcd_logical_block(int64_t nblocks) {
-    const int64_t x = blockIdx.x;
-    if (nblocks % 8 != 0) return x;
-    return (x % 8) * (nblocks / 8) + x / 8;
-}
-
 // Operands of the triangular matrix of ones L^T (L[r][u] = [u <= r]) for the
 // chunk-local prefix below, one per (row tile rt, k step): element e of lane
 // (i, j) is [k0 + j*KPL + e <= 16 rt + i].  The same fragment serves as A
