@@ -366,12 +366,14 @@ __device__ __forceinline__ float frag_f32(const TX* base, int i0, int k0) {
     return to_f32(base[(i0 + (l & 15)) * SI + (k0 + (l >> 4)) * SK]);
 }
 
-template <int M, int N, int K, int SIA, int SKA, int SIB, int SKB, int CI, typename TA, typename TB>
+template <int M, int N, int K, int SIA, int SKA, int SIB, int SKB, int CI, int WB = 0, int NWV = DTH / 64,
+          typename TA, typename TB>
 __device__ __forceinline__ void mm_lds(float alpha, const TA* A, const TB* B, float beta, float* C) {
     constexpr int NTJ = N / 16, NTILES = (M / 16) * NTJ;
-    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int wv = (int)(threadIdx.x >> 6) - WB, l = threadIdx.x & 63;
+    if (wv < 0 || wv >= NWV) return;
 #pragma unroll
-    for (int t0 = 0; t0 < NTILES; t0 += DTH / 64) {
+    for (int t0 = 0; t0 < NTILES; t0 += NWV) {
         const int t = t0 + wv;
         if (t < NTILES) {
             const int i0 = (t / NTJ) * 16, j0 = (t % NTJ) * 16;
@@ -457,9 +459,8 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
 // The operands a chunk needs are staged through registers: the next chunk's
 // values are loaded while the current chunk computes, then written to LDS.
 // Registers hold the segments back to back (W [64][D], Kt [64][D], then (QP)
-// gamma Q [64][D] and P [64][64], then a [64][16] column slice: U, or dO); every
-// segment is a multiple of the workgroup size, so each register holds one
-// segment's element.  In LDS each segment's row pitch is padded for the way the
+// gamma Q [64][D] and P [64][64], then a [64][16] column slice: U, or dO); each
+// register (vector) holds consecutive elements of one segment's row.  In LDS each segment's row pitch is padded for the way the
 // products read it (32-bit reads are served in two halves of 32 lanes over 32
 // banks): a segment read as 16 rows x 4 columns per fragment (A(i, k) = X[i][k])
 // gets pitch = 2 mod 32 dwords, one read as 16 columns x 4 rows (A(i, k) =
@@ -473,7 +474,6 @@ template <int D, bool QP, bool REV> struct SeqLayout {
     static constexpr int NW = DC * D, NPP = DC * DC, NS = DC * NSL;
     // register (unpadded) offsets
     static constexpr int UKT = NW, UQG = 2 * NW, UP = QP ? 3 * NW : 2 * NW, USL = QP ? UP + NPP : UP;
-    static constexpr int NPF = (USL + NS) / DTH;
     // LDS (padded) offsets
     static constexpr int W = 0, KT_ = DC * PW, QG = KT_ + DC * PK;
     static constexpr int P = QP ? QG + DC * PQ : QG;
@@ -494,42 +494,66 @@ __device__ __forceinline__ void store_transposed(const float* s, float* g, int64
     }
 }
 
+// The prefetch registers: the four [64][D] / [64][64] segments as 16-byte
+// vectors (each segment is a multiple of 4 x DTH floats and starts 16-byte
+// aligned: the workspace is, and every segment size is a multiple of 4 floats),
+// then the [64][16] slice one float at a time.
+template <int D, bool QP> struct SeqRegs {
+    using L = SeqLayout<D, QP, false>;
+    static constexpr int NV = L::USL / (4 * DTH), NSS = L::NS / DTH;
+    static_assert(L::USL % (4 * DTH) == 0 && L::NW % (4 * DTH) == 0 && L::NPP % (4 * DTH) == 0, "segments");
+    f32x4 v[NV];
+    float s[NSS];
+};
+
 // slice(row, col) gives the [64][16] slice's element (row < 64)
 template <int D, bool QP, typename SliceF>
-__device__ __forceinline__ void seq_fetch(float* pf, const ChunkWs& w, SliceF slice) {
+__device__ __forceinline__ void seq_fetch(SeqRegs<D, QP>& pf, const ChunkWs& w, SliceF slice) {
     using L = SeqLayout<D, QP, false>;  // (register offsets only)
 #pragma unroll
-    for (int u = 0; u < L::NPF; ++u) {
+    for (int u = 0; u < SeqRegs<D, QP>::NV; ++u) {
+        const int e = 4 * (u * DTH + (int)threadIdx.x), e0 = 4 * u * DTH;
+        const float* src;
+        if (e0 < L::UKT) src = w.W + e;
+        else if (e0 < L::UQG) src = w.Kt + (e - L::UKT);
+        else if (QP && e0 < L::UP) src = w.Qg + (e - L::UQG);
+        else src = w.P + (e - L::UP);
+        pf.v[u] = *reinterpret_cast<const f32x4*>(src);
+    }
+#pragma unroll
+    for (int u = 0; u < SeqRegs<D, QP>::NSS; ++u) {
         const int e = u * DTH + (int)threadIdx.x;
-        if (u * DTH < L::UKT) pf[u] = w.W[e];
-        else if (u * DTH < L::UQG) pf[u] = w.Kt[e - L::UKT];
-        else if (QP && u * DTH < L::UP) pf[u] = w.Qg[e - L::UQG];
-        else if (QP && u * DTH < L::USL) pf[u] = w.P[e - L::UP];
-        else pf[u] = slice((e - L::USL) / NSL, (e - L::USL) % NSL);
+        pf.s[u] = slice(e / NSL, e % NSL);
     }
 }
 
 template <int D, bool QP, bool REV>
-__device__ __forceinline__ void seq_stash(const float* pf, float* sBuf) {
+__device__ __forceinline__ void seq_stash(const SeqRegs<D, QP>& pf, float* sBuf) {
     using L = SeqLayout<D, QP, REV>;
 #pragma unroll
-    for (int u = 0; u < L::NPF; ++u) {
+    for (int u = 0; u < SeqRegs<D, QP>::NV; ++u) {
+        const int e = 4 * (u * DTH + (int)threadIdx.x), e0 = 4 * u * DTH;
+        int a;  // (four consecutive columns of one row)
+        if (e0 < L::UKT) a = L::W + (e / D) * L::PW + e % D;
+        else if (e0 < L::UQG) a = L::KT_ + ((e - L::UKT) / D) * L::PK + (e - L::UKT) % D;
+        else if (QP && e0 < L::UP) a = L::QG + ((e - L::UQG) / D) * L::PQ + (e - L::UQG) % D;
+        else a = L::P + ((e - L::UP) / DC) * L::PP + (e - L::UP) % DC;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sBuf[a + q] = pf.v[u][q];
+    }
+#pragma unroll
+    for (int u = 0; u < SeqRegs<D, QP>::NSS; ++u) {
         const int e = u * DTH + (int)threadIdx.x;
-        int a;
-        if (u * DTH < L::UKT) a = L::W + (e / D) * L::PW + e % D;
-        else if (u * DTH < L::UQG) a = L::KT_ + ((e - L::UKT) / D) * L::PK + (e - L::UKT) % D;
-        else if (QP && u * DTH < L::UP) a = L::QG + ((e - L::UQG) / D) * L::PQ + (e - L::UQG) % D;
-        else if (QP && u * DTH < L::USL) a = L::P + ((e - L::UP) / DC) * L::PP + (e - L::UP) % DC;
-        else a = L::SL + (e - L::USL);
-        sBuf[a] = pf[u];
+        sBuf[L::SL + e] = pf.s[u];
     }
 }
 
 // C (M x N) = alpha A B + beta C with A and B in LDS (fp32 or bf16, converted
 // exactly), on the fp32 matrix cores: A(i, k) = A[i*SIA + k*SKA], B(k, j) =
 // B[k*SKB + j*SIB], C(i, j) = C[i*CI + j] (LDS or global); M, N multiples of 16,
-// K of 4.  Wave w computes tiles w, w + 8, ...  Each output element is read
-// (beta) and written by one lane only.
+// K of 4.  Waves WB .. WB + NWV - 1 take part: wave WB + w computes tiles w,
+// w + NWV, ...; the other waves return at once (no barrier inside).  Each output
+// element is read (beta) and written by one lane only.
 // state pass (chunks in order): o and hT, or (BWD) S0 and Wv of every chunk
 template <typename T, bool BWD, int D>
 __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
@@ -546,7 +570,7 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
         const int r = i / NSL, j = i % NSL;
         sS[i] = a.h0 ? a.h0[(bh * D + r) * Dv + j0 + j] : 0.f;
     }
-    float pf[L::NPF];
+    SeqRegs<D, !BWD> pf;
     float carry_next;
     auto fetch = [&](int64_t c) {
         const ChunkWs w = chunk_ws(a, bh * NC + c);
@@ -554,37 +578,44 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
         carry_next = w.carry[0];
     };
     fetch(0);
+    int64_t t0_prev = 0;
+    int n_prev = 0;
+    // o of the previous chunk: sO is complete after the loop's first barrier and
+    // rewritten only after its second
+    auto store_o = [&]() {
+        T* o = (T*)a.o + (b * a.T + t0_prev) * a.H * Dv + h * Dv + j0;
+        for (int i = threadIdx.x; i < n_prev * NSL; i += DTH)
+            o[(i / NSL) * a.H * Dv + i % NSL] = from_f32<T>(sO[i]);
+    };
     for (int64_t c = 0; c < NC; ++c) {
         const ChunkWs w = chunk_ws(a, bh * NC + c);
         const int64_t t0 = c * DC;
         const int n = (int)(a.T - t0 < DC ? a.T - t0 : DC);
         const float carry = carry_next;
-        __syncthreads();  // (the previous chunk no longer reads sBuf; sS is complete)
+        __syncthreads();  // (the previous chunk no longer reads sBuf; sS and sO are complete)
+        if (!BWD && c > 0) store_o();
         seq_stash<D, !BWD, false>(pf, sBuf);
         if (BWD)
             store_transposed<D>(sS, w.S0, j0);  // S0 transposed: [value column][key row]
         __syncthreads();
-        if (c + 1 < NC) fetch(c + 1);
-        // Wv = U - W S0
+        // Wv = U - W S0 on waves 0-3; in the forward, O = (gamma Q) S0 on waves 4-7
         for (int i = threadIdx.x; i < DC * NSL; i += DTH) sWv[i] = sBuf[L::SL + i];
         __syncthreads();
-        mm_lds<DC, NSL, D, L::PW, 1, 1, NSL, NSL>(-1.f, sBuf + L::W, sS, 1.f, sWv);
+        mm_lds<DC, NSL, D, L::PW, 1, 1, NSL, NSL, 0, 4>(-1.f, sBuf + L::W, sS, 1.f, sWv);
+        if (!BWD) mm_lds<DC, NSL, D, L::PQ, 1, 1, NSL, NSL, 4, 4>(1.f, sBuf + L::QG, sS, 0.f, sO);
         __syncthreads();
-        if (BWD) {
+        if (c + 1 < NC) fetch(c + 1);
+        if (BWD)
             store_transposed<DC>(sWv, w.Wv, j0);  // Wv transposed: [value column][row]
-        } else {
-            // O = (gamma Q) S0 + P Wv
-            mm_lds<DC, NSL, D, L::PQ, 1, 1, NSL, NSL>(1.f, sBuf + L::QG, sS, 0.f, sO);
-            mm_lds<DC, NSL, DC, L::PP, 1, 1, NSL, NSL>(1.f, sBuf + L::P, sWv, 1.f, sO);
-            __syncthreads();
-            T* o = (T*)a.o + (b * a.T + t0) * a.H * Dv + h * Dv + j0;
-            for (int i = threadIdx.x; i < n * NSL; i += DTH)
-                o[(i / NSL) * a.H * Dv + i % NSL] = from_f32<T>(sO[i]);
-        }
-        // S1 = c S0 + Kt^T Wv
-        mm_lds<D, NSL, DC, 1, L::PK, 1, NSL, NSL>(1.f, sBuf + L::KT_, sWv, carry, sS);
+        else  // O += P Wv on waves 4-7
+            mm_lds<DC, NSL, DC, L::PP, 1, 1, NSL, NSL, 4, 4>(1.f, sBuf + L::P, sWv, 1.f, sO);
+        // S1 = c S0 + Kt^T Wv (8 tiles; the forward keeps waves 4-7 for O)
+        mm_lds<D, NSL, DC, 1, L::PK, 1, NSL, NSL, 0, BWD ? 8 : 4>(1.f, sBuf + L::KT_, sWv, carry, sS);
+        t0_prev = t0;
+        n_prev = n;
     }
     __syncthreads();
+    if (!BWD && NC > 0) store_o();
     if (!BWD && a.hT)
         for (int i = threadIdx.x; i < D * NSL; i += DTH) a.hT[(bh * D + i / NSL) * Dv + j0 + i % NSL] = sS[i];
 }
@@ -607,7 +638,7 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
         const int r = i / NSL, j = i % NSL;
         sdS[i] = a.dhT ? a.dhT[(bh * D + r) * Dv + j0 + j] : 0.f;
     }
-    float pf[L::NPF];
+    SeqRegs<D, true> pf;
     float carry_next;
     auto fetch = [&](int64_t c) {
         const ChunkWs w = chunk_ws(a, bh * NC + c);
