@@ -489,27 +489,28 @@ def norm_gate_main(args):
 
 def delta_flops(T, C, dk, dv):
     """FLOPs of the chunked WY/UT gated delta rule per (b, h): dense products of
-    each chunk as the method forms them (the backward recomputes the chunk-local
-    forward terms and the states entering the chunks, as a backward that keeps only
-    chunk-boundary states must)."""
+    each chunk as the method forms them.  The backward reuses the forward's
+    per-chunk factors (the workspace it is handed) and recomputes the states
+    entering the chunks, as a backward that keeps only chunk-boundary states must."""
     nc = (T + C - 1) // C
     c2k, c2v, cdd, c3 = 2 * C * C * dk, 2 * C * C * dv, 2 * C * dk * dv, 2 * C ** 3
     prep = 2 * c2k + c2v + c2k + c3 / 3           # K K^T, U, W, Q K^T, the inverse
     state = 3 * cdd + c2v                          # W S0, (gamma Q) S0, Kt^T Wv; P Wv
     fwd = prep + state
     dstate = c2v + 3 * cdd                         # P^T dO; Kt dS1, (gamma Q)^T dO, W^T dWv
-    grad = (c2k + c3 / 3 + 3 * cdd                 # K K^T, inverse; dO S0^T, Wv dS1^T, dWv S0^T
+    grad = (c2k + 3 * cdd                          # K K^T; dO S0^T, Wv dS1^T, dWv S0^T
             + c2v + 2 * c2k                        # dO Wv^T; (dP M) K, (dP M)^T Q
             + c2v + c2k + c2v + c2k                # dT (two), T^T dWv, T^T dW
             + 2 * c3 + 2 * c2k)                    # dA = -T^T dT T^T; (dG + dG^T) K
-    bwd = prep + cdd + dstate + grad               # (the state pass without readout: W S0)
+    bwd = cdd + dstate + grad                      # (the state pass without readout: W S0)
     return nc * fwd, nc * bwd
 
 
 def delta_main(args):
     """The gated delta rule at the pages' Gated DeltaNet benchmark layout (bf16,
     batch 4, 8 heads, chunk 64, d = 128) at T = 4096: one gla_delta_fwd and one
-    gla_delta_bwd per step."""
+    gla_delta_bwd per step, the backward handed the forward's workspace
+    (GLA_DELTA_WS_FROM_FWD), as the autograd wrapper does."""
     import torch
     from ssm_recurrence_amd import binding as gb
     from ssm_recurrence_amd.inputs import delta_workload
@@ -521,6 +522,7 @@ def delta_main(args):
     B, T, H, dk = c.q.shape
     dv = c.v.shape[3]
     prob = gb.delta_problem(c.q, c.v)
+    prob_b = gb.delta_problem(c.q, c.v, gb.GLA_DELTA_WS_FROM_FWD)  # the backward reuses the forward's ws
     o = torch.empty_like(c.v)
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     dq, dk_, dv_, dg, db = (torch.empty_like(c.q), torch.empty_like(c.k), torch.empty_like(c.v),
@@ -531,7 +533,7 @@ def delta_main(args):
     stream = torch.cuda.current_stream(dev)
     sp = gb.ctypes.c_void_p(stream.cuda_stream)
     lib = gb.load()
-    P = gb.ctypes.byref(prob)
+    P, PB = gb.ctypes.byref(prob), gb.ctypes.byref(prob_b)
     p = gb._p
 
     def step(ev=None):
@@ -541,7 +543,7 @@ def delta_main(args):
                                p(o), p(hT), p(ws), ws.numel(), sp)
         if ev is not None:
             ev[1].record(stream)
-        rc |= lib.gla_delta_bwd(P, p(c.q), p(c.k), p(c.v), p(c.g), p(c.beta), p(c.h0), p(c.segment_ids),
+        rc |= lib.gla_delta_bwd(PB, p(c.q), p(c.k), p(c.v), p(c.g), p(c.beta), p(c.h0), p(c.segment_ids),
                                 p(c.dO), p(c.dhT), p(dq), p(dk_), p(dv_), p(dg), p(db), p(dh0), p(ws),
                                 ws.numel(), sp)
         if ev is not None:
@@ -572,7 +574,7 @@ def delta_main(args):
             "traffic": None if traffic is None else round(traffic / 1e6, 1),
             "traffic_unit": "MB per gla_delta_bwd call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flops": round(fb / 1e9, 2),
-            "kernel": "gla_delta_bwd (its four kernels, one call): fp32 products, mostly on the matrix cores",
+            "kernel": "gla_delta_bwd (its three kernels, one call): fp32 products, mostly on the matrix cores",
             "step_frac": round((ff + fb) / ((fwd_us + bwd_us) * 1e-6) / 1e12 / PEAK["mfma_f32"], 4)}
     cpu = None
     if not args.no_cpu_baseline:

@@ -230,8 +230,17 @@ int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const
 typedef struct {
     int64_t B, T, H, d_k, d_v;
     int32_t dtype;    /* gla_dtype */
-    int32_t reserved; /* 0 */
+    int32_t flags;    /* 0, or GLA_DELTA_WS_FROM_FWD; other bits: GLA_E_UNSUPPORTED */
 } gla_delta_problem;
+
+/* gla_delta_bwd only (gla_delta_fwd ignores it): ws holds what gla_delta_fwd
+ * wrote there for the same problem and the same q, k, v, g, beta and
+ * segment_ids, unchanged since (a backward call leaves it so).  The backward then
+ * reuses the forward's per-chunk factors (the inverse T, U, W, the masked scores,
+ * gamma Q, the decayed keys and the chunk carries) instead of recomputing them.
+ * The caller vouches for this; the library cannot check it, and a stale ws gives
+ * wrong gradients without an error. */
+#define GLA_DELTA_WS_FROM_FWD 1
 
 /* Bytes of device workspace gla_delta_fwd / gla_delta_bwd need. */
 int gla_delta_workspace_size(const gla_delta_problem* p, int for_backward, size_t* bytes);

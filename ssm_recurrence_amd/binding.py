@@ -44,7 +44,7 @@ class NormGateProblem(ctypes.Structure):
 class DeltaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
 
 
 class GlaError(RuntimeError):
@@ -466,9 +466,12 @@ class NormGateFunction(torch.autograd.Function):
 
 
 # ---- gated delta rule (gla_delta_* in include/gla.h)
-def delta_problem(q, v):
+GLA_DELTA_WS_FROM_FWD = 1
+
+
+def delta_problem(q, v, flags=0):
     B, T, H, d_k = q.shape
-    return DeltaProblem(B, T, H, d_k, v.shape[3], GLA_BF16 if q.dtype == torch.bfloat16 else GLA_F32, 0)
+    return DeltaProblem(B, T, H, d_k, v.shape[3], GLA_BF16 if q.dtype == torch.bfloat16 else GLA_F32, flags)
 
 
 def delta_workspace_size(prob: DeltaProblem) -> int:
@@ -506,14 +509,18 @@ def delta_fwd(q, k, v, g, beta, h0=None, segment_ids=None, *, want_hT=True, ws=N
     return o, hT
 
 
-def delta_bwd(q, k, v, g, beta, dO, h0=None, segment_ids=None, dhT=None, *, want_dh0=True, ws=None):
-    """dq, dk, dv, dg, dbeta (input dtype) and dh0 fp32 (or None)."""
+def delta_bwd(q, k, v, g, beta, dO, h0=None, segment_ids=None, dhT=None, *, want_dh0=True, ws=None,
+              ws_from_fwd=False):
+    """dq, dk, dv, dg, dbeta (input dtype) and dh0 fp32 (or None).  ws_from_fwd: ws is
+    the workspace delta_fwd filled for these same inputs (GLA_DELTA_WS_FROM_FWD)."""
+    if ws_from_fwd and ws is None:
+        raise ValueError("ws_from_fwd needs the forward's workspace")
     _delta_checks(q, k, v, g, beta)
     _check(dO, "dO", q.dtype)
     _check(h0, "h0", torch.float32)
     _check(dhT, "dhT", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = delta_problem(q, v)
+    prob = delta_problem(q, v, GLA_DELTA_WS_FROM_FWD if ws_from_fwd else 0)
     B, T, H, d_k = q.shape
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
@@ -521,6 +528,8 @@ def delta_bwd(q, k, v, g, beta, dO, h0=None, segment_ids=None, dhT=None, *, want
            if want_dh0 else None)
     n = delta_workspace_size(prob)
     if ws is None or ws.numel() < n:
+        if ws_from_fwd:
+            raise ValueError("ws_from_fwd: the workspace is smaller than the problem needs")
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     rc = load().gla_delta_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0),
                               _p(segment_ids), _p(dO), _p(dhT), _p(dq), _p(dk), _p(dv), _p(dg),
@@ -531,12 +540,15 @@ def delta_bwd(q, k, v, g, beta, dO, h0=None, segment_ids=None, dhT=None, *, want
 
 
 class DeltaFunction(torch.autograd.Function):
-    """Autograd wrapper of the gated delta rule: both passes run the HIP library."""
+    """Autograd wrapper of the gated delta rule: both passes run the HIP library.
+    The forward's workspace (its per-chunk factors) is kept for the backward."""
 
     @staticmethod
     def forward(ctx, q, k, v, g, beta, h0, segment_ids):
-        o, hT = delta_fwd(q, k, v, g, beta, h0, segment_ids)
+        ws = torch.empty(max(delta_workspace_size(delta_problem(q, v)), 1), dtype=torch.uint8, device=q.device)
+        o, hT = delta_fwd(q, k, v, g, beta, h0, segment_ids, ws=ws)
         ctx.save_for_backward(q, k, v, g, beta, h0, segment_ids)
+        ctx.ws = ws
         return o, hT
 
     @staticmethod
@@ -544,5 +556,6 @@ class DeltaFunction(torch.autograd.Function):
         q, k, v, g, beta, h0, seg = ctx.saved_tensors
         dO = dO.contiguous() if dO is not None else torch.zeros(v.shape, dtype=v.dtype, device=v.device)
         dhT = dhT.contiguous().float() if dhT is not None else None
-        dq, dk, dv, dg, dbeta, dh0 = delta_bwd(q, k, v, g, beta, dO, h0, seg, dhT, want_dh0=h0 is not None)
+        dq, dk, dv, dg, dbeta, dh0 = delta_bwd(q, k, v, g, beta, dO, h0, seg, dhT, want_dh0=h0 is not None,
+                                               ws=ctx.ws, ws_from_fwd=True)
         return dq, dk, dv, dg, dbeta, dh0, None

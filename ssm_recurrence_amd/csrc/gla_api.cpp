@@ -357,6 +357,7 @@ int check_delta(const gla_delta_problem* p) {
     if (p->dtype != GLA_F32 && p->dtype != GLA_BF16) return GLA_E_DTYPE;
     if (p->B < 1 || p->T < 0 || p->H < 1 || p->d_k < 1 || p->d_v < 1) return GLA_E_SHAPE;
     if ((p->d_k != 64 && p->d_k != 128) || (p->d_v != 64 && p->d_v != 128)) return GLA_E_UNSUPPORTED;
+    if (p->flags & ~GLA_DELTA_WS_FROM_FWD) return GLA_E_UNSUPPORTED;
     int64_t bt, bth, x;
     if (!mul_ok(p->B, p->T, &bt) || !mul_ok(bt, p->H, &bth) || !mul_ok(bth, 128, &x) || x > ((int64_t)1 << 40))
         return GLA_E_SHAPE;
@@ -605,6 +606,7 @@ int gla_delta_bwd(const gla_delta_problem* p, const void* q, const void* k, cons
     gla::DeltaArgs a = delta_args(p, ws);
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.seg = segment_ids; a.dO = dO;
     a.dhT = dhT; a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+    a.ws_prepared = (p->flags & GLA_DELTA_WS_FROM_FWD) != 0;
     const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_delta_bwd<gla::bf16>(a, st)
                                               : gla::launch_delta_bwd<float>(a, st);
     return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;

@@ -896,9 +896,12 @@ template <typename T>
 hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st) {
     const int64_t NC = (a.T + DC - 1) / DC;
     const dim3 chunks((unsigned)(a.B * a.H * NC)), slices((unsigned)(a.B * a.H * (a.dv / NSL)));
-    hipLaunchKernelGGL(k_delta_prep<T>, chunks, dim3(DTH), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!a.ws_prepared) {  // (else the forward's factors are in ws already)
+        hipLaunchKernelGGL(k_delta_prep<T>, chunks, dim3(DTH), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e;
     if (a.dk == 128)
         hipLaunchKernelGGL((k_delta_state<T, true, 128>), slices, dim3(DTH), 0, st, a);
     else

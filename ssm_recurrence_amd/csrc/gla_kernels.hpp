@@ -132,6 +132,7 @@ struct DeltaArgs {
     void* o;                                // forward output
     float* hT;                              // forward output or null
     void *dq, *dk_out, *dv_out, *dg, *dbeta;  // backward outputs
+    int32_t ws_prepared;                    // backward: ws already holds the forward's per-chunk factors
     float* dh0;                             // backward output or null
     float* ws;                              // delta_ws_floats_per_chunk floats per (b, h, chunk)
     int64_t ws_chunk;

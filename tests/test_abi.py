@@ -325,6 +325,10 @@ def test_delta_argument_errors(lib):
     assert call_delta_fwd(lib, delta_prob(d_k=96)) == -4
     assert call_delta_bwd(lib, delta_prob(d_v=32)) == -4
     assert call_delta_fwd(lib, delta_prob(dtype=5)) == -3
+    unknown_flag = delta_prob()
+    unknown_flag.flags = 2  # only GLA_DELTA_WS_FROM_FWD (1) is defined
+    assert call_delta_fwd(lib, unknown_flag) == -4
+    assert call_delta_bwd(lib, unknown_flag) == -4
     assert call_delta_fwd(lib, delta_prob(), {"g": FAKE + 4}) == -5
     assert call_delta_bwd(lib, delta_prob(), {"dh0": FAKE + 8}) == -5
 

@@ -82,6 +82,52 @@ def test_delta_parity(B, T, H, dk, dv, dtype, lens, h0):
     compare(got, run_oracle(case), dtype, "delta small")
 
 
+REUSE_CASES = [
+    (1, 200, 2, 128, 64, torch.float32, [50, 1, 100, 49]),
+    (1, 300, 4, 128, 128, torch.bfloat16, [64, 64, 1, 171]),
+    (2, 130, 2, 64, 128, torch.bfloat16, None),
+]
+
+
+@pytest.mark.parametrize("B,T,H,dk,dv,dtype,lens", REUSE_CASES,
+                         ids=["B%d-T%d-%s" % (c[0], c[1], str(c[5])[6:]) for c in REUSE_CASES])
+def test_delta_bwd_reuses_forward_workspace(B, T, H, dk, dv, dtype, lens):
+    """GLA_DELTA_WS_FROM_FWD: the backward handed the forward's workspace skips
+    recomputing the per-chunk factors; its gradients equal, bit for bit, those of
+    a backward that recomputes them (the same kernels on the same values), match
+    the oracle, and a second backward on the same workspace gives them again."""
+    case = delta_case("reuse", B=B, T=T, H=H, d_k=dk, d_v=dv, dtype=dtype, seed=7 + T, lengths=lens,
+                      with_h0=True, with_dhT=True)
+    c = case.to("cuda")
+    print("delta reuse", B, T, H, dk, dv, dtype, lens, flush=True)
+    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(c.q, c.v)), dtype=torch.uint8, device="cuda")
+    o, hT = gb.delta_fwd(c.q, c.k, c.v, c.g, c.beta, c.h0, c.segment_ids, ws=ws)
+    args = (c.q, c.k, c.v, c.g, c.beta, c.dO, c.h0, c.segment_ids, c.dhT)
+    reused = gb.delta_bwd(*args, ws=ws, ws_from_fwd=True)
+    again = gb.delta_bwd(*args, ws=ws, ws_from_fwd=True)
+    fresh = gb.delta_bwd(*args)
+    torch.cuda.synchronize()
+    for n, x, y, z in zip(NAMES, reused, again, fresh):
+        assert torch.equal(x, z), n
+        assert torch.equal(x, y), n
+    got = dict(o=o, hT=hT)
+    got.update(zip(NAMES, reused))
+    compare(got, run_oracle(case), dtype, "delta reuse")
+
+
+def test_delta_autograd_matches_bwd():
+    """DeltaFunction keeps the forward's workspace for its backward."""
+    case = delta_case("autograd", B=1, T=150, H=2, d_k=64, d_v=64, dtype=torch.float32, seed=3,
+                      lengths=[70, 80], with_h0=True, with_dhT=True)
+    c = case.to("cuda")
+    leaves = [x.clone().requires_grad_(True) for x in (c.q, c.k, c.v, c.g, c.beta, c.h0)]
+    o, hT = gb.DeltaFunction.apply(*leaves, c.segment_ids)
+    torch.autograd.backward([o, hT], [c.dO, c.dhT])
+    ref = gb.delta_bwd(c.q, c.k, c.v, c.g, c.beta, c.dO, c.h0, c.segment_ids, c.dhT)
+    for n, leaf, r in zip(NAMES, leaves, ref):
+        assert torch.equal(leaf.grad, r), n
+
+
 def test_delta_empty_rows():
     case = delta_case("empty", B=2, T=0, H=2, d_k=64, dtype=torch.float32, seed=1).to("cuda")
     got = run_gpu(case)
