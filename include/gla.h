@@ -250,7 +250,9 @@ int gla_delta_fwd(const gla_delta_problem* p, const void* q, const void* k, cons
                   const void* g, const void* beta, const float* h0, const int32_t* segment_ids,
                   void* o, float* hT, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward: dq, dk, dv, dg, dbeta (and dh0 if non-NULL); recomputes the forward. */
+/* Backward: dq, dk, dv, dg, dbeta (and dh0 if non-NULL).  Recomputes the states
+ * entering the chunks, and the per-chunk factors unless p->flags has
+ * GLA_DELTA_WS_FROM_FWD. */
 int gla_delta_bwd(const gla_delta_problem* p, const void* q, const void* k, const void* v,
                   const void* g, const void* beta, const float* h0, const int32_t* segment_ids,
                   const void* dO, const float* dhT, void* dq, void* dk, void* dv, void* dg,
