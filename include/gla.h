@@ -14,8 +14,16 @@
  *   - GLA_GATE_SCALAR: one gate per (b, t, h), the Mamba-2 / SSD form;
  *   - GLA_GATE_VECTOR: one gate per key channel, f_t in R^{d_k}, the GLA form.
  *
- * g holds the natural logarithm of the gate, alpha_t = exp(g_t), any finite
- * value.  There is no internal 1/sqrt(d) scale: callers pre-scale q and k.
+ * g holds the natural logarithm of the gate, alpha_t = exp(g_t).  For every
+ * finite g <= 0 (a decay; the pages' gate forms are all of this kind) the
+ * results are those of the recurrence up to rounding, however strong the decay:
+ * inside a chunk whose |g| all stay within 1.875 the vector gate's decays are
+ * factored around one reference row (every factor within exp(+-60)); a chunk
+ * with a stronger gate forms each exp(beta_r - beta_s) of its score pairs
+ * directly, and its log-gate gradient from the non-cancelling terms only.
+ * Positive g are accepted and computed by the same formulas; their results stay
+ * finite while the growth they describe stays within float32's range.  There
+ * is no internal 1/sqrt(d) scale: callers pre-scale q and k.
  *
  * Document resets (JLA page, "JLA: JAX Linear Attention", the segment_ids
  * paragraph): wherever segment_ids[b,t] differs from segment_ids[b,t-1] the
@@ -42,8 +50,12 @@
  *            vector gate     [B, T, H, d_k]      dtype
  *     h0, hT, dhT, dh0       [B, H, d_k, d_v]    float32 always
  *     segment_ids            [B, T]              int32
- * dtype is GLA_F32 (IEEE float32) or GLA_BF16 (bfloat16); products run on the
- * matrix cores in that dtype with float32 accumulation, and every state, gate
+ * dtype is GLA_F32 (IEEE float32) or GLA_BF16 (bfloat16).  bf16 products run
+ * on the bf16 matrix cores with float32 accumulation.  float32 inputs with the
+ * scalar gate and d_k = d_v = 128 run every product as three bf16 products of
+ * operands split into high and low bf16 halves (x = hi + lo), float32
+ * accumulation (about 2^-16 relative error per product, the dropped lo * lo
+ * term); other float32 shapes use the float32 matrix cores.  Every state, gate
  * prefix and gate-gradient sum is carried in float32.  Outputs in bf16 are
  * rounded to nearest even.
  *

@@ -189,4 +189,54 @@ __device__ __forceinline__ void rev_chunk_info(RevChunk* ci, const RowRegs& rr) 
     }
 }
 
+// Log-gate gradient of a vector-gate chunk for one wave's 16 key channels (lane
+// (i, j): rows 16 rt + i, channels c0 + 4 j + e) when documents end inside the
+// chunk: a serial suffix sum per channel of the per-row terms x, restarting at
+// every document end, with the boundary term bnd added to the chunk's last
+// document; 0 at reset tokens, and add[rt][e] added elsewhere.  The sums run in
+// the wave's own columns of an fp32 scratch sX[r][c] (pitch PE), so only the
+// wave synchronises.  dgo points at row 0, channel 0 of the chunk's dg, rows rs apart.
+template <typename T, int PE>
+__device__ __forceinline__ void vec_dg_serial(float* sX, float* sBndW, const RevChunk& ck, int c0,
+                                              const float (&x)[4][4], const float (&bnd)[4],
+                                              const float (&add)[4][4], int nvalid, T* dgo, int64_t rs) {
+    const int l = lane_id(), j4 = l >> 4, i16 = l & 15;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+        *reinterpret_cast<f32x4*>(sX + (16 * rt + i16) * PE + c0 + 4 * j4) = f32x4{x[rt][0], x[rt][1], x[rt][2], x[rt][3]};
+    if (i16 == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sBndW[4 * j4 + e] = bnd[e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (j4 == 0) {
+        const int c = c0 + i16;
+        float run = sBndW[i16];
+        for (int r = C - 1; r >= 0; --r) {
+            float val = 0.f;
+            if (r < nvalid) {
+                if (r < nvalid - 1 && ck.doc[r + 1] != ck.doc[r]) run = 0.f;
+                run += sX[r * PE + c];
+                const bool reset = r > 0 ? ck.doc[r] != ck.doc[r - 1] : ck.doc[0] != 0;
+                val = reset ? 0.f : run;
+            }
+            sX[r * PE + c] = val;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * rt + i16;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(sX + r * PE + c0 + 4 * j4);
+        const bool reset = r > 0 ? ck.doc[r] != ck.doc[r - 1] : ck.doc[0] != 0;
+        float dg[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dg[e] = v[e] + (reset ? 0.f : add[rt][e]);
+        if (r < nvalid) store4<T>(dgo + (int64_t)r * rs + c0 + 4 * j4, dg);
+    }
+}
+
 }  // namespace gla

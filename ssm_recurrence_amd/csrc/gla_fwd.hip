@@ -21,7 +21,10 @@
 // Vector gate: A = QA KA^T with QA = q exp(beta - m), KA = k exp(m - beta),
 // m = beta at row 31 (a reference inside the chunk keeps every exponent within
 // half the chunk's total decay); the readout uses QA * exp(m) and the update
-// KA * exp(Gamma - m).  Scalar gate: A = (q k^T) * exp(beta_r - beta_s); row
+// KA * exp(Gamma - m).  A chunk with a gate too strong for that factored form
+// (gla_exact.hpp) forms its scores from the prefixes directly, one channel tile
+// of prefixes at a time, and reads out with q exp(beta), updates with
+// k exp(Gamma - beta).  Scalar gate: A = (q k^T) * exp(beta_r - beta_s); row
 // factors exp(beta_r) and exp(Gamma - beta_s) go on the readout and update.
 //
 // Pipelining: the next chunk's q, k, v, g and reset flags are loaded into
@@ -29,6 +32,7 @@
 // [16w, 16w+16): it forms only the tiles of A^T at or below the diagonal for
 // those rows and feeds them to the A v product straight from its accumulators.
 #include "gla_common.hpp"
+#include "gla_exact.hpp"
 #include "gla_kernels.hpp"
 #include "gla_tile.hpp"
 
@@ -59,6 +63,10 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
     __shared__ float sDecay[VEC ? DK : 1];
     __shared__ float sEGm[VEC ? DK : 1];
     __shared__ int sAnyReset;
+    // strong-gate chunks: one channel tile of fp32 prefixes [row][16], the per-wave flags
+    constexpr int PBB = 20;
+    __shared__ __attribute__((aligned(16))) float sBB[VEC ? C * PBB : 4];
+    __shared__ int sStrong[4];
 
     // block -> (b, h, piece, slice); the slices of one piece are adjacent (one XCD)
     const int64_t P = a.P;
@@ -124,7 +132,10 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
         pq.store_rows(sQ, PK);
         pk.store_rows(sK, PK);
         pv.store_rows(sV, PV);
-        if constexpr (VEC) pg.store_rows(sG, PK);
+        if constexpr (VEC) {
+            pg.store_rows(sG, PK);
+            strong_flag_put(sStrong, gate_regs_strong(pg));
+        }
         if (w == 0) {
             const int r = l;
             const int doc = wave_incl_scan_i(rr.reset());
@@ -146,21 +157,61 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
             }
         }
         __syncthreads();
+        [[maybe_unused]] const bool strong = VEC && strong_flag_get<4>(sStrong);
         if (it + 1 < cend) prefetch(t0 + C);
 
+        // strong-gate chunks: this wave's A^T tiles (rows s = 16st + 4j4 + e, column
+        // r = 16w + i16) summed over the channel tiles from the prefixes themselves
+        f32x4 Ax[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) Ax[st] = zero4();
         if constexpr (VEC) {
             // ---- gate prefix on the matrix cores; QA, KA in place; per-channel factors
             f32x4 beta[CPW][4];
             gate_prefix_mfma<T, CPW, PK>(sG, tri, beta);
             const bool any_reset = sAnyReset != 0;
+            if (strong) {
+                // (loops kept rolled: this path is rare and must not add register pressure)
+                const int r = 16 * w + i16;
+                const int dr = sDoc[r];
+#pragma unroll 1
+                for (int ct = 0; ct < NCT; ++ct) {
+                    if (w == ct / CPW) {
+                        const int cc = ct % CPW;
+#pragma unroll
+                        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float b = beta[0][rt][e];
+#pragma unroll
+                                for (int u = 1; u < CPW; ++u) b = cc == u ? beta[u][rt][e] : b;
+                                sBB[(16 * rt + i16) * PBB + 4 * j4 + e] = b;
+                            }
+                    }
+                    __syncthreads();
+#pragma unroll 1
+                    for (int idx = 0; idx < 16; ++idx) {
+                        const int st = idx >> 2, e = idx & 3;
+                        const int s = 16 * st + 4 * j4 + e;
+                        if (st > w) break;
+                        if (s <= r && sDoc[s] == dr) {
+                            const float x = exact_dot<T>(sQ + r * PK + 16 * ct, sK + s * PK + 16 * ct,
+                                                         sBB + r * PBB, sBB + s * PBB, 16, 0.f);
+#pragma unroll
+                            for (int u = 0; u < 16; ++u) Ax[u >> 2][u & 3] += idx == u ? x : 0.f;
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) {
                 const int c0 = 16 * (CPW * w + cc) + 4 * j4;   // this lane's 4 channels
                 float m[4], Gam[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    m[e] = __shfl(beta[cc][1][e], 16 * j4 + 15, 64);    // row 31
-                    Gam[e] = __shfl(beta[cc][3][e], 16 * j4 + 15, 64);  // row 63
+                    m[e] = strong ? 0.f : __shfl(beta[cc][1][e], 16 * j4 + 15, 64);  // row 31
+                    Gam[e] = __shfl(beta[cc][3][e], 16 * j4 + 15, 64);               // row 63
                 }
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
@@ -170,7 +221,8 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float E = __expf(beta[cc][rt][e] - m[e]);
-                        const float Ei = __builtin_amdgcn_rcpf(E);
+                        // (strong: the update operand k exp(Gamma - beta) itself)
+                        const float Ei = strong ? __expf(Gam[e] - beta[cc][rt][e]) : __builtin_amdgcn_rcpf(E);
                         qv.set(e, qv.get(e) * E);
                         kv.set(e, kv.get(e) * Ei);
                     }
@@ -181,7 +233,7 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         sDecay[c0 + e] = any_reset ? 0.f : __expf(Gam[e]);
-                        sEGm[c0 + e] = __expf(Gam[e] - m[e]);
+                        sEGm[c0 + e] = strong ? 1.f : __expf(Gam[e] - m[e]);
                     }
                 }
                 // readout copy of the state, scaled by exp(m) per channel: this
@@ -216,8 +268,8 @@ __global__ __launch_bounds__(NT) void k_fwd(const PassArgs a) {
         f32x4 At[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            At[st] = zero4();
-            if (st <= w) {
+            At[st] = Ax[st];
+            if (st <= w && !strong) {
 #pragma unroll
                 for (int kk = 0; kk < KF; ++kk)
                     At[st] = M::mma(frag_ld<T, PK, 1>(sK, 16 * st, kk * M::KSTEP), qf[kk], At[st]);

@@ -15,13 +15,16 @@
 //   (vector gate) per-channel prefix on the matrix cores, wave w for channel
 //            tile w: QA = q exp(beta - m), KA = k exp(m - beta) in place, with
 //            m = beta at row 31, and the channel factors exp(Gamma),
-//            exp(Gamma - m), exp(m);
+//            exp(Gamma - m), exp(m); a chunk with a gate too strong for that
+//            factored form (gla_exact.hpp) gets its scores from the prefixes
+//            directly and takes m = 0 for the readout and update operands;
 //   scores   masked score tiles spread over the waves (scalar gate: times
 //            exp(beta_r - beta_s)), stored to LDS; the readout of each wave's
 //            columns; the state update of each wave's columns;
 //   output   the intra-chunk product and o = O + [first doc] (exp(beta_r)) R.
 // Operand reads are issued one step ahead of the products that consume them.
 #include "gla_common.hpp"
+#include "gla_exact.hpp"
 #include "gla_kernels.hpp"
 #include "gla_tile.hpp"
 
@@ -39,6 +42,7 @@ constexpr int PKH = DK + 20;  // k (KA)
 constexpr int PH = DK + 8;    // v, last-document v, gate tile
 constexpr int PA = C + 16;    // scores [r][s]
 constexpr int PO = DV + 8;    // output rows, written to HBM a whole row at a time
+constexpr int PBF = DK + 4;   // fp32 prefixes of a chunk (strong-gate chunks only)
 
 template <bool VEC>
 struct FwdHLds {
@@ -47,13 +51,19 @@ struct FwdHLds {
     bf16 sV[C * PH];
     bf16 sVu[C * PH];
     bf16 sA[C * PA];
-    bf16 sO[C * PO];
+    // the output rows; in a strong-gate chunk first the fp32 gate prefixes, which
+    // are dead before the output is assembled
+    union {
+        bf16 sO[C * PO];
+        float sBF[VEC ? C * PBF : 4];
+    };
     bf16 sG[VEC ? C * PH : 8];
     bf16 sKU[VEC ? C * PH : 8];    // vector gate: k exp(Gamma - beta), the update's operand
     alignas(16) int sDoc[C];
     alignas(16) float sBeta[C];
     alignas(16) float sDecay[VEC ? DK : 4];
     alignas(16) float sEm[VEC ? DK : 4];
+    alignas(16) int sStrong[8];
     int sAnyReset;
 };
 
@@ -153,7 +163,10 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
         pq.store_rows_b64(sm.sQ, PQ);  // rows of q and k are 8-byte aligned only
         pk.store_rows_b64(sm.sK, PKH);
         pv.store_rows(sm.sV, PH);
-        if constexpr (VEC) pg.store_rows(sm.sG, PH);
+        if constexpr (VEC) {
+            pg.store_rows(sm.sG, PH);
+            strong_flag_put(sm.sStrong, gate_regs_strong(pg));
+        }
         {
             using TR = TileRegs<bf16, DV, NTH>;
             static_assert(TR::NV_TOT % NTH == 0, "");
@@ -170,6 +183,7 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
         }
         if (it + 1 < cend) prefetch(t0 + C);
         __syncthreads();
+        [[maybe_unused]] const bool strong = VEC && strong_flag_get<8>(sm.sStrong);
 
         if constexpr (VEC) {
             // ---- per-channel prefix for channel tile w; QA, KA in place; channel factors
@@ -186,6 +200,34 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
                 m[e] = __shfl(beta[0][1][e], 16 * j4 + 15, 64);    // row 31
                 Gam[e] = __shfl(beta[0][3][e], 16 * j4 + 15, 64);  // row 63
             }
+            if (strong) {
+                // scores from the prefixes themselves (raw q, k still in LDS); then the
+                // readout operand q exp(beta) with the unscaled state (m = 0) and the update
+                // operand k exp(Gamma - beta)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sm.sBF[(16 * rt + i16) * PBF + c0 + e] = beta[0][rt][e];
+                __syncthreads();
+                exact_scores<bf16, DK, NTH, PQ, PKH, PBF, PA, false>(sm.sA, sm.sQ, sm.sK, sm.sBF, sm.sDoc);
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[e] = 0.f;
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int r = 16 * rt + i16;
+                    Vec4<bf16> qv = Vec4<bf16>::load(sm.sQ + r * PQ + c0);
+                    const Vec4<bf16> kv = Vec4<bf16>::load(sm.sK + r * PKH + c0);
+                    Vec4<bf16> ku;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        qv.set(e, qv.get(e) * __expf(beta[0][rt][e]));
+                        ku.set(e, kv.get(e) * __expf(Gam[e] - beta[0][rt][e]));
+                    }
+                    qv.store(sm.sQ + r * PQ + c0);
+                    ku.store(sm.sKU + r * PH + c0);
+                }
+            } else {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const int r = 16 * rt + i16;
@@ -204,6 +246,7 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
                 for (int e = 0; e < 4; ++e) ku.set(e, kv.get(e) * __expf(Gam[e] - m[e]));
                 ku.store(sm.sKU + r * PH + c0);
             }
+            }
             if (i16 == 0) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -216,7 +259,7 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
 
         // ---- masked score tiles, computed transposed (rows s, column r), stored sA[r][s];
         // tiles 10 and 11 are the zero tiles (0,1) and (2,3) that a 32-wide step reads
-        for (int ti = w; ti < 12; ti += 8) {
+        for (int ti = w; ti < (strong ? 0 : 12); ti += 8) {
             const int rt = score_tile_rt(ti);
             const int st = score_tile_st(ti);
             f32x4 acc = zero4();

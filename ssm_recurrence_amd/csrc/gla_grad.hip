@@ -26,6 +26,11 @@
 //   rowsum(S1 * dS1)_c = decay_c rowsum(S0 * dS1)_c + sum_s KU[s][c] (v dS1^T)[s][c],
 // and the second sum reuses the inter-chunk part of dk.
 //
+// A vector-gate chunk whose gates are too strong for the factored form
+// QA = q exp(beta - m), KA = k exp(m - beta) (gla_exact.hpp) forms A and the
+// intra-chunk parts of dq and dk from the prefixes directly, and its
+// carried-state terms from exp(beta) and exp(Gamma - beta).
+//
 // Two kinds of workgroups per chunk:
 //   QK: 64 key channels, each wave 16 of them: dq, dk and dg (the suffix sums
 //       stay inside one wave); the state and its gradient come straight from
@@ -33,6 +38,7 @@
 //   V:  64 value columns, each wave 16 of them: dv.
 #include "gla_bwd.hpp"
 #include "gla_common.hpp"
+#include "gla_exact.hpp"
 #include "gla_kernels.hpp"
 #include "gla_tile.hpp"
 
@@ -81,6 +87,7 @@ struct GradSmall {
     float sBnd[4][16];    // per-wave boundary terms (QK role, chunks with documents inside)
     float sXs[4][C];      // scalar gate: per-wave partial sums
     float sBs[4];
+    int sStrong[4];       // vector gate: per-wave flags, a gate too strong for the factored form
 };
 
 // ============================================================== QK role
@@ -149,7 +156,10 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
 
     pq.store_rows(sQ, PB);
     pk.store_rows(sK, PB);
-    if constexpr (VEC) pg.store_rows(sG, PB);
+    if constexpr (VEC) {
+        pg.store_rows(sG, PB);
+        strong_flag_put(sm.sStrong, gate_regs_strong(pg));
+    }
     pv.store_rows(sV, PV);
     pdo.store_rows(sdO, PV);
     if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
@@ -158,6 +168,7 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
 #pragma unroll
     for (int kk = 0; kk < NKV; ++kk) sd = frag_dot(s0f[kk], dsf[kk], sd);
     __syncthreads();
+    [[maybe_unused]] const bool strong = VEC && strong_flag_get<4>(sm.sStrong);
 
     // raw q, k at this lane's output positions (rows 16rt + i16, channels cw + 4j4 + e)
     Vec4<T> qraw[4], kraw[4];
@@ -166,7 +177,9 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
         qraw[rt] = Vec4<T>::load(sQ + (16 * rt + i16) * PB + 16 * w + 4 * j4);
         kraw[rt] = Vec4<T>::load(sK + (16 * rt + i16) * PB + 16 * w + 4 * j4);
     }
-    float E[4][4];  // exp(beta - m) at those positions (vector gate)
+    // exp(beta - m) at those positions (vector gate; strong-gate chunks: beta itself)
+    float E[4][4];
+    // em = exp(m), egm = exp(Gamma - m) (strong-gate chunks: 1 and Gamma itself)
     float em[4], egm[4], dec[4];
     if constexpr (VEC) {
         // gate prefix on the matrix cores; this wave's q, k columns scaled in place to
@@ -182,10 +195,16 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
         const bool reset_in_chunk = ck.last_reset >= 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            em[e] = __expf(m[e]);
-            egm[e] = __expf(Gam[e] - m[e]);
+            em[e] = strong ? 1.f : __expf(m[e]);
+            egm[e] = strong ? Gam[e] : __expf(Gam[e] - m[e]);
             dec[e] = reset_in_chunk ? 0.f : __expf(Gam[e]);
         }
+        if (strong) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) E[rt][e] = beta[0][rt][e];
+        } else {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             Vec4<T> qa, ka;
@@ -197,6 +216,7 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
             }
             qa.store(sQ + (16 * rt + i16) * PB + 16 * w + 4 * j4);
             ka.store(sK + (16 * rt + i16) * PB + 16 * w + 4 * j4);
+        }
         }
     } else {
 #pragma unroll
@@ -222,26 +242,42 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     __syncthreads();
 
     const bool gqa = G > 1;
-    float x[4][4];  // q*dq - k*dk
+    // q*dq - k*dk; strong-gate chunks: the same without the diagonal pairs of the
+    // scores (which cancel) and without k * (the carried part of dk), kept in z
+    float x[4][4];
+    [[maybe_unused]] float z[4][4];
     // ---- dq^T = KA^T dA^T + [first doc] exp(m) S0 dO^T, times exp(beta - m)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         f32x4 a1 = zero4(), a2 = zero4();
         const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
+        if (!strong) {
 #pragma unroll
-        for (int k0 = 0; k0 < kend; k0 += KS)
-            a1 = M::mma(frag_col<T, PB, false>(sK, 16 * w, k0), frag_ld<T, PB, 1>(sdA, 16 * rt, k0), a1);
+            for (int k0 = 0; k0 < kend; k0 += KS)
+                a1 = M::mma(frag_col<T, PB, false>(sK, 16 * w, k0), frag_ld<T, PB, 1>(sdA, 16 * rt, k0), a1);
+        }
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk)
             a2 = M::mma(s0f[kk], frag_ld<T, PV, 1>(sdO, 16 * rt, kk * KS), a2);
         const int r = 16 * rt + i16;
         const float fq = ck.fq[r];
         float dq[4];
+        if (strong) {
+            float dx[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f};
+            exact_dq<T, PB, PB>(dx, dd, rt, E, sdA, sK + 16 * w + 4 * j4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float dqp = a1[e] + fq * em[e] * a2[e];
-            dq[e] = VEC ? E[rt][e] * dqp : dqp;
-            x[rt][e] = qraw[rt].get(e) * dq[e];
+            for (int e = 0; e < 4; ++e) {
+                const float dqx = dx[e] + fq * __expf(E[rt][e]) * a2[e];
+                dq[e] = dqx + dd[e];
+                x[rt][e] = qraw[rt].get(e) * dqx;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float dqp = a1[e] + fq * em[e] * a2[e];
+                dq[e] = VEC ? E[rt][e] * dqp : dqp;
+                x[rt][e] = qraw[rt].get(e) * dq[e];
+            }
         }
         if (r < nvalid) {
             if (!gqa) store4<T>((T*)a.dq + (b * T_ + t0 + r) * a.ld_dqk + hq * DK + cw + 4 * j4, dq);
@@ -255,23 +291,38 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     for (int st = 0; st < 4; ++st) {
         f32x4 a1 = zero4(), a2 = zero4();
         const int kbeg = (16 * st / KS) * KS;
+        if (!strong) {
 #pragma unroll
-        for (int k0 = kbeg; k0 < C; k0 += KS)
-            a1 = M::mma(frag_col<T, PB, false>(sQ, 16 * w, k0), frag_col<T, PB, false>(sdA, 16 * st, k0), a1);
+            for (int k0 = kbeg; k0 < C; k0 += KS)
+                a1 = M::mma(frag_col<T, PB, false>(sQ, 16 * w, k0), frag_col<T, PB, false>(sdA, 16 * st, k0), a1);
+        }
 #pragma unroll
         for (int kk = 0; kk < NKV; ++kk)
             a2 = M::mma(dsf[kk], frag_ld<T, PV, 1>(sV, 16 * st, kk * KS), a2);
         const int s = 16 * st + i16;
         const float fu = ck.fu[s];
         float dk[4];
+        if (strong) {
+            float dx[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f};
+            exact_dk<T, PB, PB>(dx, dd, st, E, sdA, sQ + 16 * w + 4 * j4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float inter = fu * egm[e] * a2[e];
-            const float rE = VEC ? __builtin_amdgcn_rcpf(E[st][e]) : 1.f;
-            const float kr = kraw[st].get(e);
-            dk[e] = (a1[e] + inter) * rE;
-            x[st][e] -= kr * dk[e];
-            bsum[e] += kr * inter * rE;
+            for (int e = 0; e < 4; ++e) {
+                const float inter = fu * __expf(egm[e] - E[st][e]) * a2[e];
+                const float kr = kraw[st].get(e);
+                dk[e] = dx[e] + dd[e] + inter;
+                x[st][e] -= kr * dx[e];
+                z[st][e] = kr * inter;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float inter = fu * egm[e] * a2[e];
+                const float rE = VEC ? __builtin_amdgcn_rcpf(E[st][e]) : 1.f;
+                const float kr = kraw[st].get(e);
+                dk[e] = (a1[e] + inter) * rE;
+                x[st][e] -= kr * dk[e];
+                bsum[e] += kr * inter * rE;
+            }
         }
         if (s < nvalid) {
             if (!gqa) store4<T>((T*)a.dk + (b * T_ + t0 + s) * a.ld_dqk + hq * DK + cw + 4 * j4, dk);
@@ -288,6 +339,23 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
     // ---- gate gradient
     if constexpr (VEC) {
         T* dgo = (T*)a.dg + ((b * T_ + t0) * a.H + h) * DK + cw + 4 * j4;
+        // strong-gate chunks: dg[r] = (suffix of x from r, within r's document) + (sum of
+        // k * (carried part of dk) over the rows before r) + [no reset] decay rowsum(S0 * dS1),
+        // the same sum as the suffix form with every cancelling pair left out (the
+        // rows before r reach dS1 only through token r's gate; z is 0 outside the
+        // chunk's last document); bnd holds the decay term alone then (bsum is 0)
+        float zp[4][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float zc[4] = {0.f, 0.f, 0.f, 0.f}, zo[4] = {0.f, 0.f, 0.f, 0.f};
+            if (strong) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) zc[rt] = z[rt][e];
+                rows_excl_prefix(zc, zo);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) zp[rt][e] = zo[rt];
+        }
         if (ck.first_reset == C) {
             // no reset in this chunk: suffix sums over the 16 rows of a tile (lanes),
             // then across tiles, starting from the boundary term
@@ -298,7 +366,7 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float y = row_suffix16(x[rt][e]);
-                    dg[e] = y + carry[e];
+                    dg[e] = y + carry[e] + zp[rt][e];
                     carry[e] += __shfl(y, 0, 16);
                 }
                 const int r = 16 * rt + i16;
@@ -338,7 +406,10 @@ __device__ void grad_qk(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, 
             for (int rt = 0; rt < 4; ++rt) {
                 const int r = 16 * rt + i16;
                 const f32x4 v = *reinterpret_cast<const f32x4*>(sX + r * PE + 16 * w + 4 * j4);
-                const float dg[4] = {v[0], v[1], v[2], v[3]};
+                const bool reset = r > 0 ? ck.doc[r] != ck.doc[r - 1] : ck.doc[0] != 0;
+                float dg[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dg[e] = v[e] + (reset ? 0.f : zp[rt][e]);
                 if (r < nvalid) store4<T>(dgo + (int64_t)r * a.H * DK, dg);
             }
         }
@@ -416,7 +487,10 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
 
     pq.store_rows(sQ, PK);
     pk.store_rows(sK, PK);
-    if constexpr (VEC) pg.store_rows(sG, PK);
+    if constexpr (VEC) {
+        pg.store_rows(sG, PK);
+        strong_flag_put(sm.sStrong, gate_regs_strong(pg));
+    }
     pdo.store_rows(sdO, PB);
     if constexpr (!VEC) {
 #pragma unroll
@@ -424,17 +498,54 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
     }
     if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
     __syncthreads();
+    [[maybe_unused]] const bool strong = VEC && strong_flag_get<4>(sm.sStrong);
 
+    // strong-gate chunks: this wave's score tiles (C layout: rows r = 16rt + 4j4 + e,
+    // column s = 16st + i16) summed over the channel tiles from the prefixes themselves
+    f32x4 Ax[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) Ax[u] = zero4();
     if constexpr (VEC) {
         f32x4 beta[CPW][4];
         gate_prefix_mfma<T, CPW, PK>(sG, tri, beta);
+        if (strong) {
+            // one channel tile of prefixes at a time, [row][16] in the place of A^T
+            constexpr int PBB = 20;
+            float* sBB = reinterpret_cast<float*>(sAT);
+            static_assert(C * PBB * 4 <= Cfg::TILE64, "prefix block does not fit");
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                if (w == ct / CPW) {
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sBB[(16 * rt + i16) * PBB + 4 * j4 + e] = beta[ct % CPW][rt][e];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    const int ti = w + 4 * u;
+                    if (ti >= 10) continue;
+                    const int rt = score_tile_rt(ti), st = score_tile_st(ti);
+                    const int s = 16 * st + i16;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * rt + 4 * j4 + e;
+                        if (s <= r && ck.doc[s] == ck.doc[r])
+                            Ax[u][e] = exact_dot<T>(sQ + r * PK + 16 * ct, sK + s * PK + 16 * ct,
+                                                    sBB + r * PBB, sBB + s * PBB, 16, Ax[u][e]);
+                    }
+                }
+                __syncthreads();
+            }
+        }
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc) {
             const int c4 = 16 * (CPW * w + cc) + 4 * j4;
             float m[4], Gam[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                m[e] = __shfl(beta[cc][1][e], 16 * j4 + 15, 64);
+                m[e] = strong ? 0.f : __shfl(beta[cc][1][e], 16 * j4 + 15, 64);
                 Gam[e] = __shfl(beta[cc][3][e], 16 * j4 + 15, 64);
             }
 #pragma unroll
@@ -445,15 +556,17 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float E = __expf(beta[cc][rt][e] - m[e]);
+                    // (strong: k exp(Gamma - beta) itself, the operand of the dv update term)
+                    const float Ei = strong ? __expf(Gam[e] - beta[cc][rt][e]) : __builtin_amdgcn_rcpf(E);
                     qv.set(e, qv.get(e) * E);
-                    kv.set(e, kv.get(e) * __builtin_amdgcn_rcpf(E));
+                    kv.set(e, kv.get(e) * Ei);
                 }
                 qv.store(sQ + r * PK + c4);
                 kv.store(sK + r * PK + c4);
             }
             if (i16 == 0)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.sEGm[c4 + e] = __expf(Gam[e] - m[e]);
+                for (int e = 0; e < 4; ++e) sm.sEGm[c4 + e] = strong ? 1.f : __expf(Gam[e] - m[e]);
         }
         __syncthreads();
         // dS1 rows scaled by exp(Gamma - m) of their channel, so that KA dS1' = KU dS1
@@ -464,11 +577,13 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
     }
 
     // ---- A = QA KA^T on the lower tiles (+ two zero upper tiles), transposed: sAT[s][r]
-    for (int ti = w; ti < 12; ti += 4) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int ti = w + 4 * u;
         const int rt = score_tile_rt(ti);
         const int st = score_tile_st(ti);
-        f32x4 acc = zero4();
-        if (ti < 10) {
+        f32x4 acc = Ax[u];
+        if (ti < 10 && !strong) {
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += KS)
                 acc = M::mma(frag_ld<T, PK, 1>(sQ, 16 * rt, k0), frag_ld<T, PK, 1>(sK, 16 * st, k0), acc);

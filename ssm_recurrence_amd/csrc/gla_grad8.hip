@@ -20,10 +20,14 @@
 //            dv for its 16 value columns;
 //   phase 4  (walk) the state gradient at the previous chunk's end.
 // The scalar gate's log-gate gradient sums over all 128 channels, which are
-// all in this workgroup, so it is finished here too.  In the walk the state
+// all in this workgroup, so it is finished here too.  A vector-gate chunk with a
+// gate too strong for the factored form (gla_exact.hpp) forms A and the
+// intra-chunk parts of dq and dk from the prefixes directly, and its
+// carried-state terms from exp(beta) and exp(Gamma - beta).  In the walk the state
 // gradient's rows come from LDS instead of HBM and no state gradient is stored.
 #include "gla_bwd.hpp"
 #include "gla_common.hpp"
+#include "gla_exact.hpp"
 #include "gla_kernels.hpp"
 #include "gla_tile.hpp"
 
@@ -42,6 +46,7 @@ struct Grad8Cfg {
     static constexpr int PB = 64 + 16;             // [64][64] score tiles
     static constexpr int PE = 132;                 // fp32 [64][128] dg scratch
     static constexpr int PF = 132;                 // fp32 [128][128] state gradient (walk)
+    static constexpr int PBF = 132;                // fp32 [64][128] prefixes (strong-gate chunks)
     static constexpr int TILE = C * P * 2;
     static constexpr int OFF_Q = 0, OFF_K = TILE, OFF_G = 2 * TILE;
     static constexpr int OFF_V = OFF_G + (VEC ? TILE : 0);
@@ -51,6 +56,7 @@ struct Grad8Cfg {
     static constexpr int OFF_DS = OFF_AT + C * PB * 2;  // dS1' [c][n] (walk: fp32)
     static constexpr int BYTES = OFF_DS + (WALK ? DK * PF * 4 : DK * P * 2);
     static_assert(2 * TILE >= C * PE * 4, "dg scratch does not fit in the v / dO region");
+    static_assert(!VEC || DK * P * 2 >= C * PBF * 4, "prefixes do not fit in the state-gradient region");
 };
 
 // WALK (scalar gate only): a workgroup walks the chunks of one (b, h, piece) from
@@ -72,6 +78,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     __shared__ RevChunk ck;
     __shared__ float sBs[8];
     __shared__ float sBnd[VEC ? 8 : 1][16];
+    __shared__ int sStrong[8];
     T* sQ = reinterpret_cast<T*>(lds + Cfg::OFF_Q);
     T* sK = reinterpret_cast<T*>(lds + Cfg::OFF_K);
     T* sG = reinterpret_cast<T*>(lds + Cfg::OFF_G);  // vector gate only
@@ -81,6 +88,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     T* sAT = reinterpret_cast<T*>(lds + Cfg::OFF_AT);
     T* sdS = reinterpret_cast<T*>(lds + Cfg::OFF_DS);
     float* sM = reinterpret_cast<float*>(lds + Cfg::OFF_DS);  // walk: state gradient [c][n]
+    // strong-gate chunks: the fp32 prefixes [r][c], until the state-gradient rows are staged
+    float* sBF = reinterpret_cast<float*>(lds + Cfg::OFF_DS);
     float* sX = reinterpret_cast<float*>(lds + Cfg::OFF_V);  // dg scratch [r][c], after dv
     // scalar gate: per-wave row sums [8][C] for dg, in the dA tile (read only before dv)
     float (*sXs)[C] = reinterpret_cast<float (*)[C]>(lds + Cfg::OFF_DA);
@@ -182,11 +191,15 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     }
     pq.store_rows(sQ, P);
     pk.store_rows(sK, P);
-    if constexpr (VEC) pg.store_rows(sG, P);
+    if constexpr (VEC) {
+        pg.store_rows(sG, P);
+        strong_flag_put(sStrong, gate_regs_strong(pg));
+    }
     pv.store_rows(sV, P);
     pdo.store_rows(sdO, P);
     if (w == 0) rev_chunk_info<T, VEC>(&ck, rr);
     __syncthreads();
+    [[maybe_unused]] const bool strong = VEC && strong_flag_get<8>(sStrong);
     // The next item's tiles (after the last item: this one's again, unused).  The
     // requests are unconditional so that a wait for this item's S0 rows, requested
     // before them, is counted exactly and does not wait for them as well.
@@ -204,6 +217,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
         qraw[rt] = Vec4<T>::load(sQ + (16 * rt + i16) * P + cw + 4 * j4);
         kraw[rt] = Vec4<T>::load(sK + (16 * rt + i16) * P + cw + 4 * j4);
     }
+    // factored form: E = exp(beta - m), em = exp(m), egm = exp(Gamma - m); strong-gate
+    // chunks: E = beta, egm = Gamma themselves (the exponentials are formed per use)
     float E[4][4];
     float em[4], egm[4], dec[4];
     if constexpr (VEC) {
@@ -218,10 +233,19 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
         const bool reset_in_chunk = ck.last_reset >= 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            em[e] = __expf(m[e]);
-            egm[e] = __expf(Gam[e] - m[e]);
+            em[e] = strong ? 1.f : __expf(m[e]);
+            egm[e] = strong ? Gam[e] : __expf(Gam[e] - m[e]);
             dec[e] = reset_in_chunk ? 0.f : __expf(Gam[e]);
         }
+        if (strong) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    E[rt][e] = beta[0][rt][e];
+                    sBF[(16 * rt + i16) * Cfg::PBF + cw + 4 * j4 + e] = beta[0][rt][e];
+                }
+        } else {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             Vec4<T> qa, ka;
@@ -255,6 +279,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
             for (int e = 0; e < 8; ++e) d[e] = (bf16)((float)d[e] * egm_i);
             *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = d;
         }
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -276,7 +301,8 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     }
     __syncthreads();
     // A = QA KA^T tiles (all channels, now scaled), masked, stored transposed A^T[s][r]
-    for (int ti = w; ti < 12; ti += Cfg::NW) {
+    if (strong) exact_scores<T, DK, NTH, P, P, Cfg::PBF, PB, true>(sAT, sQ, sK, sBF, ck.doc);
+    for (int ti = w; ti < (strong ? 0 : 12); ti += Cfg::NW) {
         const int rt = score_tile_rt(ti);
         const int st = score_tile_st(ti);
         f32x4 acc = zero4();
@@ -290,67 +316,157 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
 
     // ---- phase 3a: dq, dk for key channels cw .. cw + 15 (computed transposed)
     const bool gqa = G > 1;
-    float x[4][4];  // q*dq - k*dk
+    float x[4][4];  // q*dq - k*dk (factored form)
+    float bnd[4];   // the boundary term rowsum(S1 * dS1) per channel (factored form)
+    if (strong) {
+        // A strong-gate chunk (gla_exact.hpp): the intra-chunk parts of dq and dk from
+        // the prefixes (E holds beta, egm holds Gamma), the carried parts with exp(beta)
+        // and exp(Gamma - beta).  The log-gate gradient goes out here too, as
+        //   dg[r] = (suffix of y from r within r's document) + (sum of z over the rows
+        //           before r) + [no reset] decay rowsum(S0 * dS1),
+        // y = q * dq - k * dk without the diagonal score pairs (they cancel exactly) and
+        // without z = k * (carried part of dk): the suffix form with every cancelling
+        // pair left out (rows before r reach dS1 only through token r's gate; z is 0
+        // outside the chunk's last document).  Scratch: the prefixes' region, free
+        // once every wave is past the scores.
+        __syncthreads();
+        float y[4][4], z[4][4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        f32x4 a1 = zero4(), a2 = zero4();
-        const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 a2 = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < kend; k0 += KS)
-            a1 = M::mma(frag_col<T, P, false>(sK, cw, k0), frag_ld<T, PB, 1>(sdA, 16 * rt, k0), a1);
+            for (int kk = 0; kk < NKV; ++kk) a2 = M::mma(s0f[kk], frag_ld<T, P, 1>(sdO, 16 * rt, kk * KS), a2);
+            const int r = 16 * rt + i16;
+            const float fq = ck.fq[r];
+            float dx[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f}, dq[4];
+            exact_dq<T, P, PB>(dx, dd, rt, E, sdA, sK + cw + 4 * j4);
 #pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) a2 = M::mma(s0f[kk], frag_ld<T, P, 1>(sdO, 16 * rt, kk * KS), a2);
-        const int r = 16 * rt + i16;
-        const float fq = ck.fq[r];
-        float dq[4];
+            for (int e = 0; e < 4; ++e) {
+                const float dqx = dx[e] + fq * __expf(E[rt][e]) * a2[e];
+                dq[e] = dqx + dd[e];
+                y[rt][e] = qraw[rt].get(e) * dqx;
+            }
+            if (r < nvalid) {
+                if (!gqa) store4<T>((T*)a.dq + (b * T_ + t0 + r) * a.ld_dqk + hq * DK + cw + 4 * j4, dq);
+                else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            f32x4 a2 = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKV; ++kk) a2 = M::mma(dsf[kk], frag_ld<T, P, 1>(sV, 16 * st, kk * KS), a2);
+            const int s = 16 * st + i16;
+            const float fu = ck.fu[s];
+            float dx[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f}, dk[4];
+            exact_dk<T, P, PB>(dx, dd, st, E, sdA, sQ + cw + 4 * j4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float inter = fu * __expf(egm[e] - E[st][e]) * a2[e];
+                const float kr = kraw[st].get(e);
+                dk[e] = dx[e] + dd[e] + inter;
+                y[st][e] -= kr * dx[e];
+                z[st][e] = kr * inter;
+            }
+            if (s < nvalid) {
+                if (!gqa) store4<T>((T*)a.dk + (b * T_ + t0 + s) * a.ld_dqk + hq * DK + cw + 4 * j4, dk);
+                else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
+            }
+        }
+        float zp[4][4], bnd0[4];
+        float sd = 0.f;  // rowsum(S0 * dS1) of channel cw + i16 over this lane's n
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) sd = frag_dot(s0f[kk], dsf[kk], sd);
+        sd += __shfl_xor(sd, 16, 64);
+        sd += __shfl_xor(sd, 32, 64);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float dqp = a1[e] + fq * em[e] * a2[e];
-            dq[e] = VEC ? E[rt][e] * dqp : dqp;
-            x[rt][e] = qraw[rt].get(e) * dq[e];
+            float zc[4], zo[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) zc[rt] = z[rt][e];
+            rows_excl_prefix(zc, zo);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) zp[rt][e] = zo[rt];
+            bnd0[e] = dec[e] * __shfl(sd, 4 * j4 + e, 64);
         }
-        if (r < nvalid) {
-            if (!gqa) store4<T>((T*)a.dq + (b * T_ + t0 + r) * a.ld_dqk + hq * DK + cw + 4 * j4, dq);
-            else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
+        vec_dg_serial<T, Cfg::PBF>(sBF, sBnd[w], ck, cw, y, bnd0, zp, nvalid,
+                                   (T*)a.dg + ((b * T_ + t0) * a.H + h) * DK, a.H * DK);
+        // the update operand KU = k exp(Gamma - beta) in place of this wave's k columns
+        // (only this wave read them above) for dv; the state-gradient rows, unscaled, in
+        // the scratch's place once every wave is done with it
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            Vec4<T> ku;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ku.set(e, kraw[st].get(e) * __expf(egm[e] - E[st][e]));
+            ku.store(sK + (16 * st + i16) * P + cw + 4 * j4);
         }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk)
+            *reinterpret_cast<bf16x8*>(sdS + (cw + i16) * P + kk * KS + 8 * j4) = dsf[kk];
+        __syncthreads();  // A^T complete
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 a1 = zero4(), a2 = zero4();
+            const int kend = ((16 * (rt + 1) + KS - 1) / KS) * KS;
+#pragma unroll
+            for (int k0 = 0; k0 < kend; k0 += KS)
+                a1 = M::mma(frag_col<T, P, false>(sK, cw, k0), frag_ld<T, PB, 1>(sdA, 16 * rt, k0), a1);
+#pragma unroll
+            for (int kk = 0; kk < NKV; ++kk) a2 = M::mma(s0f[kk], frag_ld<T, P, 1>(sdO, 16 * rt, kk * KS), a2);
+            const int r = 16 * rt + i16;
+            const float fq = ck.fq[r];
+            float dq[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float dqp = a1[e] + fq * em[e] * a2[e];
+                dq[e] = VEC ? E[rt][e] * dqp : dqp;
+                x[rt][e] = qraw[rt].get(e) * dq[e];
+            }
+            if (r < nvalid) {
+                if (!gqa) store4<T>((T*)a.dq + (b * T_ + t0 + r) * a.ld_dqk + hq * DK + cw + 4 * j4, dq);
+                else store4<float>(a.ws_dq + ((b * T_ + t0 + r) * a.H + h) * DK + cw + 4 * j4, dq);
+            }
+        }
+        float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            f32x4 a1 = zero4(), a2 = zero4();
+            const int kbeg = (16 * st / KS) * KS;
+#pragma unroll
+            for (int k0 = kbeg; k0 < C; k0 += KS)
+                a1 = M::mma(frag_col<T, P, false>(sQ, cw, k0), frag_col<T, PB, false>(sdA, 16 * st, k0), a1);
+#pragma unroll
+            for (int kk = 0; kk < NKV; ++kk) a2 = M::mma(dsf[kk], frag_ld<T, P, 1>(sV, 16 * st, kk * KS), a2);
+            const int s = 16 * st + i16;
+            const float fu = ck.fu[s];
+            float dk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float inter = fu * egm[e] * a2[e];
+                const float rE = VEC ? __builtin_amdgcn_rcpf(E[st][e]) : 1.f;
+                const float kr = kraw[st].get(e);
+                dk[e] = (a1[e] + inter) * rE;
+                x[st][e] -= kr * dk[e];
+                bsum[e] += kr * inter * rE;
+            }
+            if (s < nvalid) {
+                if (!gqa) store4<T>((T*)a.dk + (b * T_ + t0 + s) * a.ld_dqk + hq * DK + cw + 4 * j4, dk);
+                else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
+            }
+        }
+        // boundary term rowsum(S1 * dS1) per channel cw + 4j4 + e
+        float sd = 0.f;  // rowsum(S0 * dS1) of channel cw + i16 over this lane's n
+#pragma unroll
+        for (int kk = 0; kk < NKV; ++kk) sd = frag_dot(s0f[kk], dsf[kk], sd);
+        sd += __shfl_xor(sd, 16, 64);
+        sd += __shfl_xor(sd, 32, 64);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bnd[e] = dec[e] * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
+        __syncthreads();  // A^T complete
     }
-    float bsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        f32x4 a1 = zero4(), a2 = zero4();
-        const int kbeg = (16 * st / KS) * KS;
-#pragma unroll
-        for (int k0 = kbeg; k0 < C; k0 += KS)
-            a1 = M::mma(frag_col<T, P, false>(sQ, cw, k0), frag_col<T, PB, false>(sdA, 16 * st, k0), a1);
-#pragma unroll
-        for (int kk = 0; kk < NKV; ++kk) a2 = M::mma(dsf[kk], frag_ld<T, P, 1>(sV, 16 * st, kk * KS), a2);
-        const int s = 16 * st + i16;
-        const float fu = ck.fu[s];
-        float dk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float inter = fu * egm[e] * a2[e];
-            const float rE = VEC ? __builtin_amdgcn_rcpf(E[st][e]) : 1.f;
-            const float kr = kraw[st].get(e);
-            dk[e] = (a1[e] + inter) * rE;
-            x[st][e] -= kr * dk[e];
-            bsum[e] += kr * inter * rE;
-        }
-        if (s < nvalid) {
-            if (!gqa) store4<T>((T*)a.dk + (b * T_ + t0 + s) * a.ld_dqk + hq * DK + cw + 4 * j4, dk);
-            else store4<float>(a.ws_dk + ((b * T_ + t0 + s) * a.H + h) * DK + cw + 4 * j4, dk);
-        }
-    }
-    // boundary term rowsum(S1 * dS1) per channel cw + 4j4 + e
-    float sd = 0.f;  // rowsum(S0 * dS1) of channel cw + i16 over this lane's n
-#pragma unroll
-    for (int kk = 0; kk < NKV; ++kk) sd = frag_dot(s0f[kk], dsf[kk], sd);
-    sd += __shfl_xor(sd, 16, 64);
-    sd += __shfl_xor(sd, 32, 64);
-    float bnd[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bnd[e] = dec[e] * __shfl(sd, 4 * j4 + e, 64) + row_sum16(bsum[e]);
-    __syncthreads();  // A^T complete
 
     // ---- phase 3b: dv^T = dO^T A + [last doc] dS1'^T KA^T for value columns cw .. cw + 15
     {
@@ -389,6 +505,9 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
 
     // ---- phase 3c: log-gate gradient
     if constexpr (VEC) {
+        if (strong) {
+            // (done with dq and dk above)
+        } else {
         T* dgo = (T*)a.dg + ((b * T_ + t0) * a.H + h) * DK + cw + 4 * j4;
         if (ck.first_reset == C) {
             float carry[4] = {bnd[0], bnd[1], bnd[2], bnd[3]};
@@ -442,6 +561,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
                 const float dg[4] = {v[0], v[1], v[2], v[3]};
                 if (r < nvalid) store4<T>(dgo + (int64_t)r * a.H * DK, dg);
             }
+        }
         }
     } else {
         // scalar gate: sum over all 128 channels of this workgroup, then a segmented

@@ -91,6 +91,22 @@ def _gate(gen, shape, kind: str):
         return -torch.exp(u) * torch.nn.functional.softplus(x)
     if kind == "gla":            # logsigmoid(N(0,1)) / 16
         return torch.nn.functional.logsigmoid(x) / 16.0
+    # Strong decays (scaled by gate_mult): every channel -1; channels alternating
+    # between -1 and -1/800 (so that x8 gives -8 and -0.01); each element -1 or
+    # -1/800 at random; -1 in the first half of the sequence and the GLA
+    # distribution in the second, so strong and ordinary chunks alternate in a row.
+    if kind == "unit":
+        return -torch.ones(shape)
+    if kind == "mix_channels":
+        alt = (torch.arange(shape[-1]) % 2 == 0).to(torch.float32)
+        return -(alt + (1.0 - alt) / 800.0).expand(shape).clone()
+    if kind == "mix_random":
+        pick = (torch.rand(shape, generator=gen) < 0.5).to(torch.float32)
+        return -(pick + (1.0 - pick) / 800.0)
+    if kind == "half_unit":
+        g = torch.nn.functional.logsigmoid(x) / 16.0
+        g[:, : shape[1] // 2] = -1.0
+        return g
     raise ValueError(kind)
 
 

@@ -246,3 +246,35 @@ def test_strong_decay_stays_finite():
     case = small_case(seed=11, B=1, T=192, H=2, d=128, gate="vector", dtype=torch.bfloat16,
                       gate_kind="gla", gate_mult=10.0)
     check(case)
+
+
+# Log gates far beyond the range of the chunk-local factored form (every |g| above
+# 1.875 in some chunk): -3 and -8 per token on every channel, channels alternating
+# between -8 and -0.01, elements drawn from {-8, -0.01}, and rows whose first half
+# is at -3 while the second half has the GLA workload's gates (strong and ordinary
+# chunks in one walk).  Both dtypes, both d_k kernels families (128: the
+# whole-head kernels; 64: the sliced ones), documents inside chunks, forced splits.
+STRONG = [
+    # (gate_kind, mult, dtype, d, T, lengths, split)
+    ("unit", 3.0, torch.bfloat16, 128, 256, [100, 28, 128], 0),
+    ("unit", 8.0, torch.bfloat16, 128, 256, [100, 28, 128], 0),
+    ("mix_channels", 8.0, torch.bfloat16, 128, 256, [100, 28, 128], 0),
+    ("mix_random", 8.0, torch.bfloat16, 128, 256, [7, 121, 128], 0),
+    ("half_unit", 3.0, torch.bfloat16, 128, 512, [300, 212], 2),
+    ("unit", 3.0, torch.float32, 128, 256, [100, 28, 128], 0),
+    ("unit", 8.0, torch.float32, 128, 256, [100, 28, 128], 0),
+    ("mix_channels", 8.0, torch.float32, 128, 256, [100, 28, 128], 0),
+    ("mix_random", 8.0, torch.float32, 128, 200, None, 2),
+    ("unit", 8.0, torch.bfloat16, 64, 256, [100, 28, 128], 0),
+    ("mix_random", 8.0, torch.bfloat16, 64, 190, [5, 7, 1, 100, 77], 0),
+    ("mix_channels", 8.0, torch.float32, 64, 256, [100, 28, 128], 3),
+]
+
+
+@pytest.mark.parametrize("kind,mult,dtype,d,T,lens,split", STRONG,
+                         ids=["%s-x%g-%s-d%d-T%d-%s-P%d" % (c[0], c[1], str(c[2])[6:], c[3], c[4],
+                              "seg" if c[5] else "noseg", c[6]) for c in STRONG])
+def test_strong_gate_parity(kind, mult, dtype, d, T, lens, split):
+    case = small_case(seed=T + d + int(mult), B=2, T=T, H=2, d=d, gate="vector", dtype=dtype,
+                      gate_kind=kind, gate_mult=mult, lengths=lens)
+    check(case, got=run_gpu(case, split=split))
