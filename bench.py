@@ -13,10 +13,14 @@ default workload is the Mamba-2/SSD shape: scalar decay, fp32, B=4, T=8192,
 8 heads in 2 q/k groups, d_k = d_v = 128, chunk 64.  Prints one JSON line.
 
 The roofline object is for gla_bwd, the dominant call of the step: its
-algorithmic work (FLOPs, or bytes for the bf16 workloads) divided by its mean
-duration, timed with HIP events on the stream the library launches on.  The
-cpu_baseline object times the fp64 CPU oracle on a bounded sample of the same
-workload (one batch row, repeated for about 10 s).
+algorithmic work divided by its mean duration, timed with HIP events on the
+stream the library launches on, against the roofline that binds the path (HBM,
+or the matrix cores the products run on: bf16 for bf16 inputs, three bf16
+products per fp32 product on the split-bf16 fp32 path).  A default run also
+times c3, c4, c5a and c5b in the same process ("also").  The cpu_baseline
+object times the fp64 CPU oracle on a bounded sample of the same workload (one
+batch row, repeated for about 10 s on all host threads; and one thread on 1024
+tokens of that row).
 """
 from __future__ import annotations
 
@@ -98,53 +102,69 @@ def algorithmic(case):
     return dict(fwd_bytes=fwd_bytes, bwd_bytes=bwd_bytes, fwd_flops=fwd_flops, bwd_flops=bwd_flops)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", type=int, default=3,
-                    help="extra untimed-region steps after a 512 MB cache flush (median reported)")
-    ap.add_argument("--fused", action="store_true",
-                    help="q, k, v as views of one [B, T, 2*H_qk*d_k + H*d_v] projection tensor, "
-                         "dq, dk, dv written into one fused gradient of that shape")
-    ap.add_argument("--split", type=int, default=0,
-                    help="sequence pieces per (b, h); 0 = the library's own choice")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+def split_bf16_path(case):
+    """fp32 inputs whose products run as three bf16 products of split operands on
+    the bf16 matrix cores (scalar gate, d_k = d_v = 128)."""
+    import torch
+    return (case.dtype == torch.float32 and case.gate == "scalar" and case.d_k == 128
+            and case.d_v == 128)
 
+
+def bound_time(case, nbytes, flops):
+    """(kind, seconds) of the roofline that binds this work on this path: HBM at
+    8 TB/s against the matrix cores the products actually run on (bf16 inputs:
+    bf16 cores; split-bf16 fp32: three bf16 products per fp32 product; other
+    fp32: the fp32 cores)."""
+    import torch
+    t_hbm = nbytes / (PEAK["hbm"] * 1e9)
+    if case.dtype == torch.bfloat16:
+        t_mma = flops / (PEAK["mfma_bf16"] * 1e12)
+    elif split_bf16_path(case):
+        t_mma = 3 * flops / (PEAK["mfma_bf16"] * 1e12)
+    else:
+        t_mma = flops / (PEAK["mfma_f32"] * 1e12)
+    return ("hbm", t_hbm) if t_hbm >= t_mma else ("mfma", t_mma)
+
+
+def copy_bandwidth(dev, mib=1024, reps=5):
+    """Device-to-device copy rate (GB/s, bytes read + written) of a torch copy."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        b.copy_(a)
+    ev[1].record()
+    torch.cuda.synchronize()
+    sec = ev[0].elapsed_time(ev[1]) / 1000.0 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / sec / 1e9
+
+
+def time_gla(name, steps, warmup, cold=0, fused=False, split=0):
+    """One gla_fwd + one gla_bwd per step on workload `name`, inputs resident in
+    device memory: event-timed fwd and bwd (mean and median), wall time per
+    step, and (cold > 0) the median of `cold` steps after a 512 MB cache flush."""
     import torch
     from ssm_recurrence_amd import binding as gb
-    from ssm_recurrence_amd.inputs import WORKLOADS, workload
+    from ssm_recurrence_amd.inputs import workload
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if args.workload == "conv":
-        conv_main(args)
-        return
-    if args.workload == "norm_gate":
-        norm_gate_main(args)
-        return
-    if args.workload == "delta":
-        delta_main(args)
-        return
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    case_cpu = workload(args.workload)
+    case_cpu = workload(name)
     case = case_cpu.to(dev)
-    prob = gb.problem_of(case.q, case.v, case.g, case.gate, case.chunk, args.split)
+    prob = gb.problem_of(case.q, case.v, case.g, case.gate, case.chunk, split)
     B, T, H, dk, dv = case.B, case.T, case.H, case.d_k, case.d_v
     o = torch.empty((B, T, H, dv), dtype=case.dtype, device=dev)
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     dq, dk_, dv_, dg = (torch.empty_like(case.q), torch.empty_like(case.k),
                         torch.empty_like(case.v), torch.empty_like(case.g))
-    if args.fused:
+    W = None
+    if fused:
         # the projection output X = q | k | v and one gradient buffer of its shape
         W = 2 * case.H_qk * dk + H * dv
         X = torch.empty((B, T, W), dtype=case.dtype, device=dev)
@@ -175,42 +195,38 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    ms_per_step = (t1 - t0) * 1000.0 / args.steps
-    fwd_us = 1000.0 * sum(fwd_ms) / len(fwd_ms)
-    bwd_us = 1000.0 * sum(bwd_ms) / len(bwd_ms)
     med = lambda xs: 1000.0 * sorted(xs)[len(xs) // 2]
+    r = dict(case=case_cpu, ms_per_step=(t1 - t0) * 1000.0 / steps,
+             fwd_us=1000.0 * sum(fwd_ms) / len(fwd_ms), bwd_us=1000.0 * sum(bwd_ms) / len(bwd_ms),
+             fwd_med=med(fwd_ms), bwd_med=med(bwd_ms), cold_f=[], cold_b=[], W=W, copies_us=None)
 
     # cold caches: 512 MB written between steps evicts L2 and the MALL (untimed)
-    cold_f, cold_b = [], []
-    if args.cold > 0:
+    if cold > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        for i in range(args.cold):
+        for i in range(cold):
             flush.fill_(i & 0xFF)
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             step(ev)
             torch.cuda.synchronize()
-            cold_f.append(ev[0].elapsed_time(ev[1]))
-            cold_b.append(ev[1].elapsed_time(ev[2]))
+            r["cold_f"].append(ev[0].elapsed_time(ev[1]))
+            r["cold_b"].append(ev[1].elapsed_time(ev[2]))
         del flush
-    tokens = B * T
-    value = tokens / (ms_per_step / 1000.0)
 
     # what the packed layout would add around each step: q, k, v split out of the
     # projection, and dq | dk | dv concatenated into its gradient (timed apart)
-    copies_us = None
-    if args.fused:
+    if fused:
         def copies():
             packed["q"].copy_(case.q)
             packed["k"].copy_(case.k)
@@ -219,78 +235,181 @@ def main():
         copies()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             copies()
         ev[1].record(stream)
         torch.cuda.synchronize()
-        copies_us = 1000.0 * ev[0].elapsed_time(ev[1]) / args.steps
+        r["copies_us"] = 1000.0 * ev[0].elapsed_time(ev[1]) / steps
+    del case, o, hT, dq, dk_, dv_, dg, dh0, wsf, wsb
+    torch.cuda.empty_cache()
+    return r
 
+
+def gla_roofline(case, fwd_us, bwd_us, copy_gbs=None):
+    """Roofline of gla_bwd (the dominant call) and of the whole step, against the
+    bound that binds the path (bound_time); fp32 paths also report the fraction
+    of the fp32 matrix-core peak their FLOPs would reach."""
+    import torch
     alg = algorithmic(case)
-    bf16 = case.dtype == torch.bfloat16
-    if bf16:
-        bound, peak, unit = "hbm", PEAK["hbm"], "GB/s"
-        achieved = alg["bwd_bytes"] / (bwd_us * 1e-6) / 1e9
-        step_ach = (alg["fwd_bytes"] + alg["bwd_bytes"]) / ((fwd_us + bwd_us) * 1e-6) / 1e9
+    kind, tb = bound_time(case, alg["bwd_bytes"], alg["bwd_flops"])
+    _, ts = bound_time(case, alg["fwd_bytes"] + alg["bwd_bytes"], alg["fwd_flops"] + alg["bwd_flops"])
+    sec = bwd_us * 1e-6
+    if kind == "hbm":
+        roof = {"bound": "hbm", "achieved": round(alg["bwd_bytes"] / sec / 1e9, 3),
+                "peak": PEAK["hbm"], "unit": "GB/s"}
     else:
-        bound, peak, unit = "mfma", PEAK["mfma_f32"], "TFLOP/s"
-        achieved = alg["bwd_flops"] / (bwd_us * 1e-6) / 1e12
-        step_ach = (alg["fwd_flops"] + alg["bwd_flops"]) / ((fwd_us + bwd_us) * 1e-6) / 1e12
-    traffic = measured_traffic(args.workload + ("f" if args.fused else ""))
-    roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4),
-            "traffic": None if traffic is None else round(traffic / 1e6, 1),
-            "traffic_unit": "MB per gla_bwd call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_bytes": round(alg["bwd_bytes"] / 1e6, 1),
-            "kernel": "gla_bwd (all its kernels, one call)",
-            "step_frac": round(step_ach / peak, 4)}
-    if not bf16:
-        # the fp32 products of the gradient kernel run as split-bf16 on the bf16 matrix
-        # cores; the byte roofline of the same call, for comparison
-        roof["hbm_frac"] = round(alg["bwd_bytes"] / (bwd_us * 1e-6) / 1e9 / PEAK["hbm"], 4)
+        mult = 3 if split_bf16_path(case) else 1
+        peak = PEAK["mfma_f32"] if (case.dtype == torch.float32 and mult == 1) else PEAK["mfma_bf16"]
+        roof = {"bound": "mfma", "achieved": round(mult * alg["bwd_flops"] / sec / 1e12, 3),
+                "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = round(tb / sec, 4)
+    roof["step_frac"] = round(ts / ((fwd_us + bwd_us) * 1e-6), 4)
+    roof["algorithmic_bytes"] = round(alg["bwd_bytes"] / 1e6, 1)
+    roof["algorithmic_gflop"] = round(alg["bwd_flops"] / 1e9, 2)
+    if copy_gbs:
+        roof["copy_gbs"] = round(copy_gbs, 1)
+        roof["copy_frac"] = round(alg["bwd_bytes"] / sec / 1e9 / copy_gbs, 4)
+    if case.dtype == torch.float32:
+        # the fp32 FLOPs against the fp32 matrix cores (the split-bf16 path does not use them)
+        roof["fp32_mfma_frac"] = round(alg["bwd_flops"] / sec / 1e12 / PEAK["mfma_f32"], 4)
+        roof["step_fp32_mfma_frac"] = round((alg["fwd_flops"] + alg["bwd_flops"])
+                                            / ((fwd_us + bwd_us) * 1e-6) / 1e12 / PEAK["mfma_f32"], 4)
+    if split_bf16_path(case):
+        roof["products"] = "fp32 as three bf16 products of split operands (bf16 matrix cores)"
+    return roof
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        threads = oracle.default_threads()
-        s = case_cpu
-        sl = slice(0, 1)  # one batch row, every head, the full sequence
-        seg = None if s.segment_ids is None else s.segment_ids[sl]
-        h0 = None if s.h0 is None else s.h0[sl]
-        dhT = None if s.dhT is None else s.dhT[sl]
+
+def cpu_baseline(case, single_seconds=5.0):
+    """The fp64 oracle on the host cores over a bounded sample: batch row 0, every
+    head, the whole sequence, fwd + bwd repeated for about 10 s on all threads in
+    the affinity mask; plus one thread on the first 1024 tokens of that row."""
+    import oracle
+    threads = oracle.default_threads()
+    s = case
+    T, H = s.T, s.H
+
+    def run(sl, tsl, nthreads, budget):
+        cut = lambda x: None if x is None else x[sl][:, tsl].contiguous()
+        st = lambda x: None if x is None else x[sl].contiguous()
+        args = (cut(s.q), cut(s.k), cut(s.v), cut(s.g))
+        seg = None if s.segment_ids is None else s.segment_ids[sl][:, tsl].contiguous()
         c0 = time.perf_counter()
         reps = 0
-        while reps == 0 or time.perf_counter() - c0 < 10.0:
-            oracle.fwd(s.q[sl], s.k[sl], s.v[sl], s.g[sl], h0, seg, gate=s.gate, threads=threads)
-            oracle.bwd(s.q[sl], s.k[sl], s.v[sl], s.g[sl], s.dO[sl], h0, seg, dhT, gate=s.gate,
-                       threads=threads)
+        while reps == 0 or time.perf_counter() - c0 < budget:
+            oracle.fwd(*args, st(s.h0), seg, gate=s.gate, threads=nthreads)
+            oracle.bwd(*args, cut(s.dO), st(s.h0), seg, st(s.dhT), gate=s.gate, threads=nthreads)
             reps += 1
-        c1 = time.perf_counter()
-        cpu = {"value": round(reps * T / (c1 - c0), 1), "unit": "tokens/s", "cores": threads,
-               "kind": "oracle",
-               "sample": "batch row 0 of the workload (%d tokens x %d heads), fwd+bwd, %d times in %.1f s"
-                         % (T, H, reps, c1 - c0)}
+        return reps, time.perf_counter() - c0
+
+    reps, sec = run(slice(0, 1), slice(0, T), threads, 10.0)
+    n1 = min(T, 1024)
+    reps1, sec1 = run(slice(0, 1), slice(0, n1), 1, single_seconds)
+    return {"value": round(reps * T / sec, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "batch row 0 of the workload (%d tokens x %d heads), fwd+bwd, %d times in %.1f s"
+                      % (T, H, reps, sec),
+            "single_thread": {"value": round(reps1 * n1 / sec1, 1), "unit": "tokens/s", "cores": 1,
+                              "sample": "tokens 0..%d of batch row 0, every head, fwd+bwd, %d times "
+                                        "in %.1f s" % (n1 - 1, reps1, sec1)}}
+
+
+# workloads timed beside the headline one in a default run (no CPU leg)
+ALSO = ["c3", "c4", "c5a", "c5b"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=3,
+                    help="extra untimed-region steps after a 512 MB cache flush (median reported)")
+    ap.add_argument("--fused", action="store_true",
+                    help="q, k, v as views of one [B, T, 2*H_qk*d_k + H*d_v] projection tensor, "
+                         "dq, dk, dv written into one fused gradient of that shape")
+    ap.add_argument("--split", type=int, default=0,
+                    help="sequence pieces per (b, h); 0 = the library's own choice")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads timed beside the main one (default: %s for "
+                         "the default workload, none otherwise; 'none' for none)" % ",".join(ALSO))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ssm_recurrence_amd import binding as gb  # noqa: F401  (fails loudly without the library)
+    from ssm_recurrence_amd.inputs import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload == "conv":
+        conv_main(args)
+        return
+    if args.workload == "norm_gate":
+        norm_gate_main(args)
+        return
+    if args.workload == "delta":
+        delta_main(args)
+        return
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copy_gbs = copy_bandwidth(dev)
+    r = time_gla(args.workload, args.steps, args.warmup, args.cold, args.fused, args.split)
+    case = r["case"]
+    B, T, H, dk, dv = case.B, case.T, case.H, case.d_k, case.d_v
+    fwd_us, bwd_us = r["fwd_us"], r["bwd_us"]
+    value = B * T / (r["ms_per_step"] / 1000.0)
+    roof = gla_roofline(case, fwd_us, bwd_us, copy_gbs)
+    traffic = measured_traffic(args.workload + ("f" if args.fused else ""))
+    roof["traffic"] = None if traffic is None else round(traffic / 1e6, 1)
+    roof["traffic_unit"] = "MB per gla_bwd call (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["kernel"] = "gla_bwd (all its kernels, one call)"
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case)
+    bf16 = case.dtype == torch.bfloat16
+    med = lambda xs: 1000.0 * sorted(xs)[len(xs) // 2]
 
     out = {
         "metric": "fwd+bwd µs and tokens/s for chunked GLA/SSD at d=128, % of MFMA/HBM roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
         "us_fwd": round(fwd_us, 1), "us_bwd": round(bwd_us, 1),
         "us_fwd_bwd": round(fwd_us + bwd_us, 1),
-        "us_fwd_median": round(med(fwd_ms), 1), "us_bwd_median": round(med(bwd_ms), 1),
-        "us_fwd_cold": round(med(cold_f), 1) if cold_f else None,
-        "us_bwd_cold": round(med(cold_b), 1) if cold_b else None,
+        "us_fwd_median": round(r["fwd_med"], 1), "us_bwd_median": round(r["bwd_med"], 1),
+        "us_fwd_cold": round(med(r["cold_f"]), 1) if r["cold_f"] else None,
+        "us_bwd_cold": round(med(r["cold_b"]), 1) if r["cold_b"] else None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic (seeded)",
         "config": {"workload": "%s: %s" % (args.workload, WORKLOADS[args.workload]),
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
                    "chunk": case.chunk, "split": args.split, "parallelism": "single GPU",
                    "layout": ("q, k, v read from one [B, T, %d] projection tensor; one fused "
-                              "gradient" % W) if args.fused else "packed q, k, v"},
+                              "gradient" % r["W"]) if args.fused else "packed q, k, v"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     if args.fused:
-        out["us_layout_copies_avoided"] = round(copies_us, 1)
+        out["us_layout_copies_avoided"] = round(r["copies_us"], 1)
+
+    also = args.also
+    if also is None:
+        also = ",".join(ALSO) if (args.workload == "c2" and not args.fused and args.split == 0) else "none"
+    others = {}
+    for name in [x for x in also.split(",") if x and x != "none"]:
+        o = time_gla(name, args.steps, args.warmup)
+        c = o["case"]
+        rf = gla_roofline(c, o["fwd_us"], o["bwd_us"], copy_gbs)
+        others[name] = {"workload": WORKLOADS[name],
+                        "us_fwd": round(o["fwd_us"], 1), "us_bwd": round(o["bwd_us"], 1),
+                        "us_fwd_bwd": round(o["fwd_us"] + o["bwd_us"], 1),
+                        "tokens_per_s": round(c.B * c.T / (o["ms_per_step"] / 1000.0), 1),
+                        "bound": rf["bound"], "bwd_frac": rf["frac"], "step_frac": rf["step_frac"],
+                        "copy_frac": rf.get("copy_frac")}
+    if others:
+        out["also"] = others
     print(json.dumps(out))
 
 
