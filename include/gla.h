@@ -100,7 +100,8 @@ typedef enum {
     GLA_E_ALIGN = -5,       /* a pointer is not 16-byte aligned */
     GLA_E_WORKSPACE = -6,   /* workspace missing or smaller than required */
     GLA_E_DEVICE = -7,      /* no HIP device, or the current device is not gfx950 */
-    GLA_E_LAUNCH = -8       /* a kernel launch failed */
+    GLA_E_LAUNCH = -8,      /* a kernel launch failed */
+    GLA_E_SCRATCH = -9      /* gla_fwd_noalloc: the problem needs more than its fixed scratch */
 } gla_status;
 
 typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
@@ -158,6 +159,27 @@ int gla_workspace_size(const gla_problem* p, int for_backward, size_t* bytes);
 int gla_fwd(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
             const float* h0, const int32_t* segment_ids, void* o, float* hT, void* ws,
             size_t ws_bytes, void* stream);
+
+/* Forward for callers that cannot allocate: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.  The same
+ * computation and kernels as gla_fwd (results identical bit for bit), without a
+ * workspace argument: the workspace gla_fwd would take (only sequence-split
+ * problems need one: the per-piece summaries and entry states) is a fixed
+ * device array inside the library, gla_fwd_noalloc_max_scratch() bytes (64 MiB),
+ * one per device for the life of the process.  A problem whose
+ * gla_workspace_size(p, 0) exceeds it returns GLA_E_SCRATCH before anything is
+ * enqueued.  The call allocates and frees nothing (the array's address is looked
+ * up once per device, on the first call made with that device current).  Every
+ * call on one device shares that device's array, which keeps the last call's
+ * contents: calls that may overlap on one device (different streams, no
+ * ordering between them) race, so order them on one stream.  Nothing in the
+ * array needs to start at zero.  Other arguments, ownership and errors as for
+ * gla_fwd. */
+int gla_fwd_noalloc(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
+                    const float* h0, const int32_t* segment_ids, void* o, float* hT, void* stream);
+
+/* Bytes of the fixed scratch gla_fwd_noalloc works in. */
+size_t gla_fwd_noalloc_max_scratch(void);
 
 /* Backward: dq, dk, dv, dg (and dh0 if non-NULL) from the forward's inputs and
  * the upstream gradients dO and dhT.  Recomputes whatever it needs from the

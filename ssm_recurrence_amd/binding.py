@@ -20,7 +20,7 @@ GLA_F32, GLA_BF16 = 0, 1
 GLA_GATE_SCALAR, GLA_GATE_VECTOR = 0, 1
 STATUS = {0: "GLA_OK", -1: "GLA_E_NULL", -2: "GLA_E_SHAPE", -3: "GLA_E_DTYPE",
           -4: "GLA_E_UNSUPPORTED", -5: "GLA_E_ALIGN", -6: "GLA_E_WORKSPACE",
-          -7: "GLA_E_DEVICE", -8: "GLA_E_LAUNCH"}
+          -7: "GLA_E_DEVICE", -8: "GLA_E_LAUNCH", -9: "GLA_E_SCRATCH"}
 
 
 class Problem(ctypes.Structure):
@@ -73,6 +73,10 @@ def load():
         lib.gla_workspace_size.restype = ctypes.c_int
         lib.gla_fwd.argtypes = [P] + [vp] * 9 + [sz, vp]
         lib.gla_fwd.restype = ctypes.c_int
+        lib.gla_fwd_noalloc.argtypes = [P] + [vp] * 9
+        lib.gla_fwd_noalloc.restype = ctypes.c_int
+        lib.gla_fwd_noalloc_max_scratch.argtypes = []
+        lib.gla_fwd_noalloc_max_scratch.restype = sz
         lib.gla_bwd.argtypes = [P] + [vp] * 14 + [sz, vp]
         lib.gla_bwd.restype = ctypes.c_int
         CP = ctypes.POINTER(ConvProblem)
@@ -202,6 +206,26 @@ def fwd(q, k, v, g, h0=None, segment_ids=None, *, gate="scalar", chunk=64, want_
                         _p(o), _p(hT), _p(ws), nws, _stream())
     if rc:
         raise GlaError(rc, "gla_fwd")
+    return o, hT
+
+
+def fwd_noalloc(q, k, v, g, h0=None, segment_ids=None, *, gate="scalar", chunk=64, want_hT=True,
+                out=None, split=0):
+    """As fwd(), through gla_fwd_noalloc: no workspace (the library's fixed scratch);
+    o and hT are allocated here unless `out` is given and want_hT is False."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, strided=True)
+    _check(g, "g", q.dtype)
+    _check(h0, "h0", torch.float32)
+    _check(segment_ids, "segment_ids", torch.int32)
+    prob = problem_of(q, v, g, gate, chunk, split, k)
+    B, T, H, d_v, d_k = prob.B, prob.T, prob.H, prob.d_v, prob.d_k
+    o = out if out is not None else torch.empty((B, T, H, d_v), dtype=q.dtype, device=q.device)
+    hT = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device) if want_hT else None
+    rc = load().gla_fwd_noalloc(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(h0),
+                                _p(segment_ids), _p(o), _p(hT), _stream())
+    if rc:
+        raise GlaError(rc, "gla_fwd_noalloc")
     return o, hT
 
 

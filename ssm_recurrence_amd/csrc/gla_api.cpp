@@ -380,6 +380,51 @@ gla::DeltaArgs delta_args(const gla_delta_problem* p, void* ws) {
     return a;
 }
 
+// The forward after its argument checks: dispatch with a workspace of at least
+// ws_layout(p, 0).total bytes.
+int fwd_checked(const gla_problem* p, const WsLayout& L, const void* q, const void* k, const void* v,
+                const void* g, const float* h0, const int32_t* segment_ids, void* o, float* hT, void* ws,
+                hipStream_t st) {
+    if (p->T == 0) return copy_state(hT, h0, p->B * p->H * p->d_k * p->d_v, st);
+    gla::PassArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.h0 = h0; a.seg = segment_ids; a.o = o; a.hT = hT;
+    a.B = p->B; a.T = p->T; a.H = p->H; a.Hqk = p->H_qk;
+    a.ld_qk = ld_or_packed(p->ld_qk, p->H_qk * p->d_k);
+    a.ld_v = ld_or_packed(p->ld_v, p->H * p->d_v);
+    a.P = L.sp.P; a.PL = L.sp.PL;
+    if (a.P > 1) {
+        char* w = (char*)ws;
+        a.L_out[0] = (float*)(w + L.pL0);
+        a.S_in = (const float*)(w + L.pS);
+        a.D_out = (float*)(w + L.pD);
+    }
+    return dispatch<FwdF>(p, a, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+}
+
+// ---- the forward that allocates nothing (gla_fwd_noalloc)
+// Its workspace is this fixed device array: one copy per device, the whole life
+// of the process.  Host code never names the array itself (on the host that name
+// is only a stand-in for the symbol): it takes each device's address once, with
+// that device current, and passes that address on.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int scratch_on_current_device(void** out) {
+    static std::mutex mu;
+    static void* addr[64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GLA_E_DEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GLA_E_DEVICE;
+        addr[dev] = ptr;
+    }
+    *out = addr[dev];
+    return GLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,24 +450,32 @@ int gla_fwd(const gla_problem* p, const void* q, const void* k, const void* v, c
     if (ws_bytes < L.total || (L.total > 0 && !ws)) return GLA_E_WORKSPACE;
     rc = check_device();
     if (rc) return rc;
-    hipStream_t st = (hipStream_t)stream;
-    if (p->T == 0) return copy_state(hT, h0, p->B * p->H * p->d_k * p->d_v, st);
-
-    gla::PassArgs a;
-    memset(&a, 0, sizeof a);
-    a.q = q; a.k = k; a.v = v; a.g = g; a.h0 = h0; a.seg = segment_ids; a.o = o; a.hT = hT;
-    a.B = p->B; a.T = p->T; a.H = p->H; a.Hqk = p->H_qk;
-    a.ld_qk = ld_or_packed(p->ld_qk, p->H_qk * p->d_k);
-    a.ld_v = ld_or_packed(p->ld_v, p->H * p->d_v);
-    a.P = L.sp.P; a.PL = L.sp.PL;
-    if (a.P > 1) {
-        char* w = (char*)ws;
-        a.L_out[0] = (float*)(w + L.pL0);
-        a.S_in = (const float*)(w + L.pS);
-        a.D_out = (float*)(w + L.pD);
-    }
-    return dispatch<FwdF>(p, a, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+    return fwd_checked(p, L, q, k, v, g, h0, segment_ids, o, hT, ws, (hipStream_t)stream);
 }
+
+int gla_fwd_noalloc(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
+                    const float* h0, const int32_t* segment_ids, void* o, float* hT, void* stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!q || !k || !v || !g || !o) return GLA_E_NULL;
+    const void* ptrs[] = {q, k, v, g, h0, segment_ids, o, hT};
+    for (const void* x : ptrs)
+        if (x && !aligned(x)) return GLA_E_ALIGN;
+    const WsLayout L = ws_layout(p, 0);
+    if (L.total > kScratchBytes) return GLA_E_SCRATCH;
+    rc = check_device();
+    if (rc) return rc;
+    // (every buffer the kernels keep there is written before it is read: nothing
+    // in the scratch needs to start at zero)
+    void* ws = nullptr;
+    if (L.total > 0) {
+        rc = scratch_on_current_device(&ws);
+        if (rc) return rc;
+    }
+    return fwd_checked(p, L, q, k, v, g, h0, segment_ids, o, hT, ws, (hipStream_t)stream);
+}
+
+size_t gla_fwd_noalloc_max_scratch(void) { return kScratchBytes; }
 
 int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
             const float* h0, const int32_t* segment_ids, const void* dO, const float* dhT,
@@ -618,7 +671,7 @@ int gla_norm_gate_workspace_size(const gla_norm_gate_problem* p, size_t* bytes) 
     if (rc) return rc;
     if (!bytes) return GLA_E_NULL;
     int64_t np = 0;
-    norm_dispatch(p, [&](auto t, auto d) {
+    (void)norm_dispatch(p, [&](auto t, auto d) {
         np = gla::norm_gate_partials<decltype(t), decltype(d)::value>(norm_rows(p));
         return hipSuccess;
     });
@@ -682,6 +735,7 @@ const char* gla_status_str(int s) {
         case GLA_E_WORKSPACE: return "workspace missing or too small";
         case GLA_E_DEVICE: return "no HIP device, or the current device is not gfx950";
         case GLA_E_LAUNCH: return "kernel launch failed";
+        case GLA_E_SCRATCH: return "the problem needs more workspace than the fixed scratch of gla_fwd_noalloc holds";
         default: return "unknown status";
     }
 }

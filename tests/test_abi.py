@@ -21,7 +21,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, -9, -1):
+    for s in range(0, -10, -1):
         assert lib.gla_status_str(s)
     assert lib.gla_version() >= 100
 
@@ -189,6 +189,36 @@ def test_binding_row_stride_and_fused_views():
 def test_valid_call_without_gpu_reports_device_error(lib):
     """No silent fallback: with no usable device a valid call returns GLA_E_DEVICE."""
     assert call_fwd(lib, prob(H_qk=4, d_v=128)) == -7
+
+
+def call_fwd_noalloc(lib, prob, ptrs=None):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, h0=None, seg=None, o=FAKE, hT=None)
+    p.update(ptrs or {})
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_fwd_noalloc(None if prob is None else ctypes.byref(prob), c(p["q"]), c(p["k"]),
+                               c(p["v"]), c(p["g"]), c(p["h0"]), c(p["seg"]), c(p["o"]), c(p["hT"]), None)
+
+
+def test_noalloc_forward_host_checks(lib):
+    """gla_fwd_noalloc: the forward's argument checks, and a problem whose forward
+    workspace exceeds the fixed scratch rejected with GLA_E_SCRATCH before any
+    device is touched (every pointer here is fake: nothing may run)."""
+    assert lib.gla_fwd_noalloc_max_scratch() == 64 << 20
+    assert call_fwd_noalloc(lib, None) == -1
+    assert call_fwd_noalloc(lib, prob(), {"o": None}) == -1
+    assert call_fwd_noalloc(lib, prob(), {"q": FAKE + 4}) == -5
+    assert call_fwd_noalloc(lib, prob(d_k=96)) == -4
+    # 64 heads x 16 pieces of 128 x 128 fp32 summaries and entry states: 128 MiB
+    big = gb.make_problem(B=1, T=65536, H=64, H_qk=64, d_k=128, d_v=128, gate="vector",
+                          dtype=torch.bfloat16, split=16)
+    assert gb.workspace_size(big, False) > lib.gla_fwd_noalloc_max_scratch()
+    assert call_fwd_noalloc(lib, big) == -9
+    assert b"scratch" in lib.gla_status_str(-9)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_noalloc_without_gpu_reports_device_error(lib):
+    assert call_fwd_noalloc(lib, prob(H_qk=4, d_v=128)) == -7
 
 
 # ---- the short depthwise causal convolution (gla_conv_*): host-side validation
