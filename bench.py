@@ -640,8 +640,9 @@ def delta_main(args):
     c = case_cpu.to(dev)
     B, T, H, dk = c.q.shape
     dv = c.v.shape[3]
-    prob = gb.delta_problem(c.q, c.v)
-    prob_b = gb.delta_problem(c.q, c.v, gb.GLA_DELTA_WS_FROM_FWD)  # the backward reuses the forward's ws
+    prob = gb.delta_problem(c.q, c.v, 0, 1)
+    # the backward may reuse the forward's factors (same inputs, same generation)
+    prob_b = gb.delta_problem(c.q, c.v, gb.GLA_DELTA_WS_FROM_FWD, 1)
     o = torch.empty_like(c.v)
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     dq, dk_, dv_, dg, db = (torch.empty_like(c.q), torch.empty_like(c.k), torch.empty_like(c.v),
@@ -649,6 +650,8 @@ def delta_main(args):
     dh0 = torch.empty_like(c.h0)
     n = gb.delta_workspace_size(prob)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    n2 = gb.delta_workspace_size(prob, True)
+    scratch = torch.empty(max(n2, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = gb.ctypes.c_void_p(stream.cuda_stream)
     lib = gb.load()
@@ -664,7 +667,7 @@ def delta_main(args):
             ev[1].record(stream)
         rc |= lib.gla_delta_bwd(PB, p(c.q), p(c.k), p(c.v), p(c.g), p(c.beta), p(c.h0), p(c.segment_ids),
                                 p(c.dO), p(c.dhT), p(dq), p(dk_), p(dv_), p(dg), p(db), p(dh0), p(ws),
-                                ws.numel(), sp)
+                                ws.numel(), p(scratch), scratch.numel(), sp)
         if ev is not None:
             ev[2].record(stream)
         if rc:

@@ -61,8 +61,9 @@
  *
  * Pointers: every tensor pointer is a device pointer on the current HIP
  * device, 16-byte aligned.  Nullable pointers: h0 (zeros), segment_ids (one
- * document per row), hT (not written), dhT (zeros), dh0 (not written).  All
- * others are required.  ws is a device workspace of ws_bytes bytes, at least
+ * document per row), hT (not written), dhT (zeros), dh0 (not written), and the
+ * activation and gradient pointers when T == 0 (then hT = h0 and dh0 = dhT, or
+ * zeros).  All others are required.  ws is a device workspace of ws_bytes bytes, at least
  * gla_workspace_size(); it may be NULL when that size is 0.
  *
  * Ownership and ordering: the caller allocates and frees every buffer; the
@@ -257,26 +258,36 @@ int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const
  * float32; segment_ids [B, T] int32.  dtype as for gla_fwd (all products and
  * sums in float32).  Sizes: B >= 1, T >= 0, H >= 1, d_k and d_v in {64, 128}.
  * Nullable: h0, segment_ids, hT, dhT, dh0 (as for gla_fwd / gla_bwd), and the
- * activation pointers when T == 0.  ws: at least gla_delta_workspace_size()
- * bytes (per-chunk fp32 intermediates: the chunk's inverse T, U, W, masked
- * scores, states and state gradients).  Ownership, ordering and errors are as
- * for gla_fwd / gla_bwd. */
+ * activation pointers when T == 0.  Ownership, ordering and errors are as for
+ * gla_fwd / gla_bwd.
+ *
+ * Workspaces.  ws (both calls): gla_delta_workspace_size(p, 0) bytes, the
+ * per-chunk factors the chunked form builds from the inputs (the inverse T, U,
+ * W, the masked scores, gamma Q, the decayed keys and the chunk carries, fp32)
+ * behind a small header.  scratch (the backward only):
+ * gla_delta_workspace_size(p, 1) bytes, the backward's own per-chunk
+ * intermediates (the states and state gradients at the chunk boundaries and
+ * the gradient blocks); nothing of it outlives the call. */
 typedef struct {
     int64_t B, T, H, d_k, d_v;
     int32_t dtype;    /* gla_dtype */
     int32_t flags;    /* 0, or GLA_DELTA_WS_FROM_FWD; other bits: GLA_E_UNSUPPORTED */
+    int64_t generation; /* the caller's count of changes to the inputs' contents; see below */
 } gla_delta_problem;
 
-/* gla_delta_bwd only (gla_delta_fwd ignores it): ws holds what gla_delta_fwd
- * wrote there for the same problem and the same q, k, v, g, beta and
- * segment_ids, unchanged since (a backward call leaves it so).  The backward then
- * reuses the forward's per-chunk factors (the inverse T, U, W, the masked scores,
- * gamma Q, the decayed keys and the chunk carries) instead of recomputing them.
- * The caller vouches for this; the library cannot check it, and a stale ws gives
- * wrong gradients without an error. */
+/* gla_delta_bwd only (gla_delta_fwd ignores it): ws may hold the factors a
+ * gla_delta_fwd computed for these inputs; reuse them instead of recomputing.
+ * Every ws carries a stamp of what its factors were computed from: the problem's
+ * sizes and dtype, the q, k, v, g, beta and segment_ids pointers and
+ * p->generation (gla_delta_fwd writes it; a backward that recomputes the factors
+ * rewrites it).  The backward's prepare pass compares the stamp with its own
+ * call's on the device and recomputes unless they are equal, so a ws from another
+ * problem, other inputs or another layer is never used.  The caller's part: give
+ * gla_delta_fwd and gla_delta_bwd the same generation only while the inputs'
+ * contents are unchanged (change it whenever they are written in place). */
 #define GLA_DELTA_WS_FROM_FWD 1
 
-/* Bytes of device workspace gla_delta_fwd / gla_delta_bwd need. */
+/* Bytes of ws (for_backward == 0) or of the backward's scratch (for_backward != 0). */
 int gla_delta_workspace_size(const gla_delta_problem* p, int for_backward, size_t* bytes);
 
 /* Forward: o (and hT if non-NULL). */
@@ -286,11 +297,12 @@ int gla_delta_fwd(const gla_delta_problem* p, const void* q, const void* k, cons
 
 /* Backward: dq, dk, dv, dg, dbeta (and dh0 if non-NULL).  Recomputes the states
  * entering the chunks, and the per-chunk factors unless p->flags has
- * GLA_DELTA_WS_FROM_FWD. */
+ * GLA_DELTA_WS_FROM_FWD and ws's stamp matches (above). */
 int gla_delta_bwd(const gla_delta_problem* p, const void* q, const void* k, const void* v,
                   const void* g, const void* beta, const float* h0, const int32_t* segment_ids,
                   const void* dO, const float* dhT, void* dq, void* dk, void* dv, void* dg,
-                  void* dbeta, float* dh0, void* ws, size_t ws_bytes, void* stream);
+                  void* dbeta, float* dh0, void* ws, size_t ws_bytes, void* scratch,
+                  size_t scratch_bytes, void* stream);
 
 /* ---- Output norm and gate (the step after the recurrence)
  *

@@ -44,7 +44,7 @@ class NormGateProblem(ctypes.Structure):
 class DeltaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("generation", ctypes.c_int64)]
 
 
 class GlaError(RuntimeError):
@@ -98,7 +98,7 @@ def load():
         lib.gla_delta_workspace_size.restype = ctypes.c_int
         lib.gla_delta_fwd.argtypes = [DP] + [vp] * 10 + [sz, vp]
         lib.gla_delta_fwd.restype = ctypes.c_int
-        lib.gla_delta_bwd.argtypes = [DP] + [vp] * 16 + [sz, vp]
+        lib.gla_delta_bwd.argtypes = [DP] + [vp] * 16 + [sz, vp, sz, vp]
         lib.gla_delta_bwd.restype = ctypes.c_int
         lib.gla_status_str.argtypes = [ctypes.c_int]
         lib.gla_status_str.restype = ctypes.c_char_p
@@ -493,14 +493,16 @@ class NormGateFunction(torch.autograd.Function):
 GLA_DELTA_WS_FROM_FWD = 1
 
 
-def delta_problem(q, v, flags=0):
+def delta_problem(q, v, flags=0, generation=0):
     B, T, H, d_k = q.shape
-    return DeltaProblem(B, T, H, d_k, v.shape[3], GLA_BF16 if q.dtype == torch.bfloat16 else GLA_F32, flags)
+    return DeltaProblem(B, T, H, d_k, v.shape[3], GLA_BF16 if q.dtype == torch.bfloat16 else GLA_F32, flags,
+                        generation)
 
 
-def delta_workspace_size(prob: DeltaProblem) -> int:
+def delta_workspace_size(prob: DeltaProblem, backward: bool = False) -> int:
+    """Bytes of ws (both calls; backward=False) or of the backward's scratch."""
     n = ctypes.c_size_t(0)
-    rc = load().gla_delta_workspace_size(ctypes.byref(prob), 1, ctypes.byref(n))
+    rc = load().gla_delta_workspace_size(ctypes.byref(prob), int(bool(backward)), ctypes.byref(n))
     if rc:
         raise GlaError(rc, "gla_delta_workspace_size")
     return n.value
@@ -514,18 +516,24 @@ def _delta_checks(q, k, v, g, beta):
         raise ValueError("delta rule: q, k [B,T,H,d_k], v [B,T,H,d_v], g, beta [B,T,H]")
 
 
-def delta_fwd(q, k, v, g, beta, h0=None, segment_ids=None, *, want_hT=True, ws=None):
-    """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted)."""
+def _buffer(n, device, buf=None):
+    if buf is None or buf.numel() < n:
+        buf = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return buf
+
+
+def delta_fwd(q, k, v, g, beta, h0=None, segment_ids=None, *, want_hT=True, ws=None, generation=0):
+    """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted).
+    ws (allocated here when None or too small) receives the per-chunk factors,
+    stamped with these inputs and `generation`."""
     _delta_checks(q, k, v, g, beta)
     _check(h0, "h0", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = delta_problem(q, v)
+    prob = delta_problem(q, v, 0, generation)
     B, T, H, d_k = q.shape
     o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
     hT = torch.empty((B, H, d_k, v.shape[3]), dtype=torch.float32, device=q.device) if want_hT else None
-    n = delta_workspace_size(prob)
-    if ws is None or ws.numel() < n:
-        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    ws = _buffer(delta_workspace_size(prob), q.device, ws)
     rc = load().gla_delta_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0),
                               _p(segment_ids), _p(o), _p(hT), _p(ws), ws.numel(), _stream())
     if rc:
@@ -534,45 +542,51 @@ def delta_fwd(q, k, v, g, beta, h0=None, segment_ids=None, *, want_hT=True, ws=N
 
 
 def delta_bwd(q, k, v, g, beta, dO, h0=None, segment_ids=None, dhT=None, *, want_dh0=True, ws=None,
-              ws_from_fwd=False):
-    """dq, dk, dv, dg, dbeta (input dtype) and dh0 fp32 (or None).  ws_from_fwd: ws is
-    the workspace delta_fwd filled for these same inputs (GLA_DELTA_WS_FROM_FWD)."""
-    if ws_from_fwd and ws is None:
-        raise ValueError("ws_from_fwd needs the forward's workspace")
+              ws_from_fwd=False, generation=0, scratch=None):
+    """dq, dk, dv, dg, dbeta (input dtype) and dh0 fp32 (or None).  ws_from_fwd: ws may
+    hold the factors delta_fwd computed for these inputs and `generation`; the library
+    reuses them only when the workspace's stamp says so, and recomputes otherwise
+    (GLA_DELTA_WS_FROM_FWD).  scratch: the backward's own workspace (allocated here
+    when None or too small)."""
     _delta_checks(q, k, v, g, beta)
     _check(dO, "dO", q.dtype)
     _check(h0, "h0", torch.float32)
     _check(dhT, "dhT", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = delta_problem(q, v, GLA_DELTA_WS_FROM_FWD if ws_from_fwd else 0)
+    prob = delta_problem(q, v, GLA_DELTA_WS_FROM_FWD if ws_from_fwd else 0, generation)
     B, T, H, d_k = q.shape
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
     dh0 = (torch.empty((B, H, d_k, v.shape[3]), dtype=torch.float32, device=q.device)
            if want_dh0 else None)
-    n = delta_workspace_size(prob)
-    if ws is None or ws.numel() < n:
-        if ws_from_fwd:
-            raise ValueError("ws_from_fwd: the workspace is smaller than the problem needs")
-        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    ws = _buffer(delta_workspace_size(prob), q.device, ws)
+    scratch = _buffer(delta_workspace_size(prob, True), q.device, scratch)
     rc = load().gla_delta_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(beta), _p(h0),
                               _p(segment_ids), _p(dO), _p(dhT), _p(dq), _p(dk), _p(dv), _p(dg),
-                              _p(dbeta), _p(dh0), _p(ws), ws.numel(), _stream())
+                              _p(dbeta), _p(dh0), _p(ws), ws.numel(), _p(scratch), scratch.numel(),
+                              _stream())
     if rc:
         raise GlaError(rc, "gla_delta_bwd")
     return dq, dk, dv, dg, dbeta, dh0
 
 
+_delta_generation = [0]
+
+
 class DeltaFunction(torch.autograd.Function):
     """Autograd wrapper of the gated delta rule: both passes run the HIP library.
-    The forward's workspace (its per-chunk factors) is kept for the backward."""
+    The forward's workspace (its per-chunk factors) is kept for the backward,
+    stamped with a generation of its own (autograd itself rejects inputs changed
+    in place in between); the backward's scratch is allocated in the backward."""
 
     @staticmethod
     def forward(ctx, q, k, v, g, beta, h0, segment_ids):
-        ws = torch.empty(max(delta_workspace_size(delta_problem(q, v)), 1), dtype=torch.uint8, device=q.device)
-        o, hT = delta_fwd(q, k, v, g, beta, h0, segment_ids, ws=ws)
+        _delta_generation[0] += 1
+        gen = _delta_generation[0]
+        ws = _buffer(delta_workspace_size(delta_problem(q, v)), q.device)
+        o, hT = delta_fwd(q, k, v, g, beta, h0, segment_ids, ws=ws, generation=gen)
         ctx.save_for_backward(q, k, v, g, beta, h0, segment_ids)
-        ctx.ws = ws
+        ctx.ws, ctx.gen = ws, gen
         return o, hT
 
     @staticmethod
@@ -581,5 +595,5 @@ class DeltaFunction(torch.autograd.Function):
         dO = dO.contiguous() if dO is not None else torch.zeros(v.shape, dtype=v.dtype, device=v.device)
         dhT = dhT.contiguous().float() if dhT is not None else None
         dq, dk, dv, dg, dbeta, dh0 = delta_bwd(q, k, v, g, beta, dO, h0, seg, dhT, want_dh0=h0 is not None,
-                                               ws=ctx.ws, ws_from_fwd=True)
+                                               ws=ctx.ws, ws_from_fwd=True, generation=ctx.gen)
         return dq, dk, dv, dg, dbeta, dh0, None

@@ -366,17 +366,35 @@ int check_delta(const gla_delta_problem* p) {
     return GLA_OK;
 }
 
+// ws: the stamp, then the forward's per-chunk factors; scratch: the backward's
+// per-chunk intermediates
 size_t delta_ws_bytes(const gla_delta_problem* p) {
     const int64_t nc = (p->T + 63) / 64;
-    return (size_t)(p->B * p->H * nc) * (size_t)gla::delta_ws_floats_per_chunk(p->d_k, p->d_v) * sizeof(float);
+    return (size_t)gla::kDeltaHeaderBytes +
+           (size_t)(p->B * p->H * nc) * (size_t)gla::delta_fwd_floats_per_chunk(p->d_k, p->d_v) * sizeof(float);
+}
+size_t delta_scratch_bytes(const gla_delta_problem* p) {
+    const int64_t nc = (p->T + 63) / 64;
+    return (size_t)(p->B * p->H * nc) * (size_t)gla::delta_bwd_floats_per_chunk(p->d_k, p->d_v) * sizeof(float);
 }
 
-gla::DeltaArgs delta_args(const gla_delta_problem* p, void* ws) {
+gla::DeltaArgs delta_args(const gla_delta_problem* p, const void* q, const void* k, const void* v,
+                          const void* g, const void* beta, const int32_t* seg, void* ws) {
     gla::DeltaArgs a;
     memset(&a, 0, sizeof a);
     a.B = p->B; a.T = p->T; a.H = p->H; a.dk = p->d_k; a.dv = p->d_v;
-    a.ws = (float*)ws;
-    a.ws_chunk = gla::delta_ws_floats_per_chunk(p->d_k, p->d_v);
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.seg = seg;
+    a.stamp = (uint64_t*)ws;
+    a.ws = (float*)((char*)ws + gla::kDeltaHeaderBytes);
+    a.ws_chunk = gla::delta_fwd_floats_per_chunk(p->d_k, p->d_v);
+    // what the per-chunk factors in ws are computed from
+    const uint64_t words[] = {0x61746c65642d6177ull /* tag */, (uint64_t)p->B, (uint64_t)p->T,
+                              (uint64_t)p->H, (uint64_t)p->d_k, (uint64_t)p->d_v, (uint64_t)p->dtype,
+                              (uint64_t)(uintptr_t)q, (uint64_t)(uintptr_t)k, (uint64_t)(uintptr_t)v,
+                              (uint64_t)(uintptr_t)g, (uint64_t)(uintptr_t)beta, (uint64_t)(uintptr_t)seg,
+                              (uint64_t)p->generation, 0, 0};
+    static_assert(sizeof words / sizeof words[0] == gla::kDeltaStampWords, "stamp words");
+    for (int i = 0; i < gla::kDeltaStampWords; ++i) a.expect.w[i] = words[i];
     return a;
 }
 
@@ -442,7 +460,7 @@ int gla_fwd(const gla_problem* p, const void* q, const void* k, const void* v, c
             size_t ws_bytes, void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
-    if (!q || !k || !v || !g || !o) return GLA_E_NULL;
+    if (p->T > 0 && (!q || !k || !v || !g || !o)) return GLA_E_NULL;
     const void* ptrs[] = {q, k, v, g, h0, segment_ids, o, hT, ws};
     for (const void* x : ptrs)
         if (x && !aligned(x)) return GLA_E_ALIGN;
@@ -457,7 +475,7 @@ int gla_fwd_noalloc(const gla_problem* p, const void* q, const void* k, const vo
                     const float* h0, const int32_t* segment_ids, void* o, float* hT, void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
-    if (!q || !k || !v || !g || !o) return GLA_E_NULL;
+    if (p->T > 0 && (!q || !k || !v || !g || !o)) return GLA_E_NULL;
     const void* ptrs[] = {q, k, v, g, h0, segment_ids, o, hT};
     for (const void* x : ptrs)
         if (x && !aligned(x)) return GLA_E_ALIGN;
@@ -483,7 +501,7 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
             void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
-    if (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg) return GLA_E_NULL;
+    if (p->T > 0 && (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg)) return GLA_E_NULL;
     const void* ptrs[] = {q, k, v, g, h0, segment_ids, dO, dhT, dq, dk, dv, dg, dh0, ws};
     for (const void* x : ptrs)
         if (x && !aligned(x)) return GLA_E_ALIGN;
@@ -609,11 +627,10 @@ int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const
 
 // ---- gated delta rule
 int gla_delta_workspace_size(const gla_delta_problem* p, int for_backward, size_t* bytes) {
-    (void)for_backward;  // (the two passes share one layout)
     const int rc = check_delta(p);
     if (rc) return rc;
     if (!bytes) return GLA_E_NULL;
-    *bytes = delta_ws_bytes(p);
+    *bytes = for_backward ? delta_scratch_bytes(p) : delta_ws_bytes(p);
     return GLA_OK;
 }
 
@@ -632,8 +649,8 @@ int gla_delta_fwd(const gla_delta_problem* p, const void* q, const void* k, cons
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     if (p->T == 0) return copy_state(hT, h0, p->B * p->H * p->d_k * p->d_v, st);
-    gla::DeltaArgs a = delta_args(p, ws);
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.seg = segment_ids; a.o = o; a.hT = hT;
+    gla::DeltaArgs a = delta_args(p, q, k, v, g, beta, segment_ids, ws);
+    a.h0 = h0; a.o = o; a.hT = hT;
     const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_delta_fwd<gla::bf16>(a, st)
                                               : gla::launch_delta_fwd<float>(a, st);
     return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
@@ -642,24 +659,27 @@ int gla_delta_fwd(const gla_delta_problem* p, const void* q, const void* k, cons
 int gla_delta_bwd(const gla_delta_problem* p, const void* q, const void* k, const void* v, const void* g,
                   const void* beta, const float* h0, const int32_t* segment_ids, const void* dO,
                   const float* dhT, void* dq, void* dk, void* dv, void* dg, void* dbeta, float* dh0,
-                  void* ws, size_t ws_bytes, void* stream) {
+                  void* ws, size_t ws_bytes, void* scratch, size_t scratch_bytes, void* stream) {
     int rc = check_delta(p);
     if (rc) return rc;
     if (p->T > 0 && (!q || !k || !v || !g || !beta || !dO || !dq || !dk || !dv || !dg || !dbeta))
         return GLA_E_NULL;
-    const void* ptrs[] = {q, k, v, g, beta, h0, segment_ids, dO, dhT, dq, dk, dv, dg, dbeta, dh0, ws};
+    const void* ptrs[] = {q, k, v, g, beta, h0, segment_ids, dO, dhT, dq, dk, dv, dg, dbeta, dh0, ws, scratch};
     for (const void* x : ptrs)
         if (x && !aligned(x)) return GLA_E_ALIGN;
-    const size_t need = delta_ws_bytes(p);
+    const size_t need = delta_ws_bytes(p), need2 = delta_scratch_bytes(p);
     if (ws_bytes < need || (need > 0 && !ws)) return GLA_E_WORKSPACE;
+    if (scratch_bytes < need2 || (need2 > 0 && !scratch)) return GLA_E_WORKSPACE;
     rc = check_device();
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     if (p->T == 0) return copy_state(dh0, dhT, p->B * p->H * p->d_k * p->d_v, st);
-    gla::DeltaArgs a = delta_args(p, ws);
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.h0 = h0; a.seg = segment_ids; a.dO = dO;
+    gla::DeltaArgs a = delta_args(p, q, k, v, g, beta, segment_ids, ws);
+    a.h0 = h0; a.dO = dO;
     a.dhT = dhT; a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
-    a.ws_prepared = (p->flags & GLA_DELTA_WS_FROM_FWD) != 0;
+    a.ws2 = (float*)scratch;
+    a.ws2_chunk = gla::delta_bwd_floats_per_chunk(p->d_k, p->d_v);
+    a.check_stamp = (p->flags & GLA_DELTA_WS_FROM_FWD) != 0;
     const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_delta_bwd<gla::bf16>(a, st)
                                               : gla::launch_delta_bwd<float>(a, st);
     return e == hipSuccess ? GLA_OK : GLA_E_LAUNCH;

@@ -125,6 +125,13 @@ template <typename T, int D> hipError_t launch_norm_gate_fwd(const NormArgs& a, 
 template <typename T, int D> hipError_t launch_norm_gate_bwd(const NormArgs& a, hipStream_t st);
 
 // the gated delta rule (chunked WY/UT form), gla_delta.hip
+// What a workspace's per-chunk factors were computed from: the problem, the
+// input pointers and the caller's generation value (kept in the workspace's
+// first bytes by the forward; see gla_delta_fwd in include/gla.h).
+constexpr int kDeltaStampWords = 16;
+struct DeltaStamp {
+    uint64_t w[kDeltaStampWords];
+};
 struct DeltaArgs {
     const void *q, *k, *v, *g, *beta, *dO;  // [B][T][H][d] (g, beta: [B][T][H]), input dtype
     const float *h0, *dhT;                  // [B][H][dk][dv] or null
@@ -132,13 +139,19 @@ struct DeltaArgs {
     void* o;                                // forward output
     float* hT;                              // forward output or null
     void *dq, *dk_out, *dv_out, *dg, *dbeta;  // backward outputs
-    int32_t ws_prepared;                    // backward: ws already holds the forward's per-chunk factors
     float* dh0;                             // backward output or null
-    float* ws;                              // delta_ws_floats_per_chunk floats per (b, h, chunk)
+    float* ws;                              // the forward's factors: delta_fwd_floats_per_chunk per (b, h, chunk)
     int64_t ws_chunk;
+    float* ws2;                             // backward only: delta_bwd_floats_per_chunk per (b, h, chunk)
+    int64_t ws2_chunk;
+    uint64_t* stamp;                        // the workspace's stamp words
+    DeltaStamp expect;                      // this call's stamp
+    int32_t check_stamp;                    // backward: skip the prepare pass when stamp == expect
     int64_t B, T, H, dk, dv;
 };
-int64_t delta_ws_floats_per_chunk(int64_t dk, int64_t dv);
+constexpr int64_t kDeltaHeaderBytes = 256;  // the stamp, ahead of the per-chunk factors
+int64_t delta_fwd_floats_per_chunk(int64_t dk, int64_t dv);
+int64_t delta_bwd_floats_per_chunk(int64_t dk, int64_t dv);
 template <typename T> hipError_t launch_delta_fwd(const DeltaArgs& a, hipStream_t st);
 template <typename T> hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st);
 

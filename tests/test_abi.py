@@ -325,7 +325,7 @@ def test_norm_gate_workspace(lib):
 def delta_prob(**kw):
     d = dict(B=2, T=100, H=4, d_k=128, d_v=64, dtype=1)
     d.update(kw)
-    return gb.DeltaProblem(d["B"], d["T"], d["H"], d["d_k"], d["d_v"], d["dtype"], 0)
+    return gb.DeltaProblem(d["B"], d["T"], d["H"], d["d_k"], d["d_v"], d["dtype"], 0, 0)
 
 
 def call_delta_fwd(lib, p, ptrs=None, ws_bytes=0):
@@ -337,13 +337,14 @@ def call_delta_fwd(lib, p, ptrs=None, ws_bytes=0):
     return lib.gla_delta_fwd(None if p is None else ctypes.byref(p), *[c(q[n]) for n in names], ws_bytes, None)
 
 
-def call_delta_bwd(lib, p, ptrs=None, ws_bytes=0):
+def call_delta_bwd(lib, p, ptrs=None, ws_bytes=0, scratch_bytes=0):
     names = ["q", "k", "v", "g", "beta", "h0", "seg", "dO", "dhT", "dq", "dk", "dv", "dg", "dbeta", "dh0", "ws"]
     q = {n: FAKE for n in names}
-    q.update(h0=None, seg=None, dhT=None, dh0=None, ws=None)
+    q.update(h0=None, seg=None, dhT=None, dh0=None, ws=None, scratch=None)
     q.update(ptrs or {})
     c = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.gla_delta_bwd(ctypes.byref(p), *[c(q[n]) for n in names], ws_bytes, None)
+    return lib.gla_delta_bwd(ctypes.byref(p), *[c(q[n]) for n in names], ws_bytes, c(q["scratch"]),
+                             scratch_bytes, None)
 
 
 def test_delta_argument_errors(lib):
@@ -363,12 +364,27 @@ def test_delta_argument_errors(lib):
     assert call_delta_bwd(lib, delta_prob(), {"dh0": FAKE + 8}) == -5
 
 
+def delta_sizes(lib, p):
+    n, m = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.gla_delta_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == 0
+    assert lib.gla_delta_workspace_size(ctypes.byref(p), 1, ctypes.byref(m)) == 0
+    return n.value, m.value
+
+
 def test_delta_workspace(lib):
-    n = ctypes.c_size_t()
-    assert lib.gla_delta_workspace_size(ctypes.byref(delta_prob()), 1, ctypes.byref(n)) == 0
-    assert n.value > 0
-    assert call_delta_fwd(lib, delta_prob(), ws_bytes=n.value) == -6
-    assert call_delta_bwd(lib, delta_prob(), {"ws": FAKE}, ws_bytes=n.value - 1) == -6
-    m = ctypes.c_size_t()
-    assert lib.gla_delta_workspace_size(ctypes.byref(delta_prob(T=200)), 1, ctypes.byref(m)) == 0
-    assert m.value == 2 * n.value  # 4 chunks against 2
+    """ws: a 256-byte stamp and the forward's per-chunk factors (T, P: 64 x 64;
+    U: 64 x d_v; W, gamma Q, decayed K: 64 x d_k; the carry: 4 floats); the
+    backward's scratch: 2 d_k x d_v + 64 (3 d_v + 5 d_k) floats per chunk."""
+    p = delta_prob()  # 2 chunks x 8 heads, d_k 128, d_v 64
+    n, m = delta_sizes(lib, p)
+    per_f = 2 * 64 * 64 + 64 * (64 + 3 * 128) + 4
+    per_b = 2 * 128 * 64 + 64 * (3 * 64 + 5 * 128)
+    assert n == 256 + 2 * 8 * per_f * 4 and m == 2 * 8 * per_b * 4
+    assert call_delta_fwd(lib, p, ws_bytes=n) == -6                       # ws NULL
+    assert call_delta_fwd(lib, p, {"ws": FAKE}, ws_bytes=n - 1) == -6
+    assert call_delta_bwd(lib, p, {"ws": FAKE}, ws_bytes=n - 1, scratch_bytes=m) == -6
+    assert call_delta_bwd(lib, p, {"ws": FAKE}, ws_bytes=n, scratch_bytes=m) == -6   # scratch NULL
+    assert call_delta_bwd(lib, p, {"ws": FAKE, "scratch": FAKE}, ws_bytes=n, scratch_bytes=m - 1) == -6
+    assert call_delta_bwd(lib, p, {"ws": FAKE, "scratch": FAKE + 8}, ws_bytes=n, scratch_bytes=m) == -5
+    n2, m2 = delta_sizes(lib, delta_prob(T=200))
+    assert n2 - 256 == 2 * (n - 256) and m2 == 2 * m  # 4 chunks against 2

@@ -115,6 +115,39 @@ def test_delta_bwd_reuses_forward_workspace(B, T, H, dk, dv, dtype, lens):
     compare(got, run_oracle(case), dtype, "delta reuse")
 
 
+def test_delta_ws_stamp_guards_reuse():
+    """GLA_DELTA_WS_FROM_FWD reuses ws only when its stamp (sizes, input pointers,
+    generation) is this call's: a workspace from other inputs, from the same
+    buffers changed in place under a new generation, or left by a backward that
+    recomputed for other inputs is recomputed, so every gradient equals the
+    recomputing backward's, bit for bit."""
+    mk = lambda seed: delta_case("stamp", B=1, T=200, H=2, d_k=64, d_v=64, dtype=torch.bfloat16, seed=seed,
+                                 lengths=[120, 80], with_h0=True, with_dhT=True).to("cuda")
+    a, b = mk(11), mk(12)
+    args = lambda c: (c.q, c.k, c.v, c.g, c.beta, c.dO, c.h0, c.segment_ids, c.dhT)
+    fresh_a, fresh_b = gb.delta_bwd(*args(a)), gb.delta_bwd(*args(b))
+    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(a.q, a.v)), dtype=torch.uint8, device="cuda")
+    gb.delta_fwd(a.q, a.k, a.v, a.g, a.beta, a.h0, a.segment_ids, ws=ws, generation=1)
+    # other inputs, same generation: their own factors
+    got_b = gb.delta_bwd(*args(b), ws=ws, ws_from_fwd=True, generation=1)
+    # the backward recomputed for b: ws now holds b's factors, stamped so; a again
+    got_a = gb.delta_bwd(*args(a), ws=ws, ws_from_fwd=True, generation=1)
+    # a's forward, then a's q changed in place under a new generation
+    gb.delta_fwd(a.q, a.k, a.v, a.g, a.beta, a.h0, a.segment_ids, ws=ws, generation=2)
+    q_old = a.q.clone()
+    a.q.copy_(b.q)
+    got_a2 = gb.delta_bwd(*args(a), ws=ws, ws_from_fwd=True, generation=3)
+    fresh_a2 = gb.delta_bwd(*args(a))
+    a.q.copy_(q_old)
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, got_b, fresh_b):
+        assert torch.equal(x, y), "other inputs: " + n
+    for n, x, y in zip(NAMES, got_a, fresh_a):
+        assert torch.equal(x, y), "after a recomputing backward: " + n
+    for n, x, y in zip(NAMES, got_a2, fresh_a2):
+        assert torch.equal(x, y), "inputs changed in place: " + n
+
+
 def test_delta_autograd_matches_bwd():
     """DeltaFunction keeps the forward's workspace for its backward."""
     case = delta_case("autograd", B=1, T=150, H=2, d_k=64, d_v=64, dtype=torch.float32, seed=3,
@@ -147,7 +180,17 @@ def test_delta_full_size_sampled():
     heads 0 and 5 compared whole against the oracle run on that slice."""
     case = delta_workload()
     print("full-size delta", tuple(case.q.shape), flush=True)
-    got = run_gpu(case.to("cuda"))
+    c = case.to("cuda")
+    got = run_gpu(c)
+    # the benchmark's backward reuses the forward's factors: bit for bit the same
+    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(c.q, c.v)), dtype=torch.uint8, device="cuda")
+    gb.delta_fwd(c.q, c.k, c.v, c.g, c.beta, c.h0, c.segment_ids, ws=ws, generation=1)
+    reused = gb.delta_bwd(c.q, c.k, c.v, c.g, c.beta, c.dO, c.h0, c.segment_ids, c.dhT, ws=ws,
+                          ws_from_fwd=True, generation=1)
+    torch.cuda.synchronize()
+    for n, x in zip(NAMES, reused):
+        assert torch.equal(x, got[n]), "full-size reuse: " + n
+    del c, ws, reused
     heads = [0, 5]
     sub = head_slice(case, heads)
     ref = run_oracle(sub)

@@ -232,6 +232,29 @@ def test_packed_documents_match_separate_runs():
         print("head", qh, len(lens), "documents match", flush=True)
 
 
+@pytest.mark.parametrize("gate,dtype,states", [("vector", torch.bfloat16, True),
+                                                ("scalar", torch.float32, True),
+                                                ("vector", torch.float32, False),
+                                                ("scalar", torch.bfloat16, False)])
+def test_empty_sequence(gate, dtype, states):
+    """T = 0: the state passes straight through, hT = h0 and dh0 = dhT (zeros when
+    absent), every output written (the outputs start as NaN)."""
+    B, H, d, dev = 2, 4, 128, "cuda"
+    mk = lambda *shape, dt=dtype: torch.empty(shape, dtype=dt, device=dev)
+    q, k, v, dO = mk(B, 0, H, d), mk(B, 0, H, d), mk(B, 0, H, d), mk(B, 0, H, d)
+    g = mk(B, 0, H, d) if gate == "vector" else mk(B, 0, H)
+    gen = torch.Generator().manual_seed(7)
+    h0 = torch.randn((B, H, d, d), generator=gen).to(dev) if states else None
+    dhT = torch.randn((B, H, d, d), generator=gen).to(dev) if states else None
+    o, hT = gb.fwd(q, k, v, g, h0, None, gate=gate)
+    dq, dk, dv, dg, dh0 = gb.bwd(q, k, v, g, dO, h0, None, dhT, gate=gate)
+    torch.cuda.synchronize()
+    zeros = torch.zeros((B, H, d, d), device=dev)
+    assert tuple(o.shape) == (B, 0, H, d) and tuple(dg.shape) == tuple(g.shape)
+    assert torch.equal(hT, h0 if states else zeros)
+    assert torch.equal(dh0, dhT if states else zeros)
+
+
 def test_deterministic():
     case = small_case(seed=3, B=1, T=200, H=4, H_qk=2, d=128, gate="vector", dtype=torch.bfloat16,
                       lengths=[70, 130])
