@@ -146,7 +146,7 @@ def copy_bandwidth(dev, mib=1024, reps=5):
     return 2 * n * 4 / sec / 1e9
 
 
-def time_gla(name, steps, warmup, cold=0, fused=False, split=0):
+def time_gla(name, steps, warmup, cold=0, fused=False, split=0, saved=True):
     """One gla_fwd + one gla_bwd per step on workload `name`, inputs resident in
     device memory: event-timed fwd and bwd (mean and median), wall time per
     step, and (cold > 0) the median of `cold` steps after a 512 MB cache flush."""
@@ -177,9 +177,16 @@ def time_gla(name, steps, warmup, cold=0, fused=False, split=0):
         dq, dk_, dv_ = gb.fused_views(dX, case.H_qk, dk, H, dv)
         prob.ld_qk = prob.ld_v = prob.ld_dqk = prob.ld_dv = W
     dh0 = torch.empty_like(case.h0) if case.h0 is not None else None
-    nf, nb = gb.workspace_size(prob, False), gb.workspace_size(prob, True)
-    wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev)
-    wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    if saved:
+        # the forward stores the per-chunk states for the backward in one shared
+        # workspace (GLA_SAVE_STATES); the inputs never change, so one generation
+        prob.flags, prob.generation = gb.GLA_SAVE_STATES, 1
+        nf = nb = gb.workspace_size(prob, True)
+        wsf = wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    else:
+        nf, nb = gb.workspace_size(prob, False), gb.workspace_size(prob, True)
+        wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device=dev)
+        wsb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = gb.ctypes.c_void_p(stream.cuda_stream)
 
@@ -330,6 +337,10 @@ def main():
                          "dq, dk, dv written into one fused gradient of that shape")
     ap.add_argument("--split", type=int, default=0,
                     help="sequence pieces per (b, h); 0 = the library's own choice")
+    ap.add_argument("--states", choices=("saved", "recompute"), default="saved",
+                    help="saved: the forward stores the per-chunk states for the backward "
+                         "(GLA_SAVE_STATES, one shared workspace); recompute: the backward "
+                         "recomputes them")
     ap.add_argument("--also", default=None,
                     help="comma-separated workloads timed beside the main one (default: %s for "
                          "the default workload, none otherwise; 'none' for none)" % ",".join(ALSO))
@@ -358,7 +369,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     copy_gbs = copy_bandwidth(dev)
-    r = time_gla(args.workload, args.steps, args.warmup, args.cold, args.fused, args.split)
+    saved = args.states == "saved"
+    r = time_gla(args.workload, args.steps, args.warmup, args.cold, args.fused, args.split, saved)
     case = r["case"]
     B, T, H, dk, dv = case.B, case.T, case.H, case.d_k, case.d_v
     fwd_us, bwd_us = r["fwd_us"], r["bwd_us"]
@@ -386,6 +398,8 @@ def main():
         "config": {"workload": "%s: %s" % (args.workload, WORKLOADS[args.workload]),
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
                    "chunk": case.chunk, "split": args.split, "parallelism": "single GPU",
+                   "states": ("stored by the forward for the backward" if saved else
+                              "recomputed by the backward"),
                    "layout": ("q, k, v read from one [B, T, %d] projection tensor; one fused "
                               "gradient" % r["W"]) if args.fused else "packed q, k, v"},
         "roofline": roof,
@@ -399,7 +413,7 @@ def main():
         also = ",".join(ALSO) if (args.workload == "c2" and not args.fused and args.split == 0) else "none"
     others = {}
     for name in [x for x in also.split(",") if x and x != "none"]:
-        o = time_gla(name, args.steps, args.warmup)
+        o = time_gla(name, args.steps, args.warmup, saved=saved)
         c = o["case"]
         rf = gla_roofline(c, o["fwd_us"], o["bwd_us"], copy_gbs)
         others[name] = {"workload": WORKLOADS[name],

@@ -123,7 +123,33 @@ typedef struct {
      * + h * d_k.  A non-zero stride is at least the packed one and a multiple of
      * 16 bytes.  o, dO, g and dg are always packed. */
     int64_t ld_qk, ld_v, ld_dqk, ld_dv;
+    int32_t flags;      /* 0, or GLA_SAVE_STATES; other bits: GLA_E_UNSUPPORTED */
+    int32_t reserved;   /* 0 */
+    int64_t generation; /* with GLA_SAVE_STATES: the caller's count of changes to the inputs */
 } gla_problem;
+
+/* Saved states (flags = GLA_SAVE_STATES, given to both calls of a forward /
+ * backward pair that share one workspace).  The backward needs the state
+ * entering every chunk; without this flag it recomputes them with a state
+ * pass over k, v and g (and, for split rows, a summary pass over the same
+ * inputs).  With it, gla_fwd also stores those states (in the input dtype) in
+ * ws, as the forward kernel passes through them, together with a stamp of what
+ * they were computed from: the problem's sizes, dtype, gate and strides, the q,
+ * k, v, g, h0 and segment_ids pointers and p->generation.  gla_bwd compares the
+ * stamp with its own call's on the device: when they are equal its state passes
+ * exit at once and it uses the stored states; otherwise it recomputes them (and
+ * stamps the workspace for its own inputs).  The caller's part: give both calls
+ * the same generation only while the inputs' contents are unchanged (change it
+ * whenever they are written in place).  The workspace size is the same for both
+ * calls with this flag (gla_workspace_size(p, 0) == gla_workspace_size(p, 1)).
+ * The forward stores states for bf16, scalar gate, d_k = d_v = 128: there the
+ * backward's state pass runs alone, before a walk over the chunks, and is
+ * skipped.  For every other problem the flag only sets the workspace size:
+ * there the state pass runs beside the state-gradient pass, so skipping it
+ * would gain less than the forward's store of every state costs, and the
+ * backward recomputes the states as without the flag.  Results equal the
+ * recomputing backward's up to float rounding order. */
+#define GLA_SAVE_STATES 1
 
 /* Fused projection.  The FLAT page ("FLAT: Flash Linear Attention on TPUs",
  * sections Gated Linear Attention (the data-movement paragraph) and Full Linear

@@ -18,6 +18,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "gla.h")
 
 GLA_F32, GLA_BF16 = 0, 1
 GLA_GATE_SCALAR, GLA_GATE_VECTOR = 0, 1
+GLA_SAVE_STATES = 1
 STATUS = {0: "GLA_OK", -1: "GLA_E_NULL", -2: "GLA_E_SHAPE", -3: "GLA_E_DTYPE",
           -4: "GLA_E_UNSUPPORTED", -5: "GLA_E_ALIGN", -6: "GLA_E_WORKSPACE",
           -7: "GLA_E_DEVICE", -8: "GLA_E_LAUNCH", -9: "GLA_E_SCRATCH"}
@@ -28,7 +29,8 @@ class Problem(ctypes.Structure):
                 ("H_qk", ctypes.c_int64), ("d_k", ctypes.c_int64), ("d_v", ctypes.c_int64),
                 ("chunk", ctypes.c_int32), ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("split", ctypes.c_int32), ("ld_qk", ctypes.c_int64), ("ld_v", ctypes.c_int64),
-                ("ld_dqk", ctypes.c_int64), ("ld_dv", ctypes.c_int64)]
+                ("ld_dqk", ctypes.c_int64), ("ld_dv", ctypes.c_int64), ("flags", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("generation", ctypes.c_int64)]
 
 
 class ConvProblem(ctypes.Structure):
@@ -116,13 +118,14 @@ def header_functions():
 
 
 def make_problem(B, T, H, H_qk, d_k, d_v, gate="scalar", dtype=torch.bfloat16, chunk=64, split=0,
-                 ld_qk=0, ld_v=0, ld_dqk=0, ld_dv=0):
+                 ld_qk=0, ld_v=0, ld_dqk=0, ld_dv=0, flags=0, generation=0):
     """gla_problem; split = sequence pieces per (b, h), 0 = chosen by the library;
-    ld_* = row strides of q/k, v, dq/dk, dv in elements (0 = packed)."""
+    ld_* = row strides of q/k, v, dq/dk, dv in elements (0 = packed); flags = 0
+    or GLA_SAVE_STATES, with the caller's input generation."""
     return Problem(B, T, H, H_qk, d_k, d_v, chunk,
                    GLA_GATE_VECTOR if gate == "vector" else GLA_GATE_SCALAR,
                    GLA_BF16 if dtype == torch.bfloat16 else GLA_F32, split,
-                   ld_qk, ld_v, ld_dqk, ld_dv)
+                   ld_qk, ld_v, ld_dqk, ld_dv, flags, 0, generation)
 
 
 def workspace_size(prob: Problem, backward: bool) -> int:
@@ -168,7 +171,7 @@ def row_stride(t, name):
     return ld
 
 
-def problem_of(q, v, g, gate, chunk=64, split=0, k=None):
+def problem_of(q, v, g, gate, chunk=64, split=0, k=None, save_states=False, generation=0):
     B, T, H_qk, d_k = q.shape
     H, d_v = v.shape[2], v.shape[3]
     want = (B, T, H, d_k) if gate == "vector" else (B, T, H)
@@ -177,31 +180,49 @@ def problem_of(q, v, g, gate, chunk=64, split=0, k=None):
     ld_qk, ld_v = row_stride(q, "q"), row_stride(v, "v")
     if k is not None and row_stride(k, "k") != ld_qk:
         raise ValueError("q and k must have the same row stride")
-    return make_problem(B, T, H, H_qk, d_k, d_v, gate, q.dtype, chunk, split, ld_qk, ld_v)
+    return make_problem(B, T, H, H_qk, d_k, d_v, gate, q.dtype, chunk, split, ld_qk, ld_v,
+                        flags=GLA_SAVE_STATES if save_states else 0, generation=generation)
 
 
-def _workspace(prob, backward, device, ws):
+def states_workspace(q, k, v, g, *, gate="scalar", chunk=64, split=0):
+    """A workspace for a fwd / bwd pair with save_states=True (one size serves both)."""
+    prob = problem_of(q, v, g, gate, chunk, split, k, save_states=True)
+    n = workspace_size(prob, True)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def _workspace(prob, backward, device, ws, keep=False):
+    """(ws, bytes): the given workspace, or a new one if it is missing or too small
+    (keep: the caller's workspace is required, as it carries saved states)."""
     n = workspace_size(prob, backward)
-    if n == 0:
+    if n == 0 and not keep:
         return None, 0
     if ws is None or ws.numel() < n:
+        if keep:
+            raise ValueError("workspace of %d bytes, %d needed" % (0 if ws is None else ws.numel(), n))
         ws = torch.empty(n, dtype=torch.uint8, device=device)
     return ws, ws.numel()
 
 
 def fwd(q, k, v, g, h0=None, segment_ids=None, *, gate="scalar", chunk=64, want_hT=True,
-        out=None, ws=None, split=0):
-    """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted)."""
+        out=None, ws=None, split=0, save_states=False, generation=0):
+    """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted).
+
+    save_states=True (GLA_SAVE_STATES): also store the per-chunk states in `ws`
+    (states_workspace() makes one), stamped with these inputs and `generation`,
+    for a bwd(..., save_states=True, ws=ws) of the same inputs."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, q.dtype, strided=True)
     _check(g, "g", q.dtype)
     _check(h0, "h0", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = problem_of(q, v, g, gate, chunk, split, k)
+    prob = problem_of(q, v, g, gate, chunk, split, k, save_states, generation)
+    if save_states and ws is None:
+        raise ValueError("save_states: pass the workspace the backward will be given")
     B, T, H, d_v, d_k = prob.B, prob.T, prob.H, prob.d_v, prob.d_k
     o = out if out is not None else torch.empty((B, T, H, d_v), dtype=q.dtype, device=q.device)
     hT = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device) if want_hT else None
-    ws, nws = _workspace(prob, False, q.device, ws)
+    ws, nws = _workspace(prob, False, q.device, ws, keep=save_states)
     rc = load().gla_fwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(h0), _p(segment_ids),
                         _p(o), _p(hT), _p(ws), nws, _stream())
     if rc:
@@ -257,14 +278,18 @@ def _fused_base(q, k, v):
 
 
 def bwd(q, k, v, g, dO, h0=None, segment_ids=None, dhT=None, *, gate="scalar", chunk=64,
-        want_dh0=True, ws=None, split=0, grads=None):
+        want_dh0=True, ws=None, split=0, grads=None, save_states=False, generation=0):
     """dq, dk [B,T,H_qk,d_k], dv [B,T,H,d_v], dg (shape of g), dh0 fp32 (or None).
 
     grads = (dq, dk, dv) writes the gradients into those tensors (token rows may
     be strided, as q, k, v may be).  Otherwise, when q, k, v are the views
     fused_views makes of one projection tensor, dq, dk, dv are returned as the
     same views of one fused gradient tensor (fused_grad() of the result gives
-    it); else they are packed."""
+    it); else they are packed.
+
+    save_states=True: `ws` is the workspace a fwd(..., save_states=True) of these
+    inputs was given; its states are used when its stamp matches these inputs and
+    `generation`, else recomputed."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, q.dtype, strided=True)
     for t, n in ((g, "g"), (dO, "dO")):
@@ -272,7 +297,9 @@ def bwd(q, k, v, g, dO, h0=None, segment_ids=None, dhT=None, *, gate="scalar", c
     _check(h0, "h0", torch.float32)
     _check(dhT, "dhT", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = problem_of(q, v, g, gate, chunk, split, k)
+    prob = problem_of(q, v, g, gate, chunk, split, k, save_states, generation)
+    if save_states and ws is None:
+        raise ValueError("save_states: pass the workspace the forward was given")
     if grads is not None:
         dq, dk, dv = grads
         for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
@@ -293,7 +320,7 @@ def bwd(q, k, v, g, dO, h0=None, segment_ids=None, dhT=None, *, gate="scalar", c
     dg = torch.empty_like(g)
     dh0 = (torch.empty((prob.B, prob.H, prob.d_k, prob.d_v), dtype=torch.float32, device=q.device)
            if want_dh0 else None)
-    ws, nws = _workspace(prob, True, q.device, ws)
+    ws, nws = _workspace(prob, True, q.device, ws, keep=save_states)
     rc = load().gla_bwd(ctypes.byref(prob), _p(q), _p(k), _p(v), _p(g), _p(h0), _p(segment_ids),
                         _p(dO), _p(dhT), _p(dq), _p(dk), _p(dv), _p(dg), _p(dh0), _p(ws), nws,
                         _stream())
@@ -310,14 +337,27 @@ def fused_grad(dq):
     return dq.as_strided((B, T, ld), (T * ld, ld, 1), dq.storage_offset())
 
 
+_gla_generation = [0]
+
+
 class GLAFunction(torch.autograd.Function):
-    """Autograd wrapper: forward and backward both run the HIP library."""
+    """Autograd wrapper: forward and backward both run the HIP library.
+    save_states=True keeps the forward's workspace, with the per-chunk states the
+    forward stored, for the backward (memory held from forward to backward in
+    exchange for the backward's state passes); the workspace is stamped with a
+    generation of its own (autograd itself rejects inputs changed in between)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, g, h0, segment_ids, gate):
-        o, hT = fwd(q, k, v, g, h0, segment_ids, gate=gate)
+    def forward(ctx, q, k, v, g, h0, segment_ids, gate, save_states=False):
+        ws, gen = None, 0
+        if save_states:
+            _gla_generation[0] += 1
+            gen = _gla_generation[0]
+            ws = states_workspace(q, k, v, g, gate=gate)
+        o, hT = fwd(q, k, v, g, h0, segment_ids, gate=gate, ws=ws, save_states=save_states,
+                    generation=gen)
         ctx.save_for_backward(q, k, v, g, h0, segment_ids)
-        ctx.gate = gate
+        ctx.gate, ctx.ws, ctx.gen, ctx.saved = gate, ws, gen, save_states
         return o, hT
 
     @staticmethod
@@ -326,8 +366,10 @@ class GLAFunction(torch.autograd.Function):
         dO = dO.contiguous() if dO is not None else torch.zeros(v.shape, dtype=v.dtype, device=v.device)
         dhT = dhT.contiguous().float() if dhT is not None else None
         dq, dk, dv, dg, dh0 = bwd(q, k, v, g, dO, h0, seg, dhT, gate=ctx.gate,
-                                  want_dh0=h0 is not None)
-        return dq, dk, dv, dg, dh0, None, None
+                                  want_dh0=h0 is not None, ws=ctx.ws, save_states=ctx.saved,
+                                  generation=ctx.gen)
+        ctx.ws = None
+        return dq, dk, dv, dg, dh0, None, None, None
 
 
 class GLAFusedFunction(torch.autograd.Function):

@@ -34,6 +34,7 @@ int check_problem(const gla_problem* p) {
     if (p->B < 1 || p->T < 0 || p->H < 1 || p->H_qk < 1 || p->H_qk > p->H) return GLA_E_SHAPE;
     if (p->H % p->H_qk != 0) return GLA_E_SHAPE;
     if (p->d_k < 1 || p->d_v < 1 || p->chunk < 1) return GLA_E_SHAPE;
+    if ((p->flags & ~GLA_SAVE_STATES) || p->reserved != 0) return GLA_E_UNSUPPORTED;
     if ((p->d_k != 64 && p->d_k != 128) || (p->d_v != 64 && p->d_v != 128)) return GLA_E_UNSUPPORTED;
     if (p->chunk != 64) return GLA_E_UNSUPPORTED;
     // every element count and launch grid must fit
@@ -77,6 +78,14 @@ bool walk_bwd(const gla_problem* p) {
     return p->dtype == GLA_BF16 && p->gate == GLA_GATE_SCALAR && p->d_k == 128 && p->d_v == 128;
 }
 
+// The forward stores the per-chunk states for the backward (GLA_SAVE_STATES) on
+// the walking backward's shape, whose state pass runs alone before the walk.
+// Elsewhere the state pass runs beside the state-gradient pass, so dropping it
+// shortens the backward by little while the forward's store costs a full write
+// of the states: the flag changes nothing there but the workspace size.
+bool saves_states(const gla_problem* p) { return (p->flags & GLA_SAVE_STATES) && walk_bwd(p); }
+bool flag_save(const gla_problem* p) { return (p->flags & GLA_SAVE_STATES) != 0; }
+
 Split plan_split(const gla_problem* p, int for_backward) {
     Split s;
     const int64_t nc = (p->T + 63) / 64;
@@ -93,6 +102,7 @@ Split plan_split(const gla_problem* p, int for_backward) {
             if (bh >= kTargetWG) return s;
             target = kTargetWG;
         } else if (for_backward) {
+            // the state and state-gradient passes run side by side
             per_head = 2 * (p->d_k / 64) * (p->d_v / 64);
             if (bh * per_head >= kNoSplitBwd) return s;
             target = kTargetWGBwd;
@@ -123,6 +133,7 @@ bool per_head_dqdk(const gla_problem* p) {
 struct WsLayout {
     size_t S = 0, dS = 0, dq = 0, dk = 0, xs = 0, bnd = 0;
     size_t pL0 = 0, pL1 = 0, pS = 0, pdS = 0, pD = 0, total = 0;
+    size_t stamp = 0;  // GLA_SAVE_STATES: the stamp, at the start (S follows it)
     Split sp;
 };
 
@@ -132,7 +143,37 @@ struct WsLayout {
 // every chunk (and the final state) and the state gradient at every chunk's
 // end, in the input dtype; per-head fp32 dq, dk when heads share q/k;
 // per-slice partial gate-gradient sums for the scalar gate.
+WsLayout ws_layout_one(const gla_problem* p, int for_backward);
+
+// GLA_SAVE_STATES: one workspace serves both calls; its size is the larger of
+// the two.  Where the forward stores states, both lay it out as the stamp, the
+// states entering every chunk, then the rest of that call's own layout.
 WsLayout ws_layout(const gla_problem* p, int for_backward) {
+    WsLayout L = ws_layout_one(p, for_backward);
+    if (flag_save(p)) {
+        const size_t other = ws_layout_one(p, !for_backward).total;
+        if (other > L.total) L.total = other;
+    }
+    return L;
+}
+
+// what a workspace's saved states are computed from (GLA_SAVE_STATES)
+gla::Stamp states_stamp(const gla_problem* p, const void* q, const void* k, const void* v, const void* g,
+                        const float* h0, const int32_t* seg) {
+    const uint64_t words[] = {0x73657461'74732d67ull /* tag */, (uint64_t)p->B, (uint64_t)p->T, (uint64_t)p->H,
+                              (uint64_t)p->H_qk, (uint64_t)p->d_k | ((uint64_t)p->d_v << 32),
+                              (uint64_t)p->gate | ((uint64_t)p->dtype << 32), (uint64_t)(uintptr_t)q,
+                              (uint64_t)(uintptr_t)k, (uint64_t)(uintptr_t)v, (uint64_t)(uintptr_t)g,
+                              (uint64_t)(uintptr_t)h0, (uint64_t)(uintptr_t)seg,
+                              (uint64_t)ld_or_packed(p->ld_qk, p->H_qk * p->d_k),
+                              (uint64_t)ld_or_packed(p->ld_v, p->H * p->d_v), (uint64_t)p->generation};
+    static_assert(sizeof words / sizeof words[0] == gla::kStampWords, "stamp words");
+    gla::Stamp st;
+    for (int i = 0; i < gla::kStampWords; ++i) st.w[i] = words[i];
+    return st;
+}
+
+WsLayout ws_layout_one(const gla_problem* p, int for_backward) {
     WsLayout L;
     L.sp = plan_split(p, for_backward);
     const int64_t nc = (p->T + 63) / 64;
@@ -140,6 +181,13 @@ WsLayout ws_layout(const gla_problem* p, int for_backward) {
     const size_t st = (size_t)p->d_k * (size_t)p->d_v * es;
     const size_t bh = (size_t)(p->B * p->H);
     size_t off = 0;
+    if (saves_states(p)) {
+        // the stamp and the per-chunk states first, where both calls find them
+        L.stamp = 0;
+        off = (size_t)gla::kStampBytes;
+        L.S = off;
+        off += round_up(bh * (size_t)(nc + 1) * st);
+    }
     if (L.sp.P > 1) {
         const size_t np = bh * (size_t)L.sp.P;
         const size_t pst = round_up(np * (size_t)(p->d_k * p->d_v) * sizeof(float));
@@ -160,8 +208,10 @@ WsLayout ws_layout(const gla_problem* p, int for_backward) {
         L.total = off;
         return L;
     }
-    L.S = off;
-    off += round_up(bh * (size_t)(nc + 1) * st);
+    if (!saves_states(p)) {
+        L.S = off;
+        off += round_up(bh * (size_t)(nc + 1) * st);
+    }
     if (!walk_bwd(p)) {
         L.dS = off;
         off += round_up(bh * (size_t)nc * st);
@@ -276,19 +326,27 @@ template <typename T, bool VEC, int DK, int DV>
 hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t st) {
     hipError_t e;
     const bool wide = wide_blocks(pa, DK, 2, 512);
+    // the states entering the chunks are in ws for these inputs once the state pass
+    // has run (or found the forward's): stamp them so
+    auto stamp = [&]() {
+        return pa.check_stamp ? gla::launch_write_stamp(const_cast<uint64_t*>(pa.stamp), pa.expect, st)
+                              : hipSuccess;
+    };
     if (pa.P > 1) {
-        e = gla::launch_states_pair<T, VEC, DK, DV>(pa, true, wide, st);
+        gla::PassArgs sa = pa;
+        sa.d_from_rev = 1;
+        e = gla::launch_states_pair<T, VEC, DK, DV>(sa, true, wide, st);
         if (e != hipSuccess) return e;
         e = gla::launch_piece_combine(combine_args(pa, DK, DV, 3), st);
         if (e != hipSuccess) return e;
     }
     if constexpr (sizeof(T) == 2 && !VEC && DK == 128 && DV == 128) {
         e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, wide_blocks(pa, DK, 1, 256), st);
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
         e = gla::launch_grad8_walk(ra, st);
     } else {
         e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
         e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
     }
     if (e != hipSuccess) return e;
@@ -393,8 +451,8 @@ gla::DeltaArgs delta_args(const gla_delta_problem* p, const void* q, const void*
                               (uint64_t)(uintptr_t)q, (uint64_t)(uintptr_t)k, (uint64_t)(uintptr_t)v,
                               (uint64_t)(uintptr_t)g, (uint64_t)(uintptr_t)beta, (uint64_t)(uintptr_t)seg,
                               (uint64_t)p->generation, 0, 0};
-    static_assert(sizeof words / sizeof words[0] == gla::kDeltaStampWords, "stamp words");
-    for (int i = 0; i < gla::kDeltaStampWords; ++i) a.expect.w[i] = words[i];
+    static_assert(sizeof words / sizeof words[0] == gla::kStampWords, "stamp words");
+    for (int i = 0; i < gla::kStampWords; ++i) a.expect.w[i] = words[i];
     return a;
 }
 
@@ -417,7 +475,13 @@ int fwd_checked(const gla_problem* p, const WsLayout& L, const void* q, const vo
         a.S_in = (const float*)(w + L.pS);
         a.D_out = (float*)(w + L.pD);
     }
-    return dispatch<FwdF>(p, a, st) == hipSuccess ? GLA_OK : GLA_E_LAUNCH;
+    if (saves_states(p)) a.save_S = (char*)ws + L.S;
+    if (dispatch<FwdF>(p, a, st) != hipSuccess) return GLA_E_LAUNCH;
+    if (saves_states(p) &&
+        gla::launch_write_stamp((uint64_t*)((char*)ws + L.stamp), states_stamp(p, q, k, v, g, h0, segment_ids),
+                                st) != hipSuccess)
+        return GLA_E_LAUNCH;
+    return GLA_OK;
 }
 
 // ---- the forward that allocates nothing (gla_fwd_noalloc)
@@ -475,6 +539,7 @@ int gla_fwd_noalloc(const gla_problem* p, const void* q, const void* k, const vo
                     const float* h0, const int32_t* segment_ids, void* o, float* hT, void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
+    if (p->flags & GLA_SAVE_STATES) return GLA_E_UNSUPPORTED;  // (no workspace to hand to a backward)
     if (p->T > 0 && (!q || !k || !v || !g || !o)) return GLA_E_NULL;
     const void* ptrs[] = {q, k, v, g, h0, segment_ids, o, hT};
     for (const void* x : ptrs)
@@ -529,6 +594,11 @@ int gla_bwd(const gla_problem* p, const void* q, const void* k, const void* v, c
         pa.S_in = (const float*)(w + L.pS);
         pa.dS_in = (const float*)(w + L.pdS);
         pa.D_out = (float*)(w + L.pD);
+    }
+    if (saves_states(p)) {
+        pa.stamp = (const uint64_t*)(w + L.stamp);
+        pa.expect = states_stamp(p, q, k, v, g, h0, segment_ids);
+        pa.check_stamp = 1;
     }
     gla::RevArgs ra;
     memset(&ra, 0, sizeof ra);

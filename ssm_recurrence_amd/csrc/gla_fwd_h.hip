@@ -181,6 +181,9 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
                 *reinterpret_cast<bf16x8*>(sm.sVu + row * PH + cv) = x;
             }
         }
+        // (for the backward) the state entering this chunk, stored while the staged
+        // tiles' registers are free and before the next chunk's loads are issued
+        if (!VEC && a.save_S) store_state_128<bf16>((bf16*)a.save_S + (bh * (NC + 1) + it) * DK * DV, S);
         if (it + 1 < cend) prefetch(t0 + C);
         __syncthreads();
         [[maybe_unused]] const bool strong = VEC && strong_flag_get<8>(sm.sStrong);
@@ -397,6 +400,7 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
         write_out(tl, T_ - tl < C ? (int)(T_ - tl) : C);
     }
 
+    if (!VEC && a.save_S && piece == P - 1) store_state_128<bf16>((bf16*)a.save_S + (bh * (NC + 1) + NC) * DK * DV, S);
     if (a.hT && piece == P - 1) {
 #pragma unroll
         for (int ct = 0; ct < DK / 16; ++ct) {

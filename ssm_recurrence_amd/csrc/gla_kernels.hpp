@@ -6,6 +6,30 @@
 
 namespace gla {
 
+// What a workspace's saved intermediates were computed from (the problem, the
+// input pointers and the caller's generation value), kept in the workspace's
+// first bytes and compared on the device before they are reused.
+constexpr int kStampWords = 16;
+constexpr int64_t kStampBytes = 256;
+struct Stamp {
+    uint64_t w[kStampWords];
+};
+// every thread of the workgroup: the workspace's stamp equals `expect`
+// (thread 0 reads it; the answer is shared through LDS with one barrier)
+__device__ __forceinline__ bool stamp_matches(const uint64_t* stamp, const Stamp& expect) {
+    __shared__ int same;
+    if (threadIdx.x == 0) {
+        int eq = 1;
+#pragma unroll
+        for (int i = 0; i < kStampWords; ++i) eq &= stamp[i] == expect.w[i];
+        same = eq;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(same) != 0;
+}
+// writes a stamp (launched after the pass that stored what it describes)
+hipError_t launch_write_stamp(uint64_t* dst, const Stamp& s, hipStream_t st);
+
 struct PassArgs {
     const void *q, *k, *v, *g, *dO;
     const float *h0, *dhT;
@@ -23,6 +47,17 @@ struct PassArgs {
     const float* dS_in;   // [B*H][P][DK][DV]: state gradient at each piece's end (P > 1)
     float* L_out[2];      // piece summaries from zero, [B*H][P][DK][DV]: forward, reverse
     float* D_out;         // decay product of each piece, [B*H][P][DK]
+    // forward: also store the state entering every chunk, and the final state, in
+    // the input dtype as ws_S's [B*H][NC+1][DK][DV] layout (null: not stored)
+    void* save_S;
+    // backward: ws_S may hold the forward's states; when the stamp there matches
+    // `expect` the passes that would recompute them (ST_STATES, ST_SUM_FWD) exit
+    const uint64_t* stamp;
+    Stamp expect;
+    int32_t check_stamp;
+    // summaries in one launch: D_out of pieces 1.. comes from ST_SUM_REV (which
+    // always runs), of piece 0 from ST_SUM_FWD
+    int32_t d_from_rev;
 };
 
 struct RevArgs {
@@ -125,13 +160,6 @@ template <typename T, int D> hipError_t launch_norm_gate_fwd(const NormArgs& a, 
 template <typename T, int D> hipError_t launch_norm_gate_bwd(const NormArgs& a, hipStream_t st);
 
 // the gated delta rule (chunked WY/UT form), gla_delta.hip
-// What a workspace's per-chunk factors were computed from: the problem, the
-// input pointers and the caller's generation value (kept in the workspace's
-// first bytes by the forward; see gla_delta_fwd in include/gla.h).
-constexpr int kDeltaStampWords = 16;
-struct DeltaStamp {
-    uint64_t w[kDeltaStampWords];
-};
 struct DeltaArgs {
     const void *q, *k, *v, *g, *beta, *dO;  // [B][T][H][d] (g, beta: [B][T][H]), input dtype
     const float *h0, *dhT;                  // [B][H][dk][dv] or null
@@ -145,11 +173,11 @@ struct DeltaArgs {
     float* ws2;                             // backward only: delta_bwd_floats_per_chunk per (b, h, chunk)
     int64_t ws2_chunk;
     uint64_t* stamp;                        // the workspace's stamp words
-    DeltaStamp expect;                      // this call's stamp
+    Stamp expect;                           // this call's stamp
     int32_t check_stamp;                    // backward: skip the prepare pass when stamp == expect
     int64_t B, T, H, dk, dv;
 };
-constexpr int64_t kDeltaHeaderBytes = 256;  // the stamp, ahead of the per-chunk factors
+constexpr int64_t kDeltaHeaderBytes = kStampBytes;  // the stamp, ahead of the per-chunk factors
 int64_t delta_fwd_floats_per_chunk(int64_t dk, int64_t dv);
 int64_t delta_bwd_floats_per_chunk(int64_t dk, int64_t dv);
 template <typename T> hipError_t launch_delta_fwd(const DeltaArgs& a, hipStream_t st);

@@ -31,6 +31,12 @@
 //               zero, chunks last to first, dL <- decay dL + QR^T dO with
 //               QR = q exp(beta) on the chunk's first document (the dS update
 //               of the reverse pass).  Its diagonal part is D_p again.
+// When the forward stored the per-chunk states (its stamp in the workspace
+// matches the backward's; scalar gate, bf16, 128 x 128), ST_STATES and
+// ST_SUM_FWD have nothing to do and exit at once.  The backward's summaries
+// (one launch of both modes) take the decay products of pieces 1 .. P - 1,
+// all the reverse combine reads, from ST_SUM_REV, so that they do not depend
+// on whether ST_SUM_FWD ran.
 #include <type_traits>
 
 #include "gla_common.hpp"
@@ -242,7 +248,11 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
             *reinterpret_cast<f32x4*>(a.L_out[MODE == ST_SUM_REV ? 1 : 0] + prow + 16 * nt + 4 * j4) = St[nt];
-        if ((MODE == ST_SUM_FWD || piece == P - 1) && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
+        // (one writer per piece: ST_SUM_FWD pieces 0 .. P - 2, ST_SUM_REV the last;
+        // with d_from_rev, ST_SUM_FWD piece 0 only and ST_SUM_REV the others)
+        if (n0 == 0 && j4 == 0 &&
+            (MODE == ST_SUM_FWD ? (!a.d_from_rev || piece == 0) : (a.d_from_rev || piece == P - 1)))
+            a.D_out[(bh * P + piece) * DK + cme] = dprod;
     }
 }
 
@@ -292,6 +302,10 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
     // reverse combine needs, comes from its reverse summary instead).
     if constexpr (MODE == ST_SUM_FWD) if (piece == P - 1) return;
     if constexpr (MODE == ST_SUM_REV) if (piece == 0) return;
+    // the forward's states are in the workspace: nothing to recompute (the
+    // forward stores them for bf16 128 x 128 problems only)
+    if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128 && (MODE == ST_STATES || MODE == ST_SUM_FWD))
+        if (a.check_stamp && stamp_matches(a.stamp, a.expect)) return;
 
     const T* k = (const T*)(REV ? a.q : a.k);
     const T* v = (const T*)(REV ? a.dO : a.v);
@@ -426,7 +440,11 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
 #pragma unroll
         for (int nt = 0; nt < NNT; ++nt)
             *reinterpret_cast<f32x4*>(a.L_out[MODE == ST_SUM_REV ? 1 : 0] + prow + 16 * nt + 4 * j4) = St[nt];
-        if ((MODE == ST_SUM_FWD || piece == P - 1) && n0 == 0 && j4 == 0) a.D_out[(bh * P + piece) * DK + cme] = dprod;
+        // (one writer per piece: ST_SUM_FWD pieces 0 .. P - 2, ST_SUM_REV the last;
+        // with d_from_rev, ST_SUM_FWD piece 0 only and ST_SUM_REV the others)
+        if (n0 == 0 && j4 == 0 &&
+            (MODE == ST_SUM_FWD ? (!a.d_from_rev || piece == 0) : (a.d_from_rev || piece == P - 1)))
+            a.D_out[(bh * P + piece) * DK + cme] = dprod;
     }
 }
 
@@ -590,6 +608,15 @@ __global__ __launch_bounds__(256) void k_piece_combine(CombineArgs c) {
             c.dS_in[base + (p - 1) * per] = s;
         }
     }
+}
+
+__global__ void k_write_stamp(uint64_t* dst, const Stamp s) {
+    if (threadIdx.x < kStampWords) dst[threadIdx.x] = s.w[threadIdx.x];
+}
+
+hipError_t launch_write_stamp(uint64_t* dst, const Stamp& s, hipStream_t st) {
+    hipLaunchKernelGGL(k_write_stamp, dim3(1), dim3(64), 0, st, dst, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st) {

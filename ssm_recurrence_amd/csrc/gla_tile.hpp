@@ -156,6 +156,35 @@ __device__ __forceinline__ void docs_from_flags(ChunkDocs* cd, int reset, int nv
     }
 }
 
+// The 128 x 128 state a workgroup of eight waves holds in accumulators (wave w,
+// lane (i, j): S[16 ct + 4 j + e][16 w + i] in S[ct][e]) stored row-major to dst
+// ([128][128], element type T, dst uniform over the workgroup).  Buffer stores
+// keep the per-lane part of the address in one register and the per-element
+// row offset in the instruction, so the 32 stores need no address registers
+// of their own (global stores would hold 32 loop-invariant 64-bit addresses).
+template <typename T>
+__device__ __forceinline__ void store_state_128(T* dst, const f32x4 (&S)[8]) {
+    constexpr int B = (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(dst, 0, 128 * 128 * B, 0x00020000);
+    // the lane index is read afresh (volatile, so not hoisted out of a caller's
+    // loop, where a precomputed offset would hold a register for the whole loop)
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int vo = ((4 * (l >> 4)) * 128 + (l & 15)) * B + 16 * B * w;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int so = (16 * ct + e) * 128 * B;
+            if constexpr (B == 4)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[ct][e]), rs, vo, so, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)S[ct][e]), rs, vo, so,
+                                                      0);
+        }
+}
+
 // Operands of the triangular matrix of ones L^T (L[r][u] = [u <= r]) for the
 // chunk-local prefix below, one per (row tile rt, k step): element e of lane
 // (i, j) is [k0 + j*KPL + e <= 16 rt + i].  The same fragment serves as A

@@ -74,9 +74,14 @@ def part_of(workload, name):
         return [fwd, bwd]
     if "k_fwd" in name:
         return [fwd]
-    m = re.search(r"k_states<[^>]*?(\d+), (\d+)>", name)
-    if m and "k_states2" not in name:
-        return [fwd] if m.group(1) == "1" else [bwd]   # mode 1: the forward split's summaries
+    if "k_states" in name and "k_states2" not in name:
+        # template integers (demangled "..., 128, 1, 128>" or mangled "Li128ELi1ELi128E"):
+        # k_states<T, VEC, DK, DV, MODE, NB>, k_states_w<T, DK, DV, MODE>; mode 1 is the
+        # forward split's summaries
+        ints = re.findall(r"Li(\d+)E", name) if name.startswith("_Z") else \
+            re.findall(r"\b(\d+)\b", name[name.find("<"):name.rfind(">") + 1])
+        mode = ints[-1] if "k_states_w" in name else ints[-2]
+        return [fwd] if mode == "1" else [bwd]
     return [bwd]
 
 

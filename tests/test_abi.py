@@ -107,6 +107,40 @@ def _ws(lib, p, backward):
     return n.value
 
 
+def test_saved_states_flags_and_workspace(lib):
+    """GLA_SAVE_STATES: other flag bits and a non-zero reserved word are refused;
+    with the flag one workspace size serves both calls; where the forward stores
+    states (bf16, scalar gate, 128 x 128) it holds the stamp (256 bytes) and the
+    state entering every chunk plus the final one, in the input dtype, besides
+    everything the backward alone needs; elsewhere it is the backward's own."""
+    for kw in (dict(flags=2), dict(flags=gb.GLA_SAVE_STATES | 4)):
+        p = prob(**kw)
+        assert call_fwd(lib, p) == -4
+        assert call_bwd(lib, p) == -4
+        assert lib.gla_workspace_size(ctypes.byref(p), 1, ctypes.byref(ctypes.c_size_t())) == -4
+    p = prob()
+    p.reserved = 1
+    assert call_fwd(lib, p) == -4
+    for dtype, es in ((torch.bfloat16, 2), (torch.float32, 4)):
+        for gate in ("scalar", "vector"):
+            for d_k, d_v in ((128, 128), (64, 128), (64, 64)):
+                for T, split in ((100, 0), (64 * 40, 4), (1, 0)):
+                    kw = dict(B=2, T=T, H=4, H_qk=2, d_k=d_k, d_v=d_v, gate=gate, dtype=dtype, split=split)
+                    plain = prob(**kw)
+                    saved = prob(flags=gb.GLA_SAVE_STATES, generation=7, **kw)
+                    nc = (T + 63) // 64
+                    states = 2 * 4 * (nc + 1) * d_k * d_v * es
+                    assert _ws(lib, saved, False) == _ws(lib, saved, True)
+                    assert _ws(lib, saved, False) >= max(_ws(lib, plain, False), _ws(lib, plain, True))
+                    if dtype == torch.bfloat16 and gate == "scalar" and d_k == d_v == 128:
+                        # (where the forward stores them)
+                        assert _ws(lib, saved, True) >= _ws(lib, plain, True) + 256
+                        assert _ws(lib, saved, False) >= 256 + states
+                    else:
+                        assert _ws(lib, saved, True) == _ws(lib, plain, True)
+    assert call_fwd_noalloc(lib, prob(flags=gb.GLA_SAVE_STATES)) == -4
+
+
 def test_split_workspace(lib):
     """The sequence split needs piece summaries and entry states: two fp32
     [B, H, P, d_k, d_v] buffers plus the decay products, in both passes."""

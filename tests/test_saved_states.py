@@ -1,0 +1,174 @@
+"""GLA_SAVE_STATES on the GPU: the forward stores the state entering every chunk
+(the recurrence of the Gated Linear Attention page, "Gated Linear Attention
+Transformers with Hardware-Efficient Training", chunkwise form: the states the
+backward's chunk-parallel gradients read), and the backward given the same
+workspace uses them instead of recomputing them.
+
+The forward stores them for bf16, scalar gate, 128 x 128 problems (the
+backward's state pass runs alone there, before its walk over the chunks); for
+every other problem the flag only sets the workspace size.
+
+Checked here, against the fp64 oracle at the tolerances of test_parity.py:
+the gradients of a forward / backward pair that shares a workspace (documents,
+GQA, forced and automatic splits of either call, one- and 64-token rows, and
+problems of both gates and dtypes whose forward stores nothing); the stored
+states themselves against the oracle's final state of each prefix of the
+sequence; a workspace whose stamp does not match the backward's inputs (other
+tensors, or the same tensors with a new generation after an in-place change)
+recomputed, and the recomputed states then reused bit for bit; the autograd
+wrapper with saved states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ssm_recurrence_amd import binding as gb
+from ssm_recurrence_amd.inputs import small_case
+from tests.test_parity import TOL, check, nan_poison, rel, run_oracle, to_np  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+STAMP_BYTES = 256
+STAMP_TAG = 0x7365746174732D67
+
+
+def run_pair(c, *, split_fwd=0, split_bwd=0, generation=1, ws=None):
+    """fwd then bwd with saved states through one workspace; returns outputs and ws."""
+    if ws is None:  # (the split is part of the problem: one workspace for both splits)
+        ws = max((gb.states_workspace(c.q, c.k, c.v, c.g, gate=c.gate, split=s) for s in (split_fwd, split_bwd)),
+                 key=lambda t: t.numel())
+    o, hT = gb.fwd(c.q, c.k, c.v, c.g, c.h0, c.segment_ids, gate=c.gate, split=split_fwd, ws=ws,
+                   save_states=True, generation=generation)
+    head = ws[:8].cpu().view(torch.int64).item() & ((1 << 64) - 1)  # the stamp's first word
+    dq, dk, dv, dg, dh0 = gb.bwd(c.q, c.k, c.v, c.g, c.dO, c.h0, c.segment_ids, c.dhT, gate=c.gate,
+                                 split=split_bwd, ws=ws, save_states=True, generation=generation)
+    torch.cuda.synchronize()
+    return dict(o=o, hT=hT, dq=dq, dk=dk, dv=dv, dg=dg, dh0=dh0), ws, head
+
+
+def bwd_saved(c, ws, generation, split=0):
+    dq, dk, dv, dg, dh0 = gb.bwd(c.q, c.k, c.v, c.g, c.dO, c.h0, c.segment_ids, c.dhT, gate=c.gate,
+                                 split=split, ws=ws, save_states=True, generation=generation)
+    torch.cuda.synchronize()
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dh0=dh0)
+
+
+def stores_states(d_k, d_v, gate, dtype):
+    """Problems whose forward stores the states (the backward walks the chunks
+    after a state pass of its own; for the others the flag changes nothing)."""
+    return d_k == 128 and d_v == 128 and dtype == torch.bfloat16 and gate == "scalar"
+
+
+CASES = [
+    # (T, d, gate, dtype, H, H_qk, lengths, split_fwd, split_bwd)
+    (300, 128, "scalar", torch.bfloat16, 4, 2, [64, 64, 1, 1, 1, 60, 109], 0, 0),
+    (64 * 12 + 5, 128, "scalar", torch.bfloat16, 2, 2, None, 3, 0),
+    (64 * 12, 128, "scalar", torch.bfloat16, 2, 2, [300, 468], 0, 4),
+    (64 * 12, 128, "scalar", torch.bfloat16, 4, 1, [500, 268], 4, 3),
+    (1, 128, "scalar", torch.bfloat16, 2, 2, None, 0, 0),
+    (64, 128, "scalar", torch.bfloat16, 2, 2, [1, 63], 0, 0),
+    # the flag changes nothing but the workspace size
+    (300, 128, "vector", torch.bfloat16, 2, 2, [100, 28, 172], 0, 0),
+    (300, 128, "scalar", torch.float32, 2, 1, None, 0, 0),
+    (200, 64, "scalar", torch.bfloat16, 2, 2, None, 0, 0),
+    (130, 128, "vector", torch.float32, 2, 2, [60, 70], 0, 0),
+]
+IDS = ["T%d-d%d-%s-%s-H%d-%d-%s-P%d-%d" % (c[0], c[1], c[2], str(c[3])[6:], c[4], c[5],
+                                           "seg" if c[6] else "noseg", c[7], c[8]) for c in CASES]
+
+
+def make(T, d, gate, dtype, H, Hqk, lens, seed=0):
+    return small_case(seed=seed + T + d + H, B=2, T=T, H=H, H_qk=Hqk, d=d, gate=gate, dtype=dtype,
+                      lengths=lens).to("cuda")
+
+
+@pytest.mark.parametrize("T,d,gate,dtype,H,Hqk,lens,pf,pb", CASES, ids=IDS)
+def test_pair_parity(T, d, gate, dtype, H, Hqk, lens, pf, pb):
+    c = make(T, d, gate, dtype, H, Hqk, lens)
+    got, ws, head = run_pair(c, split_fwd=pf, split_bwd=pb)
+    check(c.to("cpu"), got=got)
+    # the forward stamps the workspace where it stores states
+    assert (head == STAMP_TAG) == stores_states(d, d, gate, dtype), hex(head)
+
+
+@pytest.mark.parametrize("T,d,gate,dtype,H,Hqk,lens,pf,pb", [c for c in CASES if stores_states(c[1], c[1], c[2], c[3])],
+                         ids=[i for c, i in zip(CASES, IDS) if stores_states(c[1], c[1], c[2], c[3])])
+def test_stored_states_are_prefix_states(T, d, gate, dtype, H, Hqk, lens, pf, pb):
+    """The state stored for chunk c is the oracle's final state after the first
+    64 c tokens (h0 for c = 0), for sampled chunks including the last one."""
+    c = make(T, d, gate, dtype, H, Hqk, lens)
+    ws = gb.states_workspace(c.q, c.k, c.v, c.g, gate=gate, split=pf)
+    gb.fwd(c.q, c.k, c.v, c.g, c.h0, c.segment_ids, gate=gate, split=pf, ws=ws, save_states=True,
+           generation=5)
+    torch.cuda.synchronize()
+    B, nc = c.q.shape[0], (T + 63) // 64
+    n = B * H * (nc + 1) * d * d
+    S = ws[STAMP_BYTES:STAMP_BYTES + n * c.q.element_size()].view(dtype).view(B, H, nc + 1, d, d)
+    S = to_np(S)
+    cpu = c.to("cpu")
+    h0 = to_np(cpu.h0) if cpu.h0 is not None else np.zeros((B, H, d, d))
+    assert rel(S[:, :, 0], h0) <= TOL[dtype]
+    for ci in sorted({1, nc // 2, nc - 1, nc}):
+        if ci < 1:
+            continue
+        t = min(64 * ci, T)
+        _, hT = oracle.fwd(cpu.q[:, :t], cpu.k[:, :t], cpu.v[:, :t], cpu.g[:, :t], cpu.h0,
+                           None if cpu.segment_ids is None else cpu.segment_ids[:, :t], gate=gate)
+        e = rel(S[:, :, ci], hT)
+        print("chunk", ci, "of", nc, "state rel err %.2e" % e, flush=True)
+        assert e <= TOL[dtype], (ci, e)
+
+
+@pytest.mark.parametrize("dtype,gate", [(torch.bfloat16, "scalar")])
+def test_stale_stamp_recomputes(dtype, gate):
+    """A backward whose inputs differ from the forward's recomputes the states:
+    (a) other tensors, same generation; (b) the same tensors changed in place,
+    with a new generation.  A second backward with the same inputs and generation
+    then finds the states the first one computed: bit-identical gradients."""
+    a = make(256, 128, gate, dtype, 2, 2, [100, 156], seed=1)
+    b = make(256, 128, gate, dtype, 2, 2, [100, 156], seed=2)
+    _, ws, _ = run_pair(a, generation=1)
+    got_b = bwd_saved(b, ws, generation=1)
+    check(b.to("cpu"), got=got_b, ref={n: v for n, v in run_oracle(b.to("cpu")).items() if n in got_b})
+    again = bwd_saved(b, ws, generation=1)
+    for n in got_b:
+        assert torch.equal(got_b[n], again[n]), n
+    # (b): forward on a, then a's v halved in place; a new generation makes the
+    # backward recompute
+    run_pair(a, generation=3, ws=ws)
+    a.v.mul_(0.5)
+    got_a = bwd_saved(a, ws, generation=4)
+    ref = run_oracle(a.to("cpu"))
+    check(a.to("cpu"), got=got_a, ref={n: v for n, v in ref.items() if n in got_a})
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_autograd_with_saved_states(gate):
+    c = make(200, 128, gate, torch.bfloat16, 2, 2, [80, 120], seed=3)
+    outs = {}
+    for saved in (False, True):
+        leaves = [t.detach().clone().requires_grad_(True) for t in (c.q, c.k, c.v, c.g)]
+        h0 = c.h0.detach().clone().requires_grad_(True)
+        o, hT = gb.GLAFunction.apply(*leaves, h0, c.segment_ids, gate, saved)
+        (o.float() * c.dO.float()).sum().add_((hT * c.dhT).sum()).backward()
+        torch.cuda.synchronize()
+        outs[saved] = dict(o=o.detach(), hT=hT.detach(), dq=leaves[0].grad, dk=leaves[1].grad,
+                           dv=leaves[2].grad, dg=leaves[3].grad, dh0=h0.grad)
+    check(c.to("cpu"), got=outs[True])
+    for n in outs[False]:
+        assert rel(to_np(outs[True][n]), to_np(outs[False][n])) <= TOL[torch.bfloat16], n
+
+
+def test_empty_sequence_saved():
+    """T = 0 with the flag: nothing stored, hT = h0 and dh0 = dhT."""
+    B, H, d, dev = 2, 2, 128, "cuda"
+    q = torch.zeros((B, 0, H, d), dtype=torch.bfloat16, device=dev)
+    g = torch.zeros((B, 0, H), dtype=torch.bfloat16, device=dev)
+    h0 = torch.randn((B, H, d, d), device=dev)
+    dhT = torch.randn((B, H, d, d), device=dev)
+    ws = gb.states_workspace(q, q, q, g)
+    o, hT = gb.fwd(q, q, q, g, h0, ws=ws, save_states=True, generation=1)
+    dq, dk, dv, dg, dh0 = gb.bwd(q, q, q, g, q, h0, None, dhT, ws=ws, save_states=True, generation=1)
+    torch.cuda.synchronize()
+    assert torch.equal(hT, h0) and torch.equal(dh0, dhT)
