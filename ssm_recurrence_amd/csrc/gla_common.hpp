@@ -73,6 +73,19 @@ template <> struct Mma<float> {
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// threadIdx.x and the lane index as values the compiler cannot see through:
+// addresses derived from them are formed where they are used, not hoisted out
+// of a loop and held in registers across it
+__device__ __forceinline__ int opaque_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+__device__ __forceinline__ int opaque_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // Block id -> logical id so that consecutive logical ids (the slices of one
@@ -88,8 +101,7 @@ __device__ __forceinline__ int64_t xcd_logical_block(int64_t nblocks) {
 // lane (i = l%16, j = l/16) receives X(i0 + i, k0 + j*KPL + e), e < KPL, where
 // X(i, k) = base[i*SI + k*SK].  Serves A (i = row m) and B (i = column n).
 template <typename T, int SI, int SK>
-__device__ __forceinline__ typename Mma<T>::frag frag_ld(const T* base, int i0, int k0) {
-    const int l = lane_id();
+__device__ __forceinline__ typename Mma<T>::frag frag_ld(const T* base, int i0, int k0, int l = lane_id()) {
     const int i = i0 + (l & 15);
     const int k = k0 + (l >> 4) * Mma<T>::KPL;
     typename Mma<T>::frag f;
@@ -164,8 +176,8 @@ __device__ __forceinline__ v4i16_t lds_read_tr16(const bf16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
 }
 template <typename T, int P, bool CTILE>
-__device__ __forceinline__ typename Mma<T>::frag frag_col(const T* base, int i0, int k0, int sub = 0) {
-    const int l = lane_id();
+__device__ __forceinline__ typename Mma<T>::frag frag_col(const T* base, int i0, int k0, int sub = 0,
+                                                          int l = lane_id()) {
     const int j = l >> 4;
     typename Mma<T>::frag f;
     if constexpr (Mma<T>::KPL == 1) {

@@ -59,13 +59,14 @@ __device__ __forceinline__ SFrag split8(const f32x4& a, const f32x4& b) {
 }
 
 // operand fragments of a split tile (hi plane at base, lo plane PLANE elements later)
+// (l: the lane index, or opaque_lane() inside a loop)
 template <int P, int PLANE>
-__device__ __forceinline__ SFrag sld(const bf16* base, int i0, int k0) {
-    return SFrag{frag_ld<bf16, P, 1>(base, i0, k0), frag_ld<bf16, P, 1>(base + PLANE, i0, k0)};
+__device__ __forceinline__ SFrag sld(const bf16* base, int i0, int k0, int l = lane_id()) {
+    return SFrag{frag_ld<bf16, P, 1>(base, i0, k0, l), frag_ld<bf16, P, 1>(base + PLANE, i0, k0, l)};
 }
 template <int P, int PLANE>
-__device__ __forceinline__ SFrag scol(const bf16* base, int i0, int k0) {
-    return SFrag{frag_col<bf16, P, false>(base, i0, k0), frag_col<bf16, P, false>(base + PLANE, i0, k0)};
+__device__ __forceinline__ SFrag scol(const bf16* base, int i0, int k0, int l = lane_id()) {
+    return SFrag{frag_col<bf16, P, false>(base, i0, k0, 0, l), frag_col<bf16, P, false>(base + PLANE, i0, k0, 0, l)};
 }
 
 // eight consecutive fp32 values from global memory as a split fragment; with
@@ -84,11 +85,12 @@ __device__ __forceinline__ SFrag split_ld8(const float* p, float& dot_with, cons
 
 // fp32 tile rows from registers to a split LDS tile (8-byte stores per plane)
 template <int D, int NTH = NT>
-__device__ __forceinline__ void store_rows_split(const TileRegs<float, D, NTH>& t, bf16* dst, int P, int PLANE) {
+__device__ __forceinline__ void store_rows_split(const TileRegs<float, D, NTH>& t, bf16* dst, int P, int PLANE,
+                                                 int tid = (int)threadIdx.x) {
     using TR = TileRegs<float, D, NTH>;
 #pragma unroll
     for (int i = 0; i < TR::NVEC; ++i) {
-        const int idx = threadIdx.x + i * NTH;
+        const int idx = tid + i * NTH;
         if (idx < TR::NV_TOT) {
             const int row = idx / TR::VPR, cv = (idx % TR::VPR) * 4;
             const f32x4 f = __builtin_bit_cast(f32x4, t.get(i));

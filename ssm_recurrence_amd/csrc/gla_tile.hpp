@@ -28,11 +28,12 @@ struct TileRegs {
     // zero.  Every lane loads (a row past the end reads row 0 instead) and the
     // zeroing is applied where the registers are used (get): a select on loaded
     // registers here would make the compiler wait for every load in flight.
-    __device__ __forceinline__ void load(const T* src, int64_t rs, int nvalid) {
+    // (tid: threadIdx.x, or opaque_tid() in a persistent loop)
+    __device__ __forceinline__ void load(const T* src, int64_t rs, int nvalid, int tid = (int)threadIdx.x) {
         okm = 0;
 #pragma unroll
         for (int i = 0; i < NVEC; ++i) {
-            const int idx = threadIdx.x + i * NTH;
+            const int idx = tid + i * NTH;
             const int row = idx / VPR, cv = (idx % VPR) * VE;
             const bool ok = idx < NV_TOT && row < nvalid;
             r[i] = *reinterpret_cast<const i32x4*>(src + (ok ? (int64_t)row * rs + cv : (int64_t)0));
@@ -156,6 +157,21 @@ __device__ __forceinline__ void docs_from_flags(ChunkDocs* cd, int reset, int nv
     }
 }
 
+// Raw buffer resource over `bytes` bytes from a workgroup-uniform base.  Buffer
+// loads and stores take the per-lane part of the address in one register and a
+// per-element constant in the instruction (or a scalar register), where global
+// accesses at many constant offsets would each hold a 64-bit address.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 buf_ld4(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(f32x4, (u32x4_t)__builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+}
+__device__ __forceinline__ float buf_ld1(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+}
+
 // The 128 x 128 state a workgroup of eight waves holds in accumulators (wave w,
 // lane (i, j): S[16 ct + 4 j + e][16 w + i] in S[ct][e]) stored row-major to dst
 // ([128][128], element type T, dst uniform over the workgroup).  Buffer stores
@@ -166,10 +182,9 @@ template <typename T>
 __device__ __forceinline__ void store_state_128(T* dst, const f32x4 (&S)[8]) {
     constexpr int B = (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(dst, 0, 128 * 128 * B, 0x00020000);
-    // the lane index is read afresh (volatile, so not hoisted out of a caller's
-    // loop, where a precomputed offset would hold a register for the whole loop)
-    int l;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    // the lane index is read afresh (not hoisted out of a caller's loop, where a
+    // precomputed offset would hold a register for the whole loop)
+    const int l = opaque_lane();
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int vo = ((4 * (l >> 4)) * 128 + (l & 15)) * B + 16 * B * w;
 #pragma unroll
