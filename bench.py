@@ -33,15 +33,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PROFILE = {"c2": "gla_kernels_ssd_fp32_B4_T8192_H8_Hqk2_d128.md",
-           "c3": "gla_kernels_gla_bf16_B4_T4096_H16_d128.md",
-           "c4": "gla_kernels_ssd_bf16_packed_B1_T65536_H16_d128.md",
-           "c5a": "gla_kernels_gla_bf16_B1_T16384_H16_d128.md",
-           "c5b": "gla_kernels_gla_bf16_B8_T2048_H16_d128.md",
-           "c3f": "gla_kernels_gla_bf16_fused_B4_T4096_H16_d128.md",
-           "conv": "conv_kernels_bf16_B8_T4096_C2048_K4.md",
-           "norm_gate": "norm_gate_kernels_bf16_B8_T4096_H16_d128.md",
-           "delta": "delta_kernels_bf16_B4_T4096_H8_d128.md"}
+PROFILE = {w: "%s_kernels.md" % w for w in ("c2", "c3", "c4", "c5a", "c5b", "c3f", "conv", "norm_gate", "delta")}
 
 
 def source_hash():

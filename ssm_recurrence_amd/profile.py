@@ -41,6 +41,7 @@ TITLE = {
     "c4": "SSD scalar decay, bf16, packed documents, B=1 T=65536 H=16 d_k=d_v=128, chunk 64, h0",
     "c5a": "GLA vector decay, bf16, B=1 T=16384 H=16 d_k=d_v=128, chunk 64, h0 and dhT",
     "c5b": "GLA vector decay, bf16, B=8 T=2048 H=16 d_k=d_v=128, chunk 64, h0 and dhT",
+    "c3f": "c3 with q, k, v read in place from one [B, T, 3 H d] projection tensor and one fused gradient",
     "conv": "short depthwise causal convolution K=4 + bias + SiLU, bf16, B=8 T=4096 C=2048",
     "norm_gate": "output per-head RMSNorm x swish gate, bf16, B=8 T=4096 H=16 d=128",
     "delta": "gated delta rule (chunked WY/UT), bf16, B=4 T=4096 H=8 d_k=d_v=128, chunk 64",
@@ -70,7 +71,7 @@ def part_of(workload, name):
         if "delta_prep" in name:
             return [fwd, bwd]
         return [bwd]
-    if "k_piece_combine" in name:
+    if "k_piece_combine" in name or "k_write_stamp" in name:
         return [fwd, bwd]
     if "k_fwd" in name:
         return [fwd]
@@ -136,8 +137,9 @@ def mean(xs):
 
 
 def bench_cmd(workload, steps, warmup):
-    return ["python3", "bench.py", "--workload", workload, "--steps", str(steps), "--warmup",
-            str(warmup), "--cold", "0", "--no-cpu-baseline", "--also", "none"]
+    wl = ["--workload", "c3", "--fused"] if workload == "c3f" else ["--workload", workload]
+    return ["python3", "bench.py"] + wl + ["--steps", str(steps), "--warmup", str(warmup), "--cold", "0",
+                                           "--no-cpu-baseline", "--also", "none"]
 
 
 def main():
