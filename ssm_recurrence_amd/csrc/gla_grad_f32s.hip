@@ -218,6 +218,20 @@ __global__ __launch_bounds__(NT8) void k_grad_f32m(const RevArgs a) {
             }
             if (w == 0) rev_chunk_info<float, false>(&ck, hr.rr);
             __syncthreads();
+            // dS1 columns 16 (MNCT w + u) + i (channels 32 kk + 8 j ..) for dv's
+            // inter-chunk term, requested soon after the rows (lines still in L2)
+            float dtr[MNCT][DK / KS][8];
+            {
+                const int lo = opaque_lane();
+#pragma unroll
+                for (int u = 0; u < MNCT; ++u) {
+                    const int vcol = ((8 * (lo >> 4)) * DV + 16 * (MNCT * w + u) + (lo & 15)) * 4;
+#pragma unroll
+                    for (int kk = 0; kk < DK / KS; ++kk)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) dtr[u][kk][e] = buf_ld1(rdS1, vcol, (kk * KS + e) * DV * 4);
+                }
+            }
 
             // dA^T = v dO^T tiles (computed rows s, column r), masked, stored dA[r][s];
             // dk's inter-chunk term (v dS1^T)[c][s] while v is staged, and each of this
@@ -270,7 +284,6 @@ __global__ __launch_bounds__(NT8) void k_grad_f32m(const RevArgs a) {
             __syncthreads();  // dA complete; v no longer read
 
             float xr[4] = {0.f, 0.f, 0.f, 0.f}, bb = 0.f;
-            float dtr[MNCT][DK / KS][8];
             {
                 const int lo = opaque_lane(), i16 = lo & 15, j4 = lo >> 4;
                 // this head's masked A = q k^T tiles ti = w + MNW m (computed [r][s]:
@@ -320,15 +333,6 @@ __global__ __launch_bounds__(NT8) void k_grad_f32m(const RevArgs a) {
                             xr[rt] += (qh.get(e) + ql.get(e)) * dq;
                             dqs[u][rt][e] += dq;
                         }
-                    }
-                    // dS1 columns cw + i (channels 32 kk + 8 j ..) for dv's inter-chunk
-                    // term, requested once S0's fragments are no longer needed
-                    {
-                        const int vcol = ((8 * j4) * DV + cw + i16) * 4;
-#pragma unroll
-                        for (int kk = 0; kk < DK / KS; ++kk)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) dtr[u][kk][e] = buf_ld1(rdS1, vcol, (kk * KS + e) * DV * 4);
                     }
 #pragma unroll
                     for (int st = 0; st < 4; ++st) {
