@@ -244,6 +244,17 @@ def time_gla(name, steps, warmup, cold=0, fused=False, split=0, saved=True):
     return r
 
 
+def states_note(case, saved):
+    """What the backward does for the per-chunk states (GLA_SAVE_STATES stores them
+    only for bf16, scalar gate, 128 x 128; other problems recompute them)."""
+    import torch
+    if not saved:
+        return "recomputed by the backward (separate workspaces)"
+    if case.dtype == torch.bfloat16 and case.gate == "scalar" and case.d_k == 128 and case.d_v == 128:
+        return "stored by the forward for the backward (GLA_SAVE_STATES, one workspace)"
+    return "recomputed by the backward (one workspace; GLA_SAVE_STATES stores none for this problem)"
+
+
 def gla_roofline(case, fwd_us, bwd_us, copy_gbs=None):
     """Roofline of gla_bwd (the dominant call) and of the whole step, against the
     bound that binds the path (bound_time); fp32 paths also report the fraction
@@ -390,8 +401,7 @@ def main():
         "config": {"workload": "%s: %s" % (args.workload, WORKLOADS[args.workload]),
                    "global_batch": B, "seq_len": T, "heads": H, "d_k": dk, "d_v": dv,
                    "chunk": case.chunk, "split": args.split, "parallelism": "single GPU",
-                   "states": ("stored by the forward for the backward" if saved else
-                              "recomputed by the backward"),
+                   "states": states_note(case, saved),
                    "layout": ("q, k, v read from one [B, T, %d] projection tensor; one fused "
                               "gradient" % r["W"]) if args.fused else "packed q, k, v"},
         "roofline": roof,
