@@ -172,3 +172,30 @@ def test_empty_sequence_saved():
     dq, dk, dv, dg, dh0 = gb.bwd(q, q, q, g, q, h0, None, dhT, ws=ws, save_states=True, generation=1)
     torch.cuda.synchronize()
     assert torch.equal(hT, h0) and torch.equal(dh0, dhT)
+
+
+# The full workloads as bench.py times them: one workspace shared by the forward
+# and the backward with GLA_SAVE_STATES, the library's own splits; outputs
+# compared on sampled (batch row, q/k head group) pairs, each against the
+# oracle run on that slice alone.
+FULL = {"c2": [(3, 1)], "c3": [(0, 0)], "c4": [(0, 0), (0, 15)], "c5a": [(0, 7)], "c5b": [(7, 15)]}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_as_benchmarked(name):
+    from ssm_recurrence_amd.inputs import workload
+    from tests.test_parity import sub_outputs, subcase
+    case = workload(name)
+    c = case.to("cuda")
+    print("full-size, shared workspace", name, tuple(case.q.shape), flush=True)
+    got, ws, head = run_pair(c)
+    assert (head == STAMP_TAG) == stores_states(case.d_k, case.d_v, case.gate, case.dtype), hex(head)
+    # a second backward on the same workspace (what every benchmark step after the
+    # first does) gives the same gradients bit for bit
+    again = bwd_saved(c, ws, generation=1)
+    for n in again:
+        assert torch.equal(got[n], again[n]), n
+    del c
+    for b, qh in FULL[name]:
+        sub = subcase(case, b, qh)
+        check(sub, got=sub_outputs(got, case, b, qh))
