@@ -476,16 +476,19 @@ void k_states(const PassArgs a) {
     states_any<T, VEC, DK, DV, MODE, NB>(a, sm, xcd_logical_block(n));
 }
 
-// Two independent passes in one launch (the first half of the grid runs MODE_A,
-// the second MODE_B), so that both directions share the device.
+// Two independent passes in one launch (even logical blocks run MODE_A, odd ones
+// MODE_B), so that both directions share the device.  Interleaving spreads each
+// mode over all eight XCDs (also when one of them exits at once, the forward's
+// stored states found) and puts the two directions of a block on one XCD, whose
+// L2 then serves the gate both read.
 template <typename T, bool VEC, int DK, int DV, int MODE_A, int MODE_B, int NB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(states_waves<T, VEC, NB>())))
 void k_states2(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) StatesLdsFor<T, VEC, NB> sm;
     const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
     const int64_t L = xcd_logical_block(2 * n);
-    if (L < n) states_any<T, VEC, DK, DV, MODE_A, NB>(a, sm, L);
-    else states_any<T, VEC, DK, DV, MODE_B, NB>(a, sm, L - n);
+    if ((L & 1) == 0) states_any<T, VEC, DK, DV, MODE_A, NB>(a, sm, L >> 1);
+    else states_any<T, VEC, DK, DV, MODE_B, NB>(a, sm, L >> 1);
 }
 
 // Scalar gate, 128 x 128 heads: the whole state of a head per 512-thread workgroup.
@@ -499,8 +502,8 @@ __global__ __launch_bounds__(512) void k_states2_w(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) StatesLdsS<T, DV, DK> sm;
     const int64_t n = a.B * a.H * a.P;
     const int64_t L = xcd_logical_block(2 * n);
-    if (L < n) states_body_s<T, DK, DV, MODE_A, DV, DK>(a, sm, L);
-    else states_body_s<T, DK, DV, MODE_B, DV, DK>(a, sm, L - n);
+    if ((L & 1) == 0) states_body_s<T, DK, DV, MODE_A, DV, DK>(a, sm, L >> 1);
+    else states_body_s<T, DK, DV, MODE_B, DV, DK>(a, sm, L >> 1);
 }
 
 // whole-state workgroups when there are enough of them (one per compute unit);

@@ -137,6 +137,13 @@ SPLIT = [
     # bf16 scalar gate, more walking pieces (288) than workgroups (256): some
     # workgroups walk two pieces in turn; heads share q/k
     (1100, 128, 128, "scalar", torch.bfloat16, 16, 8, [500, 600], True, 12),
+    # longer rows in a few pieces: documents crossing pieces, a ragged tail, a
+    # last piece shorter than the others (76 chunks: 4 x 16 + 12)
+    (2048, 128, 128, "scalar", torch.bfloat16, 2, 2, [700, 1348], True, 2),
+    (1950, 128, 128, "vector", torch.bfloat16, 2, 2, [37, 1000, 913], True, 2),
+    (1024, 128, 128, "scalar", torch.bfloat16, 2, 1, [300, 724], False, 2),
+    (4850, 128, 128, "scalar", torch.bfloat16, 2, 2, [2000, 2850], True, 5),
+    (1536, 64, 128, "vector", torch.bfloat16, 4, 2, None, True, 3),
 ]
 
 

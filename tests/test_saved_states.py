@@ -68,6 +68,8 @@ CASES = [
     (64 * 12, 128, "scalar", torch.bfloat16, 4, 1, [500, 268], 4, 3),
     (1, 128, "scalar", torch.bfloat16, 2, 2, None, 0, 0),
     (64, 128, "scalar", torch.bfloat16, 2, 2, [1, 63], 0, 0),
+    # a longer row, split differently by the forward and the backward
+    (64 * 32, 128, "scalar", torch.bfloat16, 2, 2, [900, 1148], 2, 4),
     # the flag changes nothing but the workspace size
     (300, 128, "vector", torch.bfloat16, 2, 2, [100, 28, 172], 0, 0),
     (300, 128, "scalar", torch.float32, 2, 1, None, 0, 0),
