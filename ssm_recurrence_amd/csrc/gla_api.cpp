@@ -319,9 +319,10 @@ hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
     return gla::launch_fwd<T, VEC, DK, DV, 16>(a, st);
 }
 
-// Backward: (split: both summaries in one launch, both combines in one launch)
-// the state and state-gradient passes in one launch, the chunk-parallel
-// gradients, and the sums over heads that share q/k.
+// Backward: (split: both summaries in one launch, or in two where the forward's
+// states may be found; both combines in one launch) the state and state-gradient
+// passes in one launch (the walk: the state pass, then the walk), the gradients,
+// and the sums over heads that share q/k.
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t st) {
     hipError_t e;
@@ -335,7 +336,17 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
     if (pa.P > 1) {
         gla::PassArgs sa = pa;
         sa.d_from_rev = 1;
-        e = gla::launch_states_pair<T, VEC, DK, DV>(sa, true, wide, st);
+        if (pa.check_stamp) {
+            // the forward's states may be in ws, and then its summaries exit at once:
+            // the reverse summaries run in a launch of their own (measured on c4:
+            // 141 us alone against 202 us in a paired launch half of whose
+            // workgroups exit)
+            e = gla::launch_states<T, VEC, DK, DV>(sa, gla::ST_SUM_FWD, wide_blocks(sa, DK, 1, 256), st);
+            if (e != hipSuccess) return e;
+            e = gla::launch_states<T, VEC, DK, DV>(sa, gla::ST_SUM_REV, wide_blocks(sa, DK, 1, 256), st);
+        } else {
+            e = gla::launch_states_pair<T, VEC, DK, DV>(sa, true, wide, st);
+        }
         if (e != hipSuccess) return e;
         e = gla::launch_piece_combine(combine_args(pa, DK, DV, 3), st);
         if (e != hipSuccess) return e;
