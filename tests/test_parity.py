@@ -144,6 +144,9 @@ SPLIT = [
     (1024, 128, 128, "scalar", torch.bfloat16, 2, 1, [300, 724], False, 2),
     (4850, 128, 128, "scalar", torch.bfloat16, 2, 2, [2000, 2850], True, 5),
     (1536, 64, 128, "vector", torch.bfloat16, 4, 2, None, True, 3),
+    # fp32 state passes with a whole head per workgroup (256 workgroups) over
+    # pieces of three chunks, the last one ragged
+    (3062, 128, 128, "scalar", torch.float32, 8, 2, [1000, 2062], True, 16),
 ]
 
 
