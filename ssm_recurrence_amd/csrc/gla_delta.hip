@@ -55,8 +55,10 @@ constexpr int LP = 65;     // LDS pitch of 64 x 64 matrices
 // is loaded by the whole workgroup
 // with the unit-stride index running across lanes, written to LDS, and the
 // next tile's loads are issued before the current tile is used; the products run
-// on the fp32 matrix cores.  M, N <= 128.  `lds` holds MMT_LDS floats.  Contains
-// barriers: every thread of the workgroup calls it.
+// on the fp32 matrix cores.  M, N <= 128 and M N <= 128 x 64: at most four 16 x 16
+// output tiles per wave (fewer accumulators and less unrolled code in each of the
+// kernel's inlined calls).  `lds` holds MMT_LDS floats.  Contains barriers: every
+// thread of the workgroup calls it.
 // LDS serves a wave's 32-bit reads in two halves of 32 lanes over 32 banks.  The
 // A tile's pitch is 2 mod 32 (a fragment's half reads 16 rows x 2 columns), the
 // B tile's 16 mod 32 (16 columns x 2 rows): each half-wave read hits 32 banks.
@@ -107,11 +109,12 @@ __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* 
     // the LDS tiles hold stale values; they only reach outputs that are dropped.
     const int wv = tid >> 6, l = tid & 63;
     const int nti = (M + 15) / 16, ntj = (N + 15) / 16, ntiles = nti * ntj;
-    constexpr int TPW = 128 * 128 / 256 / (DTH / 64);  // tiles per wave at most
+    constexpr int TPW = 128 * 64 / 256 / (DTH / 64);  // tiles per wave at most
     f32x4 acc[TPW];
 #pragma unroll
     for (int q = 0; q < TPW; ++q) acc[q] = zero4();
     fetch(0);
+#pragma unroll 1
     for (int k0 = 0; k0 < K; k0 += KT) {
         __syncthreads();  // the previous tile is no longer read
         stash();
@@ -157,6 +160,7 @@ __device__ __forceinline__ void mmt(int M, int N, int K, float alpha, const TA* 
 // would otherwise keep the next load, through another, from being issued early).
 template <int EB = 8, typename L, typename S>
 __device__ __forceinline__ void ew(int n, L ld, S st) {
+#pragma unroll 1
     for (int base = threadIdx.x; base < n; base += EB * DTH) {
         float v[EB];
 #pragma unroll
@@ -294,12 +298,9 @@ __device__ __forceinline__ void gram_mfma(const T* sK, float* sG) {
 // GE = (K K^T) (.) E strictly below the diagonal (LDS, pitch LP), and
 // T = (I + diag(beta) GE)^-1 by forward substitution (lane j builds column j).
 // sK: the chunk's K rows (load_k), complete before the call.
-template <typename T>
-__device__ __forceinline__ void gram_masked(const Rows& R, const T* sK, int D, float* sGE) {
-    if (D == 128)
-        gram_mfma<T, 128>(sK, sGE);
-    else
-        gram_mfma<T, 64>(sK, sGE);
+template <typename T, int D>
+__device__ __forceinline__ void gram_masked(const Rows& R, const T* sK, float* sGE) {
+    gram_mfma<T, D>(sK, sGE);
     __syncthreads();
     for (int i = threadIdx.x; i < DC * DC; i += DTH) {
         const int t = i / DC, s = i % DC;
@@ -308,9 +309,9 @@ __device__ __forceinline__ void gram_masked(const Rows& R, const T* sK, int D, f
     __syncthreads();
 }
 
-template <typename T>
-__device__ __forceinline__ void wy_inverse(const Rows& R, const T* sK, int D, float* sGE, float* sT) {
-    gram_masked<T>(R, sK, D, sGE);
+template <typename T, int D>
+__device__ __forceinline__ void wy_inverse(const Rows& R, const T* sK, float* sGE, float* sT) {
+    gram_masked<T, D>(R, sK, sGE);
     if (threadIdx.x < DC) {
         // lane j keeps column j of T in registers; row i of GE is read as a
         // broadcast (every lane reads the same address)
@@ -394,7 +395,8 @@ __device__ __forceinline__ void mm_lds(float alpha, const TA* A, const TB* B, fl
 }
 
 // ---------------------------------------------------------------- prepare
-template <typename T>
+// (d_k = DK, d_v = DV fixed per instance: one kernel's code holds one shape)
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     __shared__ Rows R;
     __shared__ float sGE[DC * LP], sT[DC * LP];
@@ -404,7 +406,8 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
     const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
-    const int D = (int)a.dk, Dv = (int)a.dv, KP = kpitch<T>(D);
+    constexpr int D = DK, Dv = DV;
+    const int KP = kpitch<T>(D);
     const int64_t rk = a.H * D, rv = a.H * Dv;
     const T* Q = (const T*)a.q + (b * a.T + t0) * rk + h * D;
     const T* K = (const T*)a.k + (b * a.T + t0) * rk + h * D;
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     load_k<T>(R, K, rk, D, sK);
     load_k<T>(R, Q, rk, D, sQ);  // (the same row loader)
     __syncthreads();
-    wy_inverse<T>(R, sK, D, sGE, sT);
+    wy_inverse<T, DK>(R, sK, sGE, sT);
     ChunkWs w = chunk_ws(a, chunk);
     // T (whole 64 x 64), c
     for (int i = threadIdx.x; i < DC * DC; i += DTH) w.T[i] = sT[(i / DC) * LP + i % DC];
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
     __syncthreads();
     // P = (Q K^T) (.) M in sGE (reused), then copied whole; rows past n are zero
     // in both tiles
-    if (D == 128)
+    if constexpr (DK == 128)
         mm_lds<DC, DC, 128, 128 + kpad<T>(), 1, 128 + kpad<T>(), 1, LP>(1.f, sQ, sK, 0.f, sGE);
     else
         mm_lds<DC, DC, 64, 64 + kpad<T>(), 1, 64 + kpad<T>(), 1, LP>(1.f, sQ, sK, 0.f, sGE);
@@ -449,11 +452,11 @@ __global__ __launch_bounds__(DTH) void k_delta_prep(const DeltaArgs a) {
         sT[t * LP + s] *= R.beta[s];
     }
     __syncthreads();
-    if (Dv == 128)
+    if constexpr (DV == 128)
         mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sT, sV, 0.f, w.U);
     else
         mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sT, sV, 0.f, w.U);
-    if (D == 128)
+    if constexpr (DK == 128)
         mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sGE, sK, 0.f, w.W);
     else
         mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sGE, sK, 0.f, w.W);
@@ -676,7 +679,8 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
 }
 
 // ---------------------------------------------------------------- gradients
-template <typename T>
+// (d_k = DK, d_v = DV fixed per instance: one kernel's code holds one shape)
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __shared__ Rows R;
     __shared__ float sGE[DC * LP], sT[DC * LP];
@@ -689,7 +693,12 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
     const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
-    const int D = (int)a.dk, Dv = (int)a.dv;
+    // The LDS products are chosen per instance (if constexpr on DK); the staged
+    // products and elementwise passes take the sizes as run-time values (held
+    // opaque), as constant sizes let the compiler precompute and hold many more
+    // addresses across the kernel (it then spills).
+    int D = DK, Dv = DV;
+    asm volatile("" : "+s"(D), "+s"(Dv));
     const int64_t rk = a.H * D, rv = a.H * Dv;
     const T* Q = (const T*)a.q + (b * a.T + t0) * rk + h * D;
     const T* K = (const T*)a.k + (b * a.T + t0) * rk + h * D;
@@ -708,7 +717,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     // T as the prepare pass stored it (this call's, or the forward's when the stamp matched)
     ew(DC * DC, [&](int i) { return w.T[i]; }, [&](int i, float v) { sT[(i / DC) * LP + i % DC] = v; });
     __syncthreads();
-    gram_masked<T>(R, sK, D, sGE);
+    gram_masked<T, DK>(R, sK, sGE);
     for (int i = threadIdx.x; i < DC * LP; i += DTH) sX[i] = 0.f;
     __syncthreads();
     // S0, Wv, dS1 and dWv are stored transposed ([value column][row]), so that
@@ -730,6 +739,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     // carry term: c <dS1, S0>
     {
         float s = 0.f;
+#pragma unroll 1
         for (int base = threadIdx.x; base < D * Dv; base += 8 * DTH) {
             float x[8], y[8];
 #pragma unroll
@@ -780,7 +790,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     ew(DC * D, [&](int i) { return w.gQ[i] * R.gam[i / D]; }, [&](int i, float v) { w.gQ[i] = v; });
     ew(DC * D, [&](int i) { return R.kts[i / D] * w.gKt[i]; }, [&](int i, float v) { w.gK[i] = v; });
     __syncthreads();
-    if (D == 128)
+    if constexpr (DK == 128)
         mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gQ);
     else
         mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, w.gQ);
@@ -827,7 +837,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     }
     __syncthreads();
     // dK += (dG + dG^T) K (one lane reads and writes each element in both calls)
-    if (D == 128) {
+    if constexpr (DK == 128) {
         mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gK);
         mm_lds<DC, 128, DC, 1, LP, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gK);
     } else {
@@ -884,12 +894,27 @@ int64_t delta_fwd_floats_per_chunk(int64_t dk, int64_t dv) { return 2 * DC * DC 
 int64_t delta_bwd_floats_per_chunk(int64_t dk, int64_t dv) { return 2 * dk * dv + DC * (3 * dv + 5 * dk); }
 
 
+// the per-chunk kernels' instance for the problem's (d_k, d_v)
+template <typename T> struct k_delta_prep_ptr {
+    template <int DK, int DV> static constexpr auto get() { return &k_delta_prep<T, DK, DV>; }
+};
+template <typename T> struct k_delta_grad_ptr {
+    template <int DK, int DV> static constexpr auto get() { return &k_delta_grad<T, DK, DV>; }
+};
+template <typename K>
+void launch_shape(const DeltaArgs& a, dim3 grid, hipStream_t st) {
+    if (a.dk == 128 && a.dv == 128) hipLaunchKernelGGL((K::template get<128, 128>()), grid, dim3(DTH), 0, st, a);
+    else if (a.dk == 128) hipLaunchKernelGGL((K::template get<128, 64>()), grid, dim3(DTH), 0, st, a);
+    else if (a.dv == 128) hipLaunchKernelGGL((K::template get<64, 128>()), grid, dim3(DTH), 0, st, a);
+    else hipLaunchKernelGGL((K::template get<64, 64>()), grid, dim3(DTH), 0, st, a);
+}
+
 template <typename T>
 hipError_t launch_delta_fwd(const DeltaArgs& a0, hipStream_t st) {
     DeltaArgs a = a0;
     a.check_stamp = 0;
     const int64_t NC = (a.T + DC - 1) / DC;
-    hipLaunchKernelGGL(k_delta_prep<T>, dim3((unsigned)(a.B * a.H * NC)), dim3(DTH), 0, st, a);
+    launch_shape<k_delta_prep_ptr<T>>(a, dim3((unsigned)(a.B * a.H * NC)), st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((e = launch_write_stamp(a.stamp, a.expect, st)) != hipSuccess) return e;
@@ -908,7 +933,7 @@ hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st) {
     // the prepare pass exits at once when the workspace's stamp shows it holds these
     // factors already (check_stamp: the caller allows the reuse); the stamp then
     // records that it does
-    hipLaunchKernelGGL(k_delta_prep<T>, chunks, dim3(DTH), 0, st, a);
+    launch_shape<k_delta_prep_ptr<T>>(a, chunks, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((e = launch_write_stamp(a.stamp, a.expect, st)) != hipSuccess) return e;
@@ -922,7 +947,7 @@ hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st) {
     else
         hipLaunchKernelGGL((k_delta_dstate<T, 64>), slices, dim3(DTH), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_delta_grad<T>, chunks, dim3(DTH), 0, st, a);
+    launch_shape<k_delta_grad_ptr<T>>(a, chunks, st);
     return hipGetLastError();
 }
 
