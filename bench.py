@@ -246,11 +246,10 @@ def time_gla(name, steps, warmup, cold=0, fused=False, split=0, saved=True):
 
 def states_note(case, saved):
     """What the backward does for the per-chunk states (GLA_SAVE_STATES stores them
-    only for bf16, scalar gate, 128 x 128; other problems recompute them)."""
-    import torch
+    only for the scalar gate at 128 x 128; other problems recompute them)."""
     if not saved:
         return "recomputed by the backward (separate workspaces)"
-    if case.dtype == torch.bfloat16 and case.gate == "scalar" and case.d_k == 128 and case.d_v == 128:
+    if case.gate == "scalar" and case.d_k == 128 and case.d_v == 128:
         return "stored by the forward for the backward (GLA_SAVE_STATES, one workspace)"
     return "recomputed by the backward (one workspace; GLA_SAVE_STATES stores none for this problem)"
 

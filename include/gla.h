@@ -142,13 +142,15 @@ typedef struct {
  * the same generation only while the inputs' contents are unchanged (change it
  * whenever they are written in place).  The workspace size is the same for both
  * calls with this flag (gla_workspace_size(p, 0) == gla_workspace_size(p, 1)).
- * The forward stores states for bf16, scalar gate, d_k = d_v = 128: there the
- * backward's state pass runs alone, before a walk over the chunks, and is
- * skipped.  For every other problem the flag only sets the workspace size:
- * there the state pass runs beside the state-gradient pass, so skipping it
- * would gain less than the forward's store of every state costs, and the
- * backward recomputes the states as without the flag.  Results equal the
- * recomputing backward's up to float rounding order. */
+ * The forward stores states for the scalar gate with d_k = d_v = 128, bf16 or
+ * fp32: there the backward's state pass is skipped (bf16: it runs alone before
+ * a walk over the chunks; fp32: the state-gradient pass then runs alone, over
+ * the backward's own split).  For every other problem (the vector gate, other
+ * head sizes) the flag only sets the workspace size: there the state pass runs
+ * beside the state-gradient pass, so skipping it would gain less than the
+ * forward's store of every state costs, and the backward recomputes the states
+ * as without the flag.  Results equal the recomputing backward's up to float
+ * rounding order. */
 #define GLA_SAVE_STATES 1
 
 /* Fused projection.  The FLAT page ("FLAT: Flash Linear Attention on TPUs",

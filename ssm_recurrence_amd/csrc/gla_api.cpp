@@ -79,11 +79,17 @@ bool walk_bwd(const gla_problem* p) {
 }
 
 // The forward stores the per-chunk states for the backward (GLA_SAVE_STATES) on
-// the walking backward's shape, whose state pass runs alone before the walk.
-// Elsewhere the state pass runs beside the state-gradient pass, so dropping it
-// shortens the backward by little while the forward's store costs a full write
+// the walking backward's shape, whose state pass runs alone before the walk, and
+// on the fp32 scalar-gate 128 x 128 shape, whose backward then runs its
+// state-gradient pass alone, split for that pass.  Elsewhere (vector gate) the
+// state pass's share of its paired launch is small next to the forward's store
 // of the states: the flag changes nothing there but the workspace size.
-bool saves_states(const gla_problem* p) { return (p->flags & GLA_SAVE_STATES) && walk_bwd(p); }
+bool f32_scalar_128(const gla_problem* p) {
+    return p->dtype == GLA_F32 && p->gate == GLA_GATE_SCALAR && p->d_k == 128 && p->d_v == 128;
+}
+bool saves_states(const gla_problem* p) {
+    return (p->flags & GLA_SAVE_STATES) && (walk_bwd(p) || f32_scalar_128(p));
+}
 bool flag_save(const gla_problem* p) { return (p->flags & GLA_SAVE_STATES) != 0; }
 
 Split plan_split(const gla_problem* p, int for_backward) {
@@ -97,8 +103,10 @@ Split plan_split(const gla_problem* p, int for_backward) {
         P = p->split;
     } else {
         int64_t per_head, target;  // workgroups per (b, h) without a split
-        if (for_backward && walk_bwd(p)) {
-            per_head = 1;  // one walking workgroup per piece
+        if (for_backward && (walk_bwd(p) || saves_states(p))) {
+            // one walking workgroup per piece; or (fp32 with stored states) one
+            // whole-state workgroup per piece of the state-gradient pass alone
+            per_head = 1;
             if (bh >= kTargetWG) return s;
             target = kTargetWG;
         } else if (for_backward) {
@@ -356,8 +364,17 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
         if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
         e = gla::launch_grad8_walk(ra, st);
     } else {
-        e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
-        if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
+        if (pa.check_stamp) {
+            // the forward's states may be in ws: the state pass exits at once and the
+            // state-gradient pass runs in a launch of its own
+            e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, wide_blocks(pa, DK, 1, 256), st);
+            if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
+            e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_DSTATES, wide_blocks(pa, DK, 1, 256), st);
+        } else {
+            e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
+            if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
+        }
+        if (e != hipSuccess) return e;
         e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
     }
     if (e != hipSuccess) return e;

@@ -136,6 +136,9 @@ __global__ __launch_bounds__(512) void k_fwd_f32h(const PassArgs a) {
                              sVu + PLH + row * PH + cv);
             }
         }
+        // (for the backward) the state entering this chunk, stored while the staged
+        // tiles' registers are free and before the next chunk's loads are issued
+        if (a.save_S) store_state_128<float>((float*)a.save_S + (bh * (NC + 1) + it) * DK * DV, S);
         if (it + 1 < cend) prefetch(t0 + C);
         __syncthreads();
 
@@ -234,6 +237,7 @@ __global__ __launch_bounds__(512) void k_fwd_f32h(const PassArgs a) {
         __syncthreads();
     }
 
+    if (a.save_S && piece == P - 1) store_state_128<float>((float*)a.save_S + (bh * (NC + 1) + NC) * DK * DV, S);
     if (a.hT && piece == P - 1) {
 #pragma unroll
         for (int ct = 0; ct < DK / 16; ++ct) {

@@ -303,8 +303,8 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
     if constexpr (MODE == ST_SUM_FWD) if (piece == P - 1) return;
     if constexpr (MODE == ST_SUM_REV) if (piece == 0) return;
     // the forward's states are in the workspace: nothing to recompute (the
-    // forward stores them for bf16 128 x 128 problems only)
-    if constexpr (sizeof(T) == 2 && DK == 128 && DV == 128 && (MODE == ST_STATES || MODE == ST_SUM_FWD))
+    // forward stores them for 128 x 128 problems with the scalar gate only)
+    if constexpr (DK == 128 && DV == 128 && (MODE == ST_STATES || MODE == ST_SUM_FWD))
         if (a.check_stamp && stamp_matches(a.stamp, a.expect)) return;
 
     const T* k = (const T*)(REV ? a.q : a.k);

@@ -110,7 +110,7 @@ def _ws(lib, p, backward):
 def test_saved_states_flags_and_workspace(lib):
     """GLA_SAVE_STATES: other flag bits and a non-zero reserved word are refused;
     with the flag one workspace size serves both calls; where the forward stores
-    states (bf16, scalar gate, 128 x 128) it holds the stamp (256 bytes) and the
+    states (scalar gate, 128 x 128) it holds the stamp (256 bytes) and the
     state entering every chunk plus the final one, in the input dtype, besides
     everything the backward alone needs; elsewhere it is the backward's own."""
     for kw in (dict(flags=2), dict(flags=gb.GLA_SAVE_STATES | 4)):
@@ -132,7 +132,7 @@ def test_saved_states_flags_and_workspace(lib):
                     states = 2 * 4 * (nc + 1) * d_k * d_v * es
                     assert _ws(lib, saved, False) == _ws(lib, saved, True)
                     assert _ws(lib, saved, False) >= max(_ws(lib, plain, False), _ws(lib, plain, True))
-                    if dtype == torch.bfloat16 and gate == "scalar" and d_k == d_v == 128:
+                    if gate == "scalar" and d_k == d_v == 128:
                         # (where the forward stores them)
                         assert _ws(lib, saved, True) >= _ws(lib, plain, True) + 256
                         assert _ws(lib, saved, False) >= 256 + states

@@ -117,6 +117,6 @@ def test_committed_summaries_name_the_current_sources_or_none():
 def test_states_note():
     c4 = case(1, 65536, 16, 16, 128, "scalar", torch.bfloat16, dhT=False, seg=True)
     assert "stored by the forward" in bench.states_note(c4, True)
-    assert "stores none" in bench.states_note(C2, True)
+    assert "stored by the forward" in bench.states_note(C2, True)
     assert "stores none" in bench.states_note(C3, True)
     assert "recomputed" in bench.states_note(c4, False)

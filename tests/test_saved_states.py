@@ -4,9 +4,10 @@ Transformers with Hardware-Efficient Training", chunkwise form: the states the
 backward's chunk-parallel gradients read), and the backward given the same
 workspace uses them instead of recomputing them.
 
-The forward stores them for bf16, scalar gate, 128 x 128 problems (the
-backward's state pass runs alone there, before its walk over the chunks); for
-every other problem the flag only sets the workspace size.
+The forward stores them for scalar-gate 128 x 128 problems (bf16: the
+backward's state pass runs alone there, before its walk over the chunks;
+fp32: the backward then runs its state-gradient pass alone); for every other
+problem the flag only sets the workspace size.
 
 Checked here, against the fp64 oracle at the tolerances of test_parity.py:
 the gradients of a forward / backward pair that shares a workspace (documents,
@@ -55,9 +56,10 @@ def bwd_saved(c, ws, generation, split=0):
 
 
 def stores_states(d_k, d_v, gate, dtype):
-    """Problems whose forward stores the states (the backward walks the chunks
-    after a state pass of its own; for the others the flag changes nothing)."""
-    return d_k == 128 and d_v == 128 and dtype == torch.bfloat16 and gate == "scalar"
+    """Problems whose forward stores the states: scalar gate, 128 x 128 (bf16: the
+    backward walks the chunks after a state pass of its own; fp32: the backward
+    runs its state-gradient pass alone); for the others the flag changes nothing."""
+    return d_k == 128 and d_v == 128 and gate == "scalar"
 
 
 CASES = [
@@ -70,9 +72,12 @@ CASES = [
     (64, 128, "scalar", torch.bfloat16, 2, 2, [1, 63], 0, 0),
     # a longer row, split differently by the forward and the backward
     (64 * 32, 128, "scalar", torch.bfloat16, 2, 2, [900, 1148], 2, 4),
+    # fp32: the forward stores the states too, and the backward's split is its own
+    (300, 128, "scalar", torch.float32, 2, 1, None, 0, 0),
+    (64 * 20 + 7, 128, "scalar", torch.float32, 2, 2, [600, 687], 0, 0),
+    (64 * 12, 128, "scalar", torch.float32, 4, 1, [500, 268], 4, 3),
     # the flag changes nothing but the workspace size
     (300, 128, "vector", torch.bfloat16, 2, 2, [100, 28, 172], 0, 0),
-    (300, 128, "scalar", torch.float32, 2, 1, None, 0, 0),
     (200, 64, "scalar", torch.bfloat16, 2, 2, None, 0, 0),
     (130, 128, "vector", torch.float32, 2, 2, [60, 70], 0, 0),
 ]
@@ -122,14 +127,17 @@ def test_stored_states_are_prefix_states(T, d, gate, dtype, H, Hqk, lens, pf, pb
         assert e <= TOL[dtype], (ci, e)
 
 
-@pytest.mark.parametrize("dtype,gate", [(torch.bfloat16, "scalar")])
-def test_stale_stamp_recomputes(dtype, gate):
+@pytest.mark.parametrize("dtype,gate,T", [(torch.bfloat16, "scalar", 256), (torch.float32, "scalar", 256),
+                                          (torch.float32, "scalar", 64 * 24 + 5)])
+def test_stale_stamp_recomputes(dtype, gate, T):
     """A backward whose inputs differ from the forward's recomputes the states:
     (a) other tensors, same generation; (b) the same tensors changed in place,
     with a new generation.  A second backward with the same inputs and generation
-    then finds the states the first one computed: bit-identical gradients."""
-    a = make(256, 128, gate, dtype, 2, 2, [100, 156], seed=1)
-    b = make(256, 128, gate, dtype, 2, 2, [100, 156], seed=2)
+    then finds the states the first one computed: bit-identical gradients.  (The
+    longer fp32 row is split by the backward: its forward summaries recompute too.)"""
+    lens = [100, T - 100]
+    a = make(T, 128, gate, dtype, 2, 2, lens, seed=1)
+    b = make(T, 128, gate, dtype, 2, 2, lens, seed=2)
     _, ws, _ = run_pair(a, generation=1)
     got_b = bwd_saved(b, ws, generation=1)
     check(b.to("cpu"), got=got_b, ref={n: v for n, v in run_oracle(b.to("cpu")).items() if n in got_b})
@@ -145,9 +153,10 @@ def test_stale_stamp_recomputes(dtype, gate):
     check(a.to("cpu"), got=got_a, ref={n: v for n, v in ref.items() if n in got_a})
 
 
-@pytest.mark.parametrize("gate", ["scalar", "vector"])
-def test_autograd_with_saved_states(gate):
-    c = make(200, 128, gate, torch.bfloat16, 2, 2, [80, 120], seed=3)
+@pytest.mark.parametrize("gate,dtype", [("scalar", torch.bfloat16), ("vector", torch.bfloat16),
+                                        ("scalar", torch.float32)])
+def test_autograd_with_saved_states(gate, dtype):
+    c = make(200, 128, gate, dtype, 2, 2, [80, 120], seed=3)
     outs = {}
     for saved in (False, True):
         leaves = [t.detach().clone().requires_grad_(True) for t in (c.q, c.k, c.v, c.g)]
@@ -159,7 +168,7 @@ def test_autograd_with_saved_states(gate):
                            dv=leaves[2].grad, dg=leaves[3].grad, dh0=h0.grad)
     check(c.to("cpu"), got=outs[True])
     for n in outs[False]:
-        assert rel(to_np(outs[True][n]), to_np(outs[False][n])) <= TOL[torch.bfloat16], n
+        assert rel(to_np(outs[True][n]), to_np(outs[False][n])) <= TOL[dtype], n
 
 
 def test_empty_sequence_saved():
