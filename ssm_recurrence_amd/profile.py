@@ -114,12 +114,27 @@ def kernel_stats(d):
 
 
 def counters(d):
-    """{kernel: {counter: [value per dispatch]}} from a --pmc run."""
-    out = {}
+    """{kernel: {counter: [value per dispatch, in dispatch order]}} from a --pmc run."""
+    rows = []
     with open(find_csv(d, "counter_collection.csv")) as f:
         for row in csv.DictReader(f):
-            k = row["Kernel_Name"]
-            out.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+            rows.append((int(row["Dispatch_Id"]), row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])))
+    out = {}
+    for _, k, c, v in sorted(rows, key=lambda r: r[0]):
+        out.setdefault(k, {}).setdefault(c, []).append(v)
+    return out
+
+
+def dispatch_ns(d):
+    """{kernel: [duration in ns per dispatch, in dispatch order]} from a --kernel-trace run."""
+    rows = []
+    with open(find_csv(d, "kernel_trace.csv")) as f:
+        for row in csv.DictReader(f):
+            rows.append((int(row["Start_Timestamp"]), row["Kernel_Name"],
+                         int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
+    out = {}
+    for _, k, ns in sorted(rows):
+        out.setdefault(k, []).append(ns)
     return out
 
 
@@ -149,6 +164,8 @@ def main():
     ap.add_argument("--md", default=None, help="summary file (default profiles/<workload>_kernels.md)")
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--summarize-only", action="store_true",
+                    help="write the summary from the raw output already in --out (no profiler runs)")
     a = ap.parse_args()
     w = a.workload
     out = a.out or os.path.join(ROOT, "gpurun_out", "prof_" + w)
@@ -166,10 +183,12 @@ def main():
         ("copy_write", rp + [os.path.join(out, "copy_write"), "--pmc", "WRITE_SIZE", "--", "python3", "-m",
                              "ssm_recurrence_amd.calib"]),
     ]
-    for tag, cmd in passes:
-        run(cmd, os.path.join(out, tag + ".log"))
+    if not a.summarize_only:
+        for tag, cmd in passes:
+            run(cmd, os.path.join(out, tag + ".log"))
 
     stats = kernel_stats(os.path.join(out, "trace"))
+    per_dispatch = dispatch_ns(os.path.join(out, "trace"))
     simds, xcds = gpu_agent(os.path.join(out, "fetch"))
     cf, cw = counters(os.path.join(out, "fetch")), counters(os.path.join(out, "write"))
     # the copy: the largest torch copy dispatch reads and writes the calibration size
@@ -185,6 +204,7 @@ def main():
 
     rows, per_call = [], {}
     total = sum(ns * n for name, (n, ns) in stats.items() if part_of(w, name))
+    fwd_key, bwd_key = CALLS.get(w, ("gla_fwd", "gla_bwd"))
     for name, (calls, ns) in sorted(stats.items(), key=lambda x: -x[1][0] * x[1][1]):
         parts = part_of(w, name)
         if not parts:
@@ -195,8 +215,19 @@ def main():
         busy, act = mean(c1.get("SQ_VALU_MFMA_BUSY_CYCLES", [])), mean(c1.get("GRBM_GUI_ACTIVE", []))
         mfma = busy / (act / xcds * simds) if act > 0 else float("nan")
         gbs = (rd + wr) / (ns * 1e-9) / 1e9 if ns > 0 else float("nan")
-        rows.append((name, calls, ns / 1000.0, " + ".join(parts), rd / 1e6, wr / 1e6, gbs, mfma,
-                     ns * calls / total))
+        # A forward-summary pass launched twice per step: by the forward, and by a
+        # backward that finds the forward's stored states (that launch exits at
+        # once).  Its dispatches alternate forward, backward in every run.
+        both = parts == [fwd_key] and calls == 2 * launches
+        rows.append((name, calls, ns / 1000.0, (fwd_key + " + " + bwd_key) if both else " + ".join(parts),
+                     rd / 1e6, wr / 1e6, gbs, mfma, ns * calls / total))
+        if both:
+            dur = per_dispatch.get(name, [])
+            for k, key in enumerate((fwd_key, bwd_key)):
+                d = per_call.setdefault(key, [0.0, 0.0])
+                d[0] += mean(dur[k::2]) / 1000.0
+                d[1] += (mean(c1.get("FETCH_SIZE", [])[k::2]) * kf + mean(c2.get("WRITE_SIZE", [])[k::2]) * kw) * 1024.0
+            continue
         # per step, each of the calls that launch it gets an equal part of its launches
         per = calls / launches / len(parts)
         for p in parts:
@@ -227,7 +258,8 @@ def main():
                      % (name, calls, us, part, rd, wr, gbs, 100 * mfma, 100 * sh))
     lines.append("")
     lines.append("Per call and step (%d steps profiled; the sum over the kernels a call launches, a kernel "
-                 "launched by both calls counted half to each):" % launches)
+                 "launched by both calls counted half to each, except a forward-summary pass that both "
+                 "launch, whose dispatches alternate between the two calls):" % launches)
     lines.append("")
     for key in sorted(per_call):
         us, nb = per_call[key]
@@ -237,7 +269,6 @@ def main():
                  "busy cycles over the cycles the GPU was active (GRBM_GUI_ACTIVE / %d XCDs) times %d SIMDs.)"
                  % (xcds, simds))
     lines.append("")
-    bwd_key = CALLS.get(w, ("gla_fwd", "gla_bwd"))[1]
     if bwd_key in per_call:
         lines.append("traffic_bytes_per_%s: %.0f" % (bwd_key, per_call[bwd_key][1]))
     lines.append("source_hash: %s" % source_hash())
