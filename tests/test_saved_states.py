@@ -171,11 +171,12 @@ def test_autograd_with_saved_states(gate, dtype):
         assert rel(to_np(outs[True][n]), to_np(outs[False][n])) <= TOL[dtype], n
 
 
-def test_empty_sequence_saved():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_empty_sequence_saved(dtype):
     """T = 0 with the flag: nothing stored, hT = h0 and dh0 = dhT."""
     B, H, d, dev = 2, 2, 128, "cuda"
-    q = torch.zeros((B, 0, H, d), dtype=torch.bfloat16, device=dev)
-    g = torch.zeros((B, 0, H), dtype=torch.bfloat16, device=dev)
+    q = torch.zeros((B, 0, H, d), dtype=dtype, device=dev)
+    g = torch.zeros((B, 0, H), dtype=dtype, device=dev)
     h0 = torch.randn((B, H, d, d), device=dev)
     dhT = torch.randn((B, H, d, d), device=dev)
     ws = gb.states_workspace(q, q, q, g)
