@@ -66,10 +66,13 @@ def part_of(workload, name):
         return []
     fwd, bwd = CALLS.get(workload, ("gla_fwd", "gla_bwd"))
     if workload in CALLS:
-        if "fwd" in name:
-            return [fwd]
-        if "delta_prep" in name:
+        if "k_write_stamp" in name:
             return [fwd, bwd]
+        # (the delta rule's prepare pass is launched by both calls, the backward's
+        # launch exiting when the forward's factors are found: split per dispatch
+        # below; its forward state pass is k_delta_state<T, false, D>, "Lb0E" mangled)
+        if "fwd" in name or "delta_prep" in name or ("k_delta_state" in name and "Lb0E" in name):
+            return [fwd]
         return [bwd]
     if "k_piece_combine" in name or "k_write_stamp" in name:
         return [fwd, bwd]
@@ -215,9 +218,10 @@ def main():
         busy, act = mean(c1.get("SQ_VALU_MFMA_BUSY_CYCLES", [])), mean(c1.get("GRBM_GUI_ACTIVE", []))
         mfma = busy / (act / xcds * simds) if act > 0 else float("nan")
         gbs = (rd + wr) / (ns * 1e-9) / 1e9 if ns > 0 else float("nan")
-        # A forward-summary pass launched twice per step: by the forward, and by a
-        # backward that finds the forward's stored states (that launch exits at
-        # once).  Its dispatches alternate forward, backward in every run.
+        # A forward pass launched twice per step: by the forward, and by a backward
+        # that finds what the forward stored (that launch exits at once): the
+        # forward summaries, the delta rule's prepare pass.  Its dispatches
+        # alternate forward, backward in every run.
         both = parts == [fwd_key] and calls == 2 * launches
         rows.append((name, calls, ns / 1000.0, (fwd_key + " + " + bwd_key) if both else " + ".join(parts),
                      rd / 1e6, wr / 1e6, gbs, mfma, ns * calls / total))
@@ -258,8 +262,9 @@ def main():
                      % (name, calls, us, part, rd, wr, gbs, 100 * mfma, 100 * sh))
     lines.append("")
     lines.append("Per call and step (%d steps profiled; the sum over the kernels a call launches, a kernel "
-                 "launched by both calls counted half to each, except a forward-summary pass that both "
-                 "launch, whose dispatches alternate between the two calls):" % launches)
+                 "launched by both calls counted half to each, except a forward pass that the backward "
+                 "launches too (exiting at once on what the forward stored), whose dispatches alternate "
+                 "between the two calls):" % launches)
     lines.append("")
     for key in sorted(per_call):
         us, nb = per_call[key]
