@@ -655,9 +655,10 @@ def delta_main(args):
     c = case_cpu.to(dev)
     B, T, H, dk = c.q.shape
     dv = c.v.shape[3]
-    prob = gb.delta_problem(c.q, c.v, 0, 1)
-    # the backward may reuse the forward's factors (same inputs, same generation)
-    prob_b = gb.delta_problem(c.q, c.v, gb.GLA_DELTA_WS_FROM_FWD, 1)
+    # the backward may reuse what the forward left in ws: its per-chunk factors and
+    # states (same inputs, same generation; the flag on both calls)
+    prob = gb.delta_problem(c.q, c.v, gb.GLA_DELTA_WS_FROM_FWD, 1)
+    prob_b = prob
     o = torch.empty_like(c.v)
     hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     dq, dk_, dv_, dg, db = (torch.empty_like(c.q), torch.empty_like(c.k), torch.empty_like(c.v),

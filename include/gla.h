@@ -292,10 +292,12 @@ int gla_conv_bwd(const gla_conv_problem* p, const void* x, const float* w, const
  * Workspaces.  ws (both calls): gla_delta_workspace_size(p, 0) bytes, the
  * per-chunk factors the chunked form builds from the inputs (the inverse T, U,
  * W, the masked scores, gamma Q, the decayed keys and the chunk carries, fp32)
- * behind a small header.  scratch (the backward only):
+ * behind a small header; with GLA_DELTA_WS_FROM_FWD also the state entering
+ * each chunk and its effective writes.  scratch (the backward only):
  * gla_delta_workspace_size(p, 1) bytes, the backward's own per-chunk
- * intermediates (the states and state gradients at the chunk boundaries and
- * the gradient blocks); nothing of it outlives the call. */
+ * intermediates (the state gradients at the chunk boundaries, the gradient
+ * blocks, and without the flag the states); nothing of it outlives the call.
+ * Both sizes depend on the flag. */
 typedef struct {
     int64_t B, T, H, d_k, d_v;
     int32_t dtype;    /* gla_dtype */
@@ -303,16 +305,18 @@ typedef struct {
     int64_t generation; /* the caller's count of changes to the inputs' contents; see below */
 } gla_delta_problem;
 
-/* gla_delta_bwd only (gla_delta_fwd ignores it): ws may hold the factors a
- * gla_delta_fwd computed for these inputs; reuse them instead of recomputing.
- * Every ws carries a stamp of what its factors were computed from: the problem's
- * sizes and dtype, the q, k, v, g, beta and segment_ids pointers and
- * p->generation (gla_delta_fwd writes it; a backward that recomputes the factors
- * rewrites it).  The backward's prepare pass compares the stamp with its own
- * call's on the device and recomputes unless they are equal, so a ws from another
- * problem, other inputs or another layer is never used.  The caller's part: give
- * gla_delta_fwd and gla_delta_bwd the same generation only while the inputs'
- * contents are unchanged (change it whenever they are written in place). */
+/* Given to both calls of a forward / backward pair that share ws: gla_delta_fwd
+ * also stores in ws the state entering every chunk and the chunk's effective
+ * writes, and gla_delta_bwd reuses them and the per-chunk factors instead of
+ * recomputing them.  Every ws carries a stamp of what it holds: the problem's
+ * sizes, dtype and flags, the q, k, v, g, beta and segment_ids pointers and
+ * p->generation (gla_delta_fwd writes it after its last pass; a backward that
+ * recomputes rewrites it).  The backward's prepare and state passes compare the
+ * stamp with their own call's on the device and recompute unless they are equal,
+ * so a ws from another problem, other inputs, another layer or a forward without
+ * the flag is never used.  The caller's part: give gla_delta_fwd and
+ * gla_delta_bwd the same generation only while the inputs' contents are
+ * unchanged (change it whenever they are written in place). */
 #define GLA_DELTA_WS_FROM_FWD 1
 
 /* Bytes of ws (for_backward == 0) or of the backward's scratch (for_backward != 0). */
@@ -323,8 +327,8 @@ int gla_delta_fwd(const gla_delta_problem* p, const void* q, const void* k, cons
                   const void* g, const void* beta, const float* h0, const int32_t* segment_ids,
                   void* o, float* hT, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward: dq, dk, dv, dg, dbeta (and dh0 if non-NULL).  Recomputes the states
- * entering the chunks, and the per-chunk factors unless p->flags has
+/* Backward: dq, dk, dv, dg, dbeta (and dh0 if non-NULL).  Recomputes the
+ * per-chunk factors and the states entering the chunks unless p->flags has
  * GLA_DELTA_WS_FROM_FWD and ws's stamp matches (above). */
 int gla_delta_bwd(const gla_delta_problem* p, const void* q, const void* k, const void* v,
                   const void* g, const void* beta, const float* h0, const int32_t* segment_ids,

@@ -564,14 +564,18 @@ def _buffer(n, device, buf=None):
     return buf
 
 
-def delta_fwd(q, k, v, g, beta, h0=None, segment_ids=None, *, want_hT=True, ws=None, generation=0):
+def delta_fwd(q, k, v, g, beta, h0=None, segment_ids=None, *, want_hT=True, ws=None, ws_from_fwd=False,
+              generation=0):
     """o [B,T,H,d_v] (input dtype) and hT [B,H,d_k,d_v] fp32 (None if not wanted).
     ws (allocated here when None or too small) receives the per-chunk factors,
-    stamped with these inputs and `generation`."""
+    stamped with these inputs and `generation`; with ws_from_fwd
+    (GLA_DELTA_WS_FROM_FWD, for a delta_bwd(..., ws_from_fwd=True) given this ws)
+    also the states entering the chunks, which that backward then need not
+    recompute."""
     _delta_checks(q, k, v, g, beta)
     _check(h0, "h0", torch.float32)
     _check(segment_ids, "segment_ids", torch.int32)
-    prob = delta_problem(q, v, 0, generation)
+    prob = delta_problem(q, v, GLA_DELTA_WS_FROM_FWD if ws_from_fwd else 0, generation)
     B, T, H, d_k = q.shape
     o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
     hT = torch.empty((B, H, d_k, v.shape[3]), dtype=torch.float32, device=q.device) if want_hT else None
@@ -586,10 +590,10 @@ def delta_fwd(q, k, v, g, beta, h0=None, segment_ids=None, *, want_hT=True, ws=N
 def delta_bwd(q, k, v, g, beta, dO, h0=None, segment_ids=None, dhT=None, *, want_dh0=True, ws=None,
               ws_from_fwd=False, generation=0, scratch=None):
     """dq, dk, dv, dg, dbeta (input dtype) and dh0 fp32 (or None).  ws_from_fwd: ws may
-    hold the factors delta_fwd computed for these inputs and `generation`; the library
-    reuses them only when the workspace's stamp says so, and recomputes otherwise
-    (GLA_DELTA_WS_FROM_FWD).  scratch: the backward's own workspace (allocated here
-    when None or too small)."""
+    hold the factors and states a delta_fwd(..., ws_from_fwd=True) computed for these
+    inputs and `generation`; the library reuses them only when the workspace's stamp
+    says so, and recomputes otherwise (GLA_DELTA_WS_FROM_FWD).  scratch: the
+    backward's own workspace (allocated here when None or too small)."""
     _delta_checks(q, k, v, g, beta)
     _check(dO, "dO", q.dtype)
     _check(h0, "h0", torch.float32)
@@ -617,7 +621,7 @@ _delta_generation = [0]
 
 class DeltaFunction(torch.autograd.Function):
     """Autograd wrapper of the gated delta rule: both passes run the HIP library.
-    The forward's workspace (its per-chunk factors) is kept for the backward,
+    The forward's workspace (its per-chunk factors and states) is kept for the backward,
     stamped with a generation of its own (autograd itself rejects inputs changed
     in place in between); the backward's scratch is allocated in the backward."""
 
@@ -625,8 +629,8 @@ class DeltaFunction(torch.autograd.Function):
     def forward(ctx, q, k, v, g, beta, h0, segment_ids):
         _delta_generation[0] += 1
         gen = _delta_generation[0]
-        ws = _buffer(delta_workspace_size(delta_problem(q, v)), q.device)
-        o, hT = delta_fwd(q, k, v, g, beta, h0, segment_ids, ws=ws, generation=gen)
+        ws = _buffer(delta_workspace_size(delta_problem(q, v, GLA_DELTA_WS_FROM_FWD)), q.device)
+        o, hT = delta_fwd(q, k, v, g, beta, h0, segment_ids, ws=ws, ws_from_fwd=True, generation=gen)
         ctx.save_for_backward(q, k, v, g, beta, h0, segment_ids)
         ctx.ws, ctx.gen = ws, gen
         return o, hT

@@ -454,14 +454,19 @@ int check_delta(const gla_delta_problem* p) {
 
 // ws: the stamp, then the forward's per-chunk factors; scratch: the backward's
 // per-chunk intermediates
+// (with GLA_DELTA_WS_FROM_FWD the states entering the chunks and the effective
+// writes move from the scratch to ws, where the forward stores them)
+bool delta_states_in_ws(const gla_delta_problem* p) { return (p->flags & GLA_DELTA_WS_FROM_FWD) != 0; }
 size_t delta_ws_bytes(const gla_delta_problem* p) {
     const int64_t nc = (p->T + 63) / 64;
     return (size_t)gla::kDeltaHeaderBytes +
-           (size_t)(p->B * p->H * nc) * (size_t)gla::delta_fwd_floats_per_chunk(p->d_k, p->d_v) * sizeof(float);
+           (size_t)(p->B * p->H * nc) *
+               (size_t)gla::delta_fwd_floats_per_chunk(p->d_k, p->d_v, delta_states_in_ws(p)) * sizeof(float);
 }
 size_t delta_scratch_bytes(const gla_delta_problem* p) {
     const int64_t nc = (p->T + 63) / 64;
-    return (size_t)(p->B * p->H * nc) * (size_t)gla::delta_bwd_floats_per_chunk(p->d_k, p->d_v) * sizeof(float);
+    return (size_t)(p->B * p->H * nc) *
+           (size_t)gla::delta_bwd_floats_per_chunk(p->d_k, p->d_v, delta_states_in_ws(p)) * sizeof(float);
 }
 
 gla::DeltaArgs delta_args(const gla_delta_problem* p, const void* q, const void* k, const void* v,
@@ -472,13 +477,15 @@ gla::DeltaArgs delta_args(const gla_delta_problem* p, const void* q, const void*
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.seg = seg;
     a.stamp = (uint64_t*)ws;
     a.ws = (float*)((char*)ws + gla::kDeltaHeaderBytes);
-    a.ws_chunk = gla::delta_fwd_floats_per_chunk(p->d_k, p->d_v);
-    // what the per-chunk factors in ws are computed from
+    a.states_in_ws = delta_states_in_ws(p);
+    a.ws_chunk = gla::delta_fwd_floats_per_chunk(p->d_k, p->d_v, a.states_in_ws);
+    // what the per-chunk factors (and states) in ws are computed from; the flags
+    // word keeps a forward that stored no states from vouching for them
     const uint64_t words[] = {0x61746c65642d6177ull /* tag */, (uint64_t)p->B, (uint64_t)p->T,
                               (uint64_t)p->H, (uint64_t)p->d_k, (uint64_t)p->d_v, (uint64_t)p->dtype,
                               (uint64_t)(uintptr_t)q, (uint64_t)(uintptr_t)k, (uint64_t)(uintptr_t)v,
                               (uint64_t)(uintptr_t)g, (uint64_t)(uintptr_t)beta, (uint64_t)(uintptr_t)seg,
-                              (uint64_t)p->generation, 0, 0};
+                              (uint64_t)p->generation, (uint64_t)(uint32_t)p->flags, 0};
     static_assert(sizeof words / sizeof words[0] == gla::kStampWords, "stamp words");
     for (int i = 0; i < gla::kStampWords; ++i) a.expect.w[i] = words[i];
     return a;
@@ -776,7 +783,7 @@ int gla_delta_bwd(const gla_delta_problem* p, const void* q, const void* k, cons
     a.h0 = h0; a.dO = dO;
     a.dhT = dhT; a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
     a.ws2 = (float*)scratch;
-    a.ws2_chunk = gla::delta_bwd_floats_per_chunk(p->d_k, p->d_v);
+    a.ws2_chunk = gla::delta_bwd_floats_per_chunk(p->d_k, p->d_v, a.states_in_ws);
     a.check_stamp = (p->flags & GLA_DELTA_WS_FROM_FWD) != 0;
     const hipError_t e = p->dtype == GLA_BF16 ? gla::launch_delta_bwd<gla::bf16>(a, st)
                                               : gla::launch_delta_bwd<float>(a, st);

@@ -346,10 +346,12 @@ __device__ __forceinline__ ChunkWs chunk_ws(const DeltaArgs& a, int64_t chunk) {
     w.P = p; p += DC * DC;
     w.Qg = p; p += DC * D;
     w.Kt = p; p += DC * D;
-    w.carry = p;
-    p = a.ws2 + chunk * a.ws2_chunk;  // (null in the forward, whose kernels use none of these)
-    w.S0 = p; p += D * Dv;
-    w.Wv = p; p += DC * Dv;
+    w.carry = p; p += 4;
+    float* q = a.ws2 + chunk * a.ws2_chunk;  // (null in the forward)
+    float*& s = a.states_in_ws ? p : q;
+    w.S0 = s; s += D * Dv;
+    w.Wv = s; s += DC * Dv;
+    p = q;
     w.dS1 = p; p += D * Dv;
     w.dWv = p; p += DC * Dv;
     w.gQ = p; p += DC * D;
@@ -561,12 +563,17 @@ __device__ __forceinline__ void seq_stash(const SeqRegs<D, QP>& pf, float* sBuf)
 // K of 4.  Waves WB .. WB + NWV - 1 take part: wave WB + w computes tiles w,
 // w + NWV, ...; the other waves return at once (no barrier inside).  Each output
 // element is read (beta) and written by one lane only.
-// state pass (chunks in order): o and hT, or (BWD) S0 and Wv of every chunk
+// state pass (chunks in order): o and hT (and, when they live in ws, S0 and Wv of
+// every chunk for the backward), or (BWD) S0 and Wv of every chunk; the backward's
+// pass exits at once when ws holds them for these inputs
 template <typename T, bool BWD, int D>
 __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
     using L = SeqLayout<D, !BWD, false>;
     __shared__ float sBuf[L::TOTAL];
     __shared__ float sS[D * NSL], sWv[DC * NSL], sO[DC * NSL];
+    if constexpr (BWD)
+        if (a.check_stamp && a.states_in_ws && stamp_matches(a.stamp, a.expect)) return;
+    const bool keep = BWD || a.states_in_ws;  // S0 and Wv stored
     const int Dv = (int)a.dv;
     const int nsl = Dv / NSL;
     const int64_t lb = xcd_logical_block(gridDim.x);  // the slices of one head share an XCD's L2
@@ -602,7 +609,7 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
         __syncthreads();  // (the previous chunk no longer reads sBuf; sS and sO are complete)
         if (!BWD && c > 0) store_o();
         seq_stash<D, !BWD, false>(pf, sBuf);
-        if (BWD)
+        if (keep)
             store_transposed<D>(sS, w.S0, j0);  // S0 transposed: [value column][key row]
         __syncthreads();
         // Wv = U - W S0 on waves 0-3; in the forward, O = (gamma Q) S0 on waves 4-7
@@ -612,9 +619,9 @@ __global__ __launch_bounds__(DTH) void k_delta_state(const DeltaArgs a) {
         if (!BWD) mm_lds<DC, NSL, D, L::PQ, 1, 1, NSL, NSL, 4, 4>(1.f, sBuf + L::QG, sS, 0.f, sO);
         __syncthreads();
         if (c + 1 < NC) fetch(c + 1);
-        if (BWD)
+        if (keep)
             store_transposed<DC>(sWv, w.Wv, j0);  // Wv transposed: [value column][row]
-        else  // O += P Wv on waves 4-7
+        if (!BWD)  // O += P Wv on waves 4-7
             mm_lds<DC, NSL, DC, L::PP, 1, 1, NSL, NSL, 4, 4>(1.f, sBuf + L::P, sWv, 1.f, sO);
         // S1 = c S0 + Kt^T Wv (8 tiles; the forward keeps waves 4-7 for O)
         mm_lds<D, NSL, DC, 1, L::PK, 1, NSL, NSL, 0, BWD ? 8 : 4>(1.f, sBuf + L::KT_, sWv, carry, sS);
@@ -888,10 +895,14 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
 
 }  // namespace
 
-// T, P; U; W, Qg, Kt; the carry (4)
-int64_t delta_fwd_floats_per_chunk(int64_t dk, int64_t dv) { return 2 * DC * DC + DC * (dv + 3 * dk) + 4; }
-// S0, dS1; Wv, dWv, gV; gQ, gK, gKt, gW, gKb
-int64_t delta_bwd_floats_per_chunk(int64_t dk, int64_t dv) { return 2 * dk * dv + DC * (3 * dv + 5 * dk); }
+// T, P; U; W, Qg, Kt; the carry (4); (states_in_ws) S0, Wv
+int64_t delta_fwd_floats_per_chunk(int64_t dk, int64_t dv, bool states_in_ws) {
+    return 2 * DC * DC + DC * (dv + 3 * dk) + 4 + (states_in_ws ? dk * dv + DC * dv : 0);
+}
+// (unless states_in_ws) S0, Wv; dS1, dWv, gV; gQ, gK, gKt, gW, gKb
+int64_t delta_bwd_floats_per_chunk(int64_t dk, int64_t dv, bool states_in_ws) {
+    return 2 * dk * dv + DC * (3 * dv + 5 * dk) - (states_in_ws ? dk * dv + DC * dv : 0);
+}
 
 
 // the per-chunk kernels' instance for the problem's (d_k, d_v)
@@ -917,31 +928,33 @@ hipError_t launch_delta_fwd(const DeltaArgs& a0, hipStream_t st) {
     launch_shape<k_delta_prep_ptr<T>>(a, dim3((unsigned)(a.B * a.H * NC)), st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if ((e = launch_write_stamp(a.stamp, a.expect, st)) != hipSuccess) return e;
     const dim3 slices((unsigned)(a.B * a.H * (a.dv / NSL)));
     if (a.dk == 128)
         hipLaunchKernelGGL((k_delta_state<T, false, 128>), slices, dim3(DTH), 0, st, a);
     else
         hipLaunchKernelGGL((k_delta_state<T, false, 64>), slices, dim3(DTH), 0, st, a);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the stamp vouches for everything the forward stored in ws: written last
+    return launch_write_stamp(a.stamp, a.expect, st);
 }
 
 template <typename T>
 hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st) {
     const int64_t NC = (a.T + DC - 1) / DC;
     const dim3 chunks((unsigned)(a.B * a.H * NC)), slices((unsigned)(a.B * a.H * (a.dv / NSL)));
-    // the prepare pass exits at once when the workspace's stamp shows it holds these
-    // factors already (check_stamp: the caller allows the reuse); the stamp then
-    // records that it does
+    // the prepare pass (and the state pass, where S0 and Wv live in ws) exits at
+    // once when the workspace's stamp shows it holds these inputs' factors already
+    // (check_stamp: the caller allows the reuse); both read the stamp as the call
+    // found it, and the stamp then records what ws holds
     launch_shape<k_delta_prep_ptr<T>>(a, chunks, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if ((e = launch_write_stamp(a.stamp, a.expect, st)) != hipSuccess) return e;
     if (a.dk == 128)
         hipLaunchKernelGGL((k_delta_state<T, true, 128>), slices, dim3(DTH), 0, st, a);
     else
         hipLaunchKernelGGL((k_delta_state<T, true, 64>), slices, dim3(DTH), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_write_stamp(a.stamp, a.expect, st)) != hipSuccess) return e;
     if (a.dk == 128)
         hipLaunchKernelGGL((k_delta_dstate<T, 128>), slices, dim3(DTH), 0, st, a);
     else

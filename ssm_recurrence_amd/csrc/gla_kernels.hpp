@@ -174,12 +174,15 @@ struct DeltaArgs {
     int64_t ws2_chunk;
     uint64_t* stamp;                        // the workspace's stamp words
     Stamp expect;                           // this call's stamp
-    int32_t check_stamp;                    // backward: skip the prepare pass when stamp == expect
+    int32_t check_stamp;                    // backward: skip the prepare and state passes when stamp == expect
+    // the states entering the chunks and the effective writes (S0, Wv) live in ws,
+    // after each chunk's factors (the forward stores them), not in ws2
+    int32_t states_in_ws;
     int64_t B, T, H, dk, dv;
 };
 constexpr int64_t kDeltaHeaderBytes = kStampBytes;  // the stamp, ahead of the per-chunk factors
-int64_t delta_fwd_floats_per_chunk(int64_t dk, int64_t dv);
-int64_t delta_bwd_floats_per_chunk(int64_t dk, int64_t dv);
+int64_t delta_fwd_floats_per_chunk(int64_t dk, int64_t dv, bool states_in_ws);
+int64_t delta_bwd_floats_per_chunk(int64_t dk, int64_t dv, bool states_in_ws);
 template <typename T> hipError_t launch_delta_fwd(const DeltaArgs& a, hipStream_t st);
 template <typename T> hipError_t launch_delta_bwd(const DeltaArgs& a, hipStream_t st);
 

@@ -422,3 +422,10 @@ def test_delta_workspace(lib):
     assert call_delta_bwd(lib, p, {"ws": FAKE, "scratch": FAKE + 8}, ws_bytes=n, scratch_bytes=m) == -5
     n2, m2 = delta_sizes(lib, delta_prob(T=200))
     assert n2 - 256 == 2 * (n - 256) and m2 == 2 * m  # 4 chunks against 2
+    # GLA_DELTA_WS_FROM_FWD: the state entering each chunk (d_k x d_v) and the
+    # effective writes (64 x d_v) move from the scratch into ws
+    f = delta_prob()
+    f.flags = 1
+    nf, mf = delta_sizes(lib, f)
+    moved = 128 * 64 + 64 * 64
+    assert nf == n + 2 * 8 * moved * 4 and mf == m - 2 * 8 * moved * 4

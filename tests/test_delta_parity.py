@@ -92,16 +92,18 @@ REUSE_CASES = [
 @pytest.mark.parametrize("B,T,H,dk,dv,dtype,lens", REUSE_CASES,
                          ids=["B%d-T%d-%s" % (c[0], c[1], str(c[5])[6:]) for c in REUSE_CASES])
 def test_delta_bwd_reuses_forward_workspace(B, T, H, dk, dv, dtype, lens):
-    """GLA_DELTA_WS_FROM_FWD: the backward handed the forward's workspace skips
-    recomputing the per-chunk factors; its gradients equal, bit for bit, those of
-    a backward that recomputes them (the same kernels on the same values), match
-    the oracle, and a second backward on the same workspace gives them again."""
+    """GLA_DELTA_WS_FROM_FWD on both calls: the backward handed the forward's
+    workspace skips recomputing the per-chunk factors and the states entering the
+    chunks (the forward stored them); its gradients equal, bit for bit, those of a
+    backward that recomputes them (the same products in the same order), match the
+    oracle, and a second backward on the same workspace gives them again."""
     case = delta_case("reuse", B=B, T=T, H=H, d_k=dk, d_v=dv, dtype=dtype, seed=7 + T, lengths=lens,
                       with_h0=True, with_dhT=True)
     c = case.to("cuda")
     print("delta reuse", B, T, H, dk, dv, dtype, lens, flush=True)
-    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(c.q, c.v)), dtype=torch.uint8, device="cuda")
-    o, hT = gb.delta_fwd(c.q, c.k, c.v, c.g, c.beta, c.h0, c.segment_ids, ws=ws)
+    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(c.q, c.v, gb.GLA_DELTA_WS_FROM_FWD)),
+                     dtype=torch.uint8, device="cuda")
+    o, hT = gb.delta_fwd(c.q, c.k, c.v, c.g, c.beta, c.h0, c.segment_ids, ws=ws, ws_from_fwd=True)
     args = (c.q, c.k, c.v, c.g, c.beta, c.dO, c.h0, c.segment_ids, c.dhT)
     reused = gb.delta_bwd(*args, ws=ws, ws_from_fwd=True)
     again = gb.delta_bwd(*args, ws=ws, ws_from_fwd=True)
@@ -116,30 +118,40 @@ def test_delta_bwd_reuses_forward_workspace(B, T, H, dk, dv, dtype, lens):
 
 
 def test_delta_ws_stamp_guards_reuse():
-    """GLA_DELTA_WS_FROM_FWD reuses ws only when its stamp (sizes, input pointers,
-    generation) is this call's: a workspace from other inputs, from the same
-    buffers changed in place under a new generation, or left by a backward that
-    recomputed for other inputs is recomputed, so every gradient equals the
-    recomputing backward's, bit for bit."""
+    """GLA_DELTA_WS_FROM_FWD reuses ws only when its stamp (sizes, flags, input
+    pointers, generation) is this call's: a workspace from other inputs, from the
+    same buffers changed in place under a new generation, left by a backward that
+    recomputed for other inputs, or written by a forward without the flag (which
+    stores no states) is recomputed, so every gradient equals the recomputing
+    backward's, bit for bit."""
     mk = lambda seed: delta_case("stamp", B=1, T=200, H=2, d_k=64, d_v=64, dtype=torch.bfloat16, seed=seed,
                                  lengths=[120, 80], with_h0=True, with_dhT=True).to("cuda")
     a, b = mk(11), mk(12)
     args = lambda c: (c.q, c.k, c.v, c.g, c.beta, c.dO, c.h0, c.segment_ids, c.dhT)
     fresh_a, fresh_b = gb.delta_bwd(*args(a)), gb.delta_bwd(*args(b))
-    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(a.q, a.v)), dtype=torch.uint8, device="cuda")
-    gb.delta_fwd(a.q, a.k, a.v, a.g, a.beta, a.h0, a.segment_ids, ws=ws, generation=1)
+    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(a.q, a.v, gb.GLA_DELTA_WS_FROM_FWD)),
+                     dtype=torch.uint8, device="cuda")
+    ws.fill_(255)
+    gb.delta_fwd(a.q, a.k, a.v, a.g, a.beta, a.h0, a.segment_ids, ws=ws, ws_from_fwd=True, generation=1)
     # other inputs, same generation: their own factors
     got_b = gb.delta_bwd(*args(b), ws=ws, ws_from_fwd=True, generation=1)
     # the backward recomputed for b: ws now holds b's factors, stamped so; a again
     got_a = gb.delta_bwd(*args(a), ws=ws, ws_from_fwd=True, generation=1)
     # a's forward, then a's q changed in place under a new generation
-    gb.delta_fwd(a.q, a.k, a.v, a.g, a.beta, a.h0, a.segment_ids, ws=ws, generation=2)
+    gb.delta_fwd(a.q, a.k, a.v, a.g, a.beta, a.h0, a.segment_ids, ws=ws, ws_from_fwd=True, generation=2)
     q_old = a.q.clone()
     a.q.copy_(b.q)
     got_a2 = gb.delta_bwd(*args(a), ws=ws, ws_from_fwd=True, generation=3)
     fresh_a2 = gb.delta_bwd(*args(a))
     a.q.copy_(q_old)
+    # a forward without the flag stores factors only: a flagged backward on a fresh
+    # workspace (no states in it) recomputes everything
+    ws2 = torch.empty_like(ws).fill_(255)
+    gb.delta_fwd(b.q, b.k, b.v, b.g, b.beta, b.h0, b.segment_ids, ws=ws2, generation=4)
+    got_b2 = gb.delta_bwd(*args(b), ws=ws2, ws_from_fwd=True, generation=4)
     torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, got_b2, fresh_b):
+        assert torch.equal(x, y), "forward without the flag: " + n
     for n, x, y in zip(NAMES, got_b, fresh_b):
         assert torch.equal(x, y), "other inputs: " + n
     for n, x, y in zip(NAMES, got_a, fresh_a):
@@ -183,8 +195,9 @@ def test_delta_full_size_sampled():
     c = case.to("cuda")
     got = run_gpu(c)
     # the benchmark's backward reuses the forward's factors: bit for bit the same
-    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(c.q, c.v)), dtype=torch.uint8, device="cuda")
-    gb.delta_fwd(c.q, c.k, c.v, c.g, c.beta, c.h0, c.segment_ids, ws=ws, generation=1)
+    ws = torch.empty(gb.delta_workspace_size(gb.delta_problem(c.q, c.v, gb.GLA_DELTA_WS_FROM_FWD)),
+                     dtype=torch.uint8, device="cuda")
+    gb.delta_fwd(c.q, c.k, c.v, c.g, c.beta, c.h0, c.segment_ids, ws=ws, ws_from_fwd=True, generation=1)
     reused = gb.delta_bwd(c.q, c.k, c.v, c.g, c.beta, c.dO, c.h0, c.segment_ids, c.dhT, ws=ws,
                           ws_from_fwd=True, generation=1)
     torch.cuda.synchronize()
