@@ -347,11 +347,13 @@ __device__ __forceinline__ ChunkWs chunk_ws(const DeltaArgs& a, int64_t chunk) {
     w.Qg = p; p += DC * D;
     w.Kt = p; p += DC * D;
     w.carry = p; p += 4;
-    float* q = a.ws2 + chunk * a.ws2_chunk;  // (null in the forward)
-    float*& s = a.states_in_ws ? p : q;
-    w.S0 = s; s += D * Dv;
-    w.Wv = s; s += DC * Dv;
-    p = q;
+    // S0 and Wv: in ws after the factors (states_in_ws), else first in ws2
+    // (ws2 is null in the forward)
+    float* q = a.ws2 + chunk * a.ws2_chunk;
+    float* st = a.states_in_ws ? p : q;
+    w.S0 = st;
+    w.Wv = st + D * Dv;
+    p = a.states_in_ws ? q : q + D * Dv + DC * Dv;
     w.dS1 = p; p += D * Dv;
     w.dWv = p; p += DC * Dv;
     w.gQ = p; p += DC * D;

@@ -507,8 +507,9 @@ __global__ __launch_bounds__(512) void k_states2_w(const PassArgs a) {
 }
 
 // whole-state workgroups when there are enough of them (one per compute unit);
-// measured: a gain for fp32 (c2: 176 vs 192 us for the state pair), a loss for
-// bf16 (c4: 578 vs 509 us), whose passes stream more bytes per unit of work
+// measured: a gain for fp32 (B=4 T=8192 H=8: 176 vs 192 us for the state pair), a
+// loss for bf16 (B=1 T=65536 H=16: 578 vs 509 us), whose passes stream more bytes
+// per unit of work
 template <typename T, bool VEC, int DK, int DV>
 constexpr bool whole_state_ok() { return sizeof(T) == 4 && !VEC && DK == 128 && DV == 128; }
 
