@@ -289,6 +289,9 @@ gla::CombineArgs combine_args(const gla::PassArgs& pa, int DK, int DV, int which
     c.DK = DK;
     c.DV = DV;
     c.which = which;
+    c.stamp = pa.stamp;
+    c.expect = pa.expect;
+    c.check_stamp = pa.check_stamp;
     return c;
 }
 
@@ -338,11 +341,9 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
     // H=16, vector gate: 419 against 438 us for the backward with 64 x 64 blocks)
     const bool wide = wide_blocks(pa, DK, 2, sizeof(T) == 2 ? 256 : 512);
     // the states entering the chunks are in ws for these inputs once the state pass
-    // has run (or found the forward's): stamp them so
-    auto stamp = [&]() {
-        return pa.check_stamp ? gla::launch_write_stamp(const_cast<uint64_t*>(pa.stamp), pa.expect, st)
-                              : hipSuccess;
-    };
+    // has run (or found the forward's): the launch after it writes the stamp that
+    // says so (its workgroup 0, at its start)
+    uint64_t* const stamp_out = pa.check_stamp ? const_cast<uint64_t*>(pa.stamp) : nullptr;
     if (pa.P > 1) {
         gla::PassArgs sa = pa;
         sa.d_from_rev = 1;
@@ -363,18 +364,22 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
     }
     if constexpr (sizeof(T) == 2 && !VEC && DK == 128 && DV == 128) {
         e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, wide_blocks(pa, DK, 1, 256), st);
-        if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
-        e = gla::launch_grad8_walk(ra, st);
+        if (e != hipSuccess) return e;
+        gla::RevArgs wa = ra;
+        wa.stamp_out = stamp_out;
+        wa.stamp_val = pa.expect;
+        e = gla::launch_grad8_walk(wa, st);
     } else {
         if (pa.check_stamp) {
             // the forward's states may be in ws: the state pass exits at once and the
             // state-gradient pass runs in a launch of its own
             e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, wide_blocks(pa, DK, 1, 256), st);
-            if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
-            e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_DSTATES, wide_blocks(pa, DK, 1, 256), st);
+            if (e != hipSuccess) return e;
+            gla::PassArgs da = pa;
+            da.stamp_out = stamp_out;
+            e = gla::launch_states<T, VEC, DK, DV>(da, gla::ST_DSTATES, wide_blocks(pa, DK, 1, 256), st);
         } else {
             e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
-            if (e != hipSuccess || (e = stamp()) != hipSuccess) return e;
         }
         if (e != hipSuccess) return e;
         e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
@@ -512,12 +517,13 @@ int fwd_checked(const gla_problem* p, const WsLayout& L, const void* q, const vo
         a.S_in = (const float*)(w + L.pS);
         a.D_out = (float*)(w + L.pD);
     }
-    if (saves_states(p)) a.save_S = (char*)ws + L.S;
+    if (saves_states(p)) {
+        // the forward kernel stores the states and writes the stamp that vouches for them
+        a.save_S = (char*)ws + L.S;
+        a.stamp_out = (uint64_t*)((char*)ws + L.stamp);
+        a.expect = states_stamp(p, q, k, v, g, h0, segment_ids);
+    }
     if (dispatch<FwdF>(p, a, st) != hipSuccess) return GLA_E_LAUNCH;
-    if (saves_states(p) &&
-        gla::launch_write_stamp((uint64_t*)((char*)ws + L.stamp), states_stamp(p, q, k, v, g, h0, segment_ids),
-                                st) != hipSuccess)
-        return GLA_E_LAUNCH;
     return GLA_OK;
 }
 

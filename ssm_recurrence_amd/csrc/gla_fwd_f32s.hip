@@ -48,6 +48,7 @@ constexpr int PA = C + 8, PLA = C * PA;     // [64 r][64 s] split score tile
 
 __global__ __launch_bounds__(512) void k_fwd_f32h(const PassArgs a) {
     constexpr int NTH = 512;
+    put_stamp(a.stamp_out, a.expect);  // the states this kernel stores
     __shared__ __attribute__((aligned(16))) bf16 sQ[2 * PLQ];
     __shared__ __attribute__((aligned(16))) bf16 sK[2 * PLKH];
     __shared__ __attribute__((aligned(16))) bf16 sV[2 * PLH];

@@ -71,6 +71,7 @@ template <bool VEC>
 __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
     using M = Mma<bf16>;
     __shared__ __attribute__((aligned(16))) FwdHLds<VEC> sm;
+    put_stamp(a.stamp_out, a.expect);  // the states this kernel stores
 
     const int64_t P = a.P;
     const int64_t L = xcd_logical_block(a.B * a.H * P);

@@ -72,6 +72,7 @@ __global__ __launch_bounds__(512) void k_grad8(const RevArgs a) {
     using Cfg = Grad8Cfg<VEC, WALK>;
     using M = Mma<T>;
     constexpr int P = Cfg::P, PB = Cfg::PB, PE = Cfg::PE, PF = Cfg::PF, DK = 128, DV = 128;
+    put_stamp(a.stamp_out, a.stamp_val);  // the states the pass before this one found or stored
     constexpr int NTH = Cfg::NTH, KS = M::KSTEP, NKV = DV / KS;
 
     __shared__ __attribute__((aligned(16))) char lds[Cfg::BYTES];

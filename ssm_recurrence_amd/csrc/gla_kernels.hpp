@@ -27,8 +27,20 @@ __device__ __forceinline__ bool stamp_matches(const uint64_t* stamp, const Stamp
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(same) != 0;
 }
-// writes a stamp (launched after the pass that stored what it describes)
-hipError_t launch_write_stamp(uint64_t* dst, const Stamp& s, hipStream_t st);
+// Workgroup 0 writes the stamp `s` to dst (null: nothing).  Launches on one
+// stream run in order, so a kernel that stores what a stamp describes, or that
+// runs after the kernel that did, may write the stamp itself at its start: no
+// later launch reads it before every workgroup of this one has finished.  A
+// kernel whose workgroups compare the stamp must not write it (one of them could
+// see the new value before another has read the old one).
+__device__ __forceinline__ void put_stamp(uint64_t* dst, const Stamp& s) {
+    if (dst == nullptr || blockIdx.x != 0 || threadIdx.x >= kStampWords) return;
+    uint64_t w = s.w[0];
+#pragma unroll
+    for (int i = 1; i < kStampWords; ++i)
+        if ((int)threadIdx.x == i) w = s.w[i];
+    dst[threadIdx.x] = w;
+}
 
 struct PassArgs {
     const void *q, *k, *v, *g, *dO;
@@ -55,6 +67,9 @@ struct PassArgs {
     const uint64_t* stamp;
     Stamp expect;
     int32_t check_stamp;
+    // the forward kernel, or a backward pass launched after the states were
+    // stored: workgroup 0 writes `expect` here (put_stamp; null: nothing)
+    uint64_t* stamp_out;
     // summaries in one launch: D_out of pieces 1.. comes from ST_SUM_REV (which
     // always runs), of piece 0 from ST_SUM_FWD
     int32_t d_from_rev;
@@ -77,6 +92,10 @@ struct RevArgs {
     // the split of the reverse walk (launch_grad8_walk): P pieces of PL chunks
     int64_t P, PL;
     const float* dS_in;    // [B*H][P][DK][DV]: state gradient at each piece's end (P > 1)
+    // the reverse walk, launched after the states were stored: workgroup 0 writes
+    // stamp_val here (put_stamp; null: nothing)
+    uint64_t* stamp_out;
+    Stamp stamp_val;
 };
 
 struct CombineArgs {
@@ -84,6 +103,12 @@ struct CombineArgs {
     float *S_in, *dS_in;
     int64_t BH, P;
     int DK, DV, which;
+    // backward: when the stamp matches, the states entering the chunks are the
+    // forward's and the entry states of the pieces are not needed: the forward
+    // chain is skipped
+    const uint64_t* stamp;
+    Stamp expect;
+    int32_t check_stamp;
 };
 
 // modes of the state pass: per-chunk states or state gradients, per-piece summaries
@@ -175,6 +200,7 @@ struct DeltaArgs {
     uint64_t* stamp;                        // the workspace's stamp words
     Stamp expect;                           // this call's stamp
     int32_t check_stamp;                    // backward: skip the prepare and state passes when stamp == expect
+    int32_t put_stamp;                      // this launch's workgroup 0 writes expect to stamp (put_stamp)
     // the states entering the chunks and the effective writes (S0, Wv) live in ws,
     // after each chunk's factors (the forward stores them), not in ws2
     int32_t states_in_ws;

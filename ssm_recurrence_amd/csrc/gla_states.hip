@@ -472,6 +472,7 @@ template <typename T, bool VEC, int DK, int DV, int MODE, int NB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(states_waves<T, VEC, NB>())))
 void k_states(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) StatesLdsFor<T, VEC, NB> sm;
+    if constexpr (MODE == ST_DSTATES) put_stamp(a.stamp_out, a.expect);
     const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
     states_any<T, VEC, DK, DV, MODE, NB>(a, sm, xcd_logical_block(n));
 }
@@ -495,6 +496,7 @@ void k_states2(const PassArgs a) {
 template <typename T, int DK, int DV, int MODE>
 __global__ __launch_bounds__(512) void k_states_w(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) StatesLdsS<T, DV, DK> sm;
+    if constexpr (MODE == ST_DSTATES) put_stamp(a.stamp_out, a.expect);
     states_body_s<T, DK, DV, MODE, DV, DK>(a, sm, xcd_logical_block(a.B * a.H * a.P));
 }
 template <typename T, int DK, int DV, int MODE_A, int MODE_B>
@@ -591,6 +593,8 @@ __global__ __launch_bounds__(256) void k_piece_combine(CombineArgs c) {
         rev = true;
         i -= n;
     }
+    // (n is a multiple of 256: a workgroup runs one chain, and this test is uniform)
+    if (!rev && c.check_stamp && stamp_matches(c.stamp, c.expect)) return;
     if (i >= n) return;
     const int64_t bh = i / per, cn = i % per;
     const int ch = (int)(cn / c.DV);
@@ -612,15 +616,6 @@ __global__ __launch_bounds__(256) void k_piece_combine(CombineArgs c) {
             c.dS_in[base + (p - 1) * per] = s;
         }
     }
-}
-
-__global__ void k_write_stamp(uint64_t* dst, const Stamp s) {
-    if (threadIdx.x < kStampWords) dst[threadIdx.x] = s.w[threadIdx.x];
-}
-
-hipError_t launch_write_stamp(uint64_t* dst, const Stamp& s, hipStream_t st) {
-    hipLaunchKernelGGL(k_write_stamp, dim3(1), dim3(64), 0, st, dst, s);
-    return hipGetLastError();
 }
 
 hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st) {

@@ -66,15 +66,13 @@ def part_of(workload, name):
         return []
     fwd, bwd = CALLS.get(workload, ("gla_fwd", "gla_bwd"))
     if workload in CALLS:
-        if "k_write_stamp" in name:
-            return [fwd, bwd]
         # (the delta rule's prepare pass is launched by both calls, the backward's
         # launch exiting when the forward's factors are found: split per dispatch
         # below; its forward state pass is k_delta_state<T, false, D>, "Lb0E" mangled)
         if "fwd" in name or "delta_prep" in name or ("k_delta_state" in name and "Lb0E" in name):
             return [fwd]
         return [bwd]
-    if "k_piece_combine" in name or "k_write_stamp" in name:
+    if "k_piece_combine" in name:
         return [fwd, bwd]
     if "k_fwd" in name:
         return [fwd]
