@@ -310,7 +310,7 @@ typedef struct {
  * writes, and gla_delta_bwd reuses them and the per-chunk factors instead of
  * recomputing them.  Every ws carries a stamp of what it holds: the problem's
  * sizes, dtype and flags, the q, k, v, g, beta and segment_ids pointers and
- * p->generation (gla_delta_fwd writes it after its last pass; a backward that
+ * p->generation (gla_delta_fwd's last pass writes it; a backward that
  * recomputes rewrites it).  The backward's prepare and state passes compare the
  * stamp with their own call's on the device and recompute unless they are equal,
  * so a ws from another problem, other inputs, another layer or a forward without
