@@ -128,13 +128,15 @@ def test_stored_states_are_prefix_states(T, d, gate, dtype, H, Hqk, lens, pf, pb
 
 
 @pytest.mark.parametrize("dtype,gate,T", [(torch.bfloat16, "scalar", 256), (torch.float32, "scalar", 256),
+                                          (torch.bfloat16, "scalar", 64 * 24 + 5),
                                           (torch.float32, "scalar", 64 * 24 + 5)])
 def test_stale_stamp_recomputes(dtype, gate, T):
     """A backward whose inputs differ from the forward's recomputes the states:
     (a) other tensors, same generation; (b) the same tensors changed in place,
     with a new generation.  A second backward with the same inputs and generation
     then finds the states the first one computed: bit-identical gradients.  (The
-    longer fp32 row is split by the backward: its forward summaries recompute too.)"""
+    longer rows are split by the backward: its forward summaries and the forward
+    chain of its combine run too, which a matching stamp skips.)"""
     lens = [100, T - 100]
     a = make(T, 128, gate, dtype, 2, 2, lens, seed=1)
     b = make(T, 128, gate, dtype, 2, 2, lens, seed=2)
