@@ -307,14 +307,23 @@ bool wide_blocks(const gla::PassArgs& pa, int DK, int64_t passes, int64_t want) 
 template <typename T, bool VEC, int DK, int DV>
 hipError_t run_split_fwd_states(const gla::PassArgs& pa, hipStream_t st) {
     hipError_t e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_SUM_FWD, wide_blocks(pa, DK, 1, 256), st);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || pa.entry_from_summaries) return e;
     return gla::launch_piece_combine(combine_args(pa, DK, DV, 1), st);
 }
+
+// Split forwards of the whole-state kernels (128 x 128 heads: bf16, or fp32 with
+// the scalar gate) with at most this many pieces skip the combine: the workgroup
+// of piece p reads the p summaries before it, P (P - 1) / 2 in all, against 3 P
+// for the combine's round trip through S_in, and one launch fewer.
+constexpr int64_t kChainPieces = 8;
 
 // Columns of the state per forward workgroup: the widest slice that still
 // gives at least 256 workgroups (one per compute unit), else 16.
 template <typename T, bool VEC, int DK, int DV>
-hipError_t run_fwd(const gla::PassArgs& a, hipStream_t st) {
+hipError_t run_fwd(const gla::PassArgs& a0, hipStream_t st) {
+    constexpr bool whole = DK == 128 && DV == 128 && (sizeof(T) == 2 || !VEC);
+    gla::PassArgs a = a0;
+    a.entry_from_summaries = whole && a.P > 1 && a.P <= kChainPieces;
     if (a.P > 1) {
         const hipError_t e = run_split_fwd_states<T, VEC, DK, DV>(a, st);
         if (e != hipSuccess) return e;

@@ -108,15 +108,7 @@ __global__ __launch_bounds__(NTH) void k_fwd_h(const PassArgs a) {
 
     // state tiles ct = 0..7 of column tile w: lane holds S[16ct + 4j4 + e][16w + i16]
     f32x4 S[DK / 16];
-#pragma unroll
-    for (int ct = 0; ct < DK / 16; ++ct) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = 16 * ct + 4 * j4 + e, n = 16 * w + i16;
-            if (P > 1) S[ct][e] = a.S_in[((bh * P + piece) * DK + c) * DV + n];
-            else S[ct][e] = a.h0 ? a.h0[(bh * DK + c) * DV + n] : 0.f;
-        }
-    }
+    load_entry_state_128(a, bh, piece, w, j4, i16, S);
 
     TileRegs<bf16, DK, NTH> pq, pk, pv;
     TileRegs<bf16, VEC ? DK : 8, NTH> pg;

@@ -70,6 +70,10 @@ struct PassArgs {
     // the forward kernel, or a backward pass launched after the states were
     // stored: workgroup 0 writes `expect` here (put_stamp; null: nothing)
     uint64_t* stamp_out;
+    // split forward, whole-state kernels: each workgroup forms its piece's entry
+    // state from h0 and the summaries of the pieces before it (L_out[0], D_out)
+    // instead of reading S_in (no combine launch)
+    int32_t entry_from_summaries;
     // summaries in one launch: D_out of pieces 1.. comes from ST_SUM_REV (which
     // always runs), of piece 0 from ST_SUM_FWD
     int32_t d_from_rev;

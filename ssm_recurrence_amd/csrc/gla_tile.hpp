@@ -200,6 +200,43 @@ __device__ __forceinline__ void store_state_128(T* dst, const f32x4 (&S)[8]) {
         }
 }
 
+// The state entering piece `piece` of head bh (= b H + h), at the accumulator
+// positions of wave w: S[ct][e] = S[16 ct + 4 j4 + e][16 w + i16] of a 128 x 128
+// state.  Without a split, h0 (or zero).  With one, the combine's S_in, or (when
+// a.entry_from_summaries) the combine's chain S <- D_q S + L_q from h0 over the
+// pieces before this one, formed here with the same operations in the same order.
+template <typename Args>
+__device__ __forceinline__ void load_entry_state_128(const Args& a, int64_t bh, int64_t piece, int w, int j4, int i16,
+                                                     f32x4 (&S)[8]) {
+    constexpr int DK = 128, DV = 128;
+    const int64_t P = a.P;
+    const int n = 16 * w + i16;
+    if (P > 1 && !a.entry_from_summaries) {
+#pragma unroll
+        for (int ct = 0; ct < DK / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[ct][e] = a.S_in[((bh * P + piece) * DK + 16 * ct + 4 * j4 + e) * DV + n];
+        return;
+    }
+#pragma unroll
+    for (int ct = 0; ct < DK / 16; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[ct][e] = a.h0 ? a.h0[(bh * DK + 16 * ct + 4 * j4 + e) * DV + n] : 0.f;
+    if (P == 1) return;
+#pragma unroll 1
+    for (int64_t q = 0; q < piece; ++q) {
+        const float* L = a.L_out[0] + (bh * P + q) * DK * DV;
+        const float* D = a.D_out + (bh * P + q) * DK;
+#pragma unroll
+        for (int ct = 0; ct < DK / 16; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * ct + 4 * j4 + e;
+                S[ct][e] = D[c] * S[ct][e] + L[c * DV + n];
+            }
+    }
+}
+
 // Operands of the triangular matrix of ones L^T (L[r][u] = [u <= r]) for the
 // chunk-local prefix below, one per (row tile rt, k step): element e of lane
 // (i, j) is [k0 + j*KPL + e <= 16 rt + i].  The same fragment serves as A
