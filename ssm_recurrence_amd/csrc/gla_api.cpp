@@ -358,12 +358,10 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
         sa.d_from_rev = 1;
         if (pa.check_stamp) {
             // the forward's states may be in ws, and then its summaries exit at once:
-            // the reverse summaries run in a launch of their own (bf16, B=1 T=65536
-            // H=16: 141 us alone against 202 us in a paired launch half of whose
-            // workgroups exit)
-            e = gla::launch_states<T, VEC, DK, DV>(sa, gla::ST_SUM_FWD, wide_blocks(sa, DK, 1, 256), st);
-            if (e != hipSuccess) return e;
-            e = gla::launch_states<T, VEC, DK, DV>(sa, gla::ST_SUM_REV, wide_blocks(sa, DK, 1, 256), st);
+            // they take the last half of the blocks, after the reverse summaries (bf16,
+            // B=1 T=65536 H=16: 141 us for the reverse summaries alone against 202 us
+            // interleaved with workgroups that exit)
+            e = gla::launch_states_trail<T, VEC, DK, DV>(sa, true, wide_blocks(sa, DK, 1, 256), st);
         } else {
             e = gla::launch_states_pair<T, VEC, DK, DV>(sa, true, wide, st);
         }
@@ -379,19 +377,19 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
         wa.stamp_val = pa.expect;
         e = gla::launch_grad8_walk(wa, st);
     } else {
+        gla::RevArgs ga = ra;
         if (pa.check_stamp) {
-            // the forward's states may be in ws: the state pass exits at once and the
-            // state-gradient pass runs in a launch of its own
-            e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, wide_blocks(pa, DK, 1, 256), st);
-            if (e != hipSuccess) return e;
-            gla::PassArgs da = pa;
-            da.stamp_out = stamp_out;
-            e = gla::launch_states<T, VEC, DK, DV>(da, gla::ST_DSTATES, wide_blocks(pa, DK, 1, 256), st);
+            // the forward's states may be in ws: the state pass, which then exits at
+            // once, takes the last half of the blocks after the state-gradient pass;
+            // the gradient kernel writes the stamp
+            e = gla::launch_states_trail<T, VEC, DK, DV>(pa, false, wide_blocks(pa, DK, 1, 256), st);
+            ga.stamp_out = stamp_out;
+            ga.stamp_val = pa.expect;
         } else {
             e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
         }
         if (e != hipSuccess) return e;
-        e = gla::launch_grad<T, VEC, DK, DV>(ra, st);
+        e = gla::launch_grad<T, VEC, DK, DV>(ga, st);
     }
     if (e != hipSuccess) return e;
     if (ra.ws_dq) {

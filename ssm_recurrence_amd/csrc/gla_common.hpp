@@ -91,11 +91,11 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // Block id -> logical id so that consecutive logical ids (the slices of one
 // head) land on the same XCD: the hardware deals consecutive block ids round
 // robin over the 8 XCDs.
-__device__ __forceinline__ int64_t xcd_logical_block(int64_t nblocks) {
-    const int64_t x = blockIdx.x;
+__device__ __forceinline__ int64_t xcd_remap(int64_t x, int64_t nblocks) {
     if (nblocks % 8 != 0) return x;
     return (x % 8) * (nblocks / 8) + x / 8;
 }
+__device__ __forceinline__ int64_t xcd_logical_block(int64_t nblocks) { return xcd_remap(blockIdx.x, nblocks); }
 
 // Operand fragment from LDS for one matrix-core step ("natural" k order):
 // lane (i = l%16, j = l/16) receives X(i0 + i, k0 + j*KPL + e), e < KPL, where

@@ -615,6 +615,7 @@ __device__ void grad_v(const RevArgs& a, char* lds, GradSmall& sm, int64_t bh, i
 
 template <typename T, bool VEC, int DK, int DV>
 __global__ __launch_bounds__(NT) void k_grad(const RevArgs a) {
+    put_stamp(a.stamp_out, a.stamp_val);  // the states the passes before this one found or stored
     using Cfg = GradCfg<T, VEC, DK, DV>;
     __shared__ __attribute__((aligned(16))) char lds[Cfg::BYTES];
     __shared__ GradSmall sm;

@@ -141,6 +141,7 @@ __device__ __forceinline__ void m_load_qk(const RevArgs& a, const MItem& it, Til
 }
 
 __global__ __launch_bounds__(NT8) void k_grad_f32m(const RevArgs a) {
+    put_stamp(a.stamp_out, a.stamp_val);  // the states the passes before this one found or stored
     __shared__ __attribute__((aligned(16))) bf16 lds[M_ELEMS];
     __shared__ RevChunk ck;
     __shared__ float sBs[MNW];

@@ -126,6 +126,12 @@ hipError_t launch_states(const PassArgs& a, int mode, bool wide, hipStream_t st)
 template <typename T, bool VEC, int DK, int DV>
 hipError_t launch_states_pair(const PassArgs& a, bool summaries, bool wide, hipStream_t st);
 
+// ST_SUM_REV then ST_SUM_FWD (summaries = true) or ST_DSTATES then ST_STATES in
+// one launch, the second pass on the last half of the blocks (it may exit at
+// once: the forward's stored states found); blocks as launch_states shapes them
+template <typename T, bool VEC, int DK, int DV>
+hipError_t launch_states_trail(const PassArgs& a, bool summaries, bool wide, hipStream_t st);
+
 hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st);
 
 // scalar gate: dg from the per-slice partial sums (one wave per chunk)

@@ -482,11 +482,22 @@ void k_states(const PassArgs a) {
 // mode over all eight XCDs (also when one of them exits at once, the forward's
 // stored states found) and puts the two directions of a block on one XCD, whose
 // L2 then serves the gate both read.
-template <typename T, bool VEC, int DK, int DV, int MODE_A, int MODE_B, int NB>
+//
+// TRAIL: MODE_A on the first n blocks and MODE_B on the last n instead, for a
+// MODE_B that may exit at once (the forward's stored states found): the blocks
+// are dispatched in order, so MODE_A's spread over the whole device first and
+// MODE_B's take what is left (each half keeps the XCD grouping of its own).
+template <typename T, bool VEC, int DK, int DV, int MODE_A, int MODE_B, int NB, bool TRAIL = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(states_waves<T, VEC, NB>())))
 void k_states2(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) StatesLdsFor<T, VEC, NB> sm;
     const int64_t n = a.B * a.H * a.P * (DK / 64) * (DV / NB);
+    if constexpr (TRAIL) {
+        const int64_t x = blockIdx.x;
+        if (x < n) states_any<T, VEC, DK, DV, MODE_A, NB>(a, sm, xcd_remap(x, n));
+        else states_any<T, VEC, DK, DV, MODE_B, NB>(a, sm, xcd_remap(x - n, n));
+        return;
+    }
     const int64_t L = xcd_logical_block(2 * n);
     if ((L & 1) == 0) states_any<T, VEC, DK, DV, MODE_A, NB>(a, sm, L >> 1);
     else states_any<T, VEC, DK, DV, MODE_B, NB>(a, sm, L >> 1);
@@ -499,10 +510,16 @@ __global__ __launch_bounds__(512) void k_states_w(const PassArgs a) {
     if constexpr (MODE == ST_DSTATES) put_stamp(a.stamp_out, a.expect);
     states_body_s<T, DK, DV, MODE, DV, DK>(a, sm, xcd_logical_block(a.B * a.H * a.P));
 }
-template <typename T, int DK, int DV, int MODE_A, int MODE_B>
+template <typename T, int DK, int DV, int MODE_A, int MODE_B, bool TRAIL = false>
 __global__ __launch_bounds__(512) void k_states2_w(const PassArgs a) {
     __shared__ __attribute__((aligned(16))) StatesLdsS<T, DV, DK> sm;
     const int64_t n = a.B * a.H * a.P;
+    if constexpr (TRAIL) {
+        const int64_t x = blockIdx.x;
+        if (x < n) states_body_s<T, DK, DV, MODE_A, DV, DK>(a, sm, xcd_remap(x, n));
+        else states_body_s<T, DK, DV, MODE_B, DV, DK>(a, sm, xcd_remap(x - n, n));
+        return;
+    }
     const int64_t L = xcd_logical_block(2 * n);
     if ((L & 1) == 0) states_body_s<T, DK, DV, MODE_A, DV, DK>(a, sm, L >> 1);
     else states_body_s<T, DK, DV, MODE_B, DV, DK>(a, sm, L >> 1);
@@ -579,6 +596,44 @@ hipError_t launch_states_pair(const PassArgs& a, bool summaries, bool wide, hipS
     return launch_states_pair_nb<T, VEC, DK, DV, 64>(a, summaries, st);
 }
 
+// A pass and, after it in the same launch, a pass that may exit at once: the
+// reverse summaries then the forward ones (summaries), or the state gradients
+// then the states.  Each half has the block shape its single launch would have.
+template <typename T, bool VEC, int DK, int DV, int NB>
+hipError_t launch_states_trail_nb(const PassArgs& a, bool summaries, hipStream_t st) {
+    const int64_t grid = 2 * a.B * a.H * a.P * (DK / 64) * (DV / NB);
+    if (summaries)
+        hipLaunchKernelGGL((k_states2<T, VEC, DK, DV, ST_SUM_REV, ST_SUM_FWD, NB, true>), dim3((unsigned)grid),
+                           dim3(NT), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_states2<T, VEC, DK, DV, ST_DSTATES, ST_STATES, NB, true>), dim3((unsigned)grid),
+                           dim3(NT), 0, st, a);
+    return hipGetLastError();
+}
+
+// (built for the scalar gate at 128 x 128, the only shape whose forward stores states)
+template <typename T, bool VEC, int DK, int DV>
+hipError_t launch_states_trail(const PassArgs& a, bool summaries, bool wide, hipStream_t st) {
+    if constexpr (VEC || DK != 128 || DV != 128) {
+        return hipErrorInvalidValue;
+    } else {
+        if constexpr (whole_state_ok<T, VEC, DK, DV>()) {
+            const int64_t n = a.B * a.H * a.P;
+            if (wide && n >= 256) {
+                if (summaries)
+                    hipLaunchKernelGGL((k_states2_w<T, DK, DV, ST_SUM_REV, ST_SUM_FWD, true>), dim3((unsigned)(2 * n)),
+                                       dim3(512), 0, st, a);
+                else
+                    hipLaunchKernelGGL((k_states2_w<T, DK, DV, ST_DSTATES, ST_STATES, true>), dim3((unsigned)(2 * n)),
+                                       dim3(512), 0, st, a);
+                return hipGetLastError();
+            }
+        }
+        if (wide) return launch_states_trail_nb<T, VEC, DK, DV, DV>(a, summaries, st);
+        return launch_states_trail_nb<T, VEC, DK, DV, 64>(a, summaries, st);
+    }
+}
+
 // Piece-state combine: one thread per state element (b, h, c, n), P sequential
 // steps of S <- D_p[c] S + L_p[c][n].  The forward chain (from h0) gives the
 // state entering each piece; the reverse chain (from dhT, last piece first)
@@ -626,7 +681,8 @@ hipError_t launch_piece_combine(const CombineArgs& c, hipStream_t st) {
 
 #define GLA_INST_ST(T, VEC, DK, DV)                                                   \
     template hipError_t launch_states<T, VEC, DK, DV>(const PassArgs&, int, bool, hipStream_t); \
-    template hipError_t launch_states_pair<T, VEC, DK, DV>(const PassArgs&, bool, bool, hipStream_t);
+    template hipError_t launch_states_pair<T, VEC, DK, DV>(const PassArgs&, bool, bool, hipStream_t); \
+    template hipError_t launch_states_trail<T, VEC, DK, DV>(const PassArgs&, bool, bool, hipStream_t);
 #define GLA_INST_ST_D(T, VEC)                                     \
     GLA_INST_ST(T, VEC, 64, 64) GLA_INST_ST(T, VEC, 64, 128)      \
     GLA_INST_ST(T, VEC, 128, 64) GLA_INST_ST(T, VEC, 128, 128)
