@@ -414,6 +414,9 @@ __global__ __launch_bounds__(NT8) void k_grad_f32m(const RevArgs a) {
             }
             __syncthreads();  // also: every wave is done with this head's A^T, dO and ck
             if (w == 0) {
+                // the scalar log-gate gradient of this head's chunk: dg[u] = the sum of x
+                // over rows t >= u of u's document, plus the boundary term on the last row
+                // (it reaches the rows of the chunk's last document); 0 at reset rows
                 const int lo = opaque_lane();
                 float tot = 0.f, bt = 0.f;
 #pragma unroll
@@ -421,8 +424,17 @@ __global__ __launch_bounds__(NT8) void k_grad_f32m(const RevArgs a) {
                     tot += sXs[u * C + lo];
                     bt += sBs[u];
                 }
-                if (lo < nvalid) a.ws_xs[bh * T_ + t0 + lo] = tot;
-                if (lo == 0) a.ws_bnd[bh * NC + ci] = bt;
+                const int doc = ck.doc[lo];
+                const int prev = __shfl_up(doc, 1, 64);
+                const int reset = doc - (lo > 0 ? prev : 0);  // (doc counts the resets up to row lo)
+                float run = (lo < nvalid ? tot : 0.f) + (lo == nvalid - 1 ? bt : 0.f);
+#pragma unroll
+                for (int d = 1; d < C; d <<= 1) {
+                    const float y = __shfl_down(run, d, 64);
+                    const int dd = __shfl_down(doc, d, 64);
+                    if (lo + d < C && dd == doc) run += y;
+                }
+                if (lo < nvalid) ((float*)a.dg)[(b * T_ + t0 + lo) * a.H + h] = reset ? 0.f : run;
             }
         }
         {
@@ -450,9 +462,7 @@ hipError_t launch_grad_f32s(const RevArgs& a, hipStream_t st) {
     // persistent: one workgroup per compute unit (the LDS allows no more)
     const int64_t workers = 256;
     hipLaunchKernelGGL(k_grad_f32m, dim3((unsigned)(n < workers ? n : workers)), dim3(NT8), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_dg_scalar(a, 1, false, st);
+    return hipGetLastError();
 }
 
 }  // namespace gla
