@@ -353,6 +353,12 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
     // has run (or found the forward's): the launch after it writes the stamp that
     // says so (its workgroup 0, at its start)
     uint64_t* const stamp_out = pa.check_stamp ? const_cast<uint64_t*>(pa.stamp) : nullptr;
+    // the state and state-gradient passes of a split of up to kChainPieces pieces
+    // chain the summaries themselves (no combine launch); the walk reads the
+    // combine's state gradients
+    constexpr bool walk = sizeof(T) == 2 && !VEC && DK == 128 && DV == 128;
+    gla::PassArgs pb = pa;
+    pb.entry_from_summaries = !walk && pa.P > 1 && pa.P <= kChainPieces;
     if (pa.P > 1) {
         gla::PassArgs sa = pa;
         sa.d_from_rev = 1;
@@ -366,8 +372,10 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
             e = gla::launch_states_pair<T, VEC, DK, DV>(sa, true, wide, st);
         }
         if (e != hipSuccess) return e;
-        e = gla::launch_piece_combine(combine_args(pa, DK, DV, 3), st);
-        if (e != hipSuccess) return e;
+        if (!pb.entry_from_summaries) {
+            e = gla::launch_piece_combine(combine_args(pa, DK, DV, 3), st);
+            if (e != hipSuccess) return e;
+        }
     }
     if constexpr (sizeof(T) == 2 && !VEC && DK == 128 && DV == 128) {
         e = gla::launch_states<T, VEC, DK, DV>(pa, gla::ST_STATES, wide_blocks(pa, DK, 1, 256), st);
@@ -382,11 +390,11 @@ hipError_t run_bwd(const gla::PassArgs& pa, const gla::RevArgs& ra, hipStream_t 
             // the forward's states may be in ws: the state pass, which then exits at
             // once, takes the last half of the blocks after the state-gradient pass;
             // the gradient kernel writes the stamp
-            e = gla::launch_states_trail<T, VEC, DK, DV>(pa, false, wide_blocks(pa, DK, 1, 256), st);
+            e = gla::launch_states_trail<T, VEC, DK, DV>(pb, false, wide_blocks(pa, DK, 1, 256), st);
             ga.stamp_out = stamp_out;
             ga.stamp_val = pa.expect;
         } else {
-            e = gla::launch_states_pair<T, VEC, DK, DV>(pa, false, wide, st);
+            e = gla::launch_states_pair<T, VEC, DK, DV>(pb, false, wide, st);
         }
         if (e != hipSuccess) return e;
         e = gla::launch_grad<T, VEC, DK, DV>(ga, st);

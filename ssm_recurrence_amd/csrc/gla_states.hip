@@ -63,6 +63,51 @@ struct StatesLds {
 // the gradient modes).  NB = 64, or all value columns (each head's v, or dO,
 // then requested once per pass instead of once per 64-channel block).  L is the
 // workgroup's logical index within its launch.
+// A state pass's starting rows, lane row cme (columns n0 + 16 nt + 4 j4 + e):
+// ST_STATES the state entering the piece, ST_DSTATES the state gradient at its end,
+// the summary modes zero.  Without a split, h0 or dhT (or zero).  With one, the
+// combine's S_in or dS_in, or (a.entry_from_summaries) the combine's chain formed
+// here over the summaries, the same operations in the same order: S <- D_q S + L_q
+// from h0 over the pieces before this one, or from dhT over those after it, last first.
+template <int MODE, int DK, int DV, int NNT>
+__device__ __forceinline__ void entry_rows(const PassArgs& a, int64_t bh, int64_t piece, int cme, int n0, int j4,
+                                           f32x4 (&St)[NNT]) {
+    const int64_t P = a.P;
+    const int64_t prow = ((bh * P + piece) * DK + cme) * DV + n0;
+    const int64_t hrow = (bh * DK + cme) * DV + n0;
+    const bool chain = P > 1 && a.entry_from_summaries;
+#pragma unroll
+    for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = 16 * nt + 4 * j4 + e;
+            float x = 0.f;
+            if constexpr (MODE == ST_STATES) {
+                if (P > 1 && !chain) x = a.S_in[prow + n];
+                else if (a.h0) x = a.h0[hrow + n];
+            } else if constexpr (MODE == ST_DSTATES) {
+                if (P > 1 && !chain) x = a.dS_in[prow + n];
+                else if (a.dhT) x = a.dhT[hrow + n];
+            }
+            St[nt][e] = x;
+        }
+    if constexpr (MODE == ST_STATES || MODE == ST_DSTATES) {
+        if (chain) {
+            constexpr bool fwd = MODE == ST_STATES;
+            const float* Ls = a.L_out[fwd ? 0 : 1];
+#pragma unroll 1
+            for (int64_t q = fwd ? 0 : P - 1; fwd ? q < piece : q > piece; q += fwd ? 1 : -1) {
+                const float dq = a.D_out[(bh * P + q) * DK + cme];
+                const float* Lq = Ls + ((bh * P + q) * DK + cme) * DV + n0;
+#pragma unroll
+                for (int nt = 0; nt < NNT; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) St[nt][e] = dq * St[nt][e] + Lq[16 * nt + 4 * j4 + e];
+            }
+        }
+    }
+}
+
 template <typename T, bool VEC, int DK, int DV, int MODE, int NB>
 __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC, NB>& sm, int64_t L) {
     constexpr bool REV = MODE == ST_SUM_REV || MODE == ST_DSTATES;
@@ -108,23 +153,9 @@ __device__ __forceinline__ void states_body(const PassArgs& a, StatesLds<T, VEC,
     // S^T tiles of this wave: (nt, channel tile w); lane c = c0 + 16w + i16, rows n
     f32x4 St[NNT];
     const int cme = c0 + 16 * w + i16;
-    const int64_t prow = ((bh * P + piece) * DK + cme) * DV + n0;  // this lane's row of a piece state
+    const int64_t prow = ((bh * P + piece) * DK + cme) * DV + n0;  // this lane's row of a piece summary
     const int64_t hrow = (bh * DK + cme) * DV + n0;                 // ... of h0, dhT, dh0
-#pragma unroll
-    for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int n = 16 * nt + 4 * j4 + e;
-            float x = 0.f;
-            if constexpr (MODE == ST_STATES) {
-                if (P > 1) x = a.S_in[prow + n];
-                else if (a.h0) x = a.h0[hrow + n];
-            } else if constexpr (MODE == ST_DSTATES) {
-                if (P > 1) x = a.dS_in[prow + n];
-                else if (a.dhT) x = a.dhT[hrow + n];
-            }
-            St[nt][e] = x;
-        }
+    entry_rows<MODE, DK, DV, NNT>(a, bh, piece, cme, n0, j4, St);
     float dprod = 1.f;  // product of this lane's channel decays over the chunks seen
 
     TileRegs<T, CB> pk, pg;
@@ -316,23 +347,9 @@ __device__ __forceinline__ void states_body_s(const PassArgs& a, StatesLdsS<T, N
 
     f32x4 St[NNT];
     const int cme = c0 + 16 * w + i16;
-    const int64_t prow = ((bh * P + piece) * DK + cme) * DV + n0;
-    const int64_t hrow = (bh * DK + cme) * DV + n0;
-#pragma unroll
-    for (int nt = 0; nt < NNT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int n = 16 * nt + 4 * j4 + e;
-            float x = 0.f;
-            if constexpr (MODE == ST_STATES) {
-                if (P > 1) x = a.S_in[prow + n];
-                else if (a.h0) x = a.h0[hrow + n];
-            } else if constexpr (MODE == ST_DSTATES) {
-                if (P > 1) x = a.dS_in[prow + n];
-                else if (a.dhT) x = a.dhT[hrow + n];
-            }
-            St[nt][e] = x;
-        }
+    const int64_t prow = ((bh * P + piece) * DK + cme) * DV + n0;  // this lane's row of a piece summary
+    const int64_t hrow = (bh * DK + cme) * DV + n0;                 // ... of h0, dhT, dh0
+    entry_rows<MODE, DK, DV, NNT>(a, bh, piece, cme, n0, j4, St);
     float dprod = 1.f;
 
     TileRegs<T, CB, NTH> pk;
