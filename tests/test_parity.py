@@ -147,6 +147,12 @@ SPLIT = [
     # fp32 state passes with a whole head per workgroup (256 workgroups) over
     # pieces of three chunks, the last one ragged
     (3062, 128, 128, "scalar", torch.float32, 8, 2, [1000, 2062], True, 16),
+    # the most pieces whose summaries the forward kernel and the backward's state
+    # passes chain themselves (8: 24 chunks in pieces of 3), and one more piece,
+    # where the combine runs instead (27 chunks)
+    (1500, 128, 128, "vector", torch.bfloat16, 2, 2, [400, 1100], True, 8),
+    (1700, 128, 128, "vector", torch.bfloat16, 2, 2, [400, 1300], True, 9),
+    (1500, 128, 128, "scalar", torch.float32, 2, 2, [700, 800], True, 8),
 ]
 
 
