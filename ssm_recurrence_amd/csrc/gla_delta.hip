@@ -703,6 +703,9 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     float* sY = sXY + DC * LP;
     __shared__ float sdG[DC], sdB[DC], sr1[DC], sr2[DC], sdGC;
     __shared__ float smm[MMT_LDS];
+    // bf16 inputs: dK is accumulated in LDS (the room their smaller K tile leaves);
+    // fp32 inputs accumulate it in ws2
+    __shared__ __attribute__((aligned(16))) float sGK[sizeof(T) == 2 ? DC * DK : 1];
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
     const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
@@ -727,6 +730,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     const int n = R.n;
     load_k<T>(R, K, rk, D, sK);
     const ChunkWs w = chunk_ws(a, chunk);
+    float* const gK = sizeof(T) == 2 ? sGK : w.gK;
     // T as the prepare pass stored it (this call's, or the forward's when the stamp matched)
     ew(DC * DC, [&](int i) { return w.T[i]; }, [&](int i, float v) { sT[(i / DC) * LP + i % DC] = v; });
     __syncthreads();
@@ -801,13 +805,13 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     // dQ = gamma dQg (in place), then += (dP (.) M) K; dK = (dP (.) M)^T Q + Kt-scale dKt
     __syncthreads();
     ew(DC * D, [&](int i) { return w.gQ[i] * R.gam[i / D]; }, [&](int i, float v) { w.gQ[i] = v; });
-    ew(DC * D, [&](int i) { return R.kts[i / D] * w.gKt[i]; }, [&](int i, float v) { w.gK[i] = v; });
+    ew(DC * D, [&](int i) { return R.kts[i / D] * w.gKt[i]; }, [&](int i, float v) { gK[i] = v; });
     __syncthreads();
     if constexpr (DK == 128)
         mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gQ);
     else
         mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, w.gQ);
-    mmt(n, D, n, 1.f, sX, 1, LP, Q, rk, 1, 1.f, w.gK, D, 1, smm);
+    mmt(n, D, n, 1.f, sX, 1, LP, Q, rk, 1, 1.f, gK, D, 1, smm);
     __syncthreads();
     // (4) dT = dWv (beta V)^T + dW (beta gamma K)^T in sY ([i][j]), formed as
     //     dT^T = diag(beta) V dWv^T + diag(beta gamma) K dW^T
@@ -851,11 +855,11 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __syncthreads();
     // dK += (dG + dG^T) K (one lane reads and writes each element in both calls)
     if constexpr (DK == 128) {
-        mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gK);
-        mm_lds<DC, 128, DC, 1, LP, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gK);
+        mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, gK);
+        mm_lds<DC, 128, DC, 1, LP, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, gK);
     } else {
-        mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, w.gK);
-        mm_lds<DC, 64, DC, 1, LP, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, w.gK);
+        mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, gK);
+        mm_lds<DC, 64, DC, 1, LP, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, gK);
     }
     __syncthreads();
     __syncthreads();
@@ -872,7 +876,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
         sdB[t] += sr1[t] + R.gam[t] * sr2[t];
         sdG[t] += R.bg[t] * sr2[t];
     }
-    ew(DC * D, [&](int i) { return w.gK[i] + R.bg[i / D] * w.gKb[i]; }, [&](int i, float v) { w.gK[i] = v; });
+    ew(DC * D, [&](int i) { return gK[i] + R.bg[i / D] * w.gKb[i]; }, [&](int i, float v) { gK[i] = v; });
     __syncthreads();
     // (7) the gate: dGamma_last goes to the last row; dg_u = sum of dGamma over t >= u
     //     in u's document; 0 at reset rows
@@ -894,7 +898,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     T* dk = (T*)a.dk_out + row0 * rk + h * D;
     T* dv = (T*)a.dv_out + row0 * rv + h * Dv;
     ew(n * D, [&](int i) { return w.gQ[i]; }, [&](int i, float v) { dq[(i / D) * rk + i % D] = from_f32<T>(v); });
-    ew(n * D, [&](int i) { return w.gK[i]; }, [&](int i, float v) { dk[(i / D) * rk + i % D] = from_f32<T>(v); });
+    ew(n * D, [&](int i) { return gK[i]; }, [&](int i, float v) { dk[(i / D) * rk + i % D] = from_f32<T>(v); });
     ew(n * Dv, [&](int i) { return R.beta[i / Dv] * w.gV[i]; },
        [&](int i, float v) { dv[(i / Dv) * rv + i % Dv] = from_f32<T>(v); });
 }
