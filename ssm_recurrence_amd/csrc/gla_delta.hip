@@ -696,16 +696,17 @@ __global__ __launch_bounds__(DTH) void k_delta_dstate(const DeltaArgs a) {
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __shared__ Rows R;
-    __shared__ float sGE[DC * LP], sT[DC * LP];
     __shared__ __attribute__((aligned(16))) float sXY[2 * DC * LP];
     __shared__ __attribute__((aligned(16))) T sK[DC * (128 + kpad<T>())];  // the chunk's K rows
     float* sX = sXY;
     float* sY = sXY + DC * LP;
     __shared__ float sdG[DC], sdB[DC], sr1[DC], sr2[DC], sdGC;
     __shared__ float smm[MMT_LDS];
-    // bf16 inputs: dK is accumulated in LDS (the room their smaller K tile leaves);
-    // fp32 inputs accumulate it in ws2
-    __shared__ __attribute__((aligned(16))) float sGK[sizeof(T) == 2 ? DC * DK : 1];
+    // dK, and for bf16 inputs (whose K tile is half the size) dQ, accumulate in LDS
+    // rather than in ws2: T is read from ws where it is used and GE formed again
+    // where it is needed, to make the room
+    __shared__ __attribute__((aligned(16))) float sGK[DC * DK];
+    __shared__ __attribute__((aligned(16))) float sGQ[sizeof(T) == 2 ? DC * DK : 1];
     const int64_t NC = (a.T + DC - 1) / DC;
     const int64_t chunk = blockIdx.x, bh = chunk / NC, c = chunk % NC;
     const int64_t b = bh / a.H, h = bh % a.H, t0 = c * DC;
@@ -730,18 +731,15 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     const int n = R.n;
     load_k<T>(R, K, rk, D, sK);
     const ChunkWs w = chunk_ws(a, chunk);
-    float* const gK = sizeof(T) == 2 ? sGK : w.gK;
-    // T as the prepare pass stored it (this call's, or the forward's when the stamp matched)
-    ew(DC * DC, [&](int i) { return w.T[i]; }, [&](int i, float v) { sT[(i / DC) * LP + i % DC] = v; });
-    __syncthreads();
-    gram_masked<T, DK>(R, sK, sGE);
+    float* const gK = sGK;
+    float* const gQ = sizeof(T) == 2 ? sGQ : w.gQ;
     for (int i = threadIdx.x; i < DC * LP; i += DTH) sX[i] = 0.f;
     __syncthreads();
     // S0, Wv, dS1 and dWv are stored transposed ([value column][row]), so that
     // every product below reads its B operand along rows.
 
     // (1) output: dQg = dO S0^T; dP = dO Wv^T
-    mmt(n, D, Dv, 1.f, dO, rv, 1, w.S0, D, 1, 0.f, w.gQ, D, 1, smm);
+    mmt(n, D, Dv, 1.f, dO, rv, 1, w.S0, D, 1, 0.f, gQ, D, 1, smm);
     mmt(n, n, Dv, 1.f, dO, rv, 1, w.Wv, DC, 1, 0.f, sX, LP, 1, smm);
     // (2) state: dKt = Wv dS1^T
     mmt(n, D, Dv, 1.f, w.Wv, 1, DC, w.dS1, D, 1, 0.f, w.gKt, D, 1, smm);
@@ -749,7 +747,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     mmt(DC, D, Dv, -1.f, w.dWv, 1, DC, w.S0, D, 1, 0.f, w.gW, 1, DC, smm);
     __syncthreads();
     // dGamma from gamma Q: rowdot(dQg, Qg); from Kt: -rowdot(dKt, Kt) per row, + sum into dGamma_last
-    rowdot(n, D, w.gQ, D, w.Qg, D, sdG, 1.f);
+    rowdot(n, D, gQ, D, w.Qg, D, sdG, 1.f);
     if (threadIdx.x < DC) sr1[threadIdx.x] = 0.f;
     __syncthreads();
     rowdot(n, D, w.gKt, D, w.Kt, D, sr1, 1.f);
@@ -804,13 +802,13 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     }
     // dQ = gamma dQg (in place), then += (dP (.) M) K; dK = (dP (.) M)^T Q + Kt-scale dKt
     __syncthreads();
-    ew(DC * D, [&](int i) { return w.gQ[i] * R.gam[i / D]; }, [&](int i, float v) { w.gQ[i] = v; });
+    ew(DC * D, [&](int i) { return gQ[i] * R.gam[i / D]; }, [&](int i, float v) { gQ[i] = v; });
     ew(DC * D, [&](int i) { return R.kts[i / D] * w.gKt[i]; }, [&](int i, float v) { gK[i] = v; });
     __syncthreads();
     if constexpr (DK == 128)
-        mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, w.gQ);
+        mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, gQ);
     else
-        mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, w.gQ);
+        mm_lds<DC, 64, DC, LP, 1, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, gQ);
     mmt(n, D, n, 1.f, sX, 1, LP, Q, rk, 1, 1.f, gK, D, 1, smm);
     __syncthreads();
     // (4) dT = dWv (beta V)^T + dW (beta gamma K)^T in sY ([i][j]), formed as
@@ -820,23 +818,25 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __syncthreads();
     for (int i = threadIdx.x; i < DC * LP; i += DTH)
         if (i % LP >= n && i % LP < DC) sY[i] = 0.f;
-    // dVb = T^T dWv, dKb = T^T dW (before sT is consumed), formed transposed:
+    // dVb = T^T dWv, dKb = T^T dW, formed transposed:
     //     dVb^T = dWv^T T, dKb^T = dW^T T
-    mmt(Dv, n, DC, 1.f, w.dWv, DC, 1, sT, LP, 1, 0.f, w.gV, 1, Dv, smm);
-    mmt(D, n, DC, 1.f, w.gW, DC, 1, sT, LP, 1, 0.f, w.gKb, 1, D, smm);
+    // (T as the prepare pass stored it: this call's, or the forward's when the
+    // stamp matched)
+    mmt(Dv, n, DC, 1.f, w.dWv, DC, 1, w.T, DC, 1, 0.f, w.gV, 1, Dv, smm);
+    mmt(D, n, DC, 1.f, w.gW, DC, 1, w.T, DC, 1, 0.f, w.gKb, 1, D, smm);
     __syncthreads();
     // (5) dA = -T^T dT T^T: sX = dT T^T, then sY = -T^T sX
-    mm_lds<DC, DC, DC, LP, 1, LP, 1, LP>(1.f, sY, sT, 0.f, sX);
-    __syncthreads();
-    mm_lds<DC, DC, DC, 1, LP, 1, LP, LP>(-1.f, sT, sX, 0.f, sY);
-    __syncthreads();
+    mmt(DC, DC, DC, 1.f, sY, LP, 1, w.T, 1, DC, 0.f, sX, LP, 1, smm);
+    mmt(DC, DC, DC, -1.f, w.T, 1, DC, sX, LP, 1, 0.f, sY, LP, 1, smm);
+    // GE = (K K^T) (.) E strictly below the diagonal, into sX (no longer read)
+    gram_masked<T, DK>(R, sK, sX);
     // A = diag(beta) GE (strictly lower, same document): dbeta += sum_s dA GE; dGamma via
     // dA (.) A (rows +, columns -); dG = dA beta E in sX (strictly lower)
     if (threadIdx.x < DC) {
         const int t = threadIdx.x;
         float bsum = 0.f, rsum = 0.f, csum = 0.f;
         for (int s = 0; s < DC; ++s) {
-            const float ge_ts = sGE[t * LP + s], ge_st = sGE[s * LP + t];
+            const float ge_ts = sX[t * LP + s], ge_st = sX[s * LP + t];
             const float da_ts = s < t ? sY[t * LP + s] : 0.f, da_st = t < s ? sY[s * LP + t] : 0.f;
             bsum += da_ts * ge_ts;
             rsum += da_ts * ge_ts;
@@ -897,7 +897,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     T* dq = (T*)a.dq + row0 * rk + h * D;
     T* dk = (T*)a.dk_out + row0 * rk + h * D;
     T* dv = (T*)a.dv_out + row0 * rv + h * Dv;
-    ew(n * D, [&](int i) { return w.gQ[i]; }, [&](int i, float v) { dq[(i / D) * rk + i % D] = from_f32<T>(v); });
+    ew(n * D, [&](int i) { return gQ[i]; }, [&](int i, float v) { dq[(i / D) * rk + i % D] = from_f32<T>(v); });
     ew(n * D, [&](int i) { return gK[i]; }, [&](int i, float v) { dk[(i / D) * rk + i % D] = from_f32<T>(v); });
     ew(n * Dv, [&](int i) { return R.beta[i / Dv] * w.gV[i]; },
        [&](int i, float v) { dv[(i / Dv) * rv + i % Dv] = from_f32<T>(v); });
