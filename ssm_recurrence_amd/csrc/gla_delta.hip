@@ -741,8 +741,8 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     // (1) output: dQg = dO S0^T; dP = dO Wv^T
     mmt(n, D, Dv, 1.f, dO, rv, 1, w.S0, D, 1, 0.f, gQ, D, 1, smm);
     mmt(n, n, Dv, 1.f, dO, rv, 1, w.Wv, DC, 1, 0.f, sX, LP, 1, smm);
-    // (2) state: dKt = Wv dS1^T
-    mmt(n, D, Dv, 1.f, w.Wv, 1, DC, w.dS1, D, 1, 0.f, w.gKt, D, 1, smm);
+    // (2) state: dKt = Wv dS1^T, in dK's place (dK starts as it, scaled per row)
+    mmt(n, D, Dv, 1.f, w.Wv, 1, DC, w.dS1, D, 1, 0.f, gK, D, 1, smm);
     // (3) dW = -dWv S0^T, stored transposed ([key channel][row])
     mmt(DC, D, Dv, -1.f, w.dWv, 1, DC, w.S0, D, 1, 0.f, w.gW, 1, DC, smm);
     __syncthreads();
@@ -750,7 +750,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     rowdot(n, D, gQ, D, w.Qg, D, sdG, 1.f);
     if (threadIdx.x < DC) sr1[threadIdx.x] = 0.f;
     __syncthreads();
-    rowdot(n, D, w.gKt, D, w.Kt, D, sr1, 1.f);
+    rowdot(n, D, gK, D, w.Kt, D, sr1, 1.f);
     // carry term: c <dS1, S0>
     {
         float s = 0.f;
@@ -803,7 +803,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     // dQ = gamma dQg (in place), then += (dP (.) M) K; dK = (dP (.) M)^T Q + Kt-scale dKt
     __syncthreads();
     ew(DC * D, [&](int i) { return gQ[i] * R.gam[i / D]; }, [&](int i, float v) { gQ[i] = v; });
-    ew(DC * D, [&](int i) { return R.kts[i / D] * w.gKt[i]; }, [&](int i, float v) { gK[i] = v; });
+    ew(DC * D, [&](int i) { return R.kts[i / D] * gK[i]; }, [&](int i, float v) { gK[i] = v; });
     __syncthreads();
     if constexpr (DK == 128)
         mm_lds<DC, 128, DC, LP, 1, 1, 128 + kpad<T>(), 128>(1.f, sX, sK, 1.f, gQ);
