@@ -818,12 +818,6 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     __syncthreads();
     for (int i = threadIdx.x; i < DC * LP; i += DTH)
         if (i % LP >= n && i % LP < DC) sY[i] = 0.f;
-    // dVb = T^T dWv, dKb = T^T dW, formed transposed:
-    //     dVb^T = dWv^T T, dKb^T = dW^T T
-    // (T as the prepare pass stored it: this call's, or the forward's when the
-    // stamp matched)
-    mmt(Dv, n, DC, 1.f, w.dWv, DC, 1, w.T, DC, 1, 0.f, w.gV, 1, Dv, smm);
-    mmt(D, n, DC, 1.f, w.gW, DC, 1, w.T, DC, 1, 0.f, w.gKb, 1, D, smm);
     __syncthreads();
     // (5) dA = -T^T dT T^T: sX = dT T^T, then sY = -T^T sX
     mmt(DC, DC, DC, 1.f, sY, LP, 1, w.T, 1, DC, 0.f, sX, LP, 1, smm);
@@ -862,13 +856,18 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
         mm_lds<DC, 64, DC, 1, LP, 1, 64 + kpad<T>(), 64>(1.f, sX, sK, 1.f, gK);
     }
     __syncthreads();
-    __syncthreads();
+    // dVb = T^T dWv (into sX, sY: free from here on), dKb = T^T dW, formed
+    // transposed: dVb^T = dWv^T T, dKb^T = dW^T T (T as the prepare pass stored
+    // it: this call's, or the forward's when the stamp matched)
+    float* const gV = sXY;
+    mmt(Dv, n, DC, 1.f, w.dWv, DC, 1, w.T, DC, 1, 0.f, gV, 1, Dv, smm);
+    mmt(D, n, DC, 1.f, w.gW, DC, 1, w.T, DC, 1, 0.f, w.gKb, 1, D, smm);
     // (6) dV = beta dVb; dbeta += V . dVb + gamma K . dKb; dK += beta gamma dKb;
     //     dGamma += beta gamma K . dKb
     if (threadIdx.x < DC) sr1[threadIdx.x] = 0.f;
     if (threadIdx.x >= DC && threadIdx.x < 2 * DC) sr2[threadIdx.x - DC] = 0.f;
     __syncthreads();
-    rowdot(n, Dv, V, rv, w.gV, Dv, sr1, 1.f);
+    rowdot(n, Dv, V, rv, gV, Dv, sr1, 1.f);
     rowdot(n, D, K, rk, w.gKb, D, sr2, 1.f);
     __syncthreads();
     if (threadIdx.x < DC) {
@@ -899,7 +898,7 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
     T* dv = (T*)a.dv_out + row0 * rv + h * Dv;
     ew(n * D, [&](int i) { return gQ[i]; }, [&](int i, float v) { dq[(i / D) * rk + i % D] = from_f32<T>(v); });
     ew(n * D, [&](int i) { return gK[i]; }, [&](int i, float v) { dk[(i / D) * rk + i % D] = from_f32<T>(v); });
-    ew(n * Dv, [&](int i) { return R.beta[i / Dv] * w.gV[i]; },
+    ew(n * Dv, [&](int i) { return R.beta[i / Dv] * gV[i]; },
        [&](int i, float v) { dv[(i / Dv) * rv + i % Dv] = from_f32<T>(v); });
 }
 
