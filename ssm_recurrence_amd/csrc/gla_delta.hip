@@ -333,7 +333,7 @@ __device__ __forceinline__ void wy_inverse(const Rows& R, const T* sK, float* sG
 // per-chunk workspace blocks (fp32): the forward's factors T .. carry (written
 // by the prepare pass only) in ws, the backward's intermediates S0 .. gKb in ws2
 struct ChunkWs {
-    float *T, *U, *W, *P, *Qg, *Kt, *carry, *S0, *Wv, *dS1, *dWv, *gQ, *gK, *gKt, *gW, *gV, *gKb;
+    float *T, *U, *W, *P, *Qg, *Kt, *carry, *S0, *Wv, *dS1, *dWv, *gQ, *gW, *gKb;
 };
 
 __device__ __forceinline__ ChunkWs chunk_ws(const DeltaArgs& a, int64_t chunk) {
@@ -356,11 +356,8 @@ __device__ __forceinline__ ChunkWs chunk_ws(const DeltaArgs& a, int64_t chunk) {
     p = a.states_in_ws ? q : q + D * Dv + DC * Dv;
     w.dS1 = p; p += D * Dv;
     w.dWv = p; p += DC * Dv;
-    w.gQ = p; p += DC * D;
-    w.gK = p; p += DC * D;
-    w.gKt = p; p += DC * D;
+    w.gQ = p; p += DC * D;   // (fp32 inputs; bf16 inputs keep dQ in LDS)
     w.gW = p; p += DC * D;
-    w.gV = p; p += DC * Dv;
     w.gKb = p; p += DC * D;
     return w;
 }
@@ -908,9 +905,9 @@ __global__ __launch_bounds__(DTH) void k_delta_grad(const DeltaArgs a) {
 int64_t delta_fwd_floats_per_chunk(int64_t dk, int64_t dv, bool states_in_ws) {
     return 2 * DC * DC + DC * (dv + 3 * dk) + 4 + (states_in_ws ? dk * dv + DC * dv : 0);
 }
-// (unless states_in_ws) S0, Wv; dS1, dWv, gV; gQ, gK, gKt, gW, gKb
+// (unless states_in_ws) S0, Wv; dS1, dWv; gQ, gW, gKb
 int64_t delta_bwd_floats_per_chunk(int64_t dk, int64_t dv, bool states_in_ws) {
-    return 2 * dk * dv + DC * (3 * dv + 5 * dk) - (states_in_ws ? dk * dv + DC * dv : 0);
+    return 2 * dk * dv + DC * (2 * dv + 3 * dk) - (states_in_ws ? dk * dv + DC * dv : 0);
 }
 
 

@@ -408,11 +408,11 @@ def delta_sizes(lib, p):
 def test_delta_workspace(lib):
     """ws: a 256-byte stamp and the forward's per-chunk factors (T, P: 64 x 64;
     U: 64 x d_v; W, gamma Q, decayed K: 64 x d_k; the carry: 4 floats); the
-    backward's scratch: 2 d_k x d_v + 64 (3 d_v + 5 d_k) floats per chunk."""
+    backward's scratch: 2 d_k x d_v + 64 (2 d_v + 3 d_k) floats per chunk."""
     p = delta_prob()  # 2 chunks x 8 heads, d_k 128, d_v 64
     n, m = delta_sizes(lib, p)
     per_f = 2 * 64 * 64 + 64 * (64 + 3 * 128) + 4
-    per_b = 2 * 128 * 64 + 64 * (3 * 64 + 5 * 128)
+    per_b = 2 * 128 * 64 + 64 * (2 * 64 + 3 * 128)
     assert n == 256 + 2 * 8 * per_f * 4 and m == 2 * 8 * per_b * 4
     assert call_delta_fwd(lib, p, ws_bytes=n) == -6                       # ws NULL
     assert call_delta_fwd(lib, p, {"ws": FAKE}, ws_bytes=n - 1) == -6
